@@ -1,0 +1,288 @@
+"""Seeded synthetic inputs for the token-tree attention + verification path.
+
+This module only draws random data and lays it out; it computes none of the
+method's arithmetic (no softmax, no attention, no acceptance test).  Both the
+HIP path and the CPU oracle consume the same arrays produced here.
+
+Layouts (all arrays are NumPy, C-contiguous):
+
+  q            [B][Nmax][Hq][D]            float32 holding bf16-exact values when dtype == "bf16"
+  k_cache      [num_blocks][Hkv][bs][D]    token-major key blocks
+  v_cache      [num_blocks][Hkv][D][bs]    value blocks stored transposed (d-major, token contiguous)
+  block_table  [B][max_blocks]  int32     -1 past the blocks a request owns
+  prefix_len   [B] int32, n_nodes [B] int32
+  parent       [B][Nmax] int32            parent[b][0] = -1, 0 <= parent[i] < i, -1 as padding
+  tokens       [B][Nmax] int32            token of each tree node (the root's is the last emitted token)
+  target_logits, draft_logits [B][Nmax][V] float32 (zero rows past n_nodes)
+  u_accept, u_sample          [B][Nmax]    float32 uniforms in [0, 1)
+
+Trees are drawn by random attachment (each new node picks a uniformly random
+eligible parent, subject to optional width/depth caps), then renumbered to
+depth-first preorder as the SpecInfer guide lays nodes out ("Depth-First
+Flattening and KV Cache Reuse").  A child's token is an independent draw from
+the draft distribution of its parent (Gumbel-max on the parent's draft-logit
+row), so the i.i.d.-proposal precondition of rejection sampling holds.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+# Named workloads.  Sizes follow the five synthetic configurations this path is
+# measured on: a tiny fp32 case, a Llama-3-8B-shaped layer, a ragged paged
+# batch, a batch of chains (linear speculative decoding) and a 70B-shaped share.
+CONFIGS = {
+    "tiny": dict(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=64, dtype="f32",
+                 prefix=(128, 128), n_nodes=8, tree="capped", width=3, depth=3,
+                 vocab=1000, target_sd=2.0, draft_noise_sd=0.5, block_size=16, paged=False),
+    "llama8b": dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
+                    prefix=(2048, 2048), n_nodes=64, tree="capped", width=4, depth=8,
+                    vocab=128256, target_sd=3.0, draft_noise_sd=1.0, block_size=16, paged=False),
+    "ragged": dict(batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
+                   prefix=(512, 8192), n_nodes=32, tree="recursive", width=None, depth=None,
+                   vocab=128256, target_sd=3.0, draft_noise_sd=1.0, block_size=16, paged=True),
+    "chain": dict(batch=64, n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
+                  prefix=(4096, 4096), n_nodes=(3, 8), tree="chain", width=1, depth=None,
+                  vocab=128256, target_sd=3.0, draft_noise_sd=1.0, block_size=16, paged=False),
+    "llama70b_share": dict(batch=4, n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16",
+                           prefix=(32768, 32768), n_nodes=128, tree="capped", width=8, depth=10,
+                           vocab=128256, target_sd=3.0, draft_noise_sd=1.0, block_size=16, paged=False),
+}
+
+CONFIG_ORDER = ["tiny", "llama8b", "ragged", "chain", "llama70b_share"]
+
+
+def seed_for(name: str, extra: int = 0) -> int:
+    """Seed = 1000 + position of the config in CONFIG_ORDER (+100 per extra parity seed)."""
+    return 1000 + CONFIG_ORDER.index(name) + 100 * extra
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers (data preparation only)
+# --------------------------------------------------------------------------
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of float32 values that are already bf16-exact."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 bit patterns (uint16) to float32 exactly."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# trees
+# --------------------------------------------------------------------------
+
+def dfs_renumber(parent: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Renumber a tree (parent[i] < i) to depth-first preorder.
+
+    Children are visited in creation (ascending index) order.  Returns
+    (new_parent, order) where order[new_id] = old_id.
+    """
+    n = len(parent)
+    kids = [[] for _ in range(n)]
+    for i in range(1, n):
+        kids[parent[i]].append(i)
+    order = []
+    stack = [0]
+    while stack:
+        u = stack.pop()
+        order.append(u)
+        stack.extend(reversed(kids[u]))
+    new_id = np.empty(n, dtype=np.int64)
+    new_id[np.asarray(order)] = np.arange(n)
+    new_parent = np.full(n, -1, dtype=np.int32)
+    for old in range(1, n):
+        new_parent[new_id[old]] = new_id[parent[old]]
+    return new_parent, np.asarray(order)
+
+
+def random_tree(rng: np.random.Generator, n: int, kind: str, width=None, depth=None) -> np.ndarray:
+    """Parent array of an n-node tree in DFS preorder.
+
+    kind = "capped": random attachment to a node with depth < depth cap and
+    fewer than `width` children; "recursive": uniform random recursive tree
+    (no caps); "chain": parent[i] = i - 1; "star": every node hangs off the root.
+    """
+    if kind == "chain":
+        p = np.arange(-1, n - 1, dtype=np.int32)
+        return p
+    if kind == "star":
+        p = np.zeros(n, dtype=np.int32)
+        p[0] = -1
+        return p
+    parent = np.full(n, -1, dtype=np.int32)
+    dep = np.zeros(n, dtype=np.int64)
+    nkid = np.zeros(n, dtype=np.int64)
+    for i in range(1, n):
+        if kind == "recursive":
+            cand = np.arange(i)
+        elif kind == "capped":
+            ok = np.ones(i, dtype=bool)
+            if depth is not None:
+                ok &= dep[:i] < depth
+            if width is not None:
+                ok &= nkid[:i] < width
+            cand = np.nonzero(ok)[0]
+            if len(cand) == 0:
+                raise ValueError("tree caps leave no eligible parent")
+        else:
+            raise ValueError(kind)
+        pu = int(cand[rng.integers(len(cand))])
+        parent[i] = pu
+        dep[i] = dep[pu] + 1
+        nkid[pu] += 1
+    new_parent, _ = dfs_renumber(parent)
+    return new_parent
+
+
+def gumbel_max_draw(rng: np.random.Generator, logits_row: np.ndarray, count: int) -> np.ndarray:
+    """`count` i.i.d. draws from the distribution whose logits are `logits_row`
+    (Gumbel-max: argmax of logits plus standard Gumbel noise)."""
+    out = np.empty(count, dtype=np.int32)
+    z = logits_row.astype(np.float64)
+    for k in range(count):
+        g = -np.log(-np.log(rng.random(z.shape[0]) + 1e-300) + 1e-300)
+        out[k] = int(np.argmax(z + g))
+    return out
+
+
+# --------------------------------------------------------------------------
+# workload container
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    dtype: str                 # "bf16" or "f32"
+    batch: int
+    n_max: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    block_size: int
+    vocab: int
+    num_blocks: int
+    max_blocks: int
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_table: np.ndarray
+    prefix_len: np.ndarray
+    n_nodes: np.ndarray
+    parent: np.ndarray
+    tokens: np.ndarray
+    target_logits: np.ndarray | None
+    draft_logits: np.ndarray | None
+    u_accept: np.ndarray
+    u_sample: np.ndarray
+    temperature: float = 1.0
+    seed: int = 0
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def make_workload(name: str, seed: int | None = None, *, batch=None, prefix=None, n_nodes=None,
+                  vocab=None, tree=None, width="cfg", depth="cfg", n_max=None, paged=None,
+                  with_logits=True, kv_fill="normal", logits_dtype=np.float32) -> Workload:
+    """Build one seeded workload.  Keyword overrides shrink or reshape a named
+    config (parity tests use smaller prefixes / vocabularies of the same kind)."""
+    cfg = dict(CONFIGS[name])
+    if seed is None:
+        seed = seed_for(name)
+    rng = np.random.default_rng(seed)
+    B = cfg["batch"] if batch is None else batch
+    Hq, Hkv, D = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    bs = cfg["block_size"]
+    V = cfg["vocab"] if vocab is None else vocab
+    pre = cfg["prefix"] if prefix is None else prefix
+    if isinstance(pre, int):
+        pre = (pre, pre)
+    nn = cfg["n_nodes"] if n_nodes is None else n_nodes
+    kind = cfg["tree"] if tree is None else tree
+    w = cfg["width"] if width == "cfg" else width
+    d = cfg["depth"] if depth == "cfg" else depth
+    is_paged = cfg["paged"] if paged is None else paged
+
+    # request shapes
+    P = rng.integers(pre[0], pre[1] + 1, size=B).astype(np.int32)
+    if isinstance(nn, tuple):
+        N = rng.integers(nn[0], nn[1] + 1, size=B).astype(np.int32)
+    else:
+        N = np.full(B, nn, dtype=np.int32)
+    Nmax = int(N.max()) if B > 0 else 1
+    if n_max is not None:
+        Nmax = max(Nmax, n_max)
+
+    parent = np.full((B, Nmax), -1, dtype=np.int32)
+    for b in range(B):
+        parent[b, :N[b]] = random_tree(rng, int(N[b]), kind, w, d)
+
+    # paged KV pool: each request owns ceil((P + N) / bs) blocks
+    need = [(int(P[b]) + int(N[b]) + bs - 1) // bs for b in range(B)]
+    num_blocks = max(1, sum(need))
+    max_blocks = max([1] + need)
+    pool = np.arange(num_blocks, dtype=np.int32)
+    if is_paged:
+        pool = rng.permutation(pool).astype(np.int32)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :need[b]] = pool[off:off + need[b]]
+        off += need[b]
+
+    dt = cfg["dtype"]
+
+    def draw(shape):
+        if kv_fill == "normal":
+            x = rng.standard_normal(size=shape, dtype=np.float32)
+        else:
+            raise ValueError(kv_fill)
+        return round_to_bf16(x) if dt == "bf16" else x
+
+    q = draw((B, Nmax, Hq, D))
+    k_cache = draw((num_blocks, Hkv, bs, D))
+    v_cache = draw((num_blocks, Hkv, D, bs))
+
+    tokens = np.zeros((B, Nmax), dtype=np.int32)
+    tl = dl = None
+    if with_logits:
+        tl = np.zeros((B, Nmax, V), dtype=logits_dtype)
+        dl = np.zeros((B, Nmax, V), dtype=logits_dtype)
+        for b in range(B):
+            n = int(N[b])
+            t = rng.standard_normal(size=(n, V), dtype=np.float32) * np.float32(cfg["target_sd"])
+            e = rng.standard_normal(size=(n, V), dtype=np.float32) * np.float32(cfg["draft_noise_sd"])
+            tl[b, :n] = t
+            dl[b, :n] = t + e
+    for b in range(B):
+        n = int(N[b])
+        tokens[b, 0] = rng.integers(V)
+        for c in range(1, n):
+            if dl is not None:
+                tokens[b, c] = gumbel_max_draw(rng, dl[b, parent[b, c]], 1)[0]
+            else:
+                tokens[b, c] = rng.integers(V)
+    u_accept = rng.random(size=(B, Nmax), dtype=np.float32)
+    u_sample = rng.random(size=(B, Nmax), dtype=np.float32)
+
+    return Workload(name=name, dtype=dt, batch=B, n_max=Nmax, n_q_heads=Hq, n_kv_heads=Hkv,
+                    head_dim=D, block_size=bs, vocab=V, num_blocks=num_blocks, max_blocks=max_blocks,
+                    q=q, k_cache=k_cache, v_cache=v_cache, block_table=table, prefix_len=P,
+                    n_nodes=N, parent=parent, tokens=tokens, target_logits=tl, draft_logits=dl,
+                    u_accept=u_accept, u_sample=u_sample, seed=seed)
