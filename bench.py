@@ -1,0 +1,325 @@
+"""Benchmark of the token-tree attention + verification path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+tree attention -> stochastic tree verification -> accepted-path KV compaction
+(the ancestor-mask build and the split-K merge run inside the attention kernel,
+row statistics / decisions / path selection inside the verification kernel).
+
+Prints ONE JSON line.  `value` = tree nodes verified per second over the timed
+steps (sum of n_nodes over the batch / seconds per step), inputs resident in
+HBM.  Every step reads a different copy of the inputs (rotating through at least
+1 GiB) so the 256 MB Infinity Cache cannot serve repeated reads.
+
+Per-kernel durations come from HIP events recorded on the stream the kernels run
+on (torch's current stream), averaged over back-to-back calls on rotating copies.
+The CPU oracle is timed on a bounded sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tree nodes verified/sec + tree-attn HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama8b",
+                    choices=["tiny", "llama8b", "ragged", "chain", "llama70b_share"])
+    ap.add_argument("--kernel-reps", type=int, default=100, help="back-to-back calls per kernel timing")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    return ap.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "tree_verification_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    from tree_verification_amd import binding as tv
+    from tree_verification_amd.workloads import bf16_bits, make_workload, seed_for
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tv.load_library()
+    dev = torch.device("cuda:0")
+    seed = seed_for(args.config) if args.seed is None else args.seed
+    t0 = time.time()
+    wl = make_workload(args.config, seed=seed)
+    gen_s = time.time() - t0
+    B, Nmax, V = wl.batch, wl.n_max, wl.vocab
+    n_total = int(wl.n_nodes.sum())
+    esize = 2 if wl.dtype == "bf16" else 4
+
+    def kv(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(bf16_bits(x)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+
+    base = dict(q=kv(wl.q), k=kv(wl.k_cache), v=kv(wl.v_cache), table=i32(wl.block_table),
+                pre=i32(wl.prefix_len), nn=i32(wl.n_nodes), par=i32(wl.parent), tok=i32(wl.tokens),
+                tl=torch.from_numpy(wl.target_logits).to(dev), dl=torch.from_numpy(wl.draft_logits).to(dev),
+                ua=torch.from_numpy(wl.u_accept).to(dev), us=torch.from_numpy(wl.u_sample).to(dev))
+    copy_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    ncopies = max(2, math.ceil(ROTATE_BYTES / copy_bytes))
+    copies = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(ncopies - 1)]
+    pristine_k, pristine_v = base["k"].clone(), base["v"].clone()
+    for c in copies:
+        c["out"] = torch.empty_like(c["q"])
+        c["ast"] = torch.empty(B, dtype=torch.int32, device=dev)
+        c["path"] = torch.empty((B, Nmax), dtype=torch.int32, device=dev)
+        c["plen"] = torch.empty(B, dtype=torch.int32, device=dev)
+        c["otok"] = torch.empty((B, Nmax), dtype=torch.int32, device=dev)
+        c["vst"] = torch.empty(B, dtype=torch.int32, device=dev)
+        c["gpath"] = torch.empty((B, Nmax), dtype=torch.int32, device=dev)
+        c["gplen"] = torch.empty(B, dtype=torch.int32, device=dev)
+        c["gotok"] = torch.empty((B, Nmax), dtype=torch.int32, device=dev)
+        c["gst"] = torch.empty(B, dtype=torch.int32, device=dev)
+        c["src"] = torch.empty((B, Nmax), dtype=torch.int32, device=dev)
+        c["nlen"] = torch.empty(B, dtype=torch.int32, device=dev)
+        c["cst"] = torch.empty(B, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def attn(c):
+        tv.tree_attn_forward(c["q"], c["k"], c["v"], c["table"], c["pre"], c["nn"], c["par"],
+                             out=c["out"], status=c["ast"])
+
+    def verify(c):
+        tv.tree_verify_stochastic(c["tl"], c["dl"], c["tok"], c["par"], c["nn"], c["ua"], c["us"],
+                                  path=c["path"], path_len=c["plen"], out_tokens=c["otok"], status=c["vst"])
+
+    def greedy(c):
+        tv.tree_verify_greedy(c["tl"], c["tok"], c["par"], c["nn"], path=c["gpath"], path_len=c["gplen"],
+                              out_tokens=c["gotok"], status=c["gst"])
+
+    def compact(c):
+        tv.kv_compact_accepted(c["k"], c["v"], c["table"], c["pre"], c["path"], c["plen"],
+                               src_pos=c["src"], new_len=c["nlen"], status=c["cst"])
+
+    def step(c):
+        attn(c)
+        verify(c)
+        compact(c)
+
+    # one untimed step on copy 0, then restore its caches (compaction moved slots)
+    step(copies[0])
+    torch.cuda.synchronize()
+    assert int(copies[0]["ast"].abs().sum()) == 0 and int(copies[0]["vst"].abs().sum()) == 0
+    path0 = copies[0]["path"].cpu().numpy()
+    plen0 = copies[0]["plen"].cpu().numpy()
+    copies[0]["k"].copy_(pristine_k)
+    copies[0]["v"].copy_(pristine_v)
+    del pristine_k, pristine_v
+
+    # ---- whole-step timing -------------------------------------------------
+    for i in range(args.warmup):
+        step(copies[i % ncopies])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(copies[i % ncopies])
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-kernel timing (back-to-back calls on rotating copies) ----------
+    def time_calls(fn, reps):
+        for i in range(min(reps, 5)):
+            fn(copies[i % ncopies])
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(copies[i % ncopies])
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3   # microseconds per call
+
+    us_attn = time_calls(attn, args.kernel_reps)
+    us_verify = time_calls(verify, args.kernel_reps)
+    us_greedy = time_calls(greedy, args.kernel_reps)
+    us_compact = time_calls(compact, args.kernel_reps)
+
+    # ---- algorithmic bytes --------------------------------------------------
+    P = wl.prefix_len.astype(np.int64)
+    n = wl.n_nodes.astype(np.int64)
+    H, Hkv, D = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    attn_bytes = int((2 * n.sum() * H * D + 2 * (P + n).sum() * Hkv * D) * esize)
+    # prefix part: every (node, q-head) row against every prefix key (QK^T and PV)
+    attn_flops = int(sum(4 * int(n[b]) * H * D * int(P[b]) for b in range(B)))
+    # tree part: each node attends to its depth + 1 tree keys
+    for b in range(B):
+        par = wl.parent[b]
+        depth = np.zeros(int(n[b]), dtype=np.int64)
+        for u in range(1, int(n[b])):
+            depth[u] = depth[par[u]] + 1
+        attn_flops += int(4 * H * D * (depth + 1).sum())
+    internal = 0
+    passes = 0
+    for b in range(B):
+        nb = int(n[b])
+        par = wl.parent[b, :nb]
+        internal += len(set(int(x) for x in par[1:]))
+        # residual passes realised on the accepted path: rejected siblings before
+        # each accepted child, and every child of the final node
+        L = int(plen0[b])
+        pth = [int(x) for x in path0[b, :L]]
+        for j, u in enumerate(pth):
+            kids = [c for c in range(1, nb) if par[c] == u]
+            passes += kids.index(pth[j + 1]) if j + 1 < L else len(kids)
+    row = V * 4
+    verify_bytes = int(n.sum() * row + internal * row + passes * 2 * row)
+    greedy_bytes = int(n.sum() * row)
+    compact_bytes = int(2 * 2 * plen0.astype(np.int64).sum() * Hkv * D * esize)
+
+    def gbs(nbytes, us):
+        return nbytes / (us * 1e-6) / 1e9
+
+    kernels = {
+        "tree_attn": {"us": us_attn, "bytes": attn_bytes, "GBps": gbs(attn_bytes, us_attn),
+                      "TFLOPs": attn_flops / (us_attn * 1e-6) / 1e12},
+        "tree_verify_stochastic": {"us": us_verify, "bytes": verify_bytes, "GBps": gbs(verify_bytes, us_verify)},
+        "kv_compact": {"us": us_compact, "bytes": compact_bytes, "GBps": gbs(compact_bytes, us_compact)},
+    }
+    for k in kernels.values():
+        k["frac_hbm"] = k["GBps"] / HBM_PEAK_GBS
+    dominant = max(kernels, key=lambda k: kernels[k]["us"])
+    src = {"tree_attn": ("tree_attn.hip",), "tree_verify_stochastic": ("tree_verify.hip",),
+           "kv_compact": ("kv_compact.hip",)}
+
+    def roofline(name):
+        k = kernels[name]
+        return {"kernel": name, "bound": "hbm", "achieved": round(k["GBps"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(k["GBps"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic_record(name, args.config, source_hash(*src[name])),
+                "algorithmic_bytes_per_launch": k["bytes"], "avg_launch_us": round(k["us"], 3)}
+
+    # ---- CPU oracle baseline ------------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    value = n_total / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.config, "batch": B, "tree_nodes": n_total, "n_max": Nmax,
+                   "prefix_len_total": int(P.sum()), "q_heads": H, "kv_heads": Hkv, "head_dim": D,
+                   "vocab": V, "kv_dtype": wl.dtype, "verify": "stochastic", "seed": seed,
+                   "rotating_copies": ncopies, "bytes_per_copy": copy_bytes},
+        "roofline": roofline(dominant),
+        "tree_attn_roofline": roofline("tree_attn"),
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in d.items()}
+                    for k, d in kernels.items()},
+        "greedy": {"us_per_call": round(us_greedy, 3), "bytes": greedy_bytes,
+                   "GBps": round(gbs(greedy_bytes, us_greedy), 1),
+                   "nodes_per_s": n_total / (us_greedy * 1e-6)},
+        "accepted_mean": float(plen0.mean() - 1),
+        "cpu_baseline": cpu,
+        "input_generation_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle, unmodified, timed on the host on the workload's first request(s):
+    tree attention for every (node, q-head) row, stochastic verification and KV
+    compaction, repeated until `seconds` have elapsed; single BLAS thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle.attention import tree_attention
+    from oracle.kv import kv_compact
+    from oracle.verify import verify_stochastic
+
+    reqs = []
+    done_nodes = 0
+    t0 = time.perf_counter()
+    b = 0
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < seconds or not reqs:
+            sl = slice(b, b + 1)
+            outs, _ = tree_attention(wl.q[sl], wl.k_cache, wl.v_cache, wl.block_table[sl], wl.prefix_len[sl],
+                                     wl.n_nodes[sl], wl.parent[sl], n_q_heads=wl.n_q_heads,
+                                     n_kv_heads=wl.n_kv_heads, block_size=wl.block_size,
+                                     num_blocks=wl.num_blocks, n_max=wl.n_max, sm_scale=wl.sm_scale)
+            paths, _, _, _ = verify_stochastic(wl.target_logits[sl], wl.draft_logits[sl], wl.tokens[sl],
+                                               wl.parent[sl], wl.n_nodes[sl], wl.u_accept[sl],
+                                               wl.u_sample[sl], wl.n_max)
+            pth = np.full((1, wl.n_max), -1, dtype=np.int32)
+            pth[0, :len(paths[0])] = paths[0]
+            kv_compact(wl.k_cache, wl.v_cache, wl.block_table[sl], wl.prefix_len[sl], pth,
+                       np.array([len(paths[0])]), block_size=wl.block_size, num_blocks=wl.num_blocks,
+                       n_max=wl.n_max)
+            done_nodes += int(wl.n_nodes[b])
+            reqs.append(b)
+            b = (b + 1) % wl.batch
+    el = time.perf_counter() - t0
+    try:
+        model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
+    except (OSError, IndexError):
+        model = "unknown"
+    return {"value": done_nodes / el, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(reqs)} request-steps of this workload (attention for every node and q-head, "
+                      f"stochastic verification, KV compaction), {el:.1f} s, 1 BLAS thread",
+            "cpu_model": model}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * tree_verify.h -- C interface of libtreeverify.so: token-tree attention,
+ * token-tree verification and accepted-path KV compaction on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources (web pages, section names as printed):
+ *   [guide]   "SpecInfer Guide: Tree-Based Speculative LLM Serving"
+ *   [chapter] "Inference Optimization Techniques: Speed and Efficiency"
+ *
+ * General rules for every entry point:
+ *   - Array arguments are DEVICE pointers owned by the caller; the library
+ *     keeps no reference to them after the call is enqueued.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream);
+ *     nothing is synchronised and nothing returns to the host.
+ *   - The return value reports synchronous argument errors found on the host
+ *     before anything is launched (TV_OK = 0, negative = error; nothing was
+ *     enqueued).  Data errors in device arrays are reported per request in
+ *     `status[b]` as a bitwise OR of TV_REQ_* flags; a request with a non-zero
+ *     status has unspecified outputs but is never read or written out of
+ *     bounds.
+ *   - `workspace` is caller-owned device scratch of at least the size the
+ *     matching *_workspace_size() returns for the call's descriptor.  Its
+ *     layout depends on the descriptor: it must be zero-filled before its first
+ *     use with a given descriptor (and again before reuse with another one);
+ *     every call leaves its counters at zero again, so repeated calls with the
+ *     same descriptor need no clearing.  Two calls that may run concurrently
+ *     must use distinct workspaces.
+ *   - Node ids: a tree of n nodes is a parent array with parent[0] = -1 (node 0
+ *     is the root: the last token already emitted) and 0 <= parent[i] < i.
+ *     Rows are padded to n_max; padding rows are neither read nor written.
+ *   - Integer types are int32_t; bf16 tensors are passed as raw 16-bit words.
+ */
+#ifndef TREE_VERIFY_H
+#define TREE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- synchronous status codes ------------------------------------------ */
+enum {
+  TV_OK = 0,
+  TV_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad descriptor field */
+  TV_ERR_UNSUPPORTED = -2,  /* head_dim, dtype, block_size or n_max outside the supported set */
+  TV_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+  TV_ERR_HIP = -4           /* a HIP runtime call failed (device query or launch) */
+};
+
+/* ---- per-request status flags (status[b], bitwise OR) -------------------- */
+enum {
+  TV_REQ_BAD_PARENT = 1,    /* parent[0] != -1 or some parent[i] outside [0, i) */
+  TV_REQ_BAD_NNODES = 2,    /* n_nodes[b] outside [1, n_max] */
+  TV_REQ_BAD_KV = 4,        /* prefix_len < 0, positions past the block table, or a block id outside the pool */
+  TV_REQ_NONFINITE = 8,     /* a logit row that is read holds NaN or +-inf */
+  TV_REQ_BAD_TOKEN = 16,    /* a child token outside [0, vocab) (stochastic verification) */
+  TV_REQ_BAD_PATH = 32,     /* accepted path is not 0 followed by increasing node ids < n_max */
+  TV_REQ_TIMEOUT = 64       /* a bounded inter-workgroup wait expired (results unspecified) */
+};
+
+/* ---- element types ------------------------------------------------------ */
+enum { TV_F32 = 0, TV_BF16 = 1 };
+
+/* ---- attention / cache descriptor --------------------------------------- */
+typedef struct tv_attn_desc {
+  int32_t batch;              /* B >= 0 requests */
+  int32_t n_max;              /* node stride of q/out/parent/path, 1..128 */
+  int32_t n_q_heads;          /* Hq >= 1 */
+  int32_t n_kv_heads;         /* Hkv >= 1, divides Hq; q-head h reads KV head h / (Hq / Hkv) */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t block_size;         /* tokens per KV block: 16, 32, 64 or 128 */
+  int32_t max_blocks_per_seq; /* row stride of block_table (>= 1) */
+  int32_t num_blocks;         /* blocks in the pool; block ids outside [0, num_blocks) are data errors */
+  int32_t dtype;              /* TV_F32 or TV_BF16: element type of q, k_cache, v_cache and out */
+  float sm_scale;             /* softmax scale; <= 0 selects 1 / sqrt(head_dim) */
+} tv_attn_desc;
+
+/* Cache layout (both caches are indexed by physical block id):
+ *   k_cache [num_blocks][Hkv][block_size][D]   token-major key rows
+ *   v_cache [num_blocks][Hkv][D][block_size]   value blocks stored transposed
+ * Logical position p of request b lives in block block_table[b][p / block_size],
+ * slot p % block_size.  A request's prefix occupies positions [0, P) and its
+ * tree nodes positions [P, P + n) in node order ([guide] "Depth-First
+ * Flattening and KV Cache Reuse": tree tokens append their K/V to the cache). */
+
+/* Bytes of workspace tree_attn_forward needs for `desc` on the current device. */
+size_t tree_attn_workspace_size(const tv_attn_desc* desc);
+
+/* Tree attention ([guide] "Generalizing Attention to Tree Topologies" and "The
+ * Topology-Aware 2D Causal Mask"): for request b, q-head h and node u < n_b,
+ *   out[b][u][h] = sum_v alpha_v V_v,  alpha = softmax_v(sm_scale * q . K_v)
+ * over the keys v in the prefix [0, P_b) and the tree positions P_b + w with w
+ * equal to u or one of u's ancestors (parent walk of parent[b]).
+ *   q      [B][n_max][Hq][D]     (dtype)
+ *   out    [B][n_max][Hq][D]     (dtype) written for u < n_b only
+ *   block_table [B][max_blocks_per_seq], prefix_len [B], n_nodes [B], parent [B][n_max]
+ *   status [B] or NULL: TV_REQ_BAD_NNODES / _BAD_PARENT / _BAD_KV
+ * The caches are only read. */
+int tree_attn_forward(const tv_attn_desc* desc, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
+                      const int32_t* n_nodes, const int32_t* parent, void* out, int32_t* status,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- verifier descriptor ------------------------------------------------- */
+typedef struct tv_verify_desc {
+  int32_t batch;        /* B >= 0 */
+  int32_t n_max;        /* node stride, 1..128 */
+  int32_t vocab;        /* V >= 1: row length of the logit arrays */
+  float temperature;    /* > 0; logits are divided by it (stochastic verification only) */
+} tv_verify_desc;
+
+/* Outputs common to both verifiers, per request b (n = n_nodes[b]):
+ *   path [B][n_max]       path[0] = 0, then the accepted nodes root to leaf
+ *   path_len [B]          L + 1 = number of entries of path and of out_tokens
+ *                         (0 when status[b] != 0)
+ *   out_tokens [B][n_max] the L accepted tokens, then one correction/bonus token
+ *                         ([chapter] "Worked Example ...": a round emits K + 1)
+ *   status [B]            TV_REQ_* flags (required)
+ * Entries past path_len are not written. */
+
+/* Bytes of workspace either verifier needs for `desc`.  The two verifiers lay
+ * their workspaces out differently: give each its own buffer. */
+size_t tree_verify_workspace_size(const tv_verify_desc* desc);
+
+/* Greedy verification ([guide] "Greedy Verification Algorithm"): from the root,
+ * t = argmax_w target_logits[b][u][w] (lowest index among equal maxima); move to
+ * the first child c (ascending node id) with tokens[b][c] == t, else emit t and
+ * stop.  A leaf emits its argmax.
+ *   target_logits [B][n_max][V] float32 (rows u < n read); tokens, parent [B][n_max]. */
+int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
+                       const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
+                       int32_t* path, int32_t* path_len, int32_t* out_tokens, int32_t* status,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stochastic verification ([guide] "Stochastic Verification Algorithm";
+ * [chapter] acceptance rule min(1, p/q) and residual max(p - q, 0) / Z).
+ * At node u with p = softmax(target_u / T), q = softmax(draft_u / T), p' = p:
+ * children c are tried in ascending id with proposal x = tokens[c]; c is
+ * accepted when u_accept[b][c] * q(x) <= p'(x); a rejection replaces p' by
+ * max(p' - q, 0) / Z (kept when Z = 0) before the next sibling is tried.  When
+ * no child is accepted (always at a leaf) the final token is the smallest x
+ * whose cumulative p' exceeds u_sample[b][u] * sum(p').
+ *   draft_logits [B][n_max][V] float32: only rows of nodes that have children are read.
+ *   u_accept, u_sample [B][n_max] float32 uniforms in [0, 1), supplied by the caller.
+ * Decisions use float32 exponentials with float64 sums and a float64 accept test. */
+int tree_verify_stochastic(const tv_verify_desc* desc, const float* target_logits,
+                           const float* draft_logits, const int32_t* tokens,
+                           const int32_t* parent, const int32_t* n_nodes, const float* u_accept,
+                           const float* u_sample, int32_t* path, int32_t* path_len,
+                           int32_t* out_tokens, int32_t* status, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Accepted-path KV compaction ([guide] "Depth-First Flattening and KV Cache
+ * Reuse"; "PagedKV Allocation with Zero-Copy Pruning"): for j = 0..L,
+ * K/V at position P + path[j] is moved to position P + j (all KV heads) and
+ * new_len[b] = P + L + 1.  The move is in place and hazard-free (every source
+ * is read before any destination is written).  A request with path_len 0 or a
+ * malformed path is left untouched: new_len = prefix_len, src_pos = -1.
+ *   path, path_len as produced by the verifiers; src_pos [B][n_max] receives
+ *   P + path[j] for j < path_len and -1 elsewhere; new_len [B];
+ *   status [B] or NULL: TV_REQ_BAD_PATH / TV_REQ_BAD_KV.
+ * Only desc->batch, n_max, n_kv_heads, head_dim, block_size,
+ * max_blocks_per_seq, num_blocks and dtype are used. */
+int kv_compact_accepted(const tv_attn_desc* desc, void* k_cache, void* v_cache,
+                        const int32_t* block_table, const int32_t* prefix_len,
+                        const int32_t* path, const int32_t* path_len, int32_t* src_pos,
+                        int32_t* new_len, int32_t* status, hipStream_t stream);
+
+/* Human-readable name of a synchronous status code. */
+const char* tv_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREE_VERIFY_H */

@@ -1,0 +1,172 @@
+"""GPU parity of tree attention against the float64 oracle.
+
+Tolerance (the attention output is a convex combination of value rows): per
+(request, node, q-head) row, ||o - o_ref|| / ||o_ref|| <= 2e-2 for bf16 inputs
+and 1e-5 for fp32 inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from devdata import DevWorkload, out_to_np
+from oracle.attention import tree_attention
+from tree_verification_amd import binding as tv
+from tree_verification_amd.workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def run_gpu(wl, **kw):
+    d = DevWorkload(wl, logits=False)
+    out, st = tv.tree_attn_forward(d.q, d.k, d.v, d.table, d.prefix_len, d.n_nodes, d.parent, **kw)
+    torch.cuda.synchronize()
+    return out_to_np(out), st.cpu().numpy(), d, out
+
+
+def oracle(wl, requests=None, rows=None):
+    return tree_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.prefix_len, wl.n_nodes,
+                          wl.parent, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                          block_size=wl.block_size, num_blocks=wl.num_blocks, n_max=wl.n_max,
+                          sm_scale=wl.sm_scale, requests=requests, rows=rows)
+
+
+def check_all_rows(wl, out, status):
+    ref, rst = oracle(wl)
+    assert np.array_equal(status, rst)
+    worst = 0.0
+    for b in range(wl.batch):
+        if rst[b]:
+            continue
+        n = int(wl.n_nodes[b])
+        o = out[b, :n].astype(np.float64)
+        err = np.linalg.norm(o - ref[b], axis=-1) / np.linalg.norm(ref[b], axis=-1)
+        worst = max(worst, float(err.max()))
+    assert worst <= TOL[wl.dtype], worst
+    return worst
+
+
+SMALL = [
+    ("tiny", {}),
+    ("llama8b", dict(prefix=300)),                                  # 4 row tiles x 3 key splits
+    ("llama8b", dict(prefix=(0, 0), n_nodes=64)),                   # no prefix: pure tree attention
+    ("ragged", dict(batch=4, prefix=(100, 700))),                   # paged, shuffled, ragged
+    ("chain", dict(batch=16, prefix=257)),                          # R = 12..32: VALU and MFMA rows
+    ("llama70b_share", dict(batch=1, prefix=500)),                  # 16 row tiles, N = 128
+    ("llama8b", dict(prefix=333, n_nodes=1)),                       # single node: decode attention
+    ("llama8b", dict(prefix=95, n_nodes=37, tree="star")),          # star tree, ragged row tile
+    ("llama8b", dict(prefix=40, n_nodes=128, tree="chain")),        # maximum depth
+    ("chain", dict(batch=5, prefix=17, n_nodes=(1, 3))),            # R = 4..12: every VALU row count
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
+def test_attention_small(name, kw):
+    wl = make_workload(name, seed=11, with_logits=False, **kw)
+    print(f"case {name} {kw} B={wl.batch} Nmax={wl.n_max}", flush=True)
+    out, st, _, _ = run_gpu(wl)
+    check_all_rows(wl, out, st)
+
+
+@pytest.mark.parametrize("dtype_cfg", ["tiny", "llama8b"])
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_attention_block_sizes(dtype_cfg, bs):
+    from tree_verification_amd import workloads as W
+    cfg = dict(W.CONFIGS[dtype_cfg])
+    W.CONFIGS["_bs"] = dict(cfg, block_size=bs, paged=True)
+    W.CONFIG_ORDER.append("_bs")
+    try:
+        wl = make_workload("_bs", seed=5, with_logits=False, prefix=(150, 420),
+                           n_nodes=20 if dtype_cfg == "llama8b" else 8, batch=3)
+    finally:
+        W.CONFIG_ORDER.remove("_bs")
+        del W.CONFIGS["_bs"]
+    out, st, _, _ = run_gpu(wl)
+    check_all_rows(wl, out, st)
+
+
+def custom(dtype, Hq, Hkv, D, n, P, B=2, seed=3, kind="capped"):
+    from tree_verification_amd import workloads as W
+    W.CONFIGS["_c"] = dict(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, dtype=dtype,
+                           prefix=P, n_nodes=n, tree=kind, width=3, depth=6, vocab=50,
+                           target_sd=1.0, draft_noise_sd=1.0, block_size=16, paged=True)
+    W.CONFIG_ORDER.append("_c")
+    try:
+        return make_workload("_c", seed=seed, with_logits=False)
+    finally:
+        W.CONFIG_ORDER.remove("_c")
+        del W.CONFIGS["_c"]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,n,P", [
+    ("bf16", 8, 2, 64, 30, (10, 300)),      # head_dim 64 on MFMA
+    ("bf16", 4, 4, 64, 10, (0, 64)),        # G = 1, R < 16: VALU bf16
+    ("f32", 8, 2, 128, 24, (50, 200)),      # fp32, R = 96: VALU over 6 row tiles
+    ("f32", 2, 1, 64, 100, (1, 33)),        # fp32, deep tree, short prefix
+    ("bf16", 16, 2, 128, 128, (3, 3)),      # R = 1024 with a 3-token prefix
+])
+def test_attention_shapes(dtype, Hq, Hkv, D, n, P):
+    wl = custom(dtype, Hq, Hkv, D, n, P)
+    out, st, _, _ = run_gpu(wl)
+    check_all_rows(wl, out, st)
+
+
+FULL = ["tiny", "llama8b", "ragged", "chain", "llama70b_share"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_attention_full_size_sampled(name):
+    """Configurations at full size (the benchmark's launch shape); 64 sampled rows."""
+    wl = make_workload(name, with_logits=False)
+    print(f"case full {name} B={wl.batch} Nmax={wl.n_max} P={wl.prefix_len[:4]}", flush=True)
+    out, st, _, _ = run_gpu(wl)
+    assert np.all(st == 0)
+    rng = np.random.default_rng(99)
+    rows = {}
+    for _ in range(64):
+        b = int(rng.integers(wl.batch))
+        u = int(rng.integers(int(wl.n_nodes[b])))
+        h = int(rng.integers(wl.n_q_heads))
+        rows.setdefault(b, []).append((u, h))
+    ref, _ = oracle(wl, requests=sorted(rows), rows=rows)
+    worst = 0.0
+    for b, lst in rows.items():
+        for u, h in lst:
+            r = ref[b][u, h]
+            e = np.linalg.norm(out[b, u, h] - r) / np.linalg.norm(r)
+            worst = max(worst, float(e))
+    assert worst <= TOL[wl.dtype], worst
+
+
+def test_attention_deterministic_and_workspace_reuse():
+    wl = make_workload("llama8b", seed=2, with_logits=False, prefix=700)
+    d = DevWorkload(wl, logits=False)
+    a, _ = tv.tree_attn_forward(d.q, d.k, d.v, d.table, d.prefix_len, d.n_nodes, d.parent)
+    b_, _ = tv.tree_attn_forward(d.q, d.k, d.v, d.table, d.prefix_len, d.n_nodes, d.parent)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b_)
+
+
+def test_attention_status_flags():
+    wl = make_workload("llama8b", seed=4, with_logits=False, batch=5, prefix=(40, 90), n_nodes=12)
+    wl.n_nodes[1] = 0                       # bad node count
+    wl.parent[2, 5] = 7                     # parent after child
+    wl.block_table[3, 1] = wl.num_blocks    # block outside the pool
+    wl.prefix_len[4] = wl.max_blocks * wl.block_size   # positions past the table
+    out, st, _, _ = run_gpu(wl)
+    ref, rst = oracle(wl)
+    assert list(st) == list(rst) == [0, tv.REQ_BAD_NNODES, tv.REQ_BAD_PARENT, tv.REQ_BAD_KV, tv.REQ_BAD_KV]
+    n = int(wl.n_nodes[0])
+    err = np.linalg.norm(out[0, :n] - ref[0], axis=-1) / np.linalg.norm(ref[0], axis=-1)
+    assert err.max() <= TOL["bf16"]
+
+
+def test_padding_rows_untouched():
+    wl = make_workload("chain", seed=8, with_logits=False, batch=6, prefix=64)
+    d = DevWorkload(wl, logits=False)
+    out = torch.full_like(d.q, 7.0)
+    tv.tree_attn_forward(d.q, d.k, d.v, d.table, d.prefix_len, d.n_nodes, d.parent, out=out)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    for b in range(wl.batch):
+        assert np.all(o[b, int(wl.n_nodes[b]):] == 7.0)

@@ -1,0 +1,202 @@
+"""GPU parity of greedy and stochastic tree verification against the oracle.
+
+Greedy: paths and emitted tokens bit-exact.  Stochastic: bit-exact unless the
+oracle's trace holds a decision whose uniform lies within 1e-6 of its
+threshold (p'/q for an accept test, a CDF boundary for the final draw).
+"""
+import numpy as np
+import pytest
+import torch
+
+from devdata import DevWorkload
+from oracle.verify import in_band, verify_greedy, verify_stochastic
+from tree_verification_amd import binding as tv
+from tree_verification_amd.workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def plant_greedy_matches(wl, rng, prob=0.8):
+    """Make the target argmax at many internal nodes equal one child's token, so
+    greedy paths run deep."""
+    for b in range(wl.batch):
+        n = int(wl.n_nodes[b])
+        for u in range(n):
+            kids = [c for c in range(1, n) if wl.parent[b, c] == u]
+            if kids and rng.random() < prob:
+                c = kids[int(rng.integers(len(kids)))]
+                row = wl.target_logits[b, u]
+                row[wl.tokens[b, c]] = row.max() + 1.0
+
+
+def gpu_greedy(d):
+    p, l, t, s = tv.tree_verify_greedy(d.target, d.tokens, d.parent, d.n_nodes)
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), l.cpu().numpy(), t.cpu().numpy(), s.cpu().numpy()
+
+
+def gpu_stoch(d, temperature=1.0):
+    p, l, t, s = tv.tree_verify_stochastic(d.target, d.draft, d.tokens, d.parent, d.n_nodes,
+                                           d.u_accept, d.u_sample, temperature=temperature)
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), l.cpu().numpy(), t.cpu().numpy(), s.cpu().numpy()
+
+
+def check_greedy(wl, d):
+    gp, gl, gt, gs = gpu_greedy(d)
+    paths, outs, st = verify_greedy(wl.target_logits, wl.tokens, wl.parent, wl.n_nodes, wl.n_max)
+    assert np.array_equal(gs, st)
+    depth = []
+    for b in range(wl.batch):
+        if st[b]:
+            assert gl[b] == 0
+            continue
+        L = int(gl[b])
+        assert list(gp[b, :L]) == paths[b], b
+        assert list(gt[b, :L]) == outs[b], b
+        depth.append(L)
+    return depth
+
+
+def check_stoch(wl, d, temperature=1.0):
+    gp, gl, gt, gs = gpu_stoch(d, temperature)
+    paths, outs, traces, st = verify_stochastic(wl.target_logits, wl.draft_logits, wl.tokens, wl.parent,
+                                                wl.n_nodes, wl.u_accept, wl.u_sample, wl.n_max,
+                                                temperature)
+    assert np.array_equal(gs, st)
+    lens, banded = [], 0
+    for b in range(wl.batch):
+        if st[b]:
+            assert gl[b] == 0
+            continue
+        L = int(gl[b])
+        same = list(gp[b, :L]) == paths[b] and list(gt[b, :L]) == outs[b]
+        if not same:
+            assert in_band(traces[b]), (b, list(gp[b, :L]), paths[b], list(gt[b, :L]), outs[b])
+            banded += 1
+        lens.append(L)
+    return lens, banded
+
+
+CASES = [
+    ("tiny", {}),
+    ("llama8b", dict(vocab=5003)),
+    ("llama8b", {}),                                   # full vocabulary, 64 nodes
+    ("ragged", dict(batch=6, prefix=(1, 2))),
+    ("chain", dict(batch=24, prefix=1, vocab=20011)),
+    ("llama70b_share", dict(batch=1, prefix=1)),       # 128 nodes, 128256 vocabulary
+    ("llama8b", dict(vocab=1001, n_nodes=40)),         # vocabulary not a multiple of 4
+    ("llama8b", dict(vocab=16389, n_nodes=50, tree="star")),   # wide node: many siblings
+    ("llama8b", dict(vocab=3000, n_nodes=1)),          # root only
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(CASES)])
+def test_greedy(name, kw):
+    wl = make_workload(name, seed=21, **kw)
+    print(f"case greedy {name} {kw}", flush=True)
+    plant_greedy_matches(wl, np.random.default_rng(1))
+    d = DevWorkload(wl)
+    depth = check_greedy(wl, d)
+    assert len(depth) == wl.batch
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(CASES)])
+def test_stochastic(name, kw):
+    wl = make_workload(name, seed=31, **kw)
+    print(f"case stochastic {name} {kw}", flush=True)
+    d = DevWorkload(wl)
+    lens, banded = check_stoch(wl, d)
+    assert banded <= 1
+
+
+@pytest.mark.parametrize("mode", ["aligned", "independent"])
+def test_stochastic_accept_and_reject_heavy(mode):
+    """aligned: draft ~ target (long accepted paths); independent: draft unrelated to
+    the target (almost every child rejected: many residual passes per node)."""
+    wl = make_workload("llama8b", seed=41, vocab=30011, n_nodes=48, batch=3)
+    rng = np.random.default_rng(5)
+    if mode == "aligned":
+        wl.draft_logits[:] = wl.target_logits + 0.05 * rng.standard_normal(wl.target_logits.shape).astype(np.float32)
+    else:
+        wl.draft_logits[:] = 3.0 * rng.standard_normal(wl.target_logits.shape).astype(np.float32)
+    # children drawn from the new draft rows keep the i.i.d. proposal precondition
+    from tree_verification_amd.workloads import gumbel_max_draw
+    for b in range(wl.batch):
+        for c in range(1, int(wl.n_nodes[b])):
+            wl.tokens[b, c] = gumbel_max_draw(rng, wl.draft_logits[b, wl.parent[b, c]], 1)[0]
+    d = DevWorkload(wl)
+    lens, banded = check_stoch(wl, d)
+    if mode == "aligned":
+        assert max(lens) >= 4
+
+
+def test_stochastic_temperature():
+    wl = make_workload("llama8b", seed=51, vocab=7001, n_nodes=30, batch=2)
+    d = DevWorkload(wl)
+    check_stoch(wl, d, temperature=0.7)
+    check_stoch(wl, d, temperature=1.9)
+
+
+def test_duplicate_sibling_tokens():
+    wl = make_workload("llama8b", seed=61, vocab=500, n_nodes=30, batch=4, tree="star")
+    for b in range(wl.batch):
+        wl.tokens[b, 2:] = wl.tokens[b, 1]          # every sibling proposes the same token
+    plant_greedy_matches(wl, np.random.default_rng(2), prob=1.0)
+    d = DevWorkload(wl)
+    check_greedy(wl, d)
+    check_stoch(wl, d)
+
+
+def test_status_flags():
+    wl = make_workload("llama8b", seed=71, vocab=2003, n_nodes=10, batch=7)
+    wl.n_nodes[1] = 0
+    wl.n_nodes[2] = wl.n_max + 1
+    wl.parent[3, 4] = 4
+    wl.target_logits[4, 3, 17] = np.nan
+    leaf = [u for u in range(10) if not np.any(wl.parent[5, :10] == u)][0]
+    wl.draft_logits[5, leaf, 3] = np.inf          # a leaf's draft row is never read
+    wl.tokens[6, 1] = wl.vocab                    # token outside the vocabulary
+    d = DevWorkload(wl)
+    _, gl, _, gs = gpu_greedy(d)
+    _, _, gst = verify_greedy(wl.target_logits, wl.tokens, wl.parent, wl.n_nodes, wl.n_max)
+    assert list(gs) == list(gst) == [0, 2, 2, 1, 8, 0, 0]
+    _, sl, _, ss = gpu_stoch(d)
+    _, _, _, sst = verify_stochastic(wl.target_logits, wl.draft_logits, wl.tokens, wl.parent, wl.n_nodes,
+                                     wl.u_accept, wl.u_sample, wl.n_max)
+    assert list(ss) == list(sst) == [0, 2, 2, 1, 8, 0, 16]
+    assert gl[1] == gl[2] == gl[3] == gl[4] == 0 and sl[6] == 0
+
+
+def test_decisions_just_outside_the_band():
+    """Uniforms placed 3e-6 on either side of the oracle's accept thresholds: the
+    GPU must take the oracle's decision (its p/q error must stay well below 1e-6)."""
+    wl = make_workload("llama8b", seed=81, vocab=128256, n_nodes=24, batch=2)
+    d0 = DevWorkload(wl)
+    _, _, traces, _ = verify_stochastic(wl.target_logits, wl.draft_logits, wl.tokens, wl.parent,
+                                        wl.n_nodes, wl.u_accept, wl.u_sample, wl.n_max)
+    moved = 0
+    for b in range(wl.batch):
+        for rec in traces[b]:
+            if rec[0] == "accept" and 1e-3 < rec[4] < 1 - 1e-3:
+                c = rec[2]
+                side = 3e-6 if (moved % 2) else -3e-6
+                wl.u_accept[b, c] = np.float32(rec[4] + side)
+                moved += 1
+    d = DevWorkload(wl)
+    lens, banded = check_stoch(wl, d)
+    assert banded == 0
+    del d0
+
+
+def test_repeat_calls_identical():
+    wl = make_workload("ragged", seed=91, batch=4, prefix=(1, 2), vocab=9001)
+    d = DevWorkload(wl)
+    a = gpu_stoch(d)
+    b = gpu_stoch(d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    a = gpu_greedy(d)
+    b = gpu_greedy(d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

@@ -1,0 +1,109 @@
+"""The C library loads, exports every function include/tree_verify.h declares, and
+rejects malformed descriptors on the host (no GPU needed: these calls return before
+any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_verification_amd import binding as tv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tv.LIB_PATH):
+        from tree_verification_amd import build
+        build.build()
+    return tv.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{}]*\)\s*;", src)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("tree_attn_forward", "tree_verify_greedy", "tree_verify_stochastic", "kv_compact_accepted"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the binding's signature table covers them
+    assert set(names) <= set(tv._SIGS)
+
+
+def test_status_strings(lib):
+    assert lib.tv_status_string(0) == b"TV_OK"
+    assert lib.tv_status_string(-1) == b"TV_ERR_INVALID_ARG"
+    assert lib.tv_status_string(-2) == b"TV_ERR_UNSUPPORTED"
+    assert lib.tv_status_string(-3) == b"TV_ERR_WORKSPACE"
+    assert lib.tv_status_string(-4) == b"TV_ERR_HIP"
+
+
+def good_attn_desc():
+    d = tv.AttnDesc()
+    d.batch, d.n_max, d.n_q_heads, d.n_kv_heads = 1, 8, 4, 2
+    d.head_dim, d.block_size, d.max_blocks_per_seq, d.num_blocks = 64, 16, 4, 4
+    d.dtype, d.sm_scale = tv.TV_BF16, 0.0
+    return d
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, -2), ("n_max", 0, -2), ("n_max", 129, -2), ("block_size", 24, -2),
+    ("dtype", 7, -2), ("n_kv_heads", 3, -1), ("batch", -1, -1), ("num_blocks", 0, -1),
+])
+def test_attention_rejects_bad_descriptors(lib, field, value, code):
+    d = good_attn_desc()
+    setattr(d, field, value)
+    rc = lib.tree_attn_forward(ctypes.byref(d), *([None] * 10), 0, None)
+    assert rc == code
+
+
+def test_null_descriptors(lib):
+    assert lib.tree_attn_forward(None, *([None] * 10), 0, None) == -1
+    assert lib.tree_verify_greedy(None, *([None] * 9), 0, None) == -1
+    assert lib.tree_verify_stochastic(None, *([None] * 12), 0, None) == -1
+    assert lib.kv_compact_accepted(None, *([None] * 10)) == -1
+    assert lib.tree_attn_workspace_size(None) == 0
+    assert lib.tree_verify_workspace_size(None) == 0
+
+
+def test_empty_batch_is_a_no_op(lib):
+    d = good_attn_desc()
+    d.batch = 0
+    assert lib.tree_attn_forward(ctypes.byref(d), *([None] * 10), 0, None) == 0
+    assert lib.kv_compact_accepted(ctypes.byref(d), *([None] * 10)) == 0
+    v = tv.VerifyDesc()
+    v.batch, v.n_max, v.vocab, v.temperature = 0, 4, 10, 1.0
+    assert lib.tree_verify_greedy(ctypes.byref(v), *([None] * 9), 0, None) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("vocab", 0, -1), ("n_max", 200, -2), ("temperature", 0.0, -1), ("temperature", -1.0, -1),
+])
+def test_verify_rejects_bad_descriptors(lib, field, value, code):
+    v = tv.VerifyDesc()
+    v.batch, v.n_max, v.vocab, v.temperature = 2, 4, 10, 1.0
+    setattr(v, field, value)
+    assert lib.tree_verify_greedy(ctypes.byref(v), *([None] * 9), 0, None) == code
+    assert lib.tree_verify_stochastic(ctypes.byref(v), *([None] * 12), 0, None) == code
+
+
+def test_missing_pointers_rejected(lib):
+    d = good_attn_desc()
+    assert lib.tree_attn_forward(ctypes.byref(d), *([None] * 10), 0, None) == -1
+    v = tv.VerifyDesc()
+    v.batch, v.n_max, v.vocab, v.temperature = 2, 4, 10, 1.0
+    assert lib.tree_verify_greedy(ctypes.byref(v), *([None] * 9), 0, None) == -1

@@ -1,0 +1,302 @@
+"""ctypes binding of libtreeverify.so: argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks their
+shapes/dtypes, passes raw device pointers plus torch's current HIP stream to
+the C interface (include/tree_verify.h) and returns the output tensors.  All
+computation happens in the library's kernels; there is no fallback path: if
+the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtreeverify.so")
+
+TV_F32, TV_BF16 = 0, 1
+
+# per-request status flags (include/tree_verify.h)
+REQ_BAD_PARENT = 1
+REQ_BAD_NNODES = 2
+REQ_BAD_KV = 4
+REQ_NONFINITE = 8
+REQ_BAD_TOKEN = 16
+REQ_BAD_PATH = 32
+REQ_TIMEOUT = 64
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_max", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+
+class VerifyDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_max", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("temperature", ctypes.c_float)]
+
+
+class TreeVerifyError(RuntimeError):
+    pass
+
+
+_P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "tree_attn_workspace_size": (_SZ, [ctypes.POINTER(AttnDesc)]),
+    "tree_attn_forward": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 10 + [_SZ, _P]),
+    "tree_verify_workspace_size": (_SZ, [ctypes.POINTER(VerifyDesc)]),
+    "tree_verify_greedy": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 9 + [_SZ, _P]),
+    "tree_verify_stochastic": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 12 + [_SZ, _P]),
+    "kv_compact_accepted": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 10),
+    "tv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and return the C library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise TreeVerifyError(f"{p} is missing: build it with `python -m tree_verification_amd.build`")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        msg = load_library().tv_status_string(rc).decode()
+        raise TreeVerifyError(f"{name} returned {rc} ({msg})")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+# Workspaces: a workspace belongs to the descriptor it was sized for (its
+# counters sit at descriptor-dependent offsets).  Each (device, stream, kind,
+# descriptor) gets its own buffer, zero-filled once; every call leaves its
+# counters at zero again.
+_ws: dict = {}
+
+
+def _desc_key(desc) -> tuple:
+    return tuple(getattr(desc, f) for f, _ in desc._fields_)
+
+
+def workspace(nbytes: int, device: torch.device, kind: str, desc=None) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream, kind,
+           None if desc is None else _desc_key(desc))
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws[key] = buf
+    return buf
+
+
+def attn_desc(q, k_cache, block_table, n_kv_heads=None, sm_scale=None) -> AttnDesc:
+    B, n_max, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    d = AttnDesc()
+    d.batch, d.n_max, d.n_q_heads, d.n_kv_heads = B, n_max, Hq, Hkv
+    d.head_dim, d.block_size = D, bs
+    d.max_blocks_per_seq = block_table.shape[1]
+    d.num_blocks = nb
+    d.dtype = TV_BF16 if q.dtype == torch.bfloat16 else TV_F32
+    d.sm_scale = 0.0 if sm_scale is None else float(sm_scale)
+    return d
+
+
+def tree_attn_forward(q, k_cache, v_cache, block_table, prefix_len, n_nodes, parent, *,
+                      sm_scale=None, out=None, status=None, ws=None):
+    """Tree attention (include/tree_verify.h).  Shapes:
+    q [B, n_max, Hq, D]; k_cache [num_blocks, Hkv, bs, D]; v_cache [num_blocks, Hkv, D, bs];
+    block_table [B, max_blocks] int32; prefix_len, n_nodes [B] int32; parent [B, n_max] int32.
+    Returns (out [B, n_max, Hq, D], status [B] int32)."""
+    lib = load_library()
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("q must be float32 or bfloat16")
+    dev = q.device
+    B, n_max, Hq, D = q.shape
+    _need(q, "q", q.dtype)
+    _need(k_cache, "k_cache", q.dtype, device=dev)
+    nb, Hkv, bs, _ = k_cache.shape
+    _need(v_cache, "v_cache", q.dtype, (nb, Hkv, D, bs), dev)
+    if k_cache.shape[3] != D:
+        raise ValueError("k_cache head_dim differs from q")
+    _need(block_table, "block_table", torch.int32, device=dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _need(prefix_len, "prefix_len", torch.int32, (B,), dev)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    _need(parent, "parent", torch.int32, (B, n_max), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, tuple(q.shape), dev)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(status, "status", torch.int32, (B,), dev)
+    desc = attn_desc(q, k_cache, block_table, sm_scale=sm_scale)
+    need = lib.tree_attn_workspace_size(ctypes.byref(desc))
+    if ws is None:
+        ws = workspace(need, dev, "attn", desc)
+    nbytes = 0 if ws is None else ws.numel()
+    rc = lib.tree_attn_forward(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_table), _ptr(prefix_len), _ptr(n_nodes), _ptr(parent),
+                               _ptr(out), _ptr(status), _ptr(ws), nbytes, _stream(dev))
+    _check(rc, "tree_attn_forward")
+    return out, status
+
+
+def _verify_outputs(B, n_max, dev, path, path_len, out_tokens, status):
+    if path is None:
+        path = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(path, "path", torch.int32, (B, n_max), dev)
+    _need(path_len, "path_len", torch.int32, (B,), dev)
+    _need(out_tokens, "out_tokens", torch.int32, (B, n_max), dev)
+    _need(status, "status", torch.int32, (B,), dev)
+    return path, path_len, out_tokens, status
+
+
+def verify_desc(target_logits, temperature=1.0) -> VerifyDesc:
+    B, n_max, V = target_logits.shape
+    d = VerifyDesc()
+    d.batch, d.n_max, d.vocab, d.temperature = B, n_max, V, float(temperature)
+    return d
+
+
+def tree_verify_greedy(target_logits, tokens, parent, n_nodes, *, path=None, path_len=None,
+                       out_tokens=None, status=None, ws=None):
+    """Greedy tree verification.  target_logits [B, n_max, V] float32; tokens, parent
+    [B, n_max] int32; n_nodes [B] int32.  Returns (path, path_len, out_tokens, status)."""
+    lib = load_library()
+    dev = target_logits.device
+    B, n_max, V = target_logits.shape
+    _need(target_logits, "target_logits", torch.float32)
+    _need(tokens, "tokens", torch.int32, (B, n_max), dev)
+    _need(parent, "parent", torch.int32, (B, n_max), dev)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    path, path_len, out_tokens, status = _verify_outputs(B, n_max, dev, path, path_len, out_tokens, status)
+    desc = verify_desc(target_logits)
+    need = lib.tree_verify_workspace_size(ctypes.byref(desc))
+    if ws is None:
+        ws = workspace(need, dev, "greedy", desc)
+    rc = lib.tree_verify_greedy(ctypes.byref(desc), _ptr(target_logits), _ptr(tokens), _ptr(parent),
+                                _ptr(n_nodes), _ptr(path), _ptr(path_len), _ptr(out_tokens),
+                                _ptr(status), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(rc, "tree_verify_greedy")
+    return path, path_len, out_tokens, status
+
+
+def tree_verify_stochastic(target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, *,
+                           temperature=1.0, path=None, path_len=None, out_tokens=None, status=None,
+                           ws=None):
+    """Stochastic tree verification.  target/draft logits [B, n_max, V] float32; tokens,
+    parent [B, n_max] int32; n_nodes [B] int32; u_accept, u_sample [B, n_max] float32.
+    Returns (path, path_len, out_tokens, status)."""
+    lib = load_library()
+    dev = target_logits.device
+    B, n_max, V = target_logits.shape
+    _need(target_logits, "target_logits", torch.float32)
+    _need(draft_logits, "draft_logits", torch.float32, (B, n_max, V), dev)
+    _need(tokens, "tokens", torch.int32, (B, n_max), dev)
+    _need(parent, "parent", torch.int32, (B, n_max), dev)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, n_max), dev)
+    _need(u_sample, "u_sample", torch.float32, (B, n_max), dev)
+    path, path_len, out_tokens, status = _verify_outputs(B, n_max, dev, path, path_len, out_tokens, status)
+    desc = verify_desc(target_logits, temperature)
+    need = lib.tree_verify_workspace_size(ctypes.byref(desc))
+    if ws is None:
+        ws = workspace(need, dev, "stochastic", desc)
+    rc = lib.tree_verify_stochastic(ctypes.byref(desc), _ptr(target_logits), _ptr(draft_logits),
+                                    _ptr(tokens), _ptr(parent), _ptr(n_nodes), _ptr(u_accept),
+                                    _ptr(u_sample), _ptr(path), _ptr(path_len), _ptr(out_tokens),
+                                    _ptr(status), _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(dev))
+    _check(rc, "tree_verify_stochastic")
+    return path, path_len, out_tokens, status
+
+
+def kv_compact_accepted(k_cache, v_cache, block_table, prefix_len, path, path_len, *, src_pos=None,
+                        new_len=None, status=None):
+    """In-place accepted-path KV compaction.  Returns (src_pos [B, n_max], new_len [B], status [B])."""
+    lib = load_library()
+    dev = k_cache.device
+    if k_cache.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("caches must be float32 or bfloat16")
+    nb, Hkv, bs, D = k_cache.shape
+    _need(k_cache, "k_cache", k_cache.dtype)
+    _need(v_cache, "v_cache", k_cache.dtype, (nb, Hkv, D, bs), dev)
+    B, n_max = path.shape
+    _need(block_table, "block_table", torch.int32, device=dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _need(prefix_len, "prefix_len", torch.int32, (B,), dev)
+    _need(path, "path", torch.int32, (B, n_max), dev)
+    _need(path_len, "path_len", torch.int32, (B,), dev)
+    if src_pos is None:
+        src_pos = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    if new_len is None:
+        new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(src_pos, "src_pos", torch.int32, (B, n_max), dev)
+    _need(new_len, "new_len", torch.int32, (B,), dev)
+    _need(status, "status", torch.int32, (B,), dev)
+    d = AttnDesc()
+    d.batch, d.n_max, d.n_q_heads, d.n_kv_heads = B, n_max, Hkv, Hkv
+    d.head_dim, d.block_size = D, bs
+    d.max_blocks_per_seq, d.num_blocks = block_table.shape[1], nb
+    d.dtype = TV_BF16 if k_cache.dtype == torch.bfloat16 else TV_F32
+    d.sm_scale = 0.0
+    rc = lib.kv_compact_accepted(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                 _ptr(prefix_len), _ptr(path), _ptr(path_len), _ptr(src_pos),
+                                 _ptr(new_len), _ptr(status), _stream(dev))
+    _check(rc, "kv_compact_accepted")
+    return src_pos, new_len, status
