@@ -145,7 +145,8 @@ int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
  * whose cumulative p' exceeds u_sample[b][u] * sum(p').
  *   draft_logits [B][n_max][V] float32: only rows of nodes that have children are read.
  *   u_accept, u_sample [B][n_max] float32 uniforms in [0, 1), supplied by the caller.
- * Decisions use float32 exponentials with float64 sums and a float64 accept test. */
+ * Decisions use float32 exponentials with float64 sums and a float64 accept test.
+ * Supports vocab <= 524288 (TV_ERR_UNSUPPORTED beyond). */
 int tree_verify_stochastic(const tv_verify_desc* desc, const float* target_logits,
                            const float* draft_logits, const int32_t* tokens,
                            const int32_t* parent, const int32_t* n_nodes, const float* u_accept,

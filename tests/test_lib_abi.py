@@ -107,3 +107,10 @@ def test_missing_pointers_rejected(lib):
     v = tv.VerifyDesc()
     v.batch, v.n_max, v.vocab, v.temperature = 2, 4, 10, 1.0
     assert lib.tree_verify_greedy(ctypes.byref(v), *([None] * 9), 0, None) == -1
+
+
+def test_stochastic_vocabulary_limit(lib):
+    v = tv.VerifyDesc()
+    v.batch, v.n_max, v.vocab, v.temperature = 1, 4, 64 * 8192 + 1, 1.0
+    dummy = ctypes.c_void_p(4096)   # never dereferenced: the call fails before any launch
+    assert lib.tree_verify_stochastic(ctypes.byref(v), *([dummy] * 12), 0, None) == -2

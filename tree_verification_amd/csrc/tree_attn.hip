@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxNodes = 128;
+constexpr int kMaxSplits = 32;   // key splits per (request, KV head, row tile)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -134,7 +135,7 @@ struct AttnSmem {
   float wl[4][RPT];
   // VALU path scratch
   float qs[16][D];
-  float sc[4][16][64];          // per-wave probability strips
+  float sc[4][16][64];          // per-wave probability strips; split weights of the merge later
   int flag;
 };
 
@@ -565,39 +566,34 @@ __device__ void emit(const AttnParams& p, AttnSmem<RPT, D>& sm, int tile, int sp
   }
   __syncthreads();
   if (!sm.flag) return;
+  // acquire: the agent-scope fence invalidates this CU's L1 and the stale lines
+  // of this XCD's L2, so the plain loads below see the other splits' partials
   __threadfence();
   // last arrival: log-sum-exp merge of the n_active partials of this tile
-  size_t base = (size_t)tile * p.splits * RPT;
+  const size_t base = (size_t)tile * p.splits * RPT;
+  static_assert(kMaxSplits * RPT <= 4 * 16 * 64, "split weights must fit the scratch strips");
+  float(*wgt)[RPT] = reinterpret_cast<float(*)[RPT]>(&sm.sc[0][0][0]);
   if (t < rows) {
     float M = kNegInf;
-    for (int s = 0; s < n_active; ++s)
-      M = fmaxf(M, __hip_atomic_load(&p.part_ml[(base + (size_t)s * RPT + t) * 2], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT));
+    for (int s = 0; s < n_active; ++s) M = fmaxf(M, p.part_ml[(base + (size_t)s * RPT + t) * 2]);
     float L = 0.f;
     for (int s = 0; s < n_active; ++s) {
-      float ms = __hip_atomic_load(&p.part_ml[(base + (size_t)s * RPT + t) * 2], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-      float ls = __hip_atomic_load(&p.part_ml[(base + (size_t)s * RPT + t) * 2 + 1], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-      L += (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ls;
+      const float2 ml = *(const float2*)&p.part_ml[(base + (size_t)s * RPT + t) * 2];
+      const float w = (ml.x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+      L += w * ml.y;
+      wgt[s][t] = w;
     }
-    sm.m[t] = M;
     sm.l[t] = L;
   }
   __syncthreads();
   for (int idx = t; idx < rows * (D / 4); idx += kThreads) {
-    int r = idx / (D / 4), d = 4 * (idx % (D / 4));
-    float M = sm.m[r];
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const int r = idx / (D / 4), d = 4 * (idx % (D / 4));
+    tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < n_active; ++s) {
-      size_t pr = base + (size_t)s * RPT + r;
-      float ms = __hip_atomic_load(&p.part_ml[pr * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      float w = (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i] += w * __hip_atomic_load(&p.part_o[pr * D + d + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const size_t pr = base + (size_t)s * RPT + r;
+      acc += wgt[s][r] * *(const tv_f32x4*)&p.part_o[pr * D + d];
     }
-    float inv = 1.f / sm.l[r];
+    const float inv = 1.f / sm.l[r];
     float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
     store_out4<kBF16, D>(p, b, g, r0 + r, d, v4);
   }
@@ -695,19 +691,26 @@ int check_desc(const tv_attn_desc* d) {
   return TV_OK;
 }
 
-int make_plan(const tv_attn_desc* d, int cu, AttnPlan* pl) {
+// MFMA row tile: 16 * NT query rows per workgroup (bf16 only).
+int choose_nt(const tv_attn_desc* d) {
+  const long long Rmax = (long long)d->n_max * (d->n_q_heads / d->n_kv_heads);
+  if (d->dtype != TV_BF16) return 1;
+  return Rmax >= 64 ? 4 : (Rmax >= 32 ? 2 : 1);
+}
+
+int make_plan(const tv_attn_desc* d, int cu, int wg_per_cu, AttnPlan* pl) {
   const int G = d->n_q_heads / d->n_kv_heads;
   const long long Rmax = (long long)d->n_max * G;
-  int nt = 1;
-  if (d->dtype == TV_BF16) nt = Rmax >= 64 ? 4 : (Rmax >= 32 ? 2 : 1);
+  const int nt = choose_nt(d);
   pl->nt = nt;
   pl->rows_per_tile = d->dtype == TV_BF16 ? 16 * nt : 16;
   pl->row_tiles = (int)((Rmax + pl->rows_per_tile - 1) / pl->rows_per_tile);
   const long long max_keys = (long long)d->max_blocks_per_seq * d->block_size;
   const long long base = (long long)d->batch * d->n_kv_heads * pl->row_tiles;
-  long long target = 2LL * cu;
+  long long target = (long long)wg_per_cu * cu;
   long long splits = base > 0 ? (target + base - 1) / base : 1;
   long long max_splits = (max_keys + 127) / 128;
+  if (max_splits > kMaxSplits) max_splits = kMaxSplits;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   long long kps = (max_keys + splits - 1) / splits;
@@ -731,20 +734,65 @@ int make_plan(const tv_attn_desc* d, int cu, AttnPlan* pl) {
   return TV_OK;
 }
 
-template <bool kBF16, int D, int NT>
-hipError_t launch(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((tree_attn_kernel<kBF16, D, NT>), dim3(p.total), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+typedef void (*AttnKernel)(AttnParams);
+
+AttnKernel pick_kernel(const tv_attn_desc* d, int nt) {
+  const bool bf = d->dtype == TV_BF16;
+  if (d->head_dim == 128) {
+    if (!bf) return tree_attn_kernel<false, 128, 1>;
+    return nt == 4 ? tree_attn_kernel<true, 128, 4> : nt == 2 ? tree_attn_kernel<true, 128, 2> : tree_attn_kernel<true, 128, 1>;
+  }
+  if (!bf) return tree_attn_kernel<false, 64, 1>;
+  return nt == 4 ? tree_attn_kernel<true, 64, 4> : nt == 2 ? tree_attn_kernel<true, 64, 2> : tree_attn_kernel<true, 64, 1>;
+}
+
+// Resident workgroups per CU of one kernel instance on the current device (cached).
+int occupancy(AttnKernel k, int* out) {
+  static std::mutex mu;
+  static const void* keys[16];
+  static int vals[16];
+  static int dev_of[16];
+  static int n = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (keys[i] == (const void*)k && dev_of[i] == dev) {
+      *out = vals[i];
+      return TV_OK;
+    }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, kThreads, 0) != hipSuccess) return TV_ERR_HIP;
+  if (nb < 1) nb = 1;
+  if (n < 16) {
+    keys[n] = (const void*)k;
+    vals[n] = nb;
+    dev_of[n] = dev;
+    ++n;
+  }
+  *out = nb;
+  return TV_OK;
+}
+
+int plan_for(const tv_attn_desc* d, AttnPlan* pl, AttnKernel* kern) {
+  int cu = 0, occ = 0;
+  int rc = tv_device_cu_count(&cu);
+  if (rc != TV_OK) return rc;
+  const int nt = choose_nt(d);
+  AttnKernel k = pick_kernel(d, nt);
+  rc = occupancy(k, &occ);
+  if (rc != TV_OK) return rc;
+  rc = make_plan(d, cu, occ, pl);
+  if (kern) *kern = k;
+  return rc;
 }
 
 }  // namespace
 
 extern "C" size_t tree_attn_workspace_size(const tv_attn_desc* desc) {
   if (check_desc(desc) != TV_OK) return 0;
-  int cu = 0;
-  if (tv_device_cu_count(&cu) != TV_OK) return 0;
   AttnPlan pl;
-  if (make_plan(desc, cu, &pl) != TV_OK) return 0;
+  if (plan_for(desc, &pl, nullptr) != TV_OK) return 0;
   return pl.bytes;
 }
 
@@ -758,11 +806,11 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   if (desc->batch == 0) return TV_OK;
   if (!q || !k_cache || !v_cache || !block_table || !prefix_len || !n_nodes || !parent || !out)
     return TV_ERR_INVALID_ARG;
-  int cu = 0;
-  rc = tv_device_cu_count(&cu);
-  if (rc != TV_OK) return rc;
+  if ((((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15) != 0)
+    return TV_ERR_INVALID_ARG;   // 16-byte vector loads and stores
   AttnPlan pl;
-  rc = make_plan(desc, cu, &pl);
+  AttnKernel kern = nullptr;
+  rc = plan_for(desc, &pl, &kern);
   if (rc != TV_OK) return rc;
   if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return TV_ERR_WORKSPACE;
 
@@ -798,18 +846,6 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   if (total > 0x7fffffff) return TV_ERR_UNSUPPORTED;
   p.total = (int)total;
 
-  hipError_t e;
-  const bool bf = desc->dtype == TV_BF16;
-  if (desc->head_dim == 128) {
-    if (!bf) e = launch<false, 128, 1>(p, stream);
-    else if (pl.nt == 4) e = launch<true, 128, 4>(p, stream);
-    else if (pl.nt == 2) e = launch<true, 128, 2>(p, stream);
-    else e = launch<true, 128, 1>(p, stream);
-  } else {
-    if (!bf) e = launch<false, 64, 1>(p, stream);
-    else if (pl.nt == 4) e = launch<true, 64, 4>(p, stream);
-    else if (pl.nt == 2) e = launch<true, 64, 2>(p, stream);
-    else e = launch<true, 64, 1>(p, stream);
-  }
-  return e == hipSuccess ? TV_OK : TV_ERR_HIP;
+  hipLaunchKernelGGL(kern, dim3(p.total), dim3(kThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }

@@ -35,6 +35,7 @@ constexpr int kTileElems = kVThreads * 16;     // 8192 logits per tile (16 per t
 constexpr int kGreedyThreads = 256;
 constexpr int kGreedyChunk = kGreedyThreads * 32;
 constexpr int kMaxNodes = 128;
+constexpr int kMaxTiles = 64;                  // vocabulary up to 64 * 8192 = 524288
 constexpr long long kSpinLimit = 1LL << 22;   // bounded waits: ~0.5 s worst case, then TV_REQ_TIMEOUT
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -205,9 +206,9 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_kernel(GreedyParams p) 
     int bi = 0x7fffffff, bb = 0;
     for (int cc = 0; cc < p.chunks; ++cc) {
       size_t slot = ((size_t)b * p.n_max + v) * p.chunks + cc;
-      float cv = __hip_atomic_load(&p.part_val[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int ci = __hip_atomic_load(&p.part_idx[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bb |= __hip_atomic_load(&p.part_bad[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      float cv = p.part_val[slot];
+      int ci = p.part_idx[slot];
+      bb |= p.part_bad[slot];
       if (cv > bv) {   // chunks in ascending order: the first chunk wins ties
         bv = cv;
         bi = ci;
@@ -283,11 +284,18 @@ struct StochParams {
 };
 
 struct StochSmem {
+  float tm[2][kMaxTiles];     // tile maxima (target, draft) staged from the workspace
+  double ts[2][kMaxTiles];    // tile exp-sums
+  double tf[kMaxTiles];       // tile residual masses of the latest pass
+  double tcur[kMaxTiles];     // tile masses of the current residual
   double red_d[kVThreads / 64];
   float red_f[kVThreads / 64];
   int red_i[kVThreads / 64];
   double scan[kVThreads / 64];
   int kids[kMaxNodes];
+  int facc[kMaxNodes];        // request finalisation: accepted child and final token per node
+  int ffin[kMaxNodes];
+  int fflags;
   int nkids;
   int timeout;
   int sel;
@@ -300,7 +308,10 @@ struct StochSmem {
 // Bounded: on expiry the request is flagged TV_REQ_TIMEOUT and the workgroup
 // carries on (all later reads stay in bounds).
 __device__ void team_barrier(const StochParams& p, StochSmem& sm, int k, int phase) {
-  if (p.S == 1) return;
+  if (p.S == 1) {
+    __syncthreads();
+    return;
+  }
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -317,16 +328,6 @@ __device__ void team_barrier(const StochParams& p, StochSmem& sm, int k, int pha
     __threadfence();
   }
   __syncthreads();
-}
-
-__device__ __forceinline__ double ld_d(const double* a) {
-  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_f(const float* a) {
-  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_i(const int* a) {
-  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Row statistics of one tile: max, then sum of expf((z - max) * invT) in float64.
@@ -433,20 +434,26 @@ __global__ __launch_bounds__(kVThreads) void stochastic_kernel(StochParams p) {
     if (block_or<kVThreads>(bad, sm.red_i) && t == 0) atomicOr(&p.node_flags[k], TV_REQ_NONFINITE);
     int phase = 1;
     team_barrier(p, sm, k, phase++);
+    // stage every member's tile statistics into LDS (one parallel round trip)
+    for (int i = t; i < 2 * p.tiles; i += kVThreads) {
+      const int r = i / p.tiles, tl = i % p.tiles;
+      if (r == 0 || nk > 0) {
+        sm.tm[r][tl] = p.tile_m[((size_t)k * 2 + r) * p.tiles + tl];
+        sm.ts[r][tl] = p.tile_s[((size_t)k * 2 + r) * p.tiles + tl];
+      }
+    }
+    __syncthreads();
 
     // row maxima and normalisers (every member, same order -> same values)
     float Mp = kNegInf, Mq = kNegInf;
     for (int tl = 0; tl < p.tiles; ++tl) {
-      Mp = fmaxf(Mp, ld_f(&p.tile_m[((size_t)k * 2) * p.tiles + tl]));
-      if (nk > 0) Mq = fmaxf(Mq, ld_f(&p.tile_m[((size_t)k * 2 + 1) * p.tiles + tl]));
+      Mp = fmaxf(Mp, sm.tm[0][tl]);
+      if (nk > 0) Mq = fmaxf(Mq, sm.tm[1][tl]);
     }
     double Sp = 0.0, Sq = 0.0;
     for (int tl = 0; tl < p.tiles; ++tl) {
-      Sp += ld_d(&p.tile_s[((size_t)k * 2) * p.tiles + tl]) *
-            exp((double)(ld_f(&p.tile_m[((size_t)k * 2) * p.tiles + tl]) - Mp) * p.invT_d);
-      if (nk > 0)
-        Sq += ld_d(&p.tile_s[((size_t)k * 2 + 1) * p.tiles + tl]) *
-              exp((double)(ld_f(&p.tile_m[((size_t)k * 2 + 1) * p.tiles + tl]) - Mq) * p.invT_d);
+      Sp += sm.ts[0][tl] * exp((double)(sm.tm[0][tl] - Mp) * p.invT_d);
+      if (nk > 0) Sq += sm.ts[1][tl] * exp((double)(sm.tm[1][tl] - Mq) * p.invT_d);
     }
     const double ip = 1.0 / Sp, iq = nk > 0 ? 1.0 / Sq : 0.0;
     const double lse_p = (double)Mp * p.invT_d + log(Sp);
@@ -481,8 +488,10 @@ __global__ __launch_bounds__(kVThreads) void stochastic_kernel(StochParams p) {
         if (t == 0) p.tile_f[((size_t)k * 3 + buf) * p.tiles + tl] = s;
       }
       team_barrier(p, sm, k, phase++);
+      for (int i = t; i < p.tiles; i += kVThreads) sm.tf[i] = p.tile_f[((size_t)k * 3 + buf) * p.tiles + i];
+      __syncthreads();
       double F = 0.0;
-      for (int tl = 0; tl < p.tiles; ++tl) F += ld_d(&p.tile_f[((size_t)k * 3 + buf) * p.tiles + tl]);
+      for (int tl = 0; tl < p.tiles; ++tl) F += sm.tf[tl];
       // Z > 0: move to the new residual.  The next pass writes a buffer that is
       // neither the one just summed (a slower member may still be reading it)
       // nor the one holding the current residual's tile masses.
@@ -491,6 +500,8 @@ __global__ __launch_bounds__(kVThreads) void stochastic_kernel(StochParams p) {
         Cres = cn;
         Dres = F;
         cur_buf = buf;
+        __syncthreads();
+        for (int i = t; i < p.tiles; i += kVThreads) sm.tcur[i] = sm.tf[i];
       }
       buf = 0;
       while (buf == just || buf == cur_buf) ++buf;
@@ -500,23 +511,20 @@ __global__ __launch_bounds__(kVThreads) void stochastic_kernel(StochParams p) {
     int result_tok = -1;
     if (accepted < 0 && !(flags & TV_REQ_BAD_TOKEN)) {
       // two-level inverse CDF: tile masses, then a scan inside the selected tile
+      __syncthreads();
       const double us = (double)p.u_sample[(size_t)b * p.n_max + u];
       double total = 0.0;
       for (int tl = 0; tl < p.tiles; ++tl) {
-        double mass = (cur_buf < 0)
-                          ? ld_d(&p.tile_s[((size_t)k * 2) * p.tiles + tl]) *
-                                exp((double)(ld_f(&p.tile_m[((size_t)k * 2) * p.tiles + tl]) - Mp) * p.invT_d) * ip
-                          : ld_d(&p.tile_f[((size_t)k * 3 + cur_buf) * p.tiles + tl]);
+        double mass = (cur_buf < 0) ? sm.ts[0][tl] * exp((double)(sm.tm[0][tl] - Mp) * p.invT_d) * ip
+                                    : sm.tcur[tl];
         total += mass;
       }
       const double thr = us * total;
       double cum = 0.0, base = 0.0;
       int sel = -1, lastpos = 0;
       for (int tl = 0; tl < p.tiles; ++tl) {
-        double mass = (cur_buf < 0)
-                          ? ld_d(&p.tile_s[((size_t)k * 2) * p.tiles + tl]) *
-                                exp((double)(ld_f(&p.tile_m[((size_t)k * 2) * p.tiles + tl]) - Mp) * p.invT_d) * ip
-                          : ld_d(&p.tile_f[((size_t)k * 3 + cur_buf) * p.tiles + tl]);
+        double mass = (cur_buf < 0) ? sm.ts[0][tl] * exp((double)(sm.tm[0][tl] - Mp) * p.invT_d) * ip
+                                    : sm.tcur[tl];
         if (mass > 0.0) lastpos = tl;
         if (sel < 0 && cum + mass > thr) {
           sel = tl;
@@ -535,7 +543,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_kernel(StochParams p) {
         if (cur_buf < 0) {
           float xp[16];
           load16(zp, p.V, p.V, e0, xp);
-          const float Mt = ld_f(&p.tile_m[((size_t)k * 2) * p.tiles + sel]);
+          const float Mt = sm.tm[0][sel];
           const double sc = exp((double)(Mt - Mp) * p.invT_d) * ip;
 #pragma unroll
           for (int j = 0; j < 16; ++j) w[j] = (e0 + j < p.V) ? (double)expf((xp[j] - Mt) * p.invT) * sc : 0.0;
@@ -602,17 +610,23 @@ __global__ __launch_bounds__(kVThreads) void stochastic_kernel(StochParams p) {
       }
     }
     if (writer && sm.fin) {
-      __threadfence();
+      __threadfence();   // acquire: every node of the request has published its result
+      if (t == 0) sm.fflags = 0;
+      __syncthreads();
+      for (int v = t; v < n; v += kVThreads) {
+        const size_t kv = (size_t)b * p.n_max + v;
+        sm.facc[v] = p.acc_child[kv];
+        sm.ffin[v] = p.final_tok[kv];
+        const int pv = par[v];
+        const bool ok = (v == 0) ? (pv == -1) : (pv >= 0 && pv < v);
+        const int fl = p.node_flags[kv] | (ok ? 0 : TV_REQ_BAD_PARENT);
+        if (fl) atomicOr(&sm.fflags, fl);
+        p.node_flags[kv] = 0;
+      }
+      __syncthreads();
       if (t == 0) {
-        int fl = 0;
-        for (int v = 0; v < n; ++v) {
-          int pv = par[v];
-          bool ok = (v == 0) ? (pv == -1) : (pv >= 0 && pv < v);
-          if (!ok) fl |= TV_REQ_BAD_PARENT;
-          fl |= ld_i(&p.node_flags[(size_t)b * p.n_max + v]);
-        }
-        // flags of nodes whose rows were never read do not matter, but every
-        // flag raised on a read row (or a timeout) fails the request
+        // every flag raised on a row that was read (or a timeout) fails the request
+        const int fl = sm.fflags;
         if (fl) {
           p.status[b] = fl;
           p.path_len[b] = 0;
@@ -622,18 +636,16 @@ __global__ __launch_bounds__(kVThreads) void stochastic_kernel(StochParams p) {
           int cur = 0, j = 0;
           path[0] = 0;
           for (;;) {
-            int ch = ld_i(&p.acc_child[(size_t)b * p.n_max + cur]);
+            const int ch = sm.facc[cur];
             if (ch <= cur || ch >= n || j + 1 >= n) break;
             out[j] = tok[ch];
             path[++j] = ch;
             cur = ch;
           }
-          int ft = ld_i(&p.final_tok[(size_t)b * p.n_max + cur]);
-          out[j] = ft;
+          out[j] = sm.ffin[cur];
           p.path_len[b] = j + 1;
           p.status[b] = 0;
         }
-        for (int v = 0; v < n; ++v) p.node_flags[(size_t)b * p.n_max + v] = 0;
         p.req_done[b] = 0;
       }
     }
@@ -757,6 +769,7 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
     return TV_ERR_INVALID_ARG;
   if ((((uintptr_t)target_logits | (uintptr_t)draft_logits) & 15) != 0) return TV_ERR_INVALID_ARG;
   VerifyLayout L = layout(desc);
+  if (L.tiles > kMaxTiles) return TV_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < L.stoch_bytes) return TV_ERR_WORKSPACE;
   int cu = 0;
   rc = tv_device_cu_count(&cu);
