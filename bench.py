@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run one device-to-device copy of this many MiB (a reference "
+                         "kernel of known traffic for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -240,6 +243,15 @@ def main():
                 "unit": "GB/s", "frac": round(k["GBps"] / HBM_PEAK_GBS, 4),
                 "traffic": traffic_record(name, args.config, source_hash(*src[name])),
                 "algorithmic_bytes_per_launch": k["bytes"], "avg_launch_us": round(k["us"], 3)}
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src_buf = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
 
     # ---- CPU oracle baseline ------------------------------------------------
     cpu = None

@@ -8,34 +8,49 @@
 // Decomposition.  The query rows of one (request, KV head) pair are the n*G
 // (node, head-in-group) combinations; they all share the same keys, so the
 // prefix part is a dense contraction.  A workgroup owns a tile of rows and a
-// contiguous key range (split-K over the prefix, FlashDecoding-style); its four
-// waves interleave 32-key chunks of that range and merge their online-softmax
-// partials in LDS.  When a pair needs several key splits, each workgroup writes
-// its (m, l, O) partial to the workspace and the last workgroup to arrive on the
-// tile merges them by log-sum-exp and writes the output (no second kernel).
+// contiguous key range (split-K over the prefix, FlashDecoding-style).  When a
+// pair needs several key splits, every workgroup writes its (m, l, O) partial
+// to the workspace and the last one to arrive on the tile merges them by
+// log-sum-exp and writes the output (no second kernel).
 //
-// Rows per pair >= 16 with bf16 inputs run on MFMA (v_mfma_f32_16x16x32_bf16):
+// MFMA path (bf16, >= 16 rows): 32-key chunks of K and V stream from HBM into a
+// six-slot LDS ring through asynchronous global->LDS loads issued five chunks
+// ahead, so roughly 80 KB per CU are in flight.  Each lane's DMA fetches
+// exactly the 16 bytes it later feeds to v_mfma_f32_16x16x32_bf16, so operands
+// come back with conflict-free ds_read_b128.  The four waves share every chunk
+// and own disjoint 16*NTW-row slices of the tile:
 //   S^T[key][row] = K Q^T  then  O^T[d][row] += V^T P^T,
 // laid out so that a lane always owns one query row (lane % 16): the softmax
 // state is lane-local, and the C layout of S^T feeds the B operand of the PV
 // product without cross-lane moves.  Values are stored transposed per block
 // ([D][block] per head) so the PV operand (8 consecutive keys of one d) is a
-// single 16-byte load.  Fewer rows (or fp32 inputs) run on a VALU path.
+// single 16-byte piece.
 //
-// Tree mask: each wavefront builds the ancestor bitmaps of all nodes (two
-// 64-bit words per node, n <= 128) from the parent array by pointer jumping
-// with lane shuffles, then tests one bit per (row, tree key).
+// VALU path (fewer than 16 rows, or fp32): the waves interleave 64-key chunks
+// with lane = key for the scores and lane = d for PV, merged in LDS.
+//
+// Tree mask: a wavefront builds the ancestor bitmaps of all nodes (two 64-bit
+// words per node, n <= 128) from the parent array by pointer jumping with lane
+// shuffles, then tests one bit per (row, tree key).
 
 #include "tv_common.h"
 
 #include <math.h>
 #include <mutex>
 
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4] = 7 and
+// lgkmcnt[11:8] = 15 mean "no wait").
+#define TV_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0xF70)
+
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxNodes = 128;
-constexpr int kMaxSplits = 32;   // key splits per (request, KV head, row tile)
+constexpr int kMaxSplits = 32;        // key splits per (request, KV head, row tile)
+constexpr int kMaxKeysPerSplit = 32768;
+constexpr int kStages = 6;            // LDS ring slots of the MFMA path
+constexpr int kMaxTab = kMaxKeysPerSplit / 16 + 2;   // block-table entries staged per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -58,8 +73,54 @@ struct AttnParams {
 };
 
 struct AttnPlan {
-  int rows_per_tile, row_tiles, splits, keys_per_split, nt;
+  int rows_per_tile, row_tiles, splits, keys_per_split, ntw;
   size_t off_ml, off_cnt, bytes;
+};
+
+template <int D>
+struct Chunk {
+  static constexpr int KK = D / 32;            // 32-wide d pieces of the QK^T contraction
+  static constexpr int DT = D / 16;            // 16-wide d tiles of the PV product
+  static constexpr int NBLK = 2 * KK + DT;     // 1 KB operand blocks per 32-key chunk
+  static constexpr int BYTES = NBLK * 1024;
+  static constexpr int PER_WAVE = NBLK / 4;    // DMA instructions each wave issues per chunk
+};
+
+// ---------------------------------------------------------------------------
+// shared state
+// ---------------------------------------------------------------------------
+
+struct CommonSmem {
+  uint64_t anc[kMaxNodes][2];
+  int par[kMaxNodes];
+  int flag;
+};
+
+template <int D>
+struct RingSmem {
+  alignas(16) unsigned char ring[kStages][Chunk<D>::BYTES];
+  int tab[kMaxTab];
+};
+
+template <int D>
+struct ValuSmem {
+  float o[16][D + 4];           // unnormalised output rows (log2-domain softmax)
+  float m[16];
+  float l[16];
+  float wm[4][16];              // per-wave partial m / l before the intra-workgroup merge
+  float wl[4][16];
+  float qs[16][D];
+  float sc[4][16][64];          // per-wave probability strips
+};
+
+template <bool kBF16, int D>
+union AttnLds {
+  RingSmem<D> r;
+  ValuSmem<D> v;
+};
+template <int D>
+union AttnLds<false, D> {
+  ValuSmem<D> v;
 };
 
 // ---------------------------------------------------------------------------
@@ -69,7 +130,7 @@ struct AttnPlan {
 // Wave-cooperative pointer jumping: node j lives in lane j % 64, slot j / 64.
 // After round r every node holds its ancestors within distance < 2^r; seven
 // rounds cover any depth below 128.
-__device__ void build_ancestor_bitmaps(const int32_t* par, int n, uint64_t (*anc)[2], int lane) {
+__device__ void build_ancestor_bitmaps(const int* par, int n, uint64_t (*anc)[2], int lane) {
   uint64_t lo[2], hi[2];
   int jmp[2];
   for (int s = 0; s < 2; ++s) {
@@ -113,6 +174,10 @@ __device__ void build_ancestor_bitmaps(const int32_t* par, int n, uint64_t (*anc
   }
 }
 
+__device__ __forceinline__ tv_bf16x8 load_bf16x8(const uint16_t* ptr) {
+  return __builtin_bit_cast(tv_bf16x8, *(const tv_u32x4*)ptr);
+}
+
 __device__ __forceinline__ bool anc_bit(uint64_t lo, uint64_t hi, int w) {
   return w < 64 ? ((lo >> w) & 1ull) : ((hi >> (w - 64)) & 1ull);
 }
@@ -120,24 +185,6 @@ __device__ __forceinline__ bool anc_bit(uint64_t lo, uint64_t hi, int w) {
 __device__ __forceinline__ bool block_ok(int blk, int num_blocks) {
   return blk >= 0 && blk < num_blocks;
 }
-
-// ---------------------------------------------------------------------------
-// shared state of one workgroup
-// ---------------------------------------------------------------------------
-
-template <int RPT, int D>
-struct AttnSmem {
-  uint64_t anc[kMaxNodes][2];
-  float o[RPT][D + 4];          // unnormalised output rows (log2-domain softmax)
-  float m[RPT];
-  float l[RPT];
-  float wm[4][RPT];             // per-wave partial m / l before the intra-workgroup merge
-  float wl[4][RPT];
-  // VALU path scratch
-  float qs[16][D];
-  float sc[4][16][64];          // per-wave probability strips; split weights of the merge later
-  int flag;
-};
 
 // ---------------------------------------------------------------------------
 // VALU path: up to 16 rows, any element type
@@ -168,9 +215,9 @@ __device__ __forceinline__ void load8(const void* base, size_t off, float* dst) 
   }
 }
 
-template <bool kBF16, int D, int RPT, int RV>
-__device__ void attn_valu_rows(const AttnParams& p, AttnSmem<RPT, D>& sm, int b, int g, int r0, int rows,
-                               int P, int k_begin, int k_end, bool tree_in_range) {
+template <bool kBF16, int D, int RV>
+__device__ void attn_valu_rows(const AttnParams& p, ValuSmem<D>& sm, int b, int g, int r0, int rows,
+                               int P, int k_begin, int k_end, bool tree_in_range, const uint64_t (*anc)[2]) {
   constexpr int DJ = D / 64;   // d values per lane in the PV phase
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int G = p.G;
@@ -216,7 +263,7 @@ __device__ void attn_valu_rows(const AttnParams& p, AttnSmem<RPT, D>& sm, int b,
       bool ok = valid && r < rows;
       if (ok && key >= P) {
         const int node = (r0 + r) / G;
-        ok = tree_in_range && anc_bit(sm.anc[node][0], sm.anc[node][1], key - P);
+        ok = tree_in_range && anc_bit(anc[node][0], anc[node][1], key - P);
       }
       float v = ok ? s[r] : kNegInf;
       float cmax = tv_wave_max(v);
@@ -299,9 +346,9 @@ __device__ void attn_valu_rows(const AttnParams& p, AttnSmem<RPT, D>& sm, int b,
   }
 }
 
-template <bool kBF16, int D, int RPT>
-__device__ void attn_valu(const AttnParams& p, AttnSmem<RPT, D>& sm, int b, int g, int r0, int rows,
-                          int P, int k_begin, int k_end, bool tree_in_range) {
+template <bool kBF16, int D>
+__device__ void attn_valu(const AttnParams& p, ValuSmem<D>& sm, int b, int g, int r0, int rows,
+                          int P, int k_begin, int k_end, bool tree_in_range, const uint64_t (*anc)[2]) {
   const int t = threadIdx.x;
   const int G = p.G;
   // query rows, pre-scaled into the log2 domain; rows past `rows` are zero
@@ -317,208 +364,14 @@ __device__ void attn_valu(const AttnParams& p, AttnSmem<RPT, D>& sm, int b, int 
   }
   __syncthreads();
   const int rv = (rows + 3) / 4;
-  if (rv <= 1) attn_valu_rows<kBF16, D, RPT, 4>(p, sm, b, g, r0, rows, P, k_begin, k_end, tree_in_range);
-  else if (rv == 2) attn_valu_rows<kBF16, D, RPT, 8>(p, sm, b, g, r0, rows, P, k_begin, k_end, tree_in_range);
-  else if (rv == 3) attn_valu_rows<kBF16, D, RPT, 12>(p, sm, b, g, r0, rows, P, k_begin, k_end, tree_in_range);
-  else attn_valu_rows<kBF16, D, RPT, 16>(p, sm, b, g, r0, rows, P, k_begin, k_end, tree_in_range);
+  if (rv <= 1) attn_valu_rows<kBF16, D, 4>(p, sm, b, g, r0, rows, P, k_begin, k_end, tree_in_range, anc);
+  else if (rv == 2) attn_valu_rows<kBF16, D, 8>(p, sm, b, g, r0, rows, P, k_begin, k_end, tree_in_range, anc);
+  else if (rv == 3) attn_valu_rows<kBF16, D, 12>(p, sm, b, g, r0, rows, P, k_begin, k_end, tree_in_range, anc);
+  else attn_valu_rows<kBF16, D, 16>(p, sm, b, g, r0, rows, P, k_begin, k_end, tree_in_range, anc);
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path: 16*NT rows, bf16
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ tv_bf16x8 load_bf16x8(const uint16_t* ptr) {
-  return __builtin_bit_cast(tv_bf16x8, *(const tv_u32x4*)ptr);
-}
-
-template <int D, int NT>
-__device__ void attn_mfma(const AttnParams& p, AttnSmem<16 * NT, D>& sm, int b, int g, int r0, int R,
-                          int P, int n, int k_begin, int k_end, bool tree_in_range) {
-  constexpr int KK = D / 32;   // 32-wide d chunks of the QK^T contraction
-  constexpr int DT = D / 16;   // 16-wide d tiles of the PV product
-  constexpr int RPT = 16 * NT;
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int l16 = lane & 15, h4 = lane >> 4;
-  const int G = p.G;
-  const uint16_t* qg = (const uint16_t*)p.q;
-  const uint16_t* kg = (const uint16_t*)p.k;
-  const uint16_t* vg = (const uint16_t*)p.v;
-  const int32_t* trow = p.table + (size_t)b * p.max_blocks;
-
-  tv_bf16x8 qop[NT][KK];
-  uint64_t alo[NT], ahi[NT];
-  const tv_bf16x8 zero8 = {};
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int qrow = r0 + 16 * nt + l16;
-    bool ok = qrow < R;
-    int node = ok ? qrow / G : 0, hh = ok ? qrow % G : 0;
-    const uint16_t* qp = qg + (((size_t)b * p.n_max + node) * p.Hq + (size_t)g * G + hh) * D + 8 * h4;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qop[nt][kk] = ok ? load_bf16x8(qp + 32 * kk) : zero8;
-    alo[nt] = tree_in_range ? sm.anc[node][0] : 0ull;
-    ahi[nt] = tree_in_range ? sm.anc[node][1] : 0ull;
-  }
-
-  float m_run[NT], l_run[NT];
-  tv_f32x4 oacc[DT][NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = kNegInf;
-    l_run[nt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int nchunks = (k_end - k_begin + 31) / 32;
-  for (int c = wave; c < nchunks; c += 4) {
-    const int key0 = k_begin + 32 * c;
-    // K operand rows: S^T row i of tile t is key key0 + 8*(i/4) + 4*t + i%4, so the
-    // C layout gives lane l the keys key0 + 8*(l/16) + 4*t + j (j = 0..3).
-    tv_bf16x8 kop[2][KK];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      int key = key0 + 8 * (l16 >> 2) + 4 * tt + (l16 & 3);
-      bool ok = key < k_end;
-      int blk = ok ? trow[key / p.bs] : -1;
-      ok = ok && block_ok(blk, p.num_blocks);
-      const uint16_t* kp = kg + (((size_t)(ok ? blk : 0) * p.Hkv + g) * p.bs + key % p.bs) * D + 8 * h4;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = ok ? load_bf16x8(kp + 32 * kk) : zero8;
-    }
-    // V operand: lane l holds d = 16*dt + l%16 for keys key0 + 8*(l/16) .. +7
-    tv_bf16x8 vop[DT];
-    {
-      int kv = key0 + 8 * h4;
-      bool ok = kv < k_end;
-      int blk = ok ? trow[kv / p.bs] : -1;
-      ok = ok && block_ok(blk, p.num_blocks);
-      const uint16_t* vp = vg + (((size_t)(ok ? blk : 0) * p.Hkv + g) * D + l16) * p.bs + kv % p.bs;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vop[dt] = ok ? load_bf16x8(vp + (size_t)16 * dt * p.bs) : zero8;
-      if (ok && kv + 8 > k_end) {
-        // the last keys of the request share a block with slots that hold no data
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          tv_u32x4 w = __builtin_bit_cast(tv_u32x4, vop[dt]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            if (kv + j >= k_end) {
-              if (j & 1) w[j >> 1] &= 0x0000FFFFu;
-              else w[j >> 1] &= 0xFFFF0000u;
-            }
-          }
-          vop[dt] = __builtin_bit_cast(tv_bf16x8, w);
-        }
-      }
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      tv_f32x4 s[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[tt][kk], qop[nt][kk], acc, 0, 0, 0);
-        s[tt] = acc;
-      }
-      // scale, mask, chunk max
-      float cmax = kNegInf;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int key = key0 + 8 * h4 + 4 * tt + i;
-          bool ok = key < k_end;
-          if (ok && key >= P) ok = anc_bit(alo[nt], ahi[nt], key - P);
-          float v = ok ? s[tt][i] * p.scale_log2 : kNegInf;
-          s[tt][i] = v;
-          cmax = fmaxf(cmax, v);
-        }
-      }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      float m_new = fmaxf(m_run[nt], cmax);
-      float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
-      m_run[nt] = m_new;
-      float psum = 0.f;
-      uint32_t pk[4];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          float e0 = __builtin_amdgcn_exp2f(s[tt][i] - m_use);
-          float e1 = __builtin_amdgcn_exp2f(s[tt][i + 1] - m_use);
-          psum += e0 + e1;
-          pk[2 * tt + (i >> 1)] = (uint32_t)tv_f32_to_bf16_bits(e0) | ((uint32_t)tv_f32_to_bf16_bits(e1) << 16);
-        }
-      }
-      l_run[nt] = l_run[nt] * alpha + psum;
-      tv_u32x4 pw = {pk[0], pk[1], pk[2], pk[3]};
-      tv_bf16x8 pop = __builtin_bit_cast(tv_bf16x8, pw);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        oacc[dt][nt] *= alpha;
-        oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop, oacc[dt][nt], 0, 0, 0);
-      }
-    }
-  }
-
-  // merge the four waves' partials: m and l first, then the rescaled O sums
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float lt = l_run[nt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    l_run[nt] = lt;
-    if (h4 == 0) {
-      sm.wm[wave][16 * nt + l16] = m_run[nt];
-      sm.wl[wave][16 * nt + l16] = lt;
-    }
-  }
-  __syncthreads();
-  float wsc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int r = 16 * nt + l16;
-    float M = fmaxf(fmaxf(sm.wm[0][r], sm.wm[1][r]), fmaxf(sm.wm[2][r], sm.wm[3][r]));
-    wsc[nt] = (m_run[nt] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - M);
-  }
-  if (t < RPT) {
-    float M = fmaxf(fmaxf(sm.wm[0][t], sm.wm[1][t]), fmaxf(sm.wm[2][t], sm.wm[3][t]));
-    float L = 0.f;
-    for (int w = 0; w < 4; ++w) {
-      float mw = sm.wm[w][t];
-      L += (mw == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mw - M) * sm.wl[w][t];
-    }
-    sm.m[t] = M;
-    sm.l[t] = L;
-  }
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        int r = 16 * nt + l16;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          float* dst = &sm.o[r][16 * dt + 4 * h4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = wsc[nt] * oacc[dt][nt][i];
-            dst[i] = (w == 0) ? v : dst[i] + v;
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-// output / split-K merge
+// output and split-K merge
 // ---------------------------------------------------------------------------
 
 template <bool kBF16, int D>
@@ -528,16 +381,64 @@ __device__ __forceinline__ void store_out4(const AttnParams& p, int b, int g, in
   if (kBF16) {
     uint32_t lo = (uint32_t)tv_f32_to_bf16_bits(v4[0]) | ((uint32_t)tv_f32_to_bf16_bits(v4[1]) << 16);
     uint32_t hi = (uint32_t)tv_f32_to_bf16_bits(v4[2]) | ((uint32_t)tv_f32_to_bf16_bits(v4[3]) << 16);
-    uint2 w = make_uint2(lo, hi);
-    *(uint2*)((uint16_t*)p.out + off) = w;
+    *(uint2*)((uint16_t*)p.out + off) = make_uint2(lo, hi);
   } else {
     *(tv_f32x4*)((float*)p.out + off) = (tv_f32x4){v4[0], v4[1], v4[2], v4[3]};
   }
 }
 
-template <bool kBF16, int D, int RPT>
-__device__ void emit(const AttnParams& p, AttnSmem<RPT, D>& sm, int tile, int split, int n_active, int b,
-                     int g, int r0, int rows) {
+// After every split of a tile has written its partial: count this workgroup's
+// arrival; the last one merges the partials by log-sum-exp and writes the
+// output rows [r0, r0 + rows).  `scratch` holds (kMaxSplits + 1) * rows floats.
+template <bool kBF16, int D, int RW>
+__device__ void arrive_and_merge(const AttnParams& p, CommonSmem& cm, float* scratch, int tile, int n_active,
+                                 int b, int g, int r0, int rows) {
+  const int t = threadIdx.x;
+  __threadfence();   // release this workgroup's partial
+  __syncthreads();
+  if (t == 0) {
+    int prev = atomicAdd(&p.counters[tile], 1);
+    cm.flag = (prev == n_active - 1);
+  }
+  __syncthreads();
+  if (!cm.flag) return;
+  // acquire: the agent-scope fence invalidates this CU's L1 and the stale lines
+  // of this XCD's L2, so the plain loads below see the other splits' partials
+  __threadfence();
+  const size_t base = (size_t)tile * p.splits * RW;
+  float* wgt = scratch;                      // [n_active][rows]
+  float* lsum = scratch + kMaxSplits * rows;
+  if (t < rows) {
+    float M = kNegInf;
+    for (int s = 0; s < n_active; ++s) M = fmaxf(M, p.part_ml[(base + (size_t)s * RW + t) * 2]);
+    float L = 0.f;
+    for (int s = 0; s < n_active; ++s) {
+      const float2 ml = *(const float2*)&p.part_ml[(base + (size_t)s * RW + t) * 2];
+      const float w = (ml.x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+      L += w * ml.y;
+      wgt[s * rows + t] = w;
+    }
+    lsum[t] = L;
+  }
+  __syncthreads();
+  for (int idx = t; idx < rows * (D / 4); idx += kThreads) {
+    const int r = idx / (D / 4), d = 4 * (idx % (D / 4));
+    tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_active; ++s) {
+      const size_t pr = base + (size_t)s * RW + r;
+      acc += wgt[s * rows + r] * *(const tv_f32x4*)&p.part_o[pr * D + d];
+    }
+    const float inv = 1.f / lsum[r];
+    float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    store_out4<kBF16, D>(p, b, g, r0 + r, d, v4);
+  }
+  if (t == 0) p.counters[tile] = 0;   // leave the workspace ready for the next call
+}
+
+// VALU path output: rows [r0, r0 + rows) are in LDS.
+template <bool kBF16, int D, int RW>
+__device__ void emit_valu(const AttnParams& p, CommonSmem& cm, ValuSmem<D>& sm, int tile, int split, int n_active,
+                          int b, int g, int r0, int rows) {
   const int t = threadIdx.x;
   if (n_active == 1) {
     for (int idx = t; idx < rows * (D / 4); idx += kThreads) {
@@ -548,8 +449,7 @@ __device__ void emit(const AttnParams& p, AttnSmem<RPT, D>& sm, int tile, int sp
     }
     return;
   }
-  // write this split's partial
-  size_t prow = ((size_t)tile * p.splits + split) * RPT;
+  const size_t prow = ((size_t)tile * p.splits + split) * RW;
   for (int idx = t; idx < rows * (D / 4); idx += kThreads) {
     int r = idx / (D / 4), d = 4 * (idx % (D / 4));
     *(tv_f32x4*)(p.part_o + (prow + r) * D + d) = (tv_f32x4){sm.o[r][d], sm.o[r][d + 1], sm.o[r][d + 2], sm.o[r][d + 3]};
@@ -558,65 +458,322 @@ __device__ void emit(const AttnParams& p, AttnSmem<RPT, D>& sm, int tile, int sp
     p.part_ml[(prow + t) * 2] = sm.m[t];
     p.part_ml[(prow + t) * 2 + 1] = sm.l[t];
   }
-  __threadfence();
-  __syncthreads();
-  if (t == 0) {
-    int prev = atomicAdd(&p.counters[tile], 1);
-    sm.flag = (prev == n_active - 1);
+  __syncthreads();   // the merge below reuses the probability strips as scratch
+  arrive_and_merge<kBF16, D, RW>(p, cm, &sm.sc[0][0][0], tile, n_active, b, g, r0, rows);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA path: K/V ring in LDS, 16*NTW rows per wave, 64*NTW rows per workgroup
+// ---------------------------------------------------------------------------
+
+
+__device__ __forceinline__ tv_bf16x8 lds_bf16x8(const unsigned char* ptr) {
+  return __builtin_bit_cast(tv_bf16x8, *(const tv_u32x4*)ptr);
+}
+
+// Wait until at most n (<= 16) of this wave's vector-memory operations are
+// outstanding.  gfx9 s_waitcnt immediate: vmcnt[3:0] and [15:14], expcnt[6:4]
+// (7 = no wait), lgkmcnt[11:8] (15 = no wait).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(TV_VMCNT(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(TV_VMCNT(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(TV_VMCNT(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(TV_VMCNT(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(TV_VMCNT(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(TV_VMCNT(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(TV_VMCNT(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(TV_VMCNT(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(TV_VMCNT(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(TV_VMCNT(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(TV_VMCNT(10)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(TV_VMCNT(11)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(TV_VMCNT(12)); break;
+    case 13: __builtin_amdgcn_s_waitcnt(TV_VMCNT(13)); break;
+    case 14: __builtin_amdgcn_s_waitcnt(TV_VMCNT(14)); break;
+    case 15: __builtin_amdgcn_s_waitcnt(TV_VMCNT(15)); break;
+    default: __builtin_amdgcn_s_waitcnt(TV_VMCNT(16)); break;
   }
-  __syncthreads();
-  if (!sm.flag) return;
-  // acquire: the agent-scope fence invalidates this CU's L1 and the stale lines
-  // of this XCD's L2, so the plain loads below see the other splits' partials
-  __threadfence();
-  // last arrival: log-sum-exp merge of the n_active partials of this tile
-  const size_t base = (size_t)tile * p.splits * RPT;
-  static_assert(kMaxSplits * RPT <= 4 * 16 * 64, "split weights must fit the scratch strips");
-  float(*wgt)[RPT] = reinterpret_cast<float(*)[RPT]>(&sm.sc[0][0][0]);
-  if (t < rows) {
-    float M = kNegInf;
-    for (int s = 0; s < n_active; ++s) M = fmaxf(M, p.part_ml[(base + (size_t)s * RPT + t) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < n_active; ++s) {
-      const float2 ml = *(const float2*)&p.part_ml[(base + (size_t)s * RPT + t) * 2];
-      const float w = (ml.x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-      L += w * ml.y;
-      wgt[s][t] = w;
+}
+
+// One 16-byte-per-lane global->LDS load: lane l's bytes land at lds + 16*l.
+// Issued through inline asm so that the compiler's wait-count pass does not
+// treat it as a pending LDS write and drain it before every LDS read: the ring
+// loop waits for it explicitly (wait_vm + ring_barrier).
+__device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(gptr)
+               : "memory", "m0");
+}
+
+// Workgroup barrier for the ring: LDS operations of this wave complete, then
+// s_barrier.  Unlike __syncthreads() it does not wait for outstanding global
+// loads, which keeps the ring's later chunks in flight.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Issue this wave's share of the DMA loads of one 32-key chunk into `slot`.
+// Keys past k_end are redirected to key k_begin (always valid) and masked later.
+template <int D>
+__device__ __forceinline__ void issue_chunk(const AttnParams& p, const int* tab, int tab0, unsigned char* slot,
+                                            int key0, int k_begin, int k_end, int g, int wave, int lane) {
+  constexpr int KK = Chunk<D>::KK;
+  const int l16 = lane & 15, h4 = lane >> 4;
+#pragma unroll
+  for (int j = wave; j < Chunk<D>::NBLK; j += 4) {
+    const uint16_t* src;
+    if (j < 2 * KK) {
+      const int tt = j / KK, kk = j % KK;
+      int key = key0 + 8 * (l16 >> 2) + 4 * tt + (l16 & 3);
+      if (key >= k_end) key = k_begin;
+      int blk = tab[key / p.bs - tab0];
+      if (!block_ok(blk, p.num_blocks)) blk = 0;   // flagged by the request's validation
+      src = (const uint16_t*)p.k + (((size_t)blk * p.Hkv + g) * p.bs + key % p.bs) * D + 32 * kk + 8 * h4;
+    } else {
+      const int dt = j - 2 * KK;
+      int kv = key0 + 8 * h4;
+      if (kv >= k_end) kv = k_begin;
+      int blk = tab[kv / p.bs - tab0];
+      if (!block_ok(blk, p.num_blocks)) blk = 0;
+      src = (const uint16_t*)p.v + (((size_t)blk * p.Hkv + g) * D + 16 * dt + l16) * p.bs + kv % p.bs;
     }
-    sm.l[t] = L;
+    dma16(src, slot + j * 1024);
   }
-  __syncthreads();
-  for (int idx = t; idx < rows * (D / 4); idx += kThreads) {
-    const int r = idx / (D / 4), d = 4 * (idx % (D / 4));
-    tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_active; ++s) {
-      const size_t pr = base + (size_t)s * RPT + r;
-      acc += wgt[s][r] * *(const tv_f32x4*)&p.part_o[pr * D + d];
+}
+
+template <bool kBF16, int D, int NTW>
+__device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, CommonSmem& cm, RingSmem<D>& sm,
+                                                         const tv_bf16x8 (&qop)[NTW][D / 32], int tile, int split,
+                                                         int n_active, int b, int g, int r0, int R, int P,
+                                                         int k_begin, int k_end, int tab0, bool tree_in_range) {
+  constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT, RW = 64 * NTW;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int l16 = lane & 15, h4 = lane >> 4;
+  const int G = p.G;
+  const int rbase = r0 + wave * 16 * NTW;          // this wave's first row
+  const int nchunks = (k_end - k_begin + 31) / 32;
+
+  uint64_t alo[NTW], ahi[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int qrow = rbase + 16 * nt + l16;
+    const int node = qrow < R ? qrow / G : 0;
+    alo[nt] = tree_in_range ? cm.anc[node][0] : 0ull;
+    ahi[nt] = tree_in_range ? cm.anc[node][1] : 0ull;
+  }
+  // the query loads must retire before the ring starts: a wait the compiler
+  // places for them inside the loop would drain the ring on every chunk
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[nt][kk]));
+  __builtin_amdgcn_s_waitcnt(TV_VMCNT(0));
+  for (int c = 0; c < kStages - 1 && c < nchunks; ++c)
+    issue_chunk<D>(p, sm.tab, tab0, sm.ring[c], k_begin + 32 * c, k_begin, k_end, g, wave, lane);
+
+  float m_run[NTW], l_run[NTW];
+  tv_f32x4 oacc[DT][NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    m_run[nt] = kNegInf;
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int c = 0; c < nchunks; ++c) {
+    // this wave's loads of chunk c are done once at most `after` later chunks remain in flight
+    const int after = min(kStages - 2, nchunks - 1 - c);
+    wait_vm(after * Chunk<D>::PER_WAVE);
+    ring_barrier();    // every wave's share of chunk c has landed; chunk c - 1 is consumed
+    if (c + kStages - 1 < nchunks)
+      issue_chunk<D>(p, sm.tab, tab0, sm.ring[(c + kStages - 1) % kStages], k_begin + 32 * (c + kStages - 1),
+                     k_begin, k_end, g, wave, lane);
+    const int key0 = k_begin + 32 * c;
+    unsigned char* slot = sm.ring[c % kStages];
+    if (key0 + 32 > k_end) {
+      // last chunk: value slots past the request hold no data; clear them
+      if (wave == 0) {
+        const int kv = key0 + 8 * h4;
+        if (kv < k_end && kv + 8 > k_end) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            uint16_t* e = (uint16_t*)(slot + (2 * KK + dt) * 1024 + lane * 16);
+            for (int j = k_end - kv; j < 8; ++j) e[j] = 0;
+          }
+        }
+      }
+      ring_barrier();
     }
-    const float inv = 1.f / sm.l[r];
-    float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    store_out4<kBF16, D>(p, b, g, r0 + r, d, v4);
+    if (rbase >= R) continue;   // a wave without rows only helps to fill the ring
+
+    tv_bf16x8 kop[2][KK], vop[DT];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = lds_bf16x8(slot + (tt * KK + kk) * 1024 + lane * 16);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vop[dt] = lds_bf16x8(slot + (2 * KK + dt) * 1024 + lane * 16);
+
+    // phase 1: scores of every row tile (independent MFMA chains)
+    tv_f32x4 sc[NTW][2];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[tt][kk], qop[nt][kk], acc, 0, 0, 0);
+        sc[nt][tt] = acc;
+      }
+    }
+    // phase 2: scale, mask, online softmax.  Lane l holds keys
+    // key0 + 8*(l/16) + 4*tt + i of query row l % 16.  The running max is only
+    // moved when a row's max grows by more than kLazy (log2 units), so the
+    // accumulators are rescaled rarely; probabilities stay below 2^kLazy.
+    constexpr float kLazy = 8.f;
+    const bool plain = key0 + 32 <= P && key0 + 32 <= k_end;   // prefix keys only: no mask
+    tv_bf16x8 pop[NTW];
+    float alpha[NTW];
+    bool any_rescale = false;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      float cmax = kNegInf;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = sc[nt][tt][i] * p.scale_log2;
+          if (!plain) {
+            const int key = key0 + 8 * h4 + 4 * tt + i;
+            bool ok = key < k_end;
+            if (ok && key >= P) ok = anc_bit(alo[nt], ahi[nt], key - P);
+            v = ok ? v : kNegInf;
+          }
+          sc[nt][tt][i] = v;
+          cmax = fmaxf(cmax, v);
+        }
+      }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const bool move = cmax > m_run[nt] + kLazy || (m_run[nt] == kNegInf && cmax != kNegInf);
+      const float m_ref = move ? cmax : m_run[nt];
+      alpha[nt] = (move && m_run[nt] != kNegInf) ? __builtin_amdgcn_exp2f(m_run[nt] - m_ref) : 1.f;
+      any_rescale |= alpha[nt] != 1.f;
+      m_run[nt] = m_ref;
+      const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+      float psum = 0.f;
+      uint32_t pk[4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(sc[nt][tt][i] - m_use);
+          const float e1 = __builtin_amdgcn_exp2f(sc[nt][tt][i + 1] - m_use);
+          psum += e0 + e1;
+          pk[2 * tt + (i >> 1)] = (uint32_t)tv_f32_to_bf16_bits(e0) | ((uint32_t)tv_f32_to_bf16_bits(e1) << 16);
+        }
+      }
+      l_run[nt] = l_run[nt] * alpha[nt] + psum;
+      const tv_u32x4 pw = {pk[0], pk[1], pk[2], pk[3]};
+      pop[nt] = __builtin_bit_cast(tv_bf16x8, pw);
+    }
+    if (__any(any_rescale)) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] *= alpha[nt];
+    }
+    // phase 3: O^T += V^T P^T for every row tile
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[nt], oacc[dt][nt], 0, 0, 0);
   }
-  if (t == 0) p.counters[tile] = 0;   // leave the workspace ready for the next call
+
+  // output: lane l holds O[row rbase + 16*nt + l%16][16*dt + 4*(l/16) + i]
+  const size_t prow = ((size_t)tile * p.splits + split) * RW;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    float lt = l_run[nt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int qrow = rbase + 16 * nt + l16;
+    if (qrow >= R) continue;
+    if (n_active == 1) {
+      const float inv = 1.f / lt;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        float v4[4] = {oacc[dt][nt][0] * inv, oacc[dt][nt][1] * inv, oacc[dt][nt][2] * inv, oacc[dt][nt][3] * inv};
+        store_out4<kBF16, D>(p, b, g, qrow, 16 * dt + 4 * h4, v4);
+      }
+    } else {
+      const size_t row = prow + (qrow - r0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *(tv_f32x4*)(p.part_o + row * D + 16 * dt + 4 * h4) = oacc[dt][nt];
+      if (h4 == 0) *(float2*)&p.part_ml[row * 2] = make_float2(m_run[nt], lt);
+    }
+  }
+  if (n_active > 1) {
+    __syncthreads();   // the ring is dead: the merge uses it as scratch
+    arrive_and_merge<kBF16, D, RW>(p, cm, reinterpret_cast<float*>(&sm.ring[0][0]), tile, n_active, b, g, r0,
+                                   min(RW, R - r0));
+  }
 }
 
 // ---------------------------------------------------------------------------
 // kernel
 // ---------------------------------------------------------------------------
 
-template <bool kBF16, int D, int NT>
+template <bool kBF16, int D, int NTW>
 __global__ __launch_bounds__(kThreads) void tree_attn_kernel(AttnParams p) {
-  constexpr int RPT = kBF16 ? 16 * NT : 16;
-  __shared__ AttnSmem<RPT, D> sm;
+  constexpr int RW = kBF16 ? 64 * NTW : 16;
+  __shared__ CommonSmem cm;
+  __shared__ AttnLds<kBF16, D> u;
   const int t = threadIdx.x;
   const int lid = tv_xcd_remap(blockIdx.x, p.total);
   const int tile = lid / p.splits, split = lid % p.splits;
   const int bg = tile / p.row_tiles, rt = tile % p.row_tiles;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const bool designated = (g == 0 && rt == 0 && split == 0);
+  const int32_t* trow = p.table + (size_t)b * p.max_blocks;
+  const int k_begin = split * p.keys_per_split;
+  const int tab0 = k_begin / p.bs;
 
+  // one round trip: parents, this split's block-table entries, sizes, and (MFMA
+  // path) this wave's query operands; rows past the request are masked later
+  constexpr int KQ = kBF16 ? D / 32 : 1;
+  constexpr int NQ = kBF16 ? NTW : 1;
+  tv_bf16x8 qop[NQ][KQ];
+  if constexpr (kBF16) {
+    const int lane = t & 63, l16 = lane & 15, h4 = lane >> 4;
+    const int rbase = rt * RW + (t >> 6) * 16 * NTW;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int qrow = rbase + 16 * nt + l16;
+      const int node = min(qrow / p.G, p.n_max - 1), hh = qrow % p.G;
+      const uint16_t* qp =
+          (const uint16_t*)p.q + (((size_t)b * p.n_max + node) * p.Hq + (size_t)g * p.G + hh) * D + 8 * h4;
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) qop[nt][kk] = load_bf16x8(qp + 32 * kk);
+    }
+  }
+  if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
+  if constexpr (kBF16) {
+    const int ntab = min(p.max_blocks - tab0, (p.keys_per_split + p.bs - 1) / p.bs + 1);
+    for (int i = t; i < ntab; i += kThreads) u.r.tab[i] = trow[tab0 + i];
+  }
+  if (t == 0) cm.flag = 0;
   const int n = p.n_nodes[b];
   const int P = p.prefix_len[b];
+  __syncthreads();
+
   int flags = 0;
   if (n < 1 || n > p.n_max) flags |= TV_REQ_BAD_NNODES;
   else if (P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) flags |= TV_REQ_BAD_KV;
@@ -624,53 +781,49 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(AttnParams p) {
     if (designated && t == 0 && p.status) p.status[b] = flags;
     return;
   }
-  const int32_t* par = p.parent + (size_t)b * p.n_max;
   // parent array: parent[0] = -1 and 0 <= parent[i] < i
-  if (t == 0) sm.flag = 0;
-  __syncthreads();
   if (t < n) {
-    int pi = par[t];
-    bool ok = (t == 0) ? (pi == -1) : (pi >= 0 && pi < t);
-    if (!ok) sm.flag = 1;
+    const int pi = cm.par[t];
+    const bool ok = (t == 0) ? (pi == -1) : (pi >= 0 && pi < t);
+    if (!ok) cm.flag = 1;
   }
   __syncthreads();
-  if (sm.flag) {
+  if (cm.flag) {
     if (designated && t == 0 && p.status) p.status[b] = TV_REQ_BAD_PARENT;
     return;
   }
   if (designated) {
     // every block id used by positions [0, P + n) must name a pool block
-    const int32_t* trow = p.table + (size_t)b * p.max_blocks;
-    int nblk = (P + n + p.bs - 1) / p.bs;
-    __syncthreads();
+    const int nblk = (P + n + p.bs - 1) / p.bs;
     for (int i = t; i < nblk; i += kThreads)
-      if (!block_ok(trow[i], p.num_blocks)) sm.flag = 1;
+      if (!block_ok(trow[i], p.num_blocks)) cm.flag = 1;
     __syncthreads();
-    if (t == 0 && p.status) p.status[b] = sm.flag ? TV_REQ_BAD_KV : 0;
-    // keep going: loads from bad blocks are skipped, and the other workgroups
-    // of this tile count on this one in the split-K hand-off
+    if (t == 0 && p.status) p.status[b] = cm.flag ? TV_REQ_BAD_KV : 0;
+    // keep going: loads from bad blocks are redirected or skipped, and the
+    // other workgroups of this tile count on this one in the split-K hand-off
   }
 
   const int R = n * p.G;
-  const int r0 = rt * RPT;
+  const int r0 = rt * RW;
   if (r0 >= R) return;
   const int keys_total = P + n;
   const int n_active = (keys_total + p.keys_per_split - 1) / p.keys_per_split;
   if (split >= n_active) return;
-  const int k_begin = split * p.keys_per_split;
   const int k_end = min(k_begin + p.keys_per_split, keys_total);
   const bool tree_in_range = k_end > P;
-  if (tree_in_range && t < 64) build_ancestor_bitmaps(par, n, sm.anc, t);
+  if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
   __syncthreads();
 
-  int rows = min(RPT, R - r0);
-  if (kBF16 && R >= 16) {
-    if constexpr (kBF16) attn_mfma<D, NT>(p, sm, b, g, r0, R, P, n, k_begin, k_end, tree_in_range);
-  } else {
-    attn_valu<kBF16, D, RPT>(p, sm, b, g, r0, min(rows, 16), P, k_begin, k_end, tree_in_range);
-    rows = min(rows, 16);
+  if constexpr (kBF16) {
+    if (R >= 16) {
+      attn_ring<kBF16, D, NTW>(p, cm, u.r, qop, tile, split, n_active, b, g, r0, R, P, k_begin, k_end, tab0,
+                               tree_in_range);
+      return;
+    }
   }
-  emit<kBF16, D, RPT>(p, sm, tile, split, n_active, b, g, r0, rows);
+  const int rows = min(min(RW, R - r0), 16);
+  attn_valu<kBF16, D>(p, u.v, b, g, r0, rows, P, k_begin, k_end, tree_in_range, cm.anc);
+  emit_valu<kBF16, D, RW>(p, cm, u.v, tile, split, n_active, b, g, r0, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -691,32 +844,37 @@ int check_desc(const tv_attn_desc* d) {
   return TV_OK;
 }
 
-// MFMA row tile: 16 * NT query rows per workgroup (bf16 only).
-int choose_nt(const tv_attn_desc* d) {
-  const long long Rmax = (long long)d->n_max * (d->n_q_heads / d->n_kv_heads);
+// Rows per MFMA workgroup: 64 * NTW.  Wider tiles cut the re-reads of each
+// KV chunk (one per row tile) but leave fewer tiles to spread over the CUs.
+int choose_ntw(const tv_attn_desc* d, int cu) {
   if (d->dtype != TV_BF16) return 1;
-  return Rmax >= 64 ? 4 : (Rmax >= 32 ? 2 : 1);
+  const long long R = (long long)d->n_max * (d->n_q_heads / d->n_kv_heads);
+  const long long pairs = (long long)d->batch * d->n_kv_heads;
+  if (R >= 256 && pairs * ((R + 255) / 256) * 2 >= cu) return 4;
+  if (R >= 128 && pairs * ((R + 127) / 128) * 2 >= cu) return 2;
+  return 1;
 }
 
-int make_plan(const tv_attn_desc* d, int cu, int wg_per_cu, AttnPlan* pl) {
+int make_plan(const tv_attn_desc* d, int cu, int wg_per_cu, int ntw, AttnPlan* pl) {
   const int G = d->n_q_heads / d->n_kv_heads;
   const long long Rmax = (long long)d->n_max * G;
-  const int nt = choose_nt(d);
-  pl->nt = nt;
-  pl->rows_per_tile = d->dtype == TV_BF16 ? 16 * nt : 16;
+  pl->ntw = ntw;
+  pl->rows_per_tile = d->dtype == TV_BF16 ? 64 * ntw : 16;
   pl->row_tiles = (int)((Rmax + pl->rows_per_tile - 1) / pl->rows_per_tile);
   const long long max_keys = (long long)d->max_blocks_per_seq * d->block_size;
   const long long base = (long long)d->batch * d->n_kv_heads * pl->row_tiles;
-  long long target = (long long)wg_per_cu * cu;
+  const long long target = (long long)wg_per_cu * cu;
   long long splits = base > 0 ? (target + base - 1) / base : 1;
   long long max_splits = (max_keys + 127) / 128;
   if (max_splits > kMaxSplits) max_splits = kMaxSplits;
   if (splits > max_splits) splits = max_splits;
+  const long long min_splits = (max_keys + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
+  if (splits < min_splits) splits = min_splits;
+  if (splits > kMaxSplits) return TV_ERR_UNSUPPORTED;   // keys per sequence beyond 32 * 32768
   if (splits < 1) splits = 1;
   long long kps = (max_keys + splits - 1) / splits;
   kps = (kps + 31) / 32 * 32;
   splits = (max_keys + kps - 1) / kps;
-  if (kps > 0x7fffffff) return TV_ERR_UNSUPPORTED;
   pl->splits = (int)splits;
   pl->keys_per_split = (int)kps;
   const size_t tiles = (size_t)base;
@@ -736,14 +894,14 @@ int make_plan(const tv_attn_desc* d, int cu, int wg_per_cu, AttnPlan* pl) {
 
 typedef void (*AttnKernel)(AttnParams);
 
-AttnKernel pick_kernel(const tv_attn_desc* d, int nt) {
+AttnKernel pick_kernel(const tv_attn_desc* d, int ntw) {
   const bool bf = d->dtype == TV_BF16;
   if (d->head_dim == 128) {
     if (!bf) return tree_attn_kernel<false, 128, 1>;
-    return nt == 4 ? tree_attn_kernel<true, 128, 4> : nt == 2 ? tree_attn_kernel<true, 128, 2> : tree_attn_kernel<true, 128, 1>;
+    return ntw == 4 ? tree_attn_kernel<true, 128, 4> : ntw == 2 ? tree_attn_kernel<true, 128, 2> : tree_attn_kernel<true, 128, 1>;
   }
   if (!bf) return tree_attn_kernel<false, 64, 1>;
-  return nt == 4 ? tree_attn_kernel<true, 64, 4> : nt == 2 ? tree_attn_kernel<true, 64, 2> : tree_attn_kernel<true, 64, 1>;
+  return ntw == 4 ? tree_attn_kernel<true, 64, 4> : ntw == 2 ? tree_attn_kernel<true, 64, 2> : tree_attn_kernel<true, 64, 1>;
 }
 
 // Resident workgroups per CU of one kernel instance on the current device (cached).
@@ -778,11 +936,11 @@ int plan_for(const tv_attn_desc* d, AttnPlan* pl, AttnKernel* kern) {
   int cu = 0, occ = 0;
   int rc = tv_device_cu_count(&cu);
   if (rc != TV_OK) return rc;
-  const int nt = choose_nt(d);
-  AttnKernel k = pick_kernel(d, nt);
+  const int ntw = choose_ntw(d, cu);
+  AttnKernel k = pick_kernel(d, ntw);
   rc = occupancy(k, &occ);
   if (rc != TV_OK) return rc;
-  rc = make_plan(d, cu, occ, pl);
+  rc = make_plan(d, cu, occ, ntw, pl);
   if (kern) *kern = k;
   return rc;
 }
@@ -836,16 +994,15 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   p.bs = desc->block_size;
   p.max_blocks = desc->max_blocks_per_seq;
   p.num_blocks = desc->num_blocks;
-  float scale = desc->sm_scale > 0.f ? desc->sm_scale : 1.f / sqrtf((float)desc->head_dim);
+  const float scale = desc->sm_scale > 0.f ? desc->sm_scale : 1.f / sqrtf((float)desc->head_dim);
   p.scale_log2 = scale * kLog2e;
   p.rows_per_tile = pl.rows_per_tile;
   p.row_tiles = pl.row_tiles;
   p.splits = pl.splits;
   p.keys_per_split = pl.keys_per_split;
-  long long total = (long long)desc->batch * desc->n_kv_heads * pl.row_tiles * pl.splits;
+  const long long total = (long long)desc->batch * desc->n_kv_heads * pl.row_tiles * pl.splits;
   if (total > 0x7fffffff) return TV_ERR_UNSUPPORTED;
   p.total = (int)total;
-
   hipLaunchKernelGGL(kern, dim3(p.total), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
