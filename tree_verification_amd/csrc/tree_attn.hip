@@ -49,7 +49,7 @@ constexpr int kThreads = 256;
 constexpr int kMaxNodes = 128;
 constexpr int kMaxSplits = 32;        // key splits per (request, KV head, row tile)
 constexpr int kMaxKeysPerSplit = 32768;
-constexpr int kStages = 6;            // LDS ring slots of the MFMA path
+constexpr int kMaxBatch = 4;          // chunks staged per batch on the MFMA path
 constexpr int kMaxTab = kMaxKeysPerSplit / 16 + 2;   // block-table entries staged per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -66,15 +66,14 @@ struct AttnParams {
   int32_t* status;
   float* part_o;    // [tiles][splits][rows_per_tile][D]
   float* part_ml;   // [tiles][splits][rows_per_tile][2]
-  int* counters;    // [tiles]
-  int B, n_max, Hq, Hkv, G, D, bs, max_blocks, num_blocks;
+  int B, n_max, Hq, Hkv, G, D, bs, lbs, max_blocks, num_blocks;
   float scale_log2;
   int rows_per_tile, row_tiles, splits, keys_per_split, total;
 };
 
 struct AttnPlan {
   int rows_per_tile, row_tiles, splits, keys_per_split, ntw;
-  size_t off_ml, off_cnt, bytes;
+  size_t off_ml, bytes;
 };
 
 template <int D>
@@ -96,10 +95,13 @@ struct CommonSmem {
   int flag;
 };
 
-template <int D>
+// Chunks per batch: NTW = 2 keeps 4 in flight; NTW = 1 runs two workgroups
+// per CU (2 chunks each) and NTW = 4 is compute-bound (2 suffice).
+template <int D, int NTW>
 struct RingSmem {
-  alignas(16) unsigned char ring[kStages][Chunk<D>::BYTES];
-  int tab[kMaxTab];
+  static constexpr int NB = NTW == 2 ? kMaxBatch : 2;
+  alignas(16) unsigned char ring[NB][Chunk<D>::BYTES];   // one batch of K/V chunks
+  int tab[kMaxTab];   // (block, KV head) row index per block of this split
 };
 
 template <int D>
@@ -113,13 +115,13 @@ struct ValuSmem {
   float sc[4][16][64];          // per-wave probability strips
 };
 
-template <bool kBF16, int D>
+template <bool kBF16, int D, int NTW>
 union AttnLds {
-  RingSmem<D> r;
+  RingSmem<D, NTW> r;
   ValuSmem<D> v;
 };
-template <int D>
-union AttnLds<false, D> {
+template <int D, int NTW>
+union AttnLds<false, D, NTW> {
   ValuSmem<D> v;
 };
 
@@ -172,6 +174,14 @@ __device__ void build_ancestor_bitmaps(const int* par, int n, uint64_t (*anc)[2]
       anc[u][1] = hi[s];
     }
   }
+}
+
+typedef __bf16 tv_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float tv_f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((tv_f32x2){lo, hi}, tv_bf16x2));
 }
 
 __device__ __forceinline__ tv_bf16x8 load_bf16x8(const uint16_t* ptr) {
@@ -240,10 +250,10 @@ __device__ void attn_valu_rows(const AttnParams& p, ValuSmem<D>& sm, int b, int 
     for (int r = 0; r < RV; ++r) s[r] = 0.f;
     const int key = kb + lane;
     bool valid = key < k_end;
-    int blk = valid ? trow[key / p.bs] : -1;
+    int blk = valid ? trow[key >> p.lbs] : -1;
     valid = valid && block_ok(blk, p.num_blocks);
     if (valid) {
-      size_t base = (((size_t)blk * p.Hkv + g) * p.bs + key % p.bs) * D;
+      size_t base = ((((size_t)blk * p.Hkv + g) << p.lbs) + (key & (p.bs - 1))) * D;
 #pragma unroll 2
       for (int d0 = 0; d0 < D; d0 += 8) {
         float kv[8];
@@ -285,12 +295,12 @@ __device__ void attn_valu_rows(const AttnParams& p, ValuSmem<D>& sm, int b, int 
     for (int k8 = 0; k8 < 64; k8 += 8) {
       const int kk = kb + k8;
       if (kk >= k_end) break;
-      const int vb = trow[kk / p.bs];
+      const int vb = trow[kk >> p.lbs];
       if (!block_ok(vb, p.num_blocks)) continue;
       float vv[DJ][8];
 #pragma unroll
       for (int j = 0; j < DJ; ++j) {
-        size_t off = (((size_t)vb * p.Hkv + g) * D + lane + 64 * j) * p.bs + kk % p.bs;
+        size_t off = ((((size_t)vb * p.Hkv + g) * D + lane + 64 * j) << p.lbs) + (kk & (p.bs - 1));
         load8<kBF16>(p.v, off, vv[j]);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -379,60 +389,68 @@ __device__ __forceinline__ void store_out4(const AttnParams& p, int b, int g, in
   int node = qrow / p.G, hh = qrow % p.G;
   size_t off = (((size_t)b * p.n_max + node) * p.Hq + (size_t)g * p.G + hh) * D + d;
   if (kBF16) {
-    uint32_t lo = (uint32_t)tv_f32_to_bf16_bits(v4[0]) | ((uint32_t)tv_f32_to_bf16_bits(v4[1]) << 16);
-    uint32_t hi = (uint32_t)tv_f32_to_bf16_bits(v4[2]) | ((uint32_t)tv_f32_to_bf16_bits(v4[3]) << 16);
-    *(uint2*)((uint16_t*)p.out + off) = make_uint2(lo, hi);
+    *(uint2*)((uint16_t*)p.out + off) = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
   } else {
     *(tv_f32x4*)((float*)p.out + off) = (tv_f32x4){v4[0], v4[1], v4[2], v4[3]};
   }
 }
 
-// After every split of a tile has written its partial: count this workgroup's
-// arrival; the last one merges the partials by log-sum-exp and writes the
-// output rows [r0, r0 + rows).  `scratch` holds (kMaxSplits + 1) * rows floats.
-template <bool kBF16, int D, int RW>
-__device__ void arrive_and_merge(const AttnParams& p, CommonSmem& cm, float* scratch, int tile, int n_active,
-                                 int b, int g, int r0, int rows) {
+// Split-K merge, a second kernel: for every tile whose request used more than
+// one key split, combine the splits' (m, l, O) partials by log-sum-exp and
+// write the output rows.  The kernel boundary makes the partials visible (no
+// inter-workgroup fences or counters).  One workgroup per 16 rows of a tile.
+constexpr int kMergeRows = 4;
+
+template <int D>
+constexpr int merge_threads() { return kMergeRows * (D / 4); }   // one float4 item per thread
+
+template <bool kBF16, int D>
+__global__ __launch_bounds__(merge_threads<D>()) void attn_merge_kernel(AttnParams p) {
+  constexpr int ITEMS = merge_threads<D>();
   const int t = threadIdx.x;
-  __threadfence();   // release this workgroup's partial
-  __syncthreads();
-  if (t == 0) {
-    int prev = atomicAdd(&p.counters[tile], 1);
-    cm.flag = (prev == n_active - 1);
-  }
-  __syncthreads();
-  if (!cm.flag) return;
-  // acquire: the agent-scope fence invalidates this CU's L1 and the stale lines
-  // of this XCD's L2, so the plain loads below see the other splits' partials
-  __threadfence();
-  const size_t base = (size_t)tile * p.splits * RW;
-  float* wgt = scratch;                      // [n_active][rows]
-  float* lsum = scratch + kMaxSplits * rows;
-  if (t < rows) {
-    float M = kNegInf;
-    for (int s = 0; s < n_active; ++s) M = fmaxf(M, p.part_ml[(base + (size_t)s * RW + t) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < n_active; ++s) {
-      const float2 ml = *(const float2*)&p.part_ml[(base + (size_t)s * RW + t) * 2];
-      const float w = (ml.x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-      L += w * ml.y;
-      wgt[s * rows + t] = w;
+  const int groups = (p.rows_per_tile + kMergeRows - 1) / kMergeRows;
+  const int tile = blockIdx.x / groups, rg = blockIdx.x % groups;
+  const int bg = tile / p.row_tiles, rt = tile % p.row_tiles;
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const size_t base = (size_t)tile * p.splits * p.rows_per_tile + (size_t)rg * kMergeRows;
+  // issue every load first: sizes, each split's (m, l) and O pieces of this thread's item
+  const int n = p.n_nodes[b];
+  const int P = p.prefix_len[b];
+  const int r = t / (D / 4), d = 4 * (t % (D / 4));
+  float2 ml[kMaxSplits];
+  tv_f32x4 o[kMaxSplits];
+  const bool item = t < ITEMS;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < p.splits && item) {
+      const size_t pr = base + (size_t)s * p.rows_per_tile + r;
+      ml[s] = *(const float2*)&p.part_ml[pr * 2];
+      o[s] = *(const tv_f32x4*)&p.part_o[pr * D + d];
     }
-    lsum[t] = L;
   }
-  __syncthreads();
-  for (int idx = t; idx < rows * (D / 4); idx += kThreads) {
-    const int r = idx / (D / 4), d = 4 * (idx % (D / 4));
-    tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_active; ++s) {
-      const size_t pr = base + (size_t)s * RW + r;
-      acc += wgt[s * rows + r] * *(const tv_f32x4*)&p.part_o[pr * D + d];
+  if (n < 1 || n > p.n_max || P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) return;
+  const int n_active = (P + n + p.keys_per_split - 1) / p.keys_per_split;
+  if (n_active < 2) return;                 // written directly by the attention kernel
+  const int R = n * p.G;
+  const int row = rt * p.rows_per_tile + rg * kMergeRows + r;
+  if (!item || row >= R || row >= (rt + 1) * p.rows_per_tile) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < n_active) M = fmaxf(M, ml[s].x);
+  float L = 0.f;
+  tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < n_active) {
+      const float w = (ml[s].x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[s].x - M);
+      L += w * ml[s].y;
+      acc += w * o[s];
     }
-    const float inv = 1.f / lsum[r];
-    float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    store_out4<kBF16, D>(p, b, g, r0 + r, d, v4);
   }
-  if (t == 0) p.counters[tile] = 0;   // leave the workspace ready for the next call
+  const float inv = 1.f / L;
+  float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  store_out4<kBF16, D>(p, b, g, row, d, v4);
 }
 
 // VALU path output: rows [r0, r0 + rows) are in LDS.
@@ -458,8 +476,6 @@ __device__ void emit_valu(const AttnParams& p, CommonSmem& cm, ValuSmem<D>& sm, 
     p.part_ml[(prow + t) * 2] = sm.m[t];
     p.part_ml[(prow + t) * 2 + 1] = sm.l[t];
   }
-  __syncthreads();   // the merge below reuses the probability strips as scratch
-  arrive_and_merge<kBF16, D, RW>(p, cm, &sm.sc[0][0][0], tile, n_active, b, g, r0, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -471,82 +487,77 @@ __device__ __forceinline__ tv_bf16x8 lds_bf16x8(const unsigned char* ptr) {
   return __builtin_bit_cast(tv_bf16x8, *(const tv_u32x4*)ptr);
 }
 
-// Wait until at most n (<= 16) of this wave's vector-memory operations are
-// outstanding.  gfx9 s_waitcnt immediate: vmcnt[3:0] and [15:14], expcnt[6:4]
-// (7 = no wait), lgkmcnt[11:8] (15 = no wait).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(TV_VMCNT(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(TV_VMCNT(1)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(TV_VMCNT(2)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(TV_VMCNT(3)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(TV_VMCNT(4)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(TV_VMCNT(5)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(TV_VMCNT(6)); break;
-    case 7: __builtin_amdgcn_s_waitcnt(TV_VMCNT(7)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(TV_VMCNT(8)); break;
-    case 9: __builtin_amdgcn_s_waitcnt(TV_VMCNT(9)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(TV_VMCNT(10)); break;
-    case 11: __builtin_amdgcn_s_waitcnt(TV_VMCNT(11)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(TV_VMCNT(12)); break;
-    case 13: __builtin_amdgcn_s_waitcnt(TV_VMCNT(13)); break;
-    case 14: __builtin_amdgcn_s_waitcnt(TV_VMCNT(14)); break;
-    case 15: __builtin_amdgcn_s_waitcnt(TV_VMCNT(15)); break;
-    default: __builtin_amdgcn_s_waitcnt(TV_VMCNT(16)); break;
-  }
-}
 
-// One 16-byte-per-lane global->LDS load: lane l's bytes land at lds + 16*l.
-// Issued through inline asm so that the compiler's wait-count pass does not
-// treat it as a pending LDS write and drain it before every LDS read: the ring
-// loop waits for it explicitly (wait_vm + ring_barrier).
-__device__ __forceinline__ void dma16(const void* gptr, const unsigned char* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0), "v"(gptr)
-               : "memory", "m0");
-}
-
-// Workgroup barrier for the ring: LDS operations of this wave complete, then
-// s_barrier.  Unlike __syncthreads() it does not wait for outstanding global
-// loads, which keeps the ring's later chunks in flight.
+// Workgroup barrier for the chunk pipeline: LDS operations of this wave
+// complete, then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads, which keeps the prefetched chunks in flight.
 __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Issue this wave's share of the DMA loads of one 32-key chunk into `slot`.
-// Keys past k_end are redirected to key k_begin (always valid) and masked later.
+// This wave's share of one 32-key chunk: operand blocks wave, wave+4, ... of
+// the chunk (1 KB each, 16 bytes per lane), loaded into registers.  Keys past
+// k_end are redirected to key k_begin (always valid) and masked later.
 template <int D>
-__device__ __forceinline__ void issue_chunk(const AttnParams& p, const int* tab, int tab0, unsigned char* slot,
-                                            int key0, int k_begin, int k_end, int g, int wave, int lane) {
+struct ChunkRegs {
+  tv_u32x4 r[Chunk<D>::PER_WAVE];
+};
+
+template <int D>
+__device__ __forceinline__ void load_chunk(const AttnParams& p, const int* tabrow, int tab0, ChunkRegs<D>& cr,
+                                           int key0, int k_begin, int k_end, int wave, int lane) {
   constexpr int KK = Chunk<D>::KK;
   const int l16 = lane & 15, h4 = lane >> 4;
+  const int bmask = p.bs - 1;
+  const size_t row_elems = (size_t)p.bs * D;   // elements of one (block, KV head) row, K and V alike
 #pragma unroll
-  for (int j = wave; j < Chunk<D>::NBLK; j += 4) {
+  for (int i = 0; i < Chunk<D>::PER_WAVE; ++i) {
+    const int j = wave + 4 * i;
     const uint16_t* src;
-    if (j < 2 * KK) {
+    if (4 * i < 2 * KK) {   // key operand block (tt, kk)
       const int tt = j / KK, kk = j % KK;
       int key = key0 + 8 * (l16 >> 2) + 4 * tt + (l16 & 3);
-      if (key >= k_end) key = k_begin;
-      int blk = tab[key / p.bs - tab0];
-      if (!block_ok(blk, p.num_blocks)) blk = 0;   // flagged by the request's validation
-      src = (const uint16_t*)p.k + (((size_t)blk * p.Hkv + g) * p.bs + key % p.bs) * D + 32 * kk + 8 * h4;
-    } else {
+      key = key < k_end ? key : k_begin;
+      const int row = tabrow[(key >> p.lbs) - tab0];
+      src = (const uint16_t*)p.k + (size_t)row * row_elems + (key & bmask) * D + 32 * kk + 8 * h4;
+    } else {                // value operand block dt
       const int dt = j - 2 * KK;
       int kv = key0 + 8 * h4;
-      if (kv >= k_end) kv = k_begin;
-      int blk = tab[kv / p.bs - tab0];
-      if (!block_ok(blk, p.num_blocks)) blk = 0;
-      src = (const uint16_t*)p.v + (((size_t)blk * p.Hkv + g) * D + 16 * dt + l16) * p.bs + kv % p.bs;
+      kv = kv < k_end ? kv : k_begin;
+      const int row = tabrow[(kv >> p.lbs) - tab0];
+      src = (const uint16_t*)p.v + (size_t)row * row_elems + ((16 * dt + l16) << p.lbs) + (kv & bmask);
     }
-    dma16(src, slot + j * 1024);
+    cr.r[i] = *(const tv_u32x4*)src;
+  }
+}
+
+// Write this wave's share of a chunk to LDS.  In the request's last chunk the
+// value slots past k_end (same block, no data) are cleared first.
+template <int D>
+__device__ __forceinline__ void store_chunk(unsigned char* slot, const ChunkRegs<D>& cr, int key0, int k_end,
+                                            int wave, int lane) {
+  constexpr int KK = Chunk<D>::KK;
+  const int h4 = lane >> 4;
+  const int kv = key0 + 8 * h4;
+#pragma unroll
+  for (int i = 0; i < Chunk<D>::PER_WAVE; ++i) {
+    const int j = wave + 4 * i;
+    tv_u32x4 w = cr.r[i];
+    if (j >= 2 * KK && kv + 8 > k_end && kv < k_end) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (kv + e >= k_end) {
+          if (e & 1) w[e >> 1] &= 0x0000FFFFu;
+          else w[e >> 1] &= 0xFFFF0000u;
+        }
+      }
+    }
+    *(tv_u32x4*)(slot + j * 1024 + lane * 16) = w;
   }
 }
 
 template <bool kBF16, int D, int NTW>
-__device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, CommonSmem& cm, RingSmem<D>& sm,
+__device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, CommonSmem& cm, RingSmem<D, NTW>& sm,
                                                          const tv_bf16x8 (&qop)[NTW][D / 32], int tile, int split,
                                                          int n_active, int b, int g, int r0, int R, int P,
                                                          int k_begin, int k_end, int tab0, bool tree_in_range) {
@@ -565,16 +576,6 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
     alo[nt] = tree_in_range ? cm.anc[node][0] : 0ull;
     ahi[nt] = tree_in_range ? cm.anc[node][1] : 0ull;
   }
-  // the query loads must retire before the ring starts: a wait the compiler
-  // places for them inside the loop would drain the ring on every chunk
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qop[nt][kk]));
-  __builtin_amdgcn_s_waitcnt(TV_VMCNT(0));
-  for (int c = 0; c < kStages - 1 && c < nchunks; ++c)
-    issue_chunk<D>(p, sm.tab, tab0, sm.ring[c], k_begin + 32 * c, k_begin, k_end, g, wave, lane);
-
   float m_run[NTW], l_run[NTW];
   tv_f32x4 oacc[DT][NTW];
 #pragma unroll
@@ -584,32 +585,33 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
   }
-
-  for (int c = 0; c < nchunks; ++c) {
-    // this wave's loads of chunk c are done once at most `after` later chunks remain in flight
-    const int after = min(kStages - 2, nchunks - 1 - c);
-    wait_vm(after * Chunk<D>::PER_WAVE);
-    ring_barrier();    // every wave's share of chunk c has landed; chunk c - 1 is consumed
-    if (c + kStages - 1 < nchunks)
-      issue_chunk<D>(p, sm.tab, tab0, sm.ring[(c + kStages - 1) % kStages], k_begin + 32 * (c + kStages - 1),
-                     k_begin, k_end, g, wave, lane);
-    const int key0 = k_begin + 32 * c;
-    unsigned char* slot = sm.ring[c % kStages];
-    if (key0 + 32 > k_end) {
-      // last chunk: value slots past the request hold no data; clear them
-      if (wave == 0) {
-        const int kv = key0 + 8 * h4;
-        if (kv < k_end && kv + 8 > k_end) {
+  // Chunks move in batches of NB: while a batch is computed from LDS, the next
+  // batch is in flight in registers (about 64 KB per CU).  Loads never stay
+  // pending across more than one batch, which keeps the compiler's wait counts
+  // exact (no drain of younger loads).
+  constexpr int NB = RingSmem<D, NTW>::NB;
+  ChunkRegs<D> cr[NB];
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            uint16_t* e = (uint16_t*)(slot + (2 * KK + dt) * 1024 + lane * 16);
-            for (int j = k_end - kv; j < 8; ++j) e[j] = 0;
-          }
-        }
-      }
-      ring_barrier();
-    }
-    if (rbase >= R) continue;   // a wave without rows only helps to fill the ring
+  for (int i = 0; i < NB; ++i)
+    if (i < nchunks) load_chunk<D>(p, sm.tab, tab0, cr[i], k_begin + 32 * i, k_begin, k_end, wave, lane);
+
+  for (int c0 = 0; c0 < nchunks; c0 += NB) {
+    ring_barrier();   // every wave has finished the previous batch: its LDS slots are free
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib)
+      if (c0 + ib < nchunks) store_chunk<D>(sm.ring[ib], cr[ib], k_begin + 32 * (c0 + ib), k_end, wave, lane);
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib)
+      if (c0 + NB + ib < nchunks)
+        load_chunk<D>(p, sm.tab, tab0, cr[ib], k_begin + 32 * (c0 + NB + ib), k_begin, k_end, wave, lane);
+    ring_barrier();   // the batch is in LDS
+#pragma unroll
+  for (int ib = 0; ib < NB; ++ib) {
+    const int c = c0 + ib;
+    if (c >= nchunks) break;
+    unsigned char* slot = sm.ring[ib];
+    const int key0 = k_begin + 32 * c;
+    if (rbase >= R) continue;   // a wave without rows only helps to stage chunks
 
     tv_bf16x8 kop[2][KK], vop[DT];
 #pragma unroll
@@ -632,10 +634,12 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
         sc[nt][tt] = acc;
       }
     }
-    // phase 2: scale, mask, online softmax.  Lane l holds keys
-    // key0 + 8*(l/16) + 4*tt + i of query row l % 16.  The running max is only
-    // moved when a row's max grows by more than kLazy (log2 units), so the
-    // accumulators are rescaled rarely; probabilities stay below 2^kLazy.
+    // phase 2: mask, online softmax.  Lane l holds keys
+    // key0 + 8*(l/16) + 4*tt + i of query row l % 16.  The max is taken over
+    // the raw scores (the scale is positive) and the scale is folded into the
+    // exponent's FMA.  The running max is only moved when a row's max grows by
+    // more than kLazy (log2 units), so the accumulators are rescaled rarely;
+    // probabilities stay below 2^kLazy.
     constexpr float kLazy = 8.f;
     const bool plain = key0 + 32 <= P && key0 + 32 <= k_end;   // prefix keys only: no mask
     tv_bf16x8 pop[NTW];
@@ -643,44 +647,37 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
     bool any_rescale = false;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
-      float cmax = kNegInf;
+      if (!plain) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sc[nt][tt][i] * p.scale_log2;
-          if (!plain) {
+          for (int i = 0; i < 4; ++i) {
             const int key = key0 + 8 * h4 + 4 * tt + i;
             bool ok = key < k_end;
             if (ok && key >= P) ok = anc_bit(alo[nt], ahi[nt], key - P);
-            v = ok ? v : kNegInf;
+            sc[nt][tt][i] = ok ? sc[nt][tt][i] : kNegInf;
           }
-          sc[nt][tt][i] = v;
-          cmax = fmaxf(cmax, v);
         }
       }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      float rmax = fmaxf(fmaxf(fmaxf(sc[nt][0][0], sc[nt][0][1]), fmaxf(sc[nt][0][2], sc[nt][0][3])),
+                         fmaxf(fmaxf(sc[nt][1][0], sc[nt][1][1]), fmaxf(sc[nt][1][2], sc[nt][1][3])));
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+      const float cmax = rmax * p.scale_log2;   // -inf stays -inf
       const bool move = cmax > m_run[nt] + kLazy || (m_run[nt] == kNegInf && cmax != kNegInf);
       const float m_ref = move ? cmax : m_run[nt];
       alpha[nt] = (move && m_run[nt] != kNegInf) ? __builtin_amdgcn_exp2f(m_run[nt] - m_ref) : 1.f;
       any_rescale |= alpha[nt] != 1.f;
       m_run[nt] = m_ref;
-      const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-      float psum = 0.f;
-      uint32_t pk[4];
+      const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+      float e[8];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(sc[nt][tt][i] - m_use);
-          const float e1 = __builtin_amdgcn_exp2f(sc[nt][tt][i + 1] - m_use);
-          psum += e0 + e1;
-          pk[2 * tt + (i >> 1)] = (uint32_t)tv_f32_to_bf16_bits(e0) | ((uint32_t)tv_f32_to_bf16_bits(e1) << 16);
-        }
-      }
-      l_run[nt] = l_run[nt] * alpha[nt] + psum;
-      const tv_u32x4 pw = {pk[0], pk[1], pk[2], pk[3]};
+        for (int i = 0; i < 4; ++i) e[4 * tt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nt][tt][i], p.scale_log2, neg_m));
+      l_run[nt] = l_run[nt] * alpha[nt] + (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+      const tv_u32x4 pw = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                           pack_bf16x2(e[6], e[7])};
       pop[nt] = __builtin_bit_cast(tv_bf16x8, pw);
     }
     if (__any(any_rescale)) {
@@ -695,6 +692,7 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[nt], oacc[dt][nt], 0, 0, 0);
+  }
   }
 
   // output: lane l holds O[row rbase + 16*nt + l%16][16*dt + 4*(l/16) + i]
@@ -720,11 +718,6 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
       if (h4 == 0) *(float2*)&p.part_ml[row * 2] = make_float2(m_run[nt], lt);
     }
   }
-  if (n_active > 1) {
-    __syncthreads();   // the ring is dead: the merge uses it as scratch
-    arrive_and_merge<kBF16, D, RW>(p, cm, reinterpret_cast<float*>(&sm.ring[0][0]), tile, n_active, b, g, r0,
-                                   min(RW, R - r0));
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -732,10 +725,10 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
 // ---------------------------------------------------------------------------
 
 template <bool kBF16, int D, int NTW>
-__global__ __launch_bounds__(kThreads) void tree_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (kBF16 && NTW == 1) ? 2 : 1) void tree_attn_kernel(AttnParams p) {
   constexpr int RW = kBF16 ? 64 * NTW : 16;
   __shared__ CommonSmem cm;
-  __shared__ AttnLds<kBF16, D> u;
+  __shared__ AttnLds<kBF16, D, NTW> u;
   const int t = threadIdx.x;
   const int lid = tv_xcd_remap(blockIdx.x, p.total);
   const int tile = lid / p.splits, split = lid % p.splits;
@@ -767,7 +760,12 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(AttnParams p) {
   if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
   if constexpr (kBF16) {
     const int ntab = min(p.max_blocks - tab0, (p.keys_per_split + p.bs - 1) / p.bs + 1);
-    for (int i = t; i < ntab; i += kThreads) u.r.tab[i] = trow[tab0 + i];
+    for (int i = t; i < ntab; i += kThreads) {
+      const int blk = trow[tab0 + i];
+      // row index of (block, KV head); ids outside the pool (flagged by the
+      // request's validation) read block 0 instead
+      u.r.tab[i] = (block_ok(blk, p.num_blocks) ? blk : 0) * p.Hkv + g;
+    }
   }
   if (t == 0) cm.flag = 0;
   const int n = p.n_nodes[b];
@@ -863,7 +861,10 @@ int make_plan(const tv_attn_desc* d, int cu, int wg_per_cu, int ntw, AttnPlan* p
   pl->row_tiles = (int)((Rmax + pl->rows_per_tile - 1) / pl->rows_per_tile);
   const long long max_keys = (long long)d->max_blocks_per_seq * d->block_size;
   const long long base = (long long)d->batch * d->n_kv_heads * pl->row_tiles;
-  const long long target = (long long)wg_per_cu * cu;
+  // one workgroup per CU: more splits only add partials to merge, and tiles
+  // that already cover the CUs need no key splitting at all
+  (void)wg_per_cu;
+  const long long target = cu;
   long long splits = base > 0 ? (target + base - 1) / base : 1;
   long long max_splits = (max_keys + 127) / 128;
   if (max_splits > kMaxSplits) max_splits = kMaxSplits;
@@ -883,10 +884,8 @@ int make_plan(const tv_attn_desc* d, int cu, int wg_per_cu, int ntw, AttnPlan* p
     bytes = tiles * pl->splits * pl->rows_per_tile * (size_t)d->head_dim * sizeof(float);
     pl->off_ml = tv_align_up(bytes, 256);
     bytes = pl->off_ml + tiles * pl->splits * pl->rows_per_tile * 2 * sizeof(float);
-    pl->off_cnt = tv_align_up(bytes, 256);
-    bytes = pl->off_cnt + tiles * sizeof(int);
   } else {
-    pl->off_ml = pl->off_cnt = 0;
+    pl->off_ml = 0;
   }
   pl->bytes = tv_align_up(bytes, 256);
   return TV_OK;
@@ -984,7 +983,6 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   p.status = status;
   p.part_o = (float*)workspace;
   p.part_ml = (float*)((char*)workspace + pl.off_ml);
-  p.counters = (int*)((char*)workspace + pl.off_cnt);
   p.B = desc->batch;
   p.n_max = desc->n_max;
   p.Hq = desc->n_q_heads;
@@ -992,6 +990,7 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   p.G = desc->n_q_heads / desc->n_kv_heads;
   p.D = desc->head_dim;
   p.bs = desc->block_size;
+  p.lbs = __builtin_ctz((unsigned)desc->block_size);
   p.max_blocks = desc->max_blocks_per_seq;
   p.num_blocks = desc->num_blocks;
   const float scale = desc->sm_scale > 0.f ? desc->sm_scale : 1.f / sqrtf((float)desc->head_dim);
@@ -1004,5 +1003,17 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   if (total > 0x7fffffff) return TV_ERR_UNSUPPORTED;
   p.total = (int)total;
   hipLaunchKernelGGL(kern, dim3(p.total), dim3(kThreads), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  if (pl.splits > 1) {
+    const long long tiles = (long long)desc->batch * desc->n_kv_heads * pl.row_tiles;
+    const long long grid = tiles * ((pl.rows_per_tile + kMergeRows - 1) / kMergeRows);
+    if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+    const bool bf = desc->dtype == TV_BF16;
+    void (*mk)(AttnParams) = desc->head_dim == 128 ? (bf ? attn_merge_kernel<true, 128> : attn_merge_kernel<false, 128>)
+                                                   : (bf ? attn_merge_kernel<true, 64> : attn_merge_kernel<false, 64>);
+    const int mthreads = desc->head_dim == 128 ? merge_threads<128>() : merge_threads<64>();
+    hipLaunchKernelGGL(mk, dim3((unsigned)grid), dim3(mthreads), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  }
+  return TV_OK;
 }
