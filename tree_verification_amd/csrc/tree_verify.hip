@@ -1,28 +1,46 @@
 // Token-tree verification for gfx950.
 //
-// Greedy ([guide] "Greedy Verification Algorithm"): one workgroup per (node,
-// vocabulary chunk) computes the chunk's max / first argmax of the target row;
-// the last workgroup to finish a request combines the chunks, picks for every
-// node the first child whose token equals the node's argmax, and walks the
-// root path (at most depth + 1 dependent steps).
+// Results pass between kernels at kernel boundaries, which order every global
+// write before the next kernel's reads; no workgroup issues a device-wide fence
+// (on this part an agent-scope fence writes back and invalidates the XCD's
+// whole L2).
+//
+// Greedy ([guide] "Greedy Verification Algorithm"):
+//   greedy_argmax_kernel  one workgroup per (node, 8192-logit chunk) reduces its
+//                         chunk to one 64-bit key that orders by value, then by
+//                         lower index;
+//   greedy_chase_kernel   one workgroup per request takes each node's largest
+//                         key, matches children against the argmaxes and walks
+//                         the root path.
 //
 // Stochastic ([guide] "Stochastic Verification Algorithm"; [chapter] the
-// min(1, p/q) acceptance rule and the residual max(p - q, 0) / Z): each node's
-// decision depends only on its own two rows, its children's tokens and their
-// uniforms, so every node decides in parallel and the path is chased at the
-// end.  At node u with children c_1, c_2, ... the residual after i rejections
-// has the closed form
-//     p^(i)(w) = max(p(w) - C_i q(w), 0) / D_i,
-//     C_0 = 0, D_0 = 1,  C_{i+1} = C_i + D_i,  D_{i+1} = F(C_{i+1}),
-//     F(c) = sum_w max(p(w) - c q(w), 0),
-// (induction on the recursive residual; Z_{i+1} = F(C_{i+1}) / D_i), so a
-// rejection costs one vocabulary pass evaluating F at a known point, and the
-// accept test of c_{i+1} is  u * q(x) * D_i <= max(p(x) - C_i q(x), 0).
-// A team of S workgroups shares each node: each owns a slice of vocabulary
-// tiles, and the team meets at bounded barriers (cooperative launch keeps the
-// whole grid resident, so a team's members always run together).  The final
-// draw is a two-level inverse CDF: tile masses, then a scan inside one tile.
-// Exponentials are float32 (expf), sums and the accept test float64.
+// min(1, p/q) acceptance rule and the residual max(p - q, 0) / Z):
+//   stoch_node_kernel     a team of S workgroups per node, each member owning a
+//                         slice of 4096-logit chunks: chunk maxima and sums of
+//                         exp((z - max) / T) of the target row (and of the draft
+//                         row for nodes with children), then for nodes with
+//                         children the tests of the children in ascending id.
+//                         At node u with children c_1, c_2, ... the residual
+//                         after i rejections has the closed form
+//                             p^(i)(w) = max(p(w) - C_i q(w), 0) / D_i,
+//                             C_0 = 0, D_0 = 1, C_{i+1} = C_i + D_i,
+//                             D_{i+1} = F(C_{i+1}),  F(c) = sum_w max(p(w) - c q(w), 0)
+//                         (induction on the recursive residual, Z_{i+1} =
+//                         F(C_{i+1}) / D_i; when F = 0 the residual is kept), so
+//                         the accept test of c_{i+1} is
+//                             u * q(x) * D_i <= max(p(x) - C_i q(x), 0)
+//                         and a rejection costs one evaluation of F, split over
+//                         the team.  Members publish float64 partials in 64-bit
+//                         slots whose top bit marks them written, so a member
+//                         waits only for its team's slots.  A member whose slice
+//                         is at most two chunks keeps its exponentials on chip
+//                         across rejections.  Each node also makes the draw it
+//                         emits when no child is accepted: an inverse CDF over
+//                         member masses, chunk masses, then one chunk;
+//   stoch_chase_kernel    one workgroup per request: status, the root path and
+//                         its final token, and the exchange slots cleared for
+//                         the next call.
+// Vocabulary exponentials are float32 (exp_t), sums and the accept test float64.
 
 #include "tv_common.h"
 
@@ -30,18 +48,60 @@
 
 namespace {
 
-constexpr int kVThreads = 512;
-constexpr int kTileElems = kVThreads * 16;     // 8192 logits per tile (16 per thread)
-constexpr int kGreedyThreads = 256;
-constexpr int kGreedyChunk = kGreedyThreads * 32;
 constexpr int kMaxNodes = 128;
-constexpr int kMaxTiles = 64;                  // vocabulary up to 64 * 8192 = 524288
-constexpr long long kSpinLimit = 1LL << 22;   // bounded waits: ~0.5 s worst case, then TV_REQ_TIMEOUT
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// ---------------------------------------------------------------------------
-// small block reductions
-// ---------------------------------------------------------------------------
+constexpr int kGreedyThreads = 256;
+constexpr int kGreedyChunk = kGreedyThreads * 32;   // 8192 logits per workgroup
+
+constexpr int kSThreads = 256;
+constexpr int kChunk = kSThreads * 16;              // 4096 logits per chunk
+constexpr int kMaxChunks = 128;                     // vocabulary up to 128 * 4096 = 524288
+constexpr int kMaxTeam = 16;
+constexpr int kResident = 2;                        // chunks a member holds in registers
+constexpr long long kSpinLimit = 1LL << 19;         // bounded waits (~0.5 s), then TV_REQ_TIMEOUT
+constexpr unsigned long long kWritten = 1ull << 63;  // marks a published exchange slot
+
+// Buffer resource over one logit row of V floats.  Buffer loads address the row
+// with a 32-bit offset plus an immediate (one VGPR per batch of loads instead of a
+// 64-bit address per load) and return 0 past the row's end instead of reading it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int V) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, V * 4, 0x00020000);
+}
+
+// 16 consecutive logits of one thread; elements at or past V read as -inf.  Rows
+// whose length is a multiple of 4 are 16-byte aligned and use 16-byte loads (a
+// 4-vector starting below V then lies wholly inside the row).
+__device__ __forceinline__ void load16(__amdgpu_buffer_rsrc_t rs, int V, int e0, float* x) {
+  if ((V & 3) == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const tv_f32x4 a = __builtin_bit_cast(tv_f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * e0 + 16 * i, 0, 0));
+      x[4 * i] = a[0];
+      x[4 * i + 1] = a[1];
+      x[4 * i + 2] = a[2];
+      x[4 * i + 3] = a[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (e0 + i), 0, 0));
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = (e0 + i < V) ? x[i] : kNegInf;
+}
+
+// Children of u among nodes [1, n) of a parent row, ascending, written by wave 0
+// into kids[]; returns the count to lane 0 of wave 0 (n <= 128: two ballots).
+__device__ __forceinline__ int collect_children(const int32_t* par, int n, int u, int* kids) {
+  const int l = threadIdx.x & 63;
+  const bool k0 = (1 + l < n) && par[1 + l] == u;
+  const bool k1 = (65 + l < n) && par[65 + l] == u;
+  const unsigned long long b0 = __ballot(k0), b1 = __ballot(k1);
+  const unsigned long long below = (1ull << l) - 1ull;
+  if (k0) kids[__popcll(b0 & below)] = 1 + l;
+  if (k1) kids[__popcll(b0) + __popcll(b1 & below)] = 65 + l;
+  return __popcll(b0) + __popcll(b1);
+}
 
 template <int NT>
 __device__ float block_max(float v, float* red) {
@@ -67,36 +127,6 @@ __device__ double block_sum_d(double v, double* red) {
   return r;
 }
 
-template <int NT>
-__device__ int block_or(int v, int* red) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  unsigned long long bal = __ballot(v != 0);
-  __syncthreads();
-  if (l == 0) red[w] = bal != 0ull;
-  __syncthreads();
-  int r = 0;
-  for (int i = 0; i < NT / 64; ++i) r |= red[i];
-  return r;
-}
-
-// 16 consecutive logits of one thread (elements at or past `bound` read as -inf);
-// rows whose length is a multiple of 4 are 16-byte aligned and use vector loads.
-__device__ __forceinline__ void load16(const float* row, int V, int bound, int e0, float* x) {
-  if ((V & 3) == 0 && e0 + 16 <= bound) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tv_f32x4 a = *(const tv_f32x4*)(row + e0 + 4 * i);
-      x[4 * i] = a[0];
-      x[4 * i + 1] = a[1];
-      x[4 * i + 2] = a[2];
-      x[4 * i + 3] = a[3];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (e0 + i < bound) ? row[e0 + i] : kNegInf;
-  }
-}
-
 // ===========================================================================
 // greedy
 // ===========================================================================
@@ -110,145 +140,129 @@ struct GreedyParams {
   int32_t* path_len;
   int32_t* out_tokens;
   int32_t* status;
-  float* part_val;   // [B][n_max][chunks]
-  int* part_idx;     // [B][n_max][chunks]
-  int* part_bad;     // [B][n_max][chunks]
-  int* counters;     // [B]
+  unsigned long long* keys;   // [B][n_max][chunks] (value, index) maximum of each chunk
+  int* flags;                 // [B][n_max] non-finite logit seen
   int B, n_max, V, chunks;
 };
 
-__global__ __launch_bounds__(kGreedyThreads) void greedy_kernel(GreedyParams p) {
-  __shared__ float s_val[kGreedyThreads / 64];
-  __shared__ int s_idx[kGreedyThreads / 64];
-  __shared__ int s_bad[kGreedyThreads / 64];
-  __shared__ int s_last;
+// Order-preserving key: larger value first, then lower index.  -0 and +0 tie.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  const uint32_t hi = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)hi << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+__global__ __launch_bounds__(kGreedyThreads) void greedy_argmax_kernel(GreedyParams p) {
+  const int t = threadIdx.x, l = t & 63;
+  const int c = blockIdx.x % p.chunks;
+  const int k = blockIdx.x / p.chunks;
+  const int b = k / p.n_max, u = k % p.n_max;
+  const int n = p.n_nodes[b];
+  if (n < 1 || n > p.n_max || u >= n) return;
+  const __amdgpu_buffer_rsrc_t row = row_rsrc(p.logits + (size_t)k * p.V, p.V);
+  const int lo = c * kGreedyChunk, hi = min(p.V, lo + kGreedyChunk);
+  const int e0 = lo + 16 * t, e1 = e0 + 16 * kGreedyThreads;
+  float x[16], y[16];
+  load16(row, p.V, e0, x);   // both halves issued before either is used
+  load16(row, p.V, e1, y);
+  unsigned long long best = 0ull;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (e0 + i < hi) {
+      bad |= !isfinite(x[i]);
+      const unsigned long long kx = argmax_key(x[i], e0 + i);
+      best = kx > best ? kx : best;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (e1 + i < hi) {
+      bad |= !isfinite(y[i]);
+      const unsigned long long ky = argmax_key(y[i], e1 + i);
+      best = ky > best ? ky : best;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long ob = __shfl_xor(best, o);
+    best = ob > best ? ob : best;
+  }
+  __shared__ unsigned long long s_best[kGreedyThreads / 64];
+  const unsigned long long anybad = __ballot(bad != 0);
+  if (l == 0) {
+    s_best[t >> 6] = best;
+    if (anybad) atomicOr(&p.flags[k], 1);
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int i = 1; i < kGreedyThreads / 64; ++i) best = s_best[i] > best ? s_best[i] : best;
+    p.keys[(size_t)k * p.chunks + c] = best;
+  }
+}
+
+__global__ __launch_bounds__(kMaxNodes) void greedy_chase_kernel(GreedyParams p) {
   __shared__ int s_arg[kMaxNodes];
   __shared__ int s_child[kMaxNodes];
-  __shared__ int s_flags;
-
-  const int t = threadIdx.x, w = t >> 6, l = t & 63;
-  const int lid = blockIdx.x;
-  const int c = lid % p.chunks;
-  const int u = (lid / p.chunks) % p.n_max;
-  const int b = lid / (p.chunks * p.n_max);
+  __shared__ int s_badpar, s_nonfinite;
+  const int t = threadIdx.x, b = blockIdx.x;
   const int n = p.n_nodes[b];
   if (n < 1 || n > p.n_max) {
-    if (u == 0 && c == 0 && t == 0) {
+    if (t == 0) {
       p.status[b] = TV_REQ_BAD_NNODES;
       p.path_len[b] = 0;
     }
     return;
   }
-  if (u >= n) return;
-
-  // chunk max with the lowest index among equal maxima
-  const float* row = p.logits + ((size_t)b * p.n_max + u) * p.V;
-  const int lo = c * kGreedyChunk, hi = min(p.V, lo + kGreedyChunk);
-  float best = kNegInf;
-  int bidx = 0x7fffffff;
-  int bad = 0;
-  for (int e0 = lo + 16 * t; e0 < hi; e0 += 16 * kGreedyThreads) {
-    float x[16];
-    load16(row, p.V, hi, e0, x);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (e0 + i < hi) {
-        bad |= !isfinite(x[i]);
-        if (x[i] > best) {
-          best = x[i];
-          bidx = e0 + i;
-        }
-      }
-    }
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(best, o);
-    int oi = __shfl_xor(bidx, o);
-    if (ov > best || (ov == best && oi < bidx)) {
-      best = ov;
-      bidx = oi;
-    }
-  }
-  unsigned long long anybad = __ballot(bad != 0);
-  if (l == 0) {
-    s_val[w] = best;
-    s_idx[w] = bidx;
-    s_bad[w] = anybad != 0ull;
-  }
-  __syncthreads();
-  if (t == 0) {
-    for (int i = 1; i < kGreedyThreads / 64; ++i) {
-      if (s_val[i] > best || (s_val[i] == best && s_idx[i] < bidx)) {
-        best = s_val[i];
-        bidx = s_idx[i];
-      }
-      s_bad[0] |= s_bad[i];
-    }
-    size_t slot = ((size_t)b * p.n_max + u) * p.chunks + c;
-    p.part_val[slot] = best;
-    p.part_idx[slot] = bidx;
-    p.part_bad[slot] = s_bad[0];
-    __threadfence();
-    int prev = atomicAdd(&p.counters[b], 1);
-    s_last = (prev == n * p.chunks - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // last arrival for request b: per-node argmax, matching child, root path
-  if (t == 0) s_flags = 0;
-  __syncthreads();
   const int32_t* par = p.parent + (size_t)b * p.n_max;
   const int32_t* tok = p.tokens + (size_t)b * p.n_max;
-  for (int v = t; v < n; v += kGreedyThreads) {
-    float bv = kNegInf;
-    int bi = 0x7fffffff, bb = 0;
-    for (int cc = 0; cc < p.chunks; ++cc) {
-      size_t slot = ((size_t)b * p.n_max + v) * p.chunks + cc;
-      float cv = p.part_val[slot];
-      int ci = p.part_idx[slot];
-      bb |= p.part_bad[slot];
-      if (cv > bv) {   // chunks in ascending order: the first chunk wins ties
-        bv = cv;
-        bi = ci;
-      }
-    }
-    s_arg[v] = (bi == 0x7fffffff) ? 0 : bi;
-    s_child[v] = 0x7fffffff;
-    int pv = par[v];
-    bool ok = (v == 0) ? (pv == -1) : (pv >= 0 && pv < v);
-    if (!ok) atomicOr(&s_flags, TV_REQ_BAD_PARENT);
-    if (bb) atomicOr(&s_flags, TV_REQ_NONFINITE);
+  if (t == 0) {
+    s_badpar = 0;
+    s_nonfinite = 0;
   }
   __syncthreads();
-  if (s_flags == 0) {
-    for (int v = 1 + t; v < n; v += kGreedyThreads) {
-      int pv = par[v];
-      if (tok[v] == s_arg[pv]) atomicMin(&s_child[pv], v);
+  if (t < n) {
+    const size_t kv = (size_t)b * p.n_max + t;
+    unsigned long long key = 0ull;
+    for (int c = 0; c < p.chunks; ++c) {
+      const unsigned long long kc = p.keys[kv * p.chunks + c];
+      key = kc > key ? kc : key;
     }
+    s_arg[t] = (int)(0xFFFFFFFFu - (uint32_t)key);
+    s_child[t] = 0x7fffffff;
+    if (p.flags[kv]) {
+      s_nonfinite = 1;
+      p.flags[kv] = 0;
+    }
+    const int pv = par[t];
+    if (!((t == 0) ? (pv == -1) : (pv >= 0 && pv < t))) s_badpar = 1;
+  }
+  __syncthreads();
+  const int fl = s_badpar ? TV_REQ_BAD_PARENT : (s_nonfinite ? TV_REQ_NONFINITE : 0);
+  if (fl == 0 && t >= 1 && t < n) {
+    const int pv = par[t];
+    if (tok[t] == s_arg[pv]) atomicMin(&s_child[pv], t);
   }
   __syncthreads();
   if (t == 0) {
-    if (s_flags) {
-      p.status[b] = s_flags;
+    if (fl) {
+      p.status[b] = fl;
       p.path_len[b] = 0;
-    } else {
-      int32_t* path = p.path + (size_t)b * p.n_max;
-      int32_t* out = p.out_tokens + (size_t)b * p.n_max;
-      int cur = 0, j = 0;
-      path[0] = 0;
-      while (s_child[cur] != 0x7fffffff && j + 1 < n) {
-        int ch = s_child[cur];
-        out[j] = tok[ch];
-        path[++j] = ch;
-        cur = ch;
-      }
-      out[j] = s_arg[cur];
-      p.path_len[b] = j + 1;
-      p.status[b] = 0;
+      return;
     }
-    p.counters[b] = 0;
+    int32_t* path = p.path + (size_t)b * p.n_max;
+    int32_t* out = p.out_tokens + (size_t)b * p.n_max;
+    int cur = 0, j = 0;
+    path[0] = 0;
+    while (s_child[cur] != 0x7fffffff && j + 1 < n) {
+      const int ch = s_child[cur];
+      out[j] = tok[ch];
+      path[++j] = ch;
+      cur = ch;
+    }
+    out[j] = s_arg[cur];
+    p.path_len[b] = j + 1;
+    p.status[b] = 0;
   }
 }
 
@@ -269,387 +283,562 @@ struct StochParams {
   int32_t* out_tokens;
   int32_t* status;
   // workspace
-  float* tile_m;     // [nodes][2][tiles]   per-tile max of the target / draft row
-  double* tile_s;    // [nodes][2][tiles]   per-tile sum exp((z - tile max) / T)
-  double* tile_f;    // [nodes][3][tiles]   per-tile residual mass of the last passes
-  int* acc_child;    // [nodes]
-  int* final_tok;    // [nodes]
-  int* node_flags;   // [nodes]
-  int* arrive;       // [nodes]  team barrier counters
-  int* depart;       // [nodes]
-  int* req_done;     // [B]
-  int B, n_max, V, tiles, S, slots;
-  float invT;
+  unsigned long long* xch;   // [nodes][kMaxTeam]    member masses after child `node` is rejected
+  unsigned long long* sxch;  // [nodes][kMaxTeam][4] member (max, sum) of the target and draft rows
+  int* node_flags;           // [nodes]  NONFINITE / BAD_TOKEN / TIMEOUT
+  int* node_acc;             // [nodes]  accepted child, -1 when none
+  int* node_tok;             // [nodes]  draw made when no child is accepted
+  int B, n_max, V, chunks, S, per;   // per = chunks per team member
+  float k2hi, k2lo;                  // log2(e) / T as a float32 head and tail
   double invT_d;
 };
 
-struct StochSmem {
-  float tm[2][kMaxTiles];     // tile maxima (target, draft) staged from the workspace
-  double ts[2][kMaxTiles];    // tile exp-sums
-  double tf[kMaxTiles];       // tile residual masses of the latest pass
-  double tcur[kMaxTiles];     // tile masses of the current residual
-  double red_d[kVThreads / 64];
-  float red_f[kVThreads / 64];
-  int red_i[kVThreads / 64];
-  double scan[kVThreads / 64];
+// exp(d / T) for d <= 0 in float32: exp2 of d * log2(e) / T, with the product
+// carried as head + tail (the tail from an exact fma residual) so that rounding
+// the exponent does not cost accuracy; results below 2^-160 are 0.
+__device__ __forceinline__ float exp_t(float d, float k2hi, float k2lo) {
+  const float h = d * k2hi;
+  const float lo = fmaf(d, k2hi, -h) + d * k2lo;
+  const float r = __builtin_amdgcn_exp2f(h);
+  const float y = fmaf(r, lo * 0.693147180559945309f, r);
+  return h > -160.f ? y : 0.f;
+}
+
+// Weight of one vocabulary entry under max(p - c q, 0).  ep / eq are the
+// float32 exponentials exp((z - m) / T) relative to the entry's chunk maxima of
+// the target / draft row; a / b = exp((m - M) / T) / sum turn them into p and q
+// (float64).
+__device__ __forceinline__ double residual_weight(float ep, float eq, double a, double b, double c) {
+  return fmax((double)ep * a - c * ((double)eq * b), 0.0);
+}
+
+template <bool kRes>
+struct NodeSmem {
+  static constexpr int MM = kRes ? kResident : kMaxChunks;   // chunks per member
+  float red_f[kSThreads / 64][2 * kResident];   // per-wave maxima of a batch (chunk, row)
+  double red_d[kSThreads / 64][2 * kResident];  // per-wave exponential sums of a batch
+  float cm[2][MM];        // this member's chunk maxima (target, draft)
+  double cs[2][MM];       // ... chunk sums of exp((z - chunk max) / T)
+  double ca[2][MM];       // ... scale factors exp((m - M) / T) / sum
+  double part[kSThreads / 64][MM];   // per-wave residual sums of this member's chunks
+  double rlast[MM];       // this member's chunk masses of the latest pass
+  double rcur[MM];        // ... of the current residual
+  double xv[kMaxTeam];    // member masses of the latest pass
+  double xcur[kMaxTeam];  // ... of the current residual
+  float xm[2][kMaxTeam];  // member row maxima (target, draft)
+  double xs[2][kMaxTeam]; // member exponential sums relative to those maxima
+  float rowM[2];          // team row maxima and exponential sums
+  double rowS[2];
+  double scan[kSThreads / 64];
   int kids[kMaxNodes];
-  int facc[kMaxNodes];        // request finalisation: accepted child and final token per node
-  int ffin[kMaxNodes];
-  int fflags;
-  int nkids;
-  int timeout;
-  int sel;
-  int last;
-  int fin;
-  int badtok;
+  float kzp[kMaxNodes], kzq[kMaxNodes], kua[kMaxNodes];   // per child: logits of its token, its uniform
+  int nk, bad, timeout, owner, sel, res_sel, res_last, res_tok;
+  double base, thr;
+  // draft exponentials of the resident slice, [chunk][group of 4][thread]
+  tv_f32x4 qe[kRes ? kResident * 4 * kSThreads : 1];
 };
 
-// Team barrier: every member adds one arrival and waits for S * phase of them.
-// Bounded: on expiry the request is flagged TV_REQ_TIMEOUT and the workgroup
-// carries on (all later reads stay in bounds).
-__device__ void team_barrier(const StochParams& p, StochSmem& sm, int k, int phase) {
-  if (p.S == 1) {
-    __syncthreads();
-    return;
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    atomicAdd(&p.arrive[k], 1);
-    const int target = p.S * phase;
-    long long it = 0;
-    while (__hip_atomic_load(&p.arrive[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++it > kSpinLimit) {
-        sm.timeout = 1;
-        break;
+// LDS-only workgroup barrier: unlike __syncthreads it does not first wait for
+// this wave's outstanding global loads, so later chunks keep streaming in.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Sum of 16 floats, pairwise.
+__device__ __forceinline__ float sum16(const float* x) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = x[2 * i] + x[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] += a[i + 4];
+  return (a[0] + a[2]) + (a[1] + a[3]);
+}
+
+// Statistics of a batch of up to kResident chunks of the target row (and of the
+// draft row when `both`): every chunk's maximum m and sum of exp((z - m) / T)
+// over the workgroup, stored at local chunk index j0 + r.  The thread's logits
+// are replaced by those exponentials.  Units (row, chunk) are taken in the order
+// their loads were issued, each as soon as its own data has arrived.
+// Non-finite logits set sm.bad.
+template <bool kRes>
+__device__ void batch_stats(NodeSmem<kRes>& sm, float (&xp)[kResident][16], float (&xq)[kResident][16], int nb,
+                            bool both, int my_c0, int j0, int V, float k2hi, float k2lo) {
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  int bad = 0;
+#pragma unroll
+  for (int row = 0; row < 2; ++row) {
+#pragma unroll
+    for (int r = 0; r < kResident; ++r) {
+      if (r < nb && (row == 0 || both)) {
+        float* x = row ? xq[r] : xp[r];
+        const int e0 = (my_c0 + j0 + r) * kChunk + 16 * t;
+        float m = kNegInf;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (e0 + e < V) {
+            bad |= !isfinite(x[e]);
+            m = fmaxf(m, x[e]);
+          }
+        }
+        m = tv_wave_max(m);
+        if (l == 0) sm.red_f[w][2 * r + row] = m;
+        lds_barrier();
+        m = sm.red_f[0][2 * r + row];
+        for (int i = 1; i < kSThreads / 64; ++i) m = fmaxf(m, sm.red_f[i][2 * r + row]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = exp_t(x[e] - m, k2hi, k2lo);   // entries past V hold -inf and become 0
+        const double sw = tv_wave_sum_d((double)sum16(x));
+        if (l == 0) sm.red_d[w][2 * r + row] = sw;
+        if (t == 0) sm.cm[row][j0 + r] = m;
       }
     }
-    __threadfence();
+  }
+  if (__ballot(bad != 0) != 0ull && l == 0) sm.bad = 1;
+  __syncthreads();
+  if (t < 2 * nb) {
+    double s = 0.0;
+    for (int i = 0; i < kSThreads / 64; ++i) s += sm.red_d[i][t];
+    sm.cs[t & 1][j0 + (t >> 1)] = s;
+  }
+  __syncthreads();   // the next batch may overwrite red_f / red_d
+}
+
+// Publish one 64-bit word in slot `slot` (top bit marks it written).
+__device__ __forceinline__ void xch_put(unsigned long long* slot, unsigned long long bits) {
+  __hip_atomic_store(slot, bits | kWritten, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait for a published slot (bounded); returns its payload, 0 after a timeout.
+__device__ __forceinline__ unsigned long long xch_get(unsigned long long* slot, int* timeout) {
+  unsigned long long v;
+  long long it = 0;
+  while (((v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & kWritten) == 0ull) {
+    if (++it > kSpinLimit) {
+      *timeout = 1;
+      return 0ull;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return v & ~kWritten;
+}
+
+// Inverse CDF inside one chunk: the smallest index whose running mass (from
+// `base`) exceeds thr.  Thread ranges come from one scan of the per-thread
+// sums; only the first thread whose range ends past thr walks its 16 weights.
+// When rounding leaves no such thread, or no weight of that thread crosses, the
+// last positive weight at or before it is taken.  w: this thread's 16 weights.
+// Returns the index to every thread.
+template <class Smem>
+__device__ int chunk_draw(Smem& sm, const double (&w)[16], int e0, double base, double thr, int fallback) {
+  const int t = threadIdx.x, wv = t >> 6, ln = t & 63;
+  double loc = 0.0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) loc += w[j];
+  double incl = loc;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(incl, o);
+    incl += (ln >= o) ? y : 0.0;
+  }
+  if (ln == 63) sm.scan[wv] = incl;
+  if (t == 0) {
+    sm.res_sel = 0x7fffffff;
+    sm.res_last = -1;
   }
   __syncthreads();
-}
-
-// Row statistics of one tile: max, then sum of expf((z - max) * invT) in float64.
-__device__ void tile_stats(const StochParams& p, StochSmem& sm, const float* row, int tile, float* m_out,
-                           double* s_out, int* bad) {
-  const int t = threadIdx.x;
-  const int e0 = tile * kTileElems + 16 * t;
-  float x[16];
-  load16(row, p.V, p.V, e0, x);
-  float mx = kNegInf;
-  int nb = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (e0 + i < p.V) {
-      nb |= !isfinite(x[i]);
-      mx = fmaxf(mx, x[i]);
-    }
-  }
-  *bad |= nb;
-  const float M = block_max<kVThreads>(mx, sm.red_f);
-  double s = 0.0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (e0 + i < p.V) s += (double)expf((x[i] - M) * p.invT);
-  s = block_sum_d<kVThreads>(s, sm.red_d);
-  *m_out = M;
-  *s_out = s;
-}
-
-// Residual weights max(p - c q, 0) of 16 logits, float32 exponentials, float64 combination.
-__device__ __forceinline__ void residual16(const StochParams& p, const float* zp, const float* zq, int e0,
-                                           float Mp, float Mq, double ip, double iq, double c, double* w) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (e0 + i < p.V) {
-      double pw = (double)expf((zp[i] - Mp) * p.invT) * ip;
-      double qw = (double)expf((zq[i] - Mq) * p.invT) * iq;
-      w[i] = fmax(pw - c * qw, 0.0);
-    } else {
-      w[i] = 0.0;
-    }
-  }
-}
-
-__global__ __launch_bounds__(kVThreads) void stochastic_kernel(StochParams p) {
-  __shared__ StochSmem sm;
-  const int t = threadIdx.x;
-  const int slot = blockIdx.x / p.S, member = blockIdx.x % p.S;
-  const int tiles_per = (p.tiles + p.S - 1) / p.S;
-  const int my_t0 = member * tiles_per, my_t1 = min(p.tiles, my_t0 + tiles_per);
-  const int total_nodes = p.B * p.n_max;
-  for (int k = slot; k < total_nodes; k += p.slots) {
-    const int b = k / p.n_max, u = k % p.n_max;
-    const int n = p.n_nodes[b];
-    if (n < 1 || n > p.n_max) {
-      if (u == 0 && member == 0 && t == 0) {
-        p.status[b] = TV_REQ_BAD_NNODES;
-        p.path_len[b] = 0;
-      }
-      continue;
-    }
-    if (u >= n) continue;
-    const int32_t* par = p.parent + (size_t)b * p.n_max;
-    const int32_t* tok = p.tokens + (size_t)b * p.n_max;
-    const float* zp = p.target + ((size_t)b * p.n_max + u) * p.V;
-    const float* zq = p.draft + ((size_t)b * p.n_max + u) * p.V;
-
-    // children of u in ascending id
-    __syncthreads();
-    if (t == 0) {
-      int c = 0, badtok = 0;
-      for (int v = 1; v < n; ++v) {
-        if (par[v] == u) {
-          sm.kids[c++] = v;
-          badtok |= (tok[v] < 0 || tok[v] >= p.V);
+  double lo = base;
+  for (int i = 0; i < wv; ++i) lo += sm.scan[i];
+  lo += incl - loc;
+  if (loc > 0.0 && lo + loc > thr) atomicMin(&sm.res_sel, t);   // candidate thread
+  if (loc > 0.0) atomicMax(&sm.res_last, t);
+  __syncthreads();
+  const int ct = sm.res_sel != 0x7fffffff ? sm.res_sel : sm.res_last;
+  if (t == 0) sm.res_tok = fallback;
+  __syncthreads();
+  if (t == ct) {
+    double run = lo;
+    int found = -1, lastw = -1;
+    for (int j = 0; j < 16; ++j) {
+      run += w[j];
+      if (w[j] > 0.0) {
+        lastw = e0 + j;
+        if (run > thr) {
+          found = e0 + j;
+          break;
         }
       }
-      sm.nkids = c;
-      sm.badtok = badtok;
+    }
+    sm.res_tok = found >= 0 ? found : lastw;
+  }
+  __syncthreads();
+  return sm.res_tok;
+}
+
+// First index of `m[0..count)` (in order) whose running sum from `base`
+// exceeds thr, with the running sum before it; the last positive entry (and the
+// full sum) when rounding leaves none.
+__device__ __forceinline__ int select_mass(const double* m, int count, double thr, double* base) {
+  int sel = -1, lastpos = 0;
+  double cum = *base, b = *base;
+  for (int i = 0; i < count; ++i) {
+    if (m[i] > 0.0) lastpos = i;
+    if (sel < 0 && cum + m[i] > thr) {
+      sel = i;
+      b = cum;
+    }
+    cum += m[i];
+  }
+  if (sel < 0) {
+    sel = lastpos;
+    b = cum;
+  }
+  *base = b;
+  return sel;
+}
+
+// One team of S workgroups per node (team = blockIdx / S, members on consecutive
+// ids), each member owning `per` consecutive chunks of the vocabulary.  Every
+// member reads its slice of the target row (and of the draft row when the node
+// has children) once; the team exchanges each slice's (max, sum), tests the
+// children, and makes the node's draw for the case that no child is accepted
+// (the chase kernel uses it when the accepted path ends at this node).  Members
+// wait only on their own team: with workgroups dispatched in id order every
+// team becomes fully resident once the teams before it have left, and a wait
+// that still expires flags TV_REQ_TIMEOUT instead of hanging.  kRes: every
+// member's slice is at most kResident chunks and its exponentials stay on chip
+// (target in registers, draft in LDS); otherwise each pass re-reads the slice.
+// Four workgroups per CU: a 16-member team per node for up to 64 nodes on 256 CUs.
+template <bool kRes>
+__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4))) void stoch_node_kernel(StochParams p) {
+  __shared__ NodeSmem<kRes> sm;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int k = blockIdx.x / p.S, member = blockIdx.x % p.S;
+  const int my_c0 = min(member * p.per, p.chunks);
+  const int nmine = min(my_c0 + p.per, p.chunks) - my_c0;   // at most kResident when kRes
+  const int b = k / p.n_max, u = k % p.n_max;
+  const int n = p.n_nodes[b];
+  if (n < 1 || n > p.n_max || u >= n) return;
+  const int32_t* par = p.parent + (size_t)b * p.n_max;
+  const int32_t* tok = p.tokens + (size_t)b * p.n_max;
+  const float* zp_row = p.target + (size_t)k * p.V;
+  const float* zq_row = p.draft + (size_t)k * p.V;
+  const __amdgpu_buffer_rsrc_t zp_rs = row_rsrc(zp_row, p.V), zq_rs = row_rsrc(zq_row, p.V);
+
+  // first batch of the slice: the target at once, the draft as soon as one
+  // ballot over the parent row (loaded ahead of the slice, so it does not queue
+  // behind it) shows that u has children
+  const int pv0 = (1 + l < n) ? par[1 + l] : -1;
+  const int pv1 = (65 + l < n) ? par[65 + l] : -1;
+  const float us = p.u_sample[k];
+  float ep[kResident][16], eq[kResident][16];
+#pragma unroll
+  for (int r = 0; r < kResident; ++r)
+    if (r < nmine) load16(zp_rs, p.V, (my_c0 + r) * kChunk + 16 * t, ep[r]);
+  const bool internal = (__ballot(pv0 == u) | __ballot(pv1 == u)) != 0ull;
+  if (internal) {
+#pragma unroll
+    for (int r = 0; r < kResident; ++r)
+      if (r < nmine) load16(zq_rs, p.V, (my_c0 + r) * kChunk + 16 * t, eq[r]);
+  }
+  if (w == 0) {
+    const int c = collect_children(par, n, u, sm.kids);
+    if (l == 0) {
+      sm.nk = c;
+      sm.bad = 0;
       sm.timeout = 0;
     }
-    __syncthreads();
-    const int nk = sm.nkids;
-    int flags = sm.badtok ? TV_REQ_BAD_TOKEN : 0;
+  }
 
-    // phase 1: per-tile statistics of my slice
-    int bad = 0;
-    for (int tl = my_t0; tl < my_t1; ++tl) {
-      float m;
-      double s;
-      tile_stats(p, sm, zp, tl, &m, &s, &bad);
-      if (t == 0) {
-        p.tile_m[((size_t)k * 2) * p.tiles + tl] = m;
-        p.tile_s[((size_t)k * 2) * p.tiles + tl] = s;
-      }
-      if (nk > 0) {
-        tile_stats(p, sm, zq, tl, &m, &s, &bad);
-        if (t == 0) {
-          p.tile_m[((size_t)k * 2 + 1) * p.tiles + tl] = m;
-          p.tile_s[((size_t)k * 2 + 1) * p.tiles + tl] = s;
-        }
-      }
-    }
-    if (block_or<kVThreads>(bad, sm.red_i) && t == 0) atomicOr(&p.node_flags[k], TV_REQ_NONFINITE);
-    int phase = 1;
-    team_barrier(p, sm, k, phase++);
-    // stage every member's tile statistics into LDS (one parallel round trip)
-    for (int i = t; i < 2 * p.tiles; i += kVThreads) {
-      const int r = i / p.tiles, tl = i % p.tiles;
-      if (r == 0 || nk > 0) {
-        sm.tm[r][tl] = p.tile_m[((size_t)k * 2 + r) * p.tiles + tl];
-        sm.ts[r][tl] = p.tile_s[((size_t)k * 2 + r) * p.tiles + tl];
-      }
-    }
-    __syncthreads();
-
-    // row maxima and normalisers (every member, same order -> same values)
-    float Mp = kNegInf, Mq = kNegInf;
-    for (int tl = 0; tl < p.tiles; ++tl) {
-      Mp = fmaxf(Mp, sm.tm[0][tl]);
-      if (nk > 0) Mq = fmaxf(Mq, sm.tm[1][tl]);
-    }
-    double Sp = 0.0, Sq = 0.0;
-    for (int tl = 0; tl < p.tiles; ++tl) {
-      Sp += sm.ts[0][tl] * exp((double)(sm.tm[0][tl] - Mp) * p.invT_d);
-      if (nk > 0) Sq += sm.ts[1][tl] * exp((double)(sm.tm[1][tl] - Mq) * p.invT_d);
-    }
-    const double ip = 1.0 / Sp, iq = nk > 0 ? 1.0 / Sq : 0.0;
-    const double lse_p = (double)Mp * p.invT_d + log(Sp);
-    const double lse_q = nk > 0 ? (double)Mq * p.invT_d + log(Sq) : 0.0;
-
-    // decisions along the children, one vocabulary pass per rejection
-    double Cres = 0.0, Dres = 1.0;
-    int cur_buf = -1, buf = 0, accepted = -1;
-    for (int i = 0; i < nk; ++i) {
-      const int c = sm.kids[i];
-      const int x = tok[c];
-      if (flags & TV_REQ_BAD_TOKEN) break;
-      const double px = exp((double)zp[x] * p.invT_d - lse_p);
-      const double qx = exp((double)zq[x] * p.invT_d - lse_q);
-      const double ua = (double)p.u_accept[(size_t)b * p.n_max + c];
-      if (ua * qx * Dres <= fmax(px - Cres * qx, 0.0)) {
-        accepted = c;
-        break;
-      }
-      const double cn = Cres + Dres;
-      for (int tl = my_t0; tl < my_t1; ++tl) {
-        const int e0 = tl * kTileElems + 16 * t;
-        float xp[16], xq[16];
-        load16(zp, p.V, p.V, e0, xp);
-        load16(zq, p.V, p.V, e0, xq);
-        double w[16];
-        residual16(p, xp, xq, e0, Mp, Mq, ip, iq, cn, w);
-        double s = 0.0;
+  // chunk statistics of this member's slice (batch_stats synchronises first)
+  for (int j0 = 0; j0 < nmine; j0 += kResident) {
+    if (j0 > 0) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s += w[j];
-        s = block_sum_d<kVThreads>(s, sm.red_d);
-        if (t == 0) p.tile_f[((size_t)k * 3 + buf) * p.tiles + tl] = s;
+      for (int r = 0; r < kResident; ++r) {
+        const int e0 = (my_c0 + min(j0 + r, nmine - 1)) * kChunk + 16 * t;
+        load16(zp_rs, p.V, e0, ep[r]);
+        if (internal) load16(zq_rs, p.V, e0, eq[r]);
       }
-      team_barrier(p, sm, k, phase++);
-      for (int i = t; i < p.tiles; i += kVThreads) sm.tf[i] = p.tile_f[((size_t)k * 3 + buf) * p.tiles + i];
-      __syncthreads();
-      double F = 0.0;
-      for (int tl = 0; tl < p.tiles; ++tl) F += sm.tf[tl];
-      // Z > 0: move to the new residual.  The next pass writes a buffer that is
-      // neither the one just summed (a slower member may still be reading it)
-      // nor the one holding the current residual's tile masses.
-      const int just = buf;
-      if (F > 0.0) {
-        Cres = cn;
-        Dres = F;
-        cur_buf = buf;
-        __syncthreads();
-        for (int i = t; i < p.tiles; i += kVThreads) sm.tcur[i] = sm.tf[i];
-      }
-      buf = 0;
-      while (buf == just || buf == cur_buf) ++buf;
     }
+    batch_stats(sm, ep, eq, min(kResident, nmine - j0), internal, my_c0, j0, p.V, p.k2hi, p.k2lo);
+  }
+  if (kRes && internal) {   // each thread later reads back only its own entries
+#pragma unroll
+    for (int r = 0; r < kResident; ++r)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        sm.qe[(r * 4 + g) * kSThreads + t] = tv_f32x4{eq[r][4 * g], eq[r][4 * g + 1], eq[r][4 * g + 2], eq[r][4 * g + 3]};
+  }
+  const int nk = sm.nk;
+  int badtok = 0;
+  if (t < nk) {   // tokens proposed by the children, and what their accept tests read
+    const int c = sm.kids[t];
+    const int x = tok[c];
+    badtok = (x < 0 || x >= p.V);
+    const int xs = badtok ? 0 : x;
+    sm.kzp[t] = zp_row[xs];
+    sm.kzq[t] = zq_row[xs];
+    sm.kua[t] = p.u_accept[(size_t)b * p.n_max + c];
+  }
+  const int bad = sm.bad;
+  if (bad && t == 0) atomicOr(&p.node_flags[k], TV_REQ_NONFINITE);
 
-    bool writer = (member == 0);
-    int result_tok = -1;
-    if (accepted < 0 && !(flags & TV_REQ_BAD_TOKEN)) {
-      // two-level inverse CDF: tile masses, then a scan inside the selected tile
-      __syncthreads();
-      const double us = (double)p.u_sample[(size_t)b * p.n_max + u];
-      double total = 0.0;
-      for (int tl = 0; tl < p.tiles; ++tl) {
-        double mass = (cur_buf < 0) ? sm.ts[0][tl] * exp((double)(sm.tm[0][tl] - Mp) * p.invT_d) * ip
-                                    : sm.tcur[tl];
-        total += mass;
-      }
-      const double thr = us * total;
-      double cum = 0.0, base = 0.0;
-      int sel = -1, lastpos = 0;
-      for (int tl = 0; tl < p.tiles; ++tl) {
-        double mass = (cur_buf < 0) ? sm.ts[0][tl] * exp((double)(sm.tm[0][tl] - Mp) * p.invT_d) * ip
-                                    : sm.tcur[tl];
-        if (mass > 0.0) lastpos = tl;
-        if (sel < 0 && cum + mass > thr) {
-          sel = tl;
-          base = cum;
-        }
-        cum += mass;
-      }
-      if (sel < 0) {
-        sel = lastpos;
-        base = cum;   // nothing crosses: the scan falls back to the last positive weight
-      }
-      writer = (sel >= my_t0 && sel < my_t1);
-      if (writer) {
-        const int e0 = sel * kTileElems + 16 * t;
-        double w[16];
-        if (cur_buf < 0) {
-          float xp[16];
-          load16(zp, p.V, p.V, e0, xp);
-          const float Mt = sm.tm[0][sel];
-          const double sc = exp((double)(Mt - Mp) * p.invT_d) * ip;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) w[j] = (e0 + j < p.V) ? (double)expf((xp[j] - Mt) * p.invT) * sc : 0.0;
-        } else {
-          float xp[16], xq[16];
-          load16(zp, p.V, p.V, e0, xp);
-          load16(zq, p.V, p.V, e0, xq);
-          residual16(p, xp, xq, e0, Mp, Mq, ip, iq, Cres, w);
-        }
-        double loc = 0.0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) loc += w[j];
-        // exclusive scan of the per-thread totals (wave scan, then across waves)
-        const int wv = t >> 6, ln = t & 63;
-        double incl = loc;
-        for (int o = 1; o < 64; o <<= 1) {
-          double y = __shfl_up(incl, o);
-          if (ln >= o) incl += y;
-        }
-        __syncthreads();
-        if (ln == 63) sm.scan[wv] = incl;
-        __syncthreads();
-        double pre = base;
-        for (int i2 = 0; i2 < wv; ++i2) pre += sm.scan[i2];
-        pre += incl - loc;
-        int found = 0x7fffffff, lastw = -1;
-        double run = pre;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          run += w[j];
-          if (found == 0x7fffffff && w[j] > 0.0 && run > thr) found = e0 + j;
-          if (w[j] > 0.0) lastw = e0 + j;
-        }
-        if (t == 0) {
-          sm.sel = 0x7fffffff;
-          sm.last = -1;
-        }
-        __syncthreads();
-        if (found != 0x7fffffff) atomicMin(&sm.sel, found);
-        if (lastw >= 0) atomicMax(&sm.last, lastw);
-        __syncthreads();
-        result_tok = (sm.sel != 0x7fffffff) ? sm.sel : (sm.last >= 0 ? sm.last : sel * kTileElems);
-      }
+  // this member's (max, sum) of both rows (wave 0: target, wave 1: draft; the
+  // lanes take chunks l and l + 64), exchanged with the team
+  unsigned long long* sx = p.sxch + (size_t)k * kMaxTeam * 4;
+  if (w < 2) {
+    float M = kNegInf;
+    double S = 0.0;
+    if (w == 0 || internal) {
+      const bool h0 = l < nmine, h1 = l + 64 < nmine;
+      const float m0 = h0 ? sm.cm[w][l] : kNegInf, m1 = h1 ? sm.cm[w][l + 64] : kNegInf;
+      M = tv_wave_max(fmaxf(m0, m1));
+      double e = h0 ? sm.cs[w][l] * exp((double)(m0 - M) * p.invT_d) : 0.0;
+      if (h1) e += sm.cs[w][l + 64] * exp((double)(m1 - M) * p.invT_d);
+      S = tv_wave_sum_d(e);
     }
+    if (l == 0) {
+      const unsigned long long sb = bad ? 0x7FF8000000000000ull : (unsigned long long)__double_as_longlong(S);
+      xch_put(sx + member * 4 + 2 * w, __float_as_uint(M));
+      xch_put(sx + member * 4 + 2 * w + 1, sb);
+    }
+  }
+  if (t < 4 * p.S) {
+    const unsigned long long v = xch_get(sx + t, &sm.timeout);
+    const int mem = t >> 2, row = (t >> 1) & 1;
+    if (t & 1)
+      sm.xs[row][mem] = __longlong_as_double((long long)v);
+    else
+      sm.xm[row][mem] = __uint_as_float((uint32_t)v);
+  }
+  badtok = __syncthreads_or(badtok);
+  if (badtok) {   // the request fails
+    if (member == 0 && t == 0) atomicOr(&p.node_flags[k], TV_REQ_BAD_TOKEN);
+    return;
+  }
+  // team row statistics: lanes 16 r + s of wave 0 combine member s of row r with
+  // a fixed shuffle tree, so every member obtains the same values
+  if (w == 0) {
+    const int row = (l >> 4) & 1, s2 = l & 15;
+    const bool on = l < 32 && s2 < p.S && (row == 0 || internal);
+    const float m = on ? sm.xm[row][s2] : kNegInf;
+    float M = m;
+    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    double e = on ? sm.xs[row][s2] * exp((double)(m - M) * p.invT_d) : 0.0;
+    for (int o = 8; o > 0; o >>= 1) e += __shfl_xor(e, o);
+    if (l == 0 || l == 16) {
+      sm.rowM[row] = M;
+      sm.rowS[row] = e;
+    }
+  }
+  __syncthreads();
+  const float Mp = sm.rowM[0], Mq = sm.rowM[1];
+  const double Sp = sm.rowS[0], Sq = sm.rowS[1];
+  if (!isfinite(Sp) || (internal && !isfinite(Sq))) return;   // some member saw a non-finite logit
+  const double ip = 1.0 / Sp, iq = internal ? 1.0 / Sq : 0.0;
+  const double lse_p = (double)Mp * p.invT_d + log(Sp);
+  const double lse_q = internal ? (double)Mq * p.invT_d + log(Sq) : 0.0;
+  if (t < nmine) {
+    sm.ca[0][t] = exp((double)(sm.cm[0][t] - Mp) * p.invT_d) * ip;
+    sm.ca[1][t] = internal ? exp((double)(sm.cm[1][t] - Mq) * p.invT_d) * iq : 0.0;
+  }
+  __syncthreads();
 
-    // publish the node's result; the last node of the request chases the path
-    __syncthreads();
-    if (writer && t == 0) {
-      if (sm.timeout) flags |= TV_REQ_TIMEOUT;
-      if (flags) atomicOr(&p.node_flags[k], flags);
-      p.acc_child[k] = accepted;
-      p.final_tok[k] = result_tok;
-      __threadfence();
-      int prev = atomicAdd(&p.req_done[b], 1);
-      sm.fin = (prev == n - 1);
+  // children in ascending id, one team-wide evaluation of F per rejection
+  double Cres = 0.0, Dres = 1.0;
+  int accepted = -1, cur = -1;
+  for (int i = 0; i < nk; ++i) {
+    const double px = exp((double)sm.kzp[i] * p.invT_d - lse_p);
+    const double qx = exp((double)sm.kzq[i] * p.invT_d - lse_q);
+    if ((double)sm.kua[i] * qx * Dres <= fmax(px - Cres * qx, 0.0)) {
+      accepted = sm.kids[i];
+      break;
     }
-    __syncthreads();
-    // leave the team counters at zero: the last member to depart resets them
-    if (p.S > 1 && t == 0) {
-      int prev = atomicAdd(&p.depart[k], 1);
-      if (prev == p.S - 1) {
-        p.arrive[k] = 0;
-        p.depart[k] = 0;
-      }
-    }
-    if (writer && sm.fin) {
-      __threadfence();   // acquire: every node of the request has published its result
-      if (t == 0) sm.fflags = 0;
-      __syncthreads();
-      for (int v = t; v < n; v += kVThreads) {
-        const size_t kv = (size_t)b * p.n_max + v;
-        sm.facc[v] = p.acc_child[kv];
-        sm.ffin[v] = p.final_tok[kv];
-        const int pv = par[v];
-        const bool ok = (v == 0) ? (pv == -1) : (pv >= 0 && pv < v);
-        const int fl = p.node_flags[kv] | (ok ? 0 : TV_REQ_BAD_PARENT);
-        if (fl) atomicOr(&sm.fflags, fl);
-        p.node_flags[kv] = 0;
-      }
-      __syncthreads();
-      if (t == 0) {
-        // every flag raised on a row that was read (or a timeout) fails the request
-        const int fl = sm.fflags;
-        if (fl) {
-          p.status[b] = fl;
-          p.path_len[b] = 0;
-        } else {
-          int32_t* path = p.path + (size_t)b * p.n_max;
-          int32_t* out = p.out_tokens + (size_t)b * p.n_max;
-          int cur = 0, j = 0;
-          path[0] = 0;
-          for (;;) {
-            const int ch = sm.facc[cur];
-            if (ch <= cur || ch >= n || j + 1 >= n) break;
-            out[j] = tok[ch];
-            path[++j] = ch;
-            cur = ch;
+    const double cn = Cres + Dres;
+    for (int j0 = 0; j0 < nmine; j0 += kResident) {
+      if (!kRes) {   // re-read the batch and rebuild its exponentials
+#pragma unroll
+        for (int r = 0; r < kResident; ++r) {
+          const int e0 = (my_c0 + min(j0 + r, nmine - 1)) * kChunk + 16 * t;
+          load16(zp_rs, p.V, e0, ep[r]);
+          load16(zq_rs, p.V, e0, eq[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < kResident; ++r) {
+          const int jr = min(j0 + r, nmine - 1);
+          const float mp = sm.cm[0][jr], mq = sm.cm[1][jr];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            ep[r][e] = exp_t(ep[r][e] - mp, p.k2hi, p.k2lo);
+            eq[r][e] = exp_t(eq[r][e] - mq, p.k2hi, p.k2lo);
           }
-          out[j] = sm.ffin[cur];
-          p.path_len[b] = j + 1;
-          p.status[b] = 0;
         }
-        p.req_done[b] = 0;
+      }
+#pragma unroll
+      for (int r = 0; r < kResident; ++r) {
+        if (j0 + r < nmine) {
+          const double a = sm.ca[0][j0 + r], bq = sm.ca[1][j0 + r];
+          double s = 0.0;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const tv_f32x4 q4 = kRes ? sm.qe[(r * 4 + g) * kSThreads + t]
+                                     : tv_f32x4{eq[r][4 * g], eq[r][4 * g + 1], eq[r][4 * g + 2], eq[r][4 * g + 3]};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s += residual_weight(ep[r][4 * g + e], q4[e], a, bq, cn);
+          }
+          s = tv_wave_sum_d(s);
+          if (l == 0) sm.part[w][j0 + r] = s;
+        }
       }
     }
     __syncthreads();
+    if (t < nmine) {
+      double s = 0.0;
+      for (int i2 = 0; i2 < kSThreads / 64; ++i2) s += sm.part[i2][t];
+      sm.rlast[t] = s;
+    }
+    __syncthreads();
+    double mine = 0.0;
+    for (int j = 0; j < nmine; ++j) mine += sm.rlast[j];
+    // publish this member's mass for this rejection, gather the team's
+    unsigned long long* xs = p.xch + ((size_t)b * p.n_max + sm.kids[i]) * kMaxTeam;
+    if (t == 0) xch_put(xs + member, (unsigned long long)__double_as_longlong(mine));
+    if (t < p.S) sm.xv[t] = __longlong_as_double((long long)xch_get(xs + t, &sm.timeout));
+    __syncthreads();
+    double F = 0.0;
+    for (int s = 0; s < p.S; ++s) F += sm.xv[s];
+    if (F > 0.0) {   // Z > 0: move to the new residual
+      Cres = cn;
+      Dres = F;
+      cur = i;
+      if (t < p.S) sm.xcur[t] = sm.xv[t];
+      if (t < nmine) sm.rcur[t] = sm.rlast[t];
+    }
+  }
+
+  if (accepted < 0) {
+    // the node's draw: inverse CDF over member masses, this member's chunk
+    // masses, then inside one chunk; masses are those of p while no rejection
+    // has moved the residual, else of the current residual
+    if (cur < 0) {
+      if (t < p.S) sm.xcur[t] = sm.xs[0][t] * exp((double)(sm.xm[0][t] - Mp) * p.invT_d) * ip;   // parallel over members
+      if (t < nmine) sm.rcur[t] = sm.cs[0][t] * sm.ca[0][t];
+    }
+    __syncthreads();
+    if (t == 0) {
+      double total = 0.0;
+      for (int s = 0; s < p.S; ++s) total += sm.xcur[s];
+      const double thr = (double)us * total;
+      double base = 0.0;
+      const int ms = select_mass(sm.xcur, p.S, thr, &base);
+      sm.owner = ms;
+      if (ms == member) sm.sel = select_mass(sm.rcur, nmine, thr, &base);
+      sm.base = base;
+      sm.thr = thr;
+    }
+    __syncthreads();
+    if (sm.owner == member && nmine > 0) {
+      const int j = min(sm.sel, nmine - 1);
+      const int e0 = (my_c0 + j) * kChunk + 16 * t;
+      const double a = sm.ca[0][j], bq = sm.ca[1][j];
+      const bool res = cur >= 0;
+      double wts[16];
+      if (kRes) {
+        float pe[16], qe[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pe[e] = (j == 0) ? ep[0][e] : ep[kResident - 1][e];
+        if (res) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const tv_f32x4 q4 = sm.qe[(j * 4 + g) * kSThreads + t];
+            qe[4 * g] = q4[0];
+            qe[4 * g + 1] = q4[1];
+            qe[4 * g + 2] = q4[2];
+            qe[4 * g + 3] = q4[3];
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) wts[e] = residual_weight(pe[e], qe[e], a, bq, Cres);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) wts[e] = (double)pe[e] * a;
+        }
+      } else {
+        float xp[16], xq[16];
+        load16(zp_rs, p.V, e0, xp);
+        const float mp = sm.cm[0][j], mq = sm.cm[1][j];
+        if (res) {
+          load16(zq_rs, p.V, e0, xq);
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            wts[e] = residual_weight(exp_t(xp[e] - mp, p.k2hi, p.k2lo), exp_t(xq[e] - mq, p.k2hi, p.k2lo), a, bq, Cres);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) wts[e] = (double)exp_t(xp[e] - mp, p.k2hi, p.k2lo) * a;
+        }
+      }
+      const int y = chunk_draw(sm, wts, e0, sm.base, sm.thr, (my_c0 + j) * kChunk);
+      if (t == 0) p.node_tok[k] = y;
+    }
+  }
+  if (t == 0) {
+    if (member == 0) p.node_acc[k] = accepted;
+    if (sm.timeout) atomicOr(&p.node_flags[k], TV_REQ_TIMEOUT);
+  }
+}
+
+// One workgroup per request: status, the accepted path and its final token,
+// and the exchange slots cleared for the next call.
+__global__ __launch_bounds__(kMaxNodes) void stoch_chase_kernel(StochParams p) {
+  __shared__ int s_acc[kMaxNodes], s_fin[kMaxNodes], s_tok[kMaxNodes];
+  __shared__ int s_flags, s_badpar;
+  const int t = threadIdx.x, b = blockIdx.x;
+  const int n = p.n_nodes[b];
+  if (n < 1 || n > p.n_max) {
+    if (t == 0) {
+      p.status[b] = TV_REQ_BAD_NNODES;
+      p.path_len[b] = 0;
+    }
+    return;
+  }
+  if (t == 0) {
+    s_flags = 0;
+    s_badpar = 0;
+  }
+  __syncthreads();
+  // every exchange slot the node kernel may have written for this request
+  for (int i = t; i < n * kMaxTeam * 4; i += kMaxNodes) p.sxch[(size_t)b * p.n_max * kMaxTeam * 4 + i] = 0ull;
+  for (int i = t; i < n * kMaxTeam; i += kMaxNodes) p.xch[(size_t)b * p.n_max * kMaxTeam + i] = 0ull;
+  if (t < n) {
+    const size_t kv = (size_t)b * p.n_max + t;
+    const int fl = p.node_flags[kv];
+    if (fl) {
+      atomicOr(&s_flags, fl);
+      p.node_flags[kv] = 0;
+    }
+    s_acc[t] = p.node_acc[kv];
+    s_fin[t] = p.node_tok[kv];
+    s_tok[t] = p.tokens[kv];
+    const int pv = p.parent[kv];
+    if (!((t == 0) ? (pv == -1) : (pv >= 0 && pv < t))) s_badpar = 1;
+  }
+  __syncthreads();
+  if (t == 0) {
+    const int fl = s_badpar ? TV_REQ_BAD_PARENT : s_flags;
+    if (fl) {
+      p.status[b] = fl;
+      p.path_len[b] = 0;
+      return;
+    }
+    int32_t* path = p.path + (size_t)b * p.n_max;
+    int32_t* out = p.out_tokens + (size_t)b * p.n_max;
+    int cur = 0, j = 0;
+    path[0] = 0;
+    for (;;) {
+      const int ch = s_acc[cur];
+      if (ch <= cur || ch >= n || j + 1 >= n) break;
+      out[j] = s_tok[ch];
+      path[++j] = ch;
+      cur = ch;
+    }
+    out[j] = s_fin[cur];
+    p.path_len[b] = j + 1;
+    p.status[b] = 0;
   }
 }
 
@@ -666,50 +855,54 @@ int check_vdesc(const tv_verify_desc* d) {
 }
 
 struct VerifyLayout {
-  size_t greedy_val, greedy_idx, greedy_bad, greedy_cnt, greedy_bytes;
-  size_t tm, ts, tf, acc, fin, flg, arr, dep, req, stoch_bytes;
-  int chunks, tiles;
+  size_t g_keys, g_flags, greedy_bytes;
+  size_t xch, sxch, flg, acc, tok, stoch_bytes;
+  int gchunks, chunks;
 };
 
 VerifyLayout layout(const tv_verify_desc* d) {
   VerifyLayout L;
   const size_t nodes = (size_t)d->batch * d->n_max;
-  L.chunks = (d->vocab + kGreedyChunk - 1) / kGreedyChunk;
-  L.tiles = (d->vocab + kTileElems - 1) / kTileElems;
+  L.gchunks = (d->vocab + kGreedyChunk - 1) / kGreedyChunk;
+  L.chunks = (d->vocab + kChunk - 1) / kChunk;
   size_t o = 0;
-  L.greedy_val = o;
-  o = tv_align_up(o + nodes * L.chunks * sizeof(float), 256);
-  L.greedy_idx = o;
-  o = tv_align_up(o + nodes * L.chunks * sizeof(int), 256);
-  L.greedy_bad = o;
-  o = tv_align_up(o + nodes * L.chunks * sizeof(int), 256);
-  L.greedy_cnt = o;
-  o = tv_align_up(o + (size_t)d->batch * sizeof(int), 256);
+  L.g_keys = o;
+  o = tv_align_up(o + nodes * L.gchunks * sizeof(unsigned long long), 256);
+  L.g_flags = o;
+  o = tv_align_up(o + nodes * sizeof(int), 256);
   L.greedy_bytes = o;
   o = 0;
-  L.tm = o;
-  o = tv_align_up(o + nodes * 2 * L.tiles * sizeof(float), 256);
-  L.ts = o;
-  o = tv_align_up(o + nodes * 2 * L.tiles * sizeof(double), 256);
-  L.tf = o;
-  o = tv_align_up(o + nodes * 3 * L.tiles * sizeof(double), 256);
-  L.acc = o;
-  o = tv_align_up(o + nodes * sizeof(int), 256);
-  L.fin = o;
-  o = tv_align_up(o + nodes * sizeof(int), 256);
+  L.xch = o;
+  o = tv_align_up(o + nodes * kMaxTeam * sizeof(unsigned long long), 256);
+  L.sxch = o;
+  o = tv_align_up(o + nodes * kMaxTeam * 4 * sizeof(unsigned long long), 256);
   L.flg = o;
   o = tv_align_up(o + nodes * sizeof(int), 256);
-  L.arr = o;
+  L.acc = o;
   o = tv_align_up(o + nodes * sizeof(int), 256);
-  L.dep = o;
+  L.tok = o;
   o = tv_align_up(o + nodes * sizeof(int), 256);
-  L.req = o;
-  o = tv_align_up(o + (size_t)d->batch * sizeof(int), 256);
   L.stoch_bytes = o;
   return L;
 }
 
-int g_stoch_blocks_per_cu = -1;
+int g_decide_occ[2] = {-1, -1};   // resident workgroups per CU: streaming / register-resident variant
+
+struct TeamPlan {
+  int S;     // workgroups per node
+  int per;   // chunks per member
+};
+
+// Team size: at most kMaxTeam members and at most one per chunk, as many as a
+// grid of `capacity` co-resident workgroups holds with one team per node.
+TeamPlan plan_team(long long nodes, int chunks, long long capacity) {
+  TeamPlan tp;
+  int S = 1;
+  while (S * 2 <= kMaxTeam && S * 2 <= chunks && nodes * S * 2 <= capacity) S *= 2;
+  tp.S = S;
+  tp.per = (chunks + S - 1) / S;
+  return tp;
+}
 
 }  // namespace
 
@@ -741,17 +934,17 @@ extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* targe
   p.path_len = path_len;
   p.out_tokens = out_tokens;
   p.status = status;
-  p.part_val = (float*)((char*)workspace + L.greedy_val);
-  p.part_idx = (int*)((char*)workspace + L.greedy_idx);
-  p.part_bad = (int*)((char*)workspace + L.greedy_bad);
-  p.counters = (int*)((char*)workspace + L.greedy_cnt);
+  p.keys = (unsigned long long*)((char*)workspace + L.g_keys);
+  p.flags = (int*)((char*)workspace + L.g_flags);
   p.B = desc->batch;
   p.n_max = desc->n_max;
   p.V = desc->vocab;
-  p.chunks = L.chunks;
-  long long grid = (long long)desc->batch * desc->n_max * L.chunks;
+  p.chunks = L.gchunks;
+  const long long grid = (long long)desc->batch * desc->n_max * L.gchunks;
   if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)grid), dim3(kGreedyThreads), 0, stream, p);
+  hipLaunchKernelGGL(greedy_argmax_kernel, dim3((unsigned)grid), dim3(kGreedyThreads), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  hipLaunchKernelGGL(greedy_chase_kernel, dim3((unsigned)desc->batch), dim3(kMaxNodes), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
@@ -769,25 +962,25 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
     return TV_ERR_INVALID_ARG;
   if ((((uintptr_t)target_logits | (uintptr_t)draft_logits) & 15) != 0) return TV_ERR_INVALID_ARG;
   VerifyLayout L = layout(desc);
-  if (L.tiles > kMaxTiles) return TV_ERR_UNSUPPORTED;
+  if (L.chunks > kMaxChunks) return TV_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < L.stoch_bytes) return TV_ERR_WORKSPACE;
+  const long long nodes = (long long)desc->batch * desc->n_max;
   int cu = 0;
   rc = tv_device_cu_count(&cu);
   if (rc != TV_OK) return rc;
-  if (g_stoch_blocks_per_cu < 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, stochastic_kernel, kVThreads, 0) != hipSuccess)
+  if (g_decide_occ[0] < 0) {
+    int nb0 = 0, nb1 = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb0, stoch_node_kernel<false>, kSThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb1, stoch_node_kernel<true>, kSThreads, 0) != hipSuccess)
       return TV_ERR_HIP;
-    g_stoch_blocks_per_cu = nb < 1 ? 1 : nb;
+    g_decide_occ[1] = nb1 < 1 ? 1 : nb1;
+    g_decide_occ[0] = nb0 < 1 ? 1 : nb0;
   }
-  const long long capacity = (long long)g_stoch_blocks_per_cu * cu;
-  const long long nodes = (long long)desc->batch * desc->n_max;
-  // team size: enough members to fill the grid, at most one tile each, at most 16
-  int S = 1;
-  while (S * 2 <= 16 && S * 2 <= L.tiles && nodes * S * 2 <= capacity) S *= 2;
-  long long slots = capacity / S;
-  if (slots > nodes) slots = nodes;
-  if (slots < 1) slots = 1;
+  // Prefer the register-resident variant when its resident grid gives every
+  // member at most kResident chunks; otherwise members stream their slices.
+  TeamPlan tp = plan_team(nodes, L.chunks, (long long)g_decide_occ[1] * cu);
+  const bool resident = tp.per <= kResident;
+  if (!resident) tp = plan_team(nodes, L.chunks, (long long)g_decide_occ[0] * cu);
 
   StochParams p;
   p.target = target_logits;
@@ -802,25 +995,29 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
   p.out_tokens = out_tokens;
   p.status = status;
   char* ws = (char*)workspace;
-  p.tile_m = (float*)(ws + L.tm);
-  p.tile_s = (double*)(ws + L.ts);
-  p.tile_f = (double*)(ws + L.tf);
-  p.acc_child = (int*)(ws + L.acc);
-  p.final_tok = (int*)(ws + L.fin);
+  p.xch = (unsigned long long*)(ws + L.xch);
+  p.sxch = (unsigned long long*)(ws + L.sxch);
   p.node_flags = (int*)(ws + L.flg);
-  p.arrive = (int*)(ws + L.arr);
-  p.depart = (int*)(ws + L.dep);
-  p.req_done = (int*)(ws + L.req);
+  p.node_acc = (int*)(ws + L.acc);
+  p.node_tok = (int*)(ws + L.tok);
   p.B = desc->batch;
   p.n_max = desc->n_max;
   p.V = desc->vocab;
-  p.tiles = L.tiles;
-  p.S = S;
-  p.slots = (int)slots;
-  p.invT = 1.0f / desc->temperature;
+  p.chunks = L.chunks;
+  p.S = tp.S;
+  p.per = tp.per;
   p.invT_d = 1.0 / (double)desc->temperature;
-  void* args[] = {&p};
-  hipError_t e = hipLaunchCooperativeKernel((const void*)stochastic_kernel, dim3((unsigned)(slots * S)),
-                                            dim3(kVThreads), args, 0, stream);
-  return e == hipSuccess ? TV_OK : TV_ERR_HIP;
+  const double k2 = 1.4426950408889634074 * p.invT_d;   // log2(e) / T
+  p.k2hi = (float)k2;
+  p.k2lo = (float)(k2 - (double)p.k2hi);
+
+  const long long grid = nodes * tp.S;
+  if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  if (resident)
+    hipLaunchKernelGGL(stoch_node_kernel<true>, dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(stoch_node_kernel<false>, dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kMaxNodes), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
