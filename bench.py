@@ -47,8 +47,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="after timing, run one device-to-device copy of this many MiB (a reference "
+                    help="after timing, run one elementwise copy of this many MiB (a reference "
                          "kernel of known traffic for hardware byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE, both with --calibrate-copy-mib) into profiles/traffic_*.json")
     return ap.parse_args()
 
 
@@ -75,8 +78,69 @@ def traffic_record(kernel: str, workload: str, src_hash: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+# kernels launched by each entry point (rocprofv3 kernel names contain these)
+ENTRY_KERNELS = {
+    "tree_attn": ("tree_attn_kernel", "attn_merge_kernel"),
+    "tree_verify_stochastic": ("stoch_node_kernel", "stoch_chase_kernel"),
+    "tree_verify_greedy": ("greedy_argmax_kernel", "greedy_chase_kernel"),
+    "kv_compact": ("compact_kernel",),
+}
+ENTRY_SOURCES = {"tree_attn": ("tree_attn.hip",), "tree_verify_stochastic": ("tree_verify.hip",),
+                 "tree_verify_greedy": ("tree_verify.hip",), "kv_compact": ("kv_compact.hip",)}
+CALIB_KERNEL = "elementwise"
+
+
+def read_counters(run_dir: str, counter: str):
+    """(kernel name, value) per dispatch for one counter from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name") == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, v) for _, k, v in rows]
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, calib_mib: int):
+    out = {}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = read_counters(d, counter)
+        calib = [v for k, v in rows if CALIB_KERNEL in k]
+        if not calib:
+            raise SystemExit(f"no calibration kernel among the {counter} dispatches in {d}")
+        scale = (calib_mib << 20) / (calib[-1] * 1024.0)   # counter KiB -> bytes
+        per[counter] = {"calibration_kib": calib[-1], "bytes_per_kib": scale}
+        for entry, names in ENTRY_KERNELS.items():
+            first = [v for k, v in rows if names[0] in k]
+            if not first:
+                continue
+            tot = sum(v for k, v in rows if any(nm in k for nm in names))
+            out.setdefault(entry, {})[counter] = tot * 1024.0 * scale / len(first)
+            out[entry]["launches"] = len(first)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for entry, rec in out.items():
+        if "FETCH_SIZE" not in rec or "WRITE_SIZE" not in rec:
+            continue
+        doc = {"entry_point": entry, "workload": workload, "kernels": list(ENTRY_KERNELS[entry]),
+               "source_hash": source_hash(*ENTRY_SOURCES[entry]),
+               "fetch_bytes_per_launch": round(rec["FETCH_SIZE"]), "write_bytes_per_launch": round(rec["WRITE_SIZE"]),
+               "hbm_bytes_per_launch": round(rec["FETCH_SIZE"] + rec["WRITE_SIZE"]),
+               "launches_counted": rec["launches"], "calibration": per,
+               "method": "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of bench.py, each counter "
+                         f"scaled by its reading for a {calib_mib} MiB elementwise copy"}
+        path = os.path.join(ROOT, "profiles", f"traffic_{entry}_{workload}.json")
+        json.dump(doc, open(path, "w"), indent=1)
+        print(path, doc["hbm_bytes_per_launch"])
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, args.calibrate_copy_mib or 256)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -173,11 +237,31 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
     # ---- per-kernel timing (back-to-back calls on rotating copies) ----------
+    # A spin kernel holds the stream while the host enqueues all calls, so the
+    # events bracket GPU execution only (small entry points are otherwise
+    # limited by the host's launch rate).
+    def spin_cycles_per_s():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(20_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        return 20_000_000 / (a.elapsed_time(b) * 1e-3)
+
+    cyc_per_s = spin_cycles_per_s()
+
     def time_calls(fn, reps):
         for i in range(min(reps, 5)):
             fn(copies[i % ncopies])
         torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for i in range(reps):
+            fn(copies[i % ncopies])
+        host_s = time.perf_counter() - h0
+        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(cyc_per_s * (2.0 * host_s + 2e-3)))
         a.record()
         for i in range(reps):
             fn(copies[i % ncopies])
@@ -218,7 +302,9 @@ def main():
             kids = [c for c in range(1, nb) if par[c] == u]
             passes += kids.index(pth[j + 1]) if j + 1 < L else len(kids)
     row = V * 4
-    verify_bytes = int(n.sum() * row + internal * row + passes * 2 * row)
+    # every target row is read (status checks and draws) and the draft row of
+    # every node with children; rejections re-use the rows held on chip
+    verify_bytes = int(n.sum() * row + internal * row)
     greedy_bytes = int(n.sum() * row)
     compact_bytes = int(2 * 2 * plen0.astype(np.int64).sum() * Hkv * D * esize)
 
@@ -234,22 +320,21 @@ def main():
     for k in kernels.values():
         k["frac_hbm"] = k["GBps"] / HBM_PEAK_GBS
     dominant = max(kernels, key=lambda k: kernels[k]["us"])
-    src = {"tree_attn": ("tree_attn.hip",), "tree_verify_stochastic": ("tree_verify.hip",),
-           "kv_compact": ("kv_compact.hip",)}
 
     def roofline(name):
         k = kernels[name]
         return {"kernel": name, "bound": "hbm", "achieved": round(k["GBps"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(k["GBps"] / HBM_PEAK_GBS, 4),
-                "traffic": traffic_record(name, args.config, source_hash(*src[name])),
+                "traffic": traffic_record(name, args.config, source_hash(*ENTRY_SOURCES[name])),
                 "algorithmic_bytes_per_launch": k["bytes"], "avg_launch_us": round(k["us"], 3)}
 
     if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib << 20
-        src_buf = torch.empty(n, dtype=torch.uint8, device=dev)
+        # a plain elementwise kernel that reads and writes exactly this many bytes
+        nf = (args.calibrate_copy_mib << 20) // 4
+        src_buf = torch.ones(nf, dtype=torch.float32, device=dev)
         dst_buf = torch.empty_like(src_buf)
         torch.cuda.synchronize()
-        dst_buf.copy_(src_buf)
+        torch.mul(src_buf, 1.0, out=dst_buf)
         torch.cuda.synchronize()
         del src_buf, dst_buf
 
@@ -284,6 +369,7 @@ def main():
                    "GBps": round(gbs(greedy_bytes, us_greedy), 1),
                    "nodes_per_s": n_total / (us_greedy * 1e-6)},
         "accepted_mean": float(plen0.mean() - 1),
+        "rejection_passes_on_path": passes,
         "cpu_baseline": cpu,
         "input_generation_s": round(gen_s, 2),
     }
