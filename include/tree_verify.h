@@ -19,12 +19,14 @@
  *     status has unspecified outputs but is never read or written out of
  *     bounds.
  *   - `workspace` is caller-owned device scratch of at least the size the
- *     matching *_workspace_size() returns for the call's descriptor.  Its
- *     layout depends on the descriptor: it must be zero-filled before its first
- *     use with a given descriptor (and again before reuse with another one);
- *     every call leaves its counters at zero again, so repeated calls with the
- *     same descriptor need no clearing.  Two calls that may run concurrently
- *     must use distinct workspaces.
+ *     matching *_workspace_size() returns for the call's descriptor.  The
+ *     verifiers' workspaces hold exchange slots and flags whose layout depends
+ *     on the descriptor: zero-fill them before their first use with a given
+ *     descriptor (and again before reuse with another one); every call leaves
+ *     them at zero again, so repeated calls with the same descriptor need no
+ *     clearing.  The attention workspace holds only per-call partial results
+ *     and needs no initialisation.  Two calls that may run concurrently must
+ *     use distinct workspaces.
  *   - Node ids: a tree of n nodes is a parent array with parent[0] = -1 (node 0
  *     is the root: the last token already emitted) and 0 <= parent[i] < i.
  *     Rows are padded to n_max; padding rows are neither read nor written.
@@ -119,6 +121,9 @@ typedef struct tv_verify_desc {
  *   out_tokens [B][n_max] the L accepted tokens, then one correction/bonus token
  *                         ([chapter] "Worked Example ...": a round emits K + 1)
  *   status [B]            TV_REQ_* flags (required)
+ * Teams of workgroups that cooperate on one node wait on each other through
+ * bounded spins; if a wait expires (other work holding the GPU for a long
+ * time) the request gets TV_REQ_TIMEOUT instead of hanging.
  * Entries past path_len are not written. */
 
 /* Bytes of workspace either verifier needs for `desc`.  The two verifiers lay

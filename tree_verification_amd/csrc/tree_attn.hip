@@ -8,23 +8,26 @@
 // Decomposition.  The query rows of one (request, KV head) pair are the n*G
 // (node, head-in-group) combinations; they all share the same keys, so the
 // prefix part is a dense contraction.  A workgroup owns a tile of rows and a
-// contiguous key range (split-K over the prefix, FlashDecoding-style).  When a
-// pair needs several key splits, every workgroup writes its (m, l, O) partial
-// to the workspace and the last one to arrive on the tile merges them by
-// log-sum-exp and writes the output (no second kernel).
+// contiguous key range (split-K over the prefix, FlashDecoding-style), one
+// workgroup per CU.  A workgroup that owns all keys of its tile writes the
+// output directly; otherwise it writes its (m, l, O) partial to the workspace
+// and attn_merge_kernel combines the splits of each row by log-sum-exp (a
+// kernel boundary orders the hand-off, so no workgroup waits on a fence).
 //
-// MFMA path (bf16, >= 16 rows): 32-key chunks of K and V stream from HBM into a
-// six-slot LDS ring through asynchronous global->LDS loads issued five chunks
-// ahead, so roughly 80 KB per CU are in flight.  Each lane's DMA fetches
-// exactly the 16 bytes it later feeds to v_mfma_f32_16x16x32_bf16, so operands
-// come back with conflict-free ds_read_b128.  The four waves share every chunk
-// and own disjoint 16*NTW-row slices of the tile:
+// MFMA path (bf16, >= 16 rows): 32-key chunks of K and V move in batches of
+// NB chunks: while one batch is computed from LDS, the next is in flight in
+// registers (about 64 KB per CU), then stored to LDS between two LDS-only
+// barriers.  Each lane stores exactly the 16 bytes it later feeds to
+// v_mfma_f32_16x16x32_bf16, so operands come back with conflict-free
+// ds_read_b128.  The four waves share every chunk and own disjoint 16*NTW-row
+// slices of the tile:
 //   S^T[key][row] = K Q^T  then  O^T[d][row] += V^T P^T,
 // laid out so that a lane always owns one query row (lane % 16): the softmax
 // state is lane-local, and the C layout of S^T feeds the B operand of the PV
 // product without cross-lane moves.  Values are stored transposed per block
 // ([D][block] per head) so the PV operand (8 consecutive keys of one d) is a
-// single 16-byte piece.
+// single 16-byte piece.  The running max moves only when a row's max grows by
+// more than 8 (log2 units), which keeps most chunks free of rescaling.
 //
 // VALU path (fewer than 16 rows, or fp32): the waves interleave 64-key chunks
 // with lane = key for the scores and lane = d for PV, merged in LDS.
@@ -37,11 +40,6 @@
 
 #include <math.h>
 #include <mutex>
-
-// s_waitcnt immediate that waits until at most n vector-memory operations are
-// outstanding (gfx9 encoding: vmcnt[3:0] and [15:14], expcnt[6:4] = 7 and
-// lgkmcnt[11:8] = 15 mean "no wait").
-#define TV_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0xF70)
 
 namespace {
 
