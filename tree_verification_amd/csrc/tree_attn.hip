@@ -659,8 +659,7 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
       }
       float rmax = fmaxf(fmaxf(fmaxf(sc[nt][0][0], sc[nt][0][1]), fmaxf(sc[nt][0][2], sc[nt][0][3])),
                          fmaxf(fmaxf(sc[nt][1][0], sc[nt][1][1]), fmaxf(sc[nt][1][2], sc[nt][1][3])));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+      rmax = tv_rows_max(rmax);
       const float cmax = rmax * p.scale_log2;   // -inf stays -inf
       const bool move = cmax > m_run[nt] + kLazy || (m_run[nt] == kNegInf && cmax != kNegInf);
       const float m_ref = move ? cmax : m_run[nt];
@@ -698,8 +697,7 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     float lt = l_run[nt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    lt = tv_rows_sum(lt);
     const int qrow = rbase + 16 * nt + l16;
     if (qrow >= R) continue;
     if (n_active == 1) {

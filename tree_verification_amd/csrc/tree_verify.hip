@@ -184,10 +184,7 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_argmax_kernel(GreedyPar
       best = ky > best ? ky : best;
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long ob = __shfl_xor(best, o);
-    best = ob > best ? ob : best;
-  }
+  best = tv_wave_max_u64(best);
   __shared__ unsigned long long s_best[kGreedyThreads / 64];
   const unsigned long long anybad = __ballot(bad != 0);
   if (l == 0) {
@@ -618,10 +615,8 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4))) 
     const int row = (l >> 4) & 1, s2 = l & 15;
     const bool on = l < 32 && s2 < p.S && (row == 0 || internal);
     const float m = on ? sm.xm[row][s2] : kNegInf;
-    float M = m;
-    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    double e = on ? sm.xs[row][s2] * exp((double)(m - M) * p.invT_d) : 0.0;
-    for (int o = 8; o > 0; o >>= 1) e += __shfl_xor(e, o);
+    const float M = tv_row16_max(m);
+    const double e = tv_row16_sum_d(on ? sm.xs[row][s2] * exp((double)(m - M) * p.invT_d) : 0.0);
     if (l == 0 || l == 16) {
       sm.rowM[row] = M;
       sm.rowS[row] = e;

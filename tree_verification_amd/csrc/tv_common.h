@@ -37,19 +37,106 @@ __device__ __forceinline__ uint16_t tv_f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float tv_wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// Full-wave butterflies without LDS traffic: four DPP patterns inside each row
+// of 16 lanes (quad swaps, half-row and row mirrors), then the row swaps of
+// v_permlane16_swap / v_permlane32_swap.  Every lane ends with the same value,
+// combined in the same order (each step pairs a with b and b with a), so the
+// result does not depend on the lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t tv_dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t tv_wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, tv_dpp<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, tv_dpp<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, tv_dpp<0x141>(v));   // row_half_mirror
+  v = op(v, tv_dpp<0x140>(v));   // row_mirror
+  auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r16[0], r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r32[0], r32[1]);
+}
+
+template <class Op>
+__device__ __forceinline__ uint64_t tv_wave_reduce_u64(uint64_t v, Op op) {
+  auto step = [&](uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; };
+  v = op(v, step(tv_dpp<0xB1>((uint32_t)v), tv_dpp<0xB1>((uint32_t)(v >> 32))));
+  v = op(v, step(tv_dpp<0x4E>((uint32_t)v), tv_dpp<0x4E>((uint32_t)(v >> 32))));
+  v = op(v, step(tv_dpp<0x141>((uint32_t)v), tv_dpp<0x141>((uint32_t)(v >> 32))));
+  v = op(v, step(tv_dpp<0x140>((uint32_t)v), tv_dpp<0x140>((uint32_t)(v >> 32))));
+  {
+    auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    v = op(step(lo[0], hi[0]), step(lo[1], hi[1]));
+  }
+  {
+    auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    v = op(step(lo[0], hi[0]), step(lo[1], hi[1]));
+  }
   return v;
 }
 
-__device__ __forceinline__ double tv_wave_sum_d(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ float tv_wave_max(float v) {
+  return __uint_as_float(tv_wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    const float x = __uint_as_float(a), y = __uint_as_float(b);
+    return __float_as_uint(x > y ? x : y);
+  }));
 }
 
 __device__ __forceinline__ float tv_wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return __uint_as_float(tv_wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+
+__device__ __forceinline__ double tv_wave_sum_d(double v) {
+  return __longlong_as_double((long long)tv_wave_reduce_u64((uint64_t)__double_as_longlong(v), [](uint64_t a, uint64_t b) {
+    return (uint64_t)__double_as_longlong(__longlong_as_double((long long)a) + __longlong_as_double((long long)b));
+  }));
+}
+
+// Reductions inside each row of 16 lanes (every lane of a row gets its row's result).
+__device__ __forceinline__ float tv_row16_max(float v) {
+  auto mx = [](float a, float b) { return a > b ? a : b; };
+  v = mx(v, __uint_as_float(tv_dpp<0xB1>(__float_as_uint(v))));
+  v = mx(v, __uint_as_float(tv_dpp<0x4E>(__float_as_uint(v))));
+  v = mx(v, __uint_as_float(tv_dpp<0x141>(__float_as_uint(v))));
+  return mx(v, __uint_as_float(tv_dpp<0x140>(__float_as_uint(v))));
+}
+
+__device__ __forceinline__ double tv_row16_sum_d(double v) {
+  auto part = [](double x, auto sel) {
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    return __longlong_as_double((long long)(((uint64_t)sel((uint32_t)(b >> 32)) << 32) | sel((uint32_t)b)));
+  };
+  v += part(v, [](uint32_t x) { return tv_dpp<0xB1>(x); });
+  v += part(v, [](uint32_t x) { return tv_dpp<0x4E>(x); });
+  v += part(v, [](uint32_t x) { return tv_dpp<0x141>(x); });
+  v += part(v, [](uint32_t x) { return tv_dpp<0x140>(x); });
   return v;
+}
+
+// Combine the four rows of 16 lanes (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float tv_rows_max(float v) {
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+__device__ __forceinline__ float tv_rows_sum(float v) {
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// Unsigned 64-bit maximum over the wave.
+__device__ __forceinline__ unsigned long long tv_wave_max_u64(unsigned long long v) {
+  return tv_wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 
 // Acquire/release helpers for inter-workgroup hand-offs through global memory.
