@@ -93,8 +93,9 @@ struct CommonSmem {
   int flag;
 };
 
-// Chunks per batch: NTW = 2 keeps 4 in flight; NTW = 1 runs two workgroups
-// per CU (2 chunks each) and NTW = 4 is compute-bound (2 suffice).
+// Chunks per batch.  More in flight does not help NTW = 1 (its waves are
+// bound by the latency of the MFMA / softmax chain, not by loads) and costs
+// LDS; NTW = 2 keeps four; NTW = 4 is compute-bound and two suffice.
 template <int D, int NTW>
 struct RingSmem {
   static constexpr int NB = NTW == 2 ? kMaxBatch : 2;
@@ -486,13 +487,6 @@ __device__ __forceinline__ tv_bf16x8 lds_bf16x8(const unsigned char* ptr) {
 }
 
 
-// Workgroup barrier for the chunk pipeline: LDS operations of this wave
-// complete, then s_barrier.  Unlike __syncthreads() it does not wait for
-// outstanding global loads, which keeps the prefetched chunks in flight.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // This wave's share of one 32-key chunk: operand blocks wave, wave+4, ... of
 // the chunk (1 KB each, 16 bytes per lane), loaded into registers.  Keys past
 // k_end are redirected to key k_begin (always valid) and masked later.
@@ -556,7 +550,8 @@ __device__ __forceinline__ void store_chunk(unsigned char* slot, const ChunkRegs
 
 template <bool kBF16, int D, int NTW>
 __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, CommonSmem& cm, RingSmem<D, NTW>& sm,
-                                                         const tv_bf16x8 (&qop)[NTW][D / 32], int tile, int split,
+                                                         const tv_bf16x8 (&qop)[NTW][D / 32],
+                                                         ChunkRegs<D> (&cr)[RingSmem<D, NTW>::NB], int tile, int split,
                                                          int n_active, int b, int g, int r0, int R, int P,
                                                          int k_begin, int k_end, int tab0, bool tree_in_range) {
   constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT, RW = 64 * NTW;
@@ -584,17 +579,13 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
     for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
   }
   // Chunks move in batches of NB: while a batch is computed from LDS, the next
-  // batch is in flight in registers (about 64 KB per CU).  Loads never stay
-  // pending across more than one batch, which keeps the compiler's wait counts
-  // exact (no drain of younger loads).
+  // batch is in flight in registers.  The first batch was issued in the
+  // prologue.  Loads never stay pending across more than one batch, which keeps
+  // the compiler's wait counts exact (no drain of younger loads).
   constexpr int NB = RingSmem<D, NTW>::NB;
-  ChunkRegs<D> cr[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-    if (i < nchunks) load_chunk<D>(p, sm.tab, tab0, cr[i], k_begin + 32 * i, k_begin, k_end, wave, lane);
 
   for (int c0 = 0; c0 < nchunks; c0 += NB) {
-    ring_barrier();   // every wave has finished the previous batch: its LDS slots are free
+    tv_lds_barrier();   // every wave has finished the previous batch: its LDS slots are free
 #pragma unroll
     for (int ib = 0; ib < NB; ++ib)
       if (c0 + ib < nchunks) store_chunk<D>(sm.ring[ib], cr[ib], k_begin + 32 * (c0 + ib), k_end, wave, lane);
@@ -602,7 +593,7 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
     for (int ib = 0; ib < NB; ++ib)
       if (c0 + NB + ib < nchunks)
         load_chunk<D>(p, sm.tab, tab0, cr[ib], k_begin + 32 * (c0 + NB + ib), k_begin, k_end, wave, lane);
-    ring_barrier();   // the batch is in LDS
+    tv_lds_barrier();   // the batch is in LDS
 #pragma unroll
   for (int ib = 0; ib < NB; ++ib) {
     const int c = c0 + ib;
@@ -775,13 +766,36 @@ __global__ __launch_bounds__(kThreads, (kBF16 && NTW == 1) ? 2 : 1) void tree_at
     if (designated && t == 0 && p.status) p.status[b] = flags;
     return;
   }
+  const int R = n * p.G;
+  const int r0 = rt * RW;
+  const int keys_total = P + n;
+  const int n_active = (keys_total + p.keys_per_split - 1) / p.keys_per_split;
+  const bool works = r0 < R && split < n_active;
+  const int k_end = min(k_begin + p.keys_per_split, keys_total);
+
+  // MFMA path: the first batch of K/V chunks goes out now, so its latency
+  // overlaps the rest of the prologue (the sizes are valid, so every key and
+  // block-table index stays inside this split's staged table); the barriers
+  // below are LDS-only and leave it in flight
+  constexpr int NBR = RingSmem<D, NTW>::NB;
+  ChunkRegs<D> cr[kBF16 ? NBR : 1];
+  const bool ring = kBF16 && works && R >= 16;
+  if constexpr (kBF16) {
+    if (ring) {
+      const int nchunks = (k_end - k_begin + 31) / 32;
+#pragma unroll
+      for (int i = 0; i < NBR; ++i)
+        if (i < nchunks) load_chunk<D>(p, u.r.tab, tab0, cr[i], k_begin + 32 * i, k_begin, k_end, t >> 6, t & 63);
+    }
+  }
+
   // parent array: parent[0] = -1 and 0 <= parent[i] < i
   if (t < n) {
     const int pi = cm.par[t];
     const bool ok = (t == 0) ? (pi == -1) : (pi >= 0 && pi < t);
     if (!ok) cm.flag = 1;
   }
-  __syncthreads();
+  tv_lds_barrier();
   if (cm.flag) {
     if (designated && t == 0 && p.status) p.status[b] = TV_REQ_BAD_PARENT;
     return;
@@ -793,24 +807,16 @@ __global__ __launch_bounds__(kThreads, (kBF16 && NTW == 1) ? 2 : 1) void tree_at
       if (!block_ok(trow[i], p.num_blocks)) cm.flag = 1;
     __syncthreads();
     if (t == 0 && p.status) p.status[b] = cm.flag ? TV_REQ_BAD_KV : 0;
-    // keep going: loads from bad blocks are redirected or skipped, and the
-    // other workgroups of this tile count on this one in the split-K hand-off
+    // keep going: loads from bad blocks are redirected or skipped
   }
-
-  const int R = n * p.G;
-  const int r0 = rt * RW;
-  if (r0 >= R) return;
-  const int keys_total = P + n;
-  const int n_active = (keys_total + p.keys_per_split - 1) / p.keys_per_split;
-  if (split >= n_active) return;
-  const int k_end = min(k_begin + p.keys_per_split, keys_total);
+  if (!works) return;
   const bool tree_in_range = k_end > P;
   if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
-  __syncthreads();
+  tv_lds_barrier();
 
   if constexpr (kBF16) {
-    if (R >= 16) {
-      attn_ring<kBF16, D, NTW>(p, cm, u.r, qop, tile, split, n_active, b, g, r0, R, P, k_begin, k_end, tab0,
+    if (ring) {
+      attn_ring<kBF16, D, NTW>(p, cm, u.r, qop, cr, tile, split, n_active, b, g, r0, R, P, k_begin, k_end, tab0,
                                tree_in_range);
       return;
     }

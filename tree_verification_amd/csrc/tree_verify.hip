@@ -69,11 +69,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int
   return __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, V * 4, 0x00020000);
 }
 
-// 16 consecutive logits of one thread; elements at or past V read as -inf.  Rows
-// whose length is a multiple of 4 are 16-byte aligned and use 16-byte loads (a
-// 4-vector starting below V then lies wholly inside the row).
-__device__ __forceinline__ void load16(__amdgpu_buffer_rsrc_t rs, int V, int e0, float* x) {
-  if ((V & 3) == 0) {
+// Issue the loads of 16 consecutive logits of one thread (elements past the
+// row's end read as 0; callers mask them by index where the values are used).
+// Nothing here consumes the data, so consecutive calls keep all their loads in
+// flight together.  kVec: rows are 16-byte aligned (V a multiple of 4), so
+// 16-byte loads are used and a 4-vector starting below V lies wholly inside
+// the row.
+template <bool kVec>
+__device__ __forceinline__ void load16(__amdgpu_buffer_rsrc_t rs, int e0, float* x) {
+  if (kVec) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const tv_f32x4 a = __builtin_bit_cast(tv_f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * e0 + 16 * i, 0, 0));
@@ -86,8 +90,6 @@ __device__ __forceinline__ void load16(__amdgpu_buffer_rsrc_t rs, int V, int e0,
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (e0 + i), 0, 0));
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = (e0 + i < V) ? x[i] : kNegInf;
 }
 
 // Children of u among nodes [1, n) of a parent row, ascending, written by wave 0
@@ -153,6 +155,7 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
   return ((unsigned long long)hi << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
+template <bool kVec>
 __global__ __launch_bounds__(kGreedyThreads) void greedy_argmax_kernel(GreedyParams p) {
   const int t = threadIdx.x, l = t & 63;
   const int c = blockIdx.x % p.chunks;
@@ -164,8 +167,8 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_argmax_kernel(GreedyPar
   const int lo = c * kGreedyChunk, hi = min(p.V, lo + kGreedyChunk);
   const int e0 = lo + 16 * t, e1 = e0 + 16 * kGreedyThreads;
   float x[16], y[16];
-  load16(row, p.V, e0, x);   // both halves issued before either is used
-  load16(row, p.V, e1, y);
+  load16<kVec>(row, e0, x);   // both halves issued before either is used
+  load16<kVec>(row, e1, y);
   unsigned long long best = 0ull;
   int bad = 0;
 #pragma unroll
@@ -335,10 +338,6 @@ struct NodeSmem {
   tv_f32x4 qe[kRes ? kResident * 4 * kSThreads : 1];
 };
 
-// LDS-only workgroup barrier: unlike __syncthreads it does not first wait for
-// this wave's outstanding global loads, so later chunks keep streaming in.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // Sum of 16 floats, pairwise.
 __device__ __forceinline__ float sum16(const float* x) {
   float a[8];
@@ -377,11 +376,11 @@ __device__ void batch_stats(NodeSmem<kRes>& sm, float (&xp)[kResident][16], floa
         }
         m = tv_wave_max(m);
         if (l == 0) sm.red_f[w][2 * r + row] = m;
-        lds_barrier();
+        tv_lds_barrier();
         m = sm.red_f[0][2 * r + row];
         for (int i = 1; i < kSThreads / 64; ++i) m = fmaxf(m, sm.red_f[i][2 * r + row]);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = exp_t(x[e] - m, k2hi, k2lo);   // entries past V hold -inf and become 0
+        for (int e = 0; e < 16; ++e) x[e] = e0 + e < V ? exp_t(x[e] - m, k2hi, k2lo) : 0.f;
         const double sw = tv_wave_sum_d((double)sum16(x));
         if (l == 0) sm.red_d[w][2 * r + row] = sw;
         if (t == 0) sm.cm[row][j0 + r] = m;
@@ -501,9 +500,11 @@ __device__ __forceinline__ int select_mass(const double* m, int count, double th
 // that still expires flags TV_REQ_TIMEOUT instead of hanging.  kRes: every
 // member's slice is at most kResident chunks and its exponentials stay on chip
 // (target in registers, draft in LDS); otherwise each pass re-reads the slice.
-// Four workgroups per CU: a 16-member team per node for up to 64 nodes on 256 CUs.
-template <bool kRes>
-__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4))) void stoch_node_kernel(StochParams p) {
+// The resident variant runs four workgroups per CU (a 16-member team per node
+// for up to 64 nodes on 256 CUs); the streaming variant keeps two batches of
+// loads in flight and runs three.
+template <bool kRes, bool kVec>
+__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes ? 4 : 2))) void stoch_node_kernel(StochParams p) {
   __shared__ NodeSmem<kRes> sm;
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int k = blockIdx.x / p.S, member = blockIdx.x % p.S;
@@ -527,12 +528,12 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   float ep[kResident][16], eq[kResident][16];
 #pragma unroll
   for (int r = 0; r < kResident; ++r)
-    if (r < nmine) load16(zp_rs, p.V, (my_c0 + r) * kChunk + 16 * t, ep[r]);
+    if (r < nmine) load16<kVec>(zp_rs, (my_c0 + r) * kChunk + 16 * t, ep[r]);
   const bool internal = (__ballot(pv0 == u) | __ballot(pv1 == u)) != 0ull;
   if (internal) {
 #pragma unroll
     for (int r = 0; r < kResident; ++r)
-      if (r < nmine) load16(zq_rs, p.V, (my_c0 + r) * kChunk + 16 * t, eq[r]);
+      if (r < nmine) load16<kVec>(zq_rs, (my_c0 + r) * kChunk + 16 * t, eq[r]);
   }
   if (w == 0) {
     const int c = collect_children(par, n, u, sm.kids);
@@ -549,8 +550,8 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
       for (int r = 0; r < kResident; ++r) {
         const int e0 = (my_c0 + min(j0 + r, nmine - 1)) * kChunk + 16 * t;
-        load16(zp_rs, p.V, e0, ep[r]);
-        if (internal) load16(zq_rs, p.V, e0, eq[r]);
+        load16<kVec>(zp_rs, e0, ep[r]);
+        if (internal) load16<kVec>(zq_rs, e0, eq[r]);
       }
     }
     batch_stats(sm, ep, eq, min(kResident, nmine - j0), internal, my_c0, j0, p.V, p.k2hi, p.k2lo);
@@ -651,17 +652,19 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
         for (int r = 0; r < kResident; ++r) {
           const int e0 = (my_c0 + min(j0 + r, nmine - 1)) * kChunk + 16 * t;
-          load16(zp_rs, p.V, e0, ep[r]);
-          load16(zq_rs, p.V, e0, eq[r]);
+          load16<kVec>(zp_rs, e0, ep[r]);
+          load16<kVec>(zq_rs, e0, eq[r]);
         }
 #pragma unroll
         for (int r = 0; r < kResident; ++r) {
           const int jr = min(j0 + r, nmine - 1);
+          const int e0 = (my_c0 + jr) * kChunk + 16 * t;
           const float mp = sm.cm[0][jr], mq = sm.cm[1][jr];
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            ep[r][e] = exp_t(ep[r][e] - mp, p.k2hi, p.k2lo);
-            eq[r][e] = exp_t(eq[r][e] - mq, p.k2hi, p.k2lo);
+            const bool in = e0 + e < p.V;
+            ep[r][e] = in ? exp_t(ep[r][e] - mp, p.k2hi, p.k2lo) : 0.f;
+            eq[r][e] = in ? exp_t(eq[r][e] - mq, p.k2hi, p.k2lo) : 0.f;
           }
         }
       }
@@ -755,16 +758,18 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(4))) 
         }
       } else {
         float xp[16], xq[16];
-        load16(zp_rs, p.V, e0, xp);
+        load16<kVec>(zp_rs, e0, xp);
+        if (res) load16<kVec>(zq_rs, e0, xq);
         const float mp = sm.cm[0][j], mq = sm.cm[1][j];
         if (res) {
-          load16(zq_rs, p.V, e0, xq);
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            wts[e] = residual_weight(exp_t(xp[e] - mp, p.k2hi, p.k2lo), exp_t(xq[e] - mq, p.k2hi, p.k2lo), a, bq, Cres);
+            wts[e] = e0 + e < p.V ? residual_weight(exp_t(xp[e] - mp, p.k2hi, p.k2lo), exp_t(xq[e] - mq, p.k2hi, p.k2lo),
+                                                    a, bq, Cres)
+                                  : 0.0;
         } else {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) wts[e] = (double)exp_t(xp[e] - mp, p.k2hi, p.k2lo) * a;
+          for (int e = 0; e < 16; ++e) wts[e] = e0 + e < p.V ? (double)exp_t(xp[e] - mp, p.k2hi, p.k2lo) * a : 0.0;
         }
       }
       const int y = chunk_draw(sm, wts, e0, sm.base, sm.thr, (my_c0 + j) * kChunk);
@@ -881,19 +886,20 @@ VerifyLayout layout(const tv_verify_desc* d) {
   return L;
 }
 
-int g_decide_occ[2] = {-1, -1};   // resident workgroups per CU: streaming / register-resident variant
-
 struct TeamPlan {
   int S;     // workgroups per node
   int per;   // chunks per member
 };
 
-// Team size: at most kMaxTeam members and at most one per chunk, as many as a
-// grid of `capacity` co-resident workgroups holds with one team per node.
-TeamPlan plan_team(long long nodes, int chunks, long long capacity) {
+// Team size: enough members (a power of two, at most kMaxTeam and at most one
+// per chunk) that every member's slice fits on chip (kResident chunks).  Teams
+// need not all be resident at once: a team waits only on its own members,
+// which sit on consecutive workgroup ids, so teams dispatched later simply
+// start when earlier ones leave.
+TeamPlan plan_team(int chunks) {
   TeamPlan tp;
   int S = 1;
-  while (S * 2 <= kMaxTeam && S * 2 <= chunks && nodes * S * 2 <= capacity) S *= 2;
+  while (S * 2 <= kMaxTeam && S * 2 <= chunks && (chunks + S - 1) / S > kResident) S *= 2;
   tp.S = S;
   tp.per = (chunks + S - 1) / S;
   return tp;
@@ -937,7 +943,10 @@ extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* targe
   p.chunks = L.gchunks;
   const long long grid = (long long)desc->batch * desc->n_max * L.gchunks;
   if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(greedy_argmax_kernel, dim3((unsigned)grid), dim3(kGreedyThreads), 0, stream, p);
+  if ((desc->vocab & 3) == 0)
+    hipLaunchKernelGGL(greedy_argmax_kernel<true>, dim3((unsigned)grid), dim3(kGreedyThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(greedy_argmax_kernel<false>, dim3((unsigned)grid), dim3(kGreedyThreads), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   hipLaunchKernelGGL(greedy_chase_kernel, dim3((unsigned)desc->batch), dim3(kMaxNodes), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
@@ -960,22 +969,8 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
   if (L.chunks > kMaxChunks) return TV_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < L.stoch_bytes) return TV_ERR_WORKSPACE;
   const long long nodes = (long long)desc->batch * desc->n_max;
-  int cu = 0;
-  rc = tv_device_cu_count(&cu);
-  if (rc != TV_OK) return rc;
-  if (g_decide_occ[0] < 0) {
-    int nb0 = 0, nb1 = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb0, stoch_node_kernel<false>, kSThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb1, stoch_node_kernel<true>, kSThreads, 0) != hipSuccess)
-      return TV_ERR_HIP;
-    g_decide_occ[1] = nb1 < 1 ? 1 : nb1;
-    g_decide_occ[0] = nb0 < 1 ? 1 : nb0;
-  }
-  // Prefer the register-resident variant when its resident grid gives every
-  // member at most kResident chunks; otherwise members stream their slices.
-  TeamPlan tp = plan_team(nodes, L.chunks, (long long)g_decide_occ[1] * cu);
+  const TeamPlan tp = plan_team(L.chunks);
   const bool resident = tp.per <= kResident;
-  if (!resident) tp = plan_team(nodes, L.chunks, (long long)g_decide_occ[0] * cu);
 
   StochParams p;
   p.target = target_logits;
@@ -1008,10 +1003,15 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
 
   const long long grid = nodes * tp.S;
   if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
-  if (resident)
-    hipLaunchKernelGGL(stoch_node_kernel<true>, dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
+  const bool vec = (desc->vocab & 3) == 0;
+  if (resident && vec)
+    hipLaunchKernelGGL((stoch_node_kernel<true, true>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
+  else if (resident)
+    hipLaunchKernelGGL((stoch_node_kernel<true, false>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
+  else if (vec)
+    hipLaunchKernelGGL((stoch_node_kernel<false, true>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(stoch_node_kernel<false>, dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
+    hipLaunchKernelGGL((stoch_node_kernel<false, false>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kMaxNodes), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;

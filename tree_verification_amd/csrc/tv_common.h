@@ -139,6 +139,10 @@ __device__ __forceinline__ unsigned long long tv_wave_max_u64(unsigned long long
   return tv_wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 
+// LDS-only workgroup barrier: unlike __syncthreads it does not first wait for
+// the wave's outstanding global loads, so loads issued earlier stay in flight.
+__device__ __forceinline__ void tv_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Acquire/release helpers for inter-workgroup hand-offs through global memory.
 __device__ __forceinline__ int tv_atomic_add_release(int* p, int v) {
   __threadfence();
