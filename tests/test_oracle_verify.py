@@ -431,3 +431,38 @@ def test_accept_comparison_is_less_or_equal():
     path, out, _ = verify_stochastic_request(tl, dl, tok, par, 2, np.array([0, 2.0 ** -24]),
                                              np.array([0.5, 0.5]))
     assert path == [0] and out[0] in (1, 2)
+
+
+# --------------------------------------------------------------------------
+# chi-square over 10^6 seeded trials: the first two emitted tokens
+# --------------------------------------------------------------------------
+
+@pytest.mark.slow
+def test_chi_square_two_tokens_million_trials():
+    """10^6 trials of an order-1 Markov target on the guide's mask-figure tree
+    shape: the first two emitted tokens (taken from a second round when the
+    first emits only one) must follow P[start] x P exactly."""
+    from markov_trials import SHAPE, chi_square_pvalue, draw_round, markov_tables, softmax_rows
+    V, T, start = 4, 1_000_000, 1
+    LT, LQ = markov_tables(700, V)
+    rng = np.random.default_rng(701)
+    n = len(SHAPE)
+    tok, tl, dl, ua, us = draw_round(rng, LT, LQ, np.full(T, start))
+    x1 = np.empty(T, dtype=np.int64)
+    x2 = np.full(T, -1, dtype=np.int64)
+    for t in range(T):
+        _, out, _ = verify_stochastic_request(tl[t], dl[t], tok[t], SHAPE, n, ua[t], us[t])
+        x1[t] = out[0]
+        if len(out) > 1:
+            x2[t] = out[1]
+    need = np.nonzero(x2 < 0)[0]
+    tok2, tl2, dl2, ua2, us2 = draw_round(rng, LT, LQ, x1[need])
+    for i, t in enumerate(need):
+        _, out, _ = verify_stochastic_request(tl2[i], dl2[i], tok2[i], SHAPE, n, ua2[i], us2[i])
+        x2[t] = out[0]
+    counts = np.zeros((V, V))
+    np.add.at(counts, (x1, x2), 1)
+    Pt = softmax_rows(LT)
+    expected = np.outer(Pt[start], np.ones(V)) * Pt * T
+    chi2, pval = chi_square_pvalue(counts, expected)
+    assert pval > 1e-3, (chi2, pval)
