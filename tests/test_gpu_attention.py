@@ -51,12 +51,12 @@ SMALL = [
     ("llama8b", dict(prefix=300)),                                  # 4 row tiles x 3 key splits
     ("llama8b", dict(prefix=(0, 0), n_nodes=64)),                   # no prefix: pure tree attention
     ("ragged", dict(batch=4, prefix=(100, 700))),                   # paged, shuffled, ragged
-    ("chain", dict(batch=16, prefix=257)),                          # R = 12..32: VALU and MFMA rows
+    ("chain", dict(batch=16, prefix=257)),                          # R = 12..32: one partly filled row tile
     ("llama70b_share", dict(batch=1, prefix=500)),                  # 16 row tiles, N = 128
     ("llama8b", dict(prefix=333, n_nodes=1)),                       # single node: decode attention
     ("llama8b", dict(prefix=95, n_nodes=37, tree="star")),          # star tree, ragged row tile
     ("llama8b", dict(prefix=40, n_nodes=128, tree="chain")),        # maximum depth
-    ("chain", dict(batch=5, prefix=17, n_nodes=(1, 3))),            # R = 4..12: every VALU row count
+    ("chain", dict(batch=5, prefix=17, n_nodes=(1, 3))),            # R = 4..12: mostly padding rows
 ]
 
 
@@ -100,7 +100,7 @@ def custom(dtype, Hq, Hkv, D, n, P, B=2, seed=3, kind="capped"):
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,n,P", [
     ("bf16", 8, 2, 64, 30, (10, 300)),      # head_dim 64 on MFMA
-    ("bf16", 4, 4, 64, 10, (0, 64)),        # G = 1, R < 16: VALU bf16
+    ("bf16", 4, 4, 64, 10, (0, 64)),        # G = 1, R < 16: one MFMA wave, padding rows
     ("f32", 8, 2, 128, 24, (50, 200)),      # fp32, R = 96: VALU over 6 row tiles
     ("f32", 2, 1, 64, 100, (1, 33)),        # fp32, deep tree, short prefix
     ("bf16", 16, 2, 128, 128, (3, 3)),      # R = 1024 with a 3-token prefix

@@ -14,13 +14,13 @@
 // and attn_merge_kernel combines the splits of each row by log-sum-exp (a
 // kernel boundary orders the hand-off, so no workgroup waits on a fence).
 //
-// MFMA path (bf16, >= 16 rows): 32-key chunks of K and V move in batches of
-// NB chunks: while one batch is computed from LDS, the next is in flight in
-// registers (about 64 KB per CU), then stored to LDS between two LDS-only
-// barriers.  Each lane stores exactly the 16 bytes it later feeds to
-// v_mfma_f32_16x16x32_bf16, so operands come back with conflict-free
-// ds_read_b128.  The four waves share every chunk and own disjoint 16*NTW-row
-// slices of the tile:
+// MFMA path (bf16): four MFMA waves own disjoint 16*NTW-row slices of the
+// tile (rows past the request are padding) and a fifth, producer wave moves
+// 32-key chunks of K and V straight from HBM into a four-slot LDS ring with
+// global_load_lds_dwordx4, so the MFMA waves issue no memory operations while
+// they compute.  Each lane's 16 bytes land exactly where lane l of every MFMA
+// wave reads the operand it feeds to v_mfma_f32_16x16x32_bf16 (conflict-free
+// ds_read_b128):
 //   S^T[key][row] = K Q^T  then  O^T[d][row] += V^T P^T,
 // laid out so that a lane always owns one query row (lane % 16): the softmax
 // state is lane-local, and the C layout of S^T feeds the B operand of the PV
@@ -29,8 +29,8 @@
 // single 16-byte piece.  The running max moves only when a row's max grows by
 // more than 8 (log2 units), which keeps most chunks free of rescaling.
 //
-// VALU path (fewer than 16 rows, or fp32): the waves interleave 64-key chunks
-// with lane = key for the scores and lane = d for PV, merged in LDS.
+// VALU path (fp32): the waves interleave 64-key chunks with lane = key for the
+// scores and lane = d for PV, merged in LDS.
 //
 // Tree mask: a wavefront builds the ancestor bitmaps of all nodes (two 64-bit
 // words per node, n <= 128) from the parent array by pointer jumping with lane
@@ -43,11 +43,13 @@
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;        // VALU path (fp32): four waves
+constexpr int kMfmaWaves = 4;        // MFMA path: four waves own the rows ...
+constexpr int kMfmaThreads = 64 * (kMfmaWaves + 1);   // ... and a fifth moves the K/V chunks
 constexpr int kMaxNodes = 128;
 constexpr int kMaxSplits = 32;        // key splits per (request, KV head, row tile)
 constexpr int kMaxKeysPerSplit = 32768;
-constexpr int kMaxBatch = 4;          // chunks staged per batch on the MFMA path
+constexpr int kStages = 4;            // LDS ring slots (chunks in flight) on the MFMA path
 constexpr int kMaxTab = kMaxKeysPerSplit / 16 + 2;   // block-table entries staged per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -62,7 +64,7 @@ struct AttnParams {
   const int32_t* parent;
   void* out;
   int32_t* status;
-  float* part_o;    // [tiles][splits][rows_per_tile][D]
+  void* part_o;     // [tiles][splits][rows_per_tile][D] O / l of each split (PartT<kBF16>)
   float* part_ml;   // [tiles][splits][rows_per_tile][2]
   int B, n_max, Hq, Hkv, G, D, bs, lbs, max_blocks, num_blocks;
   float scale_log2;
@@ -93,16 +95,6 @@ struct CommonSmem {
   int flag;
 };
 
-// Chunks per batch.  More in flight does not help NTW = 1 (its waves are
-// bound by the latency of the MFMA / softmax chain, not by loads) and costs
-// LDS; NTW = 2 keeps four; NTW = 4 is compute-bound and two suffice.
-template <int D, int NTW>
-struct RingSmem {
-  static constexpr int NB = NTW == 2 ? kMaxBatch : 2;
-  alignas(16) unsigned char ring[NB][Chunk<D>::BYTES];   // one batch of K/V chunks
-  int tab[kMaxTab];   // (block, KV head) row index per block of this split
-};
-
 template <int D>
 struct ValuSmem {
   float o[16][D + 4];           // unnormalised output rows (log2-domain softmax)
@@ -112,16 +104,6 @@ struct ValuSmem {
   float wl[4][16];
   float qs[16][D];
   float sc[4][16][64];          // per-wave probability strips
-};
-
-template <bool kBF16, int D, int NTW>
-union AttnLds {
-  RingSmem<D, NTW> r;
-  ValuSmem<D> v;
-};
-template <int D, int NTW>
-union AttnLds<false, D, NTW> {
-  ValuSmem<D> v;
 };
 
 // ---------------------------------------------------------------------------
@@ -383,6 +365,26 @@ __device__ void attn_valu(const AttnParams& p, ValuSmem<D>& sm, int b, int g, in
 // output and split-K merge
 // ---------------------------------------------------------------------------
 
+// Split partials hold the split's normalised output O / l (|O / l| <= max |v|)
+// beside its (m, l).  For bf16 inputs they are stored as fp16 (relative
+// rounding 2^-11, far inside the bf16 output's own rounding), which halves the
+// bytes written and re-read; fp32 inputs keep fp32.
+typedef _Float16 tv_f16x4 __attribute__((ext_vector_type(4)));
+
+template <bool kBF16>
+__device__ __forceinline__ void store_part4(void* part_o, size_t off, tv_f32x4 v) {
+  if (kBF16)
+    *(tv_f16x4*)((_Float16*)part_o + off) = __builtin_convertvector(v, tv_f16x4);
+  else
+    *(tv_f32x4*)((float*)part_o + off) = v;
+}
+
+template <bool kBF16>
+__device__ __forceinline__ tv_f32x4 load_part4(const void* part_o, size_t off) {
+  if (kBF16) return __builtin_convertvector(*(const tv_f16x4*)((const _Float16*)part_o + off), tv_f32x4);
+  return *(const tv_f32x4*)((const float*)part_o + off);
+}
+
 template <bool kBF16, int D>
 __device__ __forceinline__ void store_out4(const AttnParams& p, int b, int g, int qrow, int d, const float* v4) {
   int node = qrow / p.G, hh = qrow % p.G;
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(merge_threads<D>()) void attn_merge_kernel(AttnPara
     if (s < p.splits && item) {
       const size_t pr = base + (size_t)s * p.rows_per_tile + r;
       ml[s] = *(const float2*)&p.part_ml[pr * 2];
-      o[s] = *(const tv_f32x4*)&p.part_o[pr * D + d];
+      o[s] = load_part4<kBF16>(p.part_o, pr * D + d);
     }
   }
   if (n < 1 || n > p.n_max || P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) return;
@@ -442,8 +444,8 @@ __global__ __launch_bounds__(merge_threads<D>()) void attn_merge_kernel(AttnPara
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < n_active) {
-      const float w = (ml[s].x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[s].x - M);
-      L += w * ml[s].y;
+      const float w = (ml[s].x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[s].x - M) * ml[s].y;
+      L += w;
       acc += w * o[s];
     }
   }
@@ -469,7 +471,9 @@ __device__ void emit_valu(const AttnParams& p, CommonSmem& cm, ValuSmem<D>& sm, 
   const size_t prow = ((size_t)tile * p.splits + split) * RW;
   for (int idx = t; idx < rows * (D / 4); idx += kThreads) {
     int r = idx / (D / 4), d = 4 * (idx % (D / 4));
-    *(tv_f32x4*)(p.part_o + (prow + r) * D + d) = (tv_f32x4){sm.o[r][d], sm.o[r][d + 1], sm.o[r][d + 2], sm.o[r][d + 3]};
+    const float inv = sm.l[r] > 0.f ? 1.f / sm.l[r] : 0.f;
+    store_part4<kBF16>(p.part_o, (prow + r) * D + d,
+                       (tv_f32x4){sm.o[r][d] * inv, sm.o[r][d + 1] * inv, sm.o[r][d + 2] * inv, sm.o[r][d + 3] * inv});
   }
   if (t < rows) {
     p.part_ml[(prow + t) * 2] = sm.m[t];
@@ -478,64 +482,126 @@ __device__ void emit_valu(const AttnParams& p, CommonSmem& cm, ValuSmem<D>& sm, 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path: K/V ring in LDS, 16*NTW rows per wave, 64*NTW rows per workgroup
+// MFMA path: K/V chunks DMA'd into an LDS ring, 16*NTW rows per wave
 // ---------------------------------------------------------------------------
-
 
 __device__ __forceinline__ tv_bf16x8 lds_bf16x8(const unsigned char* ptr) {
   return __builtin_bit_cast(tv_bf16x8, *(const tv_u32x4*)ptr);
 }
 
+// s_waitcnt that only waits for the vector-memory counter (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-// This wave's share of one 32-key chunk: operand blocks wave, wave+4, ... of
-// the chunk (1 KB each, 16 bytes per lane), loaded into registers.  Keys past
-// k_end are redirected to key k_begin (always valid) and masked later.
-template <int D>
-struct ChunkRegs {
-  tv_u32x4 r[Chunk<D>::PER_WAVE];
+typedef __attribute__((address_space(3))) void* tv_lds_ptr;
+
+// One 32-key chunk, sent straight from HBM into its LDS slot by the producer
+// wave with global_load_lds_dwordx4: operand block j (1 KB) gets lane l's 16
+// bytes at slot + 1024*j + 16*l, the bytes lane l of every MFMA wave later
+// feeds to v_mfma.  A chunk starts at a multiple of 32 keys, so it spans at
+// most two blocks (A and B; only when the block size is 16): its addresses are
+// two wave-uniform row bases plus per-lane offsets fixed for the whole split.
+// Keys at or past k_end read whatever their (in-pool) block holds and are
+// masked at use.
+struct DmaLane {
+  uint32_t koff[2];   // key block (tt, kk = 0): byte offset of this lane's 8 d values from the row base
+  uint32_t voff;      // value block dt = 0: byte offset of this lane's 8 keys
+  bool kb, vb;        // the lane's key / value bytes come from the chunk's second block
 };
 
 template <int D>
-__device__ __forceinline__ void load_chunk(const AttnParams& p, const int* tabrow, int tab0, ChunkRegs<D>& cr,
-                                           int key0, int k_begin, int k_end, int wave, int lane) {
-  constexpr int KK = Chunk<D>::KK;
+__device__ __forceinline__ DmaLane dma_lane(int bs, int lane) {
   const int l16 = lane & 15, h4 = lane >> 4;
-  const int bmask = p.bs - 1;
-  const size_t row_elems = (size_t)p.bs * D;   // elements of one (block, KV head) row, K and V alike
+  const int wrap = (bs < 32 ? bs : 32) - 1;   // in-block position of a key offset within the chunk
+  DmaLane dl;
 #pragma unroll
-  for (int i = 0; i < Chunk<D>::PER_WAVE; ++i) {
-    const int j = wave + 4 * i;
-    const uint16_t* src;
-    if (4 * i < 2 * KK) {   // key operand block (tt, kk)
-      const int tt = j / KK, kk = j % KK;
-      int key = key0 + 8 * (l16 >> 2) + 4 * tt + (l16 & 3);
-      key = key < k_end ? key : k_begin;
-      const int row = tabrow[(key >> p.lbs) - tab0];
-      src = (const uint16_t*)p.k + (size_t)row * row_elems + (key & bmask) * D + 32 * kk + 8 * h4;
-    } else {                // value operand block dt
-      const int dt = j - 2 * KK;
-      int kv = key0 + 8 * h4;
-      kv = kv < k_end ? kv : k_begin;
-      const int row = tabrow[(kv >> p.lbs) - tab0];
-      src = (const uint16_t*)p.v + (size_t)row * row_elems + ((16 * dt + l16) << p.lbs) + (kv & bmask);
-    }
-    cr.r[i] = *(const tv_u32x4*)src;
+  for (int tt = 0; tt < 2; ++tt) {   // key row 8*(l16/4) + 4*tt + l16%4 of the chunk, d = 8*h4 + 32*kk
+    const int koff = 8 * (l16 >> 2) + 4 * tt + (l16 & 3);
+    dl.koff[tt] = (uint32_t)(((koff & wrap) * D + 8 * h4) * 2);
   }
+  dl.kb = 8 * (l16 >> 2) >= bs;
+  dl.voff = (uint32_t)((l16 * bs + ((8 * h4) & wrap)) * 2);   // value row d = l16 + 16*dt, keys 8*h4 ..
+  dl.vb = 8 * h4 >= bs;
+  return dl;
 }
 
-// Write this wave's share of a chunk to LDS.  In the request's last chunk the
-// value slots past k_end (same block, no data) are cleared first.
+// Row indices of the two blocks of the chunk at key0 (the second clamped into
+// the staged table; it is only read for keys past the request's end then).
+__device__ __forceinline__ int2 chunk_rows(const int* tab, int tab0, int ntab, int key0, int lbs) {
+  const int ia = (key0 >> lbs) - tab0;
+  const int ib = min(((key0 + 16) >> lbs) - tab0, ntab - 1);
+  return make_int2(__builtin_amdgcn_readfirstlane(tab[ia]), __builtin_amdgcn_readfirstlane(tab[ib]));
+}
+
 template <int D>
-__device__ __forceinline__ void store_chunk(unsigned char* slot, const ChunkRegs<D>& cr, int key0, int k_end,
-                                            int wave, int lane) {
-  constexpr int KK = Chunk<D>::KK;
-  const int h4 = lane >> 4;
-  const int kv = key0 + 8 * h4;
+__device__ __forceinline__ void dma_chunk(const AttnParams& p, const DmaLane& dl, int2 rows, int key0,
+                                          unsigned char* slot) {
+  constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT;
+  const size_t row_bytes = (size_t)p.bs * D * 2;   // one (block, KV head) row, K and V alike
+  const size_t kin = (size_t)(key0 & (p.bs - 1));  // the chunk's first in-block position
+  const size_t ra = (size_t)(uint32_t)rows.x * row_bytes, rb = (size_t)(uint32_t)rows.y * row_bytes;
+  const char* kbase = (const char*)p.k + (dl.kb ? rb : ra) + kin * D * 2;
+  const char* vbase = (const char*)p.v + (dl.vb ? rb : ra) + kin * 2;
 #pragma unroll
-  for (int i = 0; i < Chunk<D>::PER_WAVE; ++i) {
-    const int j = wave + 4 * i;
-    tv_u32x4 w = cr.r[i];
-    if (j >= 2 * KK && kv + 8 > k_end && kv < k_end) {
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + dl.koff[tt] + 64 * kk),
+                                       (tv_lds_ptr)(slot + (tt * KK + kk) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    __builtin_amdgcn_global_load_lds((const void*)(vbase + dl.voff + (size_t)dt * 32 * p.bs),
+                                     (tv_lds_ptr)(slot + (2 * KK + dt) * 1024), 16, 0, 0);
+}
+
+// Running softmax state and output accumulators of one wave (16*NTW rows).
+template <int D, int NTW>
+struct WaveAcc {
+  float m_run[NTW], l_run[NTW];
+  tv_f32x4 oacc[Chunk<D>::DT][NTW];
+};
+
+// One 32-key chunk from an LDS slot: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
+template <int D, int NTW>
+__device__ __forceinline__ void mfma_chunk(const unsigned char* slot, const tv_bf16x8 (&qop)[NTW][D / 32],
+                                           WaveAcc<D, NTW>& a, const uint64_t (&alo)[NTW],
+                                           const uint64_t (&ahi)[NTW], int key0, int P, int k_end,
+                                           float scale_log2, int lane) {
+  constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT;
+  const int h4 = lane >> 4;
+  tv_bf16x8 kop[2][KK], vop[DT];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = lds_bf16x8(slot + (tt * KK + kk) * 1024 + lane * 16);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) vop[dt] = lds_bf16x8(slot + (2 * KK + dt) * 1024 + lane * 16);
+
+  // phase 1: scores of every row tile (independent MFMA chains)
+  tv_f32x4 sc[NTW][2];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[tt][kk], qop[nt][kk], acc, 0, 0, 0);
+      sc[nt][tt] = acc;
+    }
+  }
+  // The request's last chunk: value slots at or past k_end hold no data (zero
+  // them so that 0 * garbage cannot reach the sum).  Lane l holds keys
+  // key0 + 8*(l/16) + e of value row d.
+  const bool plain = key0 + 32 <= P && key0 + 32 <= k_end;   // prefix keys only: no mask
+  if (key0 + 32 > k_end) {
+    const int kv = key0 + 8 * h4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      tv_u32x4 w = __builtin_bit_cast(tv_u32x4, vop[dt]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (kv + e >= k_end) {
@@ -543,22 +609,92 @@ __device__ __forceinline__ void store_chunk(unsigned char* slot, const ChunkRegs
           else w[e >> 1] &= 0xFFFF0000u;
         }
       }
+      vop[dt] = __builtin_bit_cast(tv_bf16x8, w);
     }
-    *(tv_u32x4*)(slot + j * 1024 + lane * 16) = w;
   }
+  // phase 2: mask, online softmax.  Lane l holds keys key0 + 8*(l/16) + 4*tt + i
+  // of query row l % 16.  The max is taken over the raw scores (the scale is
+  // positive) and the scale is folded into the exponent's FMA.  The running max
+  // only moves when a row's max grows by more than kLazy (log2 units), so the
+  // accumulators are rescaled rarely; probabilities stay below 2^kLazy.
+  constexpr float kLazy = 8.f;
+  tv_bf16x8 pop[NTW];
+  float alpha[NTW];
+  bool any_rescale = false;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    if (!plain) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = key0 + 8 * h4 + 4 * tt + i;
+          bool ok = key < k_end;
+          if (ok && key >= P) ok = anc_bit(alo[nt], ahi[nt], key - P);
+          sc[nt][tt][i] = ok ? sc[nt][tt][i] : kNegInf;
+        }
+      }
+    }
+    float rmax = fmaxf(fmaxf(fmaxf(sc[nt][0][0], sc[nt][0][1]), fmaxf(sc[nt][0][2], sc[nt][0][3])),
+                       fmaxf(fmaxf(sc[nt][1][0], sc[nt][1][1]), fmaxf(sc[nt][1][2], sc[nt][1][3])));
+    rmax = tv_rows_max(rmax);
+    const float cmax = rmax * scale_log2;   // -inf stays -inf
+    const bool move = cmax > a.m_run[nt] + kLazy || (a.m_run[nt] == kNegInf && cmax != kNegInf);
+    const float m_ref = move ? cmax : a.m_run[nt];
+    alpha[nt] = (move && a.m_run[nt] != kNegInf) ? __builtin_amdgcn_exp2f(a.m_run[nt] - m_ref) : 1.f;
+    any_rescale |= alpha[nt] != 1.f;
+    a.m_run[nt] = m_ref;
+    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+    float e[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[4 * tt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nt][tt][i], scale_log2, neg_m));
+    a.l_run[nt] = a.l_run[nt] * alpha[nt] + (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+    const tv_u32x4 pw = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                         pack_bf16x2(e[6], e[7])};
+    pop[nt] = __builtin_bit_cast(tv_bf16x8, pw);
+  }
+  if (__any(any_rescale)) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] *= alpha[nt];
+  }
+  // phase 3: O^T += V^T P^T for every row tile
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      a.oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[nt], a.oacc[dt][nt], 0, 0, 0);
 }
 
-template <bool kBF16, int D, int NTW>
-__device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, CommonSmem& cm, RingSmem<D, NTW>& sm,
+// The key range of one split, chunk by chunk through an NS-slot LDS ring.  The
+// producer wave sent the first NS-1 chunks in the prologue and read the block
+// rows of chunk NS-1.  Per chunk c: the producer waits for its DMA of c (later
+// chunks stay in flight); one barrier (chunk c has landed and every MFMA wave
+// is done with chunk c-1); the producer sends chunk c+NS-1 into c-1's slot and
+// reads the block rows of chunk c+NS (used one step later, so the LDS read's
+// latency stays hidden) while the MFMA waves compute c.  Issuing a DMA stalls
+// the issuing wave until the memory pipeline takes it, so keeping all of them
+// on one wave lets the chunk's compute run under the transfer of later chunks.
+// The slots are distinct LDS objects and the stage loop is unrolled, so the
+// compiler sees which DMA writes which slot and adds no waits of its own
+// before the slot reads (the MFMA waves have no memory operations in flight).
+template <int D, int NTW>
+__device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, CommonSmem& cm, const int* tab,
+                                                         unsigned char* const (&slots)[kStages],
                                                          const tv_bf16x8 (&qop)[NTW][D / 32],
-                                                         ChunkRegs<D> (&cr)[RingSmem<D, NTW>::NB], int tile, int split,
+                                                         const DmaLane& dl, int2 next_rows, int tile, int split,
                                                          int n_active, int b, int g, int r0, int R, int P,
-                                                         int k_begin, int k_end, int tab0, bool tree_in_range) {
-  constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT, RW = 64 * NTW;
+                                                         int k_begin, int k_end, int tab0, int ntab,
+                                                         bool tree_in_range) {
+  constexpr int DT = Chunk<D>::DT, RW = 64 * NTW, NB = Chunk<D>::NBLK, NS = kStages;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, h4 = lane >> 4;
   const int G = p.G;
-  const int rbase = r0 + wave * 16 * NTW;          // this wave's first row
+  const bool producer = wave == kMfmaWaves;
+  const int rbase = producer ? R : r0 + wave * 16 * NTW;   // this wave's first row (none for the producer)
   const int nchunks = (k_end - k_begin + 31) / 32;
 
   uint64_t alo[NTW], ahi[NTW];
@@ -569,125 +705,39 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
     alo[nt] = tree_in_range ? cm.anc[node][0] : 0ull;
     ahi[nt] = tree_in_range ? cm.anc[node][1] : 0ull;
   }
-  float m_run[NTW], l_run[NTW];
-  tv_f32x4 oacc[DT][NTW];
+  WaveAcc<D, NTW> a;
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    m_run[nt] = kNegInf;
-    l_run[nt] = 0.f;
+    a.m_run[nt] = kNegInf;
+    a.l_run[nt] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
   }
-  // Chunks move in batches of NB: while a batch is computed from LDS, the next
-  // batch is in flight in registers.  The first batch was issued in the
-  // prologue.  Loads never stay pending across more than one batch, which keeps
-  // the compiler's wait counts exact (no drain of younger loads).
-  constexpr int NB = RingSmem<D, NTW>::NB;
 
-  for (int c0 = 0; c0 < nchunks; c0 += NB) {
-    tv_lds_barrier();   // every wave has finished the previous batch: its LDS slots are free
+  for (int c0 = 0; c0 < nchunks; c0 += NS) {
 #pragma unroll
-    for (int ib = 0; ib < NB; ++ib)
-      if (c0 + ib < nchunks) store_chunk<D>(sm.ring[ib], cr[ib], k_begin + 32 * (c0 + ib), k_end, wave, lane);
-#pragma unroll
-    for (int ib = 0; ib < NB; ++ib)
-      if (c0 + NB + ib < nchunks)
-        load_chunk<D>(p, sm.tab, tab0, cr[ib], k_begin + 32 * (c0 + NB + ib), k_begin, k_end, wave, lane);
-    tv_lds_barrier();   // the batch is in LDS
-#pragma unroll
-  for (int ib = 0; ib < NB; ++ib) {
-    const int c = c0 + ib;
-    if (c >= nchunks) break;
-    unsigned char* slot = sm.ring[ib];
-    const int key0 = k_begin + 32 * c;
-    if (rbase >= R) continue;   // a wave without rows only helps to stage chunks
-
-    tv_bf16x8 kop[2][KK], vop[DT];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = lds_bf16x8(slot + (tt * KK + kk) * 1024 + lane * 16);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vop[dt] = lds_bf16x8(slot + (2 * KK + dt) * 1024 + lane * 16);
-
-    // phase 1: scores of every row tile (independent MFMA chains)
-    tv_f32x4 sc[NTW][2];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[tt][kk], qop[nt][kk], acc, 0, 0, 0);
-        sc[nt][tt] = acc;
+    for (int s = 0; s < NS; ++s) {
+      const int c = c0 + s;
+      if (c >= nchunks) break;
+      if (producer) {
+        if (c + NS - 2 < nchunks) wait_vmcnt<(NS - 2) * NB>();
+        else wait_vmcnt<0>();
+      }
+      tv_lds_barrier();
+      if (producer) {
+        if (c + NS - 1 < nchunks) dma_chunk<D>(p, dl, next_rows, k_begin + 32 * (c + NS - 1), slots[(s + NS - 1) % NS]);
+        if (c + NS < nchunks) next_rows = chunk_rows(tab, tab0, ntab, k_begin + 32 * (c + NS), p.lbs);
+      } else if (rbase < R) {
+        mfma_chunk<D, NTW>(slots[s], qop, a, alo, ahi, k_begin + 32 * c, P, k_end, p.scale_log2, lane);
       }
     }
-    // phase 2: mask, online softmax.  Lane l holds keys
-    // key0 + 8*(l/16) + 4*tt + i of query row l % 16.  The max is taken over
-    // the raw scores (the scale is positive) and the scale is folded into the
-    // exponent's FMA.  The running max is only moved when a row's max grows by
-    // more than kLazy (log2 units), so the accumulators are rescaled rarely;
-    // probabilities stay below 2^kLazy.
-    constexpr float kLazy = 8.f;
-    const bool plain = key0 + 32 <= P && key0 + 32 <= k_end;   // prefix keys only: no mask
-    tv_bf16x8 pop[NTW];
-    float alpha[NTW];
-    bool any_rescale = false;
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      if (!plain) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 8 * h4 + 4 * tt + i;
-            bool ok = key < k_end;
-            if (ok && key >= P) ok = anc_bit(alo[nt], ahi[nt], key - P);
-            sc[nt][tt][i] = ok ? sc[nt][tt][i] : kNegInf;
-          }
-        }
-      }
-      float rmax = fmaxf(fmaxf(fmaxf(sc[nt][0][0], sc[nt][0][1]), fmaxf(sc[nt][0][2], sc[nt][0][3])),
-                         fmaxf(fmaxf(sc[nt][1][0], sc[nt][1][1]), fmaxf(sc[nt][1][2], sc[nt][1][3])));
-      rmax = tv_rows_max(rmax);
-      const float cmax = rmax * p.scale_log2;   // -inf stays -inf
-      const bool move = cmax > m_run[nt] + kLazy || (m_run[nt] == kNegInf && cmax != kNegInf);
-      const float m_ref = move ? cmax : m_run[nt];
-      alpha[nt] = (move && m_run[nt] != kNegInf) ? __builtin_amdgcn_exp2f(m_run[nt] - m_ref) : 1.f;
-      any_rescale |= alpha[nt] != 1.f;
-      m_run[nt] = m_ref;
-      const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
-      float e[8];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[4 * tt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[nt][tt][i], p.scale_log2, neg_m));
-      l_run[nt] = l_run[nt] * alpha[nt] + (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
-      const tv_u32x4 pw = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                           pack_bf16x2(e[6], e[7])};
-      pop[nt] = __builtin_bit_cast(tv_bf16x8, pw);
-    }
-    if (__any(any_rescale)) {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt][nt] *= alpha[nt];
-    }
-    // phase 3: O^T += V^T P^T for every row tile
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[nt], oacc[dt][nt], 0, 0, 0);
-  }
   }
 
   // output: lane l holds O[row rbase + 16*nt + l%16][16*dt + 4*(l/16) + i]
   const size_t prow = ((size_t)tile * p.splits + split) * RW;
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    float lt = l_run[nt];
+    float lt = a.l_run[nt];
     lt = tv_rows_sum(lt);
     const int qrow = rbase + 16 * nt + l16;
     if (qrow >= R) continue;
@@ -695,14 +745,16 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
       const float inv = 1.f / lt;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        float v4[4] = {oacc[dt][nt][0] * inv, oacc[dt][nt][1] * inv, oacc[dt][nt][2] * inv, oacc[dt][nt][3] * inv};
-        store_out4<kBF16, D>(p, b, g, qrow, 16 * dt + 4 * h4, v4);
+        float v4[4] = {a.oacc[dt][nt][0] * inv, a.oacc[dt][nt][1] * inv, a.oacc[dt][nt][2] * inv,
+                       a.oacc[dt][nt][3] * inv};
+        store_out4<true, D>(p, b, g, qrow, 16 * dt + 4 * h4, v4);
       }
     } else {
       const size_t row = prow + (qrow - r0);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *(tv_f32x4*)(p.part_o + row * D + 16 * dt + 4 * h4) = oacc[dt][nt];
-      if (h4 == 0) *(float2*)&p.part_ml[row * 2] = make_float2(m_run[nt], lt);
+      for (int dt = 0; dt < DT; ++dt) store_part4<true>(p.part_o, row * D + 16 * dt + 4 * h4, a.oacc[dt][nt] * inv);
+      if (h4 == 0) *(float2*)&p.part_ml[row * 2] = make_float2(a.m_run[nt], lt);
     }
   }
 }
@@ -711,11 +763,18 @@ __device__ __attribute__((always_inline)) void attn_ring(const AttnParams& p, Co
 // kernel
 // ---------------------------------------------------------------------------
 
+// Launch bounds: NTW = 1 leaves room for two workgroups per CU (ten waves,
+// under 80 KB of LDS each); wider tiles take more of the register file.
+template <bool kBF16, int NTW>
+constexpr int wg_per_cu() { return (kBF16 && NTW > 1) ? 1 : 2; }
+
+template <bool kBF16>
+constexpr int block_threads() { return kBF16 ? kMfmaThreads : kThreads; }
+
 template <bool kBF16, int D, int NTW>
-__global__ __launch_bounds__(kThreads, (kBF16 && NTW == 1) ? 2 : 1) void tree_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())) void tree_attn_kernel(AttnParams p) {
   constexpr int RW = kBF16 ? 64 * NTW : 16;
   __shared__ CommonSmem cm;
-  __shared__ AttnLds<kBF16, D, NTW> u;
   const int t = threadIdx.x;
   const int lid = tv_xcd_remap(blockIdx.x, p.total);
   const int tile = lid / p.splits, split = lid % p.splits;
@@ -726,104 +785,148 @@ __global__ __launch_bounds__(kThreads, (kBF16 && NTW == 1) ? 2 : 1) void tree_at
   const int k_begin = split * p.keys_per_split;
   const int tab0 = k_begin / p.bs;
 
-  // one round trip: parents, this split's block-table entries, sizes, and (MFMA
-  // path) this wave's query operands; rows past the request are masked later
-  constexpr int KQ = kBF16 ? D / 32 : 1;
-  constexpr int NQ = kBF16 ? NTW : 1;
-  tv_bf16x8 qop[NQ][KQ];
   if constexpr (kBF16) {
-    const int lane = t & 63, l16 = lane & 15, h4 = lane >> 4;
-    const int rbase = rt * RW + (t >> 6) * 16 * NTW;
+    // the ring: distinct LDS objects, one chunk each
+    __shared__ alignas(16) unsigned char ring0[Chunk<D>::BYTES];
+    __shared__ alignas(16) unsigned char ring1[Chunk<D>::BYTES];
+    __shared__ alignas(16) unsigned char ring2[Chunk<D>::BYTES];
+    __shared__ alignas(16) unsigned char ring3[Chunk<D>::BYTES];
+    __shared__ int tab[kMaxTab];   // (block, KV head) row index per block of this split
+    static_assert(kStages == 4, "one LDS object per ring slot");
+    unsigned char* const slots[kStages] = {ring0, ring1, ring2, ring3};
+
+    // one round trip: parents, this split's block-table entries, sizes and this
+    // wave's query operands (rows past the request are masked later)
+    constexpr int KQ = D / 32;
+    tv_bf16x8 qop[NTW][KQ];
+    if ((t >> 6) < kMfmaWaves) {
+      const int lane = t & 63, l16 = lane & 15, h4 = lane >> 4;
+      const int rbase = rt * RW + (t >> 6) * 16 * NTW;
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const int qrow = rbase + 16 * nt + l16;
-      const int node = min(qrow / p.G, p.n_max - 1), hh = qrow % p.G;
-      const uint16_t* qp =
-          (const uint16_t*)p.q + (((size_t)b * p.n_max + node) * p.Hq + (size_t)g * p.G + hh) * D + 8 * h4;
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int qrow = rbase + 16 * nt + l16;
+        const int node = min(qrow / p.G, p.n_max - 1), hh = qrow % p.G;
+        const uint16_t* qp =
+            (const uint16_t*)p.q + (((size_t)b * p.n_max + node) * p.Hq + (size_t)g * p.G + hh) * D + 8 * h4;
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) qop[nt][kk] = load_bf16x8(qp + 32 * kk);
+        for (int kk = 0; kk < KQ; ++kk) qop[nt][kk] = load_bf16x8(qp + 32 * kk);
+      }
     }
-  }
-  if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
-  if constexpr (kBF16) {
+    if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
     const int ntab = min(p.max_blocks - tab0, (p.keys_per_split + p.bs - 1) / p.bs + 1);
-    for (int i = t; i < ntab; i += kThreads) {
-      const int blk = trow[tab0 + i];
-      // row index of (block, KV head); ids outside the pool (flagged by the
-      // request's validation) read block 0 instead
-      u.r.tab[i] = (block_ok(blk, p.num_blocks) ? blk : 0) * p.Hkv + g;
+    {
+      for (int i = t; i < ntab; i += kMfmaThreads) {
+        const int blk = trow[tab0 + i];
+        // ids outside the pool (flagged by the request's validation) read block 0
+        tab[i] = (block_ok(blk, p.num_blocks) ? blk : 0) * p.Hkv + g;
+      }
     }
-  }
-  if (t == 0) cm.flag = 0;
-  const int n = p.n_nodes[b];
-  const int P = p.prefix_len[b];
-  __syncthreads();
+    if (t == 0) cm.flag = 0;
+    const int n = p.n_nodes[b];
+    const int P = p.prefix_len[b];
+    __syncthreads();   // also completes the query loads before any DMA is in flight
 
-  int flags = 0;
-  if (n < 1 || n > p.n_max) flags |= TV_REQ_BAD_NNODES;
-  else if (P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) flags |= TV_REQ_BAD_KV;
-  if (flags) {
-    if (designated && t == 0 && p.status) p.status[b] = flags;
-    return;
-  }
-  const int R = n * p.G;
-  const int r0 = rt * RW;
-  const int keys_total = P + n;
-  const int n_active = (keys_total + p.keys_per_split - 1) / p.keys_per_split;
-  const bool works = r0 < R && split < n_active;
-  const int k_end = min(k_begin + p.keys_per_split, keys_total);
-
-  // MFMA path: the first batch of K/V chunks goes out now, so its latency
-  // overlaps the rest of the prologue (the sizes are valid, so every key and
-  // block-table index stays inside this split's staged table); the barriers
-  // below are LDS-only and leave it in flight
-  constexpr int NBR = RingSmem<D, NTW>::NB;
-  ChunkRegs<D> cr[kBF16 ? NBR : 1];
-  const bool ring = kBF16 && works && R >= 16;
-  if constexpr (kBF16) {
-    if (ring) {
-      const int nchunks = (k_end - k_begin + 31) / 32;
-#pragma unroll
-      for (int i = 0; i < NBR; ++i)
-        if (i < nchunks) load_chunk<D>(p, u.r.tab, tab0, cr[i], k_begin + 32 * i, k_begin, k_end, t >> 6, t & 63);
-    }
-  }
-
-  // parent array: parent[0] = -1 and 0 <= parent[i] < i
-  if (t < n) {
-    const int pi = cm.par[t];
-    const bool ok = (t == 0) ? (pi == -1) : (pi >= 0 && pi < t);
-    if (!ok) cm.flag = 1;
-  }
-  tv_lds_barrier();
-  if (cm.flag) {
-    if (designated && t == 0 && p.status) p.status[b] = TV_REQ_BAD_PARENT;
-    return;
-  }
-  if (designated) {
-    // every block id used by positions [0, P + n) must name a pool block
-    const int nblk = (P + n + p.bs - 1) / p.bs;
-    for (int i = t; i < nblk; i += kThreads)
-      if (!block_ok(trow[i], p.num_blocks)) cm.flag = 1;
-    __syncthreads();
-    if (t == 0 && p.status) p.status[b] = cm.flag ? TV_REQ_BAD_KV : 0;
-    // keep going: loads from bad blocks are redirected or skipped
-  }
-  if (!works) return;
-  const bool tree_in_range = k_end > P;
-  if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
-  tv_lds_barrier();
-
-  if constexpr (kBF16) {
-    if (ring) {
-      attn_ring<kBF16, D, NTW>(p, cm, u.r, qop, cr, tile, split, n_active, b, g, r0, R, P, k_begin, k_end, tab0,
-                               tree_in_range);
+    if (n < 1 || n > p.n_max) {
+      if (designated && t == 0 && p.status) p.status[b] = TV_REQ_BAD_NNODES;
       return;
     }
+    if (P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) {
+      if (designated && t == 0 && p.status) p.status[b] = TV_REQ_BAD_KV;
+      return;
+    }
+    const int R = n * p.G;
+    const int r0 = rt * RW;
+    const int keys_total = P + n;
+    const int n_active = (keys_total + p.keys_per_split - 1) / p.keys_per_split;
+    const bool works = r0 < R && split < n_active;
+    const int k_end = min(k_begin + p.keys_per_split, keys_total);
+
+    // parent array: parent[0] = -1 and 0 <= parent[i] < i
+    if (t < n) {
+      const int pi = cm.par[t];
+      const bool ok = (t == 0) ? (pi == -1) : (pi >= 0 && pi < t);
+      if (!ok) cm.flag = 1;
+    }
+    tv_lds_barrier();
+    if (cm.flag) {
+      if (designated && t == 0 && p.status) p.status[b] = TV_REQ_BAD_PARENT;
+      return;
+    }
+    // The first chunks go out now, so their latency overlaps the rest of the
+    // prologue (the sizes are valid, so every key and block-table index stays
+    // inside this split's staged table).  From here on no workgroup leaves
+    // before its DMAs have landed, and the barriers are LDS-only.
+    const DmaLane dl = dma_lane<D>(p.bs, t & 63);
+    int2 next_rows = make_int2(0, 0);
+    if (works && (t >> 6) == kMfmaWaves) {
+      const int nchunks = (k_end - k_begin + 31) / 32;
+#pragma unroll
+      for (int i = 0; i < kStages - 1; ++i)
+        if (i < nchunks)
+          dma_chunk<D>(p, dl, chunk_rows(tab, tab0, ntab, k_begin + 32 * i, p.lbs), k_begin + 32 * i, slots[i]);
+      if (kStages - 1 < nchunks) next_rows = chunk_rows(tab, tab0, ntab, k_begin + 32 * (kStages - 1), p.lbs);
+    }
+    if (designated) {
+      // every block id used by positions [0, P + n) must name a pool block
+      const int nblk = (P + n + p.bs - 1) / p.bs;
+      for (int i = t; i < nblk; i += kMfmaThreads)
+        if (!block_ok(trow[i], p.num_blocks)) cm.flag = 1;
+      tv_lds_barrier();
+      if (t == 0 && p.status) p.status[b] = cm.flag ? TV_REQ_BAD_KV : 0;
+      // keep going: loads from bad blocks are redirected
+    }
+    if (!works) return;
+    const bool tree_in_range = k_end > P;
+    if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
+    tv_lds_barrier();
+    attn_mfma<D, NTW>(p, cm, tab, slots, qop, dl, next_rows, tile, split, n_active, b, g, r0, R, P, k_begin, k_end,
+                      tab0, ntab, tree_in_range);
+  } else {
+    __shared__ ValuSmem<D> vs;
+    if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
+    if (t == 0) cm.flag = 0;
+    const int n = p.n_nodes[b];
+    const int P = p.prefix_len[b];
+    __syncthreads();
+
+    int flags = 0;
+    if (n < 1 || n > p.n_max) flags |= TV_REQ_BAD_NNODES;
+    else if (P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) flags |= TV_REQ_BAD_KV;
+    if (flags) {
+      if (designated && t == 0 && p.status) p.status[b] = flags;
+      return;
+    }
+    const int R = n * p.G;
+    const int r0 = rt * RW;
+    const int keys_total = P + n;
+    const int n_active = (keys_total + p.keys_per_split - 1) / p.keys_per_split;
+    const bool works = r0 < R && split < n_active;
+    const int k_end = min(k_begin + p.keys_per_split, keys_total);
+    if (t < n) {
+      const int pi = cm.par[t];
+      const bool ok = (t == 0) ? (pi == -1) : (pi >= 0 && pi < t);
+      if (!ok) cm.flag = 1;
+    }
+    __syncthreads();
+    if (cm.flag) {
+      if (designated && t == 0 && p.status) p.status[b] = TV_REQ_BAD_PARENT;
+      return;
+    }
+    if (designated) {
+      const int nblk = (P + n + p.bs - 1) / p.bs;
+      for (int i = t; i < nblk; i += kThreads)
+        if (!block_ok(trow[i], p.num_blocks)) cm.flag = 1;
+      __syncthreads();
+      if (t == 0 && p.status) p.status[b] = cm.flag ? TV_REQ_BAD_KV : 0;
+    }
+    if (!works) return;
+    const bool tree_in_range = k_end > P;
+    if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
+    __syncthreads();
+    const int rows = min(RW, R - r0);
+    attn_valu<false, D>(p, vs, b, g, r0, rows, P, k_begin, k_end, tree_in_range, cm.anc);
+    emit_valu<false, D, RW>(p, cm, vs, tile, split, n_active, b, g, r0, rows);
   }
-  const int rows = min(min(RW, R - r0), 16);
-  attn_valu<kBF16, D>(p, u.v, b, g, r0, rows, P, k_begin, k_end, tree_in_range, cm.anc);
-  emit_valu<kBF16, D, RW>(p, cm, u.v, tile, split, n_active, b, g, r0, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -844,14 +947,16 @@ int check_desc(const tv_attn_desc* d) {
   return TV_OK;
 }
 
-// Rows per MFMA workgroup: 64 * NTW.  Wider tiles cut the re-reads of each
-// KV chunk (one per row tile) but leave fewer tiles to spread over the CUs.
+// Rows per MFMA workgroup: 64 * NTW.  Every MFMA wave reads each chunk's 16 KB
+// of operands from LDS once per 16*NTW rows, so wider tiles spend less on LDS
+// reads and re-read each chunk from HBM / L2 fewer times (once per row tile),
+// but leave fewer tiles to spread over the CUs (more key splits to merge).
+// NTW = 2 when its tiles alone cover a quarter of the CUs.
 int choose_ntw(const tv_attn_desc* d, int cu) {
   if (d->dtype != TV_BF16) return 1;
   const long long R = (long long)d->n_max * (d->n_q_heads / d->n_kv_heads);
   const long long pairs = (long long)d->batch * d->n_kv_heads;
-  if (R >= 256 && pairs * ((R + 255) / 256) * 2 >= cu) return 4;
-  if (R >= 128 && pairs * ((R + 127) / 128) * 2 >= cu) return 2;
+  if (R >= 128 && pairs * ((R + 127) / 128) * 4 >= cu) return 2;
   return 1;
 }
 
@@ -883,7 +988,8 @@ int make_plan(const tv_attn_desc* d, int cu, int wg_per_cu, int ntw, AttnPlan* p
   const size_t tiles = (size_t)base;
   size_t bytes = 0;
   if (pl->splits > 1) {
-    bytes = tiles * pl->splits * pl->rows_per_tile * (size_t)d->head_dim * sizeof(float);
+    const size_t esz = d->dtype == TV_BF16 ? 2 : 4;   // partial O element: fp16 for bf16 inputs
+    bytes = tiles * pl->splits * pl->rows_per_tile * (size_t)d->head_dim * esz;
     pl->off_ml = tv_align_up(bytes, 256);
     bytes = pl->off_ml + tiles * pl->splits * pl->rows_per_tile * 2 * sizeof(float);
   } else {
@@ -899,14 +1005,14 @@ AttnKernel pick_kernel(const tv_attn_desc* d, int ntw) {
   const bool bf = d->dtype == TV_BF16;
   if (d->head_dim == 128) {
     if (!bf) return tree_attn_kernel<false, 128, 1>;
-    return ntw == 4 ? tree_attn_kernel<true, 128, 4> : ntw == 2 ? tree_attn_kernel<true, 128, 2> : tree_attn_kernel<true, 128, 1>;
+    return ntw == 2 ? tree_attn_kernel<true, 128, 2> : tree_attn_kernel<true, 128, 1>;
   }
   if (!bf) return tree_attn_kernel<false, 64, 1>;
-  return ntw == 4 ? tree_attn_kernel<true, 64, 4> : ntw == 2 ? tree_attn_kernel<true, 64, 2> : tree_attn_kernel<true, 64, 1>;
+  return ntw == 2 ? tree_attn_kernel<true, 64, 2> : tree_attn_kernel<true, 64, 1>;
 }
 
 // Resident workgroups per CU of one kernel instance on the current device (cached).
-int occupancy(AttnKernel k, int* out) {
+int occupancy(AttnKernel k, int threads, int* out) {
   static std::mutex mu;
   static const void* keys[16];
   static int vals[16];
@@ -921,7 +1027,7 @@ int occupancy(AttnKernel k, int* out) {
       return TV_OK;
     }
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, kThreads, 0) != hipSuccess) return TV_ERR_HIP;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, threads, 0) != hipSuccess) return TV_ERR_HIP;
   if (nb < 1) nb = 1;
   if (n < 16) {
     keys[n] = (const void*)k;
@@ -939,7 +1045,7 @@ int plan_for(const tv_attn_desc* d, AttnPlan* pl, AttnKernel* kern) {
   if (rc != TV_OK) return rc;
   const int ntw = choose_ntw(d, cu);
   AttnKernel k = pick_kernel(d, ntw);
-  rc = occupancy(k, &occ);
+  rc = occupancy(k, d->dtype == TV_BF16 ? kMfmaThreads : kThreads, &occ);
   if (rc != TV_OK) return rc;
   rc = make_plan(d, cu, occ, ntw, pl);
   if (kern) *kern = k;
@@ -983,7 +1089,7 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   p.parent = parent;
   p.out = out;
   p.status = status;
-  p.part_o = (float*)workspace;
+  p.part_o = workspace;
   p.part_ml = (float*)((char*)workspace + pl.off_ml);
   p.B = desc->batch;
   p.n_max = desc->n_max;
@@ -1004,7 +1110,7 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   const long long total = (long long)desc->batch * desc->n_kv_heads * pl.row_tiles * pl.splits;
   if (total > 0x7fffffff) return TV_ERR_UNSUPPORTED;
   p.total = (int)total;
-  hipLaunchKernelGGL(kern, dim3(p.total), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(kern, dim3(p.total), dim3(desc->dtype == TV_BF16 ? kMfmaThreads : kThreads), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (pl.splits > 1) {
     const long long tiles = (long long)desc->batch * desc->n_kv_heads * pl.row_tiles;
