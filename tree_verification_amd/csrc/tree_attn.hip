@@ -48,9 +48,14 @@ constexpr int kMfmaWaves = 4;        // MFMA path: four waves own the rows ...
 constexpr int kMfmaThreads = 64 * (kMfmaWaves + 1);   // ... and a fifth moves the K/V chunks
 constexpr int kMaxNodes = 128;
 constexpr int kMaxSplits = 32;        // key splits per (request, KV head, row tile)
-constexpr int kMaxKeysPerSplit = 32768;
+constexpr int kMaxKeysPerSplit = 32768;   // NTW = 1 (two workgroups per CU); twice that for NTW = 2
 constexpr int kStages = 4;            // LDS ring slots (chunks in flight) on the MFMA path
-constexpr int kMaxTab = kMaxKeysPerSplit / 16 + 2;   // block-table entries staged per workgroup
+// Keys one split may own, and the block-table entries a workgroup stages for
+// them (block size 16 at least).
+template <int NTW>
+constexpr int max_keys_per_split() { return NTW == 1 ? kMaxKeysPerSplit : 2 * kMaxKeysPerSplit; }
+template <int NTW>
+constexpr int max_tab() { return max_keys_per_split<NTW>() / 16 + 2; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -397,61 +402,97 @@ __device__ __forceinline__ void store_out4(const AttnParams& p, int b, int g, in
 }
 
 // Split-K merge, a second kernel: for every tile whose request used more than
-// one key split, combine the splits' (m, l, O) partials by log-sum-exp and
+// one key split, combine the splits' (m, l, O/l) partials by log-sum-exp and
 // write the output rows.  The kernel boundary makes the partials visible (no
-// inter-workgroup fences or counters).  One workgroup per 16 rows of a tile.
-constexpr int kMergeRows = 4;
+// inter-workgroup fences or counters).  A thread owns 8 d values of one row
+// and walks the splits in batches whose loads are in flight together,
+// rescaling its running sum when a batch raises the row's max.
+constexpr int kMergeThreads = 128;
+constexpr int kMergeVec = 8;     // d values per thread
+constexpr int kMergeBatch = 8;   // splits loaded together
 
 template <int D>
-constexpr int merge_threads() { return kMergeRows * (D / 4); }   // one float4 item per thread
+constexpr int merge_rows() { return kMergeThreads / (D / kMergeVec); }   // rows per workgroup
+
+template <bool kBF16>
+__device__ __forceinline__ void load_part8(const void* part_o, size_t off, float (&o)[kMergeVec]) {
+  const tv_f32x4 lo = load_part4<kBF16>(part_o, off), hi = load_part4<kBF16>(part_o, off + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[i] = lo[i];
+    o[4 + i] = hi[i];
+  }
+}
 
 template <bool kBF16, int D>
-__global__ __launch_bounds__(merge_threads<D>()) void attn_merge_kernel(AttnParams p) {
-  constexpr int ITEMS = merge_threads<D>();
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p) {
+  constexpr int TPR = D / kMergeVec, RPB = merge_rows<D>();
   const int t = threadIdx.x;
-  const int groups = (p.rows_per_tile + kMergeRows - 1) / kMergeRows;
+  const int groups = (p.rows_per_tile + RPB - 1) / RPB;
   const int tile = blockIdx.x / groups, rg = blockIdx.x % groups;
   const int bg = tile / p.row_tiles, rt = tile % p.row_tiles;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
-  const size_t base = (size_t)tile * p.splits * p.rows_per_tile + (size_t)rg * kMergeRows;
-  // issue every load first: sizes, each split's (m, l) and O pieces of this thread's item
+  const int r = rg * RPB + t / TPR, d = kMergeVec * (t % TPR);   // row within the tile, first d
+  const bool in_tile = r < p.rows_per_tile;
+  const size_t base = (size_t)tile * p.splits * p.rows_per_tile + r;
+  // the first batch of partials goes out with the sizes (always inside the workspace)
   const int n = p.n_nodes[b];
   const int P = p.prefix_len[b];
-  const int r = t / (D / 4), d = 4 * (t % (D / 4));
-  float2 ml[kMaxSplits];
-  tv_f32x4 o[kMaxSplits];
-  const bool item = t < ITEMS;
+  float2 ml[kMergeBatch];
+  float o[kMergeBatch][kMergeVec];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < p.splits && item) {
-      const size_t pr = base + (size_t)s * p.rows_per_tile + r;
+  for (int s = 0; s < kMergeBatch; ++s) {
+    if (s < p.splits && in_tile) {
+      const size_t pr = base + (size_t)s * p.rows_per_tile;
       ml[s] = *(const float2*)&p.part_ml[pr * 2];
-      o[s] = load_part4<kBF16>(p.part_o, pr * D + d);
+      load_part8<kBF16>(p.part_o, pr * D + d, o[s]);
     }
   }
   if (n < 1 || n > p.n_max || P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) return;
   const int n_active = (P + n + p.keys_per_split - 1) / p.keys_per_split;
   if (n_active < 2) return;                 // written directly by the attention kernel
-  const int R = n * p.G;
-  const int row = rt * p.rows_per_tile + rg * kMergeRows + r;
-  if (!item || row >= R || row >= (rt + 1) * p.rows_per_tile) return;
-  float M = kNegInf;
+  const int row = rt * p.rows_per_tile + r;
+  if (!in_tile || row >= n * p.G) return;
+  float M = kNegInf, L = 0.f, acc[kMergeVec];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s)
-    if (s < n_active) M = fmaxf(M, ml[s].x);
-  float L = 0.f;
-  tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kMergeVec; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < n_active; s0 += kMergeBatch) {
+    if (s0 > 0) {
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < n_active) {
-      const float w = (ml[s].x == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[s].x - M) * ml[s].y;
-      L += w;
-      acc += w * o[s];
+      for (int s = 0; s < kMergeBatch; ++s) {
+        if (s0 + s < n_active) {
+          const size_t pr = base + (size_t)(s0 + s) * p.rows_per_tile;
+          ml[s] = *(const float2*)&p.part_ml[pr * 2];
+          load_part8<kBF16>(p.part_o, pr * D + d, o[s]);
+        }
+      }
+    }
+    float mb = kNegInf;
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s)
+      if (s0 + s < n_active) mb = fmaxf(mb, ml[s].x);
+    if (mb > M) {   // the batch raises the row's max: rescale what is summed so far
+      const float sc = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - mb);
+      L *= sc;
+#pragma unroll
+      for (int i = 0; i < kMergeVec; ++i) acc[i] *= sc;
+      M = mb;
+    }
+#pragma unroll
+    for (int s = 0; s < kMergeBatch; ++s) {
+      if (s0 + s < n_active && ml[s].x != kNegInf) {
+        const float w = __builtin_amdgcn_exp2f(ml[s].x - M) * ml[s].y;
+        L += w;
+#pragma unroll
+        for (int i = 0; i < kMergeVec; ++i) acc[i] += w * o[s][i];
+      }
     }
   }
   const float inv = 1.f / L;
   float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
   store_out4<kBF16, D>(p, b, g, row, d, v4);
+  float w4[4] = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  store_out4<kBF16, D>(p, b, g, row, d + 4, w4);
 }
 
 // VALU path output: rows [r0, r0 + rows) are in LDS.
@@ -791,7 +832,7 @@ __global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())
     __shared__ alignas(16) unsigned char ring1[Chunk<D>::BYTES];
     __shared__ alignas(16) unsigned char ring2[Chunk<D>::BYTES];
     __shared__ alignas(16) unsigned char ring3[Chunk<D>::BYTES];
-    __shared__ int tab[kMaxTab];   // (block, KV head) row index per block of this split
+    __shared__ int tab[max_tab<NTW>()];   // (block, KV head) row index per block of this split
     static_assert(kStages == 4, "one LDS object per ring slot");
     unsigned char* const slots[kStages] = {ring0, ring1, ring2, ring3};
 
@@ -976,9 +1017,10 @@ int make_plan(const tv_attn_desc* d, int cu, int wg_per_cu, int ntw, AttnPlan* p
   long long max_splits = (max_keys + 127) / 128;
   if (max_splits > kMaxSplits) max_splits = kMaxSplits;
   if (splits > max_splits) splits = max_splits;
-  const long long min_splits = (max_keys + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
+  const long long max_kps = ntw == 1 ? max_keys_per_split<1>() : max_keys_per_split<2>();
+  const long long min_splits = (max_keys + max_kps - 1) / max_kps;
   if (splits < min_splits) splits = min_splits;
-  if (splits > kMaxSplits) return TV_ERR_UNSUPPORTED;   // keys per sequence beyond 32 * 32768
+  if (splits > kMaxSplits) return TV_ERR_UNSUPPORTED;   // keys per sequence beyond 32 splits of the maximum
   if (splits < 1) splits = 1;
   long long kps = (max_keys + splits - 1) / splits;
   kps = (kps + 31) / 32 * 32;
@@ -1114,13 +1156,13 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (pl.splits > 1) {
     const long long tiles = (long long)desc->batch * desc->n_kv_heads * pl.row_tiles;
-    const long long grid = tiles * ((pl.rows_per_tile + kMergeRows - 1) / kMergeRows);
+    const int rpb = desc->head_dim == 128 ? merge_rows<128>() : merge_rows<64>();
+    const long long grid = tiles * ((pl.rows_per_tile + rpb - 1) / rpb);
     if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
     const bool bf = desc->dtype == TV_BF16;
     void (*mk)(AttnParams) = desc->head_dim == 128 ? (bf ? attn_merge_kernel<true, 128> : attn_merge_kernel<false, 128>)
                                                    : (bf ? attn_merge_kernel<true, 64> : attn_merge_kernel<false, 64>);
-    const int mthreads = desc->head_dim == 128 ? merge_threads<128>() : merge_threads<64>();
-    hipLaunchKernelGGL(mk, dim3((unsigned)grid), dim3(mthreads), 0, stream, p);
+    hipLaunchKernelGGL(mk, dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   }
   return TV_OK;
