@@ -92,16 +92,23 @@ __device__ __forceinline__ void load16(__amdgpu_buffer_rsrc_t rs, int e0, float*
   }
 }
 
-// Children of u among nodes [1, n) of a parent row, ascending, written by wave 0
-// into kids[]; returns the count to lane 0 of wave 0 (n <= 128: two ballots).
-__device__ __forceinline__ int collect_children(const int32_t* par, int n, int u, int* kids) {
+// Children of u among nodes [1, n), ascending, written by one wave into kids[]
+// with their tokens in ktok[]; returns the count to every lane (n <= 128: two
+// ballots).  pv0 / pv1 and tk0 / tk1: parent and token of nodes 1 + l and
+// 65 + l (parent -1 past the request).
+__device__ __forceinline__ int collect_children(int pv0, int pv1, int tk0, int tk1, int u, int* kids, int* ktok) {
   const int l = threadIdx.x & 63;
-  const bool k0 = (1 + l < n) && par[1 + l] == u;
-  const bool k1 = (65 + l < n) && par[65 + l] == u;
+  const bool k0 = pv0 == u, k1 = pv1 == u;
   const unsigned long long b0 = __ballot(k0), b1 = __ballot(k1);
   const unsigned long long below = (1ull << l) - 1ull;
-  if (k0) kids[__popcll(b0 & below)] = 1 + l;
-  if (k1) kids[__popcll(b0) + __popcll(b1 & below)] = 65 + l;
+  if (k0) {
+    kids[__popcll(b0 & below)] = 1 + l;
+    ktok[__popcll(b0 & below)] = tk0;
+  }
+  if (k1) {
+    kids[__popcll(b0) + __popcll(b1 & below)] = 65 + l;
+    ktok[__popcll(b0) + __popcll(b1 & below)] = tk1;
+  }
   return __popcll(b0) + __popcll(b1);
 }
 
@@ -330,9 +337,10 @@ struct NodeSmem {
   float rowM[2];          // team row maxima and exponential sums
   double rowS[2];
   double scan[kSThreads / 64];
-  int kids[kMaxNodes];
+  int wcross[kSThreads / 64], wlast[kSThreads / 64];   // per wave: first crossing lane, last lane with mass
+  int kids[kMaxNodes], ktok[kMaxNodes];
   float kzp[kMaxNodes], kzq[kMaxNodes], kua[kMaxNodes];   // per child: logits of its token, its uniform
-  int nk, bad, timeout, owner, sel, res_sel, res_last, res_tok;
+  int nk, bad, badtok, timeout, owner, sel, res_tok;
   double base, thr;
   // draft exponentials of the resident slice, [chunk][group of 4][thread]
   tv_f32x4 qe[kRes ? kResident * 4 * kSThreads : 1];
@@ -388,13 +396,13 @@ __device__ void batch_stats(NodeSmem<kRes>& sm, float (&xp)[kResident][16], floa
     }
   }
   if (__ballot(bad != 0) != 0ull && l == 0) sm.bad = 1;
-  __syncthreads();
+  tv_lds_barrier();
   if (t < 2 * nb) {
     double s = 0.0;
     for (int i = 0; i < kSThreads / 64; ++i) s += sm.red_d[i][t];
     sm.cs[t & 1][j0 + (t >> 1)] = s;
   }
-  __syncthreads();   // the next batch may overwrite red_f / red_d
+  tv_lds_barrier();   // the next batch may overwrite red_f / red_d
 }
 
 // Publish one 64-bit word in slot `slot` (top bit marks it written).
@@ -417,37 +425,47 @@ __device__ __forceinline__ unsigned long long xch_get(unsigned long long* slot, 
 }
 
 // Inverse CDF inside one chunk: the smallest index whose running mass (from
-// `base`) exceeds thr.  Thread ranges come from one scan of the per-thread
-// sums; only the first thread whose range ends past thr walks its 16 weights.
-// When rounding leaves no such thread, or no weight of that thread crosses, the
-// last positive weight at or before it is taken.  w: this thread's 16 weights.
+// `base`) exceeds thr.  The thread ranges come from a wave scan of the
+// per-thread sums and the waves' totals; the first thread with mass whose
+// range ends past thr (found by ballots) walks its 16 weights.  When rounding
+// leaves no such thread, or no weight of that thread crosses, the last
+// positive weight at or before it is taken.  w: this thread's 16 weights.
 // Returns the index to every thread.
 template <class Smem>
 __device__ int chunk_draw(Smem& sm, const double (&w)[16], int e0, double base, double thr, int fallback) {
+  constexpr int NW = kSThreads / 64;
   const int t = threadIdx.x, wv = t >> 6, ln = t & 63;
-  double loc = 0.0;
+  double loc;
+  {
+    double a[8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) loc += w[j];
-  double incl = loc;
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(incl, o);
-    incl += (ln >= o) ? y : 0.0;
+    for (int j = 0; j < 8; ++j) a[j] = w[2 * j] + w[2 * j + 1];
+    loc = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   }
+  const double incl = tv_wave_incl_scan_d(loc, ln);
   if (ln == 63) sm.scan[wv] = incl;
-  if (t == 0) {
-    sm.res_sel = 0x7fffffff;
-    sm.res_last = -1;
+  tv_lds_barrier();
+  double off = base;   // mass before this wave
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (i < wv) off += sm.scan[i];
+  const double lo = off + (incl - loc);   // mass before this thread
+  const uint64_t cross = __ballot(loc > 0.0 && lo + loc > thr), pos = __ballot(loc > 0.0);
+  if (ln == 0) {
+    sm.wcross[wv] = cross ? __builtin_ctzll(cross) : -1;
+    sm.wlast[wv] = pos ? 63 - __builtin_clzll(pos) : -1;
   }
-  __syncthreads();
-  double lo = base;
-  for (int i = 0; i < wv; ++i) lo += sm.scan[i];
-  lo += incl - loc;
-  if (loc > 0.0 && lo + loc > thr) atomicMin(&sm.res_sel, t);   // candidate thread
-  if (loc > 0.0) atomicMax(&sm.res_last, t);
-  __syncthreads();
-  const int ct = sm.res_sel != 0x7fffffff ? sm.res_sel : sm.res_last;
-  if (t == 0) sm.res_tok = fallback;
-  __syncthreads();
+  tv_lds_barrier();
+  int ct = -1;
+#pragma unroll
+  for (int i = NW - 1; i >= 0; --i)
+    if (sm.wcross[i] >= 0) ct = 64 * i + sm.wcross[i];
+  if (ct < 0) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      if (sm.wlast[i] >= 0) ct = 64 * i + sm.wlast[i];
+  }
+  if (ct < 0) return fallback;   // no mass in the chunk
   if (t == ct) {
     double run = lo;
     int found = -1, lastw = -1;
@@ -463,23 +481,32 @@ __device__ int chunk_draw(Smem& sm, const double (&w)[16], int e0, double base, 
     }
     sm.res_tok = found >= 0 ? found : lastw;
   }
-  __syncthreads();
+  tv_lds_barrier();
   return sm.res_tok;
 }
 
 // First index of `m[0..count)` (in order) whose running sum from `base`
 // exceeds thr, with the running sum before it; the last positive entry (and the
 // full sum) when rounding leaves none.
+// (LDS reads go out eight at a time, ahead of the dependent sums.)
 __device__ __forceinline__ int select_mass(const double* m, int count, double thr, double* base) {
   int sel = -1, lastpos = 0;
   double cum = *base, b = *base;
-  for (int i = 0; i < count; ++i) {
-    if (m[i] > 0.0) lastpos = i;
-    if (sel < 0 && cum + m[i] > thr) {
-      sel = i;
-      b = cum;
+  for (int i0 = 0; i0 < count; i0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = i0 + j < count ? m[i0 + j] : 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (i0 + j < count) {
+        if (v[j] > 0.0) lastpos = i0 + j;
+        if (sel < 0 && cum + v[j] > thr) {
+          sel = i0 + j;
+          b = cum;
+        }
+        cum += v[j];
+      }
     }
-    cum += m[i];
   }
   if (sel < 0) {
     sel = lastpos;
@@ -524,6 +551,8 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
   // behind it) shows that u has children
   const int pv0 = (1 + l < n) ? par[1 + l] : -1;
   const int pv1 = (65 + l < n) ? par[65 + l] : -1;
+  const int tk0 = (w == 0 && 1 + l < n) ? tok[1 + l] : 0;   // tokens, for the children's accept tests
+  const int tk1 = (w == 0 && 65 + l < n) ? tok[65 + l] : 0;
   const float us = p.u_sample[k];
   float ep[kResident][16], eq[kResident][16];
 #pragma unroll
@@ -535,12 +564,27 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     for (int r = 0; r < kResident; ++r)
       if (r < nmine) load16<kVec>(zq_rs, (my_c0 + r) * kChunk + 16 * t, eq[r]);
   }
+  // wave 0: the children, and the logits and uniforms their accept tests read
+  // (issued now, behind the slice's loads, so they arrive with them instead of
+  // a round trip after the statistics)
+  // (children past the first 64 are read after the statistics)
+  float kzp_v = 0.f, kzq_v = 0.f, kua_v = 0.f;
+  int badtok = 0;
   if (w == 0) {
-    const int c = collect_children(par, n, u, sm.kids);
+    const int c = collect_children(pv0, pv1, tk0, tk1, u, sm.kids, sm.ktok);
     if (l == 0) {
       sm.nk = c;
       sm.bad = 0;
+      sm.badtok = 0;
       sm.timeout = 0;
+    }
+    if (l < c) {
+      const int x = sm.ktok[l];
+      badtok = x < 0 || x >= p.V;
+      const int xs = badtok ? 0 : x;
+      kzp_v = zp_row[xs];
+      kzq_v = zq_row[xs];
+      kua_v = p.u_accept[(size_t)b * p.n_max + sm.kids[l]];
     }
   }
 
@@ -564,15 +608,19 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
         sm.qe[(r * 4 + g) * kSThreads + t] = tv_f32x4{eq[r][4 * g], eq[r][4 * g + 1], eq[r][4 * g + 2], eq[r][4 * g + 3]};
   }
   const int nk = sm.nk;
-  int badtok = 0;
-  if (t < nk) {   // tokens proposed by the children, and what their accept tests read
-    const int c = sm.kids[t];
-    const int x = tok[c];
-    badtok = (x < 0 || x >= p.V);
-    const int xs = badtok ? 0 : x;
-    sm.kzp[t] = zp_row[xs];
-    sm.kzq[t] = zq_row[xs];
-    sm.kua[t] = p.u_accept[(size_t)b * p.n_max + c];
+  if (t < nk) {
+    if (t < 64) {
+      sm.kzp[t] = kzp_v;
+      sm.kzq[t] = kzq_v;
+      sm.kua[t] = kua_v;
+    } else {
+      const int x = sm.ktok[t];
+      badtok = x < 0 || x >= p.V;
+      const int xs = badtok ? 0 : x;
+      sm.kzp[t] = zp_row[xs];
+      sm.kzq[t] = zq_row[xs];
+      sm.kua[t] = p.u_accept[(size_t)b * p.n_max + sm.kids[t]];
+    }
   }
   const int bad = sm.bad;
   if (bad && t == 0) atomicOr(&p.node_flags[k], TV_REQ_NONFINITE);
@@ -605,7 +653,9 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     else
       sm.xm[row][mem] = __uint_as_float((uint32_t)v);
   }
-  badtok = __syncthreads_or(badtok);
+  if (badtok) sm.badtok = 1;
+  tv_lds_barrier();   // (LDS-only barriers below: no wave waits here for its exchange stores to land)
+  badtok = sm.badtok;
   if (badtok) {   // the request fails
     if (member == 0 && t == 0) atomicOr(&p.node_flags[k], TV_REQ_BAD_TOKEN);
     return;
@@ -623,7 +673,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
       sm.rowS[row] = e;
     }
   }
-  __syncthreads();
+  tv_lds_barrier();
   const float Mp = sm.rowM[0], Mq = sm.rowM[1];
   const double Sp = sm.rowS[0], Sq = sm.rowS[1];
   if (!isfinite(Sp) || (internal && !isfinite(Sq))) return;   // some member saw a non-finite logit
@@ -634,7 +684,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     sm.ca[0][t] = exp((double)(sm.cm[0][t] - Mp) * p.invT_d) * ip;
     sm.ca[1][t] = internal ? exp((double)(sm.cm[1][t] - Mq) * p.invT_d) * iq : 0.0;
   }
-  __syncthreads();
+  tv_lds_barrier();
 
   // children in ascending id, one team-wide evaluation of F per rejection
   double Cres = 0.0, Dres = 1.0;
@@ -685,22 +735,31 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
         }
       }
     }
-    __syncthreads();
+    tv_lds_barrier();
     if (t < nmine) {
       double s = 0.0;
       for (int i2 = 0; i2 < kSThreads / 64; ++i2) s += sm.part[i2][t];
       sm.rlast[t] = s;
     }
-    __syncthreads();
+    tv_lds_barrier();
     double mine = 0.0;
-    for (int j = 0; j < nmine; ++j) mine += sm.rlast[j];
+    for (int j0 = 0; j0 < nmine; j0 += 8) {   // reads ahead of the dependent sums, same order
+      double v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = j0 + j < nmine ? sm.rlast[j0 + j] : 0.0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j0 + j < nmine) mine += v[j];
+    }
     // publish this member's mass for this rejection, gather the team's
     unsigned long long* xs = p.xch + ((size_t)b * p.n_max + sm.kids[i]) * kMaxTeam;
     if (t == 0) xch_put(xs + member, (unsigned long long)__double_as_longlong(mine));
     if (t < p.S) sm.xv[t] = __longlong_as_double((long long)xch_get(xs + t, &sm.timeout));
-    __syncthreads();
+    tv_lds_barrier();
     double F = 0.0;
-    for (int s = 0; s < p.S; ++s) F += sm.xv[s];
+#pragma unroll
+    for (int s = 0; s < kMaxTeam; ++s)
+      if (s < p.S) F += sm.xv[s];
     if (F > 0.0) {   // Z > 0: move to the new residual
       Cres = cn;
       Dres = F;
@@ -718,10 +777,12 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
       if (t < p.S) sm.xcur[t] = sm.xs[0][t] * exp((double)(sm.xm[0][t] - Mp) * p.invT_d) * ip;   // parallel over members
       if (t < nmine) sm.rcur[t] = sm.cs[0][t] * sm.ca[0][t];
     }
-    __syncthreads();
+    tv_lds_barrier();
     if (t == 0) {
       double total = 0.0;
-      for (int s = 0; s < p.S; ++s) total += sm.xcur[s];
+#pragma unroll
+      for (int s = 0; s < kMaxTeam; ++s)
+        if (s < p.S) total += sm.xcur[s];
       const double thr = (double)us * total;
       double base = 0.0;
       const int ms = select_mass(sm.xcur, p.S, thr, &base);
@@ -730,7 +791,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
       sm.base = base;
       sm.thr = thr;
     }
-    __syncthreads();
+    tv_lds_barrier();
     if (sm.owner == member && nmine > 0) {
       const int j = min(sm.sel, nmine - 1);
       const int e0 = (my_c0 + j) * kChunk + 16 * t;

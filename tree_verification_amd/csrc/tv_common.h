@@ -119,6 +119,30 @@ __device__ __forceinline__ double tv_row16_sum_d(double v) {
   return v;
 }
 
+// Inclusive prefix sums of doubles over the wave: shifts by 1, 2, 4 and 8
+// lanes inside each row of 16 (lanes shifted in from outside the row read 0),
+// then the rows' totals (lanes 15, 31, 47) added in row order.
+__device__ __forceinline__ double tv_wave_incl_scan_d(double x, int lane) {
+  auto shifted = [](double v, auto sel) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    return __longlong_as_double((long long)(((uint64_t)sel((uint32_t)(b >> 32)) << 32) | sel((uint32_t)b)));
+  };
+  x += shifted(x, [](uint32_t v) { return tv_dpp<0x111>(v); });   // row_shr:1
+  x += shifted(x, [](uint32_t v) { return tv_dpp<0x112>(v); });   // row_shr:2
+  x += shifted(x, [](uint32_t v) { return tv_dpp<0x114>(v); });   // row_shr:4
+  x += shifted(x, [](uint32_t v) { return tv_dpp<0x118>(v); });   // row_shr:8
+  auto lane_d = [](double v, int src) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  };
+  const double r0 = lane_d(x, 15), r1 = lane_d(x, 31), r2 = lane_d(x, 47);
+  const double o1 = r0, o2 = r0 + r1, o3 = o2 + r2;
+  const int row = lane >> 4;
+  return x + (row == 0 ? 0.0 : row == 1 ? o1 : row == 2 ? o2 : o3);
+}
+
 // Combine the four rows of 16 lanes (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float tv_rows_max(float v) {
   auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
