@@ -88,6 +88,7 @@ CASES = [
     ("llama8b", dict(vocab=1001, n_nodes=40)),         # vocabulary not a multiple of 4
     ("llama8b", dict(vocab=16389, n_nodes=50, tree="star")),   # wide node: many siblings
     ("llama8b", dict(vocab=3000, n_nodes=1)),          # root only
+    ("chain", dict(batch=16, prefix=1, vocab=36001)),  # 9 chunks: a team of 8, three members own no chunk
 ]
 
 

@@ -340,6 +340,7 @@ struct NodeSmem {
   int wcross[kSThreads / 64], wlast[kSThreads / 64];   // per wave: first crossing lane, last lane with mass
   int kids[kMaxNodes], ktok[kMaxNodes];
   float kzp[kMaxNodes], kzq[kMaxNodes], kua[kMaxNodes];   // per child: logits of its token, its uniform
+  double kpx[kMaxNodes], kqx[kMaxNodes];                   // ... and p(x), q(x) of that token
   int nk, bad, badtok, timeout, owner, sel, res_tok;
   double base, thr;
   // draft exponentials of the resident slice, [chunk][group of 4][thread]
@@ -485,35 +486,29 @@ __device__ int chunk_draw(Smem& sm, const double (&w)[16], int e0, double base, 
   return sm.res_tok;
 }
 
-// First index of `m[0..count)` (in order) whose running sum from `base`
-// exceeds thr, with the running sum before it; the last positive entry (and the
-// full sum) when rounding leaves none.
-// (LDS reads go out eight at a time, ahead of the dependent sums.)
-__device__ __forceinline__ int select_mass(const double* m, int count, double thr, double* base) {
-  int sel = -1, lastpos = 0;
-  double cum = *base, b = *base;
-  for (int i0 = 0; i0 < count; i0 += 8) {
-    double v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = i0 + j < count ? m[i0 + j] : 0.0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (i0 + j < count) {
-        if (v[j] > 0.0) lastpos = i0 + j;
-        if (sel < 0 && cum + v[j] > thr) {
-          sel = i0 + j;
-          b = cum;
-        }
-        cum += v[j];
-      }
+// First index of m[0..count) (in order, count <= 128) whose running sum from
+// *base exceeds thr, with the running sum before it in *base; the last
+// positive entry (0 when none) and the full sum when rounding leaves none.
+// One wave, 64 entries per scan; every lane gets the result.
+__device__ int wave_select_mass(const double* m, int count, double thr, double* base, int lane) {
+  double b0 = *base;
+  int lastpos = 0;
+  for (int h0 = 0; h0 < count; h0 += 64) {
+    const int i = h0 + lane;
+    const double x = i < count ? m[i] : 0.0;
+    const double incl = tv_wave_incl_scan_d(x, lane);
+    const uint64_t hit = __ballot(i < count && b0 + incl > thr);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      *base = b0 + tv_readlane_d(incl - x, f);
+      return h0 + f;
     }
+    const uint64_t pos = __ballot(i < count && x > 0.0);
+    if (pos) lastpos = h0 + 63 - __builtin_clzll(pos);
+    b0 += tv_readlane_d(incl, 63);
   }
-  if (sel < 0) {
-    sel = lastpos;
-    b = cum;
-  }
-  *base = b;
-  return sel;
+  *base = b0;
+  return lastpos;
 }
 
 // One team of S workgroups per node (team = blockIdx / S, members on consecutive
@@ -587,6 +582,9 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
       kua_v = p.u_accept[(size_t)b * p.n_max + sm.kids[l]];
     }
   }
+  // the children and the flags above are read by every wave (also when this
+  // member's slice is empty and the statistics below run no barrier)
+  tv_lds_barrier();
 
   // chunk statistics of this member's slice (batch_stats synchronises first)
   for (int j0 = 0; j0 < nmine; j0 += kResident) {
@@ -684,14 +682,18 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     sm.ca[0][t] = exp((double)(sm.cm[0][t] - Mp) * p.invT_d) * ip;
     sm.ca[1][t] = internal ? exp((double)(sm.cm[1][t] - Mq) * p.invT_d) * iq : 0.0;
   }
+  if (t >= kSThreads - kMaxNodes && t - (kSThreads - kMaxNodes) < nk) {   // every child's test operands at once
+    const int i = t - (kSThreads - kMaxNodes);
+    sm.kpx[i] = exp((double)sm.kzp[i] * p.invT_d - lse_p);
+    sm.kqx[i] = exp((double)sm.kzq[i] * p.invT_d - lse_q);
+  }
   tv_lds_barrier();
 
   // children in ascending id, one team-wide evaluation of F per rejection
   double Cres = 0.0, Dres = 1.0;
   int accepted = -1, cur = -1;
   for (int i = 0; i < nk; ++i) {
-    const double px = exp((double)sm.kzp[i] * p.invT_d - lse_p);
-    const double qx = exp((double)sm.kzq[i] * p.invT_d - lse_q);
+    const double px = sm.kpx[i], qx = sm.kqx[i];
     if ((double)sm.kua[i] * qx * Dres <= fmax(px - Cres * qx, 0.0)) {
       accepted = sm.kids[i];
       break;
@@ -778,18 +780,19 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
       if (t < nmine) sm.rcur[t] = sm.cs[0][t] * sm.ca[0][t];
     }
     tv_lds_barrier();
-    if (t == 0) {
-      double total = 0.0;
-#pragma unroll
-      for (int s = 0; s < kMaxTeam; ++s)
-        if (s < p.S) total += sm.xcur[s];
+    if (w == 0) {   // member, then chunk, by wave scans
+      const double x = l < p.S ? sm.xcur[l] : 0.0;
+      const double total = tv_readlane_d(tv_wave_incl_scan_d(x, l), 63);
       const double thr = (double)us * total;
       double base = 0.0;
-      const int ms = select_mass(sm.xcur, p.S, thr, &base);
-      sm.owner = ms;
-      if (ms == member) sm.sel = select_mass(sm.rcur, nmine, thr, &base);
-      sm.base = base;
-      sm.thr = thr;
+      const int ms = wave_select_mass(sm.xcur, p.S, thr, &base, l);
+      const int sel = ms == member ? wave_select_mass(sm.rcur, nmine, thr, &base, l) : 0;
+      if (l == 0) {
+        sm.owner = ms;
+        sm.sel = sel;
+        sm.base = base;
+        sm.thr = thr;
+      }
     }
     tv_lds_barrier();
     if (sm.owner == member && nmine > 0) {

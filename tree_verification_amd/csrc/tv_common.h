@@ -119,6 +119,14 @@ __device__ __forceinline__ double tv_row16_sum_d(double v) {
   return v;
 }
 
+// The double held by lane `src` (wave-uniform), to every lane.
+__device__ __forceinline__ double tv_readlane_d(double v, int src) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Inclusive prefix sums of doubles over the wave: shifts by 1, 2, 4 and 8
 // lanes inside each row of 16 (lanes shifted in from outside the row read 0),
 // then the rows' totals (lanes 15, 31, 47) added in row order.
@@ -131,13 +139,7 @@ __device__ __forceinline__ double tv_wave_incl_scan_d(double x, int lane) {
   x += shifted(x, [](uint32_t v) { return tv_dpp<0x112>(v); });   // row_shr:2
   x += shifted(x, [](uint32_t v) { return tv_dpp<0x114>(v); });   // row_shr:4
   x += shifted(x, [](uint32_t v) { return tv_dpp<0x118>(v); });   // row_shr:8
-  auto lane_d = [](double v, int src) {
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-  };
-  const double r0 = lane_d(x, 15), r1 = lane_d(x, 31), r2 = lane_d(x, 47);
+  const double r0 = tv_readlane_d(x, 15), r1 = tv_readlane_d(x, 31), r2 = tv_readlane_d(x, 47);
   const double o1 = r0, o2 = r0 + r1, o3 = o2 + r2;
   const int row = lane >> 4;
   return x + (row == 0 ? 0.0 : row == 1 ? o1 : row == 2 ? o2 : o3);
