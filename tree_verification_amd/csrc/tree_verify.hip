@@ -633,8 +633,8 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
       const bool h0 = l < nmine, h1 = l + 64 < nmine;
       const float m0 = h0 ? sm.cm[w][l] : kNegInf, m1 = h1 ? sm.cm[w][l + 64] : kNegInf;
       M = tv_wave_max(fmaxf(m0, m1));
-      double e = h0 ? sm.cs[w][l] * exp((double)(m0 - M) * p.invT_d) : 0.0;
-      if (h1) e += sm.cs[w][l + 64] * exp((double)(m1 - M) * p.invT_d);
+      double e = h0 ? sm.cs[w][l] * exp(((double)m0 - (double)M) * p.invT_d) : 0.0;
+      if (h1) e += sm.cs[w][l + 64] * exp(((double)m1 - (double)M) * p.invT_d);
       S = tv_wave_sum_d(e);
     }
     if (l == 0) {
@@ -665,7 +665,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     const bool on = l < 32 && s2 < p.S && (row == 0 || internal);
     const float m = on ? sm.xm[row][s2] : kNegInf;
     const float M = tv_row16_max(m);
-    const double e = tv_row16_sum_d(on ? sm.xs[row][s2] * exp((double)(m - M) * p.invT_d) : 0.0);
+    const double e = tv_row16_sum_d(on ? sm.xs[row][s2] * exp(((double)m - (double)M) * p.invT_d) : 0.0);
     if (l == 0 || l == 16) {
       sm.rowM[row] = M;
       sm.rowS[row] = e;
@@ -676,16 +676,14 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
   const double Sp = sm.rowS[0], Sq = sm.rowS[1];
   if (!isfinite(Sp) || (internal && !isfinite(Sq))) return;   // some member saw a non-finite logit
   const double ip = 1.0 / Sp, iq = internal ? 1.0 / Sq : 0.0;
-  const double lse_p = (double)Mp * p.invT_d + log(Sp);
-  const double lse_q = internal ? (double)Mq * p.invT_d + log(Sq) : 0.0;
   if (t < nmine) {
-    sm.ca[0][t] = exp((double)(sm.cm[0][t] - Mp) * p.invT_d) * ip;
-    sm.ca[1][t] = internal ? exp((double)(sm.cm[1][t] - Mq) * p.invT_d) * iq : 0.0;
+    sm.ca[0][t] = exp(((double)sm.cm[0][t] - (double)Mp) * p.invT_d) * ip;
+    sm.ca[1][t] = internal ? exp(((double)sm.cm[1][t] - (double)Mq) * p.invT_d) * iq : 0.0;
   }
   if (t >= kSThreads - kMaxNodes && t - (kSThreads - kMaxNodes) < nk) {   // every child's test operands at once
     const int i = t - (kSThreads - kMaxNodes);
-    sm.kpx[i] = exp((double)sm.kzp[i] * p.invT_d - lse_p);
-    sm.kqx[i] = exp((double)sm.kzq[i] * p.invT_d - lse_q);
+    sm.kpx[i] = exp(((double)sm.kzp[i] - (double)Mp) * p.invT_d) * ip;   // p(x) = exp((z - M) / T) / S
+    sm.kqx[i] = internal ? exp(((double)sm.kzq[i] - (double)Mq) * p.invT_d) * iq : 0.0;
   }
   tv_lds_barrier();
 
@@ -776,7 +774,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     // masses, then inside one chunk; masses are those of p while no rejection
     // has moved the residual, else of the current residual
     if (cur < 0) {
-      if (t < p.S) sm.xcur[t] = sm.xs[0][t] * exp((double)(sm.xm[0][t] - Mp) * p.invT_d) * ip;   // parallel over members
+      if (t < p.S) sm.xcur[t] = sm.xs[0][t] * exp(((double)sm.xm[0][t] - (double)Mp) * p.invT_d) * ip;   // parallel over members
       if (t < nmine) sm.rcur[t] = sm.cs[0][t] * sm.ca[0][t];
     }
     tv_lds_barrier();
