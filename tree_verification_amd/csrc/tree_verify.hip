@@ -61,6 +61,7 @@ constexpr int kMaxTeam = 16;
 constexpr int kResident = 2;                        // chunks a member holds in registers
 constexpr long long kSpinLimit = 1LL << 19;         // bounded waits (~0.5 s), then TV_REQ_TIMEOUT
 constexpr unsigned long long kWritten = 1ull << 63;  // marks a published exchange slot
+constexpr int kPrioSteps = 3;                        // load-order classes: 0, 1, 2, 3+ children
 
 // Buffer resource over one logit row of V floats.  Buffer loads address the row
 // with a 32-bit offset plus an immediate (one VGPR per batch of loads instead of a
@@ -295,6 +296,7 @@ struct StochParams {
   int* node_flags;           // [nodes]  NONFINITE / BAD_TOKEN / TIMEOUT
   int* node_acc;             // [nodes]  accepted child, -1 when none
   int* node_tok;             // [nodes]  draw made when no child is accepted
+  int prio_ticks;            // load delay per missing child below kPrioSteps, 100 MHz ticks (0: none)
   int B, n_max, V, chunks, S, per;   // per = chunks per team member
   float k2hi, k2lo;                  // log2(e) / T as a float32 head and tail
   double invT_d;
@@ -550,6 +552,18 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
   const int tk1 = (w == 0 && 65 + l < n) ? tok[65 + l] : 0;
   const float us = p.u_sample[k];
   float ep[kResident][16], eq[kResident][16];
+  if (p.prio_ticks > 0) {
+    // The whole grid is resident and every member's loads share HBM: a node with
+    // fewer children (a shorter chain of rejections after its loads) issues its
+    // loads later, so the rows of nodes with longer chains arrive first.  Timed
+    // on the 100 MHz real-time counter.
+    const int nkc = __popcll(__ballot(pv0 == u)) + __popcll(__ballot(pv1 == u));
+    if (nkc < kPrioSteps) {
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      const unsigned long long d = (unsigned long long)p.prio_ticks * (unsigned long long)(kPrioSteps - nkc);
+      while (__builtin_amdgcn_s_memrealtime() - t0 < d) __builtin_amdgcn_s_sleep(8);
+    }
+  }
 #pragma unroll
   for (int r = 0; r < kResident; ++r)
     if (r < nmine) load16<kVec>(zp_rs, (my_c0 + r) * kChunk + 16 * t, ep[r]);
@@ -1065,6 +1079,16 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
 
   const long long grid = nodes * tp.S;
   if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  // When the whole grid is resident at once (four workgroups per CU), load order
+  // follows the number of children: each class waits a quarter of the time the
+  // target rows take to stream at about 5.5 TB/s (measured on MI355X: 1.5 us per
+  // class at 64 nodes x 128256 logits took the slowest chain 2.3 us earlier).
+  int cu = 0;
+  p.prio_ticks = 0;
+  if (resident && tv_device_cu_count(&cu) == TV_OK && grid <= 4LL * cu) {
+    const double row_bytes = (double)nodes * (double)desc->vocab * 4.0;
+    p.prio_ticks = (int)fmin(row_bytes / (4.0 * 5.5e12) * 1e8, 1000.0);
+  }
   const bool vec = (desc->vocab & 3) == 0;
   if (resident && vec)
     hipLaunchKernelGGL((stoch_node_kernel<true, true>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
