@@ -18,6 +18,7 @@ Modules:
   attention  masked tree attention over a paged prefix KV cache
   verify     greedy and stochastic tree verification, linear speculative decoding
   kv         accepted-path KV compaction
+  construct  token-tree construction: merge of candidates, top-k expansion
 
 Pins: every function here is checked by tests marked "not gpu" against values
 the pages print, closed forms, library routines on special cases and brute
@@ -31,5 +32,6 @@ BAD_KV = 4          # prefix/positions outside the block table, or a block id ou
 NONFINITE = 8       # a logit row that is read holds NaN or +-inf
 BAD_TOKEN = 16      # a child token outside [0, vocab) (stochastic verification)
 BAD_PATH = 32       # accepted-path description that is not a root path of increasing node ids
+TREE_OVERFLOW = 128 # a constructed tree would exceed n_max nodes
 
-from . import tree, attention, verify, kv  # noqa: E402,F401
+from . import tree, attention, verify, kv, construct  # noqa: E402,F401
