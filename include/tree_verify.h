@@ -60,7 +60,9 @@ enum {
   TV_REQ_NONFINITE = 8,     /* a logit row that is read holds NaN or +-inf */
   TV_REQ_BAD_TOKEN = 16,    /* a child token outside [0, vocab) (stochastic verification) */
   TV_REQ_BAD_PATH = 32,     /* accepted path is not 0 followed by increasing node ids < n_max */
-  TV_REQ_TIMEOUT = 64       /* a bounded inter-workgroup wait expired (results unspecified) */
+  TV_REQ_TIMEOUT = 64,      /* a bounded inter-workgroup wait expired (results unspecified) */
+  TV_REQ_TREE_OVERFLOW = 128, /* a constructed tree would need more than n_max nodes */
+  TV_REQ_BAD_LEN = 256      /* a candidate length, frontier count or frontier node id out of range */
 };
 
 /* ---- element types ------------------------------------------------------ */
@@ -174,6 +176,72 @@ int kv_compact_accepted(const tv_attn_desc* desc, void* k_cache, void* v_cache,
                         const int32_t* block_table, const int32_t* prefix_len,
                         const int32_t* path, const int32_t* path_len, int32_t* src_pos,
                         int32_t* new_len, int32_t* status, hipStream_t stream);
+
+/* ---- token-tree construction ---------------------------------------------
+ * [guide] "Token Tree Construction: Expansion vs. Merge".  Both entry points
+ * produce the parent-array trees the entry points above consume: node 0 is
+ * the root (the last token already emitted) and parent[i] < i. */
+
+typedef struct tv_merge_desc {
+  int32_t batch;        /* B >= 0 */
+  int32_t n_cand;       /* M: candidate sequences per request, 1..64 */
+  int32_t max_len;      /* Lmax: candidate stride, 1..32 */
+  int32_t n_max;        /* node stride of the output tree, 1..1024 */
+} tv_merge_desc;
+
+/* Merge-based construction ([guide] Method B, the merge condition "every node
+ * of every candidate has a node of M with the same token sequence"): request
+ * b's candidates (continuations drafted by several draft models) become one
+ * tree whose node 0 carries root_token[b].  Every prefix of every candidate is
+ * the token sequence of exactly one node; identical prefixes share it.  Nodes
+ * are numbered in depth-first preorder, siblings in the order of the first
+ * candidate that contains them.
+ *   cand_tokens [B][M][Lmax] int32 (entries past cand_len are not read)
+ *   cand_len [B][M] int32 in [0, Lmax]; root_token [B] int32
+ * Outputs: tokens, parent [B][n_max] (entries past n_nodes[b] not written);
+ *   n_nodes [B]; node_of [B][M][Lmax] or NULL: the node of each candidate
+ *   position (-1 past cand_len); status [B]: TV_REQ_BAD_LEN (a cand_len out of
+ *   range) or TV_REQ_TREE_OVERFLOW (more than n_max nodes needed), both with
+ *   n_nodes = 0 and nothing else written.
+ * No workspace.  TV_ERR_UNSUPPORTED outside the limits of the descriptor. */
+int tree_merge_candidates(const tv_merge_desc* desc, const int32_t* cand_tokens,
+                          const int32_t* cand_len, const int32_t* root_token, int32_t* tokens,
+                          int32_t* parent, int32_t* n_nodes, int32_t* node_of, int32_t* status,
+                          hipStream_t stream);
+
+typedef struct tv_expand_desc {
+  int32_t batch;        /* B >= 0 */
+  int32_t f_max;        /* F >= 1: frontier stride (draft rows per request) */
+  int32_t vocab;        /* V >= 1: row length of draft_logits */
+  int32_t n_max;        /* node stride of the tree, 1..1024 */
+  int32_t k;            /* expansion factor of this level, 1..16 and <= V */
+} tv_expand_desc;
+
+/* Bytes of workspace tree_expand_topk needs for `desc` (0 for an invalid one). */
+size_t tree_expand_workspace_size(const tv_expand_desc* desc);
+
+/* One level of expansion-based construction ([guide] Method A, schedule
+ * <k_1, ..., k_m>: call once per depth i with k = k_i and the draft model's
+ * logits at the previous level's nodes).  Frontier node f < n_frontier[b] of
+ * request b, in order, receives as children the k tokens of largest logit in
+ * its draft row (best first; equal logits: lower token index first), appended
+ * after the tree's last node: child r of frontier f gets id
+ * n_nodes[b] + f * k + r.
+ *   draft_logits [B][F][V] float32, 16-byte aligned: row f = logits at frontier[b][f]
+ *   frontier [B][F] int32 node ids below n_nodes[b]; n_frontier [B] in [0, F]
+ * In/out: tokens, parent [B][n_max]; n_nodes [B] (grows by n_frontier * k).
+ * Out: new_frontier [B][F * k] (the appended ids, in order); n_new [B];
+ *   status [B]: TV_REQ_BAD_NNODES (n_nodes outside [1, n_max]),
+ *   TV_REQ_BAD_LEN (n_frontier or a frontier id out of range),
+ *   TV_REQ_TREE_OVERFLOW (more than n_max nodes), TV_REQ_NONFINITE (a read
+ *   row holds NaN or +-inf); with any of them nothing is appended and n_new = 0.
+ * Workspace: per-call partial results, no initialisation; concurrent calls
+ * need distinct workspaces.  TV_ERR_UNSUPPORTED when V > 131072 at k = 16
+ * (ceil(V / 8192) * k must stay <= 256). */
+int tree_expand_topk(const tv_expand_desc* desc, const float* draft_logits, const int32_t* frontier,
+                     const int32_t* n_frontier, int32_t* tokens, int32_t* parent, int32_t* n_nodes,
+                     int32_t* new_frontier, int32_t* n_new, int32_t* status, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable name of a synchronous status code. */
 const char* tv_status_string(int code);

@@ -114,3 +114,48 @@ def test_stochastic_vocabulary_limit(lib):
     v.batch, v.n_max, v.vocab, v.temperature = 1, 4, 64 * 8192 + 1, 1.0
     dummy = ctypes.c_void_p(4096)   # never dereferenced: the call fails before any launch
     assert lib.tree_verify_stochastic(ctypes.byref(v), *([dummy] * 12), 0, None) == -2
+
+
+def test_construction_descriptors_rejected(lib):
+    m = tv.MergeDesc()
+    m.batch, m.n_cand, m.max_len, m.n_max = 1, 65, 4, 16
+    assert lib.tree_merge_candidates(ctypes.byref(m), *([None] * 9)) == -2   # over 64 candidates
+    m.n_cand = 0
+    assert lib.tree_merge_candidates(ctypes.byref(m), *([None] * 9)) == -1
+    m.n_cand, m.max_len = 4, 33
+    assert lib.tree_merge_candidates(ctypes.byref(m), *([None] * 9)) == -2
+    m.max_len, m.n_max = 4, 1025
+    assert lib.tree_merge_candidates(ctypes.byref(m), *([None] * 9)) == -2
+    m.n_max, m.batch = 16, 0
+    assert lib.tree_merge_candidates(ctypes.byref(m), *([None] * 9)) == 0    # nothing to do
+    m.batch = 1
+    assert lib.tree_merge_candidates(ctypes.byref(m), *([None] * 9)) == -1   # missing pointers
+    assert lib.tree_merge_candidates(None, *([None] * 9)) == -1
+
+    e = tv.ExpandDesc()
+    e.batch, e.f_max, e.vocab, e.n_max, e.k = 1, 2, 100, 64, 17
+    assert lib.tree_expand_workspace_size(ctypes.byref(e)) == 0
+    assert lib.tree_expand_topk(ctypes.byref(e), *([None] * 10), 0, None) == -2
+    e.k = 0
+    assert lib.tree_expand_topk(ctypes.byref(e), *([None] * 10), 0, None) == -1
+    e.vocab, e.k = 10, 11                                                      # k > V
+    assert lib.tree_expand_topk(ctypes.byref(e), *([None] * 10), 0, None) == -1
+    e.vocab, e.k = 200000, 16                                                  # 25 chunks x 16 keys
+    assert lib.tree_expand_topk(ctypes.byref(e), *([None] * 10), 0, None) == -2
+    e.vocab, e.k = 128256, 4
+    need = lib.tree_expand_workspace_size(ctypes.byref(e))
+    assert need >= 2 * 16 * 4 * 8
+    assert lib.tree_expand_topk(ctypes.byref(e), *([None] * 10), 0, None) == -1
+    dummy = ctypes.c_void_p(4096)   # never dereferenced: these calls fail before any launch
+    odd = ctypes.c_void_p(4100)
+    assert lib.tree_expand_topk(ctypes.byref(e), odd, *([dummy] * 9), need, None) == -1
+    assert lib.tree_expand_topk(ctypes.byref(e), *([dummy] * 10), need - 1, None) == -3
+
+
+def test_binding_arity_matches_header():
+    """Each ctypes signature takes exactly the parameters the header declares."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    for name, params in re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(([^;{}]*)\)\s*;", src):
+        n = 0 if params.strip() in ("", "void") else params.count(",") + 1
+        assert len(tv._SIGS[name][1]) == n, name

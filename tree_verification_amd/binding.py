@@ -27,6 +27,8 @@ REQ_NONFINITE = 8
 REQ_BAD_TOKEN = 16
 REQ_BAD_PATH = 32
 REQ_TIMEOUT = 64
+REQ_TREE_OVERFLOW = 128
+REQ_BAD_LEN = 256
 
 
 class AttnDesc(ctypes.Structure):
@@ -42,6 +44,16 @@ class VerifyDesc(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("temperature", ctypes.c_float)]
 
 
+class MergeDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_cand", ctypes.c_int32),
+                ("max_len", ctypes.c_int32), ("n_max", ctypes.c_int32)]
+
+
+class ExpandDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("f_max", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("n_max", ctypes.c_int32), ("k", ctypes.c_int32)]
+
+
 class TreeVerifyError(RuntimeError):
     pass
 
@@ -55,6 +67,9 @@ _SIGS = {
     "tree_verify_greedy": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 9 + [_SZ, _P]),
     "tree_verify_stochastic": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 12 + [_SZ, _P]),
     "kv_compact_accepted": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 10),
+    "tree_merge_candidates": (ctypes.c_int, [ctypes.POINTER(MergeDesc)] + [_P] * 9),
+    "tree_expand_workspace_size": (_SZ, [ctypes.POINTER(ExpandDesc)]),
+    "tree_expand_topk": (ctypes.c_int, [ctypes.POINTER(ExpandDesc)] + [_P] * 10 + [_SZ, _P]),
     "tv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -300,3 +315,66 @@ def kv_compact_accepted(k_cache, v_cache, block_table, prefix_len, path, path_le
                                  _ptr(new_len), _ptr(status), _stream(dev))
     _check(rc, "kv_compact_accepted")
     return src_pos, new_len, status
+
+
+def tree_merge_candidates(cand_tokens, cand_len, root_token, n_max, *, tokens=None, parent=None,
+                          n_nodes=None, node_of=None, status=None):
+    """Merge candidate sequences into one token tree.  cand_tokens [B, M, Lmax] int32,
+    cand_len [B, M] int32, root_token [B] int32.  Returns (tokens [B, n_max],
+    parent [B, n_max], n_nodes [B], node_of [B, M, Lmax], status [B])."""
+    lib = load_library()
+    dev = cand_tokens.device
+    B, M, L = cand_tokens.shape
+    _need(cand_tokens, "cand_tokens", torch.int32)
+    _need(cand_len, "cand_len", torch.int32, (B, M), dev)
+    _need(root_token, "root_token", torch.int32, (B,), dev)
+    out = []
+    for t, name, shape in ((tokens, "tokens", (B, n_max)), (parent, "parent", (B, n_max)),
+                           (n_nodes, "n_nodes", (B,)), (node_of, "node_of", (B, M, L)),
+                           (status, "status", (B,))):
+        if t is None:
+            t = torch.empty(shape, dtype=torch.int32, device=dev)
+        _need(t, name, torch.int32, shape, dev)
+        out.append(t)
+    d = MergeDesc()
+    d.batch, d.n_cand, d.max_len, d.n_max = B, M, L, int(n_max)
+    rc = lib.tree_merge_candidates(ctypes.byref(d), _ptr(cand_tokens), _ptr(cand_len), _ptr(root_token),
+                                   *[_ptr(t) for t in out], _stream(dev))
+    _check(rc, "tree_merge_candidates")
+    return tuple(out)
+
+
+def tree_expand_topk(draft_logits, frontier, n_frontier, tokens, parent, n_nodes, k, *, new_frontier=None,
+                     n_new=None, status=None, ws=None):
+    """One level of top-k expansion.  draft_logits [B, F, V] float32; frontier [B, F] int32;
+    n_frontier [B] int32; tokens, parent [B, n_max] int32 and n_nodes [B] int32 are updated
+    in place.  Returns (new_frontier [B, F * k], n_new [B], status [B])."""
+    lib = load_library()
+    dev = draft_logits.device
+    B, F, V = draft_logits.shape
+    n_max = tokens.shape[1]
+    _need(draft_logits, "draft_logits", torch.float32)
+    _need(frontier, "frontier", torch.int32, (B, F), dev)
+    _need(n_frontier, "n_frontier", torch.int32, (B,), dev)
+    _need(tokens, "tokens", torch.int32, (B, n_max), dev)
+    _need(parent, "parent", torch.int32, (B, n_max), dev)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    if new_frontier is None:
+        new_frontier = torch.empty((B, F * int(k)), dtype=torch.int32, device=dev)
+    if n_new is None:
+        n_new = torch.empty(B, dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(new_frontier, "new_frontier", torch.int32, (B, F * int(k)), dev)
+    _need(n_new, "n_new", torch.int32, (B,), dev)
+    _need(status, "status", torch.int32, (B,), dev)
+    d = ExpandDesc()
+    d.batch, d.f_max, d.vocab, d.n_max, d.k = B, F, V, n_max, int(k)
+    need = lib.tree_expand_workspace_size(ctypes.byref(d))
+    if ws is None:
+        ws = workspace(need, dev, "expand", d)
+    rc = lib.tree_expand_topk(ctypes.byref(d), _ptr(draft_logits), _ptr(frontier), _ptr(n_frontier),
+                              _ptr(tokens), _ptr(parent), _ptr(n_nodes), _ptr(new_frontier), _ptr(n_new),
+                              _ptr(status), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(rc, "tree_expand_topk")
+    return new_frontier, n_new, status

@@ -286,3 +286,48 @@ def make_workload(name: str, seed: int | None = None, *, batch=None, prefix=None
                     q=q, k_cache=k_cache, v_cache=v_cache, block_table=table, prefix_len=P,
                     n_nodes=N, parent=parent, tokens=tokens, target_logits=tl, draft_logits=dl,
                     u_accept=u_accept, u_sample=u_sample, seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# token-tree construction inputs
+# ---------------------------------------------------------------------------
+
+def make_candidates(batch: int, n_cand: int, max_len: int, vocab: int, seed: int, share: float = 0.7,
+                    min_len: int = 0):
+    """Candidate continuations for a merge, as several draft models would propose them.
+
+    Returns (cand_tokens [B][M][Lmax] int32, zero past each length; cand_len [B][M]
+    int32; root_token [B] int32).  Lengths are uniform in [min_len, max_len].  With
+    probability `share` a candidate copies a random earlier candidate of its
+    request up to a random cut and continues from there (draft models agreeing on a
+    prefix); otherwise it starts fresh.  Tokens are uniform in [0, vocab).
+    """
+    rng = np.random.default_rng(seed)
+    toks = np.zeros((batch, n_cand, max_len), dtype=np.int32)
+    lens = np.zeros((batch, n_cand), dtype=np.int32)
+    for b in range(batch):
+        for i in range(n_cand):
+            L = int(rng.integers(min_len, max_len + 1))
+            seq = []
+            if i > 0 and rng.random() < share:
+                src = int(rng.integers(i))
+                cut = int(rng.integers(0, lens[b, src] + 1))
+                seq = list(toks[b, src, :cut])
+            while len(seq) < L:
+                seq.append(int(rng.integers(vocab)))
+            seq = seq[:L]
+            toks[b, i, :L] = seq
+            lens[b, i] = L
+    root = rng.integers(0, vocab, size=batch).astype(np.int32)
+    return toks, lens, root
+
+
+def make_expand_rows(batch: int, f_max: int, vocab: int, seed: int, sd: float = 3.0, ties: bool = False):
+    """Draft logit rows of one expansion level, [B][F][V] float32 ~ N(0, sd) (the spread
+    of the configurations' target rows).  ties=True rounds them to multiples of 0.5 so
+    that equal logits occur and the tie order is exercised."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((batch, f_max, vocab)) * sd).astype(np.float32)
+    if ties:
+        x = (np.round(x * 2.0) / 2.0).astype(np.float32)
+    return x
