@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=100, help="back-to-back calls per kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-construction", action="store_true", help="skip the tree-construction timings")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one elementwise copy of this many MiB (a reference "
@@ -348,6 +349,9 @@ def main():
         torch.cuda.synchronize()
         del src_buf, dst_buf
 
+    # tree construction on the GPU, timed before any host-side oracle work
+    constr = None if args.no_construction else bench_construction(args, dev, cyc_per_s)
+
     # ---- CPU oracle baseline ------------------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -383,7 +387,132 @@ def main():
         "cpu_baseline": cpu,
         "input_generation_s": round(gen_s, 2),
     }
+    if constr is not None:
+        if not args.no_cpu_baseline:
+            construction_oracle(constr)
+        line["construction"] = {k: v for k, v in constr.items() if not k.startswith("_")}
     print(json.dumps(line), flush=True)
+
+
+# Token-tree construction, measured beside the step (not part of `value`):
+#   expand: one level of a <3, 2, 1, 1> schedule at a Llama-3 vocabulary, a batch
+#           of 16 requests with 6 frontier nodes each (k = 1), i.e. 96 draft rows
+#           of 128256 logits read per call;
+#   merge:  4 draft models' 8-token guesses per request, a batch of 64 requests.
+EXPAND_SHAPE = dict(batch=16, f_max=6, vocab=128256, k=1, n_max=1024, n0=10)
+MERGE_SHAPE = dict(batch=64, n_cand=4, max_len=8, vocab=128256, n_max=64)
+
+
+def bench_construction(args, dev, cyc_per_s):
+    import torch
+    from tree_verification_amd import binding as tv
+    from tree_verification_amd.workloads import make_candidates, make_expand_rows
+
+    def timed(fns, reps):
+        """GPU microseconds per call of back-to-back calls (rotating over fns), behind a
+        spin kernel that holds the stream while the host enqueues them."""
+        for f in fns[:2]:
+            f()
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for i in range(reps):
+            fns[i % len(fns)]()
+        host_s = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(cyc_per_s * (2.0 * host_s + 2e-3)))
+        a.record()
+        for i in range(reps):
+            fns[i % len(fns)]()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    out = {}
+    e = EXPAND_SHAPE
+    B, F, V, k, n_max, n0 = e["batch"], e["f_max"], e["vocab"], e["k"], e["n_max"], e["n0"]
+    seed = 4242
+    rows_host = make_expand_rows(B, F, V, seed)
+    rng = np.random.default_rng(seed)
+    front_host = rng.integers(0, n0, size=(B, F)).astype(np.int32)
+    rows0 = torch.from_numpy(rows_host).to(dev)
+    ncp = max(2, math.ceil(ROTATE_BYTES / (rows0.numel() * 4)))
+    sets = []
+    for i in range(ncp):
+        sets.append(dict(rows=rows0 if i == 0 else rows0.clone(),
+                         fr=torch.from_numpy(front_host).to(dev),
+                         nf=torch.full((B,), F, dtype=torch.int32, device=dev),
+                         tok=torch.zeros((B, n_max), dtype=torch.int32, device=dev),
+                         par=torch.full((B, n_max), -1, dtype=torch.int32, device=dev),
+                         nn=torch.full((B,), n0, dtype=torch.int32, device=dev),
+                         nfo=torch.empty((B, F * k), dtype=torch.int32, device=dev),
+                         nnew=torch.empty(B, dtype=torch.int32, device=dev),
+                         st=torch.empty(B, dtype=torch.int32, device=dev)))
+
+    def expand_fn(c):
+        return lambda: tv.tree_expand_topk(c["rows"], c["fr"], c["nf"], c["tok"], c["par"], c["nn"], k,
+                                           new_frontier=c["nfo"], n_new=c["nnew"], status=c["st"])
+
+    reps = max(args.kernel_reps, 20)
+    # every call appends F * k nodes per request: reset the counts so that no call overflows
+    # (timed() makes two passes of `reps` calls plus a warm-up call per set)
+    us_exp = timed([expand_fn(c) for c in sets], min(reps, ((n_max - n0) // (F * k) - 2) // 2 * ncp))
+    for c in sets:
+        c["nn"].fill_(n0)
+    expand_fn(sets[0])()
+    torch.cuda.synchronize()
+    assert int(sets[0]["st"].abs().sum()) == 0
+    nbytes = B * F * V * 4
+    out["expand"] = {"workload": f"batch {B}, {F} frontier rows of {V} logits, k = {k}",
+                     "us_per_call": round(us_exp, 3), "bytes": nbytes,
+                     "GBps": round(nbytes / (us_exp * 1e-6) / 1e9, 1),
+                     "roofline": {"bound": "hbm", "achieved": round(nbytes / (us_exp * 1e-6) / 1e9, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(nbytes / (us_exp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "rows_per_s": B * F / (us_exp * 1e-6)}
+
+    m = MERGE_SHAPE
+    toks, lens, root = make_candidates(m["batch"], m["n_cand"], m["max_len"], m["vocab"], seed)
+    ct, cl, rt = (torch.from_numpy(x).to(dev) for x in (toks, lens, root))
+    outs = [torch.empty((m["batch"], m["n_max"]), dtype=torch.int32, device=dev) for _ in range(2)]
+    nn_m = torch.empty(m["batch"], dtype=torch.int32, device=dev)
+    no_m = torch.empty(toks.shape, dtype=torch.int32, device=dev)
+    st_m = torch.empty(m["batch"], dtype=torch.int32, device=dev)
+
+    def merge_fn():
+        tv.tree_merge_candidates(ct, cl, rt, m["n_max"], tokens=outs[0], parent=outs[1], n_nodes=nn_m,
+                                 node_of=no_m, status=st_m)
+
+    us_merge = timed([merge_fn], reps)
+    assert int(st_m.abs().sum()) == 0
+    out["merge"] = {"workload": f"batch {m['batch']}, {m['n_cand']} candidates of up to {m['max_len']} tokens",
+                    "us_per_call": round(us_merge, 3), "trees_per_s": m["batch"] / (us_merge * 1e-6),
+                    "nodes_per_s": float(nn_m.sum().item()) / (us_merge * 1e-6),
+                    "roofline": {"bound": "latency", "note": "one workgroup per request, a few KB each"}}
+
+    out["_inputs"] = dict(n0=n0, k=k, n_max=n_max, B=B, F=F, front=front_host, rows=rows_host, toks=toks,
+                          lens=lens, root=root)
+    return out
+
+
+def construction_oracle(out):
+    """The oracle's construction functions, timed on the host on (a sample of) the
+    same inputs the GPU timings used."""
+    from oracle.construct import expand_level, merge_candidates
+    x = out["_inputs"]
+    n0, k, n_max, B, F = x["n0"], x["k"], x["n_max"], x["B"], x["F"]
+    front_host, rows_host, toks, lens, root = x["front"], x["rows"], x["toks"], x["lens"], x["root"]
+    m = MERGE_SHAPE
+    t0 = time.perf_counter()
+    expand_level([0] * n0, [-1] + [0] * (n0 - 1), n0, list(front_host[0]), list(rows_host[0]), k, n_max)
+    el = time.perf_counter() - t0
+    out["expand"]["cpu_oracle"] = {"us_per_call": el * B * 1e6, "cores": 1,
+                                   "sample": f"request 0 of the batch ({F} rows), {el:.2f} s, scaled by {B}"}
+    t0 = time.perf_counter()
+    for b in range(m["batch"]):
+        merge_candidates(int(root[b]), [list(toks[b, i, :lens[b, i]]) for i in range(m["n_cand"])], m["n_max"])
+    el = time.perf_counter() - t0
+    out["merge"]["cpu_oracle"] = {"us_per_call": el * 1e6, "cores": 1, "sample": f"all {m['batch']} requests, {el:.3f} s"}
 
 
 def cpu_baseline(wl, seconds: float):
