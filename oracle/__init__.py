@@ -19,6 +19,7 @@ Modules:
   verify     greedy and stochastic tree verification, linear speculative decoding
   kv         accepted-path KV compaction
   construct  token-tree construction: merge of candidates, top-k expansion
+  pool       paged speculative-block allocation and release
 
 Pins: every function here is checked by tests marked "not gpu" against values
 the pages print, closed forms, library routines on special cases and brute
@@ -33,5 +34,7 @@ NONFINITE = 8       # a logit row that is read holds NaN or +-inf
 BAD_TOKEN = 16      # a child token outside [0, vocab) (stochastic verification)
 BAD_PATH = 32       # accepted-path description that is not a root path of increasing node ids
 TREE_OVERFLOW = 128 # a constructed tree would exceed n_max nodes
+BAD_LEN = 256       # a candidate length, frontier count or frontier node id out of range
+POOL_EXHAUSTED = 512  # the block pool cannot serve an allocation, or a release would overfill it
 
-from . import tree, attention, verify, kv, construct  # noqa: E402,F401
+from . import tree, attention, verify, kv, construct, pool  # noqa: E402,F401
