@@ -401,6 +401,10 @@ def main():
 #   merge:  4 draft models' 8-token guesses per request, a batch of 64 requests.
 EXPAND_SHAPE = dict(batch=16, f_max=6, vocab=128256, k=1, n_max=1024, n0=10)
 MERGE_SHAPE = dict(batch=64, n_cand=4, max_len=8, vocab=128256, n_max=64)
+#   pool:   speculative blocks of 64-node trees after 4096-token prefixes in 16-token
+#           blocks, a batch of 64: allocation of 4 blocks per request, then release
+#           of the 3 past a 3-token accepted path.
+POOL_SHAPE = dict(batch=64, prefix=4096, nodes=64, accepted=3, block=16)
 
 
 def bench_construction(args, dev, cyc_per_s):
@@ -490,8 +494,41 @@ def bench_construction(args, dev, cyc_per_s):
                     "nodes_per_s": float(nn_m.sum().item()) / (us_merge * 1e-6),
                     "roofline": {"bound": "latency", "note": "one workgroup per request, a few KB each"}}
 
+    q = POOL_SHAPE
+    Bp, bs = q["batch"], q["block"]
+    mapped = q["prefix"] // bs
+    max_blocks = (q["prefix"] + q["nodes"]) // bs + 1
+    num_blocks = Bp * max_blocks
+    perm = np.random.default_rng(seed).permutation(num_blocks).astype(np.int32)
+    table = np.full((Bp, max_blocks), -1, dtype=np.int32)
+    table[:, :mapped] = perm[:Bp * mapped].reshape(Bp, mapped)
+    free = np.concatenate([perm[Bp * mapped:], np.full(Bp * mapped, -1, dtype=np.int32)])
+    d_table = torch.from_numpy(table).to(dev)
+    d_nblk = torch.full((Bp,), mapped, dtype=torch.int32, device=dev)
+    d_free = torch.from_numpy(free).to(dev)
+    d_count = torch.tensor([num_blocks - Bp * mapped], dtype=torch.int32, device=dev)
+    d_pre = torch.full((Bp,), q["prefix"], dtype=torch.int32, device=dev)
+    d_n = torch.full((Bp,), q["nodes"], dtype=torch.int32, device=dev)
+    d_new = torch.full((Bp,), q["prefix"] + q["accepted"], dtype=torch.int32, device=dev)
+    d_spec = torch.empty(Bp, dtype=torch.int32, device=dev)
+    d_st = torch.empty(Bp, dtype=torch.int32, device=dev)
+    d_st2 = torch.empty(Bp, dtype=torch.int32, device=dev)
+
+    def pool_fn():   # allocation then release: the pool returns to the same state
+        tv.kv_alloc_tree_blocks(d_table, d_nblk, d_pre, d_n, d_free, d_count, block_size=bs,
+                                spec_from=d_spec, status=d_st)
+        tv.kv_release_blocks(d_table, d_nblk, d_new, d_free, d_count, block_size=bs, status=d_st2)
+
+    us_pool = timed([pool_fn], reps)
+    assert int(d_st.abs().sum()) == 0 and int(d_st2.abs().sum()) == 0
+    out["pool"] = {"workload": f"batch {Bp}, {q['nodes']}-node trees after {q['prefix']}-token prefixes, "
+                               f"{bs}-token blocks: allocate {(q['prefix'] + q['nodes']) // bs - mapped}, "
+                               f"release {(q['prefix'] + q['nodes']) // bs - (q['prefix'] + q['accepted'] + bs - 1) // bs} per request",
+                   "us_per_alloc_and_release": round(us_pool, 3),
+                   "roofline": {"bound": "latency", "note": "one workgroup, one thread per request"}}
+
     out["_inputs"] = dict(n0=n0, k=k, n_max=n_max, B=B, F=F, front=front_host, rows=rows_host, toks=toks,
-                          lens=lens, root=root)
+                          lens=lens, root=root, pool=(table, free, mapped, num_blocks))
     return out
 
 
@@ -513,6 +550,18 @@ def construction_oracle(out):
         merge_candidates(int(root[b]), [list(toks[b, i, :lens[b, i]]) for i in range(m["n_cand"])], m["n_max"])
     el = time.perf_counter() - t0
     out["merge"]["cpu_oracle"] = {"us_per_call": el * 1e6, "cores": 1, "sample": f"all {m['batch']} requests, {el:.3f} s"}
+    from oracle.pool import alloc_tree_blocks, release_blocks
+    q = POOL_SHAPE
+    table, free, mapped, num_blocks = x["pool"]
+    Bp = q["batch"]
+    t0 = time.perf_counter()
+    t, nb, f, c, _, _ = alloc_tree_blocks(table, np.full(Bp, mapped), np.full(Bp, q["prefix"]),
+                                          np.full(Bp, q["nodes"]), free, num_blocks - Bp * mapped,
+                                          block_size=q["block"], num_blocks=num_blocks)
+    release_blocks(t, nb, np.full(Bp, q["prefix"] + q["accepted"]), f, c, block_size=q["block"],
+                   num_blocks=num_blocks)
+    el = time.perf_counter() - t0
+    out["pool"]["cpu_oracle"] = {"us_per_call": el * 1e6, "cores": 1, "sample": f"all {Bp} requests, {el:.4f} s"}
 
 
 def cpu_baseline(wl, seconds: float):

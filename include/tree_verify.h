@@ -62,7 +62,8 @@ enum {
   TV_REQ_BAD_PATH = 32,     /* accepted path is not 0 followed by increasing node ids < n_max */
   TV_REQ_TIMEOUT = 64,      /* a bounded inter-workgroup wait expired (results unspecified) */
   TV_REQ_TREE_OVERFLOW = 128, /* a constructed tree would need more than n_max nodes */
-  TV_REQ_BAD_LEN = 256      /* a candidate length, frontier count or frontier node id out of range */
+  TV_REQ_BAD_LEN = 256,     /* a candidate length, frontier count or frontier node id out of range */
+  TV_REQ_POOL_EXHAUSTED = 512 /* the block pool cannot serve an allocation, or a release would overfill it */
 };
 
 /* ---- element types ------------------------------------------------------ */
@@ -176,6 +177,44 @@ int kv_compact_accepted(const tv_attn_desc* desc, void* k_cache, void* v_cache,
                         const int32_t* block_table, const int32_t* prefix_len,
                         const int32_t* path, const int32_t* path_len, int32_t* src_pos,
                         int32_t* new_len, int32_t* status, hipStream_t stream);
+
+/* ---- speculative KV blocks -------------------------------------------------
+ * [guide] "PagedKV Allocation with Zero-Copy Pruning": the tree's KV blocks are
+ * taken from the paged pool and marked speculative; after verification the
+ * blocks of the unselected branches return to the free pool in one metadata
+ * update.  The pool is a stack of free block ids, free_ids[0 .. *free_count),
+ * top at *free_count - 1.  Each call serves the batch in request order, pops or
+ * pushes one contiguous segment of the stack and updates *free_count once.  A
+ * request the pool cannot serve gets TV_REQ_POOL_EXHAUSTED and so does every
+ * later request that needs blocks moved (requests moving none always succeed);
+ * failed requests are left unchanged.  *free_count outside [0, num_blocks]
+ * fails every request with TV_REQ_BAD_KV.  Only desc->batch, block_size,
+ * max_blocks_per_seq and num_blocks are used.  One workgroup; no workspace. */
+
+/* Allocation: request b's table maps n_blocks[b] blocks; it is extended to the
+ * ceil((prefix_len[b] + n_nodes[b]) / block_size) blocks that hold its prefix
+ * and its tree (the tree's K/V goes to positions prefix_len .. + n_nodes), the
+ * new entries popped from the top of the stack one by one.  spec_from[b] = the
+ * first speculative table index (the old n_blocks[b]; -1 when the request
+ * failed).  TV_REQ_BAD_KV: negative prefix_len / n_nodes, n_blocks outside
+ * [0, max_blocks], or more than max_blocks blocks needed.
+ *   block_table [B][max_blocks] and n_blocks [B] in/out; free_ids [num_blocks] in;
+ *   free_count [1] in/out; spec_from, status [B] out. */
+int kv_alloc_tree_blocks(const tv_attn_desc* desc, int32_t* block_table, int32_t* n_blocks,
+                         const int32_t* prefix_len, const int32_t* n_nodes, const int32_t* free_ids,
+                         int32_t* free_count, int32_t* spec_from, int32_t* status, hipStream_t stream);
+
+/* Release: request b keeps the ceil(new_len[b] / block_size) blocks that hold
+ * its first new_len positions (new_len from kv_compact_accepted: prefix plus
+ * accepted path) and pushes every later mapped block onto the stack, in table
+ * order, setting its table entry to -1 and n_blocks[b] to the kept count.
+ * TV_REQ_BAD_KV: new_len < 0, n_blocks outside [0, max_blocks], new_len beyond
+ * the mapped blocks, or a block id to release outside [0, num_blocks).
+ *   block_table [B][max_blocks], n_blocks [B] in/out; new_len [B] in;
+ *   free_ids [num_blocks], free_count [1] in/out; status [B] out. */
+int kv_release_blocks(const tv_attn_desc* desc, int32_t* block_table, int32_t* n_blocks,
+                      const int32_t* new_len, int32_t* free_ids, int32_t* free_count, int32_t* status,
+                      hipStream_t stream);
 
 /* ---- token-tree construction ---------------------------------------------
  * [guide] "Token Tree Construction: Expansion vs. Merge".  Both entry points

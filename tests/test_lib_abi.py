@@ -159,3 +159,16 @@ def test_binding_arity_matches_header():
     for name, params in re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(([^;{}]*)\)\s*;", src):
         n = 0 if params.strip() in ("", "void") else params.count(",") + 1
         assert len(tv._SIGS[name][1]) == n, name
+
+
+def test_pool_descriptors_rejected(lib):
+    d = good_attn_desc()
+    assert lib.kv_alloc_tree_blocks(ctypes.byref(d), *([None] * 9)) == -1     # missing pointers
+    assert lib.kv_release_blocks(ctypes.byref(d), *([None] * 7)) == -1
+    d.block_size = 0
+    assert lib.kv_alloc_tree_blocks(ctypes.byref(d), *([None] * 9)) == -1
+    d.block_size, d.num_blocks = 16, 0
+    assert lib.kv_release_blocks(ctypes.byref(d), *([None] * 7)) == -1
+    d.num_blocks, d.batch = 4, 0
+    assert lib.kv_alloc_tree_blocks(ctypes.byref(d), *([None] * 9)) == 0      # nothing to do
+    assert lib.kv_release_blocks(None, *([None] * 7)) == -1

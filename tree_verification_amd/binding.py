@@ -29,6 +29,7 @@ REQ_BAD_PATH = 32
 REQ_TIMEOUT = 64
 REQ_TREE_OVERFLOW = 128
 REQ_BAD_LEN = 256
+REQ_POOL_EXHAUSTED = 512
 
 
 class AttnDesc(ctypes.Structure):
@@ -67,6 +68,8 @@ _SIGS = {
     "tree_verify_greedy": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 9 + [_SZ, _P]),
     "tree_verify_stochastic": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 12 + [_SZ, _P]),
     "kv_compact_accepted": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 10),
+    "kv_alloc_tree_blocks": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 9),
+    "kv_release_blocks": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 7),
     "tree_merge_candidates": (ctypes.c_int, [ctypes.POINTER(MergeDesc)] + [_P] * 9),
     "tree_expand_workspace_size": (_SZ, [ctypes.POINTER(ExpandDesc)]),
     "tree_expand_topk": (ctypes.c_int, [ctypes.POINTER(ExpandDesc)] + [_P] * 10 + [_SZ, _P]),
@@ -378,3 +381,62 @@ def tree_expand_topk(draft_logits, frontier, n_frontier, tokens, parent, n_nodes
                               _ptr(status), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(rc, "tree_expand_topk")
     return new_frontier, n_new, status
+
+
+def _pool_desc(block_table, block_size, num_blocks) -> AttnDesc:
+    d = AttnDesc()
+    d.batch, d.max_blocks_per_seq = block_table.shape
+    d.block_size, d.num_blocks = int(block_size), int(num_blocks)
+    d.n_max, d.n_q_heads, d.n_kv_heads, d.head_dim, d.dtype, d.sm_scale = 1, 1, 1, 1, TV_F32, 0.0
+    return d
+
+
+def kv_alloc_tree_blocks(block_table, n_blocks, prefix_len, n_nodes, free_ids, free_count, *, block_size,
+                         spec_from=None, status=None):
+    """Pop the speculative blocks of every request's tree from the free stack.
+    block_table [B, max_blocks], n_blocks [B] and free_count [1] (int32) are updated
+    in place.  Returns (spec_from [B], status [B])."""
+    lib = load_library()
+    dev = block_table.device
+    B, _ = block_table.shape
+    nb = free_ids.shape[0]
+    _need(block_table, "block_table", torch.int32)
+    _need(n_blocks, "n_blocks", torch.int32, (B,), dev)
+    _need(prefix_len, "prefix_len", torch.int32, (B,), dev)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    _need(free_ids, "free_ids", torch.int32, (nb,), dev)
+    _need(free_count, "free_count", torch.int32, (1,), dev)
+    if spec_from is None:
+        spec_from = torch.empty(B, dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(spec_from, "spec_from", torch.int32, (B,), dev)
+    _need(status, "status", torch.int32, (B,), dev)
+    d = _pool_desc(block_table, block_size, nb)
+    rc = lib.kv_alloc_tree_blocks(ctypes.byref(d), _ptr(block_table), _ptr(n_blocks), _ptr(prefix_len),
+                                  _ptr(n_nodes), _ptr(free_ids), _ptr(free_count), _ptr(spec_from),
+                                  _ptr(status), _stream(dev))
+    _check(rc, "kv_alloc_tree_blocks")
+    return spec_from, status
+
+
+def kv_release_blocks(block_table, n_blocks, new_len, free_ids, free_count, *, block_size, status=None):
+    """Push every block past the kept length back onto the free stack.  block_table,
+    n_blocks, free_ids and free_count are updated in place.  Returns status [B]."""
+    lib = load_library()
+    dev = block_table.device
+    B, _ = block_table.shape
+    nb = free_ids.shape[0]
+    _need(block_table, "block_table", torch.int32)
+    _need(n_blocks, "n_blocks", torch.int32, (B,), dev)
+    _need(new_len, "new_len", torch.int32, (B,), dev)
+    _need(free_ids, "free_ids", torch.int32, (nb,), dev)
+    _need(free_count, "free_count", torch.int32, (1,), dev)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(status, "status", torch.int32, (B,), dev)
+    d = _pool_desc(block_table, block_size, nb)
+    rc = lib.kv_release_blocks(ctypes.byref(d), _ptr(block_table), _ptr(n_blocks), _ptr(new_len),
+                               _ptr(free_ids), _ptr(free_count), _ptr(status), _stream(dev))
+    _check(rc, "kv_release_blocks")
+    return status
