@@ -212,8 +212,29 @@ __global__ __launch_bounds__(kGreedyThreads) void greedy_argmax_kernel(GreedyPar
 __global__ __launch_bounds__(kMaxNodes) void greedy_chase_kernel(GreedyParams p) {
   __shared__ int s_arg[kMaxNodes];
   __shared__ int s_child[kMaxNodes];
+  __shared__ int s_tok[kMaxNodes];
   __shared__ int s_badpar, s_nonfinite;
   const int t = threadIdx.x, b = blockIdx.x;
+  const int32_t* par = p.parent + (size_t)b * p.n_max;
+  const int32_t* tok = p.tokens + (size_t)b * p.n_max;
+  // every load of the request's rows is issued at once, before n_nodes is
+  // known (rows are n_max long; entries past n are not used)
+  const size_t kv = (size_t)b * p.n_max + t;
+  int pv = -1, tk = 0, flg = 0;
+  unsigned long long key = 0ull;
+  if (t < p.n_max) {
+    pv = par[t];
+    tk = tok[t];
+    flg = p.flags[kv];
+    const unsigned long long* kp = p.keys + kv * p.chunks;
+    for (int c0 = 0; c0 < p.chunks; c0 += 16) {
+      unsigned long long kc[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) kc[c] = c0 + c < p.chunks ? kp[c0 + c] : 0ull;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) key = kc[c] > key ? kc[c] : key;
+    }
+  }
   const int n = p.n_nodes[b];
   if (n < 1 || n > p.n_max) {
     if (t == 0) {
@@ -222,34 +243,25 @@ __global__ __launch_bounds__(kMaxNodes) void greedy_chase_kernel(GreedyParams p)
     }
     return;
   }
-  const int32_t* par = p.parent + (size_t)b * p.n_max;
-  const int32_t* tok = p.tokens + (size_t)b * p.n_max;
   if (t == 0) {
     s_badpar = 0;
     s_nonfinite = 0;
   }
   __syncthreads();
   if (t < n) {
-    const size_t kv = (size_t)b * p.n_max + t;
-    unsigned long long key = 0ull;
-    for (int c = 0; c < p.chunks; ++c) {
-      const unsigned long long kc = p.keys[kv * p.chunks + c];
-      key = kc > key ? kc : key;
-    }
     s_arg[t] = (int)(0xFFFFFFFFu - (uint32_t)key);
     s_child[t] = 0x7fffffff;
-    if (p.flags[kv]) {
+    s_tok[t] = tk;
+    if (flg) {
       s_nonfinite = 1;
       p.flags[kv] = 0;
     }
-    const int pv = par[t];
     if (!((t == 0) ? (pv == -1) : (pv >= 0 && pv < t))) s_badpar = 1;
   }
   __syncthreads();
   const int fl = s_badpar ? TV_REQ_BAD_PARENT : (s_nonfinite ? TV_REQ_NONFINITE : 0);
   if (fl == 0 && t >= 1 && t < n) {
-    const int pv = par[t];
-    if (tok[t] == s_arg[pv]) atomicMin(&s_child[pv], t);
+    if (tk == s_arg[pv]) atomicMin(&s_child[pv], t);
   }
   __syncthreads();
   if (t == 0) {
@@ -264,7 +276,7 @@ __global__ __launch_bounds__(kMaxNodes) void greedy_chase_kernel(GreedyParams p)
     path[0] = 0;
     while (s_child[cur] != 0x7fffffff && j + 1 < n) {
       const int ch = s_child[cur];
-      out[j] = tok[ch];
+      out[j] = s_tok[ch];
       path[++j] = ch;
       cur = ch;
     }
@@ -864,6 +876,17 @@ __global__ __launch_bounds__(kMaxNodes) void stoch_chase_kernel(StochParams p) {
   __shared__ int s_acc[kMaxNodes], s_fin[kMaxNodes], s_tok[kMaxNodes];
   __shared__ int s_flags, s_badpar;
   const int t = threadIdx.x, b = blockIdx.x;
+  // every load of the request's rows is issued at once, before n_nodes is
+  // known (rows are n_max long; entries past n are not used)
+  const size_t kv = (size_t)b * p.n_max + t;
+  int fl = 0, acc = -1, fin = 0, tk = 0, pv = -1;
+  if (t < p.n_max) {
+    fl = p.node_flags[kv];
+    acc = p.node_acc[kv];
+    fin = p.node_tok[kv];
+    tk = p.tokens[kv];
+    pv = p.parent[kv];
+  }
   const int n = p.n_nodes[b];
   if (n < 1 || n > p.n_max) {
     if (t == 0) {
@@ -881,16 +904,13 @@ __global__ __launch_bounds__(kMaxNodes) void stoch_chase_kernel(StochParams p) {
   for (int i = t; i < n * kMaxTeam * 4; i += kMaxNodes) p.sxch[(size_t)b * p.n_max * kMaxTeam * 4 + i] = 0ull;
   for (int i = t; i < n * kMaxTeam; i += kMaxNodes) p.xch[(size_t)b * p.n_max * kMaxTeam + i] = 0ull;
   if (t < n) {
-    const size_t kv = (size_t)b * p.n_max + t;
-    const int fl = p.node_flags[kv];
     if (fl) {
       atomicOr(&s_flags, fl);
       p.node_flags[kv] = 0;
     }
-    s_acc[t] = p.node_acc[kv];
-    s_fin[t] = p.node_tok[kv];
-    s_tok[t] = p.tokens[kv];
-    const int pv = p.parent[kv];
+    s_acc[t] = acc;
+    s_fin[t] = fin;
+    s_tok[t] = tk;
     if (!((t == 0) ? (pv == -1) : (pv >= 0 && pv < t))) s_badpar = 1;
   }
   __syncthreads();
