@@ -327,10 +327,10 @@ __device__ __forceinline__ float exp_t(float d, float k2hi, float k2lo) {
 
 // Weight of one vocabulary entry under max(p - c q, 0).  ep / eq are the
 // float32 exponentials exp((z - m) / T) relative to the entry's chunk maxima of
-// the target / draft row; a / b = exp((m - M) / T) / sum turn them into p and q
-// (float64).
-__device__ __forceinline__ double residual_weight(float ep, float eq, double a, double b, double c) {
-  return fmax((double)ep * a - c * ((double)eq * b), 0.0);
+// the target / draft row; a = exp((m - M) / T) / sum turns ep into p, and
+// cb = c times the same factor of the draft row turns eq into c q (float64).
+__device__ __forceinline__ double residual_weight(float ep, float eq, double a, double cb) {
+  return fmax(fma((double)ep, a, -(cb * (double)eq)), 0.0);
 }
 
 template <bool kRes>
@@ -348,8 +348,7 @@ struct NodeSmem {
   double xcur[kMaxTeam];  // ... of the current residual
   float xm[2][kMaxTeam];  // member row maxima (target, draft)
   double xs[2][kMaxTeam]; // member exponential sums relative to those maxima
-  float rowM[2];          // team row maxima and exponential sums
-  double rowS[2];
+  double rowS[2];         // team exponential sums relative to the team maxima
   double scan[kSThreads / 64];
   int wcross[kSThreads / 64], wlast[kSThreads / 64];   // per wave: first crossing lane, last lane with mass
   int kids[kMaxNodes], ktok[kMaxNodes];
@@ -360,6 +359,16 @@ struct NodeSmem {
   // draft exponentials of the resident slice, [chunk][group of 4][thread]
   tv_f32x4 qe[kRes ? kResident * 4 * kSThreads : 1];
 };
+
+// Sum of 16 doubles, pairwise.
+__device__ __forceinline__ double sum16_d(const double* x) {
+  double a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = x[2 * i] + x[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] += a[i + 4];
+  return (a[0] + a[2]) + (a[1] + a[3]);
+}
 
 // Sum of 16 floats, pairwise.
 __device__ __forceinline__ float sum16(const float* x) {
@@ -684,32 +693,47 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     if (member == 0 && t == 0) atomicOr(&p.node_flags[k], TV_REQ_BAD_TOKEN);
     return;
   }
-  // team row statistics: lanes 16 r + s of wave 0 combine member s of row r with
-  // a fixed shuffle tree, so every member obtains the same values
+  // team row maxima: every thread takes them from the members' maxima (a max
+  // is exact, so all threads and all members agree); then every exponential
+  // that needs only the maxima runs at once, beside the team sums
+  float Mp = kNegInf, Mq = kNegInf;
+  for (int s2 = 0; s2 < p.S; ++s2) {
+    Mp = fmaxf(Mp, sm.xm[0][s2]);
+    Mq = fmaxf(Mq, sm.xm[1][s2]);
+  }
+  if (!internal) Mq = kNegInf;
+  double ea0 = 0.0, ea1 = 0.0, ekp = 0.0, ekq = 0.0;
+  if (t < nmine) {
+    ea0 = exp(((double)sm.cm[0][t] - (double)Mp) * p.invT_d);
+    ea1 = internal ? exp(((double)sm.cm[1][t] - (double)Mq) * p.invT_d) : 0.0;
+  }
+  const int ci = t - (kSThreads - kMaxNodes);   // every child's test operands at once
+  const bool child_t = ci >= 0 && ci < nk;
+  if (child_t) {
+    ekp = exp(((double)sm.kzp[ci] - (double)Mp) * p.invT_d);   // p(x) = exp((z - M) / T) / S
+    ekq = internal ? exp(((double)sm.kzq[ci] - (double)Mq) * p.invT_d) : 0.0;
+  }
+  // team row sums: lanes 16 r + s of wave 0 combine member s of row r with a
+  // fixed shuffle tree, so every member obtains the same values
   if (w == 0) {
     const int row = (l >> 4) & 1, s2 = l & 15;
     const bool on = l < 32 && s2 < p.S && (row == 0 || internal);
     const float m = on ? sm.xm[row][s2] : kNegInf;
-    const float M = tv_row16_max(m);
+    const float M = row ? Mq : Mp;
     const double e = tv_row16_sum_d(on ? sm.xs[row][s2] * exp(((double)m - (double)M) * p.invT_d) : 0.0);
-    if (l == 0 || l == 16) {
-      sm.rowM[row] = M;
-      sm.rowS[row] = e;
-    }
+    if (l == 0 || l == 16) sm.rowS[row] = e;
   }
   tv_lds_barrier();
-  const float Mp = sm.rowM[0], Mq = sm.rowM[1];
   const double Sp = sm.rowS[0], Sq = sm.rowS[1];
   if (!isfinite(Sp) || (internal && !isfinite(Sq))) return;   // some member saw a non-finite logit
   const double ip = 1.0 / Sp, iq = internal ? 1.0 / Sq : 0.0;
   if (t < nmine) {
-    sm.ca[0][t] = exp(((double)sm.cm[0][t] - (double)Mp) * p.invT_d) * ip;
-    sm.ca[1][t] = internal ? exp(((double)sm.cm[1][t] - (double)Mq) * p.invT_d) * iq : 0.0;
+    sm.ca[0][t] = ea0 * ip;
+    sm.ca[1][t] = internal ? ea1 * iq : 0.0;
   }
-  if (t >= kSThreads - kMaxNodes && t - (kSThreads - kMaxNodes) < nk) {   // every child's test operands at once
-    const int i = t - (kSThreads - kMaxNodes);
-    sm.kpx[i] = exp(((double)sm.kzp[i] - (double)Mp) * p.invT_d) * ip;   // p(x) = exp((z - M) / T) / S
-    sm.kqx[i] = internal ? exp(((double)sm.kzq[i] - (double)Mq) * p.invT_d) * iq : 0.0;
+  if (child_t) {
+    sm.kpx[ci] = ekp * ip;
+    sm.kqx[ci] = internal ? ekq * iq : 0.0;
   }
   tv_lds_barrier();
 
@@ -747,15 +771,16 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
 #pragma unroll
       for (int r = 0; r < kResident; ++r) {
         if (j0 + r < nmine) {
-          const double a = sm.ca[0][j0 + r], bq = sm.ca[1][j0 + r];
-          double s = 0.0;
+          const double a = sm.ca[0][j0 + r], cb = cn * sm.ca[1][j0 + r];
+          double wv[16];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const tv_f32x4 q4 = kRes ? sm.qe[(r * 4 + g) * kSThreads + t]
                                      : tv_f32x4{eq[r][4 * g], eq[r][4 * g + 1], eq[r][4 * g + 2], eq[r][4 * g + 3]};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s += residual_weight(ep[r][4 * g + e], q4[e], a, bq, cn);
+            for (int e = 0; e < 4; ++e) wv[4 * g + e] = residual_weight(ep[r][4 * g + e], q4[e], a, cb);
           }
+          double s = sum16_d(wv);   // pairwise: a short dependent chain
           s = tv_wave_sum_d(s);
           if (l == 0) sm.part[w][j0 + r] = s;
         }
@@ -839,7 +864,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
             qe[4 * g + 3] = q4[3];
           }
 #pragma unroll
-          for (int e = 0; e < 16; ++e) wts[e] = residual_weight(pe[e], qe[e], a, bq, Cres);
+          for (int e = 0; e < 16; ++e) wts[e] = residual_weight(pe[e], qe[e], a, Cres * bq);
         } else {
 #pragma unroll
           for (int e = 0; e < 16; ++e) wts[e] = (double)pe[e] * a;
@@ -853,7 +878,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
 #pragma unroll
           for (int e = 0; e < 16; ++e)
             wts[e] = e0 + e < p.V ? residual_weight(exp_t(xp[e] - mp, p.k2hi, p.k2lo), exp_t(xq[e] - mq, p.k2hi, p.k2lo),
-                                                    a, bq, Cres)
+                                                    a, Cres * bq)
                                   : 0.0;
         } else {
 #pragma unroll
