@@ -9,6 +9,7 @@ package imports nothing from the product.
 Sources (web pages; section names as printed on them):
   [guide]   "SpecInfer Guide: Tree-Based Speculative LLM Serving" (aifetchly blog)
   [chapter] "Inference Optimization Techniques: Speed and Efficiency" (aicomputerinstitute)
+  [cohere]  Cohere's blog post on hardware-aware dynamic speculative decoding
 
 Readings taken where the pages are silent or garbled are listed in the
 design notes; each function names the one it relies on.
@@ -20,6 +21,7 @@ Modules:
   kv         accepted-path KV compaction
   construct  token-tree construction: merge of candidates, top-k expansion
   pool       paged speculative-block allocation and release
+  budget     expected acceptance length of a tree, goodput and the tree-size table
 
 Pins: every function here is checked by tests marked "not gpu" against values
 the pages print, closed forms, library routines on special cases and brute
@@ -36,5 +38,6 @@ BAD_PATH = 32       # accepted-path description that is not a root path of incre
 TREE_OVERFLOW = 128 # a constructed tree would exceed n_max nodes
 BAD_LEN = 256       # a candidate length, frontier count or frontier node id out of range
 POOL_EXHAUSTED = 512  # the block pool cannot serve an allocation, or a release would overfill it
+BAD_PROB = 1024     # an acceptance probability that is NaN or outside [0, 1] (tree-budget calibration)
 
-from . import tree, attention, verify, kv, construct, pool  # noqa: E402,F401
+from . import tree, attention, verify, kv, construct, pool, budget  # noqa: E402,F401
