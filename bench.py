@@ -52,6 +52,10 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one elementwise copy of this many MiB (a reference "
                          "kernel of known traffic for hardware byte counters)")
+    ap.add_argument("--budget-table", action="store_true",
+                    help="instead of the step: measure step latency per (batch size, tree shape) at this "
+                         "workload's layer shape and print the goodput tree-size table")
+    ap.add_argument("--budget-out", default=None, help="also write the table as markdown to this path")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
                          "WRITE_SIZE, both with --calibrate-copy-mib) into profiles/traffic_*.json")
@@ -156,6 +160,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     tv.load_library()
     dev = torch.device("cuda:0")
+    if args.budget_table:
+        budget_table(args, dev)
+        return
     seed = seed_for(args.config) if args.seed is None else args.seed
     t0 = time.time()
     wl = make_workload(args.config, seed=seed)
@@ -391,6 +398,7 @@ def main():
         if not args.no_cpu_baseline:
             construction_oracle(constr)
         line["construction"] = {k: v for k, v in constr.items() if not k.startswith("_")}
+        line["budget"] = constr.pop("_budget")
     print(json.dumps(line), flush=True)
 
 
@@ -405,6 +413,8 @@ MERGE_SHAPE = dict(batch=64, n_cand=4, max_len=8, vocab=128256, n_max=64)
 #           blocks, a batch of 64: allocation of 4 blocks per request, then release
 #           of the 3 past a 3-token accepted path.
 POOL_SHAPE = dict(batch=64, prefix=4096, nodes=64, accepted=3, block=16)
+#   budget: expected acceptance length of 256 trees of up to 128 nodes.
+BUDGET_SHAPE = dict(batch=256, n_max=128)
 
 
 def bench_construction(args, dev, cyc_per_s):
@@ -529,7 +539,181 @@ def bench_construction(args, dev, cyc_per_s):
 
     out["_inputs"] = dict(n0=n0, k=k, n_max=n_max, B=B, F=F, front=front_host, rows=rows_host, toks=toks,
                           lens=lens, root=root, pool=(table, free, mapped, num_blocks))
+
+    # expected acceptance length of a batch of trees (tree-budget calibration)
+    from tree_verification_amd.workloads import make_budget_trees
+    bt = BUDGET_SHAPE
+    bpar, bn, bprob = make_budget_trees(bt["batch"], bt["n_max"], seed)
+    d_bpar, d_bn, d_bprob = (torch.from_numpy(x).to(dev) for x in (bpar, bn, bprob))
+    d_reach = torch.empty(bpar.shape, dtype=torch.float64, device=dev)
+    d_al = torch.empty(bt["batch"], dtype=torch.float64, device=dev)
+    d_bst = torch.empty(bt["batch"], dtype=torch.int32, device=dev)
+
+    def budget_fn():
+        tv.tree_expected_accept_length(d_bpar, d_bn, d_bprob, reach=d_reach, expected_len=d_al, status=d_bst)
+
+    us_budget = timed([budget_fn], reps)
+    assert int(d_bst.abs().sum()) == 0
+    out["_budget"] = {"workload": f"batch {bt['batch']} trees of up to {bt['n_max']} nodes "
+                                  f"({int(bn.sum())} nodes), per-node acceptance probabilities",
+                      "us_per_call": round(us_budget, 3), "trees_per_s": bt["batch"] / (us_budget * 1e-6),
+                      "roofline": {"bound": "latency", "note": "one wavefront per tree, ~1.5 KB read each"}}
+    if not args.no_cpu_baseline:
+        from oracle.budget import expected_length
+        t0 = time.perf_counter()
+        expected_length(bpar.tolist(), bn.tolist(), bprob.tolist(), bt["n_max"])
+        el = time.perf_counter() - t0
+        out["_budget"]["cpu_oracle"] = {"us_per_call": el * 1e6, "cores": 1,
+                                        "sample": f"all {bt['batch']} trees, {el:.3f} s"}
     return out
+
+
+# Tree-budget table ([cohere] goodput = AL / ITL, an offline lookup of the best
+# draft budget per batch size; [guide] "Dynamic Tree Budget Calibration").
+# Candidate trees are expansion schedules (node counts 2, 4, 7, 15, 28, 61);
+# every drafted node is accepted with probability BUDGET_ALPHA when tested
+# ([chapter]'s representative alpha).  Latencies are measured for this path's
+# step at the 8B layer shape (one tree-attention layer, stochastic verification,
+# compaction).  A second column prices a whole round with a stated model of the
+# parts this path does not build: the target's 32 attention layers as 32 x the
+# measured layer, plus its dense weights read once per round or its GEMMs,
+# whichever is slower (8.03e9 bf16 parameters, 8 TB/s, 2.5 PFLOP/s).
+BUDGET_SCHEDULES = ([1], [1, 1, 1], [2, 1, 1], [2, 2, 1, 1], [3, 2, 1, 1, 1], [4, 2, 2, 1, 1])
+BUDGET_BATCHES = (1, 4, 16, 64)
+BUDGET_ALPHA = 0.7
+BUDGET_LAYER = dict(prefix=2048, n_q_heads=32, n_kv_heads=8, head_dim=128, vocab=128256, block=16, layers=32,
+                    params=8.03e9)
+
+
+def budget_table(args, dev):
+    import torch
+    from tree_verification_amd import binding as tv
+    from tree_verification_amd.workloads import schedule_tree
+
+    L = BUDGET_LAYER
+    P, Hq, Hkv, D, V, bs = L["prefix"], L["n_q_heads"], L["n_kv_heads"], L["head_dim"], L["vocab"], L["block"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2024)
+    shapes = [schedule_tree(sch) for sch in BUDGET_SCHEDULES]
+    n_max = max(len(x) for x in shapes)
+
+    # acceptance lengths of the candidate shapes, on the GPU
+    par_all = np.full((len(shapes), n_max), -1, dtype=np.int32)
+    nn_all = np.array([len(x) for x in shapes], dtype=np.int32)
+    prob = np.zeros((len(shapes), n_max))
+    for i, x in enumerate(shapes):
+        par_all[i, :len(x)] = x
+        prob[i, 1:len(x)] = BUDGET_ALPHA
+    _, al_d, st_d = tv.tree_expected_accept_length(torch.from_numpy(par_all).to(dev),
+                                                   torch.from_numpy(nn_all).to(dev),
+                                                   torch.from_numpy(prob).to(dev))
+    torch.cuda.synchronize()
+    assert int(st_d.abs().sum()) == 0
+    al = al_d.cpu().tolist()
+
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    a0.record()
+    torch.cuda._sleep(20_000_000)
+    a1.record()
+    torch.cuda.synchronize()
+    cyc_per_s = 20_000_000 / (a0.elapsed_time(a1) * 1e-3)
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        host_s = time.perf_counter() - h0
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(cyc_per_s * (2.0 * host_s + 2e-3)))   # holds the stream while the calls queue
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    rows = []
+    for B in BUDGET_BATCHES:
+        row = []
+        for si, par in enumerate(shapes):
+            N = len(par)
+            nblk = (P + N + bs - 1) // bs
+            q = torch.randn((B, N, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+            kc = torch.randn((B * nblk, Hkv, bs, D), generator=gen, device=dev).to(torch.bfloat16)
+            vc = torch.randn((B * nblk, Hkv, D, bs), generator=gen, device=dev).to(torch.bfloat16)
+            table = torch.arange(B * nblk, dtype=torch.int32, device=dev).view(B, nblk)
+            pre = torch.full((B,), P, dtype=torch.int32, device=dev)
+            nn = torch.full((B,), N, dtype=torch.int32, device=dev)
+            pp = torch.from_numpy(np.tile(par, (B, 1))).to(dev)
+            tl = torch.randn((B, N, V), generator=gen, device=dev) * 3.0
+            dl = tl + torch.randn((B, N, V), generator=gen, device=dev)
+            tok = torch.zeros((B, N), dtype=torch.int32, device=dev)
+            if N > 1:   # children drawn from the parent's draft row (Gumbel-max)
+                pidx = torch.from_numpy(par[1:].astype(np.int64)).to(dev)
+                u = torch.rand((B, N - 1, V), generator=gen, device=dev).clamp_min_(1e-30)
+                tok[:, 1:] = (dl[:, pidx, :] - torch.log(-torch.log(u))).argmax(-1).to(torch.int32)
+                del u
+            ua = torch.rand((B, N), generator=gen, device=dev)
+            us = torch.rand((B, N), generator=gen, device=dev)
+            out = torch.empty_like(q)
+            bufs = [torch.empty((B, N), dtype=torch.int32, device=dev) for _ in range(3)]
+            ints = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(6)]
+
+            def attn():
+                tv.tree_attn_forward(q, kc, vc, table, pre, nn, pp, out=out, status=ints[0])
+
+            def verify():
+                tv.tree_verify_stochastic(tl, dl, tok, pp, nn, ua, us, path=bufs[0], path_len=ints[1],
+                                          out_tokens=bufs[1], status=ints[2])
+
+            def compact():
+                tv.kv_compact_accepted(kc, vc, table, pre, bufs[0], ints[1], src_pos=bufs[2], new_len=ints[3],
+                                       status=ints[4])
+
+            attn(), verify(), compact()
+            torch.cuda.synchronize()
+            assert int(ints[0].abs().sum()) == 0 and int(ints[2].abs().sum()) == 0
+            t_attn, t_ver, t_cmp = timed(attn), timed(verify), timed(compact)
+            t_step = t_attn + t_ver + t_cmp
+            dense = max(L["params"] * 2 / (HBM_PEAK_GBS * 1e9), 2 * L["params"] * B * N / 2.5e15) * 1e6
+            t_round = dense + L["layers"] * t_attn + t_ver + t_cmp
+            row.append(dict(shape=si, nodes=N, al=al[si], us_attn=t_attn, us_verify=t_ver, us_compact=t_cmp,
+                            us_step=t_step, us_round_model=t_round))
+            print(json.dumps({"batch": B, "schedule": BUDGET_SCHEDULES[si], **row[-1]}), flush=True)
+            del q, kc, vc, tl, dl, out
+            torch.cuda.empty_cache()
+        rows.append(row)
+
+    best_step = tv.tree_budget_select(al, [[r["us_step"] for r in row] for row in rows])
+    best_round = tv.tree_budget_select(al, [[r["us_round_model"] for r in row] for row in rows])
+    result = {"table": "tree budget", "alpha": BUDGET_ALPHA, "batches": list(BUDGET_BATCHES),
+              "schedules": [list(s) for s in BUDGET_SCHEDULES], "nodes": [len(x) for x in shapes], "al": al,
+              "best_shape_step": best_step, "best_shape_round_model": best_round,
+              "rows": rows}
+    print(json.dumps(result), flush=True)
+    if args.budget_out:
+        with open(args.budget_out, "w") as f:
+            f.write(budget_markdown(result))
+
+
+def budget_markdown(r) -> str:
+    lines = ["| batch | schedule | nodes | AL | attention us | verify us | compact us | step us | "
+             "tokens/s (step) | round us (model) | tokens/s (round model) |",
+             "|---:|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for bi, B in enumerate(r["batches"]):
+        for x in r["rows"][bi]:
+            s = x["shape"]
+            mark1 = " **best**" if r["best_shape_step"][bi] == s else ""
+            mark2 = " **best**" if r["best_shape_round_model"][bi] == s else ""
+            lines.append(f"| {B} | {r['schedules'][s]} | {x['nodes']} | {x['al']:.3f} | {x['us_attn']:.1f} | "
+                         f"{x['us_verify']:.1f} | {x['us_compact']:.1f} | {x['us_step']:.1f} | "
+                         f"{B * x['al'] / (x['us_step'] * 1e-6):,.0f}{mark1} | {x['us_round_model']:.0f} | "
+                         f"{B * x['al'] / (x['us_round_model'] * 1e-6):,.0f}{mark2} |")
+    return "\n".join(lines) + "\n"
 
 
 def construction_oracle(out):

@@ -6,6 +6,7 @@
  * Sources (web pages, section names as printed):
  *   [guide]   "SpecInfer Guide: Tree-Based Speculative LLM Serving"
  *   [chapter] "Inference Optimization Techniques: Speed and Efficiency"
+ *   [cohere]  Cohere's blog post "hardware-aware dynamic speculative decoding"
  *
  * General rules for every entry point:
  *   - Array arguments are DEVICE pointers owned by the caller; the library
@@ -63,7 +64,8 @@ enum {
   TV_REQ_TIMEOUT = 64,      /* a bounded inter-workgroup wait expired (results unspecified) */
   TV_REQ_TREE_OVERFLOW = 128, /* a constructed tree would need more than n_max nodes */
   TV_REQ_BAD_LEN = 256,     /* a candidate length, frontier count or frontier node id out of range */
-  TV_REQ_POOL_EXHAUSTED = 512 /* the block pool cannot serve an allocation, or a release would overfill it */
+  TV_REQ_POOL_EXHAUSTED = 512, /* the block pool cannot serve an allocation, or a release would overfill it */
+  TV_REQ_BAD_PROB = 1024    /* an acceptance probability that is NaN or outside [0, 1] (tree budget) */
 };
 
 /* ---- element types ------------------------------------------------------ */
@@ -281,6 +283,57 @@ int tree_expand_topk(const tv_expand_desc* desc, const float* draft_logits, cons
                      const int32_t* n_frontier, int32_t* tokens, int32_t* parent, int32_t* n_nodes,
                      int32_t* new_frontier, int32_t* n_new, int32_t* status, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
+
+/* ---- tree-budget calibration ----------------------------------------------
+ * [chapter] "Worked Example: How Many Tokens Land Per Expensive Pass?" models
+ * acceptance events as independent draws and counts the tokens one round
+ * emits as T = K + 1 (K accepted drafts plus one correction or bonus token);
+ * for a chain of gamma drafts with acceptance alpha, E[T] = (1 - alpha^(gamma+1))
+ * / (1 - alpha).  [cohere] "Dynamic speculative decoding" picks the number of
+ * drafts per batch size by goodput = AL / ITL (acceptance length over
+ * inter-token latency) from offline measurements kept as a lookup table, and
+ * [guide] "Dynamic Tree Budget Calibration" asks tree size to follow the batch
+ * size.  The two calls below are that calculation for token trees. */
+
+typedef struct tv_budget_desc {
+  int32_t batch;        /* B >= 0 trees */
+  int32_t n_max;        /* node stride, 1..128 */
+} tv_budget_desc;
+
+/* Expected acceptance length of each tree under the per-node independence
+ * model: drafted node v, when it is tested, is accepted with probability
+ * accept_prob[b][v], independently of every other test; the children of a node
+ * are tested in ascending id and the first accepted one continues the walk
+ * (the order of the verification walk, [guide] "Stochastic Verification
+ * Algorithm").  For a chain with every probability alpha this is [chapter]'s
+ * model exactly.
+ *   parent [B][n_max] int32 (parent[0] = -1, 0 <= parent[i] < i); n_nodes [B]
+ *   accept_prob [B][n_max] float64; entry 0 (the root, never tested) and
+ *     entries past n_nodes[b] are not read.
+ * Outputs (float64):
+ *   reach [B][n_max]: P(node v lies on the accepted path); reach[b][0] = 1 and
+ *     every entry from n_nodes[b] to n_max - 1 is written as 0;
+ *   expected_len [B]: AL = E[T] = 1 + sum over v >= 1 of reach[b][v];
+ *   status [B]: TV_REQ_BAD_NNODES, else TV_REQ_BAD_PARENT, else
+ *     TV_REQ_BAD_PROB (a probability that is NaN or outside [0, 1]); a failed
+ *     request gets expected_len = 0 and a reach row of zeros.
+ * One wavefront per tree; no workspace.  Sums and products are float64 in an
+ * order other than the walk's, so results agree with a sequential evaluation
+ * to rounding (relative 1e-12 and better). */
+int tree_expected_accept_length(const tv_budget_desc* desc, const int32_t* parent, const int32_t* n_nodes,
+                                const double* accept_prob, double* reach, double* expected_len,
+                                int32_t* status, hipStream_t stream);
+
+/* Tree-size lookup table from measurements ([cohere] goodput): for each batch
+ * size i, best[i] = the shape s with the largest al[s] / itl[i][s] among the
+ * latencies that are positive and finite (equal goodputs keep the lower s;
+ * -1 when there is none).  A host computation on HOST arrays: al [n_shapes]
+ * (acceptance length of each candidate shape, e.g. from
+ * tree_expected_accept_length), itl [n_batch_sizes][n_shapes] (measured step
+ * latency, any unit), best [n_batch_sizes] out.  Nothing is launched.
+ * TV_ERR_INVALID_ARG for a null array or a negative count. */
+int tree_budget_select(int32_t n_batch_sizes, int32_t n_shapes, const double* al, const double* itl,
+                       int32_t* best);
 
 /* Human-readable name of a synchronous status code. */
 const char* tv_status_string(int code);

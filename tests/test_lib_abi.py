@@ -172,3 +172,37 @@ def test_pool_descriptors_rejected(lib):
     d.num_blocks, d.batch = 4, 0
     assert lib.kv_alloc_tree_blocks(ctypes.byref(d), *([None] * 9)) == 0      # nothing to do
     assert lib.kv_release_blocks(None, *([None] * 7)) == -1
+
+
+def test_budget_rejects_bad_descriptors(lib):
+    d = tv.BudgetDesc()
+    d.batch, d.n_max = 2, 129
+    assert lib.tree_expected_accept_length(ctypes.byref(d), *([None] * 7)) == -2
+    d.n_max = 0
+    assert lib.tree_expected_accept_length(ctypes.byref(d), *([None] * 7)) == -2
+    d.batch, d.n_max = -1, 8
+    assert lib.tree_expected_accept_length(ctypes.byref(d), *([None] * 7)) == -1
+    d.batch = 2
+    assert lib.tree_expected_accept_length(ctypes.byref(d), *([None] * 7)) == -1   # null arrays
+    d.batch = 0
+    assert lib.tree_expected_accept_length(ctypes.byref(d), *([None] * 7)) == 0    # nothing to do
+    assert lib.tree_expected_accept_length(None, *([None] * 7)) == -1
+    assert lib.tree_budget_select(-1, 3, None, None, None) == -1
+    assert lib.tree_budget_select(2, 3, None, None, None) == -1
+
+
+def test_budget_select_is_the_oracle_lookup(lib):
+    """tree_budget_select is host code: compared with the oracle's goodput table."""
+    import numpy as np
+    from oracle.budget import select_budget
+    rng = np.random.default_rng(77)
+    for _ in range(200):
+        S, I = int(rng.integers(1, 9)), int(rng.integers(1, 6))
+        al = 1.0 + rng.random(S) * 4
+        itl = rng.random((I, S)) * 10
+        # special entries: non-positive, infinite and NaN latencies, exact ties
+        for _ in range(int(rng.integers(0, 4))):
+            itl[rng.integers(I), rng.integers(S)] = rng.choice([0.0, -1.0, np.inf, np.nan])
+        if S > 1 and rng.random() < 0.3:
+            al[1], itl[:, 1] = 2 * al[0], 2 * itl[:, 0]
+        assert tv.tree_budget_select(al, itl) == select_budget(al, itl)

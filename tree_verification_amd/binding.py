@@ -30,6 +30,7 @@ REQ_TIMEOUT = 64
 REQ_TREE_OVERFLOW = 128
 REQ_BAD_LEN = 256
 REQ_POOL_EXHAUSTED = 512
+REQ_BAD_PROB = 1024
 
 
 class AttnDesc(ctypes.Structure):
@@ -55,6 +56,10 @@ class ExpandDesc(ctypes.Structure):
                 ("n_max", ctypes.c_int32), ("k", ctypes.c_int32)]
 
 
+class BudgetDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_max", ctypes.c_int32)]
+
+
 class TreeVerifyError(RuntimeError):
     pass
 
@@ -73,6 +78,8 @@ _SIGS = {
     "tree_merge_candidates": (ctypes.c_int, [ctypes.POINTER(MergeDesc)] + [_P] * 9),
     "tree_expand_workspace_size": (_SZ, [ctypes.POINTER(ExpandDesc)]),
     "tree_expand_topk": (ctypes.c_int, [ctypes.POINTER(ExpandDesc)] + [_P] * 10 + [_SZ, _P]),
+    "tree_expected_accept_length": (ctypes.c_int, [ctypes.POINTER(BudgetDesc)] + [_P] * 7),
+    "tree_budget_select": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "tv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -440,3 +447,48 @@ def kv_release_blocks(block_table, n_blocks, new_len, free_ids, free_count, *, b
                                _ptr(free_ids), _ptr(free_count), _ptr(status), _stream(dev))
     _check(rc, "kv_release_blocks")
     return status
+
+
+def tree_expected_accept_length(parent, n_nodes, accept_prob, *, reach=None, expected_len=None, status=None):
+    """Expected acceptance length of each tree under the per-node independence
+    model.  parent [B, n_max] int32, n_nodes [B] int32, accept_prob [B, n_max]
+    float64.  Returns (reach [B, n_max], expected_len [B], status [B])."""
+    lib = load_library()
+    dev = parent.device
+    B, n_max = parent.shape
+    _need(parent, "parent", torch.int32)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    _need(accept_prob, "accept_prob", torch.float64, (B, n_max), dev)
+    if reach is None:
+        reach = torch.empty(B, n_max, dtype=torch.float64, device=dev)
+    if expected_len is None:
+        expected_len = torch.empty(B, dtype=torch.float64, device=dev)
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(reach, "reach", torch.float64, (B, n_max), dev)
+    _need(expected_len, "expected_len", torch.float64, (B,), dev)
+    _need(status, "status", torch.int32, (B,), dev)
+    d = BudgetDesc()
+    d.batch, d.n_max = B, n_max
+    rc = lib.tree_expected_accept_length(ctypes.byref(d), _ptr(parent), _ptr(n_nodes), _ptr(accept_prob),
+                                         _ptr(reach), _ptr(expected_len), _ptr(status), _stream(dev))
+    _check(rc, "tree_expected_accept_length")
+    return reach, expected_len, status
+
+
+def tree_budget_select(al, itl):
+    """Best shape per batch size by goodput al[s] / itl[i][s] (host arrays:
+    al of length S, itl of I rows of S latencies).  Returns a list of I shape
+    indices (-1 where no latency is positive and finite)."""
+    lib = load_library()
+    al = [float(x) for x in al]
+    rows = [[float(x) for x in r] for r in itl]
+    S, I = len(al), len(rows)
+    if any(len(r) != S for r in rows):
+        raise ValueError("every latency row needs one entry per shape")
+    al_c = (ctypes.c_double * max(S, 1))(*al)
+    itl_c = (ctypes.c_double * max(S * I, 1))(*[x for r in rows for x in r])
+    best = (ctypes.c_int32 * max(I, 1))()
+    rc = lib.tree_budget_select(I, S, ctypes.cast(al_c, _P), ctypes.cast(itl_c, _P), ctypes.cast(best, _P))
+    _check(rc, "tree_budget_select")
+    return [int(best[i]) for i in range(I)]

@@ -331,3 +331,49 @@ def make_expand_rows(batch: int, f_max: int, vocab: int, seed: int, sd: float = 
     if ties:
         x = (np.round(x * 2.0) / 2.0).astype(np.float32)
     return x
+
+
+def schedule_tree(schedule) -> np.ndarray:
+    """Parent array of the tree an expansion schedule <k_1, ..., k_m> builds below
+    the root: every node of level i - 1 gets k_i children, appended level by level
+    (frontier order, then rank).  Shape only; no tokens."""
+    parent = [-1]
+    frontier = [0]
+    for k in schedule:
+        nxt = []
+        for f in frontier:
+            for _ in range(int(k)):
+                nxt.append(len(parent))
+                parent.append(f)
+        frontier = nxt
+    return np.asarray(parent, dtype=np.int32)
+
+
+def make_budget_trees(batch: int, n_max: int, seed: int):
+    """Trees and per-node acceptance probabilities for the expected-length
+    calculation: [B][n_max] int32 parents (padding -1), [B] int32 node counts,
+    [B][n_max] float64 probabilities (root and padding entries 0).  Node counts
+    are uniform in 1..n_max with every fifth request full; shapes cycle through
+    capped, recursive, chain and star trees; probabilities are U(0, 1) with
+    about one in eight set to exactly 0 or 1."""
+    rng = np.random.default_rng(seed)
+    parent = np.full((batch, n_max), -1, dtype=np.int32)
+    n_nodes = np.empty(batch, dtype=np.int32)
+    prob = np.zeros((batch, n_max), dtype=np.float64)
+    kinds = ("capped", "recursive", "chain", "star")
+    for b in range(batch):
+        n = n_max if b % 5 == 0 else int(rng.integers(1, n_max + 1))
+        kind = kinds[b % 4]
+        if kind == "capped":
+            par = random_tree(rng, n, "capped", width=int(rng.integers(2, 9)), depth=None)
+        else:
+            par = random_tree(rng, n, kind)
+        parent[b, :n] = par
+        n_nodes[b] = n
+        a = rng.random(n)
+        pick = rng.random(n)
+        a[pick < 1 / 16] = 0.0
+        a[(pick >= 1 / 16) & (pick < 1 / 8)] = 1.0
+        a[0] = 0.0
+        prob[b, :n] = a
+    return parent, n_nodes, prob
