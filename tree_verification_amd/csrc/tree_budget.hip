@@ -13,9 +13,10 @@
 // (a round emits the accepted nodes plus one more token).
 //
 // One wavefront per tree (n <= 128: node j lives in lane j % 64, slot j / 64).
-// The edge weights come from a scan of the node's earlier siblings in LDS;
-// the root-path products come from pointer jumping with lane shuffles (seven
-// rounds reach any depth below 128), all in float64.
+// Each node's children are collected as bit masks (LDS atomics), which give
+// every node its previous sibling; the products over earlier siblings and then
+// over the root path are both taken by pointer jumping with lane shuffles
+// (seven rounds cover any chain below 128), all in float64.
 
 #include "tv_common.h"
 
@@ -23,7 +24,6 @@
 
 namespace {
 
-constexpr int kBudgetWaves = 4;
 constexpr int kBudgetMaxNodes = 128;
 
 struct BudgetParams {
@@ -43,16 +43,42 @@ __device__ __forceinline__ double shfl_d(double v, int src) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-__global__ __launch_bounds__(64 * kBudgetWaves) void expected_len_kernel(BudgetParams p) {
-  __shared__ int par_s[kBudgetWaves][kBudgetMaxNodes];
-  __shared__ double a_s[kBudgetWaves][kBudgetMaxNodes];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int b = blockIdx.x * kBudgetWaves + wave;
-  if (b >= p.B) return;   // whole waves only: no workgroup barrier below
+// Products along links by pointer jumping: on return val[j] holds the product
+// of val over j, link(j), link(link(j)), ... (node j: lane j % 64, slot j / 64;
+// link -1 ends a chain).  Seven rounds cover chains shorter than 128.
+__device__ __forceinline__ void jump_products(double (&val)[2], int (&link)[2]) {
+  for (int r = 0; r < 7; ++r) {
+    double nval[2];
+    int nlink[2];
+    for (int s = 0; s < 2; ++s) {
+      const int j = link[s];
+      const int src = j < 0 ? 0 : (j & 63);
+      const double v0 = shfl_d(val[0], src), v1 = shfl_d(val[1], src);
+      const int j0 = __shfl(link[0], src), j1 = __shfl(link[1], src);
+      if (j >= 0) {
+        nval[s] = val[s] * (j >= 64 ? v1 : v0);
+        nlink[s] = j >= 64 ? j1 : j0;
+      } else {
+        nval[s] = val[s];
+        nlink[s] = -1;
+      }
+    }
+    for (int s = 0; s < 2; ++s) {
+      val[s] = nval[s];
+      link[s] = nlink[s];
+    }
+  }
+}
+
+// One wavefront (one workgroup) per tree.
+__global__ __launch_bounds__(64) void expected_len_kernel(BudgetParams p) {
+  __shared__ int par[kBudgetMaxNodes];
+  __shared__ double a[kBudgetMaxNodes];
+  __shared__ unsigned long long kids[kBudgetMaxNodes][2];   // children of each node, as bit masks
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x;
   const int n = p.n_nodes[b];
   const size_t row = (size_t)b * p.n_max;
-  int* par = par_s[wave];
-  double* a = a_s[wave];
 
   int flags = 0;
   if (n < 1 || n > p.n_max) {
@@ -66,6 +92,8 @@ __global__ __launch_bounds__(64 * kBudgetWaves) void expected_len_kernel(BudgetP
         const double au = u > 0 ? p.prob[row + u] : 0.0;
         par[u] = pu;
         a[u] = au;
+        kids[u][0] = 0ull;
+        kids[u][1] = 0ull;
         bad_par |= (u == 0) ? (pu != -1) : (pu < 0 || pu >= u);
         bad_prob |= u > 0 && !(au >= 0.0 && au <= 1.0);   // NaN fails both compares
       }
@@ -81,51 +109,46 @@ __global__ __launch_bounds__(64 * kBudgetWaves) void expected_len_kernel(BudgetP
     }
     return;
   }
-  // The LDS writes above came from this wave only; make them visible to its
-  // other lanes before the sibling scan reads them.
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-
-  // edge weight of each node: a[v] times the rejection of every earlier sibling
-  double val[2];
-  int jmp[2];
+  __syncthreads();
   for (int s = 0; s < 2; ++s) {
     const int v = lane + 64 * s;
-    if (v == 0 || v >= n) {
-      val[s] = 1.0;
-      jmp[s] = -1;
-      continue;
-    }
-    const int pv = par[v];
-    double rej = 1.0;
-    for (int w = pv + 1; w < v; ++w)
-      if (par[w] == pv) rej *= 1.0 - a[w];
-    val[s] = rej * a[v];
-    jmp[s] = pv;
+    if (v >= 1 && v < n) atomicOr(&kids[par[v]][s], 1ull << lane);
   }
-  // root-path products: after round r, val[v] is the product of the edge
-  // weights of v and its ancestors within distance < 2^r, jmp[v] the next one up
-  for (int r = 0; r < 7; ++r) {
-    double nval[2];
-    int njmp[2];
-    for (int s = 0; s < 2; ++s) {
-      const int j = jmp[s];
-      const int src = j < 0 ? 0 : (j & 63);
-      const double v0 = shfl_d(val[0], src), v1 = shfl_d(val[1], src);
-      const int j0 = __shfl(jmp[0], src), j1 = __shfl(jmp[1], src);
-      if (j >= 0) {
-        nval[s] = val[s] * (j >= 64 ? v1 : v0);
-        njmp[s] = j >= 64 ? j1 : j0;
-      } else {
-        nval[s] = val[s];
-        njmp[s] = -1;
+  __syncthreads();
+
+  // previous sibling of each node, and the rejection of every earlier sibling
+  // as a product along previous-sibling links
+  const unsigned long long below = (1ull << lane) - 1ull;
+  double val[2];
+  int link[2];
+  for (int s = 0; s < 2; ++s) {
+    const int v = lane + 64 * s;
+    val[s] = 1.0;
+    link[s] = -1;
+    if (v >= 1 && v < n) {
+      const int pv = par[v];
+      const unsigned long long m0 = s == 0 ? (kids[pv][0] & below) : kids[pv][0];
+      const unsigned long long m1 = s == 0 ? 0ull : (kids[pv][1] & below);
+      const int prev = m1 ? 64 + 63 - __clzll(m1) : (m0 ? 63 - __clzll(m0) : -1);
+      if (prev >= 0) {
+        val[s] = 1.0 - a[prev];
+        link[s] = prev;
       }
     }
-    for (int s = 0; s < 2; ++s) {
-      val[s] = nval[s];
-      jmp[s] = njmp[s];
+  }
+  jump_products(val, link);
+  // edge weight a[v] * rejection of the earlier siblings, then root-path products
+  for (int s = 0; s < 2; ++s) {
+    const int v = lane + 64 * s;
+    if (v >= 1 && v < n) {
+      val[s] *= a[v];
+      link[s] = par[v];
+    } else {
+      val[s] = 1.0;
+      link[s] = -1;
     }
   }
+  jump_products(val, link);
   double part = 0.0;
   for (int s = 0; s < 2; ++s) {
     const int v = lane + 64 * s;
@@ -157,8 +180,7 @@ extern "C" int tree_expected_accept_length(const tv_budget_desc* desc, const int
   p.status = status;
   p.B = desc->batch;
   p.n_max = desc->n_max;
-  const int grid = (desc->batch + kBudgetWaves - 1) / kBudgetWaves;
-  hipLaunchKernelGGL(expected_len_kernel, dim3(grid), dim3(64 * kBudgetWaves), 0, stream, p);
+  hipLaunchKernelGGL(expected_len_kernel, dim3(desc->batch), dim3(64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
