@@ -429,7 +429,10 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p)
   constexpr int TPR = D / kMergeVec, RPB = merge_rows<D>();
   const int t = threadIdx.x;
   const int groups = (p.rows_per_tile + RPB - 1) / RPB;
-  const int tile = blockIdx.x / groups, rg = blockIdx.x % groups;
+  // same XCD-aware numbering as the attention grid: a tile's merge workgroups
+  // run on the XCD whose L2 took its partials
+  const int lid = tv_xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = lid / groups, rg = lid % groups;
   const int bg = tile / p.row_tiles, rt = tile % p.row_tiles;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int r = rg * RPB + t / TPR, d = kMergeVec * (t % TPR);   // row within the tile, first d
