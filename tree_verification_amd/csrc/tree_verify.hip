@@ -309,6 +309,7 @@ struct StochParams {
   int* node_acc;             // [nodes]  accepted child, -1 when none
   int* node_tok;             // [nodes]  draw made when no child is accepted
   int prio_ticks;            // load delay per missing child below kPrioSteps, 100 MHz ticks (0: none)
+  int xcd_teams;             // 1: the whole grid is resident; a team's members share an XCD
   int B, n_max, V, chunks, S, per;   // per = chunks per team member
   float k2hi, k2lo;                  // log2(e) / T as a float32 head and tail
   double invT_d;
@@ -552,7 +553,12 @@ template <bool kRes, bool kVec>
 __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes ? 4 : 2))) void stoch_node_kernel(StochParams p) {
   __shared__ NodeSmem<kRes> sm;
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
-  const int k = blockIdx.x / p.S, member = blockIdx.x % p.S;
+  // With the whole grid resident, team members are numbered so that they run
+  // on one XCD (workgroup i goes to XCD i mod 8), where their exchange hand-offs
+  // are shorter.  Otherwise teams stay consecutive workgroup ids, which in-order
+  // dispatch makes resident one after another.
+  const int lid = p.xcd_teams ? tv_xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int k = lid / p.S, member = lid % p.S;
   const int my_c0 = min(member * p.per, p.chunks);
   const int nmine = min(my_c0 + p.per, p.chunks) - my_c0;   // at most kResident when kRes
   const int b = k / p.n_max, u = k % p.n_max;
@@ -1130,7 +1136,9 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
   // class at 64 nodes x 128256 logits took the slowest chain 2.3 us earlier).
   int cu = 0;
   p.prio_ticks = 0;
+  p.xcd_teams = 0;
   if (resident && tv_device_cu_count(&cu) == TV_OK && grid <= 4LL * cu) {
+    p.xcd_teams = 1;
     const double row_bytes = (double)nodes * (double)desc->vocab * 4.0;
     p.prio_ticks = (int)fmin(row_bytes / (4.0 * 5.5e12) * 1e8, 1000.0);
   }
