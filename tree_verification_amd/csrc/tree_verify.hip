@@ -903,7 +903,9 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
 
 // One workgroup per request: status, the accepted path and its final token,
 // and the exchange slots cleared for the next call.
-__global__ __launch_bounds__(kMaxNodes) void stoch_chase_kernel(StochParams p) {
+constexpr int kChaseThreads = 256;
+
+__global__ __launch_bounds__(kChaseThreads) void stoch_chase_kernel(StochParams p) {
   __shared__ int s_acc[kMaxNodes], s_fin[kMaxNodes], s_tok[kMaxNodes];
   __shared__ int s_flags, s_badpar;
   const int t = threadIdx.x, b = blockIdx.x;
@@ -931,9 +933,16 @@ __global__ __launch_bounds__(kMaxNodes) void stoch_chase_kernel(StochParams p) {
     s_badpar = 0;
   }
   __syncthreads();
-  // every exchange slot the node kernel may have written for this request
-  for (int i = t; i < n * kMaxTeam * 4; i += kMaxNodes) p.sxch[(size_t)b * p.n_max * kMaxTeam * 4 + i] = 0ull;
-  for (int i = t; i < n * kMaxTeam; i += kMaxNodes) p.xch[(size_t)b * p.n_max * kMaxTeam + i] = 0ull;
+  // every exchange slot the node kernel may have written for this request, in
+  // 16-byte stores (a request's slots start 16-byte aligned: the slot arrays
+  // are 256-byte aligned and a request owns a multiple of 16 slots)
+  {
+    tv_u32x4* sx = (tv_u32x4*)(p.sxch + (size_t)b * p.n_max * kMaxTeam * 4);
+    tv_u32x4* xc = (tv_u32x4*)(p.xch + (size_t)b * p.n_max * kMaxTeam);
+    const tv_u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = t; i < n * kMaxTeam * 2; i += kChaseThreads) sx[i] = z;
+    for (int i = t; i < n * kMaxTeam / 2; i += kChaseThreads) xc[i] = z;
+  }
   if (t < n) {
     if (fl) {
       atomicOr(&s_flags, fl);
@@ -1152,6 +1161,6 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
   else
     hipLaunchKernelGGL((stoch_node_kernel<false, false>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kMaxNodes), 0, stream, p);
+  hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kChaseThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
