@@ -38,13 +38,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source additions.  tree_attn.hip runs without IEEE mode: its softmax takes
+# fmax over finite scores and -inf masks, and IEEE mode would add a
+# canonicalising v_max before every one of them (no NaN input is defined there).
+EXTRA_FLAGS = {"tree_attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
