@@ -56,6 +56,10 @@ def parse():
                     help="instead of the step: measure step latency per (batch size, tree shape) at this "
                          "workload's layer shape and print the goodput tree-size table")
     ap.add_argument("--budget-out", default=None, help="also write the table as markdown to this path")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="no GPU work: turn a rocprofv3 --pmc run of this script with SQ_VALU_MFMA_BUSY_CYCLES, "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_BUSY_CU_CYCLES and GRBM_GUI_ACTIVE into "
+                         "profiles/mfma_<workload>.md")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
                          "WRITE_SIZE, both with --calibrate-copy-mib) into profiles/traffic_*.json")
@@ -147,6 +151,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config, args.calibrate_copy_mib or 256)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary, args.config)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
@@ -746,6 +753,61 @@ def construction_oracle(out):
                    num_blocks=num_blocks)
     el = time.perf_counter() - t0
     out["pool"]["cpu_oracle"] = {"us_per_call": el * 1e6, "cores": 1, "sample": f"all {Bp} requests, {el:.4f} s"}
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
+SIMD_COUNT = 256 * 4      # 256 CUs of four SIMDs
+XCD_COUNT = 8             # GRBM_GUI_ACTIVE is reported summed over the XCDs
+
+
+def mfma_summary(run_dir: str, workload: str):
+    """Matrix-core use of the attention kernel from one rocprofv3 --pmc run:
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GUI-active cycles of one XCD * SIMDs)
+    (rocprofv3's MfmaUtil, which takes GRBM_GUI_ACTIVE's maximum over the XCDs;
+    the csv holds their sum), and the bf16 MFMA flops executed
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512) beside the algorithmic flops of the same
+    call.  The dispatch timestamps give the duration and the implied clock."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            if "tree_attn_kernel" not in name and "attn_merge_kernel" not in name:
+                continue
+            key = "tree_attn_kernel" if "tree_attn_kernel" in name else "attn_merge_kernel"
+            d = per.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    if "tree_attn_kernel" not in per:
+        raise SystemExit(f"no tree_attn_kernel dispatches in {run_dir}")
+    from tree_verification_amd.workloads import make_workload
+    wl = make_workload(workload, with_logits=False)
+    P, n = wl.prefix_len.astype(np.int64), wl.n_nodes.astype(np.int64)
+    flops = sum(4 * int(n[b]) * wl.n_q_heads * wl.head_dim * int(P[b]) for b in range(wl.batch))
+    for b in range(wl.batch):
+        par = wl.parent[b]
+        depth = np.zeros(int(n[b]), dtype=np.int64)
+        for u in range(1, int(n[b])):
+            depth[u] = depth[par[u]] + 1
+        flops += int(4 * wl.n_q_heads * wl.head_dim * (depth + 1).sum())
+    lines = ["| kernel | dispatches | us | GUI-active cycles per XCD | implied GHz | MFMA busy % | "
+             "bf16 MFMA flops executed | algorithmic flops | executed TFLOP/s |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for key, disp in per.items():
+        vals = [d for d in disp.values() if all(c in d for c in MFMA_COUNTERS)]
+        if not vals:
+            continue
+        gui = sum(d["GRBM_GUI_ACTIVE"] for d in vals) / len(vals) / XCD_COUNT
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in vals) / len(vals)
+        mops = sum(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in vals) / len(vals) * 512
+        us = sum(d["ns"] for d in vals) / len(vals) / 1e3
+        alg = f"{flops:,}" if key == "tree_attn_kernel" else "—"
+        lines.append(f"| `{key}` | {len(vals)} | {us:.1f} | {gui:,.0f} | {gui / (us * 1e3):.2f} | "
+                     f"{100 * busy / (gui * SIMD_COUNT):.1f} | {mops:,.0f} | {alg} | {mops / (us * 1e-6) / 1e12:.1f} |")
+    table = "\n".join(lines) + "\n"
+    print(table)
+    return table
 
 
 def cpu_baseline(wl, seconds: float):
