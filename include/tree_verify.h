@@ -180,6 +180,28 @@ int kv_compact_accepted(const tv_attn_desc* desc, void* k_cache, void* v_cache,
                         const int32_t* path, const int32_t* path_len, int32_t* src_pos,
                         int32_t* new_len, int32_t* status, hipStream_t stream);
 
+/* Verify-and-compact: tree_verify_stochastic followed by kv_compact_accepted of
+ * the path it selects ([guide] "Stochastic Verification Algorithm", then
+ * "Depth-First Flattening and KV Cache Reuse"), in one call whose last kernel
+ * both walks the path and moves the K/V, so the path does not travel through
+ * memory between two launches.  Every output equals that of the two calls in
+ * sequence: path, path_len, out_tokens and status as tree_verify_stochastic
+ * gives them; the caches, src_pos, new_len and kv_status (NULL allowed) as
+ * kv_compact_accepted gives them for that path.  kv_desc->batch and n_max must
+ * equal desc->batch and n_max (TV_ERR_INVALID_ARG otherwise); the workspace is
+ * tree_verify_workspace_size(desc) bytes, as for tree_verify_stochastic.
+ * Batches of more than 4 requests run the chase and the compaction as two
+ * kernels (the compaction then spreads over one workgroup per KV head). */
+int tree_verify_stochastic_compact(const tv_verify_desc* desc, const tv_attn_desc* kv_desc,
+                                   const float* target_logits, const float* draft_logits,
+                                   const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
+                                   const float* u_accept, const float* u_sample, int32_t* path,
+                                   int32_t* path_len, int32_t* out_tokens, int32_t* status,
+                                   void* k_cache, void* v_cache, const int32_t* block_table,
+                                   const int32_t* prefix_len, int32_t* src_pos, int32_t* new_len,
+                                   int32_t* kv_status, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* ---- speculative KV blocks -------------------------------------------------
  * [guide] "PagedKV Allocation with Zero-Copy Pruning": the tree's KV blocks are
  * taken from the paged pool and marked speculative; after verification the

@@ -31,6 +31,8 @@ def test_empty_batch_every_entry_point():
 
     src, new_len, cst = tv.kv_compact_accepted(k, v, table, pre, z((0, n_max)), z((0,)))
     assert src.shape == (0, n_max) and new_len.shape == (0,)
+    res = tv.tree_verify_stochastic_compact(logits, logits, tok, par, nn, u, u, k, v, table, pre)
+    assert [tuple(x.shape) for x in res] == [(0, n_max), (0,), (0, n_max), (0,), (0, n_max), (0,), (0,)]
 
     merged = tv.tree_merge_candidates(z((0, 3, 5)), z((0, 3)), z((0,)), n_max)
     assert merged[2].shape == (0,)

@@ -76,6 +76,7 @@ def test_null_descriptors(lib):
     assert lib.tree_verify_greedy(None, *([None] * 9), 0, None) == -1
     assert lib.tree_verify_stochastic(None, *([None] * 12), 0, None) == -1
     assert lib.kv_compact_accepted(None, *([None] * 10)) == -1
+    assert lib.tree_verify_stochastic_compact(None, None, *([None] * 19), 0, None) == -1
     assert lib.tree_attn_workspace_size(None) == 0
     assert lib.tree_verify_workspace_size(None) == 0
 
@@ -107,6 +108,40 @@ def test_missing_pointers_rejected(lib):
     v = tv.VerifyDesc()
     v.batch, v.n_max, v.vocab, v.temperature = 2, 4, 10, 1.0
     assert lib.tree_verify_greedy(ctypes.byref(v), *([None] * 9), 0, None) == -1
+
+
+def _fused(lib, v, d, ptr=None, ws_bytes=0):
+    return lib.tree_verify_stochastic_compact(ctypes.byref(v) if v is not None else None,
+                                              ctypes.byref(d) if d is not None else None,
+                                              *([ptr] * 19), ws_bytes, None)
+
+
+def test_fused_verify_compact_rejections(lib):
+    """The verify-and-compact call checks both descriptors, their agreement and its
+    pointers before any launch (nothing is dereferenced on these paths)."""
+    v = tv.VerifyDesc()
+    v.batch, v.n_max, v.vocab, v.temperature = 2, 4, 10, 1.0
+    d = good_attn_desc()
+    d.batch, d.n_max = 2, 4
+    assert _fused(lib, None, d) == -1
+    assert _fused(lib, v, None) == -1
+    bad = good_attn_desc()
+    bad.batch, bad.n_max, bad.head_dim = 2, 4, 96
+    assert _fused(lib, v, bad) == -2                   # compaction descriptor unsupported
+    v.temperature = 0.0
+    assert _fused(lib, v, d) == -1                     # verification descriptor invalid
+    v.temperature = 1.0
+    d.batch = 3
+    assert _fused(lib, v, d) == -1                     # batches differ
+    d.batch, d.n_max = 2, 8
+    assert _fused(lib, v, d) == -1                     # n_max differs
+    d.n_max = 4
+    assert _fused(lib, v, d) == -1                     # null pointers
+    v.batch = d.batch = 0
+    assert _fused(lib, v, d) == 0                      # empty batch: no-op
+    v.batch = d.batch = 2
+    dummy = ctypes.c_void_p(4096)   # never dereferenced: the workspace check fails first
+    assert _fused(lib, v, d, dummy, 0) == -3
 
 
 def test_stochastic_vocabulary_limit(lib):

@@ -73,6 +73,8 @@ _SIGS = {
     "tree_verify_greedy": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 9 + [_SZ, _P]),
     "tree_verify_stochastic": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 12 + [_SZ, _P]),
     "kv_compact_accepted": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 10),
+    "tree_verify_stochastic_compact": (ctypes.c_int, [ctypes.POINTER(VerifyDesc), ctypes.POINTER(AttnDesc)]
+                                       + [_P] * 19 + [_SZ, _P]),
     "kv_alloc_tree_blocks": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 9),
     "kv_release_blocks": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 7),
     "tree_merge_candidates": (ctypes.c_int, [ctypes.POINTER(MergeDesc)] + [_P] * 9),
@@ -288,23 +290,18 @@ def tree_verify_stochastic(target_logits, draft_logits, tokens, parent, n_nodes,
     return path, path_len, out_tokens, status
 
 
-def kv_compact_accepted(k_cache, v_cache, block_table, prefix_len, path, path_len, *, src_pos=None,
-                        new_len=None, status=None):
-    """In-place accepted-path KV compaction.  Returns (src_pos [B, n_max], new_len [B], status [B])."""
-    lib = load_library()
+def _compact_args(k_cache, v_cache, block_table, prefix_len, B, n_max, src_pos, new_len, status):
+    """Checks of the compaction's cache arguments; returns (desc, src_pos, new_len, status)."""
     dev = k_cache.device
     if k_cache.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("caches must be float32 or bfloat16")
     nb, Hkv, bs, D = k_cache.shape
     _need(k_cache, "k_cache", k_cache.dtype)
     _need(v_cache, "v_cache", k_cache.dtype, (nb, Hkv, D, bs), dev)
-    B, n_max = path.shape
     _need(block_table, "block_table", torch.int32, device=dev)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks]")
     _need(prefix_len, "prefix_len", torch.int32, (B,), dev)
-    _need(path, "path", torch.int32, (B, n_max), dev)
-    _need(path_len, "path_len", torch.int32, (B,), dev)
     if src_pos is None:
         src_pos = torch.empty((B, n_max), dtype=torch.int32, device=dev)
     if new_len is None:
@@ -320,11 +317,61 @@ def kv_compact_accepted(k_cache, v_cache, block_table, prefix_len, path, path_le
     d.max_blocks_per_seq, d.num_blocks = block_table.shape[1], nb
     d.dtype = TV_BF16 if k_cache.dtype == torch.bfloat16 else TV_F32
     d.sm_scale = 0.0
+    return d, src_pos, new_len, status
+
+
+def kv_compact_accepted(k_cache, v_cache, block_table, prefix_len, path, path_len, *, src_pos=None,
+                        new_len=None, status=None):
+    """In-place accepted-path KV compaction.  Returns (src_pos [B, n_max], new_len [B], status [B])."""
+    lib = load_library()
+    dev = k_cache.device
+    B, n_max = path.shape
+    d, src_pos, new_len, status = _compact_args(k_cache, v_cache, block_table, prefix_len, B, n_max, src_pos,
+                                                new_len, status)
+    _need(path, "path", torch.int32, (B, n_max), dev)
+    _need(path_len, "path_len", torch.int32, (B,), dev)
     rc = lib.kv_compact_accepted(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                  _ptr(prefix_len), _ptr(path), _ptr(path_len), _ptr(src_pos),
                                  _ptr(new_len), _ptr(status), _stream(dev))
     _check(rc, "kv_compact_accepted")
     return src_pos, new_len, status
+
+
+def tree_verify_stochastic_compact(target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample,
+                                   k_cache, v_cache, block_table, prefix_len, *, temperature=1.0, path=None,
+                                   path_len=None, out_tokens=None, status=None, src_pos=None, new_len=None,
+                                   kv_status=None, ws=None):
+    """Stochastic verification and the accepted path's KV compaction in one call (arguments as
+    tree_verify_stochastic, then as kv_compact_accepted without the path).
+    Returns (path, path_len, out_tokens, status, src_pos, new_len, kv_status)."""
+    lib = load_library()
+    dev = target_logits.device
+    B, n_max, V = target_logits.shape
+    _need(target_logits, "target_logits", torch.float32)
+    _need(draft_logits, "draft_logits", torch.float32, (B, n_max, V), dev)
+    _need(tokens, "tokens", torch.int32, (B, n_max), dev)
+    _need(parent, "parent", torch.int32, (B, n_max), dev)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    _need(u_accept, "u_accept", torch.float32, (B, n_max), dev)
+    _need(u_sample, "u_sample", torch.float32, (B, n_max), dev)
+    path, path_len, out_tokens, status = _verify_outputs(B, n_max, dev, path, path_len, out_tokens, status)
+    kd, src_pos, new_len, kv_status = _compact_args(k_cache, v_cache, block_table, prefix_len, B, n_max, src_pos,
+                                                    new_len, kv_status)
+    if k_cache.device != dev:
+        raise ValueError("caches and logits must be on one device")
+    desc = verify_desc(target_logits, temperature)
+    need = lib.tree_verify_workspace_size(ctypes.byref(desc))
+    if ws is None:
+        ws = workspace(need, dev, "stochastic", desc)
+    rc = lib.tree_verify_stochastic_compact(ctypes.byref(desc), ctypes.byref(kd), _ptr(target_logits),
+                                            _ptr(draft_logits), _ptr(tokens), _ptr(parent), _ptr(n_nodes),
+                                            _ptr(u_accept), _ptr(u_sample), _ptr(path), _ptr(path_len),
+                                            _ptr(out_tokens), _ptr(status), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(block_table), _ptr(prefix_len), _ptr(src_pos), _ptr(new_len),
+                                            _ptr(kv_status), _ptr(ws), 0 if ws is None else ws.numel(),
+                                            _stream(dev))
+    _check(rc, "tree_verify_stochastic_compact")
+    return path, path_len, out_tokens, status, src_pos, new_len, kv_status
 
 
 def tree_merge_candidates(cand_tokens, cand_len, root_token, n_max, *, tokens=None, parent=None,

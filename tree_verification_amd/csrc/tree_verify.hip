@@ -43,6 +43,7 @@
 // Vocabulary exponentials are float32 (exp_t), sums and the accept test float64.
 
 #include "tv_common.h"
+#include "tv_compact.h"
 
 #include <math.h>
 
@@ -905,32 +906,52 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
 // and the exchange slots cleared for the next call.
 constexpr int kChaseThreads = 256;
 
-__global__ __launch_bounds__(kChaseThreads) void stoch_chase_kernel(StochParams p) {
-  __shared__ int s_acc[kMaxNodes], s_fin[kMaxNodes], s_tok[kMaxNodes];
-  __shared__ int s_flags, s_badpar;
-  const int t = threadIdx.x, b = blockIdx.x;
-  // every load of the request's rows is issued at once, before n_nodes is
-  // known (rows are n_max long; entries past n are not used)
+struct ChaseSmem {
+  int acc[kMaxNodes], fin[kMaxNodes], tok[kMaxNodes], path[kMaxNodes];
+  int flags, badpar, len, bad;
+};
+
+// The request's rows the chase reads, one entry per thread (thread t < n_max
+// holds node t's).
+struct ChaseLoads {
+  int fl, acc, fin, tk, pv, n;
+};
+
+// Issues every load of request b's rows at once, before n_nodes is known (rows
+// are n_max long; entries past n are not used).
+__device__ __forceinline__ ChaseLoads chase_load(const StochParams& p, int b) {
+  const int t = threadIdx.x;
   const size_t kv = (size_t)b * p.n_max + t;
-  int fl = 0, acc = -1, fin = 0, tk = 0, pv = -1;
+  ChaseLoads c{0, -1, 0, 0, -1, 0};
   if (t < p.n_max) {
-    fl = p.node_flags[kv];
-    acc = p.node_acc[kv];
-    fin = p.node_tok[kv];
-    tk = p.tokens[kv];
-    pv = p.parent[kv];
+    c.fl = p.node_flags[kv];
+    c.acc = p.node_acc[kv];
+    c.fin = p.node_tok[kv];
+    c.tk = p.tokens[kv];
+    c.pv = p.parent[kv];
   }
-  const int n = p.n_nodes[b];
+  c.n = p.n_nodes[b];
+  return c;
+}
+
+// The chase of request b by the whole workgroup (any size of at least
+// kMaxNodes threads), from its rows loaded by chase_load.  Returns (to every
+// thread) the length of the path written, 0 when the request failed; the path
+// is also left in sm.path.
+__device__ int chase_request(const StochParams& p, ChaseSmem& sm, int b, const ChaseLoads& c) {
+  const int t = threadIdx.x;
+  const size_t kv = (size_t)b * p.n_max + t;
+  const int n = c.n;
   if (n < 1 || n > p.n_max) {
     if (t == 0) {
       p.status[b] = TV_REQ_BAD_NNODES;
       p.path_len[b] = 0;
     }
-    return;
+    return 0;
   }
   if (t == 0) {
-    s_flags = 0;
-    s_badpar = 0;
+    sm.flags = 0;
+    sm.badpar = 0;
   }
   __syncthreads();
   // every exchange slot the node kernel may have written for this request, in
@@ -940,42 +961,97 @@ __global__ __launch_bounds__(kChaseThreads) void stoch_chase_kernel(StochParams 
     tv_u32x4* sx = (tv_u32x4*)(p.sxch + (size_t)b * p.n_max * kMaxTeam * 4);
     tv_u32x4* xc = (tv_u32x4*)(p.xch + (size_t)b * p.n_max * kMaxTeam);
     const tv_u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = t; i < n * kMaxTeam * 2; i += kChaseThreads) sx[i] = z;
-    for (int i = t; i < n * kMaxTeam / 2; i += kChaseThreads) xc[i] = z;
+    for (int i = t; i < n * kMaxTeam * 2; i += blockDim.x) sx[i] = z;
+    for (int i = t; i < n * kMaxTeam / 2; i += blockDim.x) xc[i] = z;
   }
   if (t < n) {
-    if (fl) {
-      atomicOr(&s_flags, fl);
+    if (c.fl) {
+      atomicOr(&sm.flags, c.fl);
       p.node_flags[kv] = 0;
     }
-    s_acc[t] = acc;
-    s_fin[t] = fin;
-    s_tok[t] = tk;
-    if (!((t == 0) ? (pv == -1) : (pv >= 0 && pv < t))) s_badpar = 1;
+    sm.acc[t] = c.acc;
+    sm.fin[t] = c.fin;
+    sm.tok[t] = c.tk;
+    if (!((t == 0) ? (c.pv == -1) : (c.pv >= 0 && c.pv < t))) sm.badpar = 1;
   }
   __syncthreads();
   if (t == 0) {
-    const int fl = s_badpar ? TV_REQ_BAD_PARENT : s_flags;
+    const int fl = sm.badpar ? TV_REQ_BAD_PARENT : sm.flags;
     if (fl) {
       p.status[b] = fl;
       p.path_len[b] = 0;
-      return;
+      sm.len = 0;
+    } else {
+      int32_t* path = p.path + (size_t)b * p.n_max;
+      int32_t* out = p.out_tokens + (size_t)b * p.n_max;
+      int cur = 0, j = 0;
+      path[0] = 0;
+      sm.path[0] = 0;
+      for (;;) {
+        const int ch = sm.acc[cur];
+        if (ch <= cur || ch >= n || j + 1 >= n) break;
+        out[j] = sm.tok[ch];
+        ++j;
+        path[j] = ch;
+        sm.path[j] = ch;
+        cur = ch;
+      }
+      out[j] = sm.fin[cur];
+      p.path_len[b] = j + 1;
+      p.status[b] = 0;
+      sm.len = j + 1;
     }
-    int32_t* path = p.path + (size_t)b * p.n_max;
-    int32_t* out = p.out_tokens + (size_t)b * p.n_max;
-    int cur = 0, j = 0;
-    path[0] = 0;
-    for (;;) {
-      const int ch = s_acc[cur];
-      if (ch <= cur || ch >= n || j + 1 >= n) break;
-      out[j] = s_tok[ch];
-      path[++j] = ch;
-      cur = ch;
-    }
-    out[j] = s_fin[cur];
-    p.path_len[b] = j + 1;
-    p.status[b] = 0;
   }
+  __syncthreads();
+  return sm.len;
+}
+
+__global__ __launch_bounds__(kChaseThreads) void stoch_chase_kernel(StochParams p) {
+  __shared__ ChaseSmem sm;
+  chase_request(p, sm, blockIdx.x, chase_load(p, blockIdx.x));
+}
+
+// Verify-and-compact: the chase of request b, then the compaction of all its
+// KV heads along the path just found (tv_compact.h), in the same workgroup, so
+// no path round-trips through memory and no second launch is needed.  The
+// block-table entries the compaction checks and uses are read beside the
+// chase's rows, before the path is known: every entry among those of positions
+// [0, P + n) (the path's last node is below n), and the entries of positions
+// [P, P + n) kept for the moves.  1024 threads: one (KV head, element) pair
+// each up to n_kv_heads * head_dim = 1024, so every pair's moves take a single
+// load-then-store round trip.
+constexpr int kChaseCompactThreads = 1024;
+// Batches above this size take the chase and the compaction as two kernels
+// (measured on MI355X: one request gains ~1.4 us per step from the fused
+// kernel; 16 and 64 requests lose 10-14 us, their moves crowded onto one CU
+// per request).
+constexpr int kFusedChaseMaxBatch = 4;
+constexpr int kStagedBlocks = kMaxNodes / 16 + 2;   // blocks holding n <= 128 positions (block size >= 16)
+
+template <typename T>
+__global__ __launch_bounds__(kChaseCompactThreads) void stoch_chase_compact_kernel(StochParams p, TvCompactArgs c) {
+  __shared__ ChaseSmem sm;
+  __shared__ int s_first_bad;
+  __shared__ int s_stage[kStagedBlocks];
+  const int t = threadIdx.x, b = blockIdx.x;
+  const ChaseLoads cl = chase_load(p, b);
+  const int P = c.prefix_len[b];
+  if (t == 0) s_first_bad = kTvNoBadBlock;
+  __syncthreads();
+  int stage0 = 0;
+  if (cl.n >= 1 && cl.n <= p.n_max && P >= 0) {
+    const int nblk_max = (int)min((long long)(P + cl.n - 1) / c.bs + 1, (long long)c.max_blocks);
+    stage0 = P / c.bs;
+    const int32_t* trow = c.table + (size_t)b * c.max_blocks;
+    for (int i = t; i < nblk_max; i += blockDim.x) {
+      const int blk = trow[i];
+      if (blk < 0 || blk >= c.num_blocks) atomicMin(&s_first_bad, i);
+      if (i >= stage0) s_stage[i - stage0] = blk;
+    }
+  }
+  const int len = chase_request(p, sm, b, cl);   // synchronises before it returns
+  const TvTablePrefetch pre{s_first_bad, stage0, s_stage};
+  tv_compact_heads<T>(c, b, 0, c.Hkv, sm.path, len, P, &pre, &sm.bad);
 }
 
 // ===========================================================================
@@ -1088,15 +1164,17 @@ extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* targe
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
-extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* target_logits,
-                                      const float* draft_logits, const int32_t* tokens,
-                                      const int32_t* parent, const int32_t* n_nodes,
-                                      const float* u_accept, const float* u_sample, int32_t* path,
-                                      int32_t* path_len, int32_t* out_tokens, int32_t* status,
-                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Checks the arguments of a stochastic verification and launches its node
+// kernel; on TV_OK, p holds the parameters the chase needs.
+int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, const float* draft_logits,
+                       const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
+                       const float* u_accept, const float* u_sample, int32_t* path, int32_t* path_len,
+                       int32_t* out_tokens, int32_t* status, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, StochParams& p) {
   int rc = check_vdesc(desc);
   if (rc != TV_OK) return rc;
-  if (desc->batch == 0) return TV_OK;
   if (!target_logits || !draft_logits || !tokens || !parent || !n_nodes || !u_accept || !u_sample ||
       !path || !path_len || !out_tokens || !status)
     return TV_ERR_INVALID_ARG;
@@ -1108,7 +1186,6 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
   const TeamPlan tp = plan_team(L.chunks);
   const bool resident = tp.per <= kResident;
 
-  StochParams p;
   p.target = target_logits;
   p.draft = draft_logits;
   p.tokens = tokens;
@@ -1160,7 +1237,63 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
     hipLaunchKernelGGL((stoch_node_kernel<false, true>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((stoch_node_kernel<false, false>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* target_logits,
+                                      const float* draft_logits, const int32_t* tokens,
+                                      const int32_t* parent, const int32_t* n_nodes,
+                                      const float* u_accept, const float* u_sample, int32_t* path,
+                                      int32_t* path_len, int32_t* out_tokens, int32_t* status,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_vdesc(desc);
+  if (rc != TV_OK) return rc;
+  if (desc->batch == 0) return TV_OK;
+  StochParams p;
+  rc = launch_stoch_nodes(desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path,
+                          path_len, out_tokens, status, workspace, workspace_bytes, stream, p);
+  if (rc != TV_OK) return rc;
   hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kChaseThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+extern "C" int tree_verify_stochastic_compact(const tv_verify_desc* desc, const tv_attn_desc* kv_desc,
+                                              const float* target_logits, const float* draft_logits,
+                                              const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
+                                              const float* u_accept, const float* u_sample, int32_t* path,
+                                              int32_t* path_len, int32_t* out_tokens, int32_t* status,
+                                              void* k_cache, void* v_cache, const int32_t* block_table,
+                                              const int32_t* prefix_len, int32_t* src_pos, int32_t* new_len,
+                                              int32_t* kv_status, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  int rc = check_vdesc(desc);
+  if (rc != TV_OK) return rc;
+  rc = tv_compact_check_desc(kv_desc);
+  if (rc != TV_OK) return rc;
+  if (kv_desc->batch != desc->batch || kv_desc->n_max != desc->n_max) return TV_ERR_INVALID_ARG;
+  if (desc->batch == 0) return TV_OK;
+  if (!k_cache || !v_cache || !block_table || !prefix_len || !src_pos || !new_len) return TV_ERR_INVALID_ARG;
+  StochParams p;
+  rc = launch_stoch_nodes(desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path,
+                          path_len, out_tokens, status, workspace, workspace_bytes, stream, p);
+  if (rc != TV_OK) return rc;
+  if (desc->batch > kFusedChaseMaxBatch) {
+    // many requests: the chase, then the compaction's own grid of one
+    // workgroup per (request, KV head), which spreads the moves over more CUs
+    hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kChaseThreads), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+    return kv_compact_accepted(kv_desc, k_cache, v_cache, block_table, prefix_len, path, path_len, src_pos,
+                               new_len, kv_status, stream);
+  }
+  const TvCompactArgs c =
+      tv_compact_args(kv_desc, k_cache, v_cache, block_table, prefix_len, src_pos, new_len, kv_status);
+  if (kv_desc->dtype == TV_BF16)
+    hipLaunchKernelGGL(stoch_chase_compact_kernel<uint16_t>, dim3((unsigned)desc->batch), dim3(kChaseCompactThreads),
+                       0, stream, p, c);
+  else
+    hipLaunchKernelGGL(stoch_chase_compact_kernel<float>, dim3((unsigned)desc->batch), dim3(kChaseCompactThreads),
+                       0, stream, p, c);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
