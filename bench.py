@@ -264,10 +264,6 @@ def main():
     del pristine_k, pristine_v
 
     # ---- whole-step timing -------------------------------------------------
-    for i in range(args.warmup):
-        step(copies[i % ncopies])
-    torch.cuda.synchronize()
-
     def time_steps(fn):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
@@ -277,9 +273,19 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / args.steps
 
-    # The same work as three separate calls is timed first (it also keeps the
-    # GPU busy right before the headline loop); then exactly `steps` steps.
+    def warm(fn):
+        for i in range(args.warmup):
+            fn(copies[i % ncopies])
+        torch.cuda.synchronize()
+
+    # The same work as three separate calls is timed first, in a second round
+    # after one untimed round (the first timed loop after a short warm-up runs
+    # slower while the GPU ramps up); then the step: `warmup` untimed steps and
+    # exactly `steps` timed ones.
+    warm(step_separate)
+    time_steps(step_separate)
     ms_step_separate = time_steps(step_separate)
+    warm(step)
     ms_step = time_steps(step)
 
     # ---- per-kernel timing (back-to-back calls on rotating copies) ----------
