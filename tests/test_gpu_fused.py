@@ -147,3 +147,24 @@ def test_fused_repeated_calls_and_smaller_batch():
             setattr(d, f, getattr(d, f)[:nb].contiguous())
         sep, fused = _both(d)
         _same(sep, fused, SimpleNamespace(batch=nb))
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_fused_fp32_paged_block_sizes(bs):
+    """float32 caches, paged block tables (blocks scattered over the pool), two KV
+    heads, block sizes 16 and 64, short and long prefixes: the fused kernel
+    (3 requests) against the separate calls."""
+    from tree_verification_amd import workloads as W
+    W.CONFIGS["_f"] = dict(W.CONFIGS["tiny"], block_size=bs, paged=True, n_kv_heads=2, n_q_heads=2)
+    W.CONFIG_ORDER.append("_f")
+    try:
+        wl = make_workload("_f", seed=100 + bs, batch=3, prefix=(10, 200), n_nodes=12)
+    finally:
+        W.CONFIG_ORDER.remove("_f")
+        del W.CONFIGS["_f"]
+    print(f"case fused fp32 paged block_size={bs}", flush=True)
+    d = DevWorkload(wl)
+    sep, fused = _both(d)
+    assert not sep[3].any() and not sep[6].any()
+    assert (sep[1] > 1).any()            # some request moves K/V
+    _same(sep, fused, wl)

@@ -39,7 +39,11 @@
 //                         member masses, chunk masses, then one chunk;
 //   stoch_chase_kernel    one workgroup per request: status, the root path and
 //                         its final token, and the exchange slots cleared for
-//                         the next call.
+//                         the next call;
+//   stoch_chase_compact_kernel  the same chase, then the accepted path's KV
+//                         compaction ([guide] "Depth-First Flattening and KV
+//                         Cache Reuse") in the same workgroup (verify-and-compact
+//                         for up to four requests).
 // Vocabulary exponentials are float32 (exp_t), sums and the accept test float64.
 
 #include "tv_common.h"
