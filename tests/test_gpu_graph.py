@@ -1,5 +1,6 @@
-"""The step (tree attention, stochastic verification, KV compaction) captured as a
-HIP graph and replayed: every replay, with eager calls and synchronisations between
+"""The step (tree attention, stochastic verification, KV compaction; as three calls
+and as attention plus the verify-and-compact call) captured as a HIP graph and
+replayed: every replay, with eager calls and synchronisations between
 the replays, gives exactly the eager results (the verifiers' workspaces and the
 attention workspace are reused across replays, so this also checks that every call
 leaves them as the next one expects)."""
@@ -36,9 +37,15 @@ def reset(o):
             t.fill_(0 if key == "out" else -7)
 
 
-def step(dw, o):
+def step(dw, o, fused):
     tv.tree_attn_forward(dw.q, o["k"], o["v"], dw.table, dw.prefix_len, dw.n_nodes, dw.parent, out=o["out"],
                          status=o["ast"])
+    if fused:
+        tv.tree_verify_stochastic_compact(dw.target, dw.draft, dw.tokens, dw.parent, dw.n_nodes, dw.u_accept,
+                                          dw.u_sample, o["k"], o["v"], dw.table, dw.prefix_len, path=o["path"],
+                                          path_len=o["plen"], out_tokens=o["otok"], status=o["vst"],
+                                          src_pos=o["src"], new_len=o["nlen"], kv_status=o["cst"])
+        return
     tv.tree_verify_stochastic(dw.target, dw.draft, dw.tokens, dw.parent, dw.n_nodes, dw.u_accept, dw.u_sample,
                               path=o["path"], path_len=o["plen"], out_tokens=o["otok"], status=o["vst"])
     tv.kv_compact_accepted(o["k"], o["v"], dw.table, dw.prefix_len, o["path"], o["plen"], src_pos=o["src"],
@@ -49,14 +56,15 @@ def snapshot(o):
     return {key: t.clone() for key, t in o.items()}
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", ["tiny", "llama8b"])
-def test_step_graph_replays_match_eager(name):
+def test_step_graph_replays_match_eager(name, fused):
     wl = make_workload(name)
     dw = DevWorkload(wl)
     k0, v0 = dw.k.clone(), dw.v.clone()
     # eager reference on its own cache copy
     ref = outputs(dw, k0.clone(), v0.clone())
-    step(dw, ref)
+    step(dw, ref, fused)
     torch.cuda.synchronize()
     ref = snapshot(ref)
     assert int(ref["ast"].abs().sum()) == 0 and int(ref["vst"].abs().sum()) == 0
@@ -65,11 +73,11 @@ def test_step_graph_replays_match_eager(name):
     side.wait_stream(torch.cuda.current_stream())
     g_out = outputs(dw, k0.clone(), v0.clone())
     with torch.cuda.stream(side):
-        step(dw, g_out)          # eager warm-up: the side stream's workspaces
+        step(dw, g_out, fused)   # eager warm-up: the side stream's workspaces
     side.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
-        step(dw, g_out)
+        step(dw, g_out, fused)
     torch.cuda.synchronize()
 
     other = outputs(dw, k0.clone(), v0.clone())
@@ -87,7 +95,7 @@ def test_step_graph_replays_match_eager(name):
         other["k"].copy_(k0)
         other["v"].copy_(v0)
         reset(other)
-        step(dw, other)
+        step(dw, other, fused)
         torch.cuda.synchronize()
         for key, t in ref.items():
             assert torch.equal(other[key], t), (name, rep, "eager", key)

@@ -1044,7 +1044,7 @@ __global__ __launch_bounds__(kChaseCompactThreads) void stoch_chase_compact_kern
   __syncthreads();
   int stage0 = 0;
   if (cl.n >= 1 && cl.n <= p.n_max && P >= 0) {
-    const int nblk_max = (int)min((long long)(P + cl.n - 1) / c.bs + 1, (long long)c.max_blocks);
+    const int nblk_max = (int)min(((long long)P + cl.n - 1) / c.bs + 1, (long long)c.max_blocks);
     stage0 = P / c.bs;
     const int32_t* trow = c.table + (size_t)b * c.max_blocks;
     for (int i = t; i < nblk_max; i += blockDim.x) {
