@@ -89,6 +89,9 @@ CASES = [
     ("llama8b", dict(vocab=16389, n_nodes=50, tree="star")),   # wide node: many siblings
     ("llama8b", dict(vocab=3000, n_nodes=1)),          # root only
     ("chain", dict(batch=16, prefix=1, vocab=36001)),  # 9 chunks: a team of 8, three members own no chunk
+    # vocabularies past 16 members x 2 chunks: members stream their slices again per rejection
+    ("llama8b", dict(vocab=152064, n_nodes=24)),       # 38 chunks, 3 per member
+    ("ragged", dict(batch=3, prefix=(1, 2), vocab=256003)),   # 63 chunks, 4 per member, odd vocabulary
 ]
 
 
