@@ -98,15 +98,17 @@ def custom(dtype, Hq, Hkv, D, n, P, B=2, seed=3, kind="capped"):
         del W.CONFIGS["_c"]
 
 
-@pytest.mark.parametrize("dtype,Hq,Hkv,D,n,P", [
-    ("bf16", 8, 2, 64, 30, (10, 300)),      # head_dim 64 on MFMA
-    ("bf16", 4, 4, 64, 10, (0, 64)),        # G = 1, R < 16: one MFMA wave, padding rows
-    ("f32", 8, 2, 128, 24, (50, 200)),      # fp32, R = 96: VALU over 6 row tiles
-    ("f32", 2, 1, 64, 100, (1, 33)),        # fp32, deep tree, short prefix
-    ("bf16", 16, 2, 128, 128, (3, 3)),      # R = 1024 with a 3-token prefix
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,n,P,B", [
+    ("bf16", 8, 2, 64, 30, (10, 300), 2),   # head_dim 64 on MFMA
+    ("bf16", 4, 4, 64, 10, (0, 64), 2),     # G = 1, R < 16: one MFMA wave, padding rows
+    ("f32", 8, 2, 128, 24, (50, 200), 2),   # fp32, R = 96: VALU over 6 row tiles
+    ("f32", 2, 1, 64, 100, (1, 33), 2),     # fp32, deep tree, short prefix
+    ("bf16", 16, 2, 128, 128, (3, 3), 2),   # R = 1024 with a 3-token prefix
+    ("bf16", 16, 2, 64, 64, (10, 300), 8),  # head_dim 64 with 128-row tiles (16 pairs x 4 tiles)
 ])
-def test_attention_shapes(dtype, Hq, Hkv, D, n, P):
-    wl = custom(dtype, Hq, Hkv, D, n, P)
+def test_attention_shapes(dtype, Hq, Hkv, D, n, P, B):
+    wl = custom(dtype, Hq, Hkv, D, n, P, B=B)
+    print(f"case shapes {dtype} Hq={Hq} Hkv={Hkv} D={D} n={n} P={P} B={B}", flush=True)
     out, st, _, _ = run_gpu(wl)
     check_all_rows(wl, out, st)
 
