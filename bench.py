@@ -67,6 +67,36 @@ def parse():
     return ap.parse_args()
 
 
+def gated_us_per_call(call, reps: int, cyc_per_s: float) -> float:
+    """GPU microseconds per call of `reps` back-to-back calls (call(i) enqueues call i).
+
+    A spin kernel holds the stream while the host enqueues the calls, so that the
+    events bracket GPU execution only.  The spin is sized from an untimed pass of
+    the same calls; if the timed pass's enqueueing outlasts the spin (the GPU
+    would then wait for the host inside the timed region), the pass is repeated
+    with a longer spin, at most twice."""
+    import torch
+    h0 = time.perf_counter()
+    for i in range(reps):
+        call(i)
+    spin_s = 2.0 * (time.perf_counter() - h0) + 2e-3
+    torch.cuda.synchronize()
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(cyc_per_s * spin_s))
+        a.record()
+        h1 = time.perf_counter()
+        for i in range(reps):
+            call(i)
+        enq_s = time.perf_counter() - h1
+        b.record()
+        torch.cuda.synchronize()
+        if enq_s < 0.8 * spin_s:
+            break
+        spin_s = 3.0 * enq_s + 2e-3
+    return a.elapsed_time(b) / reps * 1e3
+
+
 def kernel_is(name: str, full: str) -> bool:
     """True when the profiler's kernel name `full` is kernel `name` (a whole
     identifier: compact_kernel is not stoch_chase_compact_kernel)."""
@@ -307,19 +337,7 @@ def main():
         for i in range(min(reps, 5)):
             fn(copies[i % ncopies])
         torch.cuda.synchronize()
-        h0 = time.perf_counter()
-        for i in range(reps):
-            fn(copies[i % ncopies])
-        host_s = time.perf_counter() - h0
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(int(cyc_per_s * (2.0 * host_s + 2e-3)))
-        a.record()
-        for i in range(reps):
-            fn(copies[i % ncopies])
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e3   # microseconds per call
+        return gated_us_per_call(lambda i: fn(copies[i % ncopies]), reps, cyc_per_s)
 
     us_attn = time_calls(attn, args.kernel_reps)
     us_verify = time_calls(verify, args.kernel_reps)
@@ -476,19 +494,7 @@ def bench_construction(args, dev, cyc_per_s):
         for f in fns[:2]:
             f()
         torch.cuda.synchronize()
-        h0 = time.perf_counter()
-        for i in range(reps):
-            fns[i % len(fns)]()
-        host_s = time.perf_counter() - h0
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(int(cyc_per_s * (2.0 * host_s + 2e-3)))
-        a.record()
-        for i in range(reps):
-            fns[i % len(fns)]()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e3
+        return gated_us_per_call(lambda i: fns[i % len(fns)](), reps, cyc_per_s)
 
     out = {}
     e = EXPAND_SHAPE
@@ -517,8 +523,8 @@ def bench_construction(args, dev, cyc_per_s):
 
     reps = max(args.kernel_reps, 20)
     # every call appends F * k nodes per request: reset the counts so that no call overflows
-    # (timed() makes two passes of `reps` calls plus a warm-up call per set)
-    us_exp = timed([expand_fn(c) for c in sets], min(reps, ((n_max - n0) // (F * k) - 2) // 2 * ncp))
+    # (timed() makes up to four passes of `reps` calls plus two warm-up calls)
+    us_exp = timed([expand_fn(c) for c in sets], min(reps, ((n_max - n0) // (F * k) - 2) // 4 * ncp))
     for c in sets:
         c["nn"].fill_(n0)
     expand_fn(sets[0])()
