@@ -184,15 +184,59 @@ def verify_stochastic(target_logits, draft_logits, tokens, parent, n_nodes, u_ac
     return paths, outs, traces, status
 
 
-def in_band(trace, band: float = 1e-6) -> bool:
-    """True when some traced decision's uniform lies within `band` of its threshold."""
+def divergence_in_band(trace, path, out, other_path, other_out, band: float = 1e-6) -> bool:
+    """Whether another verifier's result may differ from this oracle's (reading C18).
+
+    `trace`, `path` and `out` are this oracle's decision trace and result for
+    one request; `other_path` and `other_out` are the other result.  Equal
+    results are accepted.  Otherwise the oracle's decisions are replayed in
+    trace order and the first one whose outcome the other result does not
+    share is located:
+      * an accept test of child c at node u diverges when the other path
+        enters c after u and the oracle's does not, or the other way round;
+        it lies in the band when |u_accept - p'(x)/q(x)| < band (a test with
+        q(x) = 0 always accepts and is never in the band);
+      * the draw at the node where both walks stop diverges when the emitted
+        tokens differ; it lies in the band when u_sample is within `band` of
+        either end of the CDF interval the oracle's draw fell in.
+    Only that first divergent decision may lie in the band; later decisions
+    are not looked at (after it the two walks follow different subtrees).  A
+    difference that no decision explains (a path that leaves the oracle's
+    walk without a divergent test, or tokens that differ on agreed nodes)
+    returns False.
+    """
+    path, out = list(path), list(out)
+    other_path, other_out = list(other_path), list(other_out)
+    if path == other_path and out == other_out:
+        return True
+    pos = 0                                   # index of the current node in both paths
     for rec in trace:
+        node = rec[1]
+        if pos >= len(path) or path[pos] != node:
+            return False                      # the trace does not follow the oracle's path
+        if pos >= len(other_path) or other_path[pos] != node:
+            return False                      # the other walk left earlier without a divergent test
+        mine_next = path[pos + 1] if pos + 1 < len(path) else None
+        other_next = other_path[pos + 1] if pos + 1 < len(other_path) else None
         if rec[0] == "accept":
-            if np.isfinite(rec[4]) and abs(rec[3] - rec[4]) < band:
-                return True
+            child, ua, ratio = rec[2], rec[3], rec[4]
+            mine = mine_next == child
+            other = other_next == child
+            if mine != other:
+                return bool(np.isfinite(ratio) and abs(ua - ratio) < band)
+            if mine:
+                if pos >= len(other_out) or other_out[pos] != out[pos]:
+                    return False              # same accepted node, different token
+                pos += 1
         else:
-            if abs(rec[3] - rec[4]) < band or abs(rec[3] - rec[5]) < band:
-                return True
+            token, us, lo, hi = rec[2], rec[3], rec[4], rec[5]
+            if other_next is not None:
+                return False                  # the other walk went on past the oracle's last node
+            if pos >= len(other_out):
+                return False
+            if other_out[pos] != token:
+                return bool(abs(us - lo) < band or abs(us - hi) < band)
+            return len(other_path) == len(path) and other_out[:pos + 1] == out[:pos + 1]
     return False
 
 

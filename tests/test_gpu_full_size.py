@@ -11,7 +11,7 @@ import torch
 
 from devdata import DevWorkload
 from oracle.kv import kv_compact
-from oracle.verify import in_band, linear_greedy, linear_speculative, verify_greedy, verify_stochastic
+from oracle.verify import divergence_in_band, linear_greedy, linear_speculative, verify_greedy, verify_stochastic
 from tree_verification_amd import binding as tv
 from tree_verification_amd.workloads import make_workload
 
@@ -42,7 +42,7 @@ def test_full_size_verify_and_compact(name):
         assert st[0] == 0
         L = int(gl[b])
         if list(gp[b, :L]) != paths[0] or list(gt[b, :L]) != outs[0]:
-            assert in_band(traces[0]), (b, list(gp[b, :L]), paths[0])
+            assert divergence_in_band(traces[0], paths[0], outs[0], gp[b, :L], gt[b, :L]), (b, list(gp[b, :L]), paths[0])
             banded += 1
             band_ids.add(b)
     print(f"  stochastic: {wl.batch} requests, {banded} inside the decision band", flush=True)

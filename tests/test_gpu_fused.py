@@ -13,7 +13,7 @@ import pytest
 
 from devdata import DevWorkload, i32
 from oracle.kv import kv_compact
-from oracle.verify import in_band, verify_stochastic
+from oracle.verify import divergence_in_band, verify_stochastic
 from tree_verification_amd import binding as tv
 from tree_verification_amd.workloads import make_workload
 
@@ -83,7 +83,7 @@ def test_fused_against_the_oracle(name):
                                                     wl.u_sample[sl], wl.n_max)
         L = int(gl[b])
         if list(gp[b, :L]) != paths[0] or list(gt[b, :L]) != outs[0]:
-            assert in_band(traces[0]), b
+            assert divergence_in_band(traces[0], paths[0], outs[0], gp[b, :L], gt[b, :L]), b
             banded += 1
     assert banded <= 1
     path = np.full((wl.batch, wl.n_max), -1, dtype=np.int32)

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from markov_trials import SHAPE, chi_square_pvalue, draw_round, markov_tables, softmax_rows
-from oracle.verify import in_band, verify_stochastic_request
+from oracle.verify import divergence_in_band, verify_stochastic_request
 from tree_verification_amd import binding as tv
 
 pytestmark = pytest.mark.gpu
@@ -29,9 +29,10 @@ BATCH = 200_000
 
 def gpu_rounds(tok, tl, dl, ua, us, parent):
     """Run the trials through tree_verify_stochastic in batches; returns
-    (path_len, out_tokens, status) on the host."""
+    (path_len, out_tokens, status, paths) on the host."""
     T, n = tok.shape
     plen = np.empty(T, dtype=np.int32)
+    paths = np.empty((T, n), dtype=np.int32)
     outs = np.empty((T, n), dtype=np.int32)
     st = np.empty(T, dtype=np.int32)
     par = np.broadcast_to(parent, (min(T, BATCH), n))
@@ -40,12 +41,13 @@ def gpu_rounds(tok, tl, dl, ua, us, parent):
         f = lambda a: torch.from_numpy(np.ascontiguousarray(a[s:e])).to(DEV)
         nn = torch.full((e - s,), n, dtype=torch.int32, device=DEV)
         pt = torch.from_numpy(np.ascontiguousarray(par[: e - s])).to(DEV)
-        _, pl, ot, ss = tv.tree_verify_stochastic(f(tl), f(dl), f(tok), pt, nn, f(ua), f(us))
+        pa, pl, ot, ss = tv.tree_verify_stochastic(f(tl), f(dl), f(tok), pt, nn, f(ua), f(us))
         torch.cuda.synchronize()
+        paths[s:e] = pa.cpu().numpy()
         plen[s:e] = pl.cpu().numpy()
         outs[s:e] = ot.cpu().numpy()
         st[s:e] = ss.cpu().numpy()
-    return plen, outs, st
+    return plen, outs, st, paths
 
 
 def test_two_token_chi_square_million_trials():
@@ -55,7 +57,7 @@ def test_two_token_chi_square_million_trials():
     n = len(SHAPE)
     tok, tl, dl, ua, us = draw_round(rng, LT, LQ, np.full(T, start))
     print("round 1", flush=True)
-    plen, outs, st = gpu_rounds(tok, tl, dl, ua, us, SHAPE)
+    plen, outs, st, gpaths = gpu_rounds(tok, tl, dl, ua, us, SHAPE)
     assert not st.any()
     x1 = outs[:, 0].astype(np.int64)
     x2 = np.where(plen > 1, outs[:, 1], -1).astype(np.int64)
@@ -63,9 +65,10 @@ def test_two_token_chi_square_million_trials():
     # the first trials match the oracle request by request
     mism = 0
     for t in range(20_000):
-        _, out, trace = verify_stochastic_request(tl[t], dl[t], tok[t], SHAPE, n, ua[t], us[t])
-        if list(outs[t, :plen[t]]) != out:
-            assert in_band(trace), (t, list(outs[t, :plen[t]]), out)
+        path, out, trace = verify_stochastic_request(tl[t], dl[t], tok[t], SHAPE, n, ua[t], us[t])
+        L = int(plen[t])
+        if list(gpaths[t, :L]) != path or list(outs[t, :L]) != out:
+            assert divergence_in_band(trace, path, out, gpaths[t, :L], outs[t, :L]), (t, list(outs[t, :L]), out)
             mism += 1
     assert mism <= 2
 

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from devdata import DevWorkload
-from oracle.verify import in_band, verify_greedy, verify_stochastic
+from oracle.verify import divergence_in_band, verify_greedy, verify_stochastic
 from tree_verification_amd import binding as tv
 from tree_verification_amd.workloads import make_workload
 
@@ -72,7 +72,8 @@ def check_stoch(wl, d, temperature=1.0):
         L = int(gl[b])
         same = list(gp[b, :L]) == paths[b] and list(gt[b, :L]) == outs[b]
         if not same:
-            assert in_band(traces[b]), (b, list(gp[b, :L]), paths[b], list(gt[b, :L]), outs[b])
+            assert divergence_in_band(traces[b], paths[b], outs[b], gp[b, :L], gt[b, :L]), \
+                (b, list(gp[b, :L]), paths[b], list(gt[b, :L]), outs[b])
             banded += 1
         lens.append(L)
     return lens, banded

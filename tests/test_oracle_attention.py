@@ -187,3 +187,20 @@ def test_bad_block_table_flags():
                            np.array([2]), np.array([[-1, 0]]), n_q_heads=1, n_kv_heads=1,
                            block_size=8, num_blocks=nb, n_max=2, sm_scale=0.5)
     assert st[0] == BAD_KV
+
+
+def test_kv_status_cases():
+    """The request-level KV checks, case by case against hand-worked answers:
+    positions [0, P + n) need ceil((P + n) / bs) table entries, each naming a
+    block inside the pool; a negative prefix is malformed."""
+    from oracle.attention import kv_status
+    row = np.array([3, 0, 5, -1, -1])          # three mapped blocks, two unused entries
+    bs, nb = 8, 6
+    assert kv_status(row, 0, 1, bs, nb) == 0             # one position: block 3
+    assert kv_status(row, 20, 4, bs, nb) == 0            # 24 positions: exactly 3 blocks
+    assert kv_status(row, 20, 5, bs, nb) == BAD_KV       # 25 positions: entry 3 is -1
+    assert kv_status(row, -1, 2, bs, nb) == BAD_KV       # negative prefix
+    assert kv_status(row, 39, 1, bs, nb) == BAD_KV       # 40 positions: 5 entries, two unmapped
+    assert kv_status(row, 40, 1, bs, nb) == BAD_KV       # past the table (6 entries needed)
+    assert kv_status(np.array([3, 6]), 9, 1, bs, nb) == BAD_KV   # block 6 outside a 6-block pool
+    assert kv_status(np.array([3, 6]), 7, 1, bs, nb) == 0        # only block 3 is used

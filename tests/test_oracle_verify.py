@@ -466,3 +466,85 @@ def test_chi_square_two_tokens_million_trials():
     expected = np.outer(Pt[start], np.ones(V)) * Pt * T
     chi2, pval = chi_square_pvalue(counts, expected)
     assert pval > 1e-3, (chi2, pval)
+
+
+# --------------------------------------------------------------------------
+# the decision band (reading C18): only the first divergent decision may lie
+# within 1e-6 of its threshold
+# --------------------------------------------------------------------------
+
+def _band_case(shift, seed=3):
+    """A real request where node 0's first child is tested with its uniform set
+    at (p'(x)/q(x) + shift); returns the oracle's result there and the result
+    with the uniform moved to the other side of the threshold by the same
+    amount (what a verifier whose threshold differs by |shift| would emit)."""
+    from oracle.verify import divergence_in_band  # noqa: F401  (imported where used)
+    rng = np.random.default_rng(seed)
+    V, n = 50, 6
+    parent = np.array([-1, 0, 0, 1, 1, 2])
+    tl = rng.normal(0, 2, (n, V))
+    dl = tl + rng.normal(0, 1.0, (n, V))
+    tokens = np.array([0, 3, 7, 11, 13, 17])
+    ua = rng.uniform(size=n)
+    us = rng.uniform(size=n)
+    p0 = np.exp(tl[0] - tl[0].max()); p0 /= p0.sum()
+    q0 = np.exp(dl[0] - dl[0].max()); q0 /= q0.sum()
+    tokens[1] = int(np.argmin(np.abs(p0 / q0 - 0.5)))   # a token whose test is a fair coin flip
+    ratio = p0[tokens[1]] / q0[tokens[1]]
+    assert 0.05 < ratio < 0.95          # the test is a real coin flip, not a sure accept
+    ua_a, ua_b = ua.copy(), ua.copy()
+    ua_a[1] = ratio + shift
+    ua_b[1] = ratio - shift
+    ra = verify_stochastic_request(tl, dl, tokens, parent, n, ua_a, us)
+    rb = verify_stochastic_request(tl, dl, tokens, parent, n, ua_b, us)
+    return ra, rb
+
+
+@pytest.mark.parametrize("shift,expect", [(5e-7, True), (2e-6, False)])
+def test_band_accepts_only_near_threshold_divergence(shift, expect):
+    from oracle.verify import divergence_in_band
+    (pa, oa, ta), (pb, ob, tb) = _band_case(shift)
+    assert (pa, oa) != (pb, ob)           # the flipped test changes the walk
+    assert ta[0][0] == "accept" and ta[0][2] == 1
+    # the other result, judged against the oracle's trace on either side
+    assert divergence_in_band(ta, pa, oa, pb, ob) is expect
+    assert divergence_in_band(tb, pb, ob, pa, oa) is expect
+
+
+def test_band_equal_results_and_unexplained_differences():
+    from oracle.verify import divergence_in_band
+    (pa, oa, ta), _ = _band_case(5e-7)
+    assert divergence_in_band(ta, pa, oa, pa, oa)
+    # same walk, different final token, far from any draw boundary
+    bad = list(oa)
+    bad[-1] = (bad[-1] + 1) % 50
+    rec = ta[-1]
+    assert rec[0] == "sample"
+    far = min(abs(rec[3] - rec[4]), abs(rec[3] - rec[5])) >= 1e-6
+    assert divergence_in_band(ta, pa, oa, pa, bad) is (not far)
+    # a path that leaves the oracle's walk with a node it never tested
+    assert not divergence_in_band(ta, pa, oa, list(pa) + [5], list(oa) + [1])
+
+
+def test_band_first_divergence_decides_not_a_later_one():
+    """Hand-built trace: child 1 accepted far from its threshold, then node 1's
+    child 3 tested 5e-7 from its threshold.  A result that rejected child 1 has
+    its first divergence out of the band and must fail, although a later traced
+    decision lies inside it."""
+    from oracle.verify import divergence_in_band
+    trace = [("accept", 0, 1, 0.30, 0.90),          # accepted: 0.30 <= 0.90
+             ("accept", 1, 3, 0.5000005, 0.5),      # rejected, 5e-7 from its threshold
+             ("sample", 1, 42, 0.25, 0.20, 0.31)]
+    path, out = [0, 1], [7, 42]
+    # diverges at the second decision only: in band
+    assert divergence_in_band(trace, path, out, [0, 1, 3], [7, 9, 5])
+    # diverges at the first decision (out of band), later one in band: rejected
+    assert not divergence_in_band(trace, path, out, [0], [8])
+    # the draw: within 1e-6 of the interval's lower end, then 1e-3 away
+    trace2 = [("sample", 0, 4, 0.2000004, 0.2, 0.3)]
+    assert divergence_in_band(trace2, [0], [4], [0], [3])
+    trace3 = [("sample", 0, 4, 0.201, 0.2, 0.3)]
+    assert not divergence_in_band(trace3, [0], [4], [0], [3])
+    # a q(x) = 0 test always accepts: a result that rejected it is never explained
+    trace4 = [("accept", 0, 1, 0.9999999, float("inf")), ("sample", 1, 2, 0.5, 0.4, 0.6)]
+    assert not divergence_in_band(trace4, [0, 1], [5, 2], [0], [6])

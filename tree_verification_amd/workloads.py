@@ -288,6 +288,39 @@ def make_workload(name: str, seed: int | None = None, *, batch=None, prefix=None
                     u_accept=u_accept, u_sample=u_sample, seed=seed)
 
 
+def dominate_tree_keys(wl: Workload, seed: int, strength: float = 16.0, noise: float = 0.25) -> Workload:
+    """Rewrite the queries and the tree positions' keys so that the tree keys a
+    row may see dominate its softmax (a mask-sensitive attention input).
+
+    Per (request, KV head) a random unit direction e is drawn; every key at the
+    request's tree positions [P, P + n) and every query of the KV head's
+    q-heads become strength * e + noise * N(0, 1) (bf16-rounded for bf16
+    workloads).  Tree scores then sit near strength^2 / sqrt(D) while prefix
+    scores stay O(strength / sqrt(D)) wide, so each row's output is a weighted
+    mean of the values at its visible tree positions, and adding or dropping
+    one of them moves the row by a sizeable fraction of its norm.  In place;
+    returns wl.
+    """
+    rng = np.random.default_rng(seed)
+    D, Hkv = wl.head_dim, wl.n_kv_heads
+    G = wl.n_q_heads // Hkv
+    bs = wl.block_size
+    rnd = round_to_bf16 if wl.dtype == "bf16" else (lambda x: np.asarray(x, dtype=np.float32))
+    for b in range(wl.batch):
+        P, n = int(wl.prefix_len[b]), int(wl.n_nodes[b])
+        for g in range(Hkv):
+            e = rng.standard_normal(D)
+            e /= np.linalg.norm(e)
+            keys = strength * e[None, :] + noise * rng.standard_normal((n, D))
+            for i in range(n):
+                pos = P + i
+                blk = int(wl.block_table[b, pos // bs])
+                wl.k_cache[blk, g, pos % bs, :] = rnd(keys[i].astype(np.float32))
+            qs = strength * e[None, None, :] + noise * rng.standard_normal((wl.n_max, G, D))
+            wl.q[b, :, g * G:(g + 1) * G, :] = rnd(qs.astype(np.float32))
+    return wl
+
+
 # ---------------------------------------------------------------------------
 # token-tree construction inputs
 # ---------------------------------------------------------------------------
