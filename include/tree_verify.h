@@ -21,13 +21,13 @@
  *     bounds.
  *   - `workspace` is caller-owned device scratch of at least the size the
  *     matching *_workspace_size() returns for the call's descriptor.  The
- *     verifiers' workspaces hold exchange slots and flags whose layout depends
- *     on the descriptor: zero-fill them before their first use with a given
- *     descriptor (and again before reuse with another one); every call leaves
- *     them at zero again, so repeated calls with the same descriptor need no
- *     clearing.  The attention workspace holds only per-call partial results
- *     and needs no initialisation.  Two calls that may run concurrently must
- *     use distinct workspaces.
+ *     stochastic verifier's workspace holds exchange slots and flags whose
+ *     layout depends on the descriptor: zero-fill it before its first use with
+ *     a given descriptor (and again before reuse with another one); every call
+ *     leaves it at zero again, so repeated calls with the same descriptor need
+ *     no clearing.  The greedy verifier's and the attention's workspaces hold
+ *     only per-call results and need no initialisation.  Two calls that may
+ *     run concurrently must use distinct workspaces.
  *   - Node ids: a tree of n nodes is a parent array with parent[0] = -1 (node 0
  *     is the root: the last token already emitted) and 0 <= parent[i] < i.
  *     Rows are padded to n_max; padding rows are neither read nor written.
@@ -144,6 +144,26 @@ int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
                        const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
                        int32_t* path, int32_t* path_len, int32_t* out_tokens, int32_t* status,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* tree_verify_greedy without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Its scratch -- one 64-bit key and one flag
+ * per (node, 8192-logit chunk): 12 * B * n_max * ceil(V / 8192) bytes -- lives
+ * in a static array of tree_verify_greedy_noalloc_max_scratch() bytes (4 MiB)
+ * that every GPU the library runs on holds until the process ends; the call
+ * allocates nothing.  Descriptors needing more scratch return TV_ERR_WORKSPACE
+ * before anything is enqueued.  Arguments, results and errors otherwise as
+ * tree_verify_greedy.  Every call on one GPU shares that GPU's array: calls
+ * that may overlap on one device (different streams, or host threads) race and
+ * must be serialised by the caller.  Each call writes every scratch entry it
+ * reads, so nothing carries over from the previous call. */
+int tree_verify_greedy_noalloc(const tv_verify_desc* desc, const float* target_logits,
+                               const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
+                               int32_t* path, int32_t* path_len, int32_t* out_tokens, int32_t* status,
+                               hipStream_t stream);
+
+/* Bytes of the static scratch behind tree_verify_greedy_noalloc. */
+size_t tree_verify_greedy_noalloc_max_scratch(void);
 
 /* Stochastic verification ([guide] "Stochastic Verification Algorithm";
  * [chapter] acceptance rule min(1, p/q) and residual max(p - q, 0) / Z).

@@ -241,3 +241,19 @@ def test_budget_select_is_the_oracle_lookup(lib):
         if S > 1 and rng.random() < 0.3:
             al[1], itl[:, 1] = 2 * al[0], 2 * itl[:, 0]
         assert tv.tree_budget_select(al, itl) == select_budget(al, itl)
+
+
+def test_greedy_noalloc_rejects_oversized_scratch(lib):
+    """The static scratch holds tree_verify_greedy_noalloc_max_scratch() bytes; a
+    descriptor needing more is refused on the host with TV_ERR_WORKSPACE before
+    any HIP call (the pointers are never touched)."""
+    cap = lib.tree_verify_greedy_noalloc_max_scratch()
+    assert cap == 4 << 20
+    d = tv.VerifyDesc()
+    # 12 bytes per (node, 8192-logit chunk): 8 x 128 nodes x 512 chunks = 6 MiB
+    d.batch, d.n_max, d.vocab, d.temperature = 8, 128, 512 * 8192, 1.0
+    fake = [ctypes.c_void_p(4096 * (i + 1)) for i in range(8)]
+    rc = lib.tree_verify_greedy_noalloc(ctypes.byref(d), *fake, None)
+    assert rc == -3
+    d.batch = 0
+    assert lib.tree_verify_greedy_noalloc(ctypes.byref(d), *fake, None) == 0

@@ -72,6 +72,8 @@ _SIGS = {
     "tree_verify_workspace_size": (_SZ, [ctypes.POINTER(VerifyDesc)]),
     "tree_verify_greedy": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 9 + [_SZ, _P]),
     "tree_verify_stochastic": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 12 + [_SZ, _P]),
+    "tree_verify_greedy_noalloc": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 9),
+    "tree_verify_greedy_noalloc_max_scratch": (_SZ, []),
     "kv_compact_accepted": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 10),
     "tree_verify_stochastic_compact": (ctypes.c_int, [ctypes.POINTER(VerifyDesc), ctypes.POINTER(AttnDesc)]
                                        + [_P] * 19 + [_SZ, _P]),
@@ -257,6 +259,28 @@ def tree_verify_greedy(target_logits, tokens, parent, n_nodes, *, path=None, pat
                                 _ptr(n_nodes), _ptr(path), _ptr(path_len), _ptr(out_tokens),
                                 _ptr(status), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
     _check(rc, "tree_verify_greedy")
+    return path, path_len, out_tokens, status
+
+
+def tree_verify_greedy_noalloc(target_logits, tokens, parent, n_nodes, *, path=None, path_len=None,
+                               out_tokens=None, status=None):
+    """tree_verify_greedy without a workspace: the library's static per-device
+    scratch (tree_verify_greedy_noalloc_max_scratch() bytes) serves instead.
+    Output tensors that are not given are allocated here; pass them in to
+    allocate nothing.  Same arguments and results as tree_verify_greedy."""
+    lib = load_library()
+    dev = target_logits.device
+    B, n_max, V = target_logits.shape
+    _need(target_logits, "target_logits", torch.float32)
+    _need(tokens, "tokens", torch.int32, (B, n_max), dev)
+    _need(parent, "parent", torch.int32, (B, n_max), dev)
+    _need(n_nodes, "n_nodes", torch.int32, (B,), dev)
+    path, path_len, out_tokens, status = _verify_outputs(B, n_max, dev, path, path_len, out_tokens, status)
+    desc = verify_desc(target_logits)
+    rc = lib.tree_verify_greedy_noalloc(ctypes.byref(desc), _ptr(target_logits), _ptr(tokens), _ptr(parent),
+                                        _ptr(n_nodes), _ptr(path), _ptr(path_len), _ptr(out_tokens),
+                                        _ptr(status), _stream(dev))
+    _check(rc, "tree_verify_greedy_noalloc")
     return path, path_len, out_tokens, status
 
 

@@ -8,7 +8,7 @@
 // Greedy ([guide] "Greedy Verification Algorithm"):
 //   greedy_argmax_kernel  one workgroup per (node, 8192-logit chunk) reduces its
 //                         chunk to one 64-bit key that orders by value, then by
-//                         lower index;
+//                         lower index, and a non-finite flag;
 //   greedy_chase_kernel   one workgroup per request takes each node's largest
 //                         key, matches children against the argmaxes and walks
 //                         the root path.
@@ -50,6 +50,7 @@
 #include "tv_compact.h"
 
 #include <math.h>
+#include <mutex>
 
 namespace {
 
@@ -57,7 +58,7 @@ constexpr int kMaxNodes = 128;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 constexpr int kGreedyThreads = 256;
-constexpr int kGreedyChunk = kGreedyThreads * 32;   // 8192 logits per workgroup
+constexpr int kGreedyChunk = kGreedyThreads * 32;   // 8192 logits per (node, chunk) unit
 
 constexpr int kSThreads = 256;
 constexpr int kChunk = kSThreads * 16;              // 4096 logits per chunk
@@ -156,7 +157,7 @@ struct GreedyParams {
   int32_t* out_tokens;
   int32_t* status;
   unsigned long long* keys;   // [B][n_max][chunks] (value, index) maximum of each chunk
-  int* flags;                 // [B][n_max] non-finite logit seen
+  int* bad;                   // [B][n_max][chunks] 1 when the chunk holds NaN or +-inf
   int B, n_max, V, chunks;
 };
 
@@ -168,50 +169,83 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
   return ((unsigned long long)hi << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
+// One (node, chunk) unit's logits held by a thread: 32 values, two runs of 16
+// consecutive logits (elements lo + 16 t .. + 15 and lo + 4096 + 16 t .. + 15).
+struct GreedyUnit {
+  float x[32];
+};
+
+__device__ __forceinline__ int greedy_elem(int lo, int j) {
+  return lo + 16 * (int)threadIdx.x + (j >= 16 ? 16 * kGreedyThreads + j - 16 : j);
+}
+
+template <bool kVec>
+__device__ __forceinline__ void greedy_issue(const GreedyParams& p, int unit, GreedyUnit& u) {
+  const int c = unit % p.chunks, k = unit / p.chunks;
+  const __amdgpu_buffer_rsrc_t row = row_rsrc(p.logits + (size_t)k * p.V, p.V);
+  const int e0 = c * kGreedyChunk + 16 * (int)threadIdx.x;
+  load16<kVec>(row, e0, u.x);   // both halves issued before either is used
+  load16<kVec>(row, e0 + 16 * kGreedyThreads, u.x + 16);
+}
+
+// Reduce a unit whose loads have been issued: the chunk's largest key and
+// whether it holds a non-finite logit, written by thread 0 (`red` / `redbad`:
+// one LDS slot per wave).
+__device__ __forceinline__ void greedy_reduce(const GreedyParams& p, int unit, const GreedyUnit& x,
+                                              unsigned long long* red, int* redbad, bool live) {
+  const int c = unit % p.chunks;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int lo = c * kGreedyChunk, hi = min(p.V, lo + kGreedyChunk);
+  unsigned long long best = 0ull;
+  if (live) {
+    int bad = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int e = greedy_elem(lo, j);
+      if (e < hi) {
+        bad |= !isfinite(x.x[j]);
+        const unsigned long long kx = argmax_key(x.x[j], e);
+        best = kx > best ? kx : best;
+      }
+    }
+    best = tv_wave_max_u64(best);
+    const bool anybad = __ballot(bad != 0) != 0ull;
+    if (l == 0) {
+      red[w] = best;
+      redbad[w] = anybad ? 1 : 0;
+    }
+  }
+  tv_lds_barrier();
+  if (live && t == 0) {
+    int fl = redbad[0];
+    for (int i = 1; i < kGreedyThreads / 64; ++i) {
+      best = red[i] > best ? red[i] : best;
+      fl |= redbad[i];
+    }
+    const size_t k = (size_t)(unit / p.chunks);
+    p.keys[k * p.chunks + c] = best;
+    p.bad[k * p.chunks + c] = fl;
+  }
+}
+
+// One workgroup per (node, chunk) unit.  Units of nodes past the request's
+// size load nothing (the size is read before the row: a grid with many dead
+// units, such as a batch of short chains padded to n_max, would otherwise
+// stream their rows for nothing).  Every output slot of a live unit is written
+// on every call: the workspace carries nothing from one call to the next.
+// (A persistent grid with two units in flight per workgroup measured slower:
+// 57.7 against 48.1 us for 512 nodes x 128256 logits.)
 template <bool kVec>
 __global__ __launch_bounds__(kGreedyThreads) void greedy_argmax_kernel(GreedyParams p) {
-  const int t = threadIdx.x, l = t & 63;
-  const int c = blockIdx.x % p.chunks;
-  const int k = blockIdx.x / p.chunks;
-  const int b = k / p.n_max, u = k % p.n_max;
-  const int n = p.n_nodes[b];
-  if (n < 1 || n > p.n_max || u >= n) return;
-  const __amdgpu_buffer_rsrc_t row = row_rsrc(p.logits + (size_t)k * p.V, p.V);
-  const int lo = c * kGreedyChunk, hi = min(p.V, lo + kGreedyChunk);
-  const int e0 = lo + 16 * t, e1 = e0 + 16 * kGreedyThreads;
-  float x[16], y[16];
-  load16<kVec>(row, e0, x);   // both halves issued before either is used
-  load16<kVec>(row, e1, y);
-  unsigned long long best = 0ull;
-  int bad = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (e0 + i < hi) {
-      bad |= !isfinite(x[i]);
-      const unsigned long long kx = argmax_key(x[i], e0 + i);
-      best = kx > best ? kx : best;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (e1 + i < hi) {
-      bad |= !isfinite(y[i]);
-      const unsigned long long ky = argmax_key(y[i], e1 + i);
-      best = ky > best ? ky : best;
-    }
-  }
-  best = tv_wave_max_u64(best);
-  __shared__ unsigned long long s_best[kGreedyThreads / 64];
-  const unsigned long long anybad = __ballot(bad != 0);
-  if (l == 0) {
-    s_best[t >> 6] = best;
-    if (anybad) atomicOr(&p.flags[k], 1);
-  }
-  __syncthreads();
-  if (t == 0) {
-    for (int i = 1; i < kGreedyThreads / 64; ++i) best = s_best[i] > best ? s_best[i] : best;
-    p.keys[(size_t)k * p.chunks + c] = best;
-  }
+  __shared__ unsigned long long s_red[kGreedyThreads / 64];
+  __shared__ int s_bad[kGreedyThreads / 64];
+  const int unit = blockIdx.x;
+  const int k = unit / p.chunks;
+  const int n = p.n_nodes[k / p.n_max];
+  if (n > p.n_max || k % p.n_max >= n) return;
+  GreedyUnit x;
+  greedy_issue<kVec>(p, unit, x);
+  greedy_reduce(p, unit, x, s_red, s_bad, true);
 }
 
 __global__ __launch_bounds__(kMaxNodes) void greedy_chase_kernel(GreedyParams p) {
@@ -230,14 +264,21 @@ __global__ __launch_bounds__(kMaxNodes) void greedy_chase_kernel(GreedyParams p)
   if (t < p.n_max) {
     pv = par[t];
     tk = tok[t];
-    flg = p.flags[kv];
     const unsigned long long* kp = p.keys + kv * p.chunks;
+    const int* bp = p.bad + kv * p.chunks;
     for (int c0 = 0; c0 < p.chunks; c0 += 16) {
       unsigned long long kc[16];
+      int bc[16];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) kc[c] = c0 + c < p.chunks ? kp[c0 + c] : 0ull;
+      for (int c = 0; c < 16; ++c) {
+        kc[c] = c0 + c < p.chunks ? kp[c0 + c] : 0ull;
+        bc[c] = c0 + c < p.chunks ? bp[c0 + c] : 0;
+      }
 #pragma unroll
-      for (int c = 0; c < 16; ++c) key = kc[c] > key ? kc[c] : key;
+      for (int c = 0; c < 16; ++c) {
+        key = kc[c] > key ? kc[c] : key;
+        flg |= bc[c];
+      }
     }
   }
   const int n = p.n_nodes[b];
@@ -257,10 +298,7 @@ __global__ __launch_bounds__(kMaxNodes) void greedy_chase_kernel(GreedyParams p)
     s_arg[t] = (int)(0xFFFFFFFFu - (uint32_t)key);
     s_child[t] = 0x7fffffff;
     s_tok[t] = tk;
-    if (flg) {
-      s_nonfinite = 1;
-      p.flags[kv] = 0;
-    }
+    if (flg) s_nonfinite = 1;
     if (!((t == 0) ? (pv == -1) : (pv >= 0 && pv < t))) s_badpar = 1;
   }
   __syncthreads();
@@ -1071,7 +1109,7 @@ int check_vdesc(const tv_verify_desc* d) {
 }
 
 struct VerifyLayout {
-  size_t g_keys, g_flags, greedy_bytes;
+  size_t g_keys, g_bad, greedy_bytes;
   size_t xch, sxch, flg, acc, tok, stoch_bytes;
   int gchunks, chunks;
 };
@@ -1084,8 +1122,8 @@ VerifyLayout layout(const tv_verify_desc* d) {
   size_t o = 0;
   L.g_keys = o;
   o = tv_align_up(o + nodes * L.gchunks * sizeof(unsigned long long), 256);
-  L.g_flags = o;
-  o = tv_align_up(o + nodes * sizeof(int), 256);
+  L.g_bad = o;
+  o = tv_align_up(o + nodes * L.gchunks * sizeof(int), 256);
   L.greedy_bytes = o;
   o = 0;
   L.xch = o;
@@ -1129,19 +1167,17 @@ extern "C" size_t tree_verify_workspace_size(const tv_verify_desc* desc) {
   return L.greedy_bytes > L.stoch_bytes ? L.greedy_bytes : L.stoch_bytes;
 }
 
-extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
-                                  const int32_t* tokens, const int32_t* parent,
-                                  const int32_t* n_nodes, int32_t* path, int32_t* path_len,
-                                  int32_t* out_tokens, int32_t* status, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
-  int rc = check_vdesc(desc);
-  if (rc != TV_OK) return rc;
-  if (desc->batch == 0) return TV_OK;
-  if (!target_logits || !tokens || !parent || !n_nodes || !path || !path_len || !out_tokens || !status)
-    return TV_ERR_INVALID_ARG;
-  if (((uintptr_t)target_logits & 15) != 0) return TV_ERR_INVALID_ARG;
-  VerifyLayout L = layout(desc);
-  if (!workspace || workspace_bytes < L.greedy_bytes) return TV_ERR_WORKSPACE;
+// Scratch of tree_verify_greedy_noalloc (see below).
+constexpr size_t kNoAllocScratchBytes = 4u << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Checks the arguments of a greedy verification and launches its two kernels
+// with `ws` (at least greedy_bytes of the layout) as their scratch.
+int launch_greedy(const tv_verify_desc* desc, const float* target_logits, const int32_t* tokens,
+                  const int32_t* parent, const int32_t* n_nodes, int32_t* path, int32_t* path_len,
+                  int32_t* out_tokens, int32_t* status, char* ws, const VerifyLayout& L, hipStream_t stream) {
   GreedyParams p;
   p.logits = target_logits;
   p.tokens = tokens;
@@ -1151,8 +1187,8 @@ extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* targe
   p.path_len = path_len;
   p.out_tokens = out_tokens;
   p.status = status;
-  p.keys = (unsigned long long*)((char*)workspace + L.g_keys);
-  p.flags = (int*)((char*)workspace + L.g_flags);
+  p.keys = (unsigned long long*)(ws + L.g_keys);
+  p.bad = (int*)(ws + L.g_bad);
   p.B = desc->batch;
   p.n_max = desc->n_max;
   p.V = desc->vocab;
@@ -1166,6 +1202,77 @@ extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* targe
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   hipLaunchKernelGGL(greedy_chase_kernel, dim3((unsigned)desc->batch), dim3(kMaxNodes), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+int check_greedy_args(const tv_verify_desc* desc, const float* target_logits, const int32_t* tokens,
+                      const int32_t* parent, const int32_t* n_nodes, int32_t* path, int32_t* path_len,
+                      int32_t* out_tokens, int32_t* status) {
+  if (!target_logits || !tokens || !parent || !n_nodes || !path || !path_len || !out_tokens || !status)
+    return TV_ERR_INVALID_ARG;
+  if (((uintptr_t)target_logits & 15) != 0) return TV_ERR_INVALID_ARG;
+  return TV_OK;
+}
+
+// Scratch of tree_verify_greedy_noalloc: one static array per device (every
+// GPU the library runs on holds its own copy until the process ends), reached
+// from host code only through the device address hipGetSymbolAddress returns
+// for the current device (the array's name is a host-side stand-in).
+constexpr int kMaxDevices = 64;
+
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_rc[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per device.
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TV_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* ptr = nullptr;
+    g_scratch_rc[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch[dev] = g_scratch_rc[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_rc[dev] != hipSuccess || !g_scratch[dev]) return TV_ERR_HIP;
+  *out = g_scratch[dev];
+  return TV_OK;
+}
+
+}  // namespace
+
+extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
+                                  const int32_t* tokens, const int32_t* parent,
+                                  const int32_t* n_nodes, int32_t* path, int32_t* path_len,
+                                  int32_t* out_tokens, int32_t* status, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_vdesc(desc);
+  if (rc != TV_OK) return rc;
+  if (desc->batch == 0) return TV_OK;
+  rc = check_greedy_args(desc, target_logits, tokens, parent, n_nodes, path, path_len, out_tokens, status);
+  if (rc != TV_OK) return rc;
+  VerifyLayout L = layout(desc);
+  if (!workspace || workspace_bytes < L.greedy_bytes) return TV_ERR_WORKSPACE;
+  return launch_greedy(desc, target_logits, tokens, parent, n_nodes, path, path_len, out_tokens, status,
+                       (char*)workspace, L, stream);
+}
+
+extern "C" size_t tree_verify_greedy_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+extern "C" int tree_verify_greedy_noalloc(const tv_verify_desc* desc, const float* target_logits,
+                                          const int32_t* tokens, const int32_t* parent,
+                                          const int32_t* n_nodes, int32_t* path, int32_t* path_len,
+                                          int32_t* out_tokens, int32_t* status, hipStream_t stream) {
+  int rc = check_vdesc(desc);
+  if (rc != TV_OK) return rc;
+  if (desc->batch == 0) return TV_OK;
+  rc = check_greedy_args(desc, target_logits, tokens, parent, n_nodes, path, path_len, out_tokens, status);
+  if (rc != TV_OK) return rc;
+  VerifyLayout L = layout(desc);
+  if (L.greedy_bytes > kNoAllocScratchBytes) return TV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  rc = scratch_ptr(&ws);
+  if (rc != TV_OK) return rc;
+  return launch_greedy(desc, target_logits, tokens, parent, n_nodes, path, path_len, out_tokens, status,
+                       (char*)ws, L, stream);
 }
 
 namespace {
