@@ -75,7 +75,7 @@ def test_two_token_chi_square_million_trials():
     need = np.nonzero(x2 < 0)[0]
     tok2, tl2, dl2, ua2, us2 = draw_round(rng, LT, LQ, x1[need])
     print("round 2", len(need), flush=True)
-    plen2, outs2, st2 = gpu_rounds(tok2, tl2, dl2, ua2, us2, SHAPE)
+    plen2, outs2, st2, _ = gpu_rounds(tok2, tl2, dl2, ua2, us2, SHAPE)
     assert not st2.any()
     x2[need] = outs2[:, 0]
     counts = np.zeros((V, V))
@@ -101,7 +101,7 @@ def test_expected_tokens_per_round_on_chains(golden_dir, row):
     ua = rng.random((T, n), dtype=np.float32)
     us = rng.random((T, n), dtype=np.float32)
     parent = np.arange(-1, n - 1, dtype=np.int32)
-    plen, _, st = gpu_rounds(tok, tl, dl, ua, us, parent)
+    plen, _, st, _ = gpu_rounds(tok, tl, dl, ua, us, parent)
     assert not st.any()
     se = plen.std(ddof=1) / math.sqrt(T)
     assert abs(plen.mean() - r["E_T"]) < 5 * se + 1e-4, (r, plen.mean(), se)
