@@ -698,7 +698,7 @@ def budget_table(args, dev):
             nblk = (P + N + bs - 1) // bs
             q = torch.randn((B, N, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
             kc = torch.randn((B * nblk, Hkv, bs, D), generator=gen, device=dev).to(torch.bfloat16)
-            vc = torch.randn((B * nblk, Hkv, D, bs), generator=gen, device=dev).to(torch.bfloat16)
+            vc = torch.randn((B * nblk, Hkv, bs, D), generator=gen, device=dev).to(torch.bfloat16)
             table = torch.arange(B * nblk, dtype=torch.int32, device=dev).view(B, nblk)
             pre = torch.full((B,), P, dtype=torch.int32, device=dev)
             nn = torch.full((B,), N, dtype=torch.int32, device=dev)

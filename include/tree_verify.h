@@ -87,7 +87,7 @@ typedef struct tv_attn_desc {
 
 /* Cache layout (both caches are indexed by physical block id):
  *   k_cache [num_blocks][Hkv][block_size][D]   token-major key rows
- *   v_cache [num_blocks][Hkv][D][block_size]   value blocks stored transposed
+ *   v_cache [num_blocks][Hkv][block_size][D]   token-major value rows
  * Logical position p of request b lives in block block_table[b][p / block_size],
  * slot p % block_size.  A request's prefix occupies positions [0, P) and its
  * tree nodes positions [P, P + n) in node order ([guide] "Depth-First

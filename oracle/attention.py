@@ -22,13 +22,13 @@ from .tree import topology_mask, validate
 
 def logical_kv(k_cache, v_cache, table_row, length: int, g: int, block_size: int):
     """Contiguous K [length][D] and V [length][D] (float64) of one request and
-    KV head, rebuilt through the block table.  Key blocks are [Hkv][bs][D],
-    value blocks are stored transposed as [Hkv][D][bs]."""
+    KV head, rebuilt through the block table.  Key and value blocks are both
+    token-major, [Hkv][bs][D] (tree tokens append their rows to the cache)."""
     pos = np.arange(length)
     blk = np.asarray(table_row)[pos // block_size]
     slot = pos % block_size
     K = np.asarray(k_cache[blk, g, slot, :], dtype=np.float64)
-    V = np.asarray(v_cache[blk, g, :, slot], dtype=np.float64)
+    V = np.asarray(v_cache[blk, g, slot, :], dtype=np.float64)
     return K, V
 
 

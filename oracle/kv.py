@@ -43,7 +43,7 @@ def kv_compact(k_cache, v_cache, block_table, prefix_len, path, path_len, *, blo
                num_blocks: int, n_max: int):
     """Returns (k_new, v_new, src_pos, new_len, status) without touching the inputs.
 
-    K blocks are [Hkv][bs][D] and V blocks [Hkv][D][bs].  A request whose
+    K and V blocks are both token-major, [Hkv][bs][D].  A request whose
     path_len is 0 (verification failed) or whose path is malformed is left
     unchanged: new_len = prefix_len and src_pos = -1.
     """
@@ -68,11 +68,11 @@ def kv_compact(k_cache, v_cache, block_table, prefix_len, path, path_len, *, blo
         # read every source first, then write: a later source may sit in an
         # earlier destination slot
         k_src = [k[loc(s)[0], :, loc(s)[1], :].copy() for s in srcs]
-        v_src = [v[loc(s)[0], :, :, loc(s)[1]].copy() for s in srcs]
+        v_src = [v[loc(s)[0], :, loc(s)[1], :].copy() for s in srcs]
         for j in range(L1):
             blk, slot = loc(P + j)
             k[blk, :, slot, :] = k_src[j]
-            v[blk, :, :, slot] = v_src[j]
+            v[blk, :, slot, :] = v_src[j]
             src_pos[b, j] = srcs[j]
         new_len[b] = P + L1
     return k, v, src_pos, new_len, status

@@ -194,3 +194,68 @@ def test_padding_rows_untouched():
     o = out.float().cpu().numpy()
     for b in range(wl.batch):
         assert np.all(o[b, int(wl.n_nodes[b]):] == 7.0)
+
+
+def widen_table(wl, max_blocks):
+    """The same workload with a block table of max_blocks entries per request
+    (entries past the request's blocks are -1): a table sized for a longer
+    context than the requests use."""
+    t = np.full((wl.batch, max_blocks), -1, dtype=np.int32)
+    t[:, :wl.max_blocks] = wl.block_table
+    wl.block_table = t
+    wl.max_blocks = max_blocks
+    return wl
+
+
+@pytest.mark.parametrize("name,kw", [("llama8b", dict(prefix=2048)), ("ragged", dict(batch=5, prefix=(200, 3000)))])
+def test_attention_oversized_block_table(name, kw):
+    """A table sized for 32K tokens of context gives the same output, bit for
+    bit, as the exact-fit table: the split plan follows the requests' lengths."""
+    wl = make_workload(name, seed=21, with_logits=False, **kw)
+    print(f"case oversized table {name} {kw}", flush=True)
+    out0, st0, _, _ = run_gpu(wl)
+    widen_table(wl, 32768 // wl.block_size + 3)
+    out1, st1, _, _ = run_gpu(wl)
+    assert np.array_equal(st0, st1) and not st1.any()
+    assert np.array_equal(out0, out1)
+    check_all_rows(wl, out1, st1)
+
+
+@pytest.mark.parametrize("scale", [1e5, 1e-6])
+def test_attention_split_partials_extreme_values(scale):
+    """Values of magnitude 1e5 and 1e-6 through the split-K partials (fp16 with
+    a per-row power-of-two scale): the same tolerance as unit-scale values."""
+    from tree_verification_amd.workloads import round_to_bf16
+    wl = make_workload("llama8b", seed=23, with_logits=False, prefix=1500, n_nodes=40)
+    wl.v_cache = round_to_bf16(wl.v_cache * np.float32(scale))
+    print(f"case partial scale {scale}", flush=True)
+    out, st, _, _ = run_gpu(wl)
+    worst = check_all_rows(wl, out, st)
+    print(f"  worst (row, element) error {worst}", flush=True)
+
+
+def test_attention_ragged_balanced_plan_many_lengths():
+    """A batch planned as a whole: lengths from 1 to ~6000 keys, some requests
+    malformed (they get no split and their status), ragged row tiles."""
+    wl = make_workload("ragged", seed=27, with_logits=False, batch=12, prefix=(0, 6000), n_nodes=32)
+    wl.n_nodes[3] = 5
+    wl.n_nodes[7] = 0                         # malformed: no split planned for it
+    wl.prefix_len[9] = wl.max_blocks * wl.block_size   # past its table
+    print("case balanced plan", flush=True)
+    out, st, _, _ = run_gpu(wl)
+    ref, rst = oracle(wl)
+    assert list(st) == list(rst)
+    assert st[7] == tv.REQ_BAD_NNODES and st[9] == tv.REQ_BAD_KV
+    for b in range(wl.batch):
+        if rst[b]:
+            continue
+        n = int(wl.n_nodes[b])
+        assert max(worst_errors(out[b, :n], ref[b])) <= TOL["bf16"], b
+
+
+def test_attention_uniform_plan_bad_sizes():
+    """One request (uniform plan): malformed sizes are reported by its first workgroup."""
+    wl = make_workload("llama8b", seed=29, with_logits=False, prefix=100, n_nodes=10)
+    wl.n_nodes[0] = wl.n_max + 1
+    _, st, _, _ = run_gpu(wl)
+    assert st[0] == tv.REQ_BAD_NNODES

@@ -18,7 +18,7 @@ def test_empty_batch_every_entry_point():
     n_max, Hq, Hkv, D, bs, nblk, V = 8, 4, 2, 64, 16, 4, 1000
     q = z((0, n_max, Hq, D), torch.bfloat16)
     k = torch.randn((nblk, Hkv, bs, D), device=DEV).to(torch.bfloat16)
-    v = torch.randn((nblk, Hkv, D, bs), device=DEV).to(torch.bfloat16)
+    v = torch.randn((nblk, Hkv, bs, D), device=DEV).to(torch.bfloat16)
     table, pre, nn, par = z((0, 3)), z((0,)), z((0,)), z((0, n_max))
     out, st = tv.tree_attn_forward(q, k, v, table, pre, nn, par)
     assert out.shape == (0, n_max, Hq, D) and st.shape == (0,)

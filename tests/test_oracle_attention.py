@@ -26,14 +26,14 @@ def closure(parent, n):
 
 def scatter_paged(rng, Kl, Vl, block_size, shuffle=True, spare=3):
     """Lay logical per-request sequences Kl[b] / Vl[b] ([Hkv][L_b][D]) into a paged
-    pool: K blocks [Hkv][bs][D], V blocks [Hkv][D][bs]; returns caches + table."""
+    pool: K and V blocks [Hkv][bs][D]; returns caches + table."""
     B = len(Kl)
     Hkv, _, D = Kl[0].shape
     need = [(k.shape[1] + block_size - 1) // block_size for k in Kl]
     nb = sum(need) + spare
     ids = rng.permutation(nb) if shuffle else np.arange(nb)
     kc = rng.standard_normal((nb, Hkv, block_size, D))
-    vc = rng.standard_normal((nb, Hkv, D, block_size))
+    vc = rng.standard_normal((nb, Hkv, block_size, D))
     table = np.full((B, max(need)), -1, dtype=np.int64)
     off = 0
     for b in range(B):
@@ -42,7 +42,7 @@ def scatter_paged(rng, Kl, Vl, block_size, shuffle=True, spare=3):
         for pos in range(Kl[b].shape[1]):
             blk, slot = table[b, pos // block_size], pos % block_size
             kc[blk, :, slot, :] = Kl[b][:, pos, :]
-            vc[blk, :, :, slot] = Vl[b][:, pos, :]
+            vc[blk, :, slot, :] = Vl[b][:, pos, :]
     return kc, vc, table, nb
 
 

@@ -14,7 +14,7 @@ def paged_pool(rng, Hkv, D, lengths, bs, shuffle=True):
     nb = sum(need) + 2
     ids = rng.permutation(nb) if shuffle else np.arange(nb)
     kc = rng.standard_normal((nb, Hkv, bs, D))
-    vc = rng.standard_normal((nb, Hkv, D, bs))
+    vc = rng.standard_normal((nb, Hkv, bs, D))
     table = np.full((len(lengths), max(need)), -1, dtype=np.int64)
     off = 0
     for b, k in enumerate(need):

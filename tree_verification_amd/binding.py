@@ -178,7 +178,7 @@ def attn_desc(q, k_cache, block_table, n_kv_heads=None, sm_scale=None) -> AttnDe
 def tree_attn_forward(q, k_cache, v_cache, block_table, prefix_len, n_nodes, parent, *,
                       sm_scale=None, out=None, status=None, ws=None):
     """Tree attention (include/tree_verify.h).  Shapes:
-    q [B, n_max, Hq, D]; k_cache [num_blocks, Hkv, bs, D]; v_cache [num_blocks, Hkv, D, bs];
+    q [B, n_max, Hq, D]; k_cache and v_cache [num_blocks, Hkv, bs, D];
     block_table [B, max_blocks] int32; prefix_len, n_nodes [B] int32; parent [B, n_max] int32.
     Returns (out [B, n_max, Hq, D], status [B] int32)."""
     lib = load_library()
@@ -189,7 +189,7 @@ def tree_attn_forward(q, k_cache, v_cache, block_table, prefix_len, n_nodes, par
     _need(q, "q", q.dtype)
     _need(k_cache, "k_cache", q.dtype, device=dev)
     nb, Hkv, bs, _ = k_cache.shape
-    _need(v_cache, "v_cache", q.dtype, (nb, Hkv, D, bs), dev)
+    _need(v_cache, "v_cache", q.dtype, (nb, Hkv, bs, D), dev)
     if k_cache.shape[3] != D:
         raise ValueError("k_cache head_dim differs from q")
     _need(block_table, "block_table", torch.int32, device=dev)
@@ -321,7 +321,7 @@ def _compact_args(k_cache, v_cache, block_table, prefix_len, B, n_max, src_pos, 
         raise ValueError("caches must be float32 or bfloat16")
     nb, Hkv, bs, D = k_cache.shape
     _need(k_cache, "k_cache", k_cache.dtype)
-    _need(v_cache, "v_cache", k_cache.dtype, (nb, Hkv, D, bs), dev)
+    _need(v_cache, "v_cache", k_cache.dtype, (nb, Hkv, bs, D), dev)
     _need(block_table, "block_table", torch.int32, device=dev)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks]")

@@ -8,26 +8,35 @@
 // Decomposition.  The query rows of one (request, KV head) pair are the n*G
 // (node, head-in-group) combinations; they all share the same keys, so the
 // prefix part is a dense contraction.  A workgroup owns a tile of rows and a
-// contiguous key range (split-K over the prefix, FlashDecoding-style), one
-// workgroup per CU.  A workgroup that owns all keys of its tile writes the
-// output directly; otherwise it writes its (m, l, O) partial to the workspace
-// and attn_merge_kernel combines the splits of each row by log-sum-exp (a
-// kernel boundary orders the hand-off, so no workgroup waits on a fence).
+// contiguous range of 32-key chunks (split-K over the prefix, FlashDecoding-
+// style).  The split plan follows the requests' actual lengths, read on the
+// device: a batch whose row tiles alone leave CUs idle is planned as a whole
+// (every workgroup reads all requests' sizes and takes the same share of the
+// batch's chunk-tiles, so long requests get more splits than short ones);
+// otherwise every tile has the same number of splits and each request's own
+// length sets its keys per split.  A block table sized for a longer context
+// than the request uses costs nothing.  A workgroup that owns all keys of its
+// tile writes the output directly; otherwise it writes its (m, l, O) partial
+// to the workspace and attn_merge_kernel combines the splits of each row by
+// log-sum-exp (a kernel boundary orders the hand-off, so no workgroup waits on
+// a fence).
 //
 // MFMA path (bf16): four MFMA waves own disjoint 16*NTW-row slices of the
 // tile (rows past the request are padding) and a fifth, producer wave moves
 // 32-key chunks of K and V straight from HBM into a four-slot LDS ring with
 // global_load_lds_dwordx4, so the MFMA waves issue no memory operations while
-// they compute.  Each lane's 16 bytes land exactly where lane l of every MFMA
-// wave reads the operand it feeds to v_mfma_f32_16x16x32_bf16 (conflict-free
-// ds_read_b128):
+// they compute.  The products are
 //   S^T[key][row] = K Q^T  then  O^T[d][row] += V^T P^T,
 // laid out so that a lane always owns one query row (lane % 16): the softmax
 // state is lane-local, and the C layout of S^T feeds the B operand of the PV
-// product without cross-lane moves.  Values are stored transposed per block
-// ([D][block] per head) so the PV operand (8 consecutive keys of one d) is a
-// single 16-byte piece.  The running max moves only when a row's max grows by
-// more than 8 (log2 units), which keeps most chunks free of rescaling.
+// product without cross-lane moves.  Key bytes land exactly where lane l of
+// every MFMA wave reads the K operand of v_mfma_f32_16x16x32_bf16 (ds_read_b128).
+// Values are token-major in the cache and in LDS; the V^T operand (8
+// consecutive keys of one d per lane) comes from two ds_read_b64_tr_b16 reads,
+// the LDS transpose load of gfx950, over rows whose 16-byte pieces the DMA
+// stores XOR-swizzled so that those reads are free of bank conflicts.  The
+// running max moves only when a row's max grows by more than 8 (log2 units),
+// which keeps most chunks free of rescaling.
 //
 // VALU path (fp32): the waves interleave 64-key chunks with lane = key for the
 // scores and lane = d for PV, merged in LDS.
@@ -47,8 +56,8 @@ constexpr int kThreads = 256;        // VALU path (fp32): four waves
 constexpr int kMfmaWaves = 4;        // MFMA path: four waves own the rows ...
 constexpr int kMfmaThreads = 64 * (kMfmaWaves + 1);   // ... and a fifth moves the K/V chunks
 constexpr int kMaxNodes = 128;
-constexpr int kMaxSplits = 32;        // key splits per (request, KV head, row tile)
 constexpr int kMaxKeysPerSplit = 32768;   // NTW = 1 (two workgroups per CU); twice that for NTW = 2
+constexpr int kMinSplitChunks = 4;        // a split owns at least 128 keys (or the whole request)
 constexpr int kStages = 4;            // LDS ring slots (chunks in flight) on the MFMA path
 // Keys one split may own, and the block-table entries a workgroup stages for
 // them (block size 16 at least).
@@ -69,17 +78,223 @@ struct AttnParams {
   const int32_t* parent;
   void* out;
   int32_t* status;
-  void* part_o;     // [tiles][splits][rows_per_tile][D] O / l of each split (PartT<kBF16>)
-  float* part_ml;   // [tiles][splits][rows_per_tile][2]
+  void* part_o;     // [slots][rows_per_tile][D] O / l of each split times a power of two (fp16 or fp32)
+  float4* part_ml;  // [slots][rows_per_tile] (m, l, the power of two's inverse, 0)
   int B, n_max, Hq, Hkv, G, D, bs, lbs, max_blocks, num_blocks;
   float scale_log2;
-  int rows_per_tile, row_tiles, splits, keys_per_split, total;
+  int rows_per_tile, row_tiles;   // row tiles of one (request, KV head) at n_max nodes
+  int balanced;     // 1: the batch is planned as a whole from its lengths; 0: `splits` per tile
+  int splits;       // uniform plan: key splits per tile
+  int nwg;          // balanced plan: workgroups it aims at
+  int max_kps_ch;   // most 32-key chunks one split may own (the staged block table's reach)
+  int grid;         // attention workgroups launched
 };
 
 struct AttnPlan {
-  int rows_per_tile, row_tiles, splits, keys_per_split, ntw;
+  int rows_per_tile, row_tiles, ntw, balanced, splits, nwg, max_kps_ch, grid, slots;
   size_t off_ml, bytes;
 };
+
+// ---------------------------------------------------------------------------
+// split plan (computed on the device from the requests' sizes)
+// ---------------------------------------------------------------------------
+
+// Work shape of one request: row tiles in use and 32-key chunks of its P + n
+// keys (both 0 when its sizes are malformed: such a request gets no split).
+struct ReqShape {
+  int P, n, rt, ch;
+};
+
+__device__ __forceinline__ ReqShape req_shape(const AttnParams& p, int P, int n) {
+  ReqShape r;
+  r.P = P;
+  r.n = n;
+  const bool ok = n >= 1 && n <= p.n_max && P >= 0 && (long long)P + n <= (long long)p.max_blocks * p.bs;
+  r.rt = ok ? (n * p.G + p.rows_per_tile - 1) / p.rows_per_tile : 0;
+  r.ch = ok ? (P + n + 31) / 32 : 0;
+  return r;
+}
+
+// Status of a request whose sizes are malformed (0 otherwise).
+__device__ __forceinline__ int shape_status(const AttnParams& p, int P, int n) {
+  if (n < 1 || n > p.n_max) return TV_REQ_BAD_NNODES;
+  if (P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) return TV_REQ_BAD_KV;
+  return 0;
+}
+
+// Chunks per split of a request under the uniform plan.
+__device__ __forceinline__ int uniform_kps(const AttnParams& p, int ch) {
+  int k = (ch + p.splits - 1) / p.splits;
+  k = max(k, kMinSplitChunks);
+  return min(k, p.max_kps_ch);
+}
+
+// Wave-wide int32 sum and inclusive prefix sum over lanes (DPP and lane
+// permutes, no LDS traffic).
+__device__ __forceinline__ int wave_sum_i(int v) {
+  return (int)tv_wave_reduce_u32((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
+  x += (int)tv_dpp<0x111>((uint32_t)x);   // row_shr:1 (lanes shifted in from outside the row read 0)
+  x += (int)tv_dpp<0x112>((uint32_t)x);   // row_shr:2
+  x += (int)tv_dpp<0x114>((uint32_t)x);   // row_shr:4
+  x += (int)tv_dpp<0x118>((uint32_t)x);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
+}
+
+// Sum over the batch of f(shape of request b) (each wave computes it; lane =
+// request, 64 requests per step).  `mine` is the lane's request shape of the
+// first step, loaded once by the caller (batches of at most 64 requests then
+// need no further loads).
+template <class F>
+__device__ __forceinline__ int batch_sum(const AttnParams& p, int lane, const ReqShape& mine, F f) {
+  int acc = wave_sum_i(lane < p.B ? f(mine) : 0);
+  for (int b0 = 64; b0 < p.B; b0 += 64) {
+    const int b = b0 + lane;
+    acc += wave_sum_i(b < p.B ? f(req_shape(p, p.prefix_len[b], p.n_nodes[b])) : 0);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ ReqShape lane_shape(const AttnParams& p, int lane) {
+  if (lane < p.B) return req_shape(p, p.prefix_len[lane], p.n_nodes[lane]);
+  return ReqShape{0, 0, 0, 0};
+}
+
+// The balanced plan's chunks per split: the smallest kps for which the
+// batch's splits (every tile's ceil(ch / kps)) fit p.nwg workgroups, at least
+// kMinSplitChunks and at most p.max_kps_ch.  With W chunk-tiles over T tiles,
+// kps >= W / nwg is necessary and kps >= W / (nwg - T) sufficient; a binary
+// search over that range, each step one wave-wide sum over the batch.
+__device__ int balanced_kps(const AttnParams& p, int lane, const ReqShape& mine) {
+  const int W = batch_sum(p, lane, mine, [&](ReqShape r) { return p.Hkv * r.rt * r.ch; });
+  const int T = batch_sum(p, lane, mine, [&](ReqShape r) { return p.Hkv * r.rt; });
+  const int cap = p.max_kps_ch;
+  int lo = (W + p.nwg - 1) / p.nwg;
+  int hi = T < p.nwg ? (W + (p.nwg - T) - 1) / (p.nwg - T) : cap;
+  lo = min(max(lo, kMinSplitChunks), cap);
+  hi = min(max(hi, lo), cap);
+  while (lo < hi) {
+    const int mid = (lo + hi) / 2;
+    const int total = batch_sum(p, lane, mine, [&](ReqShape r) { return p.Hkv * r.rt * ((r.ch + mid - 1) / mid); });
+    if (total <= p.nwg) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// One workgroup's share of the plan.
+struct SplitPlan {
+  int b, g, rt, s;    // request, KV head, row tile, split
+  int P, n;           // the request's sizes
+  int rt_b;           // row tiles the request uses
+  int splits;         // splits of each of its tiles
+  int kps_ch;         // chunks per split
+  int slot;           // partial slot of this split (its logical workgroup id)
+  bool work;          // this workgroup owns a (tile, split)
+  bool shape_ok;      // the request's sizes are well formed
+};
+
+// Logical workgroup -> (request, KV head, row tile, split).  Splits of one
+// tile are consecutive logical ids, tiles of one request consecutive runs, and
+// logical ids are numbered XCD-aware (tv_xcd_remap), so a tile's splits and
+// the row tiles sharing its K/V run on one XCD.
+__device__ SplitPlan plan_split(const AttnParams& p, int phys) {
+  const int lane = threadIdx.x & 63;
+  SplitPlan sp;
+  sp.b = sp.g = sp.rt = sp.s = sp.P = sp.n = sp.rt_b = sp.splits = sp.kps_ch = sp.slot = 0;
+  sp.work = false;
+  sp.shape_ok = false;
+  if (!p.balanced) {
+    const int w = tv_xcd_remap(phys, p.grid);
+    const int per_req = p.Hkv * p.row_tiles * p.splits;
+    sp.b = w / per_req;
+    int idx = w % per_req;
+    sp.g = idx / (p.row_tiles * p.splits);
+    idx %= p.row_tiles * p.splits;
+    sp.rt = idx / p.splits;
+    sp.s = idx % p.splits;
+    sp.P = p.prefix_len[sp.b];
+    sp.n = p.n_nodes[sp.b];
+    const ReqShape r = req_shape(p, sp.P, sp.n);
+    sp.shape_ok = r.rt > 0;
+    sp.rt_b = r.rt;
+    sp.kps_ch = uniform_kps(p, r.ch);
+    sp.splits = r.ch > 0 ? (r.ch + sp.kps_ch - 1) / sp.kps_ch : 0;
+    sp.slot = w;
+    sp.work = sp.shape_ok && sp.rt < r.rt && sp.s < sp.splits;
+    return sp;
+  }
+  // balanced: every wave walks the batch (sizes are L1/L2 hits after the first)
+  const ReqShape mine = lane_shape(p, lane);
+  const int kps = balanced_kps(p, lane, mine);
+  const int total = batch_sum(p, lane, mine, [&](ReqShape r) { return p.Hkv * r.rt * ((r.ch + kps - 1) / kps); });
+  sp.kps_ch = kps;
+  if (phys >= total) return sp;
+  const int w = tv_xcd_remap(phys, total);
+  int base = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int b = b0 + lane;
+    const ReqShape r = b0 == 0 ? mine : (b < p.B ? req_shape(p, p.prefix_len[b], p.n_nodes[b]) : ReqShape{0, 0, 0, 0});
+    const int spl = (r.ch + kps - 1) / kps;
+    const int cnt = b < p.B ? p.Hkv * r.rt * spl : 0;
+    const int incl = wave_incl_scan_i(cnt, lane);
+    const bool hit_lane = w >= base + incl - cnt && w < base + incl;
+    const unsigned long long hit = __ballot(hit_lane);
+    if (hit) {
+      const int src = __ffsll((long long)hit) - 1;
+      sp.b = b0 + src;
+      sp.P = __shfl(r.P, src);
+      sp.n = __shfl(r.n, src);
+      sp.rt_b = __shfl(r.rt, src);
+      sp.splits = __shfl(spl, src);
+      int idx = w - (base + __shfl(incl - cnt, src));
+      sp.g = idx / (sp.rt_b * sp.splits);
+      idx %= sp.rt_b * sp.splits;
+      sp.rt = idx / sp.splits;
+      sp.s = idx % sp.splits;
+      sp.slot = w;
+      sp.shape_ok = true;
+      sp.work = true;
+      return sp;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  return sp;
+}
+
+// Partial slots of tile (b, g, rt) for the merge: first slot and split count
+// (0 when the tile does not exist or its request's sizes are malformed).
+__device__ int2 tile_slots(const AttnParams& p, int b, int g, int rt) {
+  const int lane = threadIdx.x & 63;
+  if (!p.balanced) {
+    const ReqShape r = req_shape(p, p.prefix_len[b], p.n_nodes[b]);
+    if (rt >= r.rt) return make_int2(0, 0);
+    const int kps = uniform_kps(p, r.ch);
+    return make_int2(((b * p.Hkv + g) * p.row_tiles + rt) * p.splits, (r.ch + kps - 1) / kps);
+  }
+  const ReqShape mine = lane_shape(p, lane);
+  const int kps = balanced_kps(p, lane, mine);
+  // slots of the requests before b
+  int start = 0;
+  for (int b0 = 0; b0 < b; b0 += 64) {
+    const int bb = b0 + lane;
+    int v = 0;
+    if (bb < b) {
+      const ReqShape r = b0 == 0 ? mine : req_shape(p, p.prefix_len[bb], p.n_nodes[bb]);
+      v = p.Hkv * r.rt * ((r.ch + kps - 1) / kps);
+    }
+    start += wave_sum_i(v);
+  }
+  const ReqShape r = req_shape(p, p.prefix_len[b], p.n_nodes[b]);
+  if (rt >= r.rt) return make_int2(0, 0);
+  const int s_b = (r.ch + kps - 1) / kps;
+  return make_int2(start + (g * r.rt + rt) * s_b, s_b);
+}
 
 template <int D>
 struct Chunk {
@@ -87,7 +302,6 @@ struct Chunk {
   static constexpr int DT = D / 16;            // 16-wide d tiles of the PV product
   static constexpr int NBLK = 2 * KK + DT;     // 1 KB operand blocks per 32-key chunk
   static constexpr int BYTES = NBLK * 1024;
-  static constexpr int PER_WAVE = NBLK / 4;    // DMA instructions each wave issues per chunk
 };
 
 // ---------------------------------------------------------------------------
@@ -211,6 +425,11 @@ __device__ __forceinline__ void load8(const void* base, size_t off, float* dst) 
   }
 }
 
+template <bool kBF16>
+__device__ __forceinline__ float val_at(const void* base, size_t off) {
+  return kBF16 ? tv_bf16_bits_to_f32(((const uint16_t*)base)[off]) : ((const float*)base)[off];
+}
+
 template <bool kBF16, int D, int RV>
 __device__ void attn_valu_rows(const AttnParams& p, ValuSmem<D>& sm, int b, int g, int r0, int rows,
                                int P, int k_begin, int k_end, bool tree_in_range, const uint64_t (*anc)[2]) {
@@ -271,7 +490,8 @@ __device__ void attn_valu_rows(const AttnParams& p, ValuSmem<D>& sm, int b, int 
       m_r[r] = m_new;
       ps[r * 64 + lane] = pv;
     }
-    // PV: lane = d (values are stored as [d][slot])
+    // PV: lane = d; value rows are token-major, so each key's row is one
+    // coalesced read across the wave (8 keys at a time, all inside one block)
 #pragma unroll
     for (int r = 0; r < RV; ++r) {
 #pragma unroll
@@ -284,13 +504,12 @@ __device__ void attn_valu_rows(const AttnParams& p, ValuSmem<D>& sm, int b, int 
       const int vb = trow[kk >> p.lbs];
       if (!block_ok(vb, p.num_blocks)) continue;
       float vv[DJ][8];
+      const size_t row0 = ((size_t)vb * p.Hkv + g) * p.bs + (kk & (p.bs - 1));
 #pragma unroll
-      for (int j = 0; j < DJ; ++j) {
-        size_t off = ((((size_t)vb * p.Hkv + g) * D + lane + 64 * j) << p.lbs) + (kk & (p.bs - 1));
-        load8<kBF16>(p.v, off, vv[j]);
+      for (int e = 0; e < 8; ++e) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (kk + e >= k_end) vv[j][e] = 0.f;   // slots past the request hold no data
+        for (int j = 0; j < DJ; ++j)   // slots past the request hold no data
+          vv[j][e] = kk + e < k_end ? val_at<kBF16>(p.v, (row0 + e) * D + lane + 64 * j) : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < RV; ++r) {
@@ -370,11 +589,21 @@ __device__ void attn_valu(const AttnParams& p, ValuSmem<D>& sm, int b, int g, in
 // output and split-K merge
 // ---------------------------------------------------------------------------
 
-// Split partials hold the split's normalised output O / l (|O / l| <= max |v|)
-// beside its (m, l).  For bf16 inputs they are stored as fp16 (relative
-// rounding 2^-11, far inside the bf16 output's own rounding), which halves the
-// bytes written and re-read; fp32 inputs keep fp32.
+// Split partials hold the split's normalised output O / l (|O / l| <= max |v|:
+// a convex combination of value rows) beside its (m, l).  For bf16 inputs they
+// are stored as fp16 after multiplying each row by a power of two that brings
+// its largest magnitude into [2^14, 2^15): every element then keeps fp16's 11
+// significant bits relative to the row's largest one (no overflow for large
+// values, no loss to subnormals for small ones), and the merge multiplies by
+// the inverse, kept in the row's (m, l) record.  fp32 inputs keep fp32 (scale 1).
 typedef _Float16 tv_f16x4 __attribute__((ext_vector_type(4)));
+
+// Power of two for a row whose largest |O / l| is amax, and its inverse.
+__device__ __forceinline__ float2 part_scale(float amax) {
+  int e = __builtin_amdgcn_frexp_expf(amax);   // amax < 2^e (0 for amax = 0)
+  e = max(e, -100);                            // keeps both factors normal floats
+  return make_float2(ldexpf(1.f, 15 - e), ldexpf(1.f, e - 15));
+}
 
 template <bool kBF16>
 __device__ __forceinline__ void store_part4(void* part_o, size_t off, tv_f32x4 v) {
@@ -404,9 +633,11 @@ __device__ __forceinline__ void store_out4(const AttnParams& p, int b, int g, in
 // Split-K merge, a second kernel: for every tile whose request used more than
 // one key split, combine the splits' (m, l, O/l) partials by log-sum-exp and
 // write the output rows.  The kernel boundary makes the partials visible (no
-// inter-workgroup fences or counters).  A thread owns 8 d values of one row
-// and walks the splits in batches whose loads are in flight together,
-// rescaling its running sum when a batch raises the row's max.
+// inter-workgroup fences or counters).  Each merge workgroup recomputes the
+// split plan (the same integer arithmetic as the attention grid) to find its
+// tile's partial slots.  A thread owns 8 d values of one row and walks the
+// splits in batches whose loads are in flight together, rescaling its running
+// sum when a batch raises the row's max.
 constexpr int kMergeThreads = 128;
 constexpr int kMergeVec = 8;     // d values per thread
 constexpr int kMergeBatch = 8;   // splits loaded together
@@ -436,38 +667,25 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p)
   const int bg = tile / p.row_tiles, rt = tile % p.row_tiles;
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int r = rg * RPB + t / TPR, d = kMergeVec * (t % TPR);   // row within the tile, first d
-  const bool in_tile = r < p.rows_per_tile;
-  const size_t base = (size_t)tile * p.splits * p.rows_per_tile + r;
-  // the first batch of partials goes out with the sizes (always inside the workspace)
+  const int2 sl = tile_slots(p, b, g, rt);
+  const int n_active = sl.y;
+  if (n_active < 2) return;                 // no tile, or written directly by the attention kernel
   const int n = p.n_nodes[b];
-  const int P = p.prefix_len[b];
-  float2 ml[kMergeBatch];
-  float o[kMergeBatch][kMergeVec];
-#pragma unroll
-  for (int s = 0; s < kMergeBatch; ++s) {
-    if (s < p.splits && in_tile) {
-      const size_t pr = base + (size_t)s * p.rows_per_tile;
-      ml[s] = *(const float2*)&p.part_ml[pr * 2];
-      load_part8<kBF16>(p.part_o, pr * D + d, o[s]);
-    }
-  }
-  if (n < 1 || n > p.n_max || P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) return;
-  const int n_active = (P + n + p.keys_per_split - 1) / p.keys_per_split;
-  if (n_active < 2) return;                 // written directly by the attention kernel
   const int row = rt * p.rows_per_tile + r;
-  if (!in_tile || row >= n * p.G) return;
+  if (r >= p.rows_per_tile || row >= n * p.G) return;
+  const size_t base = (size_t)sl.x * p.rows_per_tile + r;
+  float4 ml[kMergeBatch];
+  float o[kMergeBatch][kMergeVec];
   float M = kNegInf, L = 0.f, acc[kMergeVec];
 #pragma unroll
   for (int i = 0; i < kMergeVec; ++i) acc[i] = 0.f;
   for (int s0 = 0; s0 < n_active; s0 += kMergeBatch) {
-    if (s0 > 0) {
 #pragma unroll
-      for (int s = 0; s < kMergeBatch; ++s) {
-        if (s0 + s < n_active) {
-          const size_t pr = base + (size_t)(s0 + s) * p.rows_per_tile;
-          ml[s] = *(const float2*)&p.part_ml[pr * 2];
-          load_part8<kBF16>(p.part_o, pr * D + d, o[s]);
-        }
+    for (int s = 0; s < kMergeBatch; ++s) {
+      if (s0 + s < n_active) {
+        const size_t pr = base + (size_t)(s0 + s) * p.rows_per_tile;
+        ml[s] = p.part_ml[pr];
+        load_part8<kBF16>(p.part_o, pr * D + d, o[s]);
       }
     }
     float mb = kNegInf;
@@ -486,8 +704,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p)
       if (s0 + s < n_active && ml[s].x != kNegInf) {
         const float w = __builtin_amdgcn_exp2f(ml[s].x - M) * ml[s].y;
         L += w;
+        const float wo = w * ml[s].z;   // the stored row is O / l times 1 / ml.z
 #pragma unroll
-        for (int i = 0; i < kMergeVec; ++i) acc[i] += w * o[s][i];
+        for (int i = 0; i < kMergeVec; ++i) acc[i] += wo * o[s][i];
       }
     }
   }
@@ -500,7 +719,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p)
 
 // VALU path output: rows [r0, r0 + rows) are in LDS.
 template <bool kBF16, int D, int RW>
-__device__ void emit_valu(const AttnParams& p, CommonSmem& cm, ValuSmem<D>& sm, int tile, int split, int n_active,
+__device__ void emit_valu(const AttnParams& p, CommonSmem& cm, ValuSmem<D>& sm, int slot, int n_active,
                           int b, int g, int r0, int rows) {
   const int t = threadIdx.x;
   if (n_active == 1) {
@@ -512,17 +731,14 @@ __device__ void emit_valu(const AttnParams& p, CommonSmem& cm, ValuSmem<D>& sm, 
     }
     return;
   }
-  const size_t prow = ((size_t)tile * p.splits + split) * RW;
+  const size_t prow = (size_t)slot * RW;
   for (int idx = t; idx < rows * (D / 4); idx += kThreads) {
     int r = idx / (D / 4), d = 4 * (idx % (D / 4));
     const float inv = sm.l[r] > 0.f ? 1.f / sm.l[r] : 0.f;
     store_part4<kBF16>(p.part_o, (prow + r) * D + d,
                        (tv_f32x4){sm.o[r][d] * inv, sm.o[r][d + 1] * inv, sm.o[r][d + 2] * inv, sm.o[r][d + 3] * inv});
   }
-  if (t < rows) {
-    p.part_ml[(prow + t) * 2] = sm.m[t];
-    p.part_ml[(prow + t) * 2 + 1] = sm.l[t];
-  }
+  if (t < rows) p.part_ml[prow + t] = make_float4(sm.m[t], sm.l[t], 1.f, 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -544,32 +760,42 @@ __device__ __forceinline__ void wait_vmcnt() {
 typedef __attribute__((address_space(3))) void* tv_lds_ptr;
 
 // One 32-key chunk, sent straight from HBM into its LDS slot by the producer
-// wave with global_load_lds_dwordx4: operand block j (1 KB) gets lane l's 16
-// bytes at slot + 1024*j + 16*l, the bytes lane l of every MFMA wave later
-// feeds to v_mfma.  A chunk starts at a multiple of 32 keys, so it spans at
-// most two blocks (A and B; only when the block size is 16): its addresses are
-// two wave-uniform row bases plus per-lane offsets fixed for the whole split.
-// Keys at or past k_end read whatever their (in-pool) block holds and are
-// masked at use.
+// wave with global_load_lds_dwordx4 (lane l's 16 bytes land at 16*l of the
+// instruction's 1 KB).  A chunk starts at a multiple of 32 keys, so it spans
+// at most two blocks (only with 16-token blocks: keys 0..15 then 16..31 of the
+// chunk).  Each instruction reads from one of the chunk's two halves, whose
+// base addresses are wave-uniform (a 64-bit scalar base plus a per-lane 32-bit
+// offset fixed for the whole split); keys at or past k_end read whatever their
+// (in-pool) block holds and are masked at use.
+//   Keys: instruction (tt, kk) holds, at lane l, key 16*tt + l%16 of the chunk
+// and d values 8*(l/16) + 32*kk .. + 7: the K operand lane l of every MFMA
+// wave feeds to v_mfma_f32_16x16x32_bf16 for the keys of half tt
+// (conflict-free ds_read_b128).
+//   Values: 32 token-major rows of 2*D bytes.  Instruction j fills rows R*j ..
+// R*j + R - 1 (R = 512 / D rows per KB); in row `key` the 16-byte piece of d
+// values 8p .. 8p+7 sits at piece slot p ^ vswz<D>(key), an XOR swizzle that
+// puts the pieces one ds_read_b64_tr_b16 reads (four keys x 16 d values per
+// group of 16 lanes, eight consecutive keys per half-wave) on distinct banks.
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  return D == 128 ? 2 * (key & 7) : 2 * ((key >> 1) & 3);
+}
+
 struct DmaLane {
-  uint32_t koff[2];   // key block (tt, kk = 0): byte offset of this lane's 8 d values from the row base
-  uint32_t voff;      // value block dt = 0: byte offset of this lane's 8 keys
-  bool kb, vb;        // the lane's key / value bytes come from the chunk's second block
+  uint32_t koff;      // key instructions: this lane's row and d piece within a half
+  uint32_t voff[2];   // value instruction j: this lane's row and swizzled piece, by j & 1
 };
 
 template <int D>
-__device__ __forceinline__ DmaLane dma_lane(int bs, int lane) {
+__device__ __forceinline__ DmaLane dma_lane(int lane) {
   const int l16 = lane & 15, h4 = lane >> 4;
-  const int wrap = (bs < 32 ? bs : 32) - 1;   // in-block position of a key offset within the chunk
   DmaLane dl;
+  dl.koff = (uint32_t)(l16 * D * 2 + 16 * h4);
+  constexpr int R = 512 / D, PPR = D / 8;   // value rows per instruction, 16-byte pieces per row
+  const int r = lane / PPR, s = lane % PPR;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {   // key row 8*(l16/4) + 4*tt + l16%4 of the chunk, d = 8*h4 + 32*kk
-    const int koff = 8 * (l16 >> 2) + 4 * tt + (l16 & 3);
-    dl.koff[tt] = (uint32_t)(((koff & wrap) * D + 8 * h4) * 2);
-  }
-  dl.kb = 8 * (l16 >> 2) >= bs;
-  dl.voff = (uint32_t)((l16 * bs + ((8 * h4) & wrap)) * 2);   // value row d = l16 + 16*dt, keys 8*h4 ..
-  dl.vb = 8 * h4 >= bs;
+  for (int x = 0; x < 2; ++x)   // row R*j + r of the chunk; the swizzle depends on j only through j & 1
+    dl.voff[x] = (uint32_t)(r * D * 2 + 16 * (s ^ vswz<D>(R * x + r)));
   return dl;
 }
 
@@ -581,25 +807,58 @@ __device__ __forceinline__ int2 chunk_rows(const int* tab, int tab0, int ntab, i
   return make_int2(__builtin_amdgcn_readfirstlane(tab[ia]), __builtin_amdgcn_readfirstlane(tab[ib]));
 }
 
+__device__ __forceinline__ tv_lds_ptr lds_at(uint32_t addr) { return (tv_lds_ptr)(uintptr_t)addr; }
+
+// LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) { return (uint32_t)(uintptr_t)(tv_lds_ptr)ptr; }
+
 template <int D>
 __device__ __forceinline__ void dma_chunk(const AttnParams& p, const DmaLane& dl, int2 rows, int key0,
-                                          unsigned char* slot) {
-  constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT;
+                                          uint32_t slot) {
+  constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT, R = 512 / D;
   const size_t row_bytes = (size_t)p.bs * D * 2;   // one (block, KV head) row, K and V alike
   const size_t kin = (size_t)(key0 & (p.bs - 1));  // the chunk's first in-block position
-  const size_t ra = (size_t)(uint32_t)rows.x * row_bytes, rb = (size_t)(uint32_t)rows.y * row_bytes;
-  const char* kbase = (const char*)p.k + (dl.kb ? rb : ra) + kin * D * 2;
-  const char* vbase = (const char*)p.v + (dl.vb ? rb : ra) + kin * 2;
+  // byte offsets of the chunk's two halves (keys 0..15 and 16..31)
+  const size_t h0 = (size_t)(uint32_t)rows.x * row_bytes + kin * D * 2;
+  const size_t h1 = p.bs == 16 ? (size_t)(uint32_t)rows.y * row_bytes : h0 + 16 * D * 2;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int tt = 0; tt < 2; ++tt) {
+    const char* kb = (const char*)p.k + (tt ? h1 : h0);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + dl.koff[tt] + 64 * kk),
-                                       (tv_lds_ptr)(slot + (tt * KK + kk) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(kb + dl.koff + 64 * kk), lds_at(slot + (tt * KK + kk) * 1024),
+                                       16, 0, 0);
+  }
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    __builtin_amdgcn_global_load_lds((const void*)(vbase + dl.voff + (size_t)dt * 32 * p.bs),
-                                     (tv_lds_ptr)(slot + (2 * KK + dt) * 1024), 16, 0, 0);
+  for (int j = 0; j < DT; ++j) {
+    const int row0 = R * j;   // the instruction's first row of the chunk
+    const char* vb = (const char*)p.v + (row0 >= 16 ? h1 : h0);
+    __builtin_amdgcn_global_load_lds((const void*)(vb + dl.voff[j & 1] + (row0 & 15) * D * 2),
+                                     lds_at(slot + (2 * KK + j) * 1024), 16, 0, 0);
+  }
+}
+
+typedef __bf16 tv_bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) tv_bf16x4* tv_lds_bf16x4_ptr;
+
+// V^T operand of d tile dt for v_mfma_f32_16x16x32_bf16.  The PV product
+// contracts over the chunk's keys in the order the score tiles hold them: lane
+// l's eight k entries are keys 4*(l/16) + 0..3 (score tile 0) and 16 + 4*(l/16)
+// + 0..3 (score tile 1), so lane l needs V[those keys][d = 16*dt + l%16], as two
+// transposed reads of four keys.  In each group of 16 lanes,
+// ds_read_b64_tr_b16 hands lane j element j%4 of the 8 bytes lane 4*k + j/4
+// addressed, as its element k; so lane i of group h addresses the four d
+// values 16*dt + 4*(i%4) .. + 3 of key 16*e + 4*h + i/4 (one 8-byte half of a
+// swizzled 16-byte piece).
+template <int D>
+__device__ __forceinline__ tv_bf16x8 lds_vop(const unsigned char* vreg, int dt, int lane) {
+  const int h = lane >> 4, i = lane & 15;
+  const int key0 = 4 * h + (i >> 2);
+  const int f = vswz<D>(key0);   // the same for key0 + 16
+  const unsigned char* a0 = vreg + key0 * 2 * D + 16 * ((2 * dt + ((i & 3) >> 1)) ^ f) + 8 * (i & 1);
+  const tv_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((tv_lds_bf16x4_ptr)a0);
+  const tv_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((tv_lds_bf16x4_ptr)(a0 + 16 * 2 * D));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Running softmax state and output accumulators of one wave (16*NTW rows).
@@ -623,7 +882,7 @@ __device__ __forceinline__ void mfma_chunk(const unsigned char* slot, const tv_b
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = lds_bf16x8(slot + (tt * KK + kk) * 1024 + lane * 16);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) vop[dt] = lds_bf16x8(slot + (2 * KK + dt) * 1024 + lane * 16);
+  for (int dt = 0; dt < DT; ++dt) vop[dt] = lds_vop<D>(slot + 2 * KK * 1024, dt, lane);
 
   // phase 1: scores of every row tile (independent MFMA chains)
   tv_f32x4 sc[NTW][2];
@@ -639,16 +898,16 @@ __device__ __forceinline__ void mfma_chunk(const unsigned char* slot, const tv_b
   }
   // The request's last chunk: value slots at or past k_end hold no data (zero
   // them so that 0 * garbage cannot reach the sum).  Lane l holds keys
-  // key0 + 8*(l/16) + e of value row d.
+  // key0 + 4*(l/16) + e (e < 4) and key0 + 16 + 4*(l/16) + e - 4 (e >= 4).
   const bool plain = key0 + 32 <= P && key0 + 32 <= k_end;   // prefix keys only: no mask
   if (key0 + 32 > k_end) {
-    const int kv = key0 + 8 * h4;
+    const int kv = key0 + 4 * h4;   // element e: key kv + e (e < 4) or kv + 12 + e (e >= 4)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       tv_u32x4 w = __builtin_bit_cast(tv_u32x4, vop[dt]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (kv + e >= k_end) {
+        if (kv + (e < 4 ? e : 12 + e) >= k_end) {
           if (e & 1) w[e >> 1] &= 0x0000FFFFu;
           else w[e >> 1] &= 0xFFFF0000u;
         }
@@ -656,7 +915,7 @@ __device__ __forceinline__ void mfma_chunk(const unsigned char* slot, const tv_b
       vop[dt] = __builtin_bit_cast(tv_bf16x8, w);
     }
   }
-  // phase 2: mask, online softmax.  Lane l holds keys key0 + 8*(l/16) + 4*tt + i
+  // phase 2: mask, online softmax.  Lane l holds keys key0 + 16*tt + 4*(l/16) + i
   // of query row l % 16.  The max is taken over the raw scores (the scale is
   // positive) and the scale is folded into the exponent's FMA.  The running max
   // only moves when a row's max grows by more than kLazy (log2 units), so the
@@ -672,7 +931,7 @@ __device__ __forceinline__ void mfma_chunk(const unsigned char* slot, const tv_b
       for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 8 * h4 + 4 * tt + i;
+          const int key = key0 + 16 * tt + 4 * h4 + i;
           bool ok = key < k_end;
           if (ok && key >= P) ok = anc_bit(alo[nt], ahi[nt], key - P);
           sc[nt][tt][i] = ok ? sc[nt][tt][i] : kNegInf;
@@ -729,7 +988,7 @@ template <int D, int NTW>
 __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, CommonSmem& cm, const int* tab,
                                                          unsigned char* const (&slots)[kStages],
                                                          const tv_bf16x8 (&qop)[NTW][D / 32],
-                                                         const DmaLane& dl, int2 next_rows, int tile, int split,
+                                                         const DmaLane& dl, int2 next_rows, int slot,
                                                          int n_active, int b, int g, int r0, int R, int P,
                                                          int k_begin, int k_end, int tab0, int ntab,
                                                          bool tree_in_range) {
@@ -758,6 +1017,9 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
     for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
+  uint32_t slot_lds[NS];   // the ring slots' LDS addresses, for the DMA
+#pragma unroll
+  for (int s = 0; s < NS; ++s) slot_lds[s] = lds_addr(slots[s]);
   for (int c0 = 0; c0 < nchunks; c0 += NS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -769,7 +1031,7 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
       }
       tv_lds_barrier();
       if (producer) {
-        if (c + NS - 1 < nchunks) dma_chunk<D>(p, dl, next_rows, k_begin + 32 * (c + NS - 1), slots[(s + NS - 1) % NS]);
+        if (c + NS - 1 < nchunks) dma_chunk<D>(p, dl, next_rows, k_begin + 32 * (c + NS - 1), slot_lds[(s + NS - 1) % NS]);
         if (c + NS < nchunks) next_rows = chunk_rows(tab, tab0, ntab, k_begin + 32 * (c + NS), p.lbs);
       } else if (rbase < R) {
         mfma_chunk<D, NTW>(slots[s], qop, a, alo, ahi, k_begin + 32 * c, P, k_end, p.scale_log2, lane);
@@ -778,14 +1040,14 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
   }
 
   // output: lane l holds O[row rbase + 16*nt + l%16][16*dt + 4*(l/16) + i]
-  const size_t prow = ((size_t)tile * p.splits + split) * RW;
+  const size_t prow = (size_t)slot * RW;
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     float lt = a.l_run[nt];
     lt = tv_rows_sum(lt);
     const int qrow = rbase + 16 * nt + l16;
-    if (qrow >= R) continue;
     if (n_active == 1) {
+      if (qrow >= R) continue;
       const float inv = 1.f / lt;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -794,11 +1056,21 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
         store_out4<true, D>(p, b, g, qrow, 16 * dt + 4 * h4, v4);
       }
     } else {
-      const size_t row = prow + (qrow - r0);
+      // the row's largest |O / l| over its four lanes sets the stored power of two
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float amax = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) store_part4<true>(p.part_o, row * D + 16 * dt + 4 * h4, a.oacc[dt][nt] * inv);
-      if (h4 == 0) *(float2*)&p.part_ml[row * 2] = make_float2(a.m_run[nt], lt);
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(a.oacc[dt][nt][i] * inv));
+      amax = tv_rows_max(amax);
+      if (qrow >= R) continue;
+      const float2 sc = part_scale(amax);
+      const size_t row = prow + (qrow - r0);
+      const float f = inv * sc.x;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) store_part4<true>(p.part_o, row * D + 16 * dt + 4 * h4, a.oacc[dt][nt] * f);
+      if (h4 == 0) p.part_ml[row] = make_float4(a.m_run[nt], lt, sc.y, 0.f);
     }
   }
 }
@@ -818,16 +1090,40 @@ constexpr int block_threads() { return kBF16 ? kMfmaThreads : kThreads; }
 template <bool kBF16, int D, int NTW>
 __global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())) void tree_attn_kernel(AttnParams p) {
   constexpr int RW = kBF16 ? 64 * NTW : 16;
+  constexpr int NT = block_threads<kBF16>();
   __shared__ CommonSmem cm;
   const int t = threadIdx.x;
-  const int lid = tv_xcd_remap(blockIdx.x, p.total);
-  const int tile = lid / p.splits, split = lid % p.splits;
-  const int bg = tile / p.row_tiles, rt = tile % p.row_tiles;
-  const int b = bg / p.Hkv, g = bg % p.Hkv;
-  const bool designated = (g == 0 && rt == 0 && split == 0);
+  // balanced plans: workgroup 0 reports every request whose sizes are malformed
+  // (no workgroup is planned for those)
+  if (p.balanced && blockIdx.x == 0 && t < 64 && p.status) {
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+      const int bb = b0 + t;
+      if (bb < p.B) {
+        const int st = shape_status(p, p.prefix_len[bb], p.n_nodes[bb]);
+        if (st) p.status[bb] = st;
+      }
+    }
+  }
+  const SplitPlan sp = plan_split(p, blockIdx.x);
+  const int b = sp.b, g = sp.g, rt = sp.rt;
+  const bool designated = sp.shape_ok && g == 0 && rt == 0 && sp.s == 0;
+  if (!sp.shape_ok) {
+    // uniform plans: the request's first workgroup reports malformed sizes
+    if (!p.balanced && g == 0 && rt == 0 && sp.s == 0 && t == 0 && p.status)
+      p.status[b] = shape_status(p, sp.P, sp.n);
+    return;
+  }
+  if (!sp.work) return;
+  const int P = sp.P, n = sp.n;
   const int32_t* trow = p.table + (size_t)b * p.max_blocks;
-  const int k_begin = split * p.keys_per_split;
+  const int kps = sp.kps_ch * 32;
+  const int k_begin = sp.s * kps;
   const int tab0 = k_begin / p.bs;
+  const int R = n * p.G;
+  const int r0 = rt * RW;
+  const int keys_total = P + n;
+  const int n_active = sp.splits;
+  const int k_end = min(k_begin + kps, keys_total);
 
   if constexpr (kBF16) {
     // the ring: distinct LDS objects, one chunk each
@@ -839,13 +1135,13 @@ __global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())
     static_assert(kStages == 4, "one LDS object per ring slot");
     unsigned char* const slots[kStages] = {ring0, ring1, ring2, ring3};
 
-    // one round trip: parents, this split's block-table entries, sizes and this
+    // one round trip: parents, this split's block-table entries and this
     // wave's query operands (rows past the request are masked later)
     constexpr int KQ = D / 32;
     tv_bf16x8 qop[NTW][KQ];
     if ((t >> 6) < kMfmaWaves) {
       const int lane = t & 63, l16 = lane & 15, h4 = lane >> 4;
-      const int rbase = rt * RW + (t >> 6) * 16 * NTW;
+      const int rbase = r0 + (t >> 6) * 16 * NTW;
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         const int qrow = rbase + 16 * nt + l16;
@@ -857,33 +1153,14 @@ __global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())
       }
     }
     if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
-    const int ntab = min(p.max_blocks - tab0, (p.keys_per_split + p.bs - 1) / p.bs + 1);
-    {
-      for (int i = t; i < ntab; i += kMfmaThreads) {
-        const int blk = trow[tab0 + i];
-        // ids outside the pool (flagged by the request's validation) read block 0
-        tab[i] = (block_ok(blk, p.num_blocks) ? blk : 0) * p.Hkv + g;
-      }
+    const int ntab = min(p.max_blocks - tab0, (kps + p.bs - 1) / p.bs + 1);
+    for (int i = t; i < ntab; i += NT) {
+      const int blk = trow[tab0 + i];
+      // ids outside the pool (flagged by the request's validation) read block 0
+      tab[i] = (block_ok(blk, p.num_blocks) ? blk : 0) * p.Hkv + g;
     }
     if (t == 0) cm.flag = 0;
-    const int n = p.n_nodes[b];
-    const int P = p.prefix_len[b];
     __syncthreads();   // also completes the query loads before any DMA is in flight
-
-    if (n < 1 || n > p.n_max) {
-      if (designated && t == 0 && p.status) p.status[b] = TV_REQ_BAD_NNODES;
-      return;
-    }
-    if (P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) {
-      if (designated && t == 0 && p.status) p.status[b] = TV_REQ_BAD_KV;
-      return;
-    }
-    const int R = n * p.G;
-    const int r0 = rt * RW;
-    const int keys_total = P + n;
-    const int n_active = (keys_total + p.keys_per_split - 1) / p.keys_per_split;
-    const bool works = r0 < R && split < n_active;
-    const int k_end = min(k_begin + p.keys_per_split, keys_total);
 
     // parent array: parent[0] = -1 and 0 <= parent[i] < i
     if (t < n) {
@@ -900,52 +1177,36 @@ __global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())
     // prologue (the sizes are valid, so every key and block-table index stays
     // inside this split's staged table).  From here on no workgroup leaves
     // before its DMAs have landed, and the barriers are LDS-only.
-    const DmaLane dl = dma_lane<D>(p.bs, t & 63);
+    const DmaLane dl = dma_lane<D>(t & 63);
     int2 next_rows = make_int2(0, 0);
-    if (works && (t >> 6) == kMfmaWaves) {
+    if ((t >> 6) == kMfmaWaves) {
       const int nchunks = (k_end - k_begin + 31) / 32;
 #pragma unroll
       for (int i = 0; i < kStages - 1; ++i)
         if (i < nchunks)
-          dma_chunk<D>(p, dl, chunk_rows(tab, tab0, ntab, k_begin + 32 * i, p.lbs), k_begin + 32 * i, slots[i]);
+          dma_chunk<D>(p, dl, chunk_rows(tab, tab0, ntab, k_begin + 32 * i, p.lbs), k_begin + 32 * i,
+                       lds_addr(slots[i]));
       if (kStages - 1 < nchunks) next_rows = chunk_rows(tab, tab0, ntab, k_begin + 32 * (kStages - 1), p.lbs);
     }
     if (designated) {
       // every block id used by positions [0, P + n) must name a pool block
       const int nblk = (P + n + p.bs - 1) / p.bs;
-      for (int i = t; i < nblk; i += kMfmaThreads)
+      for (int i = t; i < nblk; i += NT)
         if (!block_ok(trow[i], p.num_blocks)) cm.flag = 1;
       tv_lds_barrier();
       if (t == 0 && p.status) p.status[b] = cm.flag ? TV_REQ_BAD_KV : 0;
       // keep going: loads from bad blocks are redirected
     }
-    if (!works) return;
     const bool tree_in_range = k_end > P;
     if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
     tv_lds_barrier();
-    attn_mfma<D, NTW>(p, cm, tab, slots, qop, dl, next_rows, tile, split, n_active, b, g, r0, R, P, k_begin, k_end,
+    attn_mfma<D, NTW>(p, cm, tab, slots, qop, dl, next_rows, sp.slot, n_active, b, g, r0, R, P, k_begin, k_end,
                       tab0, ntab, tree_in_range);
   } else {
     __shared__ ValuSmem<D> vs;
     if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
     if (t == 0) cm.flag = 0;
-    const int n = p.n_nodes[b];
-    const int P = p.prefix_len[b];
     __syncthreads();
-
-    int flags = 0;
-    if (n < 1 || n > p.n_max) flags |= TV_REQ_BAD_NNODES;
-    else if (P < 0 || (long long)P + n > (long long)p.max_blocks * p.bs) flags |= TV_REQ_BAD_KV;
-    if (flags) {
-      if (designated && t == 0 && p.status) p.status[b] = flags;
-      return;
-    }
-    const int R = n * p.G;
-    const int r0 = rt * RW;
-    const int keys_total = P + n;
-    const int n_active = (keys_total + p.keys_per_split - 1) / p.keys_per_split;
-    const bool works = r0 < R && split < n_active;
-    const int k_end = min(k_begin + p.keys_per_split, keys_total);
     if (t < n) {
       const int pi = cm.par[t];
       const bool ok = (t == 0) ? (pi == -1) : (pi >= 0 && pi < t);
@@ -958,18 +1219,17 @@ __global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())
     }
     if (designated) {
       const int nblk = (P + n + p.bs - 1) / p.bs;
-      for (int i = t; i < nblk; i += kThreads)
+      for (int i = t; i < nblk; i += NT)
         if (!block_ok(trow[i], p.num_blocks)) cm.flag = 1;
       __syncthreads();
       if (t == 0 && p.status) p.status[b] = cm.flag ? TV_REQ_BAD_KV : 0;
     }
-    if (!works) return;
     const bool tree_in_range = k_end > P;
     if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
     __syncthreads();
     const int rows = min(RW, R - r0);
     attn_valu<false, D>(p, vs, b, g, r0, rows, P, k_begin, k_end, tree_in_range, cm.anc);
-    emit_valu<false, D, RW>(p, cm, vs, tile, split, n_active, b, g, r0, rows);
+    emit_valu<false, D, RW>(p, cm, vs, sp.slot, n_active, b, g, r0, rows);
   }
 }
 
@@ -1004,41 +1264,56 @@ int choose_ntw(const tv_attn_desc* d, int cu) {
   return 1;
 }
 
-int make_plan(const tv_attn_desc* d, int cu, int wg_per_cu, int ntw, AttnPlan* pl) {
+// Host half of the split plan: which plan the device follows and how many
+// workgroups and partial slots it may use.  Keys per split are chosen on the
+// device from the requests' lengths, so none of this depends on how long a
+// context the block table could hold, beyond the staged-table limit of
+// max_keys_per_split keys per split.
+//   Uniform: every tile gets `splits` splits, enough to give each CU one
+//   workgroup (and enough for the longest sequence the table can hold).
+//   Balanced (batches whose tiles alone leave CUs idle): the device spreads the
+//   batch's chunk-tiles over `nwg` = one workgroup per CU; the grid covers the
+//   most splits that can produce (nwg + tiles, or tiles * min_splits when a
+//   split's reach is the limit).
+int make_plan(const tv_attn_desc* d, int cu, int ntw, AttnPlan* pl) {
   const int G = d->n_q_heads / d->n_kv_heads;
   const long long Rmax = (long long)d->n_max * G;
   pl->ntw = ntw;
   pl->rows_per_tile = d->dtype == TV_BF16 ? 64 * ntw : 16;
   pl->row_tiles = (int)((Rmax + pl->rows_per_tile - 1) / pl->rows_per_tile);
-  const long long max_keys = (long long)d->max_blocks_per_seq * d->block_size;
-  const long long base = (long long)d->batch * d->n_kv_heads * pl->row_tiles;
-  // one workgroup per CU: more splits only add partials to merge, and tiles
-  // that already cover the CUs need no key splitting at all
-  (void)wg_per_cu;
-  const long long target = cu;
-  long long splits = base > 0 ? (target + base - 1) / base : 1;
-  long long max_splits = (max_keys + 127) / 128;
-  if (max_splits > kMaxSplits) max_splits = kMaxSplits;
-  if (splits > max_splits) splits = max_splits;
-  const long long max_kps = ntw == 1 ? max_keys_per_split<1>() : max_keys_per_split<2>();
-  const long long min_splits = (max_keys + max_kps - 1) / max_kps;
-  if (splits < min_splits) splits = min_splits;
-  if (splits > kMaxSplits) return TV_ERR_UNSUPPORTED;   // keys per sequence beyond 32 splits of the maximum
-  if (splits < 1) splits = 1;
-  long long kps = (max_keys + splits - 1) / splits;
-  kps = (kps + 31) / 32 * 32;
-  splits = (max_keys + kps - 1) / kps;
-  pl->splits = (int)splits;
-  pl->keys_per_split = (int)kps;
-  const size_t tiles = (size_t)base;
-  size_t bytes = 0;
-  if (pl->splits > 1) {
-    const size_t esz = d->dtype == TV_BF16 ? 2 : 4;   // partial O element: fp16 for bf16 inputs
-    bytes = tiles * pl->splits * pl->rows_per_tile * (size_t)d->head_dim * esz;
-    pl->off_ml = tv_align_up(bytes, 256);
-    bytes = pl->off_ml + tiles * pl->splits * pl->rows_per_tile * 2 * sizeof(float);
+  const long long tiles = (long long)d->batch * d->n_kv_heads * pl->row_tiles;
+  const long long cap_ch = ((long long)d->max_blocks_per_seq * d->block_size + 31) / 32;
+  const long long max_kps_ch = (ntw == 1 ? max_keys_per_split<1>() : max_keys_per_split<2>()) / 32;
+  const long long min_splits = (cap_ch + max_kps_ch - 1) / max_kps_ch;
+  pl->max_kps_ch = (int)max_kps_ch;
+  pl->nwg = cu;
+  long long grid, slots;
+  // the balanced plan's device sums stay in 32 bits (chunk-tiles of the batch)
+  if (d->batch > 1 && tiles < cu && tiles * cap_ch < 0x7fffffffLL) {
+    pl->balanced = 1;
+    pl->splits = 0;
+    grid = tiles * min_splits;   // bounds the device plan's split count
+    if (cu + tiles > grid) grid = cu + tiles;
+    slots = grid;
   } else {
-    pl->off_ml = 0;
+    pl->balanced = 0;
+    long long s = tiles > 0 ? (cu + tiles - 1) / tiles : 1;
+    if (s < min_splits) s = min_splits;
+    if (s < 1) s = 1;
+    pl->splits = (int)s;
+    grid = tiles * s;
+    slots = s > 1 ? grid : 0;
+  }
+  if (grid > 0x7fffffff || slots > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  pl->grid = (int)grid;
+  pl->slots = (int)slots;
+  size_t bytes = 0;
+  pl->off_ml = 0;
+  if (slots > 0) {
+    const size_t esz = d->dtype == TV_BF16 ? 2 : 4;   // partial O element: fp16 for bf16 inputs
+    bytes = (size_t)slots * pl->rows_per_tile * (size_t)d->head_dim * esz;
+    pl->off_ml = tv_align_up(bytes, 256);
+    bytes = pl->off_ml + (size_t)slots * pl->rows_per_tile * sizeof(float4);
   }
   pl->bytes = tv_align_up(bytes, 256);
   return TV_OK;
@@ -1056,44 +1331,13 @@ AttnKernel pick_kernel(const tv_attn_desc* d, int ntw) {
   return ntw == 2 ? tree_attn_kernel<true, 64, 2> : tree_attn_kernel<true, 64, 1>;
 }
 
-// Resident workgroups per CU of one kernel instance on the current device (cached).
-int occupancy(AttnKernel k, int threads, int* out) {
-  static std::mutex mu;
-  static const void* keys[16];
-  static int vals[16];
-  static int dev_of[16];
-  static int n = 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return TV_ERR_HIP;
-  std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < n; ++i)
-    if (keys[i] == (const void*)k && dev_of[i] == dev) {
-      *out = vals[i];
-      return TV_OK;
-    }
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, threads, 0) != hipSuccess) return TV_ERR_HIP;
-  if (nb < 1) nb = 1;
-  if (n < 16) {
-    keys[n] = (const void*)k;
-    vals[n] = nb;
-    dev_of[n] = dev;
-    ++n;
-  }
-  *out = nb;
-  return TV_OK;
-}
-
 int plan_for(const tv_attn_desc* d, AttnPlan* pl, AttnKernel* kern) {
-  int cu = 0, occ = 0;
+  int cu = 0;
   int rc = tv_device_cu_count(&cu);
   if (rc != TV_OK) return rc;
   const int ntw = choose_ntw(d, cu);
-  AttnKernel k = pick_kernel(d, ntw);
-  rc = occupancy(k, d->dtype == TV_BF16 ? kMfmaThreads : kThreads, &occ);
-  if (rc != TV_OK) return rc;
-  rc = make_plan(d, cu, occ, ntw, pl);
-  if (kern) *kern = k;
+  rc = make_plan(d, cu, ntw, pl);
+  if (kern) *kern = pick_kernel(d, ntw);
   return rc;
 }
 
@@ -1135,7 +1379,7 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   p.out = out;
   p.status = status;
   p.part_o = workspace;
-  p.part_ml = (float*)((char*)workspace + pl.off_ml);
+  p.part_ml = (float4*)((char*)workspace + pl.off_ml);
   p.B = desc->batch;
   p.n_max = desc->n_max;
   p.Hq = desc->n_q_heads;
@@ -1150,14 +1394,16 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   p.scale_log2 = scale * kLog2e;
   p.rows_per_tile = pl.rows_per_tile;
   p.row_tiles = pl.row_tiles;
+  p.balanced = pl.balanced;
   p.splits = pl.splits;
-  p.keys_per_split = pl.keys_per_split;
-  const long long total = (long long)desc->batch * desc->n_kv_heads * pl.row_tiles * pl.splits;
-  if (total > 0x7fffffff) return TV_ERR_UNSUPPORTED;
-  p.total = (int)total;
-  hipLaunchKernelGGL(kern, dim3(p.total), dim3(desc->dtype == TV_BF16 ? kMfmaThreads : kThreads), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  if (pl.splits > 1) {
+  p.nwg = pl.nwg;
+  p.max_kps_ch = pl.max_kps_ch;
+  p.grid = pl.grid;
+  if (pl.grid > 0) {
+    hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(desc->dtype == TV_BF16 ? kMfmaThreads : kThreads), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  }
+  if (pl.slots > 0) {
     const long long tiles = (long long)desc->batch * desc->n_kv_heads * pl.row_tiles;
     const int rpb = desc->head_dim == 128 ? merge_rows<128>() : merge_rows<64>();
     const long long grid = tiles * ((pl.rows_per_tile + rpb - 1) / rpb);

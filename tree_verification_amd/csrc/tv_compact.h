@@ -9,9 +9,9 @@
 // earlier destination only when it belongs to a later step: a batch of steps
 // is hazard-free when every source of the batch is read before any of its
 // destinations is written, and the sources of later batches lie past every
-// destination of earlier ones.  Each (KV head, element d) pair of the key rows
-// and of the transposed value rows is moved by one thread, independently of
-// the others.
+// destination of earlier ones.  Each (KV head, element d) pair of the key and
+// value rows (both token-major) is moved by one thread, independently of the
+// others.
 #pragma once
 
 #include "tv_common.h"
@@ -111,7 +111,7 @@ __device__ void tv_compact_heads(const TvCompactArgs& p, int b, int g0, int ng, 
           size_t blk = (size_t)(pre ? pre->stage[s / p.bs - pre->stage0] : trow[s / p.bs]);
           int slot = s % p.bs;
           kreg[i] = K[((blk * p.Hkv + g) * p.bs + slot) * p.D + d];
-          vreg[i] = V[((blk * p.Hkv + g) * p.D + d) * p.bs + slot];
+          vreg[i] = V[((blk * p.Hkv + g) * p.bs + slot) * p.D + d];
         }
       }
 #pragma unroll
@@ -122,7 +122,7 @@ __device__ void tv_compact_heads(const TvCompactArgs& p, int b, int g0, int ng, 
           size_t blk = (size_t)(pre ? pre->stage[dst / p.bs - pre->stage0] : trow[dst / p.bs]);
           int slot = dst % p.bs;
           K[((blk * p.Hkv + g) * p.bs + slot) * p.D + d] = kreg[i];
-          V[((blk * p.Hkv + g) * p.D + d) * p.bs + slot] = vreg[i];
+          V[((blk * p.Hkv + g) * p.bs + slot) * p.D + d] = vreg[i];
         }
       }
     }

@@ -8,7 +8,7 @@ Layouts (all arrays are NumPy, C-contiguous):
 
   q            [B][Nmax][Hq][D]            float32 holding bf16-exact values when dtype == "bf16"
   k_cache      [num_blocks][Hkv][bs][D]    token-major key blocks
-  v_cache      [num_blocks][Hkv][D][bs]    value blocks stored transposed (d-major, token contiguous)
+  v_cache      [num_blocks][Hkv][bs][D]    token-major value blocks
   block_table  [B][max_blocks]  int32     -1 past the blocks a request owns
   prefix_len   [B] int32, n_nodes [B] int32
   parent       [B][Nmax] int32            parent[b][0] = -1, 0 <= parent[i] < i, -1 as padding
@@ -257,7 +257,7 @@ def make_workload(name: str, seed: int | None = None, *, batch=None, prefix=None
 
     q = draw((B, Nmax, Hq, D))
     k_cache = draw((num_blocks, Hkv, bs, D))
-    v_cache = draw((num_blocks, Hkv, D, bs))
+    v_cache = draw((num_blocks, Hkv, bs, D))
 
     tokens = np.zeros((B, Nmax), dtype=np.int32)
     tl = dl = None
