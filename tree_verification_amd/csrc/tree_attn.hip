@@ -53,12 +53,16 @@
 namespace {
 
 constexpr int kThreads = 256;        // VALU path (fp32): four waves
-constexpr int kMfmaWaves = 4;        // MFMA path: four waves own the rows ...
-constexpr int kMfmaThreads = 64 * (kMfmaWaves + 1);   // ... and a fifth moves the K/V chunks
+constexpr int kMfmaWaves = 4;        // MFMA path: four waves own the rows of a tile (per key group) ...
+// ... and one more per key group moves its K/V chunks: 5 waves, or 10 with two key groups
+template <int KG>
+constexpr int mfma_threads() { return 64 * (kMfmaWaves + 1) * KG; }
 constexpr int kMaxNodes = 128;
 constexpr int kMaxKeysPerSplit = 32768;   // NTW = 1 (two workgroups per CU); twice that for NTW = 2
 constexpr int kMinSplitChunks = 4;        // a split owns at least 128 keys (or the whole request)
-constexpr int kStages = 4;            // LDS ring slots (chunks in flight) on the MFMA path
+// LDS ring on the MFMA path: NS steps of KG chunks (one chunk per key group).
+template <int KG>
+constexpr int ring_steps() { return 4; }
 // Keys one split may own, and the block-table entries a workgroup stages for
 // them (block size 16 at least).
 template <int NTW>
@@ -91,7 +95,7 @@ struct AttnParams {
 };
 
 struct AttnPlan {
-  int rows_per_tile, row_tiles, ntw, balanced, splits, nwg, max_kps_ch, grid, slots;
+  int rows_per_tile, row_tiles, ntw, kg, balanced, splits, nwg, max_kps_ch, grid, slots;
   size_t off_ml, bytes;
 };
 
@@ -745,6 +749,13 @@ __device__ void emit_valu(const AttnParams& p, CommonSmem& cm, ValuSmem<D>& sm, 
 // MFMA path: K/V chunks DMA'd into an LDS ring, 16*NTW rows per wave
 // ---------------------------------------------------------------------------
 
+typedef __attribute__((address_space(3))) const tv_u32x4* tv_lds_u32x4_ptr;
+
+// 16 bytes from LDS address `addr` (ds_read_b128).
+__device__ __forceinline__ tv_bf16x8 lds_read16(uint32_t addr) {
+  return __builtin_bit_cast(tv_bf16x8, *(tv_lds_u32x4_ptr)(uintptr_t)addr);
+}
+
 __device__ __forceinline__ tv_bf16x8 lds_bf16x8(const unsigned char* ptr) {
   return __builtin_bit_cast(tv_bf16x8, *(const tv_u32x4*)ptr);
 }
@@ -851,13 +862,13 @@ typedef __attribute__((address_space(3))) tv_bf16x4* tv_lds_bf16x4_ptr;
 // values 16*dt + 4*(i%4) .. + 3 of key 16*e + 4*h + i/4 (one 8-byte half of a
 // swizzled 16-byte piece).
 template <int D>
-__device__ __forceinline__ tv_bf16x8 lds_vop(const unsigned char* vreg, int dt, int lane) {
+__device__ __forceinline__ tv_bf16x8 lds_vop(uint32_t vreg, int dt, int lane) {
   const int h = lane >> 4, i = lane & 15;
   const int key0 = 4 * h + (i >> 2);
   const int f = vswz<D>(key0);   // the same for key0 + 16
-  const unsigned char* a0 = vreg + key0 * 2 * D + 16 * ((2 * dt + ((i & 3) >> 1)) ^ f) + 8 * (i & 1);
-  const tv_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((tv_lds_bf16x4_ptr)a0);
-  const tv_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((tv_lds_bf16x4_ptr)(a0 + 16 * 2 * D));
+  const uint32_t a0 = vreg + key0 * 2 * D + 16 * ((2 * dt + ((i & 3) >> 1)) ^ f) + 8 * (i & 1);
+  const tv_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((tv_lds_bf16x4_ptr)(uintptr_t)a0);
+  const tv_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((tv_lds_bf16x4_ptr)(uintptr_t)(a0 + 16 * 2 * D));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -870,7 +881,7 @@ struct WaveAcc {
 
 // One 32-key chunk from an LDS slot: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
 template <int D, int NTW>
-__device__ __forceinline__ void mfma_chunk(const unsigned char* slot, const tv_bf16x8 (&qop)[NTW][D / 32],
+__device__ __forceinline__ void mfma_chunk(uint32_t slot, const tv_bf16x8 (&qop)[NTW][D / 32],
                                            WaveAcc<D, NTW>& a, const uint64_t (&alo)[NTW],
                                            const uint64_t (&ahi)[NTW], int key0, int P, int k_end,
                                            float scale_log2, int lane) {
@@ -880,7 +891,7 @@ __device__ __forceinline__ void mfma_chunk(const unsigned char* slot, const tv_b
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = lds_bf16x8(slot + (tt * KK + kk) * 1024 + lane * 16);
+    for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = lds_read16(slot + (tt * KK + kk) * 1024 + lane * 16);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) vop[dt] = lds_vop<D>(slot + 2 * KK * 1024, dt, lane);
 
@@ -972,33 +983,41 @@ __device__ __forceinline__ void mfma_chunk(const unsigned char* slot, const tv_b
       a.oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[nt], a.oacc[dt][nt], 0, 0, 0);
 }
 
-// The key range of one split, chunk by chunk through an NS-slot LDS ring.  The
-// producer wave sent the first NS-1 chunks in the prologue and read the block
-// rows of chunk NS-1.  Per chunk c: the producer waits for its DMA of c (later
-// chunks stay in flight); one barrier (chunk c has landed and every MFMA wave
-// is done with chunk c-1); the producer sends chunk c+NS-1 into c-1's slot and
-// reads the block rows of chunk c+NS (used one step later, so the LDS read's
-// latency stays hidden) while the MFMA waves compute c.  Issuing a DMA stalls
-// the issuing wave until the memory pipeline takes it, so keeping all of them
-// on one wave lets the chunk's compute run under the transfer of later chunks.
-// The slots are distinct LDS objects and the stage loop is unrolled, so the
-// compiler sees which DMA writes which slot and adds no waits of its own
-// before the slot reads (the MFMA waves have no memory operations in flight).
-template <int D, int NTW>
+// The key range of one split, step by step through an LDS ring of NS steps
+// of KG chunks.  With KG key groups, group k's four MFMA waves take the
+// chunks c = KG*step + k, so two waves share each SIMD and one's softmax runs
+// beside the other's matrix products; the groups' (m, l, O) are merged through
+// LDS at the end.  The producer wave sent the first NS-1 steps in the prologue
+// and read the block rows of the next chunks.  Per step: the producer waits
+// for its DMAs of the step (later steps stay in flight); one barrier (the step
+// has landed and every MFMA wave is done with the previous one); the producer
+// sends step s+NS-1 into the previous step's slots and reads the block rows
+// of the following step (used one step later, so the LDS read's latency stays
+// hidden) while the MFMA waves compute.  Issuing a DMA stalls the issuing wave
+// until the memory pipeline takes it, so keeping all of them on one wave lets
+// the chunks' compute run under the transfer of later ones.  The slots are
+// distinct LDS objects and the stage loop is unrolled, so the compiler sees
+// which DMA writes which slot and adds no waits of its own before the slot
+// reads (the MFMA waves have no memory operations in flight).
+template <int D, int NTW, int KG>
 __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, CommonSmem& cm, const int* tab,
-                                                         unsigned char* const (&slots)[kStages],
+                                                         const uint32_t (&slot_lds)[ring_steps<KG>() * KG],
                                                          const tv_bf16x8 (&qop)[NTW][D / 32],
                                                          const DmaLane& dl, int2 next_rows, int slot,
                                                          int n_active, int b, int g, int r0, int R, int P,
                                                          int k_begin, int k_end, int tab0, int ntab,
                                                          bool tree_in_range) {
-  constexpr int DT = Chunk<D>::DT, RW = 64 * NTW, NB = Chunk<D>::NBLK, NS = kStages;
+  constexpr int DT = Chunk<D>::DT, RW = 64 * NTW, NB = Chunk<D>::NBLK, NS = ring_steps<KG>();
+  constexpr int NW = kMfmaWaves * KG;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, h4 = lane >> 4;
   const int G = p.G;
-  const bool producer = wave == kMfmaWaves;
-  const int rbase = producer ? R : r0 + wave * 16 * NTW;   // this wave's first row (none for the producer)
+  const bool producer = wave >= NW;
+  // key group of an MFMA wave, or the group whose chunks a producer moves
+  const int kg = producer ? wave - NW : wave / kMfmaWaves, wr = wave % kMfmaWaves;
+  const int rbase = producer ? R : r0 + wr * 16 * NTW;   // this wave's first row (none for a producer)
   const int nchunks = (k_end - k_begin + 31) / 32;
+  const int nsteps = (nchunks + KG - 1) / KG;
 
   uint64_t alo[NTW], ahi[NTW];
 #pragma unroll
@@ -1017,25 +1036,65 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
     for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  uint32_t slot_lds[NS];   // the ring slots' LDS addresses, for the DMA
-#pragma unroll
-  for (int s = 0; s < NS; ++s) slot_lds[s] = lds_addr(slots[s]);
-  for (int c0 = 0; c0 < nchunks; c0 += NS) {
+  for (int st0 = 0; st0 < nsteps; st0 += NS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int c = c0 + s;
-      if (c >= nchunks) break;
+      const int st = st0 + s;
+      if (st >= nsteps) break;
       if (producer) {
-        if (c + NS - 2 < nchunks) wait_vmcnt<(NS - 2) * NB>();
+        // this producer's chunks of steps st+1 .. st+NS-2 stay in flight when those are full steps
+        if (st + NS - 2 < nsteps - 1) wait_vmcnt<(NS - 2) * NB>();
         else wait_vmcnt<0>();
       }
       tv_lds_barrier();
+      const uint32_t sslot = KG == 1 ? slot_lds[s] : (kg ? slot_lds[s * KG + 1] : slot_lds[s * KG]);
       if (producer) {
-        if (c + NS - 1 < nchunks) dma_chunk<D>(p, dl, next_rows, k_begin + 32 * (c + NS - 1), slot_lds[(s + NS - 1) % NS]);
-        if (c + NS < nchunks) next_rows = chunk_rows(tab, tab0, ntab, k_begin + 32 * (c + NS), p.lbs);
-      } else if (rbase < R) {
-        mfma_chunk<D, NTW>(slots[s], qop, a, alo, ahi, k_begin + 32 * c, P, k_end, p.scale_log2, lane);
+        const int sn = st + NS - 1;   // the step sent now, into the previous step's slots
+        const int ps = (s + NS - 1) % NS;
+        const uint32_t dst = KG == 1 ? slot_lds[ps] : (kg ? slot_lds[ps * KG + 1] : slot_lds[ps * KG]);
+        const int c = KG * sn + kg;
+        if (c < nchunks) dma_chunk<D>(p, dl, next_rows, k_begin + 32 * c, dst);
+        if (c + KG < nchunks) next_rows = chunk_rows(tab, tab0, ntab, k_begin + 32 * (c + KG), p.lbs);
+      } else {
+        const int c = KG * st + kg;
+        if (c < nchunks && rbase < R)
+          mfma_chunk<D, NTW>(sslot, qop, a, alo, ahi, k_begin + 32 * c, P, k_end, p.scale_log2, lane);
       }
+    }
+  }
+
+  if constexpr (KG > 1) {
+    // key group 1 hands its (m, l, O) to group 0 through LDS (the ring is free:
+    // the producer's last wait drained every DMA before the last barrier)
+    // wave wr of each group uses ring slot wr: O as [dt][nt][lane], then (m, l) as [nt][lane]
+    typedef __attribute__((address_space(3))) tv_f32x4* lds_f32x4_ptr;
+    typedef __attribute__((address_space(3))) tv_f32x2* lds_f2_ptr;
+    const uint32_t mine = wr == 0 ? slot_lds[0] : wr == 1 ? slot_lds[1] : wr == 2 ? slot_lds[2] : slot_lds[3];
+    lds_f32x4_ptr xo = (lds_f32x4_ptr)(uintptr_t)mine;
+    lds_f2_ptr xml = (lds_f2_ptr)(uintptr_t)(mine + DT * NTW * 64 * 16);
+    static_assert(DT * NTW * 64 * 16 + NTW * 64 * 8 <= Chunk<D>::BYTES && kMfmaWaves <= NS * KG,
+                  "merge buffers fit the ring");
+    tv_lds_barrier();
+    if (!producer && kg == 1) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) xo[(dt * NTW + nt) * 64 + lane] = a.oacc[dt][nt];
+        xml[nt * 64 + lane] = (tv_f32x2){a.m_run[nt], a.l_run[nt]};
+      }
+    }
+    tv_lds_barrier();
+    if (producer || kg != 0) return;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const tv_f32x2 mb = xml[nt * 64 + lane];
+      const float M = fmaxf(a.m_run[nt], mb.x);
+      const float fa = a.m_run[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(a.m_run[nt] - M);
+      const float fb = mb.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mb.x - M);
+      a.m_run[nt] = M;
+      a.l_run[nt] = a.l_run[nt] * fa + mb.y * fb;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] = a.oacc[dt][nt] * fa + xo[(dt * NTW + nt) * 64 + lane] * fb;
     }
   }
 
@@ -1081,16 +1140,17 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
 
 // Launch bounds: NTW = 1 leaves room for two workgroups per CU (ten waves,
 // under 80 KB of LDS each); wider tiles take more of the register file.
-template <bool kBF16, int NTW>
-constexpr int wg_per_cu() { return (kBF16 && NTW > 1) ? 1 : 2; }
+template <bool kBF16, int NTW, int KG>
+constexpr int wg_per_cu() { return (kBF16 && (NTW > 1 || KG > 1)) ? 1 : 2; }
 
-template <bool kBF16>
-constexpr int block_threads() { return kBF16 ? kMfmaThreads : kThreads; }
+template <bool kBF16, int KG>
+constexpr int block_threads() { return kBF16 ? mfma_threads<KG>() : kThreads; }
 
-template <bool kBF16, int D, int NTW>
-__global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())) void tree_attn_kernel(AttnParams p) {
+template <bool kBF16, int D, int NTW, int KG>
+__global__ __launch_bounds__((block_threads<kBF16, KG>()), (wg_per_cu<kBF16, NTW, KG>())) void tree_attn_kernel(AttnParams p) {
   constexpr int RW = kBF16 ? 64 * NTW : 16;
-  constexpr int NT = block_threads<kBF16>();
+  constexpr int NT = block_threads<kBF16, KG>();
+  constexpr int NW = kMfmaWaves * KG;   // MFMA waves; waves NW .. NW + KG - 1 are the producers
   __shared__ CommonSmem cm;
   const int t = threadIdx.x;
   // balanced plans: workgroup 0 reports every request whose sizes are malformed
@@ -1127,21 +1187,36 @@ __global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())
 
   if constexpr (kBF16) {
     // the ring: distinct LDS objects, one chunk each
+    constexpr int NSLOT = ring_steps<KG>() * KG;
+    static_assert(NSLOT == 4 || NSLOT == 8, "one LDS object per ring slot");
     __shared__ alignas(16) unsigned char ring0[Chunk<D>::BYTES];
     __shared__ alignas(16) unsigned char ring1[Chunk<D>::BYTES];
     __shared__ alignas(16) unsigned char ring2[Chunk<D>::BYTES];
     __shared__ alignas(16) unsigned char ring3[Chunk<D>::BYTES];
     __shared__ int tab[max_tab<NTW>()];   // (block, KV head) row index per block of this split
-    static_assert(kStages == 4, "one LDS object per ring slot");
-    unsigned char* const slots[kStages] = {ring0, ring1, ring2, ring3};
+    uint32_t slots[NSLOT];   // LDS addresses of the slots
+    slots[0] = lds_addr(ring0);
+    slots[1] = lds_addr(ring1);
+    slots[2] = lds_addr(ring2);
+    slots[3] = lds_addr(ring3);
+    if constexpr (NSLOT == 8) {
+      __shared__ alignas(16) unsigned char ring4[Chunk<D>::BYTES];
+      __shared__ alignas(16) unsigned char ring5[Chunk<D>::BYTES];
+      __shared__ alignas(16) unsigned char ring6[Chunk<D>::BYTES];
+      __shared__ alignas(16) unsigned char ring7[Chunk<D>::BYTES];
+      slots[4 % NSLOT] = lds_addr(ring4);
+      slots[5 % NSLOT] = lds_addr(ring5);
+      slots[6 % NSLOT] = lds_addr(ring6);
+      slots[7 % NSLOT] = lds_addr(ring7);
+    }
 
     // one round trip: parents, this split's block-table entries and this
     // wave's query operands (rows past the request are masked later)
     constexpr int KQ = D / 32;
     tv_bf16x8 qop[NTW][KQ];
-    if ((t >> 6) < kMfmaWaves) {
+    if ((t >> 6) < NW) {
       const int lane = t & 63, l16 = lane & 15, h4 = lane >> 4;
-      const int rbase = r0 + (t >> 6) * 16 * NTW;
+      const int rbase = r0 + ((t >> 6) % kMfmaWaves) * 16 * NTW;
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         const int qrow = rbase + 16 * nt + l16;
@@ -1178,15 +1253,22 @@ __global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())
     // inside this split's staged table).  From here on no workgroup leaves
     // before its DMAs have landed, and the barriers are LDS-only.
     const DmaLane dl = dma_lane<D>(t & 63);
+    constexpr int NS = ring_steps<KG>();
     int2 next_rows = make_int2(0, 0);
-    if ((t >> 6) == kMfmaWaves) {
+    if ((t >> 6) >= NW) {
+      // producer k moves the chunks k, k + KG, ...: steps 0 .. NS-2 now, and
+      // the block rows of its chunk of step NS-1 read ahead
+      const int pk = (t >> 6) - NW;
       const int nchunks = (k_end - k_begin + 31) / 32;
 #pragma unroll
-      for (int i = 0; i < kStages - 1; ++i)
-        if (i < nchunks)
-          dma_chunk<D>(p, dl, chunk_rows(tab, tab0, ntab, k_begin + 32 * i, p.lbs), k_begin + 32 * i,
-                       lds_addr(slots[i]));
-      if (kStages - 1 < nchunks) next_rows = chunk_rows(tab, tab0, ntab, k_begin + 32 * (kStages - 1), p.lbs);
+      for (int i = 0; i < NS - 1; ++i) {
+        const int c = KG * i + pk;
+        if (c < nchunks)
+          dma_chunk<D>(p, dl, chunk_rows(tab, tab0, ntab, k_begin + 32 * c, p.lbs), k_begin + 32 * c,
+                       KG == 1 ? slots[i] : (pk ? slots[i * KG + 1] : slots[i * KG]));
+      }
+      const int c = KG * (NS - 1) + pk;
+      if (c < nchunks) next_rows = chunk_rows(tab, tab0, ntab, k_begin + 32 * c, p.lbs);
     }
     if (designated) {
       // every block id used by positions [0, P + n) must name a pool block
@@ -1200,8 +1282,8 @@ __global__ __launch_bounds__((block_threads<kBF16>()), (wg_per_cu<kBF16, NTW>())
     const bool tree_in_range = k_end > P;
     if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
     tv_lds_barrier();
-    attn_mfma<D, NTW>(p, cm, tab, slots, qop, dl, next_rows, sp.slot, n_active, b, g, r0, R, P, k_begin, k_end,
-                      tab0, ntab, tree_in_range);
+    attn_mfma<D, NTW, KG>(p, cm, tab, slots, qop, dl, next_rows, sp.slot, n_active, b, g, r0, R, P, k_begin, k_end,
+                          tab0, ntab, tree_in_range);
   } else {
     __shared__ ValuSmem<D> vs;
     if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
@@ -1264,6 +1346,15 @@ int choose_ntw(const tv_attn_desc* d, int cu) {
   return 1;
 }
 
+// Key groups: two sets of MFMA waves on alternate chunks of a split, each
+// with its own producer wave (64-row tiles only: 128-row tiles need more
+// registers than two waves per SIMD leave).  Measured on MI355X: the 4096-key
+// chains 200 -> 193 us; 128-row tiles with one group stay better for the
+// 70B-shaped share (1005 against 1058 us as 64-row tiles with two groups).
+int choose_kg(const tv_attn_desc* d, int ntw) {
+  return (d->dtype == TV_BF16 && ntw == 1) ? 2 : 1;
+}
+
 // Host half of the split plan: which plan the device follows and how many
 // workgroups and partial slots it may use.  Keys per split are chosen on the
 // device from the requests' lengths, so none of this depends on how long a
@@ -1321,14 +1412,16 @@ int make_plan(const tv_attn_desc* d, int cu, int ntw, AttnPlan* pl) {
 
 typedef void (*AttnKernel)(AttnParams);
 
-AttnKernel pick_kernel(const tv_attn_desc* d, int ntw) {
+AttnKernel pick_kernel(const tv_attn_desc* d, int ntw, int kg) {
   const bool bf = d->dtype == TV_BF16;
   if (d->head_dim == 128) {
-    if (!bf) return tree_attn_kernel<false, 128, 1>;
-    return ntw == 2 ? tree_attn_kernel<true, 128, 2> : tree_attn_kernel<true, 128, 1>;
+    if (!bf) return tree_attn_kernel<false, 128, 1, 1>;
+    if (kg == 2) return tree_attn_kernel<true, 128, 1, 2>;
+    return ntw == 2 ? tree_attn_kernel<true, 128, 2, 1> : tree_attn_kernel<true, 128, 1, 1>;
   }
-  if (!bf) return tree_attn_kernel<false, 64, 1>;
-  return ntw == 2 ? tree_attn_kernel<true, 64, 2> : tree_attn_kernel<true, 64, 1>;
+  if (!bf) return tree_attn_kernel<false, 64, 1, 1>;
+  if (kg == 2) return tree_attn_kernel<true, 64, 1, 2>;
+  return ntw == 2 ? tree_attn_kernel<true, 64, 2, 1> : tree_attn_kernel<true, 64, 1, 1>;
 }
 
 int plan_for(const tv_attn_desc* d, AttnPlan* pl, AttnKernel* kern) {
@@ -1336,8 +1429,10 @@ int plan_for(const tv_attn_desc* d, AttnPlan* pl, AttnKernel* kern) {
   int rc = tv_device_cu_count(&cu);
   if (rc != TV_OK) return rc;
   const int ntw = choose_ntw(d, cu);
+  const int kg = choose_kg(d, ntw);
   rc = make_plan(d, cu, ntw, pl);
-  if (kern) *kern = pick_kernel(d, ntw);
+  pl->kg = kg;
+  if (kern) *kern = pick_kernel(d, ntw, kg);
   return rc;
 }
 
@@ -1400,7 +1495,8 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
   p.max_kps_ch = pl.max_kps_ch;
   p.grid = pl.grid;
   if (pl.grid > 0) {
-    hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(desc->dtype == TV_BF16 ? kMfmaThreads : kThreads), 0, stream, p);
+    const int threads = desc->dtype != TV_BF16 ? kThreads : (pl.kg == 2 ? mfma_threads<2>() : mfma_threads<1>());
+    hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(threads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   }
   if (pl.slots > 0) {
