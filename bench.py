@@ -50,6 +50,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-construction", action="store_true", help="skip the tree-construction timings")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--table-tokens", type=int, default=0,
+                    help="size every request's block table for this many tokens of context (entries past "
+                         "the request's blocks are -1); 0: exactly the blocks the request uses")
+    ap.add_argument("--accept-seeds", type=int, default=16,
+                    help="workload seeds whose stochastic verification gives the acceptance statistics")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run one elementwise copy of this many MiB (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -203,16 +209,22 @@ def main():
     from tree_verification_amd import binding as tv
     from tree_verification_amd.workloads import bf16_bits, make_workload, seed_for
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    tv.load_library()
-    dev = torch.device("cuda:0")
     if args.budget_table:
-        budget_table(args, dev)
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        budget_table(args, torch.device("cuda:0"))
         return
     seed = seed_for(args.config) if args.seed is None else args.seed
     t0 = time.time()
     wl = make_workload(args.config, seed=seed)
+    if args.table_tokens > 0:
+        widen_table(wl, args.table_tokens)
     gen_s = time.time() - t0
+    # the CPU oracle first: its worker processes are forked before the GPU is touched
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seconds)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tv.load_library()
+    dev = torch.device("cuda:0")
     B, Nmax, V = wl.batch, wl.n_max, wl.vocab
     n_total = int(wl.n_nodes.sum())
     esize = 2 if wl.dtype == "bf16" else 4
@@ -294,14 +306,22 @@ def main():
     del pristine_k, pristine_v
 
     # ---- whole-step timing -------------------------------------------------
-    def time_steps(fn):
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for i in range(args.steps):
-            fn(copies[i % ncopies])
-        ev1.record()
+    # A spin kernel holds the stream while the host enqueues the timed calls, so
+    # the events bracket GPU execution only (gated_us_per_call); the stream is
+    # synchronised on both sides of the timed region.
+    def spin_cycles_per_s():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record()
+        torch.cuda._sleep(20_000_000)
+        b.record()
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / args.steps
+        return 20_000_000 / (a.elapsed_time(b) * 1e-3)
+
+    cyc_per_s = spin_cycles_per_s()
+
+    def time_steps(fn):
+        return gated_us_per_call(lambda i: fn(copies[i % ncopies]), args.steps, cyc_per_s) * 1e-3
 
     def warm(fn):
         for i in range(args.warmup):
@@ -318,20 +338,31 @@ def main():
     warm(step)
     ms_step = time_steps(step)
 
-    # ---- per-kernel timing (back-to-back calls on rotating copies) ----------
-    # A spin kernel holds the stream while the host enqueues all calls, so the
-    # events bracket GPU execution only (small entry points are otherwise
-    # limited by the host's launch rate).
-    def spin_cycles_per_s():
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(1000)
-        a.record()
-        torch.cuda._sleep(20_000_000)
-        b.record()
+    # the same step replayed as HIP graphs (one per rotating copy, captured on a
+    # side stream after an eager warm-up there, so the captured calls reuse that
+    # stream's prepared workspaces)
+    ms_step_graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in copies:
+                step(c)
+        side.synchronize()
+        graphs = []
+        for c in copies:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(c)
+            graphs.append(g)
         torch.cuda.synchronize()
-        return 20_000_000 / (a.elapsed_time(b) * 1e-3)
+        for i in range(args.warmup):
+            graphs[i % ncopies].replay()
+        torch.cuda.synchronize()
+        ms_step_graph = gated_us_per_call(lambda i: graphs[i % ncopies].replay(), args.steps, cyc_per_s) * 1e-3
+        del graphs
 
-    cyc_per_s = spin_cycles_per_s()
+    # ---- per-kernel timing (back-to-back calls on rotating copies) ----------
 
     def time_calls(fn, reps):
         for i in range(min(reps, 5)):
@@ -373,9 +404,21 @@ def main():
             kids = [c for c in range(1, nb) if par[c] == u]
             passes += kids.index(pth[j + 1]) if j + 1 < L else len(kids)
     row = V * 4
-    # every target row is read (status checks and draws) and the draft row of
-    # every node with children; rejections re-use the rows held on chip
-    verify_bytes = int(n.sum() * row + internal * row)
+    # The algorithm reads every target row and the draft row of every node with
+    # children once (statistics and status checks), then both rows again for
+    # each residual pass on the accepted path (a rejected sibling before each
+    # accepted child, every child of the last node) and for the final draw (the
+    # target row, and the draft row when the last node has children).  The
+    # kernels hold the rows on chip across those passes (vocabularies up to
+    # 131072), so their HBM traffic stays near the first term.
+    draw_rows = 0
+    for b in range(B):
+        nb = int(n[b])
+        L = int(plen0[b])
+        last = int(path0[b, L - 1]) if L > 0 else 0
+        draw_rows += 2 if any(int(wl.parent[b, c]) == last for c in range(1, nb)) else 1
+    verify_first_bytes = int(n.sum() * row + internal * row)
+    verify_bytes = verify_first_bytes + int((2 * passes + draw_rows) * row)
     greedy_bytes = int(n.sum() * row)
     compact_bytes = int(2 * 2 * plen0.astype(np.int64).sum() * Hkv * D * esize)
 
@@ -423,10 +466,7 @@ def main():
     # tree construction on the GPU, timed before any host-side oracle work
     constr = None if args.no_construction else bench_construction(args, dev, cyc_per_s)
 
-    # ---- CPU oracle baseline ------------------------------------------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+    accept = acceptance_stats(args, dev, tv, make_workload)
 
     value = n_total / (ms_step * 1e-3)
     line = {
@@ -439,6 +479,7 @@ def main():
         "ms_per_step": ms_step,
         "step": "tree_attn_forward + tree_verify_stochastic_compact",
         "ms_per_step_separate_calls": ms_step_separate,
+        "ms_per_step_graph": ms_step_graph,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -447,6 +488,7 @@ def main():
         "config": {"workload": args.config, "batch": B, "tree_nodes": n_total, "n_max": Nmax,
                    "prefix_len_total": int(P.sum()), "q_heads": H, "kv_heads": Hkv, "head_dim": D,
                    "vocab": V, "kv_dtype": wl.dtype, "verify": "stochastic", "seed": seed,
+                   "table_tokens": int(wl.max_blocks * wl.block_size),
                    "rotating_copies": ncopies, "bytes_per_copy": copy_bytes},
         "roofline": roofline(dominant),
         "tree_attn_roofline": roofline("tree_attn"),
@@ -457,6 +499,8 @@ def main():
                    "nodes_per_s": n_total / (us_greedy * 1e-6)},
         "accepted_mean": float(plen0.mean() - 1),
         "rejection_passes_on_path": passes,
+        "verify_bytes_first_reads": verify_first_bytes,
+        "acceptance": accept,
         "cpu_baseline": cpu,
         "input_generation_s": round(gen_s, 2),
     }
@@ -857,47 +901,152 @@ def mfma_summary(run_dir: str, workload: str):
     return table
 
 
-def cpu_baseline(wl, seconds: float):
-    """The oracle, unmodified, timed on the host on the workload's first request(s):
-    tree attention for every (node, q-head) row, stochastic verification and KV
-    compaction, repeated until `seconds` have elapsed; single BLAS thread."""
+def widen_table(wl, tokens: int):
+    """Give every request a block table of ceil(tokens / block) entries (-1 past
+    the blocks it owns): a table sized for a longer context than it uses."""
+    mb = max(wl.max_blocks, -(-tokens // wl.block_size))
+    t = np.full((wl.batch, mb), -1, dtype=np.int32)
+    t[:, :wl.max_blocks] = wl.block_table
+    wl.block_table = t
+    wl.max_blocks = mb
+    return wl
+
+
+def acceptance_stats(args, dev, tv, make_workload):
+    """Accepted length per round over several seeds of the workload: the
+    histogram of K (accepted drafts; a round emits K + 1 tokens), P(K >= k) and
+    the acceptance rate by depth (tests of a child at depth d that accept, over
+    all tests at depth d), from stochastic verification on the GPU."""
+    import torch
+    from tree_verification_amd.workloads import seed_for
+    hist, tested, accepted = {}, {}, {}
+    ks = []
+    seeds = [seed_for(args.config, extra=1 + i) for i in range(max(0, args.accept_seeds))]
+    for sd in seeds:
+        wl = make_workload(args.config, seed=sd)
+        f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        p, l, _, st = tv.tree_verify_stochastic(f(wl.target_logits), f(wl.draft_logits), f(wl.tokens),
+                                                f(wl.parent), f(wl.n_nodes), f(wl.u_accept), f(wl.u_sample))
+        torch.cuda.synchronize()
+        p, l, st = p.cpu().numpy(), l.cpu().numpy(), st.cpu().numpy()
+        for b in range(wl.batch):
+            if st[b]:
+                continue
+            L = int(l[b])
+            K = L - 1
+            ks.append(K)
+            hist[K] = hist.get(K, 0) + 1
+            n = int(wl.n_nodes[b])
+            par = wl.parent[b, :n]
+            for j in range(L):
+                u = int(p[b, j])
+                if any(int(par[c]) == u for c in range(1, n)):
+                    tested[j + 1] = tested.get(j + 1, 0) + 1
+                    if j < K:
+                        accepted[j + 1] = accepted.get(j + 1, 0) + 1
+        del wl
+    if not ks:
+        return None
+    ks = np.asarray(ks)
+    kmax = int(ks.max())
+    return {"seeds": seeds, "rounds": int(len(ks)),
+            "accepted_len_hist": {str(k): hist[k] for k in sorted(hist)},
+            "mean_accepted": float(ks.mean()), "mean_tokens_per_round": float(ks.mean() + 1),
+            "p_k_at_least": [float((ks >= k).mean()) for k in range(1, kmax + 1)],
+            "acceptance_by_depth": {str(d): round(accepted.get(d, 0) / tested[d], 4) for d in sorted(tested)},
+            "tests_by_depth": {str(d): tested[d] for d in sorted(tested)}}
+
+
+def _cpu_request_step(args):
+    """One request-step of the oracle (worker process): tree attention for every
+    (node, q-head) row, stochastic verification and KV compaction of request b."""
+    b, = args
     from threadpoolctl import threadpool_limits
 
     from oracle.attention import tree_attention
     from oracle.kv import kv_compact
     from oracle.verify import verify_stochastic
-
-    reqs = []
-    done_nodes = 0
-    t0 = time.perf_counter()
-    b = 0
+    wl = _CPU_WL
+    sl = slice(b, b + 1)
     with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < seconds or not reqs:
-            sl = slice(b, b + 1)
-            outs, _ = tree_attention(wl.q[sl], wl.k_cache, wl.v_cache, wl.block_table[sl], wl.prefix_len[sl],
-                                     wl.n_nodes[sl], wl.parent[sl], n_q_heads=wl.n_q_heads,
-                                     n_kv_heads=wl.n_kv_heads, block_size=wl.block_size,
-                                     num_blocks=wl.num_blocks, n_max=wl.n_max, sm_scale=wl.sm_scale)
-            paths, _, _, _ = verify_stochastic(wl.target_logits[sl], wl.draft_logits[sl], wl.tokens[sl],
-                                               wl.parent[sl], wl.n_nodes[sl], wl.u_accept[sl],
-                                               wl.u_sample[sl], wl.n_max)
-            pth = np.full((1, wl.n_max), -1, dtype=np.int32)
-            pth[0, :len(paths[0])] = paths[0]
-            kv_compact(wl.k_cache, wl.v_cache, wl.block_table[sl], wl.prefix_len[sl], pth,
-                       np.array([len(paths[0])]), block_size=wl.block_size, num_blocks=wl.num_blocks,
-                       n_max=wl.n_max)
-            done_nodes += int(wl.n_nodes[b])
-            reqs.append(b)
-            b = (b + 1) % wl.batch
-    el = time.perf_counter() - t0
+        tree_attention(wl.q[sl], wl.k_cache, wl.v_cache, wl.block_table[sl], wl.prefix_len[sl], wl.n_nodes[sl],
+                       wl.parent[sl], n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                       block_size=wl.block_size, num_blocks=wl.num_blocks, n_max=wl.n_max, sm_scale=wl.sm_scale)
+        paths, _, _, _ = verify_stochastic(wl.target_logits[sl], wl.draft_logits[sl], wl.tokens[sl],
+                                           wl.parent[sl], wl.n_nodes[sl], wl.u_accept[sl], wl.u_sample[sl],
+                                           wl.n_max)
+        pth = np.full((1, wl.n_max), -1, dtype=np.int32)
+        pth[0, :len(paths[0])] = paths[0]
+        kv_compact(wl.k_cache, wl.v_cache, wl.block_table[sl], wl.prefix_len[sl], pth, np.array([len(paths[0])]),
+                   block_size=wl.block_size, num_blocks=wl.num_blocks, n_max=wl.n_max)
+    return int(wl.n_nodes[b])
+
+
+_CPU_WL = None
+
+
+def cpu_info():
+    fields = {}
     try:
-        model = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
-    except (OSError, IndexError):
-        model = "unknown"
-    return {"value": done_nodes / el, "unit": "nodes/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(reqs)} request-steps of this workload (attention for every node and q-head, "
-                      f"stochastic verification, KV compaction), {el:.1f} s, 1 BLAS thread",
-            "cpu_model": model}
+        for line in open("/proc/cpuinfo"):
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields.setdefault(k.strip(), v.strip())
+    except OSError:
+        pass
+    model = fields.get("model name", "unknown")
+    return f"{model} (family {fields.get('cpu family', '?')}, model {fields.get('model', '?')}, " \
+           f"stepping {fields.get('stepping', '?')})"
+
+
+def blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        import numpy  # noqa: F401  (loads its BLAS)
+        libs = [f"{d.get('internal_api')} {d.get('version')}" for d in threadpool_info() if d.get("user_api") == "blas"]
+        return ", ".join(libs) or "unknown"
+    except Exception:
+        return "unknown"
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle, unmodified, on the host's cores: a process pool (one worker per
+    core of os.sched_getaffinity, at most 16, each with one BLAS thread) runs
+    request-steps of the workload (attention for every node and q-head,
+    stochastic verification, compaction) for about `seconds`; requests cycle
+    through the batch.  Must run before the GPU is initialised (fork)."""
+    import multiprocessing as mp
+    global _CPU_WL
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    _CPU_WL = wl
+    ctx = mp.get_context("fork")
+    done_nodes = 0
+    steps = 0
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        pending = []
+        b = 0
+        while True:
+            while len(pending) < 2 * cores and (time.perf_counter() - t0 < seconds or steps + len(pending) < cores):
+                pending.append(pool.apply_async(_cpu_request_step, ((b,),)))
+                b = (b + 1) % wl.batch
+            if not pending:
+                break
+            r = pending.pop(0)
+            done_nodes += r.get()
+            steps += 1
+            if time.perf_counter() - t0 >= seconds and steps >= cores:
+                for r in pending:
+                    done_nodes += r.get()
+                    steps += 1
+                break
+    el = time.perf_counter() - t0
+    _CPU_WL = None
+    return {"value": done_nodes / el, "unit": "nodes/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} request-steps of this workload (attention for every node and q-head, "
+                      f"stochastic verification, KV compaction) on a pool of {cores} worker processes, "
+                      f"{el:.1f} s, one BLAS thread each",
+            "cpu_model": cpu_info(), "blas": blas_info()}
 
 
 if __name__ == "__main__":

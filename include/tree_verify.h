@@ -21,13 +21,15 @@
  *     bounds.
  *   - `workspace` is caller-owned device scratch of at least the size the
  *     matching *_workspace_size() returns for the call's descriptor.  The
- *     stochastic verifier's workspace holds exchange slots and flags whose
- *     layout depends on the descriptor: zero-fill it before its first use with
- *     a given descriptor (and again before reuse with another one); every call
- *     leaves it at zero again, so repeated calls with the same descriptor need
- *     no clearing.  The greedy verifier's and the attention's workspaces hold
- *     only per-call results and need no initialisation.  Two calls that may
- *     run concurrently must use distinct workspaces.
+ *     stochastic verifier's workspace holds exchange slots that must start at
+ *     zero: prepare it once with tree_verify_workspace_init (every call leaves
+ *     the slots at zero again, so later calls need nothing).  A workspace that
+ *     was not prepared, or was prepared with fewer bytes than the call needs,
+ *     is detected on the device from its header and fails every request with
+ *     TV_REQ_BAD_WORKSPACE; nothing of it is read as exchange data.  The
+ *     greedy verifier's and the attention's workspaces hold only per-call
+ *     results and need no preparation.  Two calls that may run concurrently
+ *     must use distinct workspaces.
  *   - Node ids: a tree of n nodes is a parent array with parent[0] = -1 (node 0
  *     is the root: the last token already emitted) and 0 <= parent[i] < i.
  *     Rows are padded to n_max; padding rows are neither read nor written.
@@ -65,7 +67,8 @@ enum {
   TV_REQ_TREE_OVERFLOW = 128, /* a constructed tree would need more than n_max nodes */
   TV_REQ_BAD_LEN = 256,     /* a candidate length, frontier count or frontier node id out of range */
   TV_REQ_POOL_EXHAUSTED = 512, /* the block pool cannot serve an allocation, or a release would overfill it */
-  TV_REQ_BAD_PROB = 1024    /* an acceptance probability that is NaN or outside [0, 1] (tree budget) */
+  TV_REQ_BAD_PROB = 1024,   /* an acceptance probability that is NaN or outside [0, 1] (tree budget) */
+  TV_REQ_BAD_WORKSPACE = 2048 /* the stochastic verifier's workspace was not initialised for this call */
 };
 
 /* ---- element types ------------------------------------------------------ */
@@ -134,6 +137,13 @@ typedef struct tv_verify_desc {
 /* Bytes of workspace either verifier needs for `desc`.  The two verifiers lay
  * their workspaces out differently: give each its own buffer. */
 size_t tree_verify_workspace_size(const tv_verify_desc* desc);
+
+/* Prepares a stochastic verifier's workspace (256-byte aligned, at least
+ * tree_verify_workspace_size bytes for the descriptors it will serve): zeroes
+ * it and writes the header the verifier checks.  Enqueued on `stream`.
+ * TV_ERR_WORKSPACE for a null or too small buffer, TV_ERR_INVALID_ARG when
+ * it is not 256-byte aligned. */
+int tree_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Greedy verification ([guide] "Greedy Verification Algorithm"): from the root,
  * t = argmax_w target_logits[b][u][w] (lowest index among equal maxima); move to

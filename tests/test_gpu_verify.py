@@ -205,3 +205,43 @@ def test_repeat_calls_identical():
     b = gpu_greedy(d)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_stochastic_unprepared_workspace_is_reported():
+    """A workspace that tree_verify_workspace_init never prepared (here: random
+    bytes, as a reused allocation would hold) fails every request with
+    TV_REQ_BAD_WORKSPACE instead of reading its bytes as exchange data; once
+    prepared, the same buffer gives the oracle's results."""
+    wl = make_workload("llama8b", seed=51, vocab=30011, n_nodes=20, batch=3)
+    d = DevWorkload(wl)
+    from tree_verification_amd.binding import VerifyDesc, load_library
+    lib = load_library()
+    desc = VerifyDesc()
+    desc.batch, desc.n_max, desc.vocab, desc.temperature = wl.batch, wl.n_max, wl.vocab, 1.0
+    import ctypes
+    need = lib.tree_verify_workspace_size(ctypes.byref(desc))
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda:0")
+    _, l, _, s = tv.tree_verify_stochastic(d.target, d.draft, d.tokens, d.parent, d.n_nodes, d.u_accept,
+                                           d.u_sample, ws=ws)
+    torch.cuda.synchronize()
+    assert list(s.cpu().numpy()) == [tv.REQ_BAD_WORKSPACE] * wl.batch
+    assert not l.cpu().numpy().any()
+    tv.init_verify_workspace(ws)
+    for _ in range(2):   # and again: every call leaves the slots at zero
+        p, l, t, s = tv.tree_verify_stochastic(d.target, d.draft, d.tokens, d.parent, d.n_nodes, d.u_accept,
+                                               d.u_sample, ws=ws)
+        torch.cuda.synchronize()
+        paths, outs, traces, st = verify_stochastic(wl.target_logits, wl.draft_logits, wl.tokens, wl.parent,
+                                                    wl.n_nodes, wl.u_accept, wl.u_sample, wl.n_max)
+        assert not s.cpu().numpy().any()
+        gp, gl, gt = p.cpu().numpy(), l.cpu().numpy(), t.cpu().numpy()
+        for b in range(wl.batch):
+            L = int(gl[b])
+            assert divergence_in_band(traces[b], paths[b], outs[b], gp[b, :L], gt[b, :L]), b
+    # a prepared buffer that is too small for the call's layout is refused as well
+    small = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    tv.init_verify_workspace(small[:512])
+    _, _, _, s = tv.tree_verify_stochastic(d.target, d.draft, d.tokens, d.parent, d.n_nodes, d.u_accept,
+                                           d.u_sample, ws=small)
+    torch.cuda.synchronize()
+    assert list(s.cpu().numpy()) == [tv.REQ_BAD_WORKSPACE] * wl.batch

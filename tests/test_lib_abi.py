@@ -257,3 +257,9 @@ def test_greedy_noalloc_rejects_oversized_scratch(lib):
     assert rc == -3
     d.batch = 0
     assert lib.tree_verify_greedy_noalloc(ctypes.byref(d), *fake, None) == 0
+
+
+def test_workspace_init_argument_checks(lib):
+    assert lib.tree_verify_workspace_init(None, 4096, None) == -3
+    assert lib.tree_verify_workspace_init(ctypes.c_void_p(4096), 255, None) == -3
+    assert lib.tree_verify_workspace_init(ctypes.c_void_p(4096 + 16), 4096, None) == -1

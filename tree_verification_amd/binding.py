@@ -31,6 +31,7 @@ REQ_TREE_OVERFLOW = 128
 REQ_BAD_LEN = 256
 REQ_POOL_EXHAUSTED = 512
 REQ_BAD_PROB = 1024
+REQ_BAD_WORKSPACE = 2048
 
 
 class AttnDesc(ctypes.Structure):
@@ -73,6 +74,7 @@ _SIGS = {
     "tree_verify_greedy": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 9 + [_SZ, _P]),
     "tree_verify_stochastic": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 12 + [_SZ, _P]),
     "tree_verify_greedy_noalloc": (ctypes.c_int, [ctypes.POINTER(VerifyDesc)] + [_P] * 9),
+    "tree_verify_workspace_init": (ctypes.c_int, [_P, _SZ, _P]),
     "tree_verify_greedy_noalloc_max_scratch": (_SZ, []),
     "kv_compact_accepted": (ctypes.c_int, [ctypes.POINTER(AttnDesc)] + [_P] * 10),
     "tree_verify_stochastic_compact": (ctypes.c_int, [ctypes.POINTER(VerifyDesc), ctypes.POINTER(AttnDesc)]
@@ -139,10 +141,9 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-# Workspaces: a workspace belongs to the descriptor it was sized for (its
-# counters sit at descriptor-dependent offsets).  Each (device, stream, kind,
-# descriptor) gets its own buffer, zero-filled once; every call leaves its
-# counters at zero again.
+# Workspaces: each (device, stream, kind, descriptor) gets its own buffer.  The
+# stochastic verifier's is prepared once with tree_verify_workspace_init (every
+# call leaves its exchange slots at zero again).
 _ws: dict = {}
 
 
@@ -158,7 +159,17 @@ def workspace(nbytes: int, device: torch.device, kind: str, desc=None) -> torch.
     buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if kind == "stochastic":
+            init_verify_workspace(buf)
         _ws[key] = buf
+    return buf
+
+
+def init_verify_workspace(buf: torch.Tensor) -> torch.Tensor:
+    """Prepare a stochastic verifier workspace (uint8 GPU tensor) in place."""
+    lib = load_library()
+    rc = lib.tree_verify_workspace_init(_ptr(buf), buf.numel(), _stream(buf.device))
+    _check(rc, "tree_verify_workspace_init")
     return buf
 
 

@@ -346,6 +346,8 @@ struct StochParams {
   int32_t* out_tokens;
   int32_t* status;
   // workspace
+  const unsigned long long* header;   // [2]: kWsMagic, bytes zero-filled by tree_verify_workspace_init
+  unsigned long long need;            // bytes this call's layout uses (header included)
   unsigned long long* xch;   // [nodes][kMaxTeam]    member masses after child `node` is rejected
   unsigned long long* sxch;  // [nodes][kMaxTeam][4] member (max, sum) of the target and draft rows
   int* node_flags;           // [nodes]  NONFINITE / BAD_TOKEN / TIMEOUT
@@ -357,6 +359,20 @@ struct StochParams {
   float k2hi, k2lo;                  // log2(e) / T as a float32 head and tail
   double invT_d;
 };
+
+// The stochastic verifier's workspace starts with a header that
+// tree_verify_workspace_init writes after zero-filling the rest: a magic word
+// and the number of bytes it cleared.  Exchange slots mark a published value
+// with their top bit and every call leaves them at zero, so a workspace that
+// was never initialised (or is too small for this call's layout) must not be
+// used; every workgroup checks the header (two scalar loads issued with the
+// request sizes) and such a request gets TV_REQ_BAD_WORKSPACE.
+constexpr unsigned long long kWsMagic = 0x7476777370616365ull;
+constexpr size_t kWsHeader = 256;
+
+__device__ __forceinline__ bool ws_ok(const StochParams& p) {
+  return p.header[0] == kWsMagic && p.header[1] >= p.need;
+}
 
 // exp(d / T) for d <= 0 in float32: exp2 of d * log2(e) / T, with the product
 // carried as head + tail (the tail from an exact fma residual) so that rounding
@@ -607,6 +623,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
   const int b = k / p.n_max, u = k % p.n_max;
   const int n = p.n_nodes[b];
   if (n < 1 || n > p.n_max || u >= n) return;
+  if (!ws_ok(p)) return;   // the chase reports it; no slot is read or written
   const int32_t* par = p.parent + (size_t)b * p.n_max;
   const int32_t* tok = p.tokens + (size_t)b * p.n_max;
   const float* zp_row = p.target + (size_t)k * p.V;
@@ -957,6 +974,7 @@ struct ChaseSmem {
 // holds node t's).
 struct ChaseLoads {
   int fl, acc, fin, tk, pv, n;
+  bool ws_ok;
 };
 
 // Issues every load of request b's rows at once, before n_nodes is known (rows
@@ -964,7 +982,7 @@ struct ChaseLoads {
 __device__ __forceinline__ ChaseLoads chase_load(const StochParams& p, int b) {
   const int t = threadIdx.x;
   const size_t kv = (size_t)b * p.n_max + t;
-  ChaseLoads c{0, -1, 0, 0, -1, 0};
+  ChaseLoads c{0, -1, 0, 0, -1, 0, ws_ok(p)};
   if (t < p.n_max) {
     c.fl = p.node_flags[kv];
     c.acc = p.node_acc[kv];
@@ -987,6 +1005,13 @@ __device__ int chase_request(const StochParams& p, ChaseSmem& sm, int b, const C
   if (n < 1 || n > p.n_max) {
     if (t == 0) {
       p.status[b] = TV_REQ_BAD_NNODES;
+      p.path_len[b] = 0;
+    }
+    return 0;
+  }
+  if (!c.ws_ok) {   // nothing of the workspace is trusted, read or cleared
+    if (t == 0) {
+      p.status[b] = TV_REQ_BAD_WORKSPACE;
       p.path_len[b] = 0;
     }
     return 0;
@@ -1125,7 +1150,7 @@ VerifyLayout layout(const tv_verify_desc* d) {
   L.g_bad = o;
   o = tv_align_up(o + nodes * L.gchunks * sizeof(int), 256);
   L.greedy_bytes = o;
-  o = 0;
+  o = kWsHeader;
   L.xch = o;
   o = tv_align_up(o + nodes * kMaxTeam * sizeof(unsigned long long), 256);
   L.sxch = o;
@@ -1160,6 +1185,37 @@ TeamPlan plan_team(int chunks) {
 }
 
 }  // namespace
+
+namespace {
+
+// Zero-fills workspace bytes [kWsHeader, bytes) in 16-byte stores, then (one
+// thread) writes the header; the next kernel sees both.
+__global__ __launch_bounds__(256) void ws_init_kernel(unsigned char* ws, size_t bytes) {
+  const size_t n16 = (bytes - kWsHeader) / 16;
+  tv_u32x4* z = (tv_u32x4*)(ws + kWsHeader);
+  const tv_u32x4 zero = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    z[i] = zero;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    unsigned long long* h = (unsigned long long*)ws;
+    h[0] = kWsMagic;
+    h[1] = kWsHeader + n16 * 16;
+  }
+}
+
+}  // namespace
+
+extern "C" int tree_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || workspace_bytes < kWsHeader) return TV_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255) != 0) return TV_ERR_INVALID_ARG;
+  const size_t n16 = (workspace_bytes - kWsHeader) / 16;
+  size_t grid = (n16 + 255) / 256;
+  if (grid < 1) grid = 1;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(ws_init_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (unsigned char*)workspace,
+                     workspace_bytes);
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
 
 extern "C" size_t tree_verify_workspace_size(const tv_verify_desc* desc) {
   if (check_vdesc(desc) != TV_OK) return 0;
@@ -1309,6 +1365,8 @@ int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, c
   p.out_tokens = out_tokens;
   p.status = status;
   char* ws = (char*)workspace;
+  p.header = (const unsigned long long*)ws;
+  p.need = L.stoch_bytes;
   p.xch = (unsigned long long*)(ws + L.xch);
   p.sxch = (unsigned long long*)(ws + L.sxch);
   p.node_flags = (int*)(ws + L.flg);
