@@ -34,6 +34,18 @@
  *     is the root: the last token already emitted) and 0 <= parent[i] < i.
  *     Rows are padded to n_max; padding rows are neither read nor written.
  *   - Integer types are int32_t; bf16 tensors are passed as raw 16-bit words.
+ *
+ * Environment (read once per process, at the first call):
+ *   TV_TRACE=1  every entry point is a named roctx range when the roctx
+ *               library can be loaded (rocprofv3 --marker-trace records them);
+ *               otherwise nothing happens.
+ *   TV_DEBUG=1  entry points that take trees or block tables first copy them
+ *               to the host and print each malformed request on stderr
+ *               ("[tv debug] <entry>: request <b>: ..."), then launch as usual
+ *               (the status flags are unchanged), and afterwards synchronise
+ *               `stream`, returning TV_ERR_HIP when the GPU reported an error.
+ *               This synchronises, so it must not be set for calls made under
+ *               stream capture.
  */
 #ifndef TREE_VERIFY_H
 #define TREE_VERIFY_H

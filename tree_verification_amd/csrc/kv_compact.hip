@@ -15,7 +15,7 @@ __global__ __launch_bounds__(128) void compact_kernel(TvCompactArgs p, const int
 
 }  // namespace
 
-extern "C" int kv_compact_accepted(const tv_attn_desc* desc, void* k_cache, void* v_cache,
+static int kv_compact_accepted_impl(const tv_attn_desc* desc, void* k_cache, void* v_cache,
                                    const int32_t* block_table, const int32_t* prefix_len,
                                    const int32_t* path, const int32_t* path_len, int32_t* src_pos,
                                    int32_t* new_len, int32_t* status, hipStream_t stream) {
@@ -32,4 +32,12 @@ extern "C" int kv_compact_accepted(const tv_attn_desc* desc, void* k_cache, void
   else
     hipLaunchKernelGGL(compact_kernel<float>, dim3((unsigned)grid), dim3(128), 0, stream, p, path, path_len);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+extern "C" int kv_compact_accepted(const tv_attn_desc* desc, void* k_cache, void* v_cache,
+                                   const int32_t* block_table, const int32_t* prefix_len,
+                                   const int32_t* path, const int32_t* path_len, int32_t* src_pos,
+                                   int32_t* new_len, int32_t* status, hipStream_t stream) {
+  TV_TRACE_SCOPE("kv_compact_accepted");
+  return tv_debug_finish("kv_compact_accepted", kv_compact_accepted_impl(desc, k_cache, v_cache, block_table, prefix_len, path, path_len, src_pos, new_len, status, stream), stream);
 }

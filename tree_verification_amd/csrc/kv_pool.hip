@@ -151,7 +151,7 @@ int check_pool_desc(const tv_attn_desc* d) {
 
 }  // namespace
 
-extern "C" int kv_alloc_tree_blocks(const tv_attn_desc* desc, int32_t* block_table, int32_t* n_blocks,
+static int kv_alloc_tree_blocks_impl(const tv_attn_desc* desc, int32_t* block_table, int32_t* n_blocks,
                                     const int32_t* prefix_len, const int32_t* n_nodes, const int32_t* free_ids,
                                     int32_t* free_count, int32_t* spec_from, int32_t* status, hipStream_t stream) {
   const int rc = check_pool_desc(desc);
@@ -176,7 +176,14 @@ extern "C" int kv_alloc_tree_blocks(const tv_attn_desc* desc, int32_t* block_tab
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
-extern "C" int kv_release_blocks(const tv_attn_desc* desc, int32_t* block_table, int32_t* n_blocks,
+extern "C" int kv_alloc_tree_blocks(const tv_attn_desc* desc, int32_t* block_table, int32_t* n_blocks,
+                                    const int32_t* prefix_len, const int32_t* n_nodes, const int32_t* free_ids,
+                                    int32_t* free_count, int32_t* spec_from, int32_t* status, hipStream_t stream) {
+  TV_TRACE_SCOPE("kv_alloc_tree_blocks");
+  return tv_debug_finish("kv_alloc_tree_blocks", kv_alloc_tree_blocks_impl(desc, block_table, n_blocks, prefix_len, n_nodes, free_ids, free_count, spec_from, status, stream), stream);
+}
+
+static int kv_release_blocks_impl(const tv_attn_desc* desc, int32_t* block_table, int32_t* n_blocks,
                                  const int32_t* new_len, int32_t* free_ids, int32_t* free_count, int32_t* status,
                                  hipStream_t stream) {
   const int rc = check_pool_desc(desc);
@@ -196,4 +203,11 @@ extern "C" int kv_release_blocks(const tv_attn_desc* desc, int32_t* block_table,
   p.num_blocks = desc->num_blocks;
   hipLaunchKernelGGL(release_kernel, dim3(1), dim3(kPoolThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+extern "C" int kv_release_blocks(const tv_attn_desc* desc, int32_t* block_table, int32_t* n_blocks,
+                                 const int32_t* new_len, int32_t* free_ids, int32_t* free_count, int32_t* status,
+                                 hipStream_t stream) {
+  TV_TRACE_SCOPE("kv_release_blocks");
+  return tv_debug_finish("kv_release_blocks", kv_release_blocks_impl(desc, block_table, n_blocks, new_len, free_ids, free_count, status, stream), stream);
 }

@@ -1445,7 +1445,7 @@ extern "C" size_t tree_attn_workspace_size(const tv_attn_desc* desc) {
   return pl.bytes;
 }
 
-extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const void* k_cache,
+static int tree_attn_forward_impl(const tv_attn_desc* desc, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* block_table,
                                  const int32_t* prefix_len, const int32_t* n_nodes,
                                  const int32_t* parent, void* out, int32_t* status, void* workspace,
@@ -1511,4 +1511,17 @@ extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const 
     if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   }
   return TV_OK;
+}
+
+extern "C" int tree_attn_forward(const tv_attn_desc* desc, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table,
+                                 const int32_t* prefix_len, const int32_t* n_nodes,
+                                 const int32_t* parent, void* out, int32_t* status, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  TV_TRACE_SCOPE("tree_attn_forward");
+  if (tv_debug_enabled() && desc && desc->batch > 0) {
+    tv_debug_trees("tree_attn_forward", parent, n_nodes, desc->batch, desc->n_max, stream);
+    tv_debug_kv("tree_attn_forward", block_table, prefix_len, n_nodes, desc->batch, desc->max_blocks_per_seq, desc->block_size, desc->num_blocks, stream);
+  }
+  return tv_debug_finish("tree_attn_forward", tree_attn_forward_impl(desc, q, k_cache, v_cache, block_table, prefix_len, n_nodes, parent, out, status, workspace, workspace_bytes, stream), stream);
 }

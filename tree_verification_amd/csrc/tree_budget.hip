@@ -164,7 +164,7 @@ __global__ __launch_bounds__(64) void expected_len_kernel(BudgetParams p) {
 
 }  // namespace
 
-extern "C" int tree_expected_accept_length(const tv_budget_desc* desc, const int32_t* parent, const int32_t* n_nodes,
+static int tree_expected_accept_length_impl(const tv_budget_desc* desc, const int32_t* parent, const int32_t* n_nodes,
                                            const double* accept_prob, double* reach, double* expected_len,
                                            int32_t* status, hipStream_t stream) {
   if (!desc || desc->batch < 0) return TV_ERR_INVALID_ARG;
@@ -182,6 +182,13 @@ extern "C" int tree_expected_accept_length(const tv_budget_desc* desc, const int
   p.n_max = desc->n_max;
   hipLaunchKernelGGL(expected_len_kernel, dim3(desc->batch), dim3(64), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+extern "C" int tree_expected_accept_length(const tv_budget_desc* desc, const int32_t* parent, const int32_t* n_nodes,
+                                           const double* accept_prob, double* reach, double* expected_len,
+                                           int32_t* status, hipStream_t stream) {
+  TV_TRACE_SCOPE("tree_expected_accept_length");
+  return tv_debug_finish("tree_expected_accept_length", tree_expected_accept_length_impl(desc, parent, n_nodes, accept_prob, reach, expected_len, status, stream), stream);
 }
 
 extern "C" int tree_budget_select(int32_t n_batch_sizes, int32_t n_shapes, const double* al, const double* itl,

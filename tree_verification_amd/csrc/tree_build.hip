@@ -379,7 +379,7 @@ ExpandLayout expand_layout(const tv_expand_desc* d) {
 
 }  // namespace
 
-extern "C" int tree_merge_candidates(const tv_merge_desc* desc, const int32_t* cand_tokens,
+static int tree_merge_candidates_impl(const tv_merge_desc* desc, const int32_t* cand_tokens,
                                      const int32_t* cand_len, const int32_t* root_token, int32_t* tokens,
                                      int32_t* parent, int32_t* n_nodes, int32_t* node_of, int32_t* status,
                                      hipStream_t stream) {
@@ -406,12 +406,20 @@ extern "C" int tree_merge_candidates(const tv_merge_desc* desc, const int32_t* c
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
+extern "C" int tree_merge_candidates(const tv_merge_desc* desc, const int32_t* cand_tokens,
+                                     const int32_t* cand_len, const int32_t* root_token, int32_t* tokens,
+                                     int32_t* parent, int32_t* n_nodes, int32_t* node_of, int32_t* status,
+                                     hipStream_t stream) {
+  TV_TRACE_SCOPE("tree_merge_candidates");
+  return tv_debug_finish("tree_merge_candidates", tree_merge_candidates_impl(desc, cand_tokens, cand_len, root_token, tokens, parent, n_nodes, node_of, status, stream), stream);
+}
+
 extern "C" size_t tree_expand_workspace_size(const tv_expand_desc* desc) {
   if (check_expand(desc) != TV_OK) return 0;
   return expand_layout(desc).bytes;
 }
 
-extern "C" int tree_expand_topk(const tv_expand_desc* desc, const float* draft_logits, const int32_t* frontier,
+static int tree_expand_topk_impl(const tv_expand_desc* desc, const float* draft_logits, const int32_t* frontier,
                                 const int32_t* n_frontier, int32_t* tokens, int32_t* parent, int32_t* n_nodes,
                                 int32_t* new_frontier, int32_t* n_new, int32_t* status, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
@@ -451,4 +459,12 @@ extern "C" int tree_expand_topk(const tv_expand_desc* desc, const float* draft_l
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   hipLaunchKernelGGL(topk_append_kernel, dim3((unsigned)desc->batch), dim3(kTopkThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+extern "C" int tree_expand_topk(const tv_expand_desc* desc, const float* draft_logits, const int32_t* frontier,
+                                const int32_t* n_frontier, int32_t* tokens, int32_t* parent, int32_t* n_nodes,
+                                int32_t* new_frontier, int32_t* n_new, int32_t* status, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  TV_TRACE_SCOPE("tree_expand_topk");
+  return tv_debug_finish("tree_expand_topk", tree_expand_topk_impl(desc, draft_logits, frontier, n_frontier, tokens, parent, n_nodes, new_frontier, n_new, status, workspace, workspace_bytes, stream), stream);
 }

@@ -1205,7 +1205,7 @@ __global__ __launch_bounds__(256) void ws_init_kernel(unsigned char* ws, size_t 
 
 }  // namespace
 
-extern "C" int tree_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static int tree_verify_workspace_init_impl(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace || workspace_bytes < kWsHeader) return TV_ERR_WORKSPACE;
   if (((uintptr_t)workspace & 255) != 0) return TV_ERR_INVALID_ARG;
   const size_t n16 = (workspace_bytes - kWsHeader) / 16;
@@ -1215,6 +1215,11 @@ extern "C" int tree_verify_workspace_init(void* workspace, size_t workspace_byte
   hipLaunchKernelGGL(ws_init_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (unsigned char*)workspace,
                      workspace_bytes);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+extern "C" int tree_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  TV_TRACE_SCOPE("tree_verify_workspace_init");
+  return tv_debug_finish("tree_verify_workspace_init", tree_verify_workspace_init_impl(workspace, workspace_bytes, stream), stream);
 }
 
 extern "C" size_t tree_verify_workspace_size(const tv_verify_desc* desc) {
@@ -1295,7 +1300,7 @@ int scratch_ptr(void** out) {
 
 }  // namespace
 
-extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
+static int tree_verify_greedy_impl(const tv_verify_desc* desc, const float* target_logits,
                                   const int32_t* tokens, const int32_t* parent,
                                   const int32_t* n_nodes, int32_t* path, int32_t* path_len,
                                   int32_t* out_tokens, int32_t* status, void* workspace,
@@ -1311,9 +1316,21 @@ extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* targe
                        (char*)workspace, L, stream);
 }
 
+extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
+                                  const int32_t* tokens, const int32_t* parent,
+                                  const int32_t* n_nodes, int32_t* path, int32_t* path_len,
+                                  int32_t* out_tokens, int32_t* status, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  TV_TRACE_SCOPE("tree_verify_greedy");
+  if (tv_debug_enabled() && desc && desc->batch > 0) {
+    tv_debug_trees("tree_verify_greedy", parent, n_nodes, desc->batch, desc->n_max, stream);
+  }
+  return tv_debug_finish("tree_verify_greedy", tree_verify_greedy_impl(desc, target_logits, tokens, parent, n_nodes, path, path_len, out_tokens, status, workspace, workspace_bytes, stream), stream);
+}
+
 extern "C" size_t tree_verify_greedy_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
 
-extern "C" int tree_verify_greedy_noalloc(const tv_verify_desc* desc, const float* target_logits,
+static int tree_verify_greedy_noalloc_impl(const tv_verify_desc* desc, const float* target_logits,
                                           const int32_t* tokens, const int32_t* parent,
                                           const int32_t* n_nodes, int32_t* path, int32_t* path_len,
                                           int32_t* out_tokens, int32_t* status, hipStream_t stream) {
@@ -1329,6 +1346,17 @@ extern "C" int tree_verify_greedy_noalloc(const tv_verify_desc* desc, const floa
   if (rc != TV_OK) return rc;
   return launch_greedy(desc, target_logits, tokens, parent, n_nodes, path, path_len, out_tokens, status,
                        (char*)ws, L, stream);
+}
+
+extern "C" int tree_verify_greedy_noalloc(const tv_verify_desc* desc, const float* target_logits,
+                                          const int32_t* tokens, const int32_t* parent,
+                                          const int32_t* n_nodes, int32_t* path, int32_t* path_len,
+                                          int32_t* out_tokens, int32_t* status, hipStream_t stream) {
+  TV_TRACE_SCOPE("tree_verify_greedy_noalloc");
+  if (tv_debug_enabled() && desc && desc->batch > 0) {
+    tv_debug_trees("tree_verify_greedy_noalloc", parent, n_nodes, desc->batch, desc->n_max, stream);
+  }
+  return tv_debug_finish("tree_verify_greedy_noalloc", tree_verify_greedy_noalloc_impl(desc, target_logits, tokens, parent, n_nodes, path, path_len, out_tokens, status, stream), stream);
 }
 
 namespace {
@@ -1411,7 +1439,7 @@ int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, c
 
 }  // namespace
 
-extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* target_logits,
+static int tree_verify_stochastic_impl(const tv_verify_desc* desc, const float* target_logits,
                                       const float* draft_logits, const int32_t* tokens,
                                       const int32_t* parent, const int32_t* n_nodes,
                                       const float* u_accept, const float* u_sample, int32_t* path,
@@ -1428,7 +1456,20 @@ extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* t
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
-extern "C" int tree_verify_stochastic_compact(const tv_verify_desc* desc, const tv_attn_desc* kv_desc,
+extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* target_logits,
+                                      const float* draft_logits, const int32_t* tokens,
+                                      const int32_t* parent, const int32_t* n_nodes,
+                                      const float* u_accept, const float* u_sample, int32_t* path,
+                                      int32_t* path_len, int32_t* out_tokens, int32_t* status,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  TV_TRACE_SCOPE("tree_verify_stochastic");
+  if (tv_debug_enabled() && desc && desc->batch > 0) {
+    tv_debug_trees("tree_verify_stochastic", parent, n_nodes, desc->batch, desc->n_max, stream);
+  }
+  return tv_debug_finish("tree_verify_stochastic", tree_verify_stochastic_impl(desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path, path_len, out_tokens, status, workspace, workspace_bytes, stream), stream);
+}
+
+static int tree_verify_stochastic_compact_impl(const tv_verify_desc* desc, const tv_attn_desc* kv_desc,
                                               const float* target_logits, const float* draft_logits,
                                               const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
                                               const float* u_accept, const float* u_sample, int32_t* path,
@@ -1465,4 +1506,21 @@ extern "C" int tree_verify_stochastic_compact(const tv_verify_desc* desc, const 
     hipLaunchKernelGGL(stoch_chase_compact_kernel<float>, dim3((unsigned)desc->batch), dim3(kChaseCompactThreads),
                        0, stream, p, c);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+}
+
+extern "C" int tree_verify_stochastic_compact(const tv_verify_desc* desc, const tv_attn_desc* kv_desc,
+                                              const float* target_logits, const float* draft_logits,
+                                              const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
+                                              const float* u_accept, const float* u_sample, int32_t* path,
+                                              int32_t* path_len, int32_t* out_tokens, int32_t* status,
+                                              void* k_cache, void* v_cache, const int32_t* block_table,
+                                              const int32_t* prefix_len, int32_t* src_pos, int32_t* new_len,
+                                              int32_t* kv_status, void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  TV_TRACE_SCOPE("tree_verify_stochastic_compact");
+  if (tv_debug_enabled() && desc && kv_desc && desc->batch > 0) {
+    tv_debug_trees("tree_verify_stochastic_compact", parent, n_nodes, desc->batch, desc->n_max, stream);
+    tv_debug_kv("tree_verify_stochastic_compact", block_table, prefix_len, n_nodes, kv_desc->batch, kv_desc->max_blocks_per_seq, kv_desc->block_size, kv_desc->num_blocks, stream);
+  }
+  return tv_debug_finish("tree_verify_stochastic_compact", tree_verify_stochastic_compact_impl(desc, kv_desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path, path_len, out_tokens, status, k_cache, v_cache, block_table, prefix_len, src_pos, new_len, kv_status, workspace, workspace_bytes, stream), stream);
 }

@@ -17,6 +17,34 @@ typedef uint32_t tv_u32x4 __attribute__((ext_vector_type(4)));
 // Number of compute units of the current device (cached per device).
 int tv_device_cu_count(int* cu_out);
 
+// ---- tracing and debug validation (host side, tv_api.hip) ------------------
+//
+// TV_TRACE=1 in the environment: every entry point is a roctx range (the
+// roctx library is loaded at run time when present; rocprofv3 --marker-trace
+// shows the ranges).  TV_DEBUG=1: entry points copy their tree and KV
+// metadata to the host, print every malformed request to stderr before
+// launching (the per-request status flags are produced as usual), and
+// synchronise after launching, returning TV_ERR_HIP when the GPU reported an
+// error.  Both are read once per process.
+struct TvTraceScope {
+  bool on;
+  explicit TvTraceScope(const char* name);
+  ~TvTraceScope();
+};
+#define TV_TRACE_SCOPE(name) TvTraceScope tv_trace_scope_(name)
+
+bool tv_debug_enabled();
+// Malformed trees (n_nodes outside [1, n_max], parent[0] != -1, parent[i]
+// outside [0, i)) reported on stderr; returns how many requests were reported.
+int tv_debug_trees(const char* entry, const int32_t* parent, const int32_t* n_nodes, int batch, int n_max,
+                   hipStream_t stream);
+// Requests whose positions [0, prefix_len + n_nodes) leave the block table or
+// name a block outside the pool, reported on stderr.
+int tv_debug_kv(const char* entry, const int32_t* block_table, const int32_t* prefix_len, const int32_t* n_nodes,
+                int batch, int max_blocks, int block_size, int num_blocks, hipStream_t stream);
+// After the launches: synchronise and turn a GPU error into TV_ERR_HIP (rc otherwise).
+int tv_debug_finish(const char* entry, int rc, hipStream_t stream);
+
 #define TV_HIP_TRY(expr)                    \
   do {                                      \
     if ((expr) != hipSuccess) return TV_ERR_HIP; \
