@@ -1,9 +1,11 @@
 // Token-tree verification for gfx950.
 //
-// Results pass between kernels at kernel boundaries, which order every global
-// write before the next kernel's reads; no workgroup issues a device-wide fence
-// (on this part an agent-scope fence writes back and invalidates the XCD's
-// whole L2).
+// Workgroups hand values to one another only through 64-bit words read and
+// written with agent-scope atomics (a word carries its own "written" or
+// "complete" marks, so no ordering between different addresses is needed);
+// everything else passes at kernel boundaries.  No workgroup issues a
+// device-wide fence (on this part an agent-scope fence writes back and
+// invalidates the XCD's whole L2).
 //
 // Greedy ([guide] "Greedy Verification Algorithm"):
 //   greedy_argmax_kernel  one workgroup per (node, 8192-logit chunk) reduces its
@@ -36,15 +38,18 @@
 //                         is at most two chunks keeps its exponentials on chip
 //                         across rejections.  Each node also makes the draw it
 //                         emits when no child is accepted: an inverse CDF over
-//                         member masses, chunk masses, then one chunk;
-//   stoch_chase_kernel    one workgroup per request: status, the root path and
-//                         its final token, and the exchange slots cleared for
-//                         the next call;
-//   stoch_chase_compact_kernel  the same chase, then the accepted path's KV
-//                         compaction ([guide] "Depth-First Flattening and KV
-//                         Cache Reuse") in the same workgroup (verify-and-compact
-//                         for up to four requests).
-// Vocabulary exponentials are float32 (exp_t), sums and the accept test float64.
+//                         member masses, chunk masses, then one chunk.  Every
+//                         member then ORs its part of the node's result into one
+//                         64-bit word and counts itself in on the request; the
+//                         workgroup that completes the count runs the chase:
+//                         status, the root path and its final token, every
+//                         exchange slot of the request cleared for the next call,
+//                         and for verify-and-compact (up to four requests) the
+//                         accepted path's KV compaction ([guide] "Depth-First
+//                         Flattening and KV Cache Reuse").  No second launch
+//                         waits on the nodes.
+// Vocabulary exponentials are float32 (exp_t), as is each entry's residual
+// bracket (residual_rel); sums, chunk factors and the accept test are float64.
 
 #include "tv_common.h"
 #include "tv_compact.h"
@@ -349,10 +354,8 @@ struct StochParams {
   const unsigned long long* header;   // [2]: kWsMagic, bytes zero-filled by tree_verify_workspace_init
   unsigned long long need;            // bytes this call's layout uses (header included)
   unsigned long long* xch;   // [nodes][kMaxTeam]    member masses after child `node` is rejected
-  unsigned long long* sxch;  // [nodes][kMaxTeam][4] member (max, sum) of the target and draft rows
-  int* node_flags;           // [nodes]  NONFINITE / BAD_TOKEN / TIMEOUT
-  int* node_acc;             // [nodes]  accepted child, -1 when none
-  int* node_tok;             // [nodes]  draw made when no child is accepted
+  unsigned long long* sxch;  // [nodes][chunks][4] chunk (max, sum) of the target and draft rows
+  unsigned long long* nword; // [nodes]  the node's result (see kNw*), zero between calls
   int prio_ticks;            // load delay per missing child below kPrioSteps, 100 MHz ticks (0: none)
   int xcd_teams;             // 1: the whole grid is resident; a team's members share an XCD
   int B, n_max, V, chunks, S, per;   // per = chunks per team member
@@ -370,45 +373,66 @@ struct StochParams {
 constexpr unsigned long long kWsMagic = 0x7476777370616365ull;
 constexpr size_t kWsHeader = 256;
 
+// A node's result word, assembled by its team with one atomic OR per member:
+// the draw made when no child is accepted (bits 0-31, from the member that
+// owns it), the accepted child + 1 (bits 32-39, member 0), the node's status
+// flags (bits 40-47, any member) and one bit per member that has finished
+// (bits 48-63).  The word is complete once every member's bit is set.
+constexpr int kNwAccShift = 32, kNwFlagShift = 40, kNwDoneShift = 48;
+
 __device__ __forceinline__ bool ws_ok(const StochParams& p) {
   return p.header[0] == kWsMagic && p.header[1] >= p.need;
 }
 
 // exp(d / T) for d <= 0 in float32: exp2 of d * log2(e) / T, with the product
 // carried as head + tail (the tail from an exact fma residual) so that rounding
-// the exponent does not cost accuracy; results below 2^-160 are 0.
+// the exponent does not cost accuracy.  Exponents below -150 give 0; a NaN or
+// infinite d gives NaN (callers detect non-finite logits from the sums).
 __device__ __forceinline__ float exp_t(float d, float k2hi, float k2lo) {
   const float h = d * k2hi;
   const float lo = fmaf(d, k2hi, -h) + d * k2lo;
   const float r = __builtin_amdgcn_exp2f(h);
-  const float y = fmaf(r, lo * 0.693147180559945309f, r);
-  return h > -160.f ? y : 0.f;
+  return fmaf(r, lo * 0.693147180559945309f, r);
 }
 
 // Weight of one vocabulary entry under max(p - c q, 0).  ep / eq are the
 // float32 exponentials exp((z - m) / T) relative to the entry's chunk maxima of
-// the target / draft row; a = exp((m - M) / T) / sum turns ep into p, and
-// cb = c times the same factor of the draft row turns eq into c q (float64).
-__device__ __forceinline__ double residual_weight(float ep, float eq, double a, double cb) {
-  return fmax(fma((double)ep, a, -(cb * (double)eq)), 0.0);
+// the target / draft row, and a = exp((m - M) / T) / S, b the same factor of the
+// draft row, turn them into p and q.  So max(p - c q, 0) = a max(ep - rho eq, 0)
+// with rho = c b / a for the whole chunk: the bracket is taken in float32 (one
+// fma and one max per entry) and scaled by a in float64 once per thread.
+__device__ __forceinline__ float residual_rel(float ep, float eq, float rho) {
+  return fmaxf(fmaf(eq, -rho, ep), 0.f);
 }
+
+// rho of a chunk from b and ia = 1 / a (0 for a chunk whose target mass a
+// underflowed: its weights are 0).
+__device__ __forceinline__ float chunk_rho(double ia, double b, double c) {
+  return (float)(c * b * ia);
+}
+
+// LDS of a request's chase.
+struct ChaseSmem {
+  int acc[kMaxNodes], fin[kMaxNodes], tok[kMaxNodes], path[kMaxNodes];
+  int flags, badpar, len, bad;
+};
 
 template <bool kRes>
 struct NodeSmem {
   static constexpr int MM = kRes ? kResident : kMaxChunks;   // chunks per member
+  static constexpr int MC = kRes ? kMaxTeam * kResident : kMaxChunks;   // chunks of a row
   float red_f[kSThreads / 64][2 * kResident];   // per-wave maxima of a batch (chunk, row)
   double red_d[kSThreads / 64][2 * kResident];  // per-wave exponential sums of a batch
   float cm[2][MM];        // this member's chunk maxima (target, draft)
   double cs[2][MM];       // ... chunk sums of exp((z - chunk max) / T)
-  double ca[2][MM];       // ... scale factors exp((m - M) / T) / sum
+  double ca[2][MC];       // every chunk's factor exp((m - M) / T) / S (target, draft)
+  double sc[MC];          // every chunk's target sum of exp((z - m) / T)
+  double ia[MC];          // 1 / ca[0][c] (0 where ca[0][c] is 0)
   double part[kSThreads / 64][MM];   // per-wave residual sums of this member's chunks
-  double rlast[MM];       // this member's chunk masses of the latest pass
   double rcur[MM];        // ... of the current residual
-  double xv[kMaxTeam];    // member masses of the latest pass
   double xcur[kMaxTeam];  // ... of the current residual
-  float xm[2][kMaxTeam];  // member row maxima (target, draft)
-  double xs[2][kMaxTeam]; // member exponential sums relative to those maxima
   double rowS[2];         // team exponential sums relative to the team maxima
+  double Fx;              // team residual mass of the latest rejection
   double scan[kSThreads / 64];
   int wcross[kSThreads / 64], wlast[kSThreads / 64];   // per wave: first crossing lane, last lane with mass
   int kids[kMaxNodes], ktok[kMaxNodes];
@@ -440,12 +464,23 @@ __device__ __forceinline__ float sum16(const float* x) {
   return (a[0] + a[2]) + (a[1] + a[3]);
 }
 
+// Largest of 16 floats (three-input maxima).
+__device__ __forceinline__ float max16(const float* x) {
+  const float a = fmaxf(fmaxf(x[0], x[1]), x[2]), b = fmaxf(fmaxf(x[3], x[4]), x[5]);
+  const float c = fmaxf(fmaxf(x[6], x[7]), x[8]), d = fmaxf(fmaxf(x[9], x[10]), x[11]);
+  const float e = fmaxf(fmaxf(x[12], x[13]), x[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), x[15]));
+}
+
 // Statistics of a batch of up to kResident chunks of the target row (and of the
 // draft row when `both`): every chunk's maximum m and sum of exp((z - m) / T)
 // over the workgroup, stored at local chunk index j0 + r.  The thread's logits
 // are replaced by those exponentials.  Units (row, chunk) are taken in the order
-// their loads were issued, each as soon as its own data has arrived.
-// Non-finite logits set sm.bad.
+// their loads were issued, each as soon as its own data has arrived.  Only the
+// thread holding the row's end masks entries; elsewhere the 16 entries run
+// without per-entry tests.  A non-finite logit makes its thread's sum NaN (the
+// maximum skips NaN; NaN, +inf and -inf all reach a NaN exponential), which
+// sets sm.bad.
 template <bool kRes>
 __device__ void batch_stats(NodeSmem<kRes>& sm, float (&xp)[kResident][16], float (&xq)[kResident][16], int nb,
                             bool both, int my_c0, int j0, int V, float k2hi, float k2lo) {
@@ -457,23 +492,31 @@ __device__ void batch_stats(NodeSmem<kRes>& sm, float (&xp)[kResident][16], floa
     for (int r = 0; r < kResident; ++r) {
       if (r < nb && (row == 0 || both)) {
         float* x = row ? xq[r] : xp[r];
-        const int e0 = (my_c0 + j0 + r) * kChunk + 16 * t;
-        float m = kNegInf;
+        const int nv = V - ((my_c0 + j0 + r) * kChunk + 16 * t);   // entries of this thread inside the row
+        float m;
+        if (nv >= 16) {
+          m = max16(x);
+        } else {
+          m = kNegInf;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (e0 + e < V) {
-            bad |= !isfinite(x[e]);
-            m = fmaxf(m, x[e]);
-          }
+          for (int e = 0; e < 16; ++e)
+            if (e < nv) m = fmaxf(m, x[e]);
         }
         m = tv_wave_max(m);
         if (l == 0) sm.red_f[w][2 * r + row] = m;
         tv_lds_barrier();
         m = sm.red_f[0][2 * r + row];
         for (int i = 1; i < kSThreads / 64; ++i) m = fmaxf(m, sm.red_f[i][2 * r + row]);
+        if (nv >= 16) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = e0 + e < V ? exp_t(x[e] - m, k2hi, k2lo) : 0.f;
-        const double sw = tv_wave_sum_d((double)sum16(x));
+          for (int e = 0; e < 16; ++e) x[e] = exp_t(x[e] - m, k2hi, k2lo);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x[e] = e < nv ? exp_t(x[e] - m, k2hi, k2lo) : 0.f;
+        }
+        const float st = sum16(x);
+        bad |= !isfinite(st);
+        const double sw = tv_wave_sum_d((double)st);
         if (l == 0) sm.red_d[w][2 * r + row] = sw;
         if (t == 0) sm.cm[row][j0 + r] = m;
       }
@@ -506,6 +549,43 @@ __device__ __forceinline__ unsigned long long xch_get(unsigned long long* slot, 
     __builtin_amdgcn_s_sleep(1);
   }
   return v & ~kWritten;
+}
+
+// Wait for up to N published slots at once (those with need[i]): every round
+// re-reads all slots still missing with loads issued together, so the wait
+// costs one round trip, not one per slot.  Payloads in v (0 after a timeout or
+// when not needed).
+template <int N>
+__device__ __forceinline__ void xch_get_n(unsigned long long* const (&slot)[N], const bool (&need)[N],
+                                          unsigned long long (&v)[N], int* timeout) {
+  bool done[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    v[i] = 0ull;
+    done[i] = !need[i];
+  }
+  for (long long it = 0;; ++it) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!done[i]) v[i] = __hip_atomic_load(slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (!done[i]) done[i] = (v[i] & kWritten) != 0ull;
+      all = all && done[i];
+    }
+    if (all) break;
+    if (it > kSpinLimit) {
+      *timeout = 1;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (!done[i]) v[i] = 0ull;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] &= ~kWritten;
 }
 
 // Inverse CDF inside one chunk: the smallest index whose running mass (from
@@ -594,36 +674,116 @@ __device__ int wave_select_mass(const double* m, int count, double thr, double* 
   return lastpos;
 }
 
-// One team of S workgroups per node (team = blockIdx / S, members on consecutive
-// ids), each member owning `per` consecutive chunks of the vocabulary.  Every
-// member reads its slice of the target row (and of the draft row when the node
-// has children) once; the team exchanges each slice's (max, sum), tests the
-// children, and makes the node's draw for the case that no child is accepted
-// (the chase kernel uses it when the accepted path ends at this node).  Members
-// wait only on their own team: with workgroups dispatched in id order every
-// team becomes fully resident once the teams before it have left, and a wait
-// that still expires flags TV_REQ_TIMEOUT instead of hanging.  kRes: every
-// member's slice is at most kResident chunks and its exponentials stay on chip
-// (target in registers, draft in LDS); otherwise each pass re-reads the slice.
-// The resident variant runs four workgroups per CU (a 16-member team per node
-// for up to 64 nodes on 256 CUs); the streaming variant keeps two batches of
-// loads in flight and runs three.
+// What the chase reads of request b, one entry per thread (thread t < n holds
+// node t's): its flags, accepted child and draw (from the node's result word),
+// token and parent.
+struct ChaseLoads {
+  int fl, acc, fin, tk, pv, n;
+  bool ws_ok;
+};
+
+// Issues every load of request b's rows at once, before n_nodes is known (rows
+// are n_max long; entries past n are not used).  Every member of a node has
+// ORed its part of the word before the node kernel ended.
+__device__ __forceinline__ ChaseLoads chase_load(const StochParams& p, int b) {
+  const int t = threadIdx.x;
+  const size_t kv = (size_t)b * p.n_max + t;
+  ChaseLoads c{0, -1, 0, 0, -1, 0, ws_ok(p)};
+  if (t < p.n_max) {
+    const unsigned long long wv = p.nword[kv];
+    c.fl = (int)((wv >> kNwFlagShift) & 0xffu);
+    c.acc = (int)((wv >> kNwAccShift) & 0xffu) - 1;
+    c.fin = (int)(uint32_t)wv;
+    c.tk = p.tokens[kv];
+    c.pv = p.parent[kv];
+  }
+  c.n = p.n_nodes[b];
+  return c;
+}
+
+// The chase of request b by the whole workgroup (any size of at least
+// kMaxNodes threads), from its entries in c: status, the accepted path and its
+// final token, and the request's result words cleared for the next call.
+// Returns (to every thread) the length of the path written, 0 when the request
+// failed; the path is also left in sm.path.
+__device__ int chase_request(const StochParams& p, ChaseSmem& sm, int b, const ChaseLoads& c) {
+  const int t = threadIdx.x;
+  const size_t kv = (size_t)b * p.n_max + t;
+  const int n = c.n;
+  if (n < 1 || n > p.n_max) {
+    if (t == 0) {
+      p.status[b] = TV_REQ_BAD_NNODES;
+      p.path_len[b] = 0;
+    }
+    return 0;
+  }
+  if (!c.ws_ok) {   // nothing of the workspace is trusted, read or cleared
+    if (t == 0) {
+      p.status[b] = TV_REQ_BAD_WORKSPACE;
+      p.path_len[b] = 0;
+    }
+    return 0;
+  }
+  if (t == 0) {
+    sm.flags = 0;
+    sm.badpar = 0;
+  }
+  __syncthreads();
+  if (t < n) {
+    p.nword[kv] = 0;
+    if (c.fl) atomicOr(&sm.flags, c.fl);
+    sm.acc[t] = c.acc;
+    sm.fin[t] = c.fin;
+    sm.tok[t] = c.tk;
+    if (!((t == 0) ? (c.pv == -1) : (c.pv >= 0 && c.pv < t))) sm.badpar = 1;
+  }
+  __syncthreads();
+  if (t == 0) {
+    const int fl = sm.badpar ? TV_REQ_BAD_PARENT : sm.flags;
+    if (fl) {
+      p.status[b] = fl;
+      p.path_len[b] = 0;
+      sm.len = 0;
+    } else {
+      int32_t* path = p.path + (size_t)b * p.n_max;
+      int32_t* out = p.out_tokens + (size_t)b * p.n_max;
+      int cur = 0, j = 0;
+      path[0] = 0;
+      sm.path[0] = 0;
+      for (;;) {
+        const int ch = sm.acc[cur];
+        if (ch <= cur || ch >= n || j + 1 >= n) break;
+        out[j] = sm.tok[ch];
+        ++j;
+        path[j] = ch;
+        sm.path[j] = ch;
+        cur = ch;
+      }
+      out[j] = sm.fin[cur];
+      p.path_len[b] = j + 1;
+      p.status[b] = 0;
+      sm.len = j + 1;
+    }
+  }
+  __syncthreads();
+  return sm.len;
+}
+
+
+// What one member contributes to its node's result word (thread 0's copy is used).
+struct NodeOut {
+  int flags, acc, tok;
+  bool drew;
+};
+
+// The work of member `member` of node k (request b, node u < n) up to its
+// contribution to the node's result.
 template <bool kRes, bool kVec>
-__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes ? 4 : 2))) void stoch_node_kernel(StochParams p) {
-  __shared__ NodeSmem<kRes> sm;
+__device__ __forceinline__ void node_body(const StochParams& p, NodeSmem<kRes>& sm, int k, int member, int b, int u,
+                                          int n, NodeOut& o) {
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
-  // With the whole grid resident, team members are numbered so that they run
-  // on one XCD (workgroup i goes to XCD i mod 8), where their exchange hand-offs
-  // are shorter.  Otherwise teams stay consecutive workgroup ids, which in-order
-  // dispatch makes resident one after another.
-  const int lid = p.xcd_teams ? tv_xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int k = lid / p.S, member = lid % p.S;
   const int my_c0 = min(member * p.per, p.chunks);
   const int nmine = min(my_c0 + p.per, p.chunks) - my_c0;   // at most kResident when kRes
-  const int b = k / p.n_max, u = k % p.n_max;
-  const int n = p.n_nodes[b];
-  if (n < 1 || n > p.n_max || u >= n) return;
-  if (!ws_ok(p)) return;   // the chase reports it; no slot is read or written
   const int32_t* par = p.parent + (size_t)b * p.n_max;
   const int32_t* tok = p.tokens + (size_t)b * p.n_max;
   const float* zp_row = p.target + (size_t)k * p.V;
@@ -645,6 +805,11 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     // loads later, so the rows of nodes with longer chains arrive first.  Timed
     // on the 100 MHz real-time counter.
     const int nkc = __popcll(__ballot(pv0 == u)) + __popcll(__ballot(pv1 == u));
+    // the same order for instruction issue among the waves sharing a SIMD
+    if (nkc >= 2)
+      __builtin_amdgcn_s_setprio(2);
+    else if (nkc == 1)
+      __builtin_amdgcn_s_setprio(1);
     if (nkc < kPrioSteps) {
       const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
       const unsigned long long d = (unsigned long long)p.prio_ticks * (unsigned long long)(kPrioSteps - nkc);
@@ -706,6 +871,19 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
       for (int g = 0; g < 4; ++g)
         sm.qe[(r * 4 + g) * kSThreads + t] = tv_f32x4{eq[r][4 * g], eq[r][4 * g + 1], eq[r][4 * g + 2], eq[r][4 * g + 3]};
   }
+  // From here on each step waits on the team: the waves issue ahead of the
+  // statistics of workgroups still streaming their slices.
+  __builtin_amdgcn_s_setprio(3);
+  // publish this member's chunk statistics at once: words (m, s) of the target
+  // row, then of the draft row, per chunk (a non-finite logit has made its
+  // chunk's s NaN, which the team sums carry to every member)
+  unsigned long long* sx = p.sxch + (size_t)k * p.chunks * 4;
+  for (int i = t; i < 4 * nmine; i += kSThreads) {
+    const int j = i >> 2, row = (i >> 1) & 1;
+    if (row == 0 || internal)
+      xch_put(sx + (size_t)(my_c0 + j) * 4 + (i & 3),
+              (i & 1) ? (unsigned long long)__double_as_longlong(sm.cs[row][j]) : (unsigned long long)__float_as_uint(sm.cm[row][j]));
+  }
   const int nk = sm.nk;
   if (t < nk) {
     if (t < 64) {
@@ -721,85 +899,72 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
       sm.kua[t] = p.u_accept[(size_t)b * p.n_max + sm.kids[t]];
     }
   }
-  const int bad = sm.bad;
-  if (bad && t == 0) atomicOr(&p.node_flags[k], TV_REQ_NONFINITE);
-
-  // this member's (max, sum) of both rows (wave 0: target, wave 1: draft; the
-  // lanes take chunks l and l + 64), exchanged with the team
-  unsigned long long* sx = p.sxch + (size_t)k * kMaxTeam * 4;
-  if (w < 2) {
-    float M = kNegInf;
-    double S = 0.0;
-    if (w == 0 || internal) {
-      const bool h0 = l < nmine, h1 = l + 64 < nmine;
-      const float m0 = h0 ? sm.cm[w][l] : kNegInf, m1 = h1 ? sm.cm[w][l + 64] : kNegInf;
-      M = tv_wave_max(fmaxf(m0, m1));
-      double e = h0 ? sm.cs[w][l] * exp(((double)m0 - (double)M) * p.invT_d) : 0.0;
-      if (h1) e += sm.cs[w][l + 64] * exp(((double)m1 - (double)M) * p.invT_d);
-      S = tv_wave_sum_d(e);
-    }
-    if (l == 0) {
-      const unsigned long long sb = bad ? 0x7FF8000000000000ull : (unsigned long long)__double_as_longlong(S);
-      xch_put(sx + member * 4 + 2 * w, __float_as_uint(M));
-      xch_put(sx + member * 4 + 2 * w + 1, sb);
-    }
-  }
-  if (t < 4 * p.S) {
-    const unsigned long long v = xch_get(sx + t, &sm.timeout);
-    const int mem = t >> 2, row = (t >> 1) & 1;
-    if (t & 1)
-      sm.xs[row][mem] = __longlong_as_double((long long)v);
-    else
-      sm.xm[row][mem] = __uint_as_float((uint32_t)v);
-  }
+  if (sm.bad) o.flags |= TV_REQ_NONFINITE;
   if (badtok) sm.badtok = 1;
-  tv_lds_barrier();   // (LDS-only barriers below: no wave waits here for its exchange stores to land)
-  badtok = sm.badtok;
-  if (badtok) {   // the request fails
-    if (member == 0 && t == 0) atomicOr(&p.node_flags[k], TV_REQ_BAD_TOKEN);
+  tv_lds_barrier();   // kzp / kzq / kua, badtok
+  if (sm.badtok) {   // the request fails
+    o.flags |= TV_REQ_BAD_TOKEN;
     return;
   }
-  // team row maxima: every thread takes them from the members' maxima (a max
-  // is exact, so all threads and all members agree); then every exponential
-  // that needs only the maxima runs at once, beside the team sums
-  float Mp = kNegInf, Mq = kNegInf;
-  for (int s2 = 0; s2 < p.S; ++s2) {
-    Mp = fmaxf(Mp, sm.xm[0][s2]);
-    Mq = fmaxf(Mq, sm.xm[1][s2]);
+  // Team statistics from every chunk's words: wave 0 the target row, wave 1 the
+  // draft row (lanes take chunks l and l + 64): the row maximum M, the sum
+  // S = sum_c s_c exp((m_c - M) / T) and each chunk's factor exp((m_c - M) / T) / S.
+  // All members combine the same words in the same order, so they agree exactly.
+  // Beside them, the lanes of the children (threads 128 + i) take the
+  // exponentials of their tokens' logits relative to the maxima of the chunks
+  // that hold them, so that p(x) and q(x) need one product after the barrier.
+  if (w < 2 && (w == 0 || internal)) {
+    unsigned long long* const sl[4] = {sx + (size_t)l * 4 + 2 * w, sx + (size_t)l * 4 + 2 * w + 1,
+                                       sx + (size_t)(l + 64) * 4 + 2 * w, sx + (size_t)(l + 64) * 4 + 2 * w + 1};
+    const bool nd[4] = {l < p.chunks, l < p.chunks, l + 64 < p.chunks, l + 64 < p.chunks};
+    unsigned long long v[4];
+    xch_get_n(sl, nd, v, &sm.timeout);
+    const float m0 = nd[0] ? __uint_as_float((uint32_t)v[0]) : kNegInf;
+    const float m1 = nd[2] ? __uint_as_float((uint32_t)v[2]) : kNegInf;
+    const double s0 = __longlong_as_double((long long)v[1]), s1 = __longlong_as_double((long long)v[3]);
+    const float M = tv_wave_max(fmaxf(m0, m1));
+    const double e0 = l < p.chunks ? exp(((double)m0 - (double)M) * p.invT_d) : 0.0;
+    const double e1 = l + 64 < p.chunks ? exp(((double)m1 - (double)M) * p.invT_d) : 0.0;
+    const double S = tv_wave_sum_d(s0 * e0 + s1 * e1);
+    const double iS = 1.0 / S;
+    if (l < p.chunks) {
+      const double a = e0 * iS;
+      sm.ca[w][l] = a;
+      if (w == 0) {
+        sm.sc[l] = s0;
+        sm.ia[l] = a > 0.0 ? 1.0 / a : 0.0;
+      }
+    }
+    if (l + 64 < p.chunks) {
+      const double a = e1 * iS;
+      sm.ca[w][l + 64] = a;
+      if (w == 0) {
+        sm.sc[l + 64] = s1;
+        sm.ia[l + 64] = a > 0.0 ? 1.0 / a : 0.0;
+      }
+    }
+    if (l == 0) sm.rowS[w] = S;
   }
-  if (!internal) Mq = kNegInf;
-  double ea0 = 0.0, ea1 = 0.0, ekp = 0.0, ekq = 0.0;
-  if (t < nmine) {
-    ea0 = exp(((double)sm.cm[0][t] - (double)Mp) * p.invT_d);
-    ea1 = internal ? exp(((double)sm.cm[1][t] - (double)Mq) * p.invT_d) : 0.0;
-  }
-  const int ci = t - (kSThreads - kMaxNodes);   // every child's test operands at once
+  const int ci = t - 2 * 64;   // every child's test operands at once
   const bool child_t = ci >= 0 && ci < nk;
+  double ekp = 0.0, ekq = 0.0;
+  int kc = 0;
   if (child_t) {
-    ekp = exp(((double)sm.kzp[ci] - (double)Mp) * p.invT_d);   // p(x) = exp((z - M) / T) / S
-    ekq = internal ? exp(((double)sm.kzq[ci] - (double)Mq) * p.invT_d) : 0.0;
-  }
-  // team row sums: lanes 16 r + s of wave 0 combine member s of row r with a
-  // fixed shuffle tree, so every member obtains the same values
-  if (w == 0) {
-    const int row = (l >> 4) & 1, s2 = l & 15;
-    const bool on = l < 32 && s2 < p.S && (row == 0 || internal);
-    const float m = on ? sm.xm[row][s2] : kNegInf;
-    const float M = row ? Mq : Mp;
-    const double e = tv_row16_sum_d(on ? sm.xs[row][s2] * exp(((double)m - (double)M) * p.invT_d) : 0.0);
-    if (l == 0 || l == 16) sm.rowS[row] = e;
+    kc = sm.ktok[ci] / kChunk;
+    unsigned long long* const sl[2] = {sx + (size_t)kc * 4, sx + (size_t)kc * 4 + 2};
+    const bool nd[2] = {true, internal};
+    unsigned long long v[2];
+    xch_get_n(sl, nd, v, &sm.timeout);
+    ekp = exp(((double)sm.kzp[ci] - (double)__uint_as_float((uint32_t)v[0])) * p.invT_d);
+    if (internal) ekq = exp(((double)sm.kzq[ci] - (double)__uint_as_float((uint32_t)v[1])) * p.invT_d);
   }
   tv_lds_barrier();
   const double Sp = sm.rowS[0], Sq = sm.rowS[1];
   if (!isfinite(Sp) || (internal && !isfinite(Sq))) return;   // some member saw a non-finite logit
-  const double ip = 1.0 / Sp, iq = internal ? 1.0 / Sq : 0.0;
-  if (t < nmine) {
-    sm.ca[0][t] = ea0 * ip;
-    sm.ca[1][t] = internal ? ea1 * iq : 0.0;
-  }
-  if (child_t) {
-    sm.kpx[ci] = ekp * ip;
-    sm.kqx[ci] = internal ? ekq * iq : 0.0;
+  if (!internal && t < p.chunks) sm.ca[1][t] = 0.0;
+  if (child_t) {   // p(x) = exp((z - m_c) / T) exp((m_c - M) / T) / S
+    sm.kpx[ci] = ekp * sm.ca[0][kc];
+    sm.kqx[ci] = internal ? ekq * sm.ca[1][kc] : 0.0;
   }
   tv_lds_barrier();
 
@@ -837,52 +1002,50 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
 #pragma unroll
       for (int r = 0; r < kResident; ++r) {
         if (j0 + r < nmine) {
-          const double a = sm.ca[0][j0 + r], cb = cn * sm.ca[1][j0 + r];
-          double wv[16];
+          const double a = sm.ca[0][my_c0 + j0 + r];
+          const float rho = chunk_rho(sm.ia[my_c0 + j0 + r], sm.ca[1][my_c0 + j0 + r], cn);
+          float wv[16];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const tv_f32x4 q4 = kRes ? sm.qe[(r * 4 + g) * kSThreads + t]
                                      : tv_f32x4{eq[r][4 * g], eq[r][4 * g + 1], eq[r][4 * g + 2], eq[r][4 * g + 3]};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[4 * g + e] = residual_weight(ep[r][4 * g + e], q4[e], a, cb);
+            for (int e = 0; e < 4; ++e) wv[4 * g + e] = residual_rel(ep[r][4 * g + e], q4[e], rho);
           }
-          double s = sum16_d(wv);   // pairwise: a short dependent chain
-          s = tv_wave_sum_d(s);
+          const double s = tv_wave_sum_d((double)sum16(wv) * a);   // pairwise: a short dependent chain
           if (l == 0) sm.part[w][j0 + r] = s;
         }
       }
     }
-    tv_lds_barrier();
-    if (t < nmine) {
-      double s = 0.0;
-      for (int i2 = 0; i2 < kSThreads / 64; ++i2) s += sm.part[i2][t];
-      sm.rlast[t] = s;
+    tv_lds_barrier();   // the waves' partials
+    // Wave 0: this member's chunk masses (lanes take chunks l and l + 64) and
+    // their sum, published; lanes below S gather the team's masses and add
+    // them with a fixed DPP tree, so every member obtains the same F.
+    if (w == 0) {
+      double r0 = 0.0, r1 = 0.0;
+      if (l < nmine)
+        for (int i2 = 0; i2 < kSThreads / 64; ++i2) r0 += sm.part[i2][l];
+      if (l + 64 < nmine)
+        for (int i2 = 0; i2 < kSThreads / 64; ++i2) r1 += sm.part[i2][l + 64];
+      const double mine = tv_wave_sum_d(r0 + r1);
+      unsigned long long* xs = p.xch + ((size_t)b * p.n_max + sm.kids[i]) * kMaxTeam;
+      if (l == 0) xch_put(xs + member, (unsigned long long)__double_as_longlong(mine));
+      double xv = 0.0;
+      if (l < p.S) xv = __longlong_as_double((long long)xch_get(xs + l, &sm.timeout));
+      const double F = tv_readlane_d(tv_row16_sum_d(xv), 0);
+      if (F > 0.0) {   // the residual moves: keep its member and chunk masses
+        if (l < p.S) sm.xcur[l] = xv;
+        if (l < nmine) sm.rcur[l] = r0;
+        if (l + 64 < nmine) sm.rcur[l + 64] = r1;
+      }
+      if (l == 0) sm.Fx = F;
     }
     tv_lds_barrier();
-    double mine = 0.0;
-    for (int j0 = 0; j0 < nmine; j0 += 8) {   // reads ahead of the dependent sums, same order
-      double v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = j0 + j < nmine ? sm.rlast[j0 + j] : 0.0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j0 + j < nmine) mine += v[j];
-    }
-    // publish this member's mass for this rejection, gather the team's
-    unsigned long long* xs = p.xch + ((size_t)b * p.n_max + sm.kids[i]) * kMaxTeam;
-    if (t == 0) xch_put(xs + member, (unsigned long long)__double_as_longlong(mine));
-    if (t < p.S) sm.xv[t] = __longlong_as_double((long long)xch_get(xs + t, &sm.timeout));
-    tv_lds_barrier();
-    double F = 0.0;
-#pragma unroll
-    for (int s = 0; s < kMaxTeam; ++s)
-      if (s < p.S) F += sm.xv[s];
+    const double F = sm.Fx;
     if (F > 0.0) {   // Z > 0: move to the new residual
       Cres = cn;
       Dres = F;
       cur = i;
-      if (t < p.S) sm.xcur[t] = sm.xv[t];
-      if (t < nmine) sm.rcur[t] = sm.rlast[t];
     }
   }
 
@@ -891,8 +1054,12 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     // masses, then inside one chunk; masses are those of p while no rejection
     // has moved the residual, else of the current residual
     if (cur < 0) {
-      if (t < p.S) sm.xcur[t] = sm.xs[0][t] * exp(((double)sm.xm[0][t] - (double)Mp) * p.invT_d) * ip;   // parallel over members
-      if (t < nmine) sm.rcur[t] = sm.cs[0][t] * sm.ca[0][t];
+      if (t < p.S) {   // member masses of p, parallel over members
+        double x = 0.0;
+        for (int c = t * p.per; c < min((t + 1) * p.per, p.chunks); ++c) x += sm.sc[c] * sm.ca[0][c];
+        sm.xcur[t] = x;
+      }
+      if (t < nmine) sm.rcur[t] = sm.cs[0][t] * sm.ca[0][my_c0 + t];
     }
     tv_lds_barrier();
     if (w == 0) {   // member, then chunk, by wave scans
@@ -913,7 +1080,8 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
     if (sm.owner == member && nmine > 0) {
       const int j = min(sm.sel, nmine - 1);
       const int e0 = (my_c0 + j) * kChunk + 16 * t;
-      const double a = sm.ca[0][j], bq = sm.ca[1][j];
+      const double a = sm.ca[0][my_c0 + j];
+      const float rho = chunk_rho(sm.ia[my_c0 + j], sm.ca[1][my_c0 + j], Cres);
       const bool res = cur >= 0;
       double wts[16];
       if (kRes) {
@@ -930,7 +1098,7 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
             qe[4 * g + 3] = q4[3];
           }
 #pragma unroll
-          for (int e = 0; e < 16; ++e) wts[e] = residual_weight(pe[e], qe[e], a, Cres * bq);
+          for (int e = 0; e < 16; ++e) wts[e] = (double)residual_rel(pe[e], qe[e], rho) * a;
         } else {
 #pragma unroll
           for (int e = 0; e < 16; ++e) wts[e] = (double)pe[e] * a;
@@ -943,8 +1111,8 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
         if (res) {
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            wts[e] = e0 + e < p.V ? residual_weight(exp_t(xp[e] - mp, p.k2hi, p.k2lo), exp_t(xq[e] - mq, p.k2hi, p.k2lo),
-                                                    a, Cres * bq)
+            wts[e] = e0 + e < p.V ? (double)residual_rel(exp_t(xp[e] - mp, p.k2hi, p.k2lo),
+                                                         exp_t(xq[e] - mq, p.k2hi, p.k2lo), rho) * a
                                   : 0.0;
         } else {
 #pragma unroll
@@ -952,127 +1120,74 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
         }
       }
       const int y = chunk_draw(sm, wts, e0, sm.base, sm.thr, (my_c0 + j) * kChunk);
-      if (t == 0) p.node_tok[k] = y;
+      o.tok = y;
+      o.drew = true;
     }
   }
+  o.acc = accepted;
+}
+
+// One team of S workgroups per node (team = blockIdx / S, members on consecutive
+// ids), each member owning `per` consecutive chunks of the vocabulary.  Every
+// member reads its slice of the target row (and of the draft row when the node
+// has children) once; the team exchanges each slice's (max, sum), tests the
+// children, and makes the node's draw for the case that no child is accepted
+// (the chase kernel uses it when the accepted path ends at this node).  Members
+// wait only on their own team: with workgroups dispatched in id order every
+// team becomes fully resident once the teams before it have left, and a wait
+// that still expires flags TV_REQ_TIMEOUT instead of hanging.  kRes: every
+// member's slice is at most kResident chunks and its exponentials stay on chip
+// (target in registers, draft in LDS); otherwise each pass re-reads the slice.
+// The resident variant runs four workgroups per CU (a 16-member team per node
+// for up to 64 nodes on 256 CUs); the streaming variant keeps two batches of
+// loads in flight and runs three.
+template <bool kRes, bool kVec>
+__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes ? 4 : 2))) void stoch_node_kernel(StochParams p) {
+  __shared__ NodeSmem<kRes> sm;
+  const int t = threadIdx.x;
+  // With the whole grid resident, team members are numbered so that they run
+  // on one XCD (workgroup i goes to XCD i mod 8), where their exchange hand-offs
+  // are shorter.  Otherwise teams stay consecutive workgroup ids, which in-order
+  // dispatch makes resident one after another.
+  const int lid = p.xcd_teams ? tv_xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int k = lid / p.S, member = lid % p.S;
+  const int b = k / p.n_max, u = k % p.n_max;
+  const int n = p.n_nodes[b];
+  if (n < 1 || n > p.n_max || u >= n) return;
+  if (!ws_ok(p)) return;   // the chase reports it; no slot is read or written
+  NodeOut o{0, -1, 0, false};
+  node_body<kRes, kVec>(p, sm, k, member, b, u, n, o);
+  __syncthreads();
+  // The member's part of the node's result word.  The member whose OR
+  // completes the word clears the node's exchange slots for the next call
+  // (every member has finished with them): the exchange stores all come from
+  // wave 0 and have landed before the OR.
   if (t == 0) {
-    if (member == 0) p.node_acc[k] = accepted;
-    if (sm.timeout) atomicOr(&p.node_flags[k], TV_REQ_TIMEOUT);
+    const int fl = o.flags | (sm.timeout ? TV_REQ_TIMEOUT : 0);
+    const unsigned long long mine = 1ull << (kNwDoneShift + member);
+    unsigned long long wv = mine | ((unsigned long long)(fl & 0xff) << kNwFlagShift);
+    if (member == 0) wv |= (unsigned long long)(uint32_t)(o.acc + 1) << kNwAccShift;
+    if (o.drew) wv |= (unsigned long long)(uint32_t)o.tok;
+    __builtin_amdgcn_s_waitcnt(0);
+    const unsigned long long before = __hip_atomic_fetch_or(p.nword + k, wv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long full = ((1ull << p.S) - 1ull) << kNwDoneShift;
+    sm.bad = ((before | mine) & full) == full;   // reused: this member completed the node
+  }
+  __syncthreads();
+  if (sm.bad) {   // the node's statistics words, and the rejection slots of its children
+    tv_u32x4* sx = (tv_u32x4*)(p.sxch + (size_t)k * p.chunks * 4);
+    const tv_u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = t; i < p.chunks * 2; i += kSThreads) sx[i] = z;
+    for (int i = t; i < sm.nk * (kMaxTeam / 2); i += kSThreads) {
+      tv_u32x4* xc = (tv_u32x4*)(p.xch + ((size_t)b * p.n_max + sm.kids[i / (kMaxTeam / 2)]) * kMaxTeam);
+      xc[i % (kMaxTeam / 2)] = z;
+    }
   }
 }
 
-// One workgroup per request: status, the accepted path and its final token,
-// and the exchange slots cleared for the next call.
 constexpr int kChaseThreads = 256;
 
-struct ChaseSmem {
-  int acc[kMaxNodes], fin[kMaxNodes], tok[kMaxNodes], path[kMaxNodes];
-  int flags, badpar, len, bad;
-};
-
-// The request's rows the chase reads, one entry per thread (thread t < n_max
-// holds node t's).
-struct ChaseLoads {
-  int fl, acc, fin, tk, pv, n;
-  bool ws_ok;
-};
-
-// Issues every load of request b's rows at once, before n_nodes is known (rows
-// are n_max long; entries past n are not used).
-__device__ __forceinline__ ChaseLoads chase_load(const StochParams& p, int b) {
-  const int t = threadIdx.x;
-  const size_t kv = (size_t)b * p.n_max + t;
-  ChaseLoads c{0, -1, 0, 0, -1, 0, ws_ok(p)};
-  if (t < p.n_max) {
-    c.fl = p.node_flags[kv];
-    c.acc = p.node_acc[kv];
-    c.fin = p.node_tok[kv];
-    c.tk = p.tokens[kv];
-    c.pv = p.parent[kv];
-  }
-  c.n = p.n_nodes[b];
-  return c;
-}
-
-// The chase of request b by the whole workgroup (any size of at least
-// kMaxNodes threads), from its rows loaded by chase_load.  Returns (to every
-// thread) the length of the path written, 0 when the request failed; the path
-// is also left in sm.path.
-__device__ int chase_request(const StochParams& p, ChaseSmem& sm, int b, const ChaseLoads& c) {
-  const int t = threadIdx.x;
-  const size_t kv = (size_t)b * p.n_max + t;
-  const int n = c.n;
-  if (n < 1 || n > p.n_max) {
-    if (t == 0) {
-      p.status[b] = TV_REQ_BAD_NNODES;
-      p.path_len[b] = 0;
-    }
-    return 0;
-  }
-  if (!c.ws_ok) {   // nothing of the workspace is trusted, read or cleared
-    if (t == 0) {
-      p.status[b] = TV_REQ_BAD_WORKSPACE;
-      p.path_len[b] = 0;
-    }
-    return 0;
-  }
-  if (t == 0) {
-    sm.flags = 0;
-    sm.badpar = 0;
-  }
-  __syncthreads();
-  // every exchange slot the node kernel may have written for this request, in
-  // 16-byte stores (a request's slots start 16-byte aligned: the slot arrays
-  // are 256-byte aligned and a request owns a multiple of 16 slots)
-  {
-    tv_u32x4* sx = (tv_u32x4*)(p.sxch + (size_t)b * p.n_max * kMaxTeam * 4);
-    tv_u32x4* xc = (tv_u32x4*)(p.xch + (size_t)b * p.n_max * kMaxTeam);
-    const tv_u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = t; i < n * kMaxTeam * 2; i += blockDim.x) sx[i] = z;
-    for (int i = t; i < n * kMaxTeam / 2; i += blockDim.x) xc[i] = z;
-  }
-  if (t < n) {
-    if (c.fl) {
-      atomicOr(&sm.flags, c.fl);
-      p.node_flags[kv] = 0;
-    }
-    sm.acc[t] = c.acc;
-    sm.fin[t] = c.fin;
-    sm.tok[t] = c.tk;
-    if (!((t == 0) ? (c.pv == -1) : (c.pv >= 0 && c.pv < t))) sm.badpar = 1;
-  }
-  __syncthreads();
-  if (t == 0) {
-    const int fl = sm.badpar ? TV_REQ_BAD_PARENT : sm.flags;
-    if (fl) {
-      p.status[b] = fl;
-      p.path_len[b] = 0;
-      sm.len = 0;
-    } else {
-      int32_t* path = p.path + (size_t)b * p.n_max;
-      int32_t* out = p.out_tokens + (size_t)b * p.n_max;
-      int cur = 0, j = 0;
-      path[0] = 0;
-      sm.path[0] = 0;
-      for (;;) {
-        const int ch = sm.acc[cur];
-        if (ch <= cur || ch >= n || j + 1 >= n) break;
-        out[j] = sm.tok[ch];
-        ++j;
-        path[j] = ch;
-        sm.path[j] = ch;
-        cur = ch;
-      }
-      out[j] = sm.fin[cur];
-      p.path_len[b] = j + 1;
-      p.status[b] = 0;
-      sm.len = j + 1;
-    }
-  }
-  __syncthreads();
-  return sm.len;
-}
-
+// One workgroup per request: status, the accepted path and its final token.
 __global__ __launch_bounds__(kChaseThreads) void stoch_chase_kernel(StochParams p) {
   __shared__ ChaseSmem sm;
   chase_request(p, sm, blockIdx.x, chase_load(p, blockIdx.x));
@@ -1088,11 +1203,6 @@ __global__ __launch_bounds__(kChaseThreads) void stoch_chase_kernel(StochParams 
 // each up to n_kv_heads * head_dim = 1024, so every pair's moves take a single
 // load-then-store round trip.
 constexpr int kChaseCompactThreads = 1024;
-// Batches above this size take the chase and the compaction as two kernels
-// (measured on MI355X: one request gains ~1.4 us per step from the fused
-// kernel; 16 and 64 requests lose 10-14 us, their moves crowded onto one CU
-// per request).
-constexpr int kFusedChaseMaxBatch = 4;
 constexpr int kStagedBlocks = kMaxNodes / 16 + 2;   // blocks holding n <= 128 positions (block size >= 16)
 
 template <typename T>
@@ -1135,7 +1245,7 @@ int check_vdesc(const tv_verify_desc* d) {
 
 struct VerifyLayout {
   size_t g_keys, g_bad, greedy_bytes;
-  size_t xch, sxch, flg, acc, tok, stoch_bytes;
+  size_t xch, sxch, nword, stoch_bytes;
   int gchunks, chunks;
 };
 
@@ -1154,16 +1264,37 @@ VerifyLayout layout(const tv_verify_desc* d) {
   L.xch = o;
   o = tv_align_up(o + nodes * kMaxTeam * sizeof(unsigned long long), 256);
   L.sxch = o;
-  o = tv_align_up(o + nodes * kMaxTeam * 4 * sizeof(unsigned long long), 256);
-  L.flg = o;
-  o = tv_align_up(o + nodes * sizeof(int), 256);
-  L.acc = o;
-  o = tv_align_up(o + nodes * sizeof(int), 256);
-  L.tok = o;
-  o = tv_align_up(o + nodes * sizeof(int), 256);
+  o = tv_align_up(o + nodes * (size_t)L.chunks * 4 * sizeof(unsigned long long), 256);
+  L.nword = o;
+  o = tv_align_up(o + nodes * sizeof(unsigned long long), 256);
   L.stoch_bytes = o;
   return L;
 }
+
+// Workgroups of the resident node kernel one CU holds at once (its registers
+// and LDS decide; cached per device, 0 when the query fails).  The whole-grid
+// schedule below needs every workgroup resident at the same time.
+int resident_per_cu(bool vec) {
+  constexpr int kDev = 64;
+  static std::once_flag once[kDev][2];
+  static int per[kDev][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDev) return 0;
+  std::call_once(once[dev][vec], [dev, vec]() {
+    int nb = 0;
+    const hipError_t e =
+        vec ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, stoch_node_kernel<true, true>, kSThreads, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, stoch_node_kernel<true, false>, kSThreads, 0);
+    per[dev][vec] = e == hipSuccess ? nb : 0;
+  });
+  return per[dev][vec];
+}
+
+// Batches above this size take the chase and the compaction as two kernels
+// (measured on MI355X: one request gains ~1.4 us per step from the fused
+// kernel; 16 and 64 requests lose 10-14 us, their moves crowded onto one CU
+// per request).
+constexpr int kFusedChaseMaxBatch = 4;
 
 struct TeamPlan {
   int S;     // workgroups per node
@@ -1367,7 +1498,8 @@ int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, c
                        const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
                        const float* u_accept, const float* u_sample, int32_t* path, int32_t* path_len,
                        int32_t* out_tokens, int32_t* status, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream, StochParams& p) {
+                       const TvCompactArgs* cpt, int cpt_bf16, hipStream_t stream) {
+  StochParams p{};
   int rc = check_vdesc(desc);
   if (rc != TV_OK) return rc;
   if (!target_logits || !draft_logits || !tokens || !parent || !n_nodes || !u_accept || !u_sample ||
@@ -1397,9 +1529,7 @@ int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, c
   p.need = L.stoch_bytes;
   p.xch = (unsigned long long*)(ws + L.xch);
   p.sxch = (unsigned long long*)(ws + L.sxch);
-  p.node_flags = (int*)(ws + L.flg);
-  p.node_acc = (int*)(ws + L.acc);
-  p.node_tok = (int*)(ws + L.tok);
+  p.nword = (unsigned long long*)(ws + L.nword);
   p.B = desc->batch;
   p.n_max = desc->n_max;
   p.V = desc->vocab;
@@ -1420,20 +1550,25 @@ int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, c
   int cu = 0;
   p.prio_ticks = 0;
   p.xcd_teams = 0;
-  if (resident && tv_device_cu_count(&cu) == TV_OK && grid <= 4LL * cu) {
+  const bool vec = (desc->vocab & 3) == 0;
+  if (resident && tv_device_cu_count(&cu) == TV_OK && grid <= (long long)resident_per_cu(vec) * cu) {
     p.xcd_teams = 1;
     const double row_bytes = (double)nodes * (double)desc->vocab * 4.0;
     p.prio_ticks = (int)fmin(row_bytes / (4.0 * 5.5e12) * 1e8, 1000.0);
   }
-  const bool vec = (desc->vocab & 3) == 0;
-  if (resident && vec)
-    hipLaunchKernelGGL((stoch_node_kernel<true, true>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
-  else if (resident)
-    hipLaunchKernelGGL((stoch_node_kernel<true, false>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
-  else if (vec)
-    hipLaunchKernelGGL((stoch_node_kernel<false, true>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((stoch_node_kernel<false, false>), dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
+  void (*kern)(StochParams) = resident ? (vec ? stoch_node_kernel<true, true> : stoch_node_kernel<true, false>)
+                                        : (vec ? stoch_node_kernel<false, true> : stoch_node_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  if (!cpt) {
+    hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kChaseThreads), 0, stream, p);
+  } else if (cpt_bf16) {
+    hipLaunchKernelGGL(stoch_chase_compact_kernel<uint16_t>, dim3((unsigned)desc->batch), dim3(kChaseCompactThreads),
+                       0, stream, p, *cpt);
+  } else {
+    hipLaunchKernelGGL(stoch_chase_compact_kernel<float>, dim3((unsigned)desc->batch), dim3(kChaseCompactThreads),
+                       0, stream, p, *cpt);
+  }
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
@@ -1448,12 +1583,8 @@ static int tree_verify_stochastic_impl(const tv_verify_desc* desc, const float* 
   int rc = check_vdesc(desc);
   if (rc != TV_OK) return rc;
   if (desc->batch == 0) return TV_OK;
-  StochParams p;
-  rc = launch_stoch_nodes(desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path,
-                          path_len, out_tokens, status, workspace, workspace_bytes, stream, p);
-  if (rc != TV_OK) return rc;
-  hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kChaseThreads), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+  return launch_stoch_nodes(desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path,
+                            path_len, out_tokens, status, workspace, workspace_bytes, nullptr, 0, stream);
 }
 
 extern "C" int tree_verify_stochastic(const tv_verify_desc* desc, const float* target_logits,
@@ -1485,27 +1616,20 @@ static int tree_verify_stochastic_compact_impl(const tv_verify_desc* desc, const
   if (kv_desc->batch != desc->batch || kv_desc->n_max != desc->n_max) return TV_ERR_INVALID_ARG;
   if (desc->batch == 0) return TV_OK;
   if (!k_cache || !v_cache || !block_table || !prefix_len || !src_pos || !new_len) return TV_ERR_INVALID_ARG;
-  StochParams p;
-  rc = launch_stoch_nodes(desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path,
-                          path_len, out_tokens, status, workspace, workspace_bytes, stream, p);
-  if (rc != TV_OK) return rc;
   if (desc->batch > kFusedChaseMaxBatch) {
-    // many requests: the chase, then the compaction's own grid of one
-    // workgroup per (request, KV head), which spreads the moves over more CUs
-    hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kChaseThreads), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+    // many requests: the compaction's own grid of one workgroup per (request,
+    // KV head) after the verification spreads the moves over more CUs
+    rc = launch_stoch_nodes(desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path,
+                            path_len, out_tokens, status, workspace, workspace_bytes, nullptr, 0, stream);
+    if (rc != TV_OK) return rc;
     return kv_compact_accepted(kv_desc, k_cache, v_cache, block_table, prefix_len, path, path_len, src_pos,
                                new_len, kv_status, stream);
   }
   const TvCompactArgs c =
       tv_compact_args(kv_desc, k_cache, v_cache, block_table, prefix_len, src_pos, new_len, kv_status);
-  if (kv_desc->dtype == TV_BF16)
-    hipLaunchKernelGGL(stoch_chase_compact_kernel<uint16_t>, dim3((unsigned)desc->batch), dim3(kChaseCompactThreads),
-                       0, stream, p, c);
-  else
-    hipLaunchKernelGGL(stoch_chase_compact_kernel<float>, dim3((unsigned)desc->batch), dim3(kChaseCompactThreads),
-                       0, stream, p, c);
-  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
+  return launch_stoch_nodes(desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path,
+                            path_len, out_tokens, status, workspace, workspace_bytes, &c, kv_desc->dtype == TV_BF16,
+                            stream);
 }
 
 extern "C" int tree_verify_stochastic_compact(const tv_verify_desc* desc, const tv_attn_desc* kv_desc,
