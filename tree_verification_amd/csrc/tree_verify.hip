@@ -104,6 +104,14 @@ __device__ __forceinline__ void load16(__amdgpu_buffer_rsrc_t rs, int e0, float*
   }
 }
 
+// Largest of 16 floats (three-input maxima).
+__device__ __forceinline__ float max16(const float* x) {
+  const float a = fmaxf(fmaxf(x[0], x[1]), x[2]), b = fmaxf(fmaxf(x[3], x[4]), x[5]);
+  const float c = fmaxf(fmaxf(x[6], x[7]), x[8]), d = fmaxf(fmaxf(x[9], x[10]), x[11]);
+  const float e = fmaxf(fmaxf(x[12], x[13]), x[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), x[15]));
+}
+
 // Children of u among nodes [1, n), ascending, written by one wave into kids[]
 // with their tokens in ktok[]; returns the count to every lane (n <= 128: two
 // ballots).  pv0 / pv1 and tk0 / tk1: parent and token of nodes 1 + l and
@@ -204,13 +212,27 @@ __device__ __forceinline__ void greedy_reduce(const GreedyParams& p, int unit, c
   unsigned long long best = 0ull;
   if (live) {
     int bad = 0;
+    if (hi - lo == kGreedyChunk) {
+      // A full chunk: the largest value (three-input maxima), then the first of
+      // the thread's entries (ascending index) that holds it; non-finite
+      // entries are found by class.  With every entry finite the maximum is
+      // exact and -0 / +0 compare equal, so this is the same key as below.
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int e = greedy_elem(lo, j);
-      if (e < hi) {
-        bad |= !isfinite(x.x[j]);
-        const unsigned long long kx = argmax_key(x.x[j], e);
-        best = kx > best ? kx : best;
+      for (int j = 0; j < 32; ++j) bad |= !isfinite(x.x[j]);
+      const float m = fmaxf(max16(x.x), max16(x.x + 16));
+      int jm = 31;
+#pragma unroll
+      for (int j = 30; j >= 0; --j) jm = x.x[j] == m ? j : jm;
+      best = argmax_key(m, greedy_elem(lo, jm));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int e = greedy_elem(lo, j);
+        if (e < hi) {
+          bad |= !isfinite(x.x[j]);
+          const unsigned long long kx = argmax_key(x.x[j], e);
+          best = kx > best ? kx : best;
+        }
       }
     }
     best = tv_wave_max_u64(best);
@@ -462,14 +484,6 @@ __device__ __forceinline__ float sum16(const float* x) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) a[i] += a[i + 4];
   return (a[0] + a[2]) + (a[1] + a[3]);
-}
-
-// Largest of 16 floats (three-input maxima).
-__device__ __forceinline__ float max16(const float* x) {
-  const float a = fmaxf(fmaxf(x[0], x[1]), x[2]), b = fmaxf(fmaxf(x[3], x[4]), x[5]);
-  const float c = fmaxf(fmaxf(x[6], x[7]), x[8]), d = fmaxf(fmaxf(x[9], x[10]), x[11]);
-  const float e = fmaxf(fmaxf(x[12], x[13]), x[14]);
-  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), x[15]));
 }
 
 // Statistics of a batch of up to kResident chunks of the target row (and of the
