@@ -784,22 +784,6 @@ __device__ int chase_request(const StochParams& p, ChaseSmem& sm, int b, const C
 }
 
 
-// Exchange-slot payload that a member publishes instead of its mass when it
-// has seen its node fall off every path (a NaN: masses are finite), and the
-// mark a node leaves in member 0's slot of a child it will never test.
-constexpr unsigned long long kGoneMass = 0x7ff8000000000badull;
-constexpr unsigned long long kUntested = 1ull;
-
-// Whether node u (> 0) can no longer lie on the accepted path, from two words
-// read with agent-scope atomics: member 0's slot of its parent's exchange for
-// u (written once the parent rejects u, gives up, or will never test u) and
-// the parent's result word (complete, with another accepted child or none).
-__device__ __forceinline__ bool off_path(unsigned long long slot, unsigned long long pword, int S, int u) {
-  const unsigned long long full = ((1ull << S) - 1ull) << kNwDoneShift;
-  if (slot & kWritten) return true;
-  return (pword & full) == full && (int)((pword >> kNwAccShift) & 0xffu) - 1 != u;
-}
-
 // What one member contributes to its node's result word (thread 0's copy is used).
 struct NodeOut {
   int flags, acc, tok;
@@ -914,20 +898,6 @@ __device__ __forceinline__ void node_body(const StochParams& p, NodeSmem<kRes>& 
       xch_put(sx + (size_t)(my_c0 + j) * 4 + (i & 3),
               (i & 1) ? (unsigned long long)__double_as_longlong(sm.cs[row][j]) : (unsigned long long)__float_as_uint(sm.cm[row][j]));
   }
-  // Whether u has fallen off the path is read from its parent's words; the
-  // loads ride along this member's exchanges and are used one exchange later,
-  // so no step waits for them.  A member that sees it publishes kGoneMass at
-  // its next rejection and the whole team stops there; the statistics above
-  // (and their non-finite checks) always complete.
-  const int up = u > 0 ? par[u] : -1;
-  const bool can_go = up >= 0 && up < u;
-  unsigned long long* const pk_slot = p.xch + ((size_t)b * p.n_max + u) * kMaxTeam;
-  unsigned long long* const pk_word = p.nword + (size_t)b * p.n_max + (can_go ? up : 0);
-  unsigned long long pkx = 0ull, pkw = 0ull;
-  if (t == 0 && can_go) {
-    pkx = __hip_atomic_load(pk_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    pkw = __hip_atomic_load(pk_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
   const int nk = sm.nk;
   if (t < nk) {
     if (t < 64) {
@@ -1014,13 +984,11 @@ __device__ __forceinline__ void node_body(const StochParams& p, NodeSmem<kRes>& 
 
   // children in ascending id, one team-wide evaluation of F per rejection
   double Cres = 0.0, Dres = 1.0;
-  int accepted = -1, cur = -1, stop = nk;
-  bool gone = false;
+  int accepted = -1, cur = -1;
   for (int i = 0; i < nk; ++i) {
     const double px = sm.kpx[i], qx = sm.kqx[i];
     if ((double)sm.kua[i] * qx * Dres <= fmax(px - Cres * qx, 0.0)) {
       accepted = sm.kids[i];
-      stop = i;
       break;
     }
     const double cn = Cres + Dres;
@@ -1075,54 +1043,30 @@ __device__ __forceinline__ void node_body(const StochParams& p, NodeSmem<kRes>& 
         for (int i2 = 0; i2 < kSThreads / 64; ++i2) r1 += sm.part[i2][l + 64];
       const double mine = tv_wave_sum_d(r0 + r1);
       unsigned long long* xs = p.xch + ((size_t)b * p.n_max + sm.kids[i]) * kMaxTeam;
-      if (l == 0) {
-        const bool seen = can_go && off_path(pkx, pkw, p.S, u);
-        xch_put(xs + member, seen ? kGoneMass : (unsigned long long)__double_as_longlong(mine));
-        if (can_go) {   // the next look, answered by the time the team's masses are in
-          pkx = __hip_atomic_load(pk_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          pkw = __hip_atomic_load(pk_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+      if (l == 0) xch_put(xs + member, (unsigned long long)__double_as_longlong(mine));
       double xv = 0.0;
       if (l < p.S) xv = __longlong_as_double((long long)xch_get(xs + l, &sm.timeout));
-      const bool team_gone = __ballot(l < p.S && xv != xv) != 0ull;
-      const double F = team_gone ? 0.0 : tv_readlane_d(tv_row16_sum_d(xv), 0);
+      const double F = tv_readlane_d(tv_row16_sum_d(xv), 0);
       if (F > 0.0) {   // the residual moves: keep its member and chunk masses
         if (l < p.S) sm.xcur[l] = xv;
         if (l < nmine) sm.rcur[l] = r0;
         if (l + 64 < nmine) sm.rcur[l + 64] = r1;
       }
-      if (l == 0) {
-        sm.Fx = F;
-        sm.sel = team_gone;
-      }
+      if (l == 0) sm.Fx = F;
     }
     tv_lds_barrier();
     const double F = sm.Fx;
-    if (sm.sel) {   // some member saw the node fall off the path: the team stops here
-      gone = true;
-      stop = i;
-      break;
-    }
     if (F > 0.0) {   // Z > 0: move to the new residual
       Cres = cn;
       Dres = F;
       cur = i;
     }
   }
-  // children past the stopping point will never be tested: member 0 marks them
-  // (from wave 0, whose exchange stores land before the node's word is ORed)
-  if (member == 0 && w == 0)
-    for (int j = stop + 1 + l; j < nk; j += 64)
-      xch_put(p.xch + ((size_t)b * p.n_max + sm.kids[j]) * kMaxTeam, kUntested);
-  if (gone) return;
 
   if (accepted < 0) {
     // the node's draw: inverse CDF over member masses, this member's chunk
     // masses, then inside one chunk; masses are those of p while no rejection
-    // has moved the residual, else of the current residual.  A member that has
-    // seen the node fall off the path skips it (no exchange follows).
-    if (t == 0) sm.owner = can_go && off_path(pkx, pkw, p.S, u) ? -2 : -1;
+    // has moved the residual, else of the current residual
     if (cur < 0) {
       if (t < p.S) {   // member masses of p, parallel over members
         double x = 0.0;
@@ -1132,8 +1076,6 @@ __device__ __forceinline__ void node_body(const StochParams& p, NodeSmem<kRes>& 
       if (t < nmine) sm.rcur[t] = sm.cs[0][t] * sm.ca[0][my_c0 + t];
     }
     tv_lds_barrier();
-    if (sm.owner == -2) return;
-    tv_lds_barrier();   // every thread has read the mark before wave 0 overwrites it
     if (w == 0) {   // member, then chunk, by wave scans
       const double x = l < p.S ? sm.xcur[l] : 0.0;
       const double total = tv_readlane_d(tv_wave_incl_scan_d(x, l), 63);
