@@ -105,7 +105,7 @@ def gated_us_per_call(call, reps: int, cyc_per_s: float) -> float:
 
 def kernel_is(name: str, full: str) -> bool:
     """True when the profiler's kernel name `full` is kernel `name` (a whole
-    identifier: compact_kernel is not stoch_chase_compact_kernel)."""
+    identifier: merge_kernel is not tree_merge_kernel)."""
     return re.search(r"(?<![A-Za-z0-9_])" + re.escape(name) + r"(?![A-Za-z0-9_])", full) is not None
 
 
@@ -135,10 +135,10 @@ def traffic_record(kernel: str, workload: str, src_hash: str):
 # kernels launched by each entry point (rocprofv3 kernel names contain these)
 ENTRY_KERNELS = {
     "tree_attn": ("tree_attn_kernel", "attn_merge_kernel"),
-    "tree_verify_stochastic": ("stoch_node_kernel", "stoch_chase_kernel"),
+    "tree_verify_stochastic": ("stoch_node_kernel",),
     "tree_verify_greedy": ("greedy_argmax_kernel", "greedy_chase_kernel"),
     "kv_compact": ("compact_kernel",),
-    "tree_verify_stochastic_compact": ("stoch_node_kernel", "stoch_chase_compact_kernel"),
+    "tree_verify_stochastic_compact": ("stoch_node_kernel",),
 }
 ENTRY_SOURCES = {"tree_attn": ("tree_attn.hip",), "tree_verify_stochastic": ("tree_verify.hip",),
                  "tree_verify_greedy": ("tree_verify.hip",), "kv_compact": ("kv_compact.hip", "tv_compact.h"),

@@ -374,6 +374,7 @@ struct StochParams {
   int32_t* status;
   // workspace
   const unsigned long long* header;   // [2]: kWsMagic, bytes zero-filled by tree_verify_workspace_init
+  unsigned long long* header_w;       // the same, for invalidating it after an expired wait
   unsigned long long need;            // bytes this call's layout uses (header included)
   unsigned long long* xch;   // [nodes][kMaxTeam]    member masses after child `node` is rejected
   unsigned long long* sxch;  // [nodes][chunks][4] chunk (max, sum) of the target and draft rows
@@ -383,7 +384,15 @@ struct StochParams {
   int B, n_max, V, chunks, S, per;   // per = chunks per team member
   float k2hi, k2lo;                  // log2(e) / T as a float32 head and tail
   double invT_d;
+  int G;            // node workgroups; the B workgroups after them chase the paths
+  int chase_mode;   // kChaseOnly, or the chase then the KV compaction of cpt
+  TvCompactArgs cpt;
 };
+
+// What the workgroups that follow the node workgroups do for their request:
+// walk the path, or walk it and then compact the request's KV along it (bf16
+// or float32 caches).
+enum { kChaseOnly = 0, kChaseCompactBf16 = 1, kChaseCompactF32 = 2 };
 
 // The stochastic verifier's workspace starts with a header that
 // tree_verify_workspace_init writes after zero-filling the rest: a magic word
@@ -403,7 +412,8 @@ constexpr size_t kWsHeader = 256;
 constexpr int kNwAccShift = 32, kNwFlagShift = 40, kNwDoneShift = 48;
 
 __device__ __forceinline__ bool ws_ok(const StochParams& p) {
-  return p.header[0] == kWsMagic && p.header[1] >= p.need;
+  const unsigned long long magic = p.header[0], bytes = p.header[1];   // both loads at once
+  return (magic == kWsMagic) & (bytes >= p.need);
 }
 
 // exp(d / T) for d <= 0 in float32: exp2 of d * log2(e) / T, with the product
@@ -437,6 +447,16 @@ __device__ __forceinline__ float chunk_rho(double ia, double b, double c) {
 struct ChaseSmem {
   int acc[kMaxNodes], fin[kMaxNodes], tok[kMaxNodes], path[kMaxNodes];
   int flags, badpar, len, bad;
+};
+
+constexpr int kStagedBlocks = kMaxNodes / 16 + 2;   // blocks holding n <= 128 positions (block size >= 16)
+
+// A chase workgroup's LDS (it shares the node kernel's): the chase's arrays,
+// and for the compaction the block-table entries it reads while it waits.
+struct ChaseTailSmem {
+  ChaseSmem c;
+  int first_bad;
+  int stage[kStagedBlocks];
 };
 
 template <bool kRes>
@@ -690,28 +710,46 @@ __device__ int wave_select_mass(const double* m, int count, double thr, double* 
 
 // What the chase reads of request b, one entry per thread (thread t < n holds
 // node t's): its flags, accepted child and draw (from the node's result word),
-// token and parent.
+// token and parent; done: the word was complete.
 struct ChaseLoads {
   int fl, acc, fin, tk, pv, n;
-  bool ws_ok;
+  bool ws_ok, done;
 };
 
-// Issues every load of request b's rows at once, before n_nodes is known (rows
-// are n_max long; entries past n are not used).  Every member of a node has
-// ORed its part of the word before the node kernel ended.
-__device__ __forceinline__ ChaseLoads chase_load(const StochParams& p, int b) {
+// Bounded wait of a chase workgroup: about 2 s of polling.
+constexpr long long kChaseSpinLimit = kSpinLimit << 2;
+
+// Issues the loads of request b's rows at once (rows are n_max long; entries
+// past n are not used), then polls the result words of nodes 0 .. n-1 until
+// every member of each node has ORed its part.  A word still incomplete when
+// the wait expires is flagged TV_REQ_TIMEOUT and left as it is.
+__device__ __forceinline__ ChaseLoads chase_gather(const StochParams& p, int b) {
   const int t = threadIdx.x;
   const size_t kv = (size_t)b * p.n_max + t;
-  ChaseLoads c{0, -1, 0, 0, -1, 0, ws_ok(p)};
+  ChaseLoads c{0, -1, 0, 0, -1, 0, ws_ok(p), true};
+  c.n = p.n_nodes[b];
   if (t < p.n_max) {
-    const unsigned long long wv = p.nword[kv];
-    c.fl = (int)((wv >> kNwFlagShift) & 0xffu);
-    c.acc = (int)((wv >> kNwAccShift) & 0xffu) - 1;
-    c.fin = (int)(uint32_t)wv;
     c.tk = p.tokens[kv];
     c.pv = p.parent[kv];
   }
-  c.n = p.n_nodes[b];
+  const bool mine = c.ws_ok && c.n >= 1 && c.n <= p.n_max && t < c.n;
+  const unsigned long long full = ((1ull << p.S) - 1ull) << kNwDoneShift;
+  unsigned long long wv = 0;
+  bool done = !mine;
+  for (long long it = 0;; ++it) {
+    if (!done) {
+      wv = __hip_atomic_load(p.nword + kv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      done = (wv & full) == full;
+    }
+    if (__all(done) || it > kChaseSpinLimit) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (mine) {
+    c.done = done;
+    c.fl = (int)((wv >> kNwFlagShift) & 0xffu) | (done ? 0 : TV_REQ_TIMEOUT);
+    c.acc = (int)((wv >> kNwAccShift) & 0xffu) - 1;
+    c.fin = (int)(uint32_t)wv;
+  }
   return c;
 }
 
@@ -724,16 +762,13 @@ __device__ int chase_request(const StochParams& p, ChaseSmem& sm, int b, const C
   const int t = threadIdx.x;
   const size_t kv = (size_t)b * p.n_max + t;
   const int n = c.n;
-  if (n < 1 || n > p.n_max) {
+  // status and path_len are written once, by thread 0, at the end
+  int st = 0;
+  if (n < 1 || n > p.n_max) st = TV_REQ_BAD_NNODES;
+  else if (!c.ws_ok) st = TV_REQ_BAD_WORKSPACE;   // nothing of the workspace is trusted, read or cleared
+  if (st) {
     if (t == 0) {
-      p.status[b] = TV_REQ_BAD_NNODES;
-      p.path_len[b] = 0;
-    }
-    return 0;
-  }
-  if (!c.ws_ok) {   // nothing of the workspace is trusted, read or cleared
-    if (t == 0) {
-      p.status[b] = TV_REQ_BAD_WORKSPACE;
+      p.status[b] = st;
       p.path_len[b] = 0;
     }
     return 0;
@@ -744,7 +779,12 @@ __device__ int chase_request(const StochParams& p, ChaseSmem& sm, int b, const C
   }
   __syncthreads();
   if (t < n) {
-    p.nword[kv] = 0;
+    // A complete word is cleared for the next call.  An incomplete one (its
+    // team's waits expired) may still be ORed: the workspace header is
+    // invalidated instead, so that later calls report TV_REQ_BAD_WORKSPACE
+    // until the workspace is prepared again.
+    if (c.done) p.nword[kv] = 0;
+    else p.header_w[0] = 0;
     if (c.fl) atomicOr(&sm.flags, c.fl);
     sm.acc[t] = c.acc;
     sm.fin[t] = c.fin;
@@ -753,12 +793,9 @@ __device__ int chase_request(const StochParams& p, ChaseSmem& sm, int b, const C
   }
   __syncthreads();
   if (t == 0) {
-    const int fl = sm.badpar ? TV_REQ_BAD_PARENT : sm.flags;
-    if (fl) {
-      p.status[b] = fl;
-      p.path_len[b] = 0;
-      sm.len = 0;
-    } else {
+    st = sm.badpar ? TV_REQ_BAD_PARENT : sm.flags;
+    int len = 0;
+    if (!st) {
       int32_t* path = p.path + (size_t)b * p.n_max;
       int32_t* out = p.out_tokens + (size_t)b * p.n_max;
       int cur = 0, j = 0;
@@ -774,10 +811,11 @@ __device__ int chase_request(const StochParams& p, ChaseSmem& sm, int b, const C
         cur = ch;
       }
       out[j] = sm.fin[cur];
-      p.path_len[b] = j + 1;
-      p.status[b] = 0;
-      sm.len = j + 1;
+      len = j + 1;
     }
+    p.status[b] = st;
+    p.path_len[b] = len;
+    sm.len = len;
   }
   __syncthreads();
   return sm.len;
@@ -1141,6 +1179,44 @@ __device__ __forceinline__ void node_body(const StochParams& p, NodeSmem<kRes>& 
   o.acc = accepted;
 }
 
+// The chase of request b by one of the B workgroups that follow the node
+// workgroups in the grid.  Dispatched in id order, it takes a slot only after
+// every node workgroup has one, so it never holds one a team needs.  It issues
+// its loads at once (for the compaction also the block-table entries it checks
+// and uses: every entry among those of positions [0, P + n), the path's last
+// node being below n, and the entries of positions [P, P + n) kept for the
+// moves), waits for the request's node words, walks the path, and in the
+// verify-and-compact form then compacts the request's KV heads along it
+// (tv_compact.h), so the path never round-trips through memory.
+__device__ __forceinline__ void chase_tail(const StochParams& p, ChaseTailSmem& sm, int b) {
+  const int t = threadIdx.x;
+  int P = 0, stage0 = 0;
+  if (p.chase_mode != kChaseOnly) {
+    const TvCompactArgs& c = p.cpt;
+    if (t == 0) sm.first_bad = kTvNoBadBlock;
+    __syncthreads();
+    const int n = p.n_nodes[b];
+    P = c.prefix_len[b];
+    if (n >= 1 && n <= p.n_max && P >= 0) {
+      const int nblk_max = (int)min(((long long)P + n - 1) / c.bs + 1, (long long)c.max_blocks);
+      stage0 = P / c.bs;
+      const int32_t* trow = c.table + (size_t)b * c.max_blocks;
+      for (int i = t; i < nblk_max; i += blockDim.x) {
+        const int blk = trow[i];
+        if (blk < 0 || blk >= c.num_blocks) atomicMin(&sm.first_bad, i);
+        if (i >= stage0) sm.stage[i - stage0] = blk;
+      }
+    }
+  }
+  const int len = chase_request(p, sm.c, b, chase_gather(p, b));   // synchronises before it returns
+  if (p.chase_mode == kChaseOnly) return;
+  const TvTablePrefetch pre{sm.first_bad, stage0, sm.stage};
+  if (p.chase_mode == kChaseCompactBf16)
+    tv_compact_heads<uint16_t>(p.cpt, b, 0, p.cpt.Hkv, sm.c.path, len, P, &pre, &sm.c.bad);
+  else
+    tv_compact_heads<float>(p.cpt, b, 0, p.cpt.Hkv, sm.c.path, len, P, &pre, &sm.c.bad);
+}
+
 // One team of S workgroups per node (team = blockIdx / S, members on consecutive
 // ids), each member owning `per` consecutive chunks of the vocabulary.  Every
 // member reads its slice of the target row (and of the draft row when the node
@@ -1157,18 +1233,38 @@ __device__ __forceinline__ void node_body(const StochParams& p, NodeSmem<kRes>& 
 // loads in flight and runs three.
 template <bool kRes, bool kVec>
 __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes ? 4 : 2))) void stoch_node_kernel(StochParams p) {
-  __shared__ NodeSmem<kRes> sm;
+  __shared__ union {
+    NodeSmem<kRes> node;
+    ChaseTailSmem chase;
+  } smu;
+  // A node workgroup's first loads (its request's size, the workspace header)
+  // are issued before it is known whether this is a chase workgroup: a
+  // separate test ahead of them would delay every node workgroup by one more
+  // dependent load.
+  const bool chase = (int)blockIdx.x >= p.G;
   const int t = threadIdx.x;
   // With the whole grid resident, team members are numbered so that they run
   // on one XCD (workgroup i goes to XCD i mod 8), where their exchange hand-offs
   // are shorter.  Otherwise teams stay consecutive workgroup ids, which in-order
   // dispatch makes resident one after another.
-  const int lid = p.xcd_teams ? tv_xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int lid = p.xcd_teams ? tv_xcd_remap(blockIdx.x, p.G) : blockIdx.x;
   const int k = lid / p.S, member = lid % p.S;
-  const int b = k / p.n_max, u = k % p.n_max;
+  const int b = min(k / p.n_max, p.B - 1), u = k % p.n_max;   // b clamped for chase workgroups
   const int n = p.n_nodes[b];
+  const bool wsok = ws_ok(p);
+  asm volatile("" : : "v"(n), "v"((int)wsok));   // keeps the loads above the branch
+  if (chase) {
+    // The chase reads its arguments through an opaque copy of the argument
+    // pointer, so that the compiler does not hoist them above this branch and
+    // keep them live (in spilled scalar registers) through the node's work.
+    const StochParams* kp = (const StochParams*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kp));
+    chase_tail(*kp, smu.chase, (int)blockIdx.x - kp->G);
+    return;
+  }
+  NodeSmem<kRes>& sm = smu.node;
   if (n < 1 || n > p.n_max || u >= n) return;
-  if (!ws_ok(p)) return;   // the chase reports it; no slot is read or written
+  if (!wsok) return;   // the chase reports it; no slot is read or written
   NodeOut o{0, -1, 0, false};
   node_body<kRes, kVec>(p, sm, k, member, b, u, n, o);
   __syncthreads();
@@ -1197,52 +1293,6 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
       xc[i % (kMaxTeam / 2)] = z;
     }
   }
-}
-
-constexpr int kChaseThreads = 256;
-
-// One workgroup per request: status, the accepted path and its final token.
-__global__ __launch_bounds__(kChaseThreads) void stoch_chase_kernel(StochParams p) {
-  __shared__ ChaseSmem sm;
-  chase_request(p, sm, blockIdx.x, chase_load(p, blockIdx.x));
-}
-
-// Verify-and-compact: the chase of request b, then the compaction of all its
-// KV heads along the path just found (tv_compact.h), in the same workgroup, so
-// no path round-trips through memory and no second launch is needed.  The
-// block-table entries the compaction checks and uses are read beside the
-// chase's rows, before the path is known: every entry among those of positions
-// [0, P + n) (the path's last node is below n), and the entries of positions
-// [P, P + n) kept for the moves.  1024 threads: one (KV head, element) pair
-// each up to n_kv_heads * head_dim = 1024, so every pair's moves take a single
-// load-then-store round trip.
-constexpr int kChaseCompactThreads = 1024;
-constexpr int kStagedBlocks = kMaxNodes / 16 + 2;   // blocks holding n <= 128 positions (block size >= 16)
-
-template <typename T>
-__global__ __launch_bounds__(kChaseCompactThreads) void stoch_chase_compact_kernel(StochParams p, TvCompactArgs c) {
-  __shared__ ChaseSmem sm;
-  __shared__ int s_first_bad;
-  __shared__ int s_stage[kStagedBlocks];
-  const int t = threadIdx.x, b = blockIdx.x;
-  const ChaseLoads cl = chase_load(p, b);
-  const int P = c.prefix_len[b];
-  if (t == 0) s_first_bad = kTvNoBadBlock;
-  __syncthreads();
-  int stage0 = 0;
-  if (cl.n >= 1 && cl.n <= p.n_max && P >= 0) {
-    const int nblk_max = (int)min(((long long)P + cl.n - 1) / c.bs + 1, (long long)c.max_blocks);
-    stage0 = P / c.bs;
-    const int32_t* trow = c.table + (size_t)b * c.max_blocks;
-    for (int i = t; i < nblk_max; i += blockDim.x) {
-      const int blk = trow[i];
-      if (blk < 0 || blk >= c.num_blocks) atomicMin(&s_first_bad, i);
-      if (i >= stage0) s_stage[i - stage0] = blk;
-    }
-  }
-  const int len = chase_request(p, sm, b, cl);   // synchronises before it returns
-  const TvTablePrefetch pre{s_first_bad, stage0, s_stage};
-  tv_compact_heads<T>(c, b, 0, c.Hkv, sm.path, len, P, &pre, &sm.bad);
 }
 
 // ===========================================================================
@@ -1506,8 +1556,9 @@ extern "C" int tree_verify_greedy_noalloc(const tv_verify_desc* desc, const floa
 
 namespace {
 
-// Checks the arguments of a stochastic verification and launches its node
-// kernel; on TV_OK, p holds the parameters the chase needs.
+// Checks the arguments of a stochastic verification and launches its kernel:
+// the node workgroups, then one workgroup per request that chases its path
+// (and compacts its KV when cpt is given).
 int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, const float* draft_logits,
                        const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
                        const float* u_accept, const float* u_sample, int32_t* path, int32_t* path_len,
@@ -1540,6 +1591,7 @@ int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, c
   p.status = status;
   char* ws = (char*)workspace;
   p.header = (const unsigned long long*)ws;
+  p.header_w = (unsigned long long*)ws;
   p.need = L.stoch_bytes;
   p.xch = (unsigned long long*)(ws + L.xch);
   p.sxch = (unsigned long long*)(ws + L.sxch);
@@ -1555,8 +1607,12 @@ int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, c
   p.k2hi = (float)k2;
   p.k2lo = (float)(k2 - (double)p.k2hi);
 
+  // node workgroups, then one chase workgroup per request
   const long long grid = nodes * tp.S;
-  if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  if (grid + desc->batch > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  p.G = (int)grid;
+  p.chase_mode = !cpt ? kChaseOnly : (cpt_bf16 ? kChaseCompactBf16 : kChaseCompactF32);
+  if (cpt) p.cpt = *cpt;
   // When the whole grid is resident at once (four workgroups per CU), load order
   // follows the number of children: each class waits a quarter of the time the
   // target rows take to stream at about 5.5 TB/s (measured on MI355X: 1.5 us per
@@ -1572,17 +1628,7 @@ int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, c
   }
   void (*kern)(StochParams) = resident ? (vec ? stoch_node_kernel<true, true> : stoch_node_kernel<true, false>)
                                         : (vec ? stoch_node_kernel<false, true> : stoch_node_kernel<false, false>);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kSThreads), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  if (!cpt) {
-    hipLaunchKernelGGL(stoch_chase_kernel, dim3((unsigned)desc->batch), dim3(kChaseThreads), 0, stream, p);
-  } else if (cpt_bf16) {
-    hipLaunchKernelGGL(stoch_chase_compact_kernel<uint16_t>, dim3((unsigned)desc->batch), dim3(kChaseCompactThreads),
-                       0, stream, p, *cpt);
-  } else {
-    hipLaunchKernelGGL(stoch_chase_compact_kernel<float>, dim3((unsigned)desc->batch), dim3(kChaseCompactThreads),
-                       0, stream, p, *cpt);
-  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)(grid + desc->batch)), dim3(kSThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
