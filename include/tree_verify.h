@@ -143,7 +143,10 @@ typedef struct tv_verify_desc {
  *   status [B]            TV_REQ_* flags (required)
  * Teams of workgroups that cooperate on one node wait on each other through
  * bounded spins; if a wait expires (other work holding the GPU for a long
- * time) the request gets TV_REQ_TIMEOUT instead of hanging.
+ * time) the request gets TV_REQ_TIMEOUT instead of hanging.  When the stochastic
+ * verifier's path chase itself gives up waiting for a node, it also invalidates
+ * the workspace: later calls report TV_REQ_BAD_WORKSPACE until
+ * tree_verify_workspace_init prepares it again.
  * Entries past path_len are not written. */
 
 /* Bytes of workspace either verifier needs for `desc`.  The two verifiers lay
@@ -232,8 +235,8 @@ int kv_compact_accepted(const tv_attn_desc* desc, void* k_cache, void* v_cache,
  * kv_compact_accepted gives them for that path.  kv_desc->batch and n_max must
  * equal desc->batch and n_max (TV_ERR_INVALID_ARG otherwise); the workspace is
  * tree_verify_workspace_size(desc) bytes, as for tree_verify_stochastic.
- * Batches of more than 4 requests run the chase and the compaction as two
- * kernels (the compaction then spreads over one workgroup per KV head). */
+ * The compaction moves 8 bytes at a time when both caches are 8-byte aligned;
+ * otherwise it runs as a second kernel that moves single elements. */
 int tree_verify_stochastic_compact(const tv_verify_desc* desc, const tv_attn_desc* kv_desc,
                                    const float* target_logits, const float* draft_logits,
                                    const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,

@@ -96,7 +96,7 @@ def test_fused_against_the_oracle(name):
     assert np.array_equal(d.v.float().cpu().numpy(), vref)
 
 
-@pytest.mark.parametrize("batch", [4, 8])   # one fused kernel / chase and compaction kernels
+@pytest.mark.parametrize("batch", [4, 8])
 def test_fused_failed_requests(batch):
     """Requests that fail verification (n_nodes out of range, a malformed parent
     array, a non-finite target logit, a token outside the vocabulary) get path_len
@@ -132,9 +132,9 @@ def test_fused_failed_requests(batch):
 
 
 def test_fused_repeated_calls_and_smaller_batch():
-    """Repeated calls reuse the workspace's exchange slots (both chase kernels clear
-    them): a second call, and calls on the first 5 and then the first 3 requests
-    (the two-kernel path, then the fused kernel), give the separate calls' results."""
+    """Repeated calls reuse the workspace's exchange slots and result words (each
+    call leaves them cleared): a second call, and calls on the first 5 and then
+    the first 3 requests, give the separate calls' results."""
     wl = _workload("ragged")
     print("case fused repeated calls (ragged, then its first 5 and 3 requests)", flush=True)
     d = DevWorkload(wl)
@@ -165,6 +165,34 @@ def test_fused_fp32_paged_block_sizes(bs):
     print(f"case fused fp32 paged block_size={bs}", flush=True)
     d = DevWorkload(wl)
     sep, fused = _both(d)
+    assert not sep[3].any() and not sep[6].any()
+    assert (sep[1] > 1).any()            # some request moves K/V
+    _same(sep, fused, wl)
+
+
+def test_fused_unaligned_caches():
+    """Caches that start 2 bytes past an 8-byte boundary: the fused call then
+    compacts with single-element moves in the compaction's own kernel; every
+    output still equals the separate calls'."""
+    import torch
+    wl = make_workload("tiny", seed=321, batch=2)
+    print("case fused unaligned caches", flush=True)
+    d = DevWorkload(wl)
+
+    def shifted(x):
+        buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)
+        y = buf[1:].view(x.shape)
+        y.copy_(x)
+        assert y.data_ptr() % 8 != 0
+        return y
+
+    k1, v1, k2, v2 = d.k.clone(), d.v.clone(), shifted(d.k), shifted(d.v)
+    p, l, t, s = tv.tree_verify_stochastic(d.target, d.draft, d.tokens, d.parent, d.n_nodes, d.u_accept, d.u_sample)
+    src, nl, kst = tv.kv_compact_accepted(k1, v1, d.table, d.prefix_len, p, l)
+    sep = [x.cpu().numpy() for x in (p, l, t, s, src, nl, kst, k1.float(), v1.float())]
+    res = tv.tree_verify_stochastic_compact(d.target, d.draft, d.tokens, d.parent, d.n_nodes, d.u_accept,
+                                            d.u_sample, k2, v2, d.table, d.prefix_len)
+    fused = [x.cpu().numpy() for x in res] + [k2.float().cpu().numpy(), v2.float().cpu().numpy()]
     assert not sep[3].any() and not sep[6].any()
     assert (sep[1] > 1).any()            # some request moves K/V
     _same(sep, fused, wl)

@@ -194,17 +194,25 @@ def test_decisions_just_outside_the_band():
     del d0
 
 
+def _same_results(a, b):
+    """(path, path_len, out_tokens, status) equal; path and out_tokens only up
+    to path_len (entries past it are not written)."""
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[3], b[3])
+    for r, L in enumerate(a[1]):
+        assert np.array_equal(a[0][r, :L], b[0][r, :L]) and np.array_equal(a[2][r, :L], b[2][r, :L])
+
+
 def test_repeat_calls_identical():
     wl = make_workload("ragged", seed=91, batch=4, prefix=(1, 2), vocab=9001)
     d = DevWorkload(wl)
     a = gpu_stoch(d)
     b = gpu_stoch(d)
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
+    assert (a[1] > 0).all()
+    _same_results(a, b)
     a = gpu_greedy(d)
     b = gpu_greedy(d)
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
+    assert (a[1] > 0).all()
+    _same_results(a, b)
 
 
 def test_stochastic_unprepared_workspace_is_reported():

@@ -1211,10 +1211,11 @@ __device__ __forceinline__ void chase_tail(const StochParams& p, ChaseTailSmem& 
   const int len = chase_request(p, sm.c, b, chase_gather(p, b));   // synchronises before it returns
   if (p.chase_mode == kChaseOnly) return;
   const TvTablePrefetch pre{sm.first_bad, stage0, sm.stage};
+  // 8-byte moves (the caches are 8-byte aligned on this path)
   if (p.chase_mode == kChaseCompactBf16)
-    tv_compact_heads<uint16_t>(p.cpt, b, 0, p.cpt.Hkv, sm.c.path, len, P, &pre, &sm.c.bad);
+    tv_compact_heads<uint16_t, 4>(p.cpt, b, 0, p.cpt.Hkv, sm.c.path, len, P, &pre, &sm.c.bad);
   else
-    tv_compact_heads<float>(p.cpt, b, 0, p.cpt.Hkv, sm.c.path, len, P, &pre, &sm.c.bad);
+    tv_compact_heads<float, 2>(p.cpt, b, 0, p.cpt.Hkv, sm.c.path, len, P, &pre, &sm.c.bad);
 }
 
 // One team of S workgroups per node (team = blockIdx / S, members on consecutive
@@ -1354,11 +1355,6 @@ int resident_per_cu(bool vec) {
   return per[dev][vec];
 }
 
-// Batches above this size take the chase and the compaction as two kernels
-// (measured on MI355X: one request gains ~1.4 us per step from the fused
-// kernel; 16 and 64 requests lose 10-14 us, their moves crowded onto one CU
-// per request).
-constexpr int kFusedChaseMaxBatch = 4;
 
 struct TeamPlan {
   int S;     // workgroups per node
@@ -1676,9 +1672,9 @@ static int tree_verify_stochastic_compact_impl(const tv_verify_desc* desc, const
   if (kv_desc->batch != desc->batch || kv_desc->n_max != desc->n_max) return TV_ERR_INVALID_ARG;
   if (desc->batch == 0) return TV_OK;
   if (!k_cache || !v_cache || !block_table || !prefix_len || !src_pos || !new_len) return TV_ERR_INVALID_ARG;
-  if (desc->batch > kFusedChaseMaxBatch) {
-    // many requests: the compaction's own grid of one workgroup per (request,
-    // KV head) after the verification spreads the moves over more CUs
+  if ((((uintptr_t)k_cache | (uintptr_t)v_cache) & 7) != 0) {
+    // caches not aligned to 8 bytes: the compaction's own kernel, which moves
+    // single elements, after the verification
     rc = launch_stoch_nodes(desc, target_logits, draft_logits, tokens, parent, n_nodes, u_accept, u_sample, path,
                             path_len, out_tokens, status, workspace, workspace_bytes, nullptr, 0, stream);
     if (rc != TV_OK) return rc;

@@ -16,6 +16,8 @@
 
 #include "tv_common.h"
 
+#include <type_traits>
+
 struct TvCompactArgs {
   void* k;
   void* v;
@@ -40,13 +42,21 @@ struct TvTablePrefetch {
   const int* stage;
 };
 
+// The unit one thread moves: W elements of type T (W = 1: the element itself;
+// otherwise 8 bytes, which needs caches aligned to 8 bytes).
+template <typename T, int W>
+struct TvMoveUnit {
+  static_assert(W == 1 || sizeof(T) * W == 8, "a move unit is one element or 8 bytes");
+  using type = typename std::conditional<W == 1, T, uint2>::type;
+};
+
 // Compacts KV heads g0 .. g0 + ng - 1 of request b.  Every thread of the
-// workgroup calls this (it synchronises); thread t owns the (head, element)
-// pairs t, t + blockDim.x, ... of the ng * D.  path: the request's path (global
-// or LDS), L1 its length (0: nothing accepted), P its prefix_len.  pre: table
-// entries read ahead (null: read here).  The workgroup holding head 0 writes
-// src_pos, new_len and status.
-template <typename T>
+// workgroup calls this (it synchronises); thread t owns the units of W
+// consecutive (head, element) pairs t, t + blockDim.x, ... of the ng * D / W.
+// path: the request's path (global or LDS), L1 its length (0: nothing
+// accepted), P its prefix_len.  pre: table entries read ahead (null: read
+// here).  The workgroup holding head 0 writes src_pos, new_len and status.
+template <typename T, int W = 1>
 __device__ void tv_compact_heads(const TvCompactArgs& p, int b, int g0, int ng, const int32_t* path, int L1, int P,
                                  const TvTablePrefetch* pre, int* s_bad) {
   const int t = threadIdx.x;
@@ -97,32 +107,36 @@ __device__ void tv_compact_heads(const TvCompactArgs& p, int b, int g0, int ng, 
   }
   if (!active) return;
 
-  T* K = (T*)p.k;
-  T* V = (T*)p.v;
-  for (int e = t; e < ng * p.D; e += blockDim.x) {
-    const int g = g0 + e / p.D, d = e % p.D;
-    for (int j0 = 1; j0 < L1; j0 += kTvCompactStage) {
-      T kreg[kTvCompactStage], vreg[kTvCompactStage];
+  using U = typename TvMoveUnit<T, W>::type;
+  // a batch of steps keeps 2 * kStage units in registers
+  constexpr int kStage = W == 1 ? kTvCompactStage : kTvCompactStage / 2;
+  U* K = (U*)p.k;
+  U* V = (U*)p.v;
+  const int DW = p.D / W;
+  for (int e = t; e < ng * DW; e += blockDim.x) {
+    const int g = g0 + e / DW, d = e % DW;
+    for (int j0 = 1; j0 < L1; j0 += kStage) {
+      U kreg[kStage], vreg[kStage];
 #pragma unroll
-      for (int i = 0; i < kTvCompactStage; ++i) {
+      for (int i = 0; i < kStage; ++i) {
         int j = j0 + i;
         if (j < L1 && path[j] != j) {
           int s = P + path[j];
           size_t blk = (size_t)(pre ? pre->stage[s / p.bs - pre->stage0] : trow[s / p.bs]);
           int slot = s % p.bs;
-          kreg[i] = K[((blk * p.Hkv + g) * p.bs + slot) * p.D + d];
-          vreg[i] = V[((blk * p.Hkv + g) * p.bs + slot) * p.D + d];
+          kreg[i] = K[((blk * p.Hkv + g) * p.bs + slot) * DW + d];
+          vreg[i] = V[((blk * p.Hkv + g) * p.bs + slot) * DW + d];
         }
       }
 #pragma unroll
-      for (int i = 0; i < kTvCompactStage; ++i) {
+      for (int i = 0; i < kStage; ++i) {
         int j = j0 + i;
         if (j < L1 && path[j] != j) {
           int dst = P + j;
           size_t blk = (size_t)(pre ? pre->stage[dst / p.bs - pre->stage0] : trow[dst / p.bs]);
           int slot = dst % p.bs;
-          K[((blk * p.Hkv + g) * p.bs + slot) * p.D + d] = kreg[i];
-          V[((blk * p.Hkv + g) * p.bs + slot) * p.D + d] = vreg[i];
+          K[((blk * p.Hkv + g) * p.bs + slot) * DW + d] = kreg[i];
+          V[((blk * p.Hkv + g) * p.bs + slot) * DW + d] = vreg[i];
         }
       }
     }
