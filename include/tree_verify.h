@@ -153,9 +153,9 @@ typedef struct tv_verify_desc {
  * their workspaces out differently: give each its own buffer. */
 size_t tree_verify_workspace_size(const tv_verify_desc* desc);
 
-/* Prepares a stochastic verifier's workspace (256-byte aligned, at least
+/* Prepares a verifier's workspace (256-byte aligned, at least
  * tree_verify_workspace_size bytes for the descriptors it will serve): zeroes
- * it and writes the header the verifier checks.  Enqueued on `stream`.
+ * it and writes the header the verifier checks.  Both verifiers need it.  Enqueued on `stream`.
  * TV_ERR_WORKSPACE for a null or too small buffer, TV_ERR_INVALID_ARG when
  * it is not 256-byte aligned. */
 int tree_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -164,7 +164,9 @@ int tree_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStrea
  * t = argmax_w target_logits[b][u][w] (lowest index among equal maxima); move to
  * the first child c (ascending node id) with tokens[b][c] == t, else emit t and
  * stop.  A leaf emits its argmax.
- *   target_logits [B][n_max][V] float32 (rows u < n read); tokens, parent [B][n_max]. */
+ *   target_logits [B][n_max][V] float32 (rows u < n read); tokens, parent [B][n_max].
+ * The workspace must have been prepared by tree_verify_workspace_init (each
+ * call leaves it prepared); an unprepared one gives TV_REQ_BAD_WORKSPACE. */
 int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
                        const int32_t* tokens, const int32_t* parent, const int32_t* n_nodes,
                        int32_t* path, int32_t* path_len, int32_t* out_tokens, int32_t* status,
@@ -172,8 +174,9 @@ int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
 
 /* tree_verify_greedy without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid hipMalloc).  Its scratch -- one 64-bit key and one flag
- * per (node, 8192-logit chunk): 12 * B * n_max * ceil(V / 8192) bytes -- lives
+ * harnesses that forbid hipMalloc).  Its scratch -- one 64-bit key per (node,
+ * 8192-logit chunk) after a 256-byte header: 256 + 8 * B * n_max * ceil(V / 8192)
+ * bytes, rounded up to a multiple of 256 -- lives
  * in a static array of tree_verify_greedy_noalloc_max_scratch() bytes (4 MiB)
  * that every GPU the library runs on holds until the process ends; the call
  * allocates nothing.  Descriptors needing more scratch return TV_ERR_WORKSPACE

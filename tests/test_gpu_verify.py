@@ -253,3 +253,38 @@ def test_stochastic_unprepared_workspace_is_reported():
                                            d.u_sample, ws=small)
     torch.cuda.synchronize()
     assert list(s.cpu().numpy()) == [tv.REQ_BAD_WORKSPACE] * wl.batch
+
+
+def test_greedy_unprepared_workspace_is_reported():
+    """The greedy verifier's workspace: unprepared (random bytes) fails every
+    request with TV_REQ_BAD_WORKSPACE; once prepared, repeated calls give the
+    oracle's paths (each call leaves the key slots cleared); a prepared buffer
+    too small for the layout is refused."""
+    wl = make_workload("llama8b", seed=52, vocab=30011, n_nodes=20, batch=3)
+    d = DevWorkload(wl)
+    from tree_verification_amd.binding import VerifyDesc, load_library
+    lib = load_library()
+    desc = VerifyDesc()
+    desc.batch, desc.n_max, desc.vocab, desc.temperature = wl.batch, wl.n_max, wl.vocab, 1.0
+    import ctypes
+    need = lib.tree_verify_workspace_size(ctypes.byref(desc))
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda:0")
+    _, l, _, s = tv.tree_verify_greedy(d.target, d.tokens, d.parent, d.n_nodes, ws=ws)
+    torch.cuda.synchronize()
+    assert list(s.cpu().numpy()) == [tv.REQ_BAD_WORKSPACE] * wl.batch
+    assert not l.cpu().numpy().any()
+    tv.init_verify_workspace(ws)
+    paths, outs, st = verify_greedy(wl.target_logits, wl.tokens, wl.parent, wl.n_nodes, wl.n_max)
+    for _ in range(3):
+        p, l, t, s = tv.tree_verify_greedy(d.target, d.tokens, d.parent, d.n_nodes, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(s.cpu().numpy(), st)
+        gp, gl, gt = p.cpu().numpy(), l.cpu().numpy(), t.cpu().numpy()
+        for b in range(wl.batch):
+            L = int(gl[b])
+            assert list(gp[b, :L]) == list(paths[b]) and list(gt[b, :L]) == list(outs[b]), b
+    small = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    tv.init_verify_workspace(small[:512])
+    _, _, _, s = tv.tree_verify_greedy(d.target, d.tokens, d.parent, d.n_nodes, ws=small)
+    torch.cuda.synchronize()
+    assert list(s.cpu().numpy()) == [tv.REQ_BAD_WORKSPACE] * wl.batch

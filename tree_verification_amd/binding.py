@@ -142,8 +142,8 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
 
 
 # Workspaces: each (device, stream, kind, descriptor) gets its own buffer.  The
-# stochastic verifier's is prepared once with tree_verify_workspace_init (every
-# call leaves its exchange slots at zero again).
+# verifiers' are prepared once with tree_verify_workspace_init (every call
+# leaves its slots at zero again).
 _ws: dict = {}
 
 
@@ -159,14 +159,14 @@ def workspace(nbytes: int, device: torch.device, kind: str, desc=None) -> torch.
     buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        if kind == "stochastic":
+        if kind in ("stochastic", "greedy"):
             init_verify_workspace(buf)
         _ws[key] = buf
     return buf
 
 
 def init_verify_workspace(buf: torch.Tensor) -> torch.Tensor:
-    """Prepare a stochastic verifier workspace (uint8 GPU tensor) in place."""
+    """Prepare a verifier workspace (uint8 GPU tensor) in place."""
     lib = load_library()
     rc = lib.tree_verify_workspace_init(_ptr(buf), buf.numel(), _stream(buf.device))
     _check(rc, "tree_verify_workspace_init")

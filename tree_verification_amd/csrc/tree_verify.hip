@@ -73,6 +73,16 @@ constexpr int kResident = 2;                        // chunks a member holds in 
 constexpr long long kSpinLimit = 1LL << 19;         // bounded waits (~0.5 s), then TV_REQ_TIMEOUT
 constexpr unsigned long long kWritten = 1ull << 63;  // marks a published exchange slot
 constexpr int kPrioSteps = 3;                        // load-order classes: 0, 1, 2, 3+ children
+constexpr long long kChaseSpinLimit = kSpinLimit << 2;   // a chase workgroup's bounded wait (~2 s)
+
+// A verifier's workspace starts with a header that
+// tree_verify_workspace_init writes after zero-filling the rest: a magic word
+// and the number of bytes it cleared.  The verifiers' slots tell a published
+// value from an empty one by their contents and every call leaves them at
+// zero, so a workspace that was never initialised (or is too small for this
+// call's layout) must not be used: such a request gets TV_REQ_BAD_WORKSPACE.
+constexpr unsigned long long kWsMagic = 0x7476777370616365ull;
+constexpr size_t kWsHeader = 256;
 
 // Buffer resource over one logit row of V floats.  Buffer loads address the row
 // with a 32-bit offset plus an immediate (one VGPR per batch of loads instead of a
@@ -169,10 +179,20 @@ struct GreedyParams {
   int32_t* path_len;
   int32_t* out_tokens;
   int32_t* status;
-  unsigned long long* keys;   // [B][n_max][chunks] (value, index) maximum of each chunk
-  int* bad;                   // [B][n_max][chunks] 1 when the chunk holds NaN or +-inf
+  // [B][n_max][chunks] each chunk's largest (value, index) key, kGreedyBad when
+  // the chunk holds NaN or +-inf, 0 while it is not written
+  unsigned long long* keys;
+  const unsigned long long* header;   // prepared workspace header (null: the static scratch)
+  unsigned long long* header_w;       // the same, for invalidating it after an expired wait
+  unsigned long long need;            // bytes this call's layout uses (header included)
   int B, n_max, V, chunks;
+  int G;   // argmax workgroups; when the grid holds more, the B after them chase the paths
 };
+
+// A chunk's slot when it holds a non-finite logit.  Every key of a finite
+// value has its low word at 0x80000000 or above (index < 2^31), so neither 0
+// nor this value is a key.
+constexpr unsigned long long kGreedyBad = 1ull;
 
 // Order-preserving key: larger value first, then lower index.  -0 and +0 tie.
 __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
@@ -250,110 +270,172 @@ __device__ __forceinline__ void greedy_reduce(const GreedyParams& p, int unit, c
       fl |= redbad[i];
     }
     const size_t k = (size_t)(unit / p.chunks);
-    p.keys[k * p.chunks + c] = best;
-    p.bad[k * p.chunks + c] = fl;
+    __hip_atomic_store(p.keys + k * p.chunks + c, fl ? kGreedyBad : best, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// One workgroup per (node, chunk) unit.  Units of nodes past the request's
-// size load nothing (the size is read before the row: a grid with many dead
-// units, such as a batch of short chains padded to n_max, would otherwise
-// stream their rows for nothing).  Every output slot of a live unit is written
-// on every call: the workspace carries nothing from one call to the next.
-// (A persistent grid with two units in flight per workgroup measured slower:
-// 57.7 against 48.1 us for 512 nodes x 128256 logits.)
-template <bool kVec>
-__global__ __launch_bounds__(kGreedyThreads) void greedy_argmax_kernel(GreedyParams p) {
-  __shared__ unsigned long long s_red[kGreedyThreads / 64];
-  __shared__ int s_bad[kGreedyThreads / 64];
-  const int unit = blockIdx.x;
-  const int k = unit / p.chunks;
-  const int n = p.n_nodes[k / p.n_max];
-  if (n > p.n_max || k % p.n_max >= n) return;
-  GreedyUnit x;
-  greedy_issue<kVec>(p, unit, x);
-  greedy_reduce(p, unit, x, s_red, s_bad, true);
+struct GreedyChaseSmem {
+  int arg[kMaxNodes], child[kMaxNodes], tok[kMaxNodes];
+  int badpar, nonfinite, timeout;
+};
+
+__device__ __forceinline__ bool greedy_ws_ok(const GreedyParams& p) {
+  if (!p.header) return true;
+  const unsigned long long magic = p.header[0], bytes = p.header[1];   // both loads at once
+  return (magic == kWsMagic) & (bytes >= p.need);
 }
 
-__global__ __launch_bounds__(kMaxNodes) void greedy_chase_kernel(GreedyParams p) {
-  __shared__ int s_arg[kMaxNodes];
-  __shared__ int s_child[kMaxNodes];
-  __shared__ int s_tok[kMaxNodes];
-  __shared__ int s_badpar, s_nonfinite;
-  const int t = threadIdx.x, b = blockIdx.x;
+// The greedy chase of request b by one workgroup of at least kMaxNodes
+// threads: each node's argmax (the largest of its chunks' keys), each node's
+// first child whose token equals it, and the path from the root.  kPoll: the
+// argmax workgroups of the same grid may still be running; thread t waits
+// (bounded) until every chunk slot of node t is written and clears the slots
+// it read for the next call.  Otherwise the slots were all written before this
+// kernel started (and are overwritten by the next call).
+template <bool kPoll>
+__device__ void greedy_chase(const GreedyParams& p, GreedyChaseSmem& sm, int b) {
+  const int t = threadIdx.x;
   const int32_t* par = p.parent + (size_t)b * p.n_max;
   const int32_t* tok = p.tokens + (size_t)b * p.n_max;
-  // every load of the request's rows is issued at once, before n_nodes is
-  // known (rows are n_max long; entries past n are not used)
   const size_t kv = (size_t)b * p.n_max + t;
+  const int n = p.n_nodes[b];
+  const bool wsok = greedy_ws_ok(p);
   int pv = -1, tk = 0, flg = 0;
-  unsigned long long key = 0ull;
   if (t < p.n_max) {
     pv = par[t];
     tk = tok[t];
-    const unsigned long long* kp = p.keys + kv * p.chunks;
-    const int* bp = p.bad + kv * p.chunks;
+  }
+  const bool mine = wsok && n >= 1 && n <= p.n_max && t < n;
+  unsigned long long key = 0ull;
+  bool done = true;
+  if (mine) {
+    unsigned long long* kp = p.keys + kv * p.chunks;
     for (int c0 = 0; c0 < p.chunks; c0 += 16) {
       unsigned long long kc[16];
-      int bc[16];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        kc[c] = c0 + c < p.chunks ? kp[c0 + c] : 0ull;
-        bc[c] = c0 + c < p.chunks ? bp[c0 + c] : 0;
+      for (int c = 0; c < 16; ++c) kc[c] = 0ull;
+      for (long long it = 0;; ++it) {
+        bool all = true;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          if (c0 + c < p.chunks && kc[c] == 0ull)
+            kc[c] = kPoll ? __hip_atomic_load(kp + c0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kp[c0 + c];
+          all = all && (c0 + c >= p.chunks || kc[c] != 0ull);
+        }
+        if (!kPoll || all) break;
+        if (it > kChaseSpinLimit) {
+          done = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
         key = kc[c] > key ? kc[c] : key;
-        flg |= bc[c];
+        flg |= kc[c] == kGreedyBad;
+      }
+      if (!done) break;
+    }
+    if (kPoll) {
+      // A complete node's slots are cleared for the next call.  A node whose
+      // slots were not all written in time may still be written: the
+      // workspace header is invalidated instead, so that later calls report
+      // TV_REQ_BAD_WORKSPACE until the workspace is prepared again.
+      if (done) {
+        for (int c = 0; c < p.chunks; ++c) kp[c] = 0ull;
+      } else {
+        p.header_w[0] = 0;
       }
     }
   }
-  const int n = p.n_nodes[b];
-  if (n < 1 || n > p.n_max) {
+  int st = 0;
+  if (n < 1 || n > p.n_max) st = TV_REQ_BAD_NNODES;
+  else if (!wsok) st = TV_REQ_BAD_WORKSPACE;
+  if (st) {
     if (t == 0) {
-      p.status[b] = TV_REQ_BAD_NNODES;
+      p.status[b] = st;
       p.path_len[b] = 0;
     }
     return;
   }
   if (t == 0) {
-    s_badpar = 0;
-    s_nonfinite = 0;
+    sm.badpar = 0;
+    sm.nonfinite = 0;
+    sm.timeout = 0;
   }
   __syncthreads();
   if (t < n) {
-    s_arg[t] = (int)(0xFFFFFFFFu - (uint32_t)key);
-    s_child[t] = 0x7fffffff;
-    s_tok[t] = tk;
-    if (flg) s_nonfinite = 1;
-    if (!((t == 0) ? (pv == -1) : (pv >= 0 && pv < t))) s_badpar = 1;
+    sm.arg[t] = (int)(0xFFFFFFFFu - (uint32_t)key);
+    sm.child[t] = 0x7fffffff;
+    sm.tok[t] = tk;
+    if (flg) sm.nonfinite = 1;
+    if (!done) sm.timeout = 1;
+    if (!((t == 0) ? (pv == -1) : (pv >= 0 && pv < t))) sm.badpar = 1;
   }
   __syncthreads();
-  const int fl = s_badpar ? TV_REQ_BAD_PARENT : (s_nonfinite ? TV_REQ_NONFINITE : 0);
+  const int fl = sm.badpar ? TV_REQ_BAD_PARENT
+                           : (sm.timeout ? TV_REQ_TIMEOUT : (sm.nonfinite ? TV_REQ_NONFINITE : 0));
   if (fl == 0 && t >= 1 && t < n) {
-    if (tk == s_arg[pv]) atomicMin(&s_child[pv], t);
+    if (tk == sm.arg[pv]) atomicMin(&sm.child[pv], t);
   }
   __syncthreads();
   if (t == 0) {
-    if (fl) {
-      p.status[b] = fl;
-      p.path_len[b] = 0;
-      return;
+    int len = 0;
+    if (!fl) {
+      int32_t* path = p.path + (size_t)b * p.n_max;
+      int32_t* out = p.out_tokens + (size_t)b * p.n_max;
+      int cur = 0, j = 0;
+      path[0] = 0;
+      while (sm.child[cur] != 0x7fffffff && j + 1 < n) {
+        const int ch = sm.child[cur];
+        out[j] = sm.tok[ch];
+        path[++j] = ch;
+        cur = ch;
+      }
+      out[j] = sm.arg[cur];
+      len = j + 1;
     }
-    int32_t* path = p.path + (size_t)b * p.n_max;
-    int32_t* out = p.out_tokens + (size_t)b * p.n_max;
-    int cur = 0, j = 0;
-    path[0] = 0;
-    while (s_child[cur] != 0x7fffffff && j + 1 < n) {
-      const int ch = s_child[cur];
-      out[j] = s_tok[ch];
-      path[++j] = ch;
-      cur = ch;
-    }
-    out[j] = s_arg[cur];
-    p.path_len[b] = j + 1;
-    p.status[b] = 0;
+    p.status[b] = fl;
+    p.path_len[b] = len;
   }
+}
+
+// One workgroup per (node, chunk) unit, and (when the grid holds more than the
+// G units) one per request after them that chases its path.  In-order dispatch
+// places the chase workgroups only after every unit has a slot.  Units of
+// nodes past the request's size load nothing (the size is read before the
+// row: a grid with many dead units, such as a batch of short chains padded to
+// n_max, would otherwise stream their rows for nothing).  (A persistent grid
+// with two units in flight per workgroup measured slower: 57.7 against 48.1 us
+// for 512 nodes x 128256 logits.)
+template <bool kVec>
+__global__ __launch_bounds__(kGreedyThreads) void greedy_argmax_kernel(GreedyParams p) {
+  __shared__ union {
+    struct {
+      unsigned long long red[kGreedyThreads / 64];
+      int bad[kGreedyThreads / 64];
+    } a;
+    GreedyChaseSmem c;
+  } sm;
+  const int unit = blockIdx.x;
+  const int k = unit / p.chunks;
+  const int n = p.n_nodes[min(k / p.n_max, p.B - 1)];   // clamped for chase workgroups
+  if (unit >= p.G) {
+    greedy_chase<true>(p, sm.c, unit - p.G);
+    return;
+  }
+  if (n > p.n_max || k % p.n_max >= n) return;
+  GreedyUnit x;
+  greedy_issue<kVec>(p, unit, x);
+  greedy_reduce(p, unit, x, sm.a.red, sm.a.bad, true);
+}
+
+// The chase as a kernel of its own, after the argmax kernel (the static
+// scratch of tree_verify_greedy_noalloc, which no call prepares).
+__global__ __launch_bounds__(kMaxNodes) void greedy_chase_kernel(GreedyParams p) {
+  __shared__ GreedyChaseSmem sm;
+  greedy_chase<false>(p, sm, blockIdx.x);
 }
 
 // ===========================================================================
@@ -394,15 +476,6 @@ struct StochParams {
 // or float32 caches).
 enum { kChaseOnly = 0, kChaseCompactBf16 = 1, kChaseCompactF32 = 2 };
 
-// The stochastic verifier's workspace starts with a header that
-// tree_verify_workspace_init writes after zero-filling the rest: a magic word
-// and the number of bytes it cleared.  Exchange slots mark a published value
-// with their top bit and every call leaves them at zero, so a workspace that
-// was never initialised (or is too small for this call's layout) must not be
-// used; every workgroup checks the header (two scalar loads issued with the
-// request sizes) and such a request gets TV_REQ_BAD_WORKSPACE.
-constexpr unsigned long long kWsMagic = 0x7476777370616365ull;
-constexpr size_t kWsHeader = 256;
 
 // A node's result word, assembled by its team with one atomic OR per member:
 // the draw made when no child is accepted (bits 0-31, from the member that
@@ -715,9 +788,6 @@ struct ChaseLoads {
   int fl, acc, fin, tk, pv, n;
   bool ws_ok, done;
 };
-
-// Bounded wait of a chase workgroup: about 2 s of polling.
-constexpr long long kChaseSpinLimit = kSpinLimit << 2;
 
 // Issues the loads of request b's rows at once (rows are n_max long; entries
 // past n are not used), then polls the result words of nodes 0 .. n-1 until
@@ -1309,7 +1379,7 @@ int check_vdesc(const tv_verify_desc* d) {
 }
 
 struct VerifyLayout {
-  size_t g_keys, g_bad, greedy_bytes;
+  size_t g_keys, greedy_bytes;
   size_t xch, sxch, nword, stoch_bytes;
   int gchunks, chunks;
 };
@@ -1319,11 +1389,9 @@ VerifyLayout layout(const tv_verify_desc* d) {
   const size_t nodes = (size_t)d->batch * d->n_max;
   L.gchunks = (d->vocab + kGreedyChunk - 1) / kGreedyChunk;
   L.chunks = (d->vocab + kChunk - 1) / kChunk;
-  size_t o = 0;
+  size_t o = kWsHeader;
   L.g_keys = o;
   o = tv_align_up(o + nodes * L.gchunks * sizeof(unsigned long long), 256);
-  L.g_bad = o;
-  o = tv_align_up(o + nodes * L.gchunks * sizeof(int), 256);
   L.greedy_bytes = o;
   o = kWsHeader;
   L.xch = o;
@@ -1425,11 +1493,15 @@ static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
-// Checks the arguments of a greedy verification and launches its two kernels
-// with `ws` (at least greedy_bytes of the layout) as their scratch.
+// Checks the arguments of a greedy verification and launches it with `ws`
+// (at least greedy_bytes of the layout) as its scratch.  A prepared workspace
+// (header given) takes one kernel whose grid ends with the chase workgroups;
+// the static scratch (no header) takes the argmax kernel and then the chase
+// kernel.
 int launch_greedy(const tv_verify_desc* desc, const float* target_logits, const int32_t* tokens,
                   const int32_t* parent, const int32_t* n_nodes, int32_t* path, int32_t* path_len,
-                  int32_t* out_tokens, int32_t* status, char* ws, const VerifyLayout& L, hipStream_t stream) {
+                  int32_t* out_tokens, int32_t* status, char* ws, const VerifyLayout& L, bool prepared,
+                  hipStream_t stream) {
   GreedyParams p;
   p.logits = target_logits;
   p.tokens = tokens;
@@ -1440,19 +1512,23 @@ int launch_greedy(const tv_verify_desc* desc, const float* target_logits, const 
   p.out_tokens = out_tokens;
   p.status = status;
   p.keys = (unsigned long long*)(ws + L.g_keys);
-  p.bad = (int*)(ws + L.g_bad);
+  p.header = prepared ? (const unsigned long long*)ws : nullptr;
+  p.header_w = prepared ? (unsigned long long*)ws : nullptr;
+  p.need = L.greedy_bytes;
   p.B = desc->batch;
   p.n_max = desc->n_max;
   p.V = desc->vocab;
   p.chunks = L.gchunks;
-  const long long grid = (long long)desc->batch * desc->n_max * L.gchunks;
-  if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  const long long units = (long long)desc->batch * desc->n_max * L.gchunks;
+  if (units + desc->batch > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  p.G = (int)units;
+  const unsigned grid = (unsigned)(prepared ? units + desc->batch : units);
   if ((desc->vocab & 3) == 0)
-    hipLaunchKernelGGL(greedy_argmax_kernel<true>, dim3((unsigned)grid), dim3(kGreedyThreads), 0, stream, p);
+    hipLaunchKernelGGL(greedy_argmax_kernel<true>, dim3(grid), dim3(kGreedyThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(greedy_argmax_kernel<false>, dim3((unsigned)grid), dim3(kGreedyThreads), 0, stream, p);
+    hipLaunchKernelGGL(greedy_argmax_kernel<false>, dim3(grid), dim3(kGreedyThreads), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  hipLaunchKernelGGL(greedy_chase_kernel, dim3((unsigned)desc->batch), dim3(kMaxNodes), 0, stream, p);
+  if (!prepared) hipLaunchKernelGGL(greedy_chase_kernel, dim3((unsigned)desc->batch), dim3(kMaxNodes), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
@@ -1504,7 +1580,7 @@ static int tree_verify_greedy_impl(const tv_verify_desc* desc, const float* targ
   VerifyLayout L = layout(desc);
   if (!workspace || workspace_bytes < L.greedy_bytes) return TV_ERR_WORKSPACE;
   return launch_greedy(desc, target_logits, tokens, parent, n_nodes, path, path_len, out_tokens, status,
-                       (char*)workspace, L, stream);
+                       (char*)workspace, L, true, stream);
 }
 
 extern "C" int tree_verify_greedy(const tv_verify_desc* desc, const float* target_logits,
@@ -1536,7 +1612,7 @@ static int tree_verify_greedy_noalloc_impl(const tv_verify_desc* desc, const flo
   rc = scratch_ptr(&ws);
   if (rc != TV_OK) return rc;
   return launch_greedy(desc, target_logits, tokens, parent, n_nodes, path, path_len, out_tokens, status,
-                       (char*)ws, L, stream);
+                       (char*)ws, L, false, stream);
 }
 
 extern "C" int tree_verify_greedy_noalloc(const tv_verify_desc* desc, const float* target_logits,
