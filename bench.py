@@ -136,7 +136,7 @@ def traffic_record(kernel: str, workload: str, src_hash: str):
 ENTRY_KERNELS = {
     "tree_attn": ("tree_attn_kernel", "attn_merge_kernel"),
     "tree_verify_stochastic": ("stoch_node_kernel",),
-    "tree_verify_greedy": ("greedy_argmax_kernel", "greedy_chase_kernel"),
+    "tree_verify_greedy": ("greedy_argmax_kernel",),
     "kv_compact": ("compact_kernel",),
     "tree_verify_stochastic_compact": ("stoch_node_kernel",),
 }
