@@ -902,23 +902,20 @@ struct NodeOut {
 // contribution to the node's result.
 template <bool kRes, bool kVec>
 __device__ __forceinline__ void node_body(const StochParams& p, NodeSmem<kRes>& sm, int k, int member, int b, int u,
-                                          int n, NodeOut& o) {
+                                          int n, int4 rows, NodeOut& o) {
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int my_c0 = min(member * p.per, p.chunks);
   const int nmine = min(my_c0 + p.per, p.chunks) - my_c0;   // at most kResident when kRes
-  const int32_t* par = p.parent + (size_t)b * p.n_max;
-  const int32_t* tok = p.tokens + (size_t)b * p.n_max;
   const float* zp_row = p.target + (size_t)k * p.V;
   const float* zq_row = p.draft + (size_t)k * p.V;
   const __amdgpu_buffer_rsrc_t zp_rs = row_rsrc(zp_row, p.V), zq_rs = row_rsrc(zq_row, p.V);
 
   // first batch of the slice: the target at once, the draft as soon as one
-  // ballot over the parent row (loaded ahead of the slice, so it does not queue
-  // behind it) shows that u has children
-  const int pv0 = (1 + l < n) ? par[1 + l] : -1;
-  const int pv1 = (65 + l < n) ? par[65 + l] : -1;
-  const int tk0 = (w == 0 && 1 + l < n) ? tok[1 + l] : 0;   // tokens, for the children's accept tests
-  const int tk1 = (w == 0 && 65 + l < n) ? tok[65 + l] : 0;
+  // ballot over the parent row (read with the request's size, ahead of the
+  // slice) shows that u has children.  rows: parent[1 + l], parent[65 + l] and
+  // (wave 0) the tokens of those nodes, -1 / 0 past n.
+  const int pv0 = rows.x, pv1 = rows.y;
+  const int tk0 = rows.z, tk1 = rows.w;   // tokens, for the children's accept tests
   const float us = p.u_sample[k];
   float ep[kResident][16], eq[kResident][16];
   if (p.prio_ticks > 0) {
@@ -1323,7 +1320,16 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
   const int b = min(k / p.n_max, p.B - 1), u = k % p.n_max;   // b clamped for chase workgroups
   const int n = p.n_nodes[b];
   const bool wsok = ws_ok(p);
-  asm volatile("" : : "v"(n), "v"((int)wsok));   // keeps the loads above the branch
+  // The parent and token rows are read whole (n_max entries, in bounds before n
+  // is known), beside the request size, and masked by n afterwards.
+  const int l = t & 63;
+  const int32_t* par = p.parent + (size_t)b * p.n_max;
+  const int32_t* tok = p.tokens + (size_t)b * p.n_max;
+  const int pr0 = 1 + l < p.n_max ? par[1 + l] : -1;
+  const int pr1 = 65 + l < p.n_max ? par[65 + l] : -1;
+  const int tr0 = (t < 64 && 1 + l < p.n_max) ? tok[1 + l] : 0;
+  const int tr1 = (t < 64 && 65 + l < p.n_max) ? tok[65 + l] : 0;
+  asm volatile("" : : "v"(n), "v"((int)wsok), "v"(pr0), "v"(pr1), "v"(tr0), "v"(tr1));   // keeps the loads above the branch
   if (chase) {
     // The chase reads its arguments through an opaque copy of the argument
     // pointer, so that the compiler does not hoist them above this branch and
@@ -1337,7 +1343,8 @@ __global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(kRes 
   if (n < 1 || n > p.n_max || u >= n) return;
   if (!wsok) return;   // the chase reports it; no slot is read or written
   NodeOut o{0, -1, 0, false};
-  node_body<kRes, kVec>(p, sm, k, member, b, u, n, o);
+  const int4 rows = make_int4(1 + l < n ? pr0 : -1, 65 + l < n ? pr1 : -1, 1 + l < n ? tr0 : 0, 65 + l < n ? tr1 : 0);
+  node_body<kRes, kVec>(p, sm, k, member, b, u, n, rows, o);
   __syncthreads();
   // The member's part of the node's result word.  The member whose OR
   // completes the word clears the node's exchange slots for the next call
