@@ -20,14 +20,14 @@
  *     status has unspecified outputs but is never read or written out of
  *     bounds.
  *   - `workspace` is caller-owned device scratch of at least the size the
- *     matching *_workspace_size() returns for the call's descriptor.  The
- *     stochastic verifier's workspace holds exchange slots that must start at
- *     zero: prepare it once with tree_verify_workspace_init (every call leaves
- *     the slots at zero again, so later calls need nothing).  A workspace that
- *     was not prepared, or was prepared with fewer bytes than the call needs,
- *     is detected on the device from its header and fails every request with
+ *     matching *_workspace_size() returns for the call's descriptor.  Both
+ *     verifiers' workspaces hold slots that must start at zero: prepare each
+ *     once with tree_verify_workspace_init (every call leaves the slots at
+ *     zero again, so later calls need nothing).  A workspace that was not
+ *     prepared, or was prepared with fewer bytes than the call needs, is
+ *     detected on the device from its header and fails every request with
  *     TV_REQ_BAD_WORKSPACE; nothing of it is read as exchange data.  The
- *     greedy verifier's and the attention's workspaces hold only per-call
+ *     attention's and the tree expansion's workspaces hold only per-call
  *     results and need no preparation.  Two calls that may run concurrently
  *     must use distinct workspaces.
  *   - Node ids: a tree of n nodes is a parent array with parent[0] = -1 (node 0
@@ -46,6 +46,11 @@
  *               `stream`, returning TV_ERR_HIP when the GPU reported an error.
  *               This synchronises, so it must not be set for calls made under
  *               stream capture.
+ *   TV_CHASE_SPIN_LIMIT=<n>  a test hook: the verifiers' path-chasing
+ *               workgroups give up waiting for their nodes after n polling
+ *               rounds (default about 2 s worth) and report TV_REQ_TIMEOUT,
+ *               invalidating the workspace; a negative n gives up without
+ *               waiting.  Every workgroup still ends normally.
  */
 #ifndef TREE_VERIFY_H
 #define TREE_VERIFY_H

@@ -1,0 +1,92 @@
+"""An expired chase wait, forced from the host (TV_CHASE_SPIN_LIMIT, read once
+per process, so the case runs in a child process): with a negative limit the
+verifiers' path-chasing workgroups give up without polling, every request gets
+TV_REQ_TIMEOUT, and the workspace is invalidated because node results may
+still land in it; the next call on the same workspace reports
+TV_REQ_BAD_WORKSPACE, and tree_verify_workspace_init makes it usable again.
+Every workgroup still ends normally (the node and argmax workgroups finish
+their own work).  The limit 0 polls once and must leave results either
+complete or flagged."""
+import os
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+CHILD = textwrap.dedent("""
+    import sys
+    sys.path.insert(0, {root!r})
+    sys.path.insert(0, {tests!r})
+    import ctypes
+    import torch
+    from devdata import DevWorkload
+    from tree_verification_amd import binding as tv
+    from tree_verification_amd.binding import VerifyDesc, load_library
+    from tree_verification_amd.workloads import make_workload
+
+    wl = make_workload("llama8b", seed=61, vocab=30011, n_nodes=20, batch=3)
+    d = DevWorkload(wl)
+    lib = load_library()
+    desc = VerifyDesc()
+    desc.batch, desc.n_max, desc.vocab, desc.temperature = wl.batch, wl.n_max, wl.vocab, 1.0
+    need = lib.tree_verify_workspace_size(ctypes.byref(desc))
+    for name in ("stochastic", "greedy"):
+        ws = tv.init_verify_workspace(torch.zeros(need, dtype=torch.uint8, device="cuda:0"))
+        for step in ("first", "again", "prepared"):
+            if step == "prepared":
+                tv.init_verify_workspace(ws)
+            if name == "stochastic":
+                p, l, t, s = tv.tree_verify_stochastic(d.target, d.draft, d.tokens, d.parent, d.n_nodes,
+                                                       d.u_accept, d.u_sample, ws=ws)
+            else:
+                p, l, t, s = tv.tree_verify_greedy(d.target, d.tokens, d.parent, d.n_nodes, ws=ws)
+            torch.cuda.synchronize()
+            print(name.upper(), step, s.tolist(), l.tolist(), flush=True)
+""")
+
+
+def run_child(limit):
+    env = dict(os.environ)
+    env["TV_CHASE_SPIN_LIMIT"] = str(limit)
+    code = CHILD.format(root=ROOT, tests=os.path.join(ROOT, "tests"))
+    print("child TV_CHASE_SPIN_LIMIT", limit, flush=True)
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = {}
+    for ln in r.stdout.splitlines():
+        name, step, rest = ln.split(" ", 2)
+        st, ln_ = rest.split("] [")
+        out[(name, step)] = (eval(st + "]"), eval("[" + ln_))
+    return out
+
+
+def test_expired_chase_invalidates_the_workspace():
+    from tree_verification_amd import binding as tv
+    out = run_child(-1)
+    for name in ("STOCHASTIC", "GREEDY"):
+        st, ln = out[(name, "first")]
+        assert st == [tv.REQ_TIMEOUT] * 3 and ln == [0] * 3, (name, st)
+        st, ln = out[(name, "again")]
+        assert st == [tv.REQ_BAD_WORKSPACE] * 3 and ln == [0] * 3, (name, st)
+        st, ln = out[(name, "prepared")]   # prepared again: the wait expires again, nothing else
+        assert st == [tv.REQ_TIMEOUT] * 3, (name, st)
+
+
+def test_one_polling_round_completes_or_flags():
+    from tree_verification_amd import binding as tv
+    out = run_child(0)
+    for name in ("STOCHASTIC", "GREEDY"):
+        st, ln = out[(name, "first")]
+        for s, L in zip(st, ln):
+            assert (s == 0 and L >= 1) or (s == tv.REQ_TIMEOUT and L == 0), (name, st, ln)
+        if all(s == 0 for s in st):   # nothing expired: the workspace stays usable
+            st2, _ = out[(name, "again")]
+            assert all(s in (0, tv.REQ_TIMEOUT) for s in st2), (name, st2)
+        else:
+            st2, _ = out[(name, "again")]
+            assert st2 == [tv.REQ_BAD_WORKSPACE] * 3, (name, st2)

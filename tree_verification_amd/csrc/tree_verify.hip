@@ -187,6 +187,7 @@ struct GreedyParams {
   unsigned long long need;            // bytes this call's layout uses (header included)
   int B, n_max, V, chunks;
   int G;   // argmax workgroups; when the grid holds more, the B after them chase the paths
+  long long chase_spin;   // polling rounds before a chase workgroup gives up (negative: at once)
 };
 
 // A chunk's slot when it holds a non-finite logit.  Every key of a finite
@@ -315,6 +316,10 @@ __device__ void greedy_chase(const GreedyParams& p, GreedyChaseSmem& sm, int b) 
       unsigned long long kc[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) kc[c] = 0ull;
+      if (kPoll && p.chase_spin < 0) {
+        done = false;
+        break;
+      }
       for (long long it = 0;; ++it) {
         bool all = true;
 #pragma unroll
@@ -324,7 +329,7 @@ __device__ void greedy_chase(const GreedyParams& p, GreedyChaseSmem& sm, int b) 
           all = all && (c0 + c >= p.chunks || kc[c] != 0ull);
         }
         if (!kPoll || all) break;
-        if (it > kChaseSpinLimit) {
+        if (it >= p.chase_spin) {
           done = false;
           break;
         }
@@ -468,6 +473,7 @@ struct StochParams {
   double invT_d;
   int G;            // node workgroups; the B workgroups after them chase the paths
   int chase_mode;   // kChaseOnly, or the chase then the KV compaction of cpt
+  long long chase_spin;   // polling rounds before a chase workgroup gives up (negative: at once)
   TvCompactArgs cpt;
 };
 
@@ -791,8 +797,9 @@ struct ChaseLoads {
 
 // Issues the loads of request b's rows at once (rows are n_max long; entries
 // past n are not used), then polls the result words of nodes 0 .. n-1 until
-// every member of each node has ORed its part.  A word still incomplete when
-// the wait expires is flagged TV_REQ_TIMEOUT and left as it is.
+// every member of each node has ORed its part (at most p.chase_spin rounds; a
+// negative limit polls none).  A word still incomplete when the wait expires
+// is flagged TV_REQ_TIMEOUT and left as it is.
 __device__ __forceinline__ ChaseLoads chase_gather(const StochParams& p, int b) {
   const int t = threadIdx.x;
   const size_t kv = (size_t)b * p.n_max + t;
@@ -806,12 +813,12 @@ __device__ __forceinline__ ChaseLoads chase_gather(const StochParams& p, int b) 
   const unsigned long long full = ((1ull << p.S) - 1ull) << kNwDoneShift;
   unsigned long long wv = 0;
   bool done = !mine;
-  for (long long it = 0;; ++it) {
+  for (long long it = 0; p.chase_spin >= 0; ++it) {
     if (!done) {
       wv = __hip_atomic_load(p.nword + kv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       done = (wv & full) == full;
     }
-    if (__all(done) || it > kChaseSpinLimit) break;
+    if (__all(done) || it >= p.chase_spin) break;
     __builtin_amdgcn_s_sleep(2);
   }
   if (mine) {
@@ -1529,6 +1536,7 @@ int launch_greedy(const tv_verify_desc* desc, const float* target_logits, const 
   const long long units = (long long)desc->batch * desc->n_max * L.gchunks;
   if (units + desc->batch > 0x7fffffff) return TV_ERR_UNSUPPORTED;
   p.G = (int)units;
+  p.chase_spin = tv_chase_spin_limit(kChaseSpinLimit);
   const unsigned grid = (unsigned)(prepared ? units + desc->batch : units);
   if ((desc->vocab & 3) == 0)
     hipLaunchKernelGGL(greedy_argmax_kernel<true>, dim3(grid), dim3(kGreedyThreads), 0, stream, p);
@@ -1690,6 +1698,7 @@ int launch_stoch_nodes(const tv_verify_desc* desc, const float* target_logits, c
   const long long grid = nodes * tp.S;
   if (grid + desc->batch > 0x7fffffff) return TV_ERR_UNSUPPORTED;
   p.G = (int)grid;
+  p.chase_spin = tv_chase_spin_limit(kChaseSpinLimit);
   p.chase_mode = !cpt ? kChaseOnly : (cpt_bf16 ? kChaseCompactBf16 : kChaseCompactF32);
   if (cpt) p.cpt = *cpt;
   // When the whole grid is resident at once (four workgroups per CU), load order

@@ -34,13 +34,20 @@ typedef int (*RangePopFn)();
 RangePushFn g_push = nullptr;
 RangePopFn g_pop = nullptr;
 bool g_trace = false, g_debug = false;
+bool g_spin_set = false;
+long long g_spin = 0;
 std::once_flag g_env_once;
 
 void read_env() {
   std::call_once(g_env_once, []() {
     const char* tr = getenv("TV_TRACE");
     const char* db = getenv("TV_DEBUG");
+    const char* sp = getenv("TV_CHASE_SPIN_LIMIT");
     g_debug = db && *db && *db != '0';
+    if (sp && *sp) {
+      g_spin_set = true;
+      g_spin = atoll(sp);
+    }
     if (tr && *tr && *tr != '0') {
       for (const char* lib : {"librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so", "libroctx64.so"}) {
         void* h = dlopen(lib, RTLD_NOW | RTLD_LOCAL);
@@ -79,6 +86,11 @@ TvTraceScope::~TvTraceScope() {
 bool tv_debug_enabled() {
   read_env();
   return g_debug;
+}
+
+long long tv_chase_spin_limit(long long dflt) {
+  read_env();
+  return g_spin_set ? g_spin : dflt;
 }
 
 int tv_debug_trees(const char* entry, const int32_t* parent, const int32_t* n_nodes, int batch, int n_max,

@@ -34,6 +34,10 @@ struct TvTraceScope {
 #define TV_TRACE_SCOPE(name) TvTraceScope tv_trace_scope_(name)
 
 bool tv_debug_enabled();
+// Polling rounds after which a verifier's path-chasing workgroup gives up
+// (TV_CHASE_SPIN_LIMIT, read once per process; `dflt` when unset; negative:
+// give up without waiting).
+long long tv_chase_spin_limit(long long dflt);
 // Malformed trees (n_nodes outside [1, n_max], parent[0] != -1, parent[i]
 // outside [0, i)) reported on stderr; returns how many requests were reported.
 int tv_debug_trees(const char* entry, const int32_t* parent, const int32_t* n_nodes, int batch, int n_max,
