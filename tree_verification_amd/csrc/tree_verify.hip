@@ -7,13 +7,21 @@
 // device-wide fence (on this part an agent-scope fence writes back and
 // invalidates the XCD's whole L2).
 //
+// Both verifiers are one launch each (with a prepared workspace): the grid
+// holds the per-node workgroups and then one workgroup per request that chases
+// the accepted path.  Workgroups are dispatched in id order, so a chase
+// workgroup takes a slot only after every per-node workgroup has one; it polls
+// its request's published words (bounded) and clears them for the next call.
+//
 // Greedy ([guide] "Greedy Verification Algorithm"):
 //   greedy_argmax_kernel  one workgroup per (node, 8192-logit chunk) reduces its
 //                         chunk to one 64-bit key that orders by value, then by
-//                         lower index, and a non-finite flag;
-//   greedy_chase_kernel   one workgroup per request takes each node's largest
-//                         key, matches children against the argmaxes and walks
-//                         the root path.
+//                         lower index (or a reserved value when the chunk holds
+//                         a non-finite logit) and publishes it; the chase
+//                         workgroups take each node's largest key, match
+//                         children against the argmaxes and walk the root path.
+//   greedy_chase_kernel   the same chase as a kernel of its own, for the static
+//                         scratch of tree_verify_greedy_noalloc.
 //
 // Stochastic ([guide] "Stochastic Verification Algorithm"; [chapter] the
 // min(1, p/q) acceptance rule and the residual max(p - q, 0) / Z):
@@ -40,14 +48,10 @@
 //                         emits when no child is accepted: an inverse CDF over
 //                         member masses, chunk masses, then one chunk.  Every
 //                         member then ORs its part of the node's result into one
-//                         64-bit word and counts itself in on the request; the
-//                         workgroup that completes the count runs the chase:
-//                         status, the root path and its final token, every
-//                         exchange slot of the request cleared for the next call,
-//                         and for verify-and-compact (up to four requests) the
-//                         accepted path's KV compaction ([guide] "Depth-First
-//                         Flattening and KV Cache Reuse").  No second launch
-//                         waits on the nodes.
+//                         64-bit word.  The chase workgroups read the words:
+//                         status, the root path and its final token, and for
+//                         verify-and-compact the accepted path's KV compaction
+//                         ([guide] "Depth-First Flattening and KV Cache Reuse").
 // Vocabulary exponentials are float32 (exp_t), as is each entry's residual
 // bracket (residual_rel); sums, chunk factors and the accept test are float64.
 
@@ -1297,7 +1301,7 @@ __device__ __forceinline__ void chase_tail(const StochParams& p, ChaseTailSmem& 
 // member reads its slice of the target row (and of the draft row when the node
 // has children) once; the team exchanges each slice's (max, sum), tests the
 // children, and makes the node's draw for the case that no child is accepted
-// (the chase kernel uses it when the accepted path ends at this node).  Members
+// (the chase uses it when the accepted path ends at this node).  Members
 // wait only on their own team: with workgroups dispatched in id order every
 // team becomes fully resident once the teams before it have left, and a wait
 // that still expires flags TV_REQ_TIMEOUT instead of hanging.  kRes: every

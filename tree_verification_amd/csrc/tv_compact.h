@@ -1,6 +1,7 @@
 // Accepted-path KV compaction of one (request, KV head), shared by the
-// stand-alone compaction kernel and the verifier's fused verify-and-compact
-// kernel, so that both give the same caches, src_pos, new_len and status.
+// stand-alone compaction kernel and the verify-and-compact chase workgroups of
+// the stochastic verifier, so that both give the same caches, src_pos, new_len
+// and status.
 //
 // [guide] "Depth-First Flattening and KV Cache Reuse": after verification only
 // the winning root path stays in the cache.  Position P + j receives the K/V
@@ -9,9 +10,9 @@
 // earlier destination only when it belongs to a later step: a batch of steps
 // is hazard-free when every source of the batch is read before any of its
 // destinations is written, and the sources of later batches lie past every
-// destination of earlier ones.  Each (KV head, element d) pair of the key and
-// value rows (both token-major) is moved by one thread, independently of the
-// others.
+// destination of earlier ones.  Each unit of the key and value rows (both
+// token-major) -- one element, or 8 bytes of consecutive elements of one KV
+// head -- is moved by one thread, independently of the others.
 #pragma once
 
 #include "tv_common.h"
