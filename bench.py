@@ -376,6 +376,16 @@ def main():
     us_compact = time_calls(compact, args.kernel_reps)
     us_vc = time_calls(verify_compact, args.kernel_reps)
 
+    # The practical streaming ceiling the HBM-bound kernels are compared with: a
+    # device-to-device copy of 256 MiB (256 MiB read and 256 MiB written per call).
+    copy_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+    copy_dst.copy_(copy_src)
+    torch.cuda.synchronize()
+    us_copy = gated_us_per_call(lambda i: copy_dst.copy_(copy_src), 10, cyc_per_s)
+    copy_bytes_moved = 2 * copy_src.numel() * 4
+    del copy_src, copy_dst
+
     # ---- algorithmic bytes --------------------------------------------------
     P = wl.prefix_len.astype(np.int64)
     n = wl.n_nodes.astype(np.int64)
@@ -433,8 +443,10 @@ def main():
         "tree_verify_stochastic_compact": {"us": us_vc, "bytes": verify_bytes + compact_bytes,
                                            "GBps": gbs(verify_bytes + compact_bytes, us_vc)},
     }
+    copy_gbs = gbs(copy_bytes_moved, us_copy)
     for k in kernels.values():
         k["frac_hbm"] = k["GBps"] / HBM_PEAK_GBS
+        k["frac_copy"] = k["GBps"] / copy_gbs
     # the dominant kernel among the per-row entry points (the fused call is both rows)
     dominant = max((k for k in kernels if k != "tree_verify_stochastic_compact"), key=lambda k: kernels[k]["us"])
 
@@ -496,7 +508,11 @@ def main():
                     for k, d in kernels.items()},
         "greedy": {"us_per_call": round(us_greedy, 3), "bytes": greedy_bytes,
                    "GBps": round(gbs(greedy_bytes, us_greedy), 1),
+                   "frac_copy": round(gbs(greedy_bytes, us_greedy) / copy_gbs, 4),
                    "nodes_per_s": n_total / (us_greedy * 1e-6)},
+        "copy_ceiling": {"GBps": round(copy_gbs, 1), "us_per_call": round(us_copy, 3),
+                         "bytes_per_call": copy_bytes_moved,
+                         "what": "device-to-device copy of 256 MiB (read and write), timed like the kernels"},
         "accepted_mean": float(plen0.mean() - 1),
         "rejection_passes_on_path": passes,
         "verify_bytes_first_reads": verify_first_bytes,
@@ -508,6 +524,8 @@ def main():
         if not args.no_cpu_baseline:
             construction_oracle(constr)
         line["construction"] = {k: v for k, v in constr.items() if not k.startswith("_")}
+        if "expand" in line["construction"]:
+            line["construction"]["expand"]["frac_copy"] = round(line["construction"]["expand"]["GBps"] / copy_gbs, 4)
         line["budget"] = constr.pop("_budget")
     print(json.dumps(line), flush=True)
 
