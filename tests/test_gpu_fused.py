@@ -56,7 +56,7 @@ def _same(sep, fused, wl):
             assert np.array_equal(a, b), name
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama8b", "ragged", "chain"])
+@pytest.mark.parametrize("name", ["tiny", "llama8b", "ragged", "chain", "llama70b_share"])
 def test_fused_equals_separate_calls(name):
     wl = _workload(name)
     print(f"case fused {name}: B={wl.batch} n_max={wl.n_max} V={wl.vocab}", flush=True)
