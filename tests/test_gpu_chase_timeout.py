@@ -3,7 +3,8 @@ per process, so the case runs in a child process): with a negative limit the
 verifiers' path-chasing workgroups give up without polling, every request gets
 TV_REQ_TIMEOUT, and the workspace is invalidated because node results may
 still land in it; the next call on the same workspace reports
-TV_REQ_BAD_WORKSPACE, and tree_verify_workspace_init makes it usable again.
+TV_REQ_BAD_WORKSPACE, and tree_verify_workspace_init makes it usable again;
+verify-and-compact then moves no K/V and keeps every request's length.
 Every workgroup still ends normally (the node and argmax workgroups finish
 their own work).  The limit 0 polls once and must leave results either
 complete or flagged."""
@@ -35,18 +36,27 @@ CHILD = textwrap.dedent("""
     desc = VerifyDesc()
     desc.batch, desc.n_max, desc.vocab, desc.temperature = wl.batch, wl.n_max, wl.vocab, 1.0
     need = lib.tree_verify_workspace_size(ctypes.byref(desc))
-    for name in ("stochastic", "greedy"):
+    for name in ("stochastic", "greedy", "compact"):
         ws = tv.init_verify_workspace(torch.zeros(need, dtype=torch.uint8, device="cuda:0"))
+        k0, v0 = d.k.clone(), d.v.clone()
         for step in ("first", "again", "prepared"):
             if step == "prepared":
                 tv.init_verify_workspace(ws)
             if name == "stochastic":
                 p, l, t, s = tv.tree_verify_stochastic(d.target, d.draft, d.tokens, d.parent, d.n_nodes,
                                                        d.u_accept, d.u_sample, ws=ws)
-            else:
+            elif name == "greedy":
                 p, l, t, s = tv.tree_verify_greedy(d.target, d.tokens, d.parent, d.n_nodes, ws=ws)
+            else:
+                p, l, t, s, src, nl, kst = tv.tree_verify_stochastic_compact(
+                    d.target, d.draft, d.tokens, d.parent, d.n_nodes, d.u_accept, d.u_sample,
+                    d.k, d.v, d.table, d.prefix_len, ws=ws)
             torch.cuda.synchronize()
             print(name.upper(), step, s.tolist(), l.tolist(), flush=True)
+            if name == "compact":
+                # a request without a path moves nothing and keeps its length
+                same = bool(torch.equal(d.k, k0) and torch.equal(d.v, v0))
+                print("COMPACTKV", step, [int(same)], (nl - d.prefix_len).tolist(), flush=True)
 """)
 
 
@@ -68,7 +78,10 @@ def run_child(limit):
 def test_expired_chase_invalidates_the_workspace():
     from tree_verification_amd import binding as tv
     out = run_child(-1)
-    for name in ("STOCHASTIC", "GREEDY"):
+    for step in ("first", "again", "prepared"):   # verify-and-compact: nothing moved, lengths kept
+        same, dlen = out[("COMPACTKV", step)]
+        assert same == [1] and dlen == [0] * 3, (step, same, dlen)
+    for name in ("STOCHASTIC", "GREEDY", "COMPACT"):
         st, ln = out[(name, "first")]
         assert st == [tv.REQ_TIMEOUT] * 3 and ln == [0] * 3, (name, st)
         st, ln = out[(name, "again")]
@@ -80,7 +93,7 @@ def test_expired_chase_invalidates_the_workspace():
 def test_one_polling_round_completes_or_flags():
     from tree_verification_amd import binding as tv
     out = run_child(0)
-    for name in ("STOCHASTIC", "GREEDY"):
+    for name in ("STOCHASTIC", "GREEDY", "COMPACT"):
         st, ln = out[(name, "first")]
         for s, L in zip(st, ln):
             assert (s == 0 and L >= 1) or (s == tv.REQ_TIMEOUT and L == 0), (name, st, ln)
