@@ -258,19 +258,35 @@ __global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(ExpandParams p
   row_load16<kVec>(rs, e0, x);
   row_load16<kVec>(rs, e1, x + 16);
   int bad = 0;
+  int jb;
+  unsigned long long key;
+  if (hi - lo == kTopkChunk) {
+    // A full chunk: no per-entry bounds tests.  The thread's best is its largest
+    // value (three-input maxima) at the first entry holding it, the same key
+    // as thread_best gives when every entry is finite (a row with a non-finite
+    // entry is flagged, and its keys are not used).
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const int e = j < 16 ? e0 + j : e1 + j - 16;
-    if (e < hi) bad |= !isfinite(x[j]);
-    else x[j] = -__builtin_huge_valf();   // outside the chunk: never selected
+    for (int j = 0; j < 32; ++j) bad |= !isfinite(x[j]);
+    const float m = fmaxf(tv_max16(x), tv_max16(x + 16));
+    int jm = 31;
+#pragma unroll
+    for (int j = 30; j >= 0; --j) jm = x[j] == m ? j : jm;
+    jb = jm;
+    key = topk_key(m, jm < 16 ? e0 + jm : e1 + jm - 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int e = j < 16 ? e0 + j : e1 + j - 16;
+      if (e < hi) bad |= !isfinite(x[j]);
+      else x[j] = -__builtin_huge_valf();   // outside the chunk: never selected
+    }
+    key = thread_best(x, e0, e1, &jb);
   }
   // written for every chunk of every row the append kernel reads, so the
   // workspace needs no clearing (a non-finite row yields unspecified keys; the
   // append kernel then writes nothing)
   if (__syncthreads_or(bad) && t == 0) p.flags[(size_t)row * p.chunks + c] = 1;
   else if (t == 0) p.flags[(size_t)row * p.chunks + c] = 0;
-  int jb;
-  unsigned long long key = thread_best(x, e0, e1, &jb);
   unsigned long long* out = p.keys + ((size_t)row * p.chunks + c) * p.k;
   for (int r = 0; r < p.k; ++r) {
     const unsigned long long wmax = tv_wave_max_u64(key);

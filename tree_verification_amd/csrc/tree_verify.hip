@@ -118,14 +118,6 @@ __device__ __forceinline__ void load16(__amdgpu_buffer_rsrc_t rs, int e0, float*
   }
 }
 
-// Largest of 16 floats (three-input maxima).
-__device__ __forceinline__ float max16(const float* x) {
-  const float a = fmaxf(fmaxf(x[0], x[1]), x[2]), b = fmaxf(fmaxf(x[3], x[4]), x[5]);
-  const float c = fmaxf(fmaxf(x[6], x[7]), x[8]), d = fmaxf(fmaxf(x[9], x[10]), x[11]);
-  const float e = fmaxf(fmaxf(x[12], x[13]), x[14]);
-  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), x[15]));
-}
-
 // Children of u among nodes [1, n), ascending, written by one wave into kids[]
 // with their tokens in ktok[]; returns the count to every lane (n <= 128: two
 // ballots).  pv0 / pv1 and tk0 / tk1: parent and token of nodes 1 + l and
@@ -244,7 +236,7 @@ __device__ __forceinline__ void greedy_reduce(const GreedyParams& p, int unit, c
       // exact and -0 / +0 compare equal, so this is the same key as below.
 #pragma unroll
       for (int j = 0; j < 32; ++j) bad |= !isfinite(x.x[j]);
-      const float m = fmaxf(max16(x.x), max16(x.x + 16));
+      const float m = fmaxf(tv_max16(x.x), tv_max16(x.x + 16));
       int jm = 31;
 #pragma unroll
       for (int j = 30; j >= 0; --j) jm = x.x[j] == m ? j : jm;
@@ -612,7 +604,7 @@ __device__ void batch_stats(NodeSmem<kRes>& sm, float (&xp)[kResident][16], floa
         const int nv = V - ((my_c0 + j0 + r) * kChunk + 16 * t);   // entries of this thread inside the row
         float m;
         if (nv >= 16) {
-          m = max16(x);
+          m = tv_max16(x);
         } else {
           m = kNegInf;
 #pragma unroll

@@ -199,6 +199,15 @@ __device__ __forceinline__ unsigned long long tv_wave_max_u64(unsigned long long
 
 // LDS-only workgroup barrier: unlike __syncthreads it does not first wait for
 // the wave's outstanding global loads, so loads issued earlier stay in flight.
+// Largest of 16 floats by three-input maxima (NaN entries are skipped, as by
+// fmaxf; -0 and +0 compare equal).
+__device__ __forceinline__ float tv_max16(const float* x) {
+  const float a = fmaxf(fmaxf(x[0], x[1]), x[2]), b = fmaxf(fmaxf(x[3], x[4]), x[5]);
+  const float c = fmaxf(fmaxf(x[6], x[7]), x[8]), d = fmaxf(fmaxf(x[9], x[10]), x[11]);
+  const float e = fmaxf(fmaxf(x[12], x[13]), x[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), x[15]));
+}
+
 __device__ __forceinline__ void tv_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Acquire/release helpers for inter-workgroup hand-offs through global memory.
