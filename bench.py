@@ -134,7 +134,7 @@ def traffic_record(kernel: str, workload: str, src_hash: str):
 
 # kernels launched by each entry point (rocprofv3 kernel names contain these)
 ENTRY_KERNELS = {
-    "tree_attn": ("tree_attn_kernel", "attn_merge_kernel"),
+    "tree_attn": ("tree_attn_kernel",),
     "tree_verify_stochastic": ("stoch_node_kernel",),
     "tree_verify_greedy": ("greedy_argmax_kernel",),
     "kv_compact": ("compact_kernel",),
@@ -882,9 +882,9 @@ def mfma_summary(run_dir: str, workload: str):
     for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(path)):
             name = r["Kernel_Name"]
-            if "tree_attn_kernel" not in name and "attn_merge_kernel" not in name:
+            if "tree_attn_kernel" not in name:
                 continue
-            key = "tree_attn_kernel" if "tree_attn_kernel" in name else "attn_merge_kernel"
+            key = "tree_attn_kernel"
             d = per.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), {})
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
             d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])

@@ -19,17 +19,18 @@
  *     `status[b]` as a bitwise OR of TV_REQ_* flags; a request with a non-zero
  *     status has unspecified outputs but is never read or written out of
  *     bounds.
- *   - `workspace` is caller-owned device scratch of at least the size the
- *     matching *_workspace_size() returns for the call's descriptor.  Both
- *     verifiers' workspaces hold slots that must start at zero: prepare each
- *     once with tree_verify_workspace_init (every call leaves the slots at
- *     zero again, so later calls need nothing).  A workspace that was not
- *     prepared, or was prepared with fewer bytes than the call needs, is
- *     detected on the device from its header and fails every request with
+ *   - `workspace` is caller-owned device scratch (256-byte aligned) of at
+ *     least the size the matching *_workspace_size() returns for the call's
+ *     descriptor.  Both verifiers' workspaces and the attention's hold slots
+ *     or counters that must start at zero: prepare each once with
+ *     tree_verify_workspace_init (every call leaves them at zero again, so
+ *     later calls need nothing).  A workspace that was not prepared, or was
+ *     prepared with fewer bytes than the call needs, is detected on the
+ *     device from its header and fails the requests that would use it with
  *     TV_REQ_BAD_WORKSPACE; nothing of it is read as exchange data.  The
- *     attention's and the tree expansion's workspaces hold only per-call
- *     results and need no preparation.  Two calls that may run concurrently
- *     must use distinct workspaces.
+ *     tree expansion's workspace holds only per-call results and needs no
+ *     preparation.  Two calls that may run concurrently must use distinct
+ *     workspaces.
  *   - Node ids: a tree of n nodes is a parent array with parent[0] = -1 (node 0
  *     is the root: the last token already emitted) and 0 <= parent[i] < i.
  *     Rows are padded to n_max; padding rows are neither read nor written.
@@ -85,7 +86,7 @@ enum {
   TV_REQ_BAD_LEN = 256,     /* a candidate length, frontier count or frontier node id out of range */
   TV_REQ_POOL_EXHAUSTED = 512, /* the block pool cannot serve an allocation, or a release would overfill it */
   TV_REQ_BAD_PROB = 1024,   /* an acceptance probability that is NaN or outside [0, 1] (tree budget) */
-  TV_REQ_BAD_WORKSPACE = 2048 /* the stochastic verifier's workspace was not initialised for this call */
+  TV_REQ_BAD_WORKSPACE = 2048 /* the call's workspace was not prepared by tree_verify_workspace_init (or is too small) */
 };
 
 /* ---- element types ------------------------------------------------------ */
@@ -113,7 +114,12 @@ typedef struct tv_attn_desc {
  * tree nodes positions [P, P + n) in node order ([guide] "Depth-First
  * Flattening and KV Cache Reuse": tree tokens append their K/V to the cache). */
 
-/* Bytes of workspace tree_attn_forward needs for `desc` on the current device. */
+/* Bytes of workspace tree_attn_forward needs for `desc` on the current device
+ * (0 when no tile of the call is split over keys; then `workspace` may be NULL).
+ * The workspace holds the split-K partials and one counter per tile: the last
+ * split of a tile to finish merges the tile ([guide] "The Topology-Aware 2D
+ * Causal Mask", FlashDecoding-style split-K).  Prepare it once with
+ * tree_verify_workspace_init. */
 size_t tree_attn_workspace_size(const tv_attn_desc* desc);
 
 /* Tree attention ([guide] "Generalizing Attention to Tree Topologies" and "The
@@ -124,8 +130,12 @@ size_t tree_attn_workspace_size(const tv_attn_desc* desc);
  *   q      [B][n_max][Hq][D]     (dtype)
  *   out    [B][n_max][Hq][D]     (dtype) written for u < n_b only
  *   block_table [B][max_blocks_per_seq], prefix_len [B], n_nodes [B], parent [B][n_max]
- *   status [B] or NULL: TV_REQ_BAD_NNODES / _BAD_PARENT / _BAD_KV
- * The caches are only read. */
+ *   status [B] or NULL: TV_REQ_BAD_NNODES / _BAD_PARENT / _BAD_KV, and
+ *     TV_REQ_BAD_WORKSPACE for a request whose tiles are split over keys when
+ *     the workspace was not prepared (its output rows are then not written)
+ * The caches are only read.  TV_ERR_WORKSPACE: workspace missing or too small;
+ * TV_ERR_INVALID_ARG: q, caches or out not 16-byte aligned, or a workspace
+ * not 256-byte aligned. */
 int tree_attn_forward(const tv_attn_desc* desc, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
                       const int32_t* n_nodes, const int32_t* parent, void* out, int32_t* status,
@@ -158,9 +168,9 @@ typedef struct tv_verify_desc {
  * their workspaces out differently: give each its own buffer. */
 size_t tree_verify_workspace_size(const tv_verify_desc* desc);
 
-/* Prepares a verifier's workspace (256-byte aligned, at least
- * tree_verify_workspace_size bytes for the descriptors it will serve): zeroes
- * it and writes the header the verifier checks.  Both verifiers need it.  Enqueued on `stream`.
+/* Prepares a workspace (256-byte aligned, at least the *_workspace_size bytes
+ * of the descriptors it will serve): zeroes it and writes the header the
+ * kernels check.  Both verifiers and tree_attn_forward need it.  Enqueued on `stream`.
  * TV_ERR_WORKSPACE for a null or too small buffer, TV_ERR_INVALID_ARG when
  * it is not 256-byte aligned. */
 int tree_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);

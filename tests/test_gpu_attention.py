@@ -7,6 +7,8 @@ and 1e-5 for fp32 inputs, and element-wise |o - o_ref| <= tol * max |o_ref row|
 dominate the softmax, where one wrong ancestor bit fails the check
 (tests/test_attn_check.py pins that on the CPU).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -259,3 +261,36 @@ def test_attention_uniform_plan_bad_sizes():
     wl.n_nodes[0] = wl.n_max + 1
     _, st, _, _ = run_gpu(wl)
     assert st[0] == tv.REQ_BAD_NNODES
+
+
+def test_attention_unprepared_workspace_is_reported():
+    """A call whose tiles are split over keys merges them through counters in
+    the workspace.  A workspace that was never prepared is detected from its
+    header: the request gets TV_REQ_BAD_WORKSPACE and no counter is touched.
+    Once prepared, repeated calls give identical outputs (every call leaves the
+    counters at zero), including a smaller call in between."""
+    wl = make_workload("llama8b", seed=31, with_logits=False, prefix=900)
+    d = DevWorkload(wl, logits=False)
+    wl2 = make_workload("llama8b", seed=32, with_logits=False, prefix=400, n_nodes=20)
+    d2 = DevWorkload(wl2, logits=False)
+    lib = tv.load_library()
+    needs = [lib.tree_attn_workspace_size(ctypes.byref(tv.attn_desc(x.q, x.k, x.table))) for x in (d, d2)]
+    assert min(needs) > 0
+    ws = torch.zeros(max(needs), dtype=torch.uint8, device="cuda:0")
+    _, st = tv.tree_attn_forward(d.q, d.k, d.v, d.table, d.prefix_len, d.n_nodes, d.parent, ws=ws)
+    torch.cuda.synchronize()
+    assert list(st.cpu().numpy()) == [tv.REQ_BAD_WORKSPACE]
+    tv.init_verify_workspace(ws)
+    a, st = tv.tree_attn_forward(d.q, d.k, d.v, d.table, d.prefix_len, d.n_nodes, d.parent, ws=ws)
+    torch.cuda.synchronize()
+    assert not st.cpu().numpy().any()
+    check_all_rows(wl, out_to_np(a), st.cpu().numpy())
+    # a shorter request through the same workspace, then the first one again
+    o2, st2 = tv.tree_attn_forward(d2.q, d2.k, d2.v, d2.table, d2.prefix_len, d2.n_nodes, d2.parent, ws=ws)
+    torch.cuda.synchronize()
+    check_all_rows(wl2, out_to_np(o2), st2.cpu().numpy())
+    for _ in range(3):
+        b_, st = tv.tree_attn_forward(d.q, d.k, d.v, d.table, d.prefix_len, d.n_nodes, d.parent, ws=ws)
+        torch.cuda.synchronize()
+        assert not st.cpu().numpy().any()
+        assert torch.equal(a, b_)

@@ -7,7 +7,8 @@ TV_REQ_BAD_WORKSPACE, and tree_verify_workspace_init makes it usable again;
 verify-and-compact then moves no K/V and keeps every request's length.
 Every workgroup still ends normally (the node and argmax workgroups finish
 their own work).  The limit 0 polls once and must leave results either
-complete or flagged."""
+complete or flagged.  Tree attention on a grid resident at once (its tiles'
+key splits wait for each other before merging) follows the same contract."""
 import os
 import subprocess
 import sys
@@ -57,6 +58,19 @@ CHILD = textwrap.dedent("""
                 # a request without a path moves nothing and keeps its length
                 same = bool(torch.equal(d.k, k0) and torch.equal(d.v, v0))
                 print("COMPACTKV", step, [int(same)], (nl - d.prefix_len).tolist(), flush=True)
+
+    # tree attention on a grid that is resident at once: the splits of a tile
+    # wait for each other before merging
+    wa = make_workload("llama8b", seed=62, with_logits=False, n_nodes=20, prefix=1500)
+    da = DevWorkload(wa, logits=False)
+    aneed = lib.tree_attn_workspace_size(ctypes.byref(tv.attn_desc(da.q, da.k, da.table)))
+    aws = tv.init_verify_workspace(torch.zeros(aneed, dtype=torch.uint8, device="cuda:0"))
+    for step in ("first", "again", "prepared"):
+        if step == "prepared":
+            tv.init_verify_workspace(aws)
+        o, s = tv.tree_attn_forward(da.q, da.k, da.v, da.table, da.prefix_len, da.n_nodes, da.parent, ws=aws)
+        torch.cuda.synchronize()
+        print("ATTN", step, s.tolist(), [1], flush=True)
 """)
 
 
@@ -88,6 +102,10 @@ def test_expired_chase_invalidates_the_workspace():
         assert st == [tv.REQ_BAD_WORKSPACE] * 3 and ln == [0] * 3, (name, st)
         st, ln = out[(name, "prepared")]   # prepared again: the wait expires again, nothing else
         assert st == [tv.REQ_TIMEOUT] * 3, (name, st)
+    # attention's split merge: the same contract for its workspace
+    assert out[("ATTN", "first")][0] == [tv.REQ_TIMEOUT]
+    assert out[("ATTN", "again")][0] == [tv.REQ_BAD_WORKSPACE]
+    assert out[("ATTN", "prepared")][0] == [tv.REQ_TIMEOUT]
 
 
 def test_one_polling_round_completes_or_flags():
@@ -103,3 +121,7 @@ def test_one_polling_round_completes_or_flags():
         else:
             st2, _ = out[(name, "again")]
             assert st2 == [tv.REQ_BAD_WORKSPACE] * 3, (name, st2)
+    st, _ = out[("ATTN", "first")]
+    assert st in ([0], [tv.REQ_TIMEOUT]), st
+    st2, _ = out[("ATTN", "again")]
+    assert st2 in (([0], [tv.REQ_TIMEOUT]) if st == [0] else ([tv.REQ_BAD_WORKSPACE],)), (st, st2)

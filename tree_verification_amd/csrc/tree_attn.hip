@@ -16,10 +16,11 @@
 // otherwise every tile has the same number of splits and each request's own
 // length sets its keys per split.  A block table sized for a longer context
 // than the request uses costs nothing.  A workgroup that owns all keys of its
-// tile writes the output directly; otherwise it writes its (m, l, O) partial
-// to the workspace and attn_merge_kernel combines the splits of each row by
-// log-sum-exp (a kernel boundary orders the hand-off, so no workgroup waits on
-// a fence).
+// tile writes the output directly.  Otherwise it writes its (m, l, O) partial
+// to the workspace, publishes it (release fence, then one increment of the
+// tile's counter), and the split that arrives last merges the tile's partials
+// by log-sum-exp and writes the output (no workgroup ever waits for another;
+// the merging one resets the counter, so every call leaves the counters zero).
 //
 // MFMA path (bf16): four MFMA waves own disjoint 16*NTW-row slices of the
 // tile (rows past the request are padding) and a fifth, producer wave moves
@@ -84,6 +85,11 @@ struct AttnParams {
   int32_t* status;
   void* part_o;     // [slots][rows_per_tile][D] O / l of each split times a power of two (fp16 or fp32)
   float4* part_ml;  // [slots][rows_per_tile] (m, l, the power of two's inverse, 0)
+  int* counters;    // [slots]: splits of a tile published so far, at the tile's first slot
+  const unsigned long long* header;   // [2] prepared-workspace header (magic, bytes cleared)
+  unsigned long long need;            // workspace bytes this call's layout uses
+  int coresident;   // 1: every workgroup of the grid is resident at once (the splits of a tile merge together)
+  long long spin;   // polling rounds of the bounded wait for a tile's splits (negative: give up at once)
   int B, n_max, Hq, Hkv, G, D, bs, lbs, max_blocks, num_blocks;
   float scale_log2;
   int rows_per_tile, row_tiles;   // row tiles of one (request, KV head) at n_max nodes
@@ -96,7 +102,7 @@ struct AttnParams {
 
 struct AttnPlan {
   int rows_per_tile, row_tiles, ntw, kg, balanced, splits, nwg, max_kps_ch, grid, slots;
-  size_t off_ml, bytes;
+  size_t off_cnt, off_o, off_ml, bytes;
 };
 
 // ---------------------------------------------------------------------------
@@ -269,35 +275,6 @@ __device__ SplitPlan plan_split(const AttnParams& p, int phys) {
     base += __builtin_amdgcn_readlane(incl, 63);
   }
   return sp;
-}
-
-// Partial slots of tile (b, g, rt) for the merge: first slot and split count
-// (0 when the tile does not exist or its request's sizes are malformed).
-__device__ int2 tile_slots(const AttnParams& p, int b, int g, int rt) {
-  const int lane = threadIdx.x & 63;
-  if (!p.balanced) {
-    const ReqShape r = req_shape(p, p.prefix_len[b], p.n_nodes[b]);
-    if (rt >= r.rt) return make_int2(0, 0);
-    const int kps = uniform_kps(p, r.ch);
-    return make_int2(((b * p.Hkv + g) * p.row_tiles + rt) * p.splits, (r.ch + kps - 1) / kps);
-  }
-  const ReqShape mine = lane_shape(p, lane);
-  const int kps = balanced_kps(p, lane, mine);
-  // slots of the requests before b
-  int start = 0;
-  for (int b0 = 0; b0 < b; b0 += 64) {
-    const int bb = b0 + lane;
-    int v = 0;
-    if (bb < b) {
-      const ReqShape r = b0 == 0 ? mine : req_shape(p, p.prefix_len[bb], p.n_nodes[bb]);
-      v = p.Hkv * r.rt * ((r.ch + kps - 1) / kps);
-    }
-    start += wave_sum_i(v);
-  }
-  const ReqShape r = req_shape(p, p.prefix_len[b], p.n_nodes[b]);
-  if (rt >= r.rt) return make_int2(0, 0);
-  const int s_b = (r.ch + kps - 1) / kps;
-  return make_int2(start + (g * r.rt + rt) * s_b, s_b);
 }
 
 template <int D>
@@ -601,6 +578,7 @@ __device__ void attn_valu(const AttnParams& p, ValuSmem<D>& sm, int b, int g, in
 // values, no loss to subnormals for small ones), and the merge multiplies by
 // the inverse, kept in the row's (m, l) record.  fp32 inputs keep fp32 (scale 1).
 typedef _Float16 tv_f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 tv_f16x8 __attribute__((ext_vector_type(8)));
 
 // Power of two for a row whose largest |O / l| is amax, and its inverse.
 __device__ __forceinline__ float2 part_scale(float amax) {
@@ -609,18 +587,45 @@ __device__ __forceinline__ float2 part_scale(float amax) {
   return make_float2(ldexpf(1.f, 15 - e), ldexpf(1.f, e - 15));
 }
 
+// Partials cross workgroups that may run on different XCDs, whose L2 caches
+// are not coherent with each other.  They are written and read as 64-bit
+// device-scope (agent) accesses, which write through to and read from the
+// device's coherent memory side, so no L2 write-back or invalidation is needed
+// around the hand-off (see publish_split).
+__device__ __forceinline__ void st_agent(void* ptr, uint64_t v) {
+  __hip_atomic_store((uint64_t*)ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent(const void* ptr) {
+  return __hip_atomic_load((uint64_t*)ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <bool kBF16>
 __device__ __forceinline__ void store_part4(void* part_o, size_t off, tv_f32x4 v) {
-  if (kBF16)
-    *(tv_f16x4*)((_Float16*)part_o + off) = __builtin_convertvector(v, tv_f16x4);
-  else
-    *(tv_f32x4*)((float*)part_o + off) = v;
+  if (kBF16) {
+    st_agent((_Float16*)part_o + off, __builtin_bit_cast(uint64_t, __builtin_convertvector(v, tv_f16x4)));
+  } else {
+    float* d = (float*)part_o + off;
+    st_agent(d, __builtin_bit_cast(uint64_t, (tv_f32x2){v[0], v[1]}));
+    st_agent(d + 2, __builtin_bit_cast(uint64_t, (tv_f32x2){v[2], v[3]}));
+  }
 }
 
 template <bool kBF16>
 __device__ __forceinline__ tv_f32x4 load_part4(const void* part_o, size_t off) {
-  if (kBF16) return __builtin_convertvector(*(const tv_f16x4*)((const _Float16*)part_o + off), tv_f32x4);
-  return *(const tv_f32x4*)((const float*)part_o + off);
+  if (kBF16) return __builtin_convertvector(__builtin_bit_cast(tv_f16x4, ld_agent((const _Float16*)part_o + off)), tv_f32x4);
+  const float* s = (const float*)part_o + off;
+  const tv_f32x2 lo = __builtin_bit_cast(tv_f32x2, ld_agent(s)), hi = __builtin_bit_cast(tv_f32x2, ld_agent(s + 2));
+  return (tv_f32x4){lo[0], lo[1], hi[0], hi[1]};
+}
+
+// A row's (m, l, inverse scale) record.
+__device__ __forceinline__ void store_ml(float4* rec, float m, float l, float z) {
+  st_agent(rec, __builtin_bit_cast(uint64_t, (tv_f32x2){m, l}));
+  st_agent((float*)rec + 2, __builtin_bit_cast(uint64_t, (tv_f32x2){z, 0.f}));
+}
+__device__ __forceinline__ float4 load_ml(const float4* rec) {
+  const tv_f32x2 a = __builtin_bit_cast(tv_f32x2, ld_agent(rec)), b = __builtin_bit_cast(tv_f32x2, ld_agent((const float*)rec + 2));
+  return make_float4(a[0], a[1], b[0], 0.f);
 }
 
 template <bool kBF16, int D>
@@ -634,20 +639,19 @@ __device__ __forceinline__ void store_out4(const AttnParams& p, int b, int g, in
   }
 }
 
-// Split-K merge, a second kernel: for every tile whose request used more than
-// one key split, combine the splits' (m, l, O/l) partials by log-sum-exp and
-// write the output rows.  The kernel boundary makes the partials visible (no
-// inter-workgroup fences or counters).  Each merge workgroup recomputes the
-// split plan (the same integer arithmetic as the attention grid) to find its
-// tile's partial slots.  A thread owns 8 d values of one row and walks the
-// splits in batches whose loads are in flight together, rescaling its running
-// sum when a batch raises the row's max.
-constexpr int kMergeThreads = 128;
+// Split-K merge inside the attention grid.  Every split of a tile writes its
+// partial and publishes it with one increment of the tile's counter (after a
+// barrier that follows every wave's stores).  The workgroup whose increment
+// completes the count has every other split's partial published before it,
+// merges the tile's rows by log-sum-exp from the workspace, and resets the
+// counter for the next call.  No workgroup waits
+// for another, so nothing depends on which workgroups are resident together.
+// A thread owns 8 d values of one row and walks the splits in batches whose
+// loads are in flight together, rescaling its running sum when a batch raises
+// the row's max.
 constexpr int kMergeVec = 8;     // d values per thread
-constexpr int kMergeBatch = 8;   // splits loaded together
-
-template <int D>
-constexpr int merge_rows() { return kMergeThreads / (D / kMergeVec); }   // rows per workgroup
+constexpr long long kMergeSpinLimit = 1LL << 19;   // bounded wait of a co-resident tile's splits (~0.5 s)
+constexpr int kMergeBatch = 4;   // splits loaded together
 
 template <bool kBF16>
 __device__ __forceinline__ void load_part8(const void* part_o, size_t off, float (&o)[kMergeVec]) {
@@ -659,66 +663,76 @@ __device__ __forceinline__ void load_part8(const void* part_o, size_t off, float
   }
 }
 
-template <bool kBF16, int D>
-__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnParams p) {
-  constexpr int TPR = D / kMergeVec, RPB = merge_rows<D>();
-  const int t = threadIdx.x;
-  const int groups = (p.rows_per_tile + RPB - 1) / RPB;
-  // same XCD-aware numbering as the attention grid: a tile's merge workgroups
-  // run on the XCD whose L2 took its partials
-  const int lid = tv_xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = lid / groups, rg = lid % groups;
-  const int bg = tile / p.row_tiles, rt = tile % p.row_tiles;
-  const int b = bg / p.Hkv, g = bg % p.Hkv;
-  const int r = rg * RPB + t / TPR, d = kMergeVec * (t % TPR);   // row within the tile, first d
-  const int2 sl = tile_slots(p, b, g, rt);
-  const int n_active = sl.y;
-  if (n_active < 2) return;                 // no tile, or written directly by the attention kernel
-  const int n = p.n_nodes[b];
-  const int row = rt * p.rows_per_tile + r;
-  if (r >= p.rows_per_tile || row >= n * p.G) return;
-  const size_t base = (size_t)sl.x * p.rows_per_tile + r;
-  float4 ml[kMergeBatch];
-  float o[kMergeBatch][kMergeVec];
-  float M = kNegInf, L = 0.f, acc[kMergeVec];
-#pragma unroll
-  for (int i = 0; i < kMergeVec; ++i) acc[i] = 0.f;
-  for (int s0 = 0; s0 < n_active; s0 += kMergeBatch) {
-#pragma unroll
-    for (int s = 0; s < kMergeBatch; ++s) {
-      if (s0 + s < n_active) {
-        const size_t pr = base + (size_t)(s0 + s) * p.rows_per_tile;
-        ml[s] = p.part_ml[pr];
-        load_part8<kBF16>(p.part_o, pr * D + d, o[s]);
-      }
-    }
-    float mb = kNegInf;
-#pragma unroll
-    for (int s = 0; s < kMergeBatch; ++s)
-      if (s0 + s < n_active) mb = fmaxf(mb, ml[s].x);
-    if (mb > M) {   // the batch raises the row's max: rescale what is summed so far
-      const float sc = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - mb);
-      L *= sc;
-#pragma unroll
-      for (int i = 0; i < kMergeVec; ++i) acc[i] *= sc;
-      M = mb;
-    }
-#pragma unroll
-    for (int s = 0; s < kMergeBatch; ++s) {
-      if (s0 + s < n_active && ml[s].x != kNegInf) {
-        const float w = __builtin_amdgcn_exp2f(ml[s].x - M) * ml[s].y;
-        L += w;
-        const float wo = w * ml[s].z;   // the stored row is O / l times 1 / ml.z
-#pragma unroll
-        for (int i = 0; i < kMergeVec; ++i) acc[i] += wo * o[s][i];
-      }
-    }
+// True in the workgroup that completes the tile's count (for every thread of
+// it).  Called by every thread after the partial stores; `flag` is LDS.  Each
+// wave waits until its device-scope partial stores have completed, the
+// barrier joins the waves, and one thread increments the tile's counter
+// (device scope).  The partials are written and read with device-scope
+// accesses (st_agent / ld_agent), so the stores that completed before the
+// increment are what the merging workgroup's loads, issued after it observed
+// the count, return; no cache write-back or invalidation is involved.
+__device__ __forceinline__ bool publish_split(const AttnParams& p, int* flag, int first, int n_active, bool ws_ok) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int last = 0;
+    if (ws_ok) last = __hip_atomic_fetch_add(p.counters + first, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_active - 1;
+    *flag = last;
   }
-  const float inv = 1.f / L;
-  float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-  store_out4<kBF16, D>(p, b, g, row, d, v4);
-  float w4[4] = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-  store_out4<kBF16, D>(p, b, g, row, d + 4, w4);
+  __syncthreads();
+  return *flag != 0;
+}
+
+// Rows [r0, r0 + rows) of tile `first` (its splits' partials at slots first ..
+// first + n_active - 1), by the NT threads of the merging workgroup.
+template <bool kBF16, int D, int NT>
+__device__ void merge_tile(const AttnParams& p, int first, int n_active, int b, int g, int r0, int rows) {
+  constexpr int TPR = D / kMergeVec;
+  for (int idx = threadIdx.x; idx < rows * TPR; idx += NT) {
+    const int r = idx / TPR, d = kMergeVec * (idx % TPR);
+    const size_t base = (size_t)first * p.rows_per_tile + r;
+    float4 ml[kMergeBatch];
+    float o[kMergeBatch][kMergeVec];
+    float M = kNegInf, L = 0.f, acc[kMergeVec];
+#pragma unroll
+    for (int i = 0; i < kMergeVec; ++i) acc[i] = 0.f;
+    for (int s0 = 0; s0 < n_active; s0 += kMergeBatch) {
+#pragma unroll
+      for (int s = 0; s < kMergeBatch; ++s) {
+        if (s0 + s < n_active) {
+          const size_t pr = base + (size_t)(s0 + s) * p.rows_per_tile;
+          ml[s] = load_ml(p.part_ml + pr);
+          load_part8<kBF16>(p.part_o, pr * D + d, o[s]);
+        }
+      }
+      float mb = kNegInf;
+#pragma unroll
+      for (int s = 0; s < kMergeBatch; ++s)
+        if (s0 + s < n_active) mb = fmaxf(mb, ml[s].x);
+      if (mb > M) {   // the batch raises the row's max: rescale what is summed so far
+        const float sc = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(M - mb);
+        L *= sc;
+#pragma unroll
+        for (int i = 0; i < kMergeVec; ++i) acc[i] *= sc;
+        M = mb;
+      }
+#pragma unroll
+      for (int s = 0; s < kMergeBatch; ++s) {
+        if (s0 + s < n_active && ml[s].x != kNegInf) {
+          const float w = __builtin_amdgcn_exp2f(ml[s].x - M) * ml[s].y;
+          L += w;
+          const float wo = w * ml[s].z;   // the stored row is O / l times 1 / ml.z
+#pragma unroll
+          for (int i = 0; i < kMergeVec; ++i) acc[i] += wo * o[s][i];
+        }
+      }
+    }
+    const float inv = 1.f / L;
+    float v4[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    store_out4<kBF16, D>(p, b, g, r0 + r, d, v4);
+    float w4[4] = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    store_out4<kBF16, D>(p, b, g, r0 + r, d + 4, w4);
+  }
 }
 
 // VALU path output: rows [r0, r0 + rows) are in LDS.
@@ -742,7 +756,7 @@ __device__ void emit_valu(const AttnParams& p, CommonSmem& cm, ValuSmem<D>& sm, 
     store_part4<kBF16>(p.part_o, (prow + r) * D + d,
                        (tv_f32x4){sm.o[r][d] * inv, sm.o[r][d + 1] * inv, sm.o[r][d + 2] * inv, sm.o[r][d + 3] * inv});
   }
-  if (t < rows) p.part_ml[prow + t] = make_float4(sm.m[t], sm.l[t], 1.f, 0.f);
+  if (t < rows) store_ml(p.part_ml + prow + t, sm.m[t], sm.l[t], 1.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -983,6 +997,290 @@ __device__ __forceinline__ void mfma_chunk(uint32_t slot, const tv_bf16x8 (&qop)
       a.oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[nt], a.oacc[dt][nt], 0, 0, 0);
 }
 
+// Key group 1 hands its (m, L, O) to group 0 through LDS (the ring is free:
+// every DMA has landed and the last barrier has passed).  Wave wr of each
+// group uses ring slot wr: O as [dt][nt][lane], then (m, L) as [nt][lane].
+// L is the row total.  Ends with group 0 holding the combined state.
+template <int D, int NTW, int KG>
+__device__ __forceinline__ void group_handoff(const uint32_t (&slot_lds)[ring_steps<KG>() * KG], WaveAcc<D, NTW>& a,
+                                              float (&L)[NTW], bool producer, int kg, int wr, int lane) {
+  constexpr int DT = Chunk<D>::DT;
+  typedef __attribute__((address_space(3))) tv_f32x4* lds_f32x4_ptr;
+  typedef __attribute__((address_space(3))) tv_f32x2* lds_f2_ptr;
+  const uint32_t mine = wr == 0 ? slot_lds[0] : wr == 1 ? slot_lds[1] : wr == 2 ? slot_lds[2] : slot_lds[3];
+  lds_f32x4_ptr xo = (lds_f32x4_ptr)(uintptr_t)mine;
+  lds_f2_ptr xml = (lds_f2_ptr)(uintptr_t)(mine + DT * NTW * 64 * 16);
+  static_assert(DT * NTW * 64 * 16 + NTW * 64 * 8 <= Chunk<D>::BYTES && kMfmaWaves <= ring_steps<KG>() * KG,
+                "hand-off buffers fit the ring");
+  tv_lds_barrier();
+  if (!producer && kg == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) xo[(dt * NTW + nt) * 64 + lane] = a.oacc[dt][nt];
+      xml[nt * 64 + lane] = (tv_f32x2){a.m_run[nt], L[nt]};
+    }
+  }
+  tv_lds_barrier();
+  if (producer || kg != 0) return;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const tv_f32x2 mb = xml[nt * 64 + lane];
+    const float M = fmaxf(a.m_run[nt], mb.x);
+    const float fa = a.m_run[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(a.m_run[nt] - M);
+    const float fb = mb.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mb.x - M);
+    a.m_run[nt] = M;
+    L[nt] = L[nt] * fa + mb.y * fb;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] = a.oacc[dt][nt] * fa + xo[(dt * NTW + nt) * 64 + lane] * fb;
+  }
+}
+
+// Output rows of one MFMA wave: lane l holds O[row rbase + 16*nt + l%16][16*dt + 4*(l/16) + i].
+template <int D, int NTW>
+__device__ __forceinline__ void write_rows(const AttnParams& p, const WaveAcc<D, NTW>& a, const float (&L)[NTW],
+                                           int b, int g, int rbase, int R, int lane) {
+  constexpr int DT = Chunk<D>::DT;
+  const int l16 = lane & 15, h4 = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int qrow = rbase + 16 * nt + l16;
+    if (qrow >= R) continue;
+    const float inv = 1.f / L[nt];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      float v4[4] = {a.oacc[dt][nt][0] * inv, a.oacc[dt][nt][1] * inv, a.oacc[dt][nt][2] * inv,
+                     a.oacc[dt][nt][3] * inv};
+      store_out4<true, D>(p, b, g, qrow, 16 * dt + 4 * h4, v4);
+    }
+  }
+}
+
+// Split partials of the MFMA path, in the waves' own register layout: for
+// slot s, 16-row block rb (= row in tile / 16) and d-tile pair j, lane l's 16
+// bytes are the fp16 values of oacc[2j][.] then oacc[2j+1][.] times the row's
+// power of two (O / L scaled as part_scale gives); the row's (m, L, inverse
+// power) record sits at part_ml[s * rows_per_tile + row].  Written and read
+// with 16-byte device-scope buffer accesses (cache policy sc1).
+constexpr int kSc1 = 16;   // buffer instruction cache-policy bit: device scope
+template <int D>
+__device__ __forceinline__ uint32_t part_off(int rows_per_tile, int s, int rb, int j, int lane) {
+  return (uint32_t)((((s * (rows_per_tile / 16) + rb) * (Chunk<D>::DT / 2) + j) * 64 + lane) * 16);
+}
+
+template <int D, int NTW>
+__device__ __forceinline__ void store_partial(const AttnParams& p, const WaveAcc<D, NTW>& a, const float (&L)[NTW],
+                                              int slot, int wr, int row0, int lane) {
+  constexpr int DT = Chunk<D>::DT;
+  const int l16 = lane & 15, h4 = lane >> 4;
+  const size_t slot_bytes = (size_t)p.rows_per_tile * D * 2;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((char*)p.part_o + slot * slot_bytes, (short)0,
+                                                                      (int)slot_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (size_t)slot * p.rows_per_tile, (short)0,
+                                                                      p.rows_per_tile * 16, 0x00020000);
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const float inv = L[nt] > 0.f ? 1.f / L[nt] : 0.f;
+    float amax = 0.f;   // the row's largest |O / L| over its four lanes sets the stored power of two
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(a.oacc[dt][nt][i] * inv));
+    amax = tv_rows_max(amax);
+    const float2 sc = part_scale(amax);
+    const float f = inv * sc.x;
+    const int rb = wr * NTW + nt;
+#pragma unroll
+    for (int j = 0; j < DT / 2; ++j) {
+      const tv_f16x4 lo = __builtin_convertvector(a.oacc[2 * j][nt] * f, tv_f16x4);
+      const tv_f16x4 hi = __builtin_convertvector(a.oacc[2 * j + 1][nt] * f, tv_f16x4);
+      const tv_u32x4 w = __builtin_bit_cast(tv_u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      __builtin_amdgcn_raw_buffer_store_b128(w, ro, part_off<D>(p.rows_per_tile, 0, rb, j, lane), 0, kSc1);
+    }
+    if (h4 == 0) {
+      const tv_u32x4 w = __builtin_bit_cast(tv_u32x4, (tv_f32x4){a.m_run[nt], L[nt], sc.y, 0.f});
+      __builtin_amdgcn_raw_buffer_store_b128(w, rm, (uint32_t)((row0 + 16 * nt + l16) * 16), 0, kSc1);
+    }
+  }
+}
+
+// Co-resident grids: every split of a tile merges a slice of the tile's rows
+// once all of them have published.  Thread-owned units are the 16-byte pieces
+// of the partial layout (row block rb, d-tile pair j, lane): 8 values of one
+// row.  The fold order is the same as in merge_partials (split kg, kg + KG,
+// ... per key group, then group 1 into group 0), so both ways of merging give
+// the same values.
+template <int D, int NTW, int KG, int NT>
+__device__ __forceinline__ void merge_slice(const AttnParams& p, int first, int n_active, int own_s, int b, int g,
+                                            int r0, int R) {
+  constexpr int DT = Chunk<D>::DT, JP = DT / 2;
+  const int RW = p.rows_per_tile, units = (RW / 16) * JP * 64;
+  const int u_begin = (int)((long long)units * own_s / n_active), u_end = (int)((long long)units * (own_s + 1) / n_active);
+  const size_t slot_bytes = (size_t)RW * D * 2;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((char*)p.part_o + first * slot_bytes, (short)0,
+                                                                      (int)(slot_bytes * n_active), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (size_t)first * RW, (short)0,
+                                                                      RW * 16 * n_active, 0x00020000);
+  constexpr int PB = 8;   // splits whose loads are in flight together
+  for (int u = u_begin + (int)threadIdx.x; u < u_end; u += NT) {
+    const int lane = u & 63, j = (u >> 6) % JP, rb = (u >> 6) / JP;
+    const int row = rb * 16 + (lane & 15);
+    float m[KG], l[KG];
+    tv_f32x4 lo[KG], hi[KG];
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      m[k] = kNegInf;
+      l[k] = 0.f;
+      lo[k] = hi[k] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    for (int s0 = 0; s0 < n_active; s0 += PB) {
+      tv_u32x4 po[PB], pm[PB];
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        const int sp = s0 + q;
+        if (sp < n_active) {
+          pm[q] = __builtin_amdgcn_raw_buffer_load_b128(rm, (uint32_t)((sp * RW + row) * 16), 0, kSc1);
+          po[q] = __builtin_amdgcn_raw_buffer_load_b128(ro, part_off<D>(RW, sp, rb, j, lane), 0, kSc1);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+        const int sp = s0 + q;
+        if (sp >= n_active) break;
+        const int k = KG == 1 ? 0 : sp % KG;
+        const tv_f32x4 ml = __builtin_bit_cast(tv_f32x4, pm[q]);
+        if (ml[0] == kNegInf) continue;
+        const float M = fmaxf(m[k], ml[0]);
+        const float fa = m[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[k] - M);
+        const float fb = __builtin_amdgcn_exp2f(ml[0] - M);
+        m[k] = M;
+        l[k] = l[k] * fa + ml[1] * fb;
+        const float w = fb * ml[1] * ml[2];
+        const tv_f16x8 h = __builtin_bit_cast(tv_f16x8, po[q]);
+        lo[k] = lo[k] * fa + __builtin_convertvector(__builtin_shufflevector(h, h, 0, 1, 2, 3), tv_f32x4) * w;
+        hi[k] = hi[k] * fa + __builtin_convertvector(__builtin_shufflevector(h, h, 4, 5, 6, 7), tv_f32x4) * w;
+      }
+    }
+    if constexpr (KG > 1) {
+      const float M = fmaxf(m[0], m[1]);
+      const float fa = m[0] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[0] - M);
+      const float fb = m[1] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[1] - M);
+      l[0] = l[0] * fa + l[1] * fb;
+      lo[0] = lo[0] * fa + lo[1] * fb;
+      hi[0] = hi[0] * fa + hi[1] * fb;
+    }
+    const int qrow = r0 + row;
+    if (qrow >= R) continue;
+    const float inv = 1.f / l[0];
+    const int d0 = 32 * j + 4 * (lane >> 4);
+    float v4[4] = {lo[0][0] * inv, lo[0][1] * inv, lo[0][2] * inv, lo[0][3] * inv};
+    store_out4<true, D>(p, b, g, qrow, d0, v4);
+    float w4[4] = {hi[0][0] * inv, hi[0][1] * inv, hi[0][2] * inv, hi[0][3] * inv};
+    store_out4<true, D>(p, b, g, qrow, d0 + 16, w4);
+  }
+}
+
+// Co-resident grids: count this split in, wait (bounded) until every split of
+// the tile has published, merge this split's slice of rows, then count it out;
+// the split that completes the second count resets the counter for the next
+// call.  A wait that expires (or TV_CHASE_SPIN_LIMIT < 0) gives the request
+// TV_REQ_TIMEOUT and invalidates the workspace header: the counter may be
+// left mid-count, so later calls report TV_REQ_BAD_WORKSPACE until the
+// workspace is prepared again.  No split's wait depends on a workgroup that
+// is not resident: the whole grid is.
+template <int D, int NTW, int KG, int NT>
+__device__ void merge_together(const AttnParams& p, int* flag, int first, int n_active, int own_s, bool ws_ok, int b,
+                               int g, int r0, int R) {
+  int* cnt = p.counters + first;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ok = ws_ok;
+    if (ok) {
+      __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (p.spin < 0) {
+        ok = 0;
+      } else {
+        long long it = 0;
+        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_active) {
+          if (++it > p.spin) {
+            ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      if (!ok) {
+        if (p.status) __hip_atomic_fetch_or(p.status + b, (int)TV_REQ_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store((unsigned long long*)p.header, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    *flag = ok;
+  }
+  __syncthreads();
+  if (*flag == 0) return;
+  merge_slice<D, NTW, KG, NT>(p, first, n_active, own_s, b, g, r0, R);
+  if (threadIdx.x == 0 && __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 2 * n_active - 1)
+    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The merging workgroup: MFMA wave wr of key group kg folds the tile's split
+// partials kg, kg + KG, ... (in that order) into its rows' state, PB splits
+// at a time with all their loads in flight together.
+template <int D, int NTW, int KG>
+__device__ __forceinline__ void merge_partials(const AttnParams& p, WaveAcc<D, NTW>& a, float (&L)[NTW], int first,
+                                               int n_active, int kg, int wr, int row0, int lane) {
+  constexpr int DT = Chunk<D>::DT, PB = NTW == 1 ? 4 : 2;
+  const int l16 = lane & 15;
+  const size_t slot_bytes = (size_t)p.rows_per_tile * D * 2;
+  const size_t tile_bytes = slot_bytes * n_active;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((char*)p.part_o + first * slot_bytes, (short)0,
+                                                                      (int)tile_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(p.part_ml + (size_t)first * p.rows_per_tile,
+                                                                      (short)0, p.rows_per_tile * 16 * n_active, 0x00020000);
+  for (int s0 = kg; s0 < n_active; s0 += KG * PB) {
+    tv_u32x4 po[PB][NTW][DT / 2], pm[PB][NTW];
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const int s = s0 + KG * k;
+      if (s < n_active) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const int rb = wr * NTW + nt;
+          pm[k][nt] = __builtin_amdgcn_raw_buffer_load_b128(rm, (uint32_t)((s * p.rows_per_tile + row0 + 16 * nt + l16) * 16),
+                                                            0, kSc1);
+#pragma unroll
+          for (int j = 0; j < DT / 2; ++j)
+            po[k][nt][j] = __builtin_amdgcn_raw_buffer_load_b128(ro, part_off<D>(p.rows_per_tile, s, rb, j, lane), 0, kSc1);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      if (s0 + KG * k >= n_active) break;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const tv_f32x4 ml = __builtin_bit_cast(tv_f32x4, pm[k][nt]);
+        if (ml[0] == kNegInf) continue;   // no key of that split is visible to the row
+        const float M = fmaxf(a.m_run[nt], ml[0]);
+        const float fa = a.m_run[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(a.m_run[nt] - M);
+        const float fb = __builtin_amdgcn_exp2f(ml[0] - M);
+        a.m_run[nt] = M;
+        L[nt] = L[nt] * fa + ml[1] * fb;
+        const float w = fb * ml[1] * ml[2];   // the stored row is O / L times 1 / ml[2]
+#pragma unroll
+        for (int j = 0; j < DT / 2; ++j) {
+          const tv_f16x8 h = __builtin_bit_cast(tv_f16x8, po[k][nt][j]);
+          const tv_f32x4 lo = __builtin_convertvector(__builtin_shufflevector(h, h, 0, 1, 2, 3), tv_f32x4);
+          const tv_f32x4 hi = __builtin_convertvector(__builtin_shufflevector(h, h, 4, 5, 6, 7), tv_f32x4);
+          a.oacc[2 * j][nt] = a.oacc[2 * j][nt] * fa + lo * w;
+          a.oacc[2 * j + 1][nt] = a.oacc[2 * j + 1][nt] * fa + hi * w;
+        }
+      }
+    }
+  }
+}
+
 // The key range of one split, step by step through an LDS ring of NS steps
 // of KG chunks.  With KG key groups, group k's four MFMA waves take the
 // chunks c = KG*step + k, so two waves share each SIMD and one's softmax runs
@@ -999,15 +1297,15 @@ __device__ __forceinline__ void mfma_chunk(uint32_t slot, const tv_bf16x8 (&qop)
 // distinct LDS objects and the stage loop is unrolled, so the compiler sees
 // which DMA writes which slot and adds no waits of its own before the slot
 // reads (the MFMA waves have no memory operations in flight).
-template <int D, int NTW, int KG>
+template <int D, int NTW, int KG, bool CO>
 __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, CommonSmem& cm, const int* tab,
                                                          const uint32_t (&slot_lds)[ring_steps<KG>() * KG],
                                                          const tv_bf16x8 (&qop)[NTW][D / 32],
                                                          const DmaLane& dl, int2 next_rows, int slot,
                                                          int n_active, int b, int g, int r0, int R, int P,
                                                          int k_begin, int k_end, int tab0, int ntab,
-                                                         bool tree_in_range) {
-  constexpr int DT = Chunk<D>::DT, RW = 64 * NTW, NB = Chunk<D>::NBLK, NS = ring_steps<KG>();
+                                                         bool tree_in_range, int own_s, bool ws_ok) {
+  constexpr int DT = Chunk<D>::DT, NB = Chunk<D>::NBLK, NS = ring_steps<KG>();
   constexpr int NW = kMfmaWaves * KG;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, h4 = lane >> 4;
@@ -1063,75 +1361,40 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
     }
   }
 
-  if constexpr (KG > 1) {
-    // key group 1 hands its (m, l, O) to group 0 through LDS (the ring is free:
-    // the producer's last wait drained every DMA before the last barrier)
-    // wave wr of each group uses ring slot wr: O as [dt][nt][lane], then (m, l) as [nt][lane]
-    typedef __attribute__((address_space(3))) tv_f32x4* lds_f32x4_ptr;
-    typedef __attribute__((address_space(3))) tv_f32x2* lds_f2_ptr;
-    const uint32_t mine = wr == 0 ? slot_lds[0] : wr == 1 ? slot_lds[1] : wr == 2 ? slot_lds[2] : slot_lds[3];
-    lds_f32x4_ptr xo = (lds_f32x4_ptr)(uintptr_t)mine;
-    lds_f2_ptr xml = (lds_f2_ptr)(uintptr_t)(mine + DT * NTW * 64 * 16);
-    static_assert(DT * NTW * 64 * 16 + NTW * 64 * 8 <= Chunk<D>::BYTES && kMfmaWaves <= NS * KG,
-                  "merge buffers fit the ring");
-    tv_lds_barrier();
-    if (!producer && kg == 1) {
+  // row totals of l (a lane holds the sum over its own keys of each chunk)
+  float L[NTW];
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) xo[(dt * NTW + nt) * 64 + lane] = a.oacc[dt][nt];
-        xml[nt * 64 + lane] = (tv_f32x2){a.m_run[nt], a.l_run[nt]};
-      }
-    }
-    tv_lds_barrier();
-    if (producer || kg != 0) return;
+  for (int nt = 0; nt < NTW; ++nt) L[nt] = tv_rows_sum(a.l_run[nt]);
+  if constexpr (KG > 1) group_handoff<D, NTW, KG>(slot_lds, a, L, producer, kg, wr, lane);
+  const bool writer = !producer && kg == 0;   // group 0 holds the workgroup's state now
+
+  if (n_active == 1) {
+    if (writer) write_rows<D, NTW>(p, a, L, b, g, rbase, R, lane);
+    return;
+  }
+  // split partial, then the tile's count; the last split merges
+  const int first = slot - own_s;   // the tile's splits are slots first .. first + n_active - 1
+  if (writer) store_partial<D, NTW>(p, a, L, slot, wr, rbase - r0, lane);
+  if constexpr (CO) {
+    merge_together<D, NTW, KG, 64 * (kMfmaWaves + 1) * KG>(p, &cm.flag, first, n_active, own_s, ws_ok, b, g, r0, R);
+    return;
+  }
+  if (!publish_split(p, &cm.flag, first, n_active, ws_ok)) return;
+  if (!producer) {
+    // every split's stored partial, this one's included, in split order: the
+    // result does not depend on which split arrived last
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
-      const tv_f32x2 mb = xml[nt * 64 + lane];
-      const float M = fmaxf(a.m_run[nt], mb.x);
-      const float fa = a.m_run[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(a.m_run[nt] - M);
-      const float fb = mb.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mb.x - M);
-      a.m_run[nt] = M;
-      a.l_run[nt] = a.l_run[nt] * fa + mb.y * fb;
+      a.m_run[nt] = kNegInf;
+      L[nt] = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] = a.oacc[dt][nt] * fa + xo[(dt * NTW + nt) * 64 + lane] * fb;
+      for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
     }
+    merge_partials<D, NTW, KG>(p, a, L, first, n_active, kg, wr, rbase - r0, lane);
   }
-
-  // output: lane l holds O[row rbase + 16*nt + l%16][16*dt + 4*(l/16) + i]
-  const size_t prow = (size_t)slot * RW;
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    float lt = a.l_run[nt];
-    lt = tv_rows_sum(lt);
-    const int qrow = rbase + 16 * nt + l16;
-    if (n_active == 1) {
-      if (qrow >= R) continue;
-      const float inv = 1.f / lt;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        float v4[4] = {a.oacc[dt][nt][0] * inv, a.oacc[dt][nt][1] * inv, a.oacc[dt][nt][2] * inv,
-                       a.oacc[dt][nt][3] * inv};
-        store_out4<true, D>(p, b, g, qrow, 16 * dt + 4 * h4, v4);
-      }
-    } else {
-      // the row's largest |O / l| over its four lanes sets the stored power of two
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      float amax = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(a.oacc[dt][nt][i] * inv));
-      amax = tv_rows_max(amax);
-      if (qrow >= R) continue;
-      const float2 sc = part_scale(amax);
-      const size_t row = prow + (qrow - r0);
-      const float f = inv * sc.x;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) store_part4<true>(p.part_o, row * D + 16 * dt + 4 * h4, a.oacc[dt][nt] * f);
-      if (h4 == 0) p.part_ml[row] = make_float4(a.m_run[nt], lt, sc.y, 0.f);
-    }
-  }
+  if constexpr (KG > 1) group_handoff<D, NTW, KG>(slot_lds, a, L, producer, kg, wr, lane);
+  if (writer) write_rows<D, NTW>(p, a, L, b, g, rbase, R, lane);
+  if (threadIdx.x == 0) __hip_atomic_store(p.counters + first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -1146,7 +1409,9 @@ constexpr int wg_per_cu() { return (kBF16 && (NTW > 1 || KG > 1)) ? 1 : 2; }
 template <bool kBF16, int KG>
 constexpr int block_threads() { return kBF16 ? mfma_threads<KG>() : kThreads; }
 
-template <bool kBF16, int D, int NTW, int KG>
+// CO: the whole grid is resident at once, so the splits of a tile merge
+// together (each a slice of the rows) instead of the last one merging alone.
+template <bool kBF16, int D, int NTW, int KG, bool CO>
 __global__ __launch_bounds__((block_threads<kBF16, KG>()), (wg_per_cu<kBF16, NTW, KG>())) void tree_attn_kernel(AttnParams p) {
   constexpr int RW = kBF16 ? 64 * NTW : 16;
   constexpr int NT = block_threads<kBF16, KG>();
@@ -1184,6 +1449,10 @@ __global__ __launch_bounds__((block_threads<kBF16, KG>()), (wg_per_cu<kBF16, NTW
   const int keys_total = P + n;
   const int n_active = sp.splits;
   const int k_end = min(k_begin + kps, keys_total);
+  // A tile split over keys hands its partials over through the workspace's
+  // counters, which must have been prepared: the header is loaded with the
+  // prologue's other loads and checked after its barrier.
+  unsigned long long hdr[2] = {kWsMagic, ~0ull};
 
   if constexpr (kBF16) {
     // the ring: distinct LDS objects, one chunk each
@@ -1228,6 +1497,10 @@ __global__ __launch_bounds__((block_threads<kBF16, KG>()), (wg_per_cu<kBF16, NTW
       }
     }
     if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
+    if (n_active > 1) {
+      hdr[0] = p.header[0];
+      hdr[1] = p.header[1];
+    }
     const int ntab = min(p.max_blocks - tab0, (kps + p.bs - 1) / p.bs + 1);
     for (int i = t; i < ntab; i += NT) {
       const int blk = trow[tab0 + i];
@@ -1236,6 +1509,7 @@ __global__ __launch_bounds__((block_threads<kBF16, KG>()), (wg_per_cu<kBF16, NTW
     }
     if (t == 0) cm.flag = 0;
     __syncthreads();   // also completes the query loads before any DMA is in flight
+    const bool ws_ok = (hdr[0] == kWsMagic) & (hdr[1] >= p.need);
 
     // parent array: parent[0] = -1 and 0 <= parent[i] < i
     if (t < n) {
@@ -1276,19 +1550,24 @@ __global__ __launch_bounds__((block_threads<kBF16, KG>()), (wg_per_cu<kBF16, NTW
       for (int i = t; i < nblk; i += NT)
         if (!block_ok(trow[i], p.num_blocks)) cm.flag = 1;
       tv_lds_barrier();
-      if (t == 0 && p.status) p.status[b] = cm.flag ? TV_REQ_BAD_KV : 0;
+      if (t == 0 && p.status) p.status[b] = (cm.flag ? TV_REQ_BAD_KV : 0) | (ws_ok ? 0 : TV_REQ_BAD_WORKSPACE);
       // keep going: loads from bad blocks are redirected
     }
     const bool tree_in_range = k_end > P;
     if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
     tv_lds_barrier();
-    attn_mfma<D, NTW, KG>(p, cm, tab, slots, qop, dl, next_rows, sp.slot, n_active, b, g, r0, R, P, k_begin, k_end,
-                          tab0, ntab, tree_in_range);
+    attn_mfma<D, NTW, KG, CO>(p, cm, tab, slots, qop, dl, next_rows, sp.slot, n_active, b, g, r0, R, P, k_begin, k_end,
+                          tab0, ntab, tree_in_range, sp.s, ws_ok);
   } else {
     __shared__ ValuSmem<D> vs;
     if (t < kMaxNodes) cm.par[t] = (t < p.n_max) ? p.parent[(size_t)b * p.n_max + t] : -1;
+    if (n_active > 1) {
+      hdr[0] = p.header[0];
+      hdr[1] = p.header[1];
+    }
     if (t == 0) cm.flag = 0;
     __syncthreads();
+    const bool ws_ok = (hdr[0] == kWsMagic) & (hdr[1] >= p.need);
     if (t < n) {
       const int pi = cm.par[t];
       const bool ok = (t == 0) ? (pi == -1) : (pi >= 0 && pi < t);
@@ -1304,7 +1583,7 @@ __global__ __launch_bounds__((block_threads<kBF16, KG>()), (wg_per_cu<kBF16, NTW
       for (int i = t; i < nblk; i += NT)
         if (!block_ok(trow[i], p.num_blocks)) cm.flag = 1;
       __syncthreads();
-      if (t == 0 && p.status) p.status[b] = cm.flag ? TV_REQ_BAD_KV : 0;
+      if (t == 0 && p.status) p.status[b] = (cm.flag ? TV_REQ_BAD_KV : 0) | (ws_ok ? 0 : TV_REQ_BAD_WORKSPACE);
     }
     const bool tree_in_range = k_end > P;
     if (tree_in_range && t < 64) build_ancestor_bitmaps(cm.par, n, cm.anc, t);
@@ -1312,6 +1591,10 @@ __global__ __launch_bounds__((block_threads<kBF16, KG>()), (wg_per_cu<kBF16, NTW
     const int rows = min(RW, R - r0);
     attn_valu<false, D>(p, vs, b, g, r0, rows, P, k_begin, k_end, tree_in_range, cm.anc);
     emit_valu<false, D, RW>(p, cm, vs, sp.slot, n_active, b, g, r0, rows);
+    if (n_active > 1 && publish_split(p, &cm.flag, sp.slot - sp.s, n_active, ws_ok)) {
+      merge_tile<false, D, NT>(p, sp.slot - sp.s, n_active, b, g, r0, rows);
+      if (t == 0) __hip_atomic_store(p.counters + sp.slot - sp.s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -1398,12 +1681,15 @@ int make_plan(const tv_attn_desc* d, int cu, int ntw, AttnPlan* pl) {
   if (grid > 0x7fffffff || slots > 0x7fffffff) return TV_ERR_UNSUPPORTED;
   pl->grid = (int)grid;
   pl->slots = (int)slots;
+  // workspace (only when some tile may be split): the prepared-workspace
+  // header, one counter per slot, then the partials
   size_t bytes = 0;
-  pl->off_ml = 0;
+  pl->off_cnt = pl->off_o = pl->off_ml = 0;
   if (slots > 0) {
     const size_t esz = d->dtype == TV_BF16 ? 2 : 4;   // partial O element: fp16 for bf16 inputs
-    bytes = (size_t)slots * pl->rows_per_tile * (size_t)d->head_dim * esz;
-    pl->off_ml = tv_align_up(bytes, 256);
+    pl->off_cnt = kWsHeader;
+    pl->off_o = tv_align_up(pl->off_cnt + (size_t)slots * sizeof(int), 256);
+    pl->off_ml = tv_align_up(pl->off_o + (size_t)slots * pl->rows_per_tile * (size_t)d->head_dim * esz, 256);
     bytes = pl->off_ml + (size_t)slots * pl->rows_per_tile * sizeof(float4);
   }
   pl->bytes = tv_align_up(bytes, 256);
@@ -1412,17 +1698,37 @@ int make_plan(const tv_attn_desc* d, int cu, int ntw, AttnPlan* pl) {
 
 typedef void (*AttnKernel)(AttnParams);
 
-AttnKernel pick_kernel(const tv_attn_desc* d, int ntw, int kg) {
+// Workgroups of `k` one CU holds at once (registers and LDS decide; cached per
+// device and kernel, 0 when the query fails).
+int resident_per_cu(AttnKernel k, int threads) {
+  static std::mutex mu;
+  static struct { int dev; AttnKernel k; int nb; } cache[64];
+  static int n_cache = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n_cache; ++i)
+    if (cache[i].dev == dev && cache[i].k == k) return cache[i].nb;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, threads, 0) != hipSuccess) nb = 0;
+  if (n_cache < 64) cache[n_cache++] = {dev, k, nb};
+  return nb;
+}
+
+template <bool CO>
+AttnKernel pick_kernel_co(const tv_attn_desc* d, int ntw, int kg) {
   const bool bf = d->dtype == TV_BF16;
   if (d->head_dim == 128) {
-    if (!bf) return tree_attn_kernel<false, 128, 1, 1>;
-    if (kg == 2) return tree_attn_kernel<true, 128, 1, 2>;
-    return ntw == 2 ? tree_attn_kernel<true, 128, 2, 1> : tree_attn_kernel<true, 128, 1, 1>;
+    if (!bf) return tree_attn_kernel<false, 128, 1, 1, false>;
+    if (kg == 2) return tree_attn_kernel<true, 128, 1, 2, CO>;
+    return ntw == 2 ? tree_attn_kernel<true, 128, 2, 1, CO> : tree_attn_kernel<true, 128, 1, 1, CO>;
   }
-  if (!bf) return tree_attn_kernel<false, 64, 1, 1>;
-  if (kg == 2) return tree_attn_kernel<true, 64, 1, 2>;
-  return ntw == 2 ? tree_attn_kernel<true, 64, 2, 1> : tree_attn_kernel<true, 64, 1, 1>;
+  if (!bf) return tree_attn_kernel<false, 64, 1, 1, false>;
+  if (kg == 2) return tree_attn_kernel<true, 64, 1, 2, CO>;
+  return ntw == 2 ? tree_attn_kernel<true, 64, 2, 1, CO> : tree_attn_kernel<true, 64, 1, 1, CO>;
 }
+
+AttnKernel pick_kernel(const tv_attn_desc* d, int ntw, int kg) { return pick_kernel_co<false>(d, ntw, kg); }
 
 int plan_for(const tv_attn_desc* d, AttnPlan* pl, AttnKernel* kern) {
   int cu = 0;
@@ -1462,6 +1768,7 @@ static int tree_attn_forward_impl(const tv_attn_desc* desc, const void* q, const
   rc = plan_for(desc, &pl, &kern);
   if (rc != TV_OK) return rc;
   if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return TV_ERR_WORKSPACE;
+  if (pl.bytes > 0 && ((uintptr_t)workspace & 255) != 0) return TV_ERR_INVALID_ARG;
 
   AttnParams p;
   p.q = q;
@@ -1473,8 +1780,11 @@ static int tree_attn_forward_impl(const tv_attn_desc* desc, const void* q, const
   p.parent = parent;
   p.out = out;
   p.status = status;
-  p.part_o = workspace;
+  p.header = (const unsigned long long*)workspace;
+  p.counters = (int*)((char*)workspace + pl.off_cnt);
+  p.part_o = (char*)workspace + pl.off_o;
   p.part_ml = (float4*)((char*)workspace + pl.off_ml);
+  p.need = pl.bytes;
   p.B = desc->batch;
   p.n_max = desc->n_max;
   p.Hq = desc->n_q_heads;
@@ -1494,20 +1804,20 @@ static int tree_attn_forward_impl(const tv_attn_desc* desc, const void* q, const
   p.nwg = pl.nwg;
   p.max_kps_ch = pl.max_kps_ch;
   p.grid = pl.grid;
+  p.spin = tv_chase_spin_limit(kMergeSpinLimit);
+  p.coresident = 0;
   if (pl.grid > 0) {
     const int threads = desc->dtype != TV_BF16 ? kThreads : (pl.kg == 2 ? mfma_threads<2>() : mfma_threads<1>());
+    if (pl.slots > 0 && desc->dtype == TV_BF16) {
+      // the whole grid fits on the CUs at once: the splits of a tile merge together
+      AttnKernel co = pick_kernel_co<true>(desc, pl.ntw, pl.kg);
+      int cu = 0;
+      if (tv_device_cu_count(&cu) == TV_OK && (long long)resident_per_cu(co, threads) * cu >= pl.grid) {
+        p.coresident = 1;
+        kern = co;
+      }
+    }
     hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(threads), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  }
-  if (pl.slots > 0) {
-    const long long tiles = (long long)desc->batch * desc->n_kv_heads * pl.row_tiles;
-    const int rpb = desc->head_dim == 128 ? merge_rows<128>() : merge_rows<64>();
-    const long long grid = tiles * ((pl.rows_per_tile + rpb - 1) / rpb);
-    if (grid > 0x7fffffff) return TV_ERR_UNSUPPORTED;
-    const bool bf = desc->dtype == TV_BF16;
-    void (*mk)(AttnParams) = desc->head_dim == 128 ? (bf ? attn_merge_kernel<true, 128> : attn_merge_kernel<false, 128>)
-                                                   : (bf ? attn_merge_kernel<true, 64> : attn_merge_kernel<false, 64>);
-    hipLaunchKernelGGL(mk, dim3((unsigned)grid), dim3(kMergeThreads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   }
   return TV_OK;

@@ -79,14 +79,11 @@ constexpr unsigned long long kWritten = 1ull << 63;  // marks a published exchan
 constexpr int kPrioSteps = 3;                        // load-order classes: 0, 1, 2, 3+ children
 constexpr long long kChaseSpinLimit = kSpinLimit << 2;   // a chase workgroup's bounded wait (~2 s)
 
-// A verifier's workspace starts with a header that
-// tree_verify_workspace_init writes after zero-filling the rest: a magic word
-// and the number of bytes it cleared.  The verifiers' slots tell a published
-// value from an empty one by their contents and every call leaves them at
-// zero, so a workspace that was never initialised (or is too small for this
-// call's layout) must not be used: such a request gets TV_REQ_BAD_WORKSPACE.
-constexpr unsigned long long kWsMagic = 0x7476777370616365ull;
-constexpr size_t kWsHeader = 256;
+// A verifier's workspace starts with the prepared-workspace header (kWsMagic,
+// bytes cleared).  The verifiers' slots tell a published value from an empty
+// one by their contents and every call leaves them at zero, so a workspace
+// that was never initialised (or is too small for this call's layout) must
+// not be used: such a request gets TV_REQ_BAD_WORKSPACE.
 
 // Buffer resource over one logit row of V floats.  Buffer loads address the row
 // with a 32-bit offset plus an immediate (one VGPR per batch of loads instead of a

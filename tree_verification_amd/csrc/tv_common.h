@@ -12,6 +12,14 @@ typedef __bf16 tv_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float tv_f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t tv_u32x4 __attribute__((ext_vector_type(4)));
 
+// A workspace whose slots must start at zero begins with a header that
+// tree_verify_workspace_init writes after zero-filling the rest: a magic word
+// and the number of bytes it cleared.  Kernels that use such slots check it and
+// fail their requests with TV_REQ_BAD_WORKSPACE instead of reading a buffer
+// that was never prepared (or is too small for the call's layout).
+constexpr unsigned long long kWsMagic = 0x7476777370616365ull;
+constexpr size_t kWsHeader = 256;
+
 // ---- host-side helpers ----------------------------------------------------
 
 // Number of compute units of the current device (cached per device).
