@@ -893,6 +893,85 @@ struct WaveAcc {
   tv_f32x4 oacc[Chunk<D>::DT][NTW];
 };
 
+// Online-softmax step of one 16-row tile over a chunk whose 32 keys are all
+// visible (no mask): the tile's running max moves only when the chunk's max
+// exceeds it by more than kLazy (log2 units); returns the factor the tile's
+// accumulators must be scaled by (1 when the max did not move) and the chunk's
+// probabilities as the bf16 B operand of the PV product.
+constexpr float kLazy = 8.f;
+__device__ __forceinline__ float softmax_plain(const tv_f32x4 (&sc)[2], float& m_run, float& l_run, float scale_log2,
+                                               tv_bf16x8& pop) {
+  float rmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  rmax = tv_rows_max(rmax);
+  const float cmax = rmax * scale_log2;
+  // bitwise, not short-circuit: a branch here would split the scheduling region
+  const bool fresh = m_run == kNegInf;
+  const bool move = (cmax > m_run + kLazy) | (fresh & (cmax != kNegInf));
+  const float m_ref = move ? cmax : m_run;
+  const float alpha = (move & !fresh) ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.f;
+  m_run = m_ref;
+  const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+  float e[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[4 * tt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[tt][i], scale_log2, neg_m));
+  l_run = l_run * alpha + (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+  const tv_u32x4 pw = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                       pack_bf16x2(e[6], e[7])};
+  pop = __builtin_bit_cast(tv_bf16x8, pw);
+  return alpha;
+}
+
+// A chunk of visible prefix keys for a wave with two 16-row tiles, laid out
+// so that the matrix pipe and the VALU can overlap: tile 1's S^T = K Q^T can
+// run under tile 0's softmax, and tile 0's O^T += V^T P^T under tile 1's
+// softmax.  The softmax step is branch-free and accumulator rescaling (rare
+// with the lazy max) is a uniform branch between the two halves, so each half
+// is one straight-line region the compiler schedules as a whole (pinning the
+// order with scheduling-group barriers measured no better).
+template <int D>
+__device__ __forceinline__ void mfma_chunk_plain2(uint32_t slot, const tv_bf16x8 (&qop)[2][D / 32],
+                                                  WaveAcc<D, 2>& a, float scale_log2, int lane) {
+  constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT;
+  tv_bf16x8 kop[2][KK], vop[DT];
+  tv_f32x4 sc[2][2];
+  tv_bf16x8 pop[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = lds_read16(slot + (tt * KK + kk) * 1024 + lane * 16);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[tt][kk], qop[nt][kk], acc, 0, 0, 0);
+      sc[nt][tt] = acc;
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) vop[dt] = lds_vop<D>(slot + 2 * KK * 1024, dt, lane);
+  const float alpha0 = softmax_plain(sc[0], a.m_run[0], a.l_run[0], scale_log2, pop[0]);
+  if (__any(alpha0 != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) a.oacc[dt][0] *= alpha0;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    a.oacc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[0], a.oacc[dt][0], 0, 0, 0);
+  const float alpha1 = softmax_plain(sc[1], a.m_run[1], a.l_run[1], scale_log2, pop[1]);
+  if (__any(alpha1 != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) a.oacc[dt][1] *= alpha1;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    a.oacc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[1], a.oacc[dt][1], 0, 0, 0);
+}
+
 // One 32-key chunk from an LDS slot: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
 template <int D, int NTW>
 __device__ __forceinline__ void mfma_chunk(uint32_t slot, const tv_bf16x8 (&qop)[NTW][D / 32],
@@ -900,6 +979,12 @@ __device__ __forceinline__ void mfma_chunk(uint32_t slot, const tv_bf16x8 (&qop)
                                            const uint64_t (&ahi)[NTW], int key0, int P, int k_end,
                                            float scale_log2, int lane) {
   constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT;
+  if constexpr (NTW == 2) {
+    if (key0 + 32 <= P && key0 + 32 <= k_end) {   // prefix keys only: no mask
+      mfma_chunk_plain2<D>(slot, qop, a, scale_log2, lane);
+      return;
+    }
+  }
   const int h4 = lane >> 4;
   tv_bf16x8 kop[2][KK], vop[DT];
 #pragma unroll
@@ -945,7 +1030,6 @@ __device__ __forceinline__ void mfma_chunk(uint32_t slot, const tv_bf16x8 (&qop)
   // positive) and the scale is folded into the exponent's FMA.  The running max
   // only moves when a row's max grows by more than kLazy (log2 units), so the
   // accumulators are rescaled rarely; probabilities stay below 2^kLazy.
-  constexpr float kLazy = 8.f;
   tv_bf16x8 pop[NTW];
   float alpha[NTW];
   bool any_rescale = false;
@@ -1376,7 +1460,7 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
   const int first = slot - own_s;   // the tile's splits are slots first .. first + n_active - 1
   if (writer) store_partial<D, NTW>(p, a, L, slot, wr, rbase - r0, lane);
   if constexpr (CO) {
-    merge_together<D, NTW, KG, 64 * (kMfmaWaves + 1) * KG>(p, &cm.flag, first, n_active, own_s, ws_ok, b, g, r0, R);
+    merge_together<D, NTW, KG, mfma_threads<KG>()>(p, &cm.flag, first, n_active, own_s, ws_ok, b, g, r0, R);
     return;
   }
   if (!publish_split(p, &cm.flag, first, n_active, ws_ok)) return;
@@ -1406,16 +1490,16 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
 template <bool kBF16, int NTW, int KG>
 constexpr int wg_per_cu() { return (kBF16 && (NTW > 1 || KG > 1)) ? 1 : 2; }
 
-template <bool kBF16, int KG>
+template <bool kBF16, int NTW, int KG>
 constexpr int block_threads() { return kBF16 ? mfma_threads<KG>() : kThreads; }
 
 // CO: the whole grid is resident at once, so the splits of a tile merge
 // together (each a slice of the rows) instead of the last one merging alone.
 template <bool kBF16, int D, int NTW, int KG, bool CO>
-__global__ __launch_bounds__((block_threads<kBF16, KG>()), (wg_per_cu<kBF16, NTW, KG>())) void tree_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__((block_threads<kBF16, NTW, KG>()), (wg_per_cu<kBF16, NTW, KG>())) void tree_attn_kernel(AttnParams p) {
   constexpr int RW = kBF16 ? 64 * NTW : 16;
-  constexpr int NT = block_threads<kBF16, KG>();
-  constexpr int NW = kMfmaWaves * KG;   // MFMA waves; waves NW .. NW + KG - 1 are the producers
+  constexpr int NT = block_threads<kBF16, NTW, KG>();
+  constexpr int NW = kMfmaWaves * KG;   // MFMA waves; the waves after them are the producers
   __shared__ CommonSmem cm;
   const int t = threadIdx.x;
   // balanced plans: workgroup 0 reports every request whose sizes are malformed
@@ -1633,7 +1717,9 @@ int choose_ntw(const tv_attn_desc* d, int cu) {
 // with its own producer wave (64-row tiles only: 128-row tiles need more
 // registers than two waves per SIMD leave).  Measured on MI355X: the 4096-key
 // chains 200 -> 193 us; 128-row tiles with one group stay better for the
-// 70B-shaped share (1005 against 1058 us as 64-row tiles with two groups).
+// 70B-shaped share (1005 against 1058 us as 64-row tiles with two groups, and
+// 790 against 1107 us as 128-row tiles with two groups whose MFMA waves issue
+// their own chunks' DMAs, a quarter each, without producer waves).
 int choose_kg(const tv_attn_desc* d, int ntw) {
   return (d->dtype == TV_BF16 && ntw == 1) ? 2 : 1;
 }
