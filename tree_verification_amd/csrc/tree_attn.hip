@@ -889,61 +889,64 @@ __device__ __forceinline__ tv_bf16x8 lds_vop(uint32_t vreg, int dt, int lane) {
 // Running softmax state and output accumulators of one wave (16*NTW rows).
 template <int D, int NTW>
 struct WaveAcc {
-  float m_run[NTW], l_run[NTW];
+  float m_run[NTW], l_run[NTW];     // l_run: this lane's share of the row sums of masked chunks
   tv_f32x4 oacc[Chunk<D>::DT][NTW];
+  tv_f32x4 lacc[NTW];               // row sums of unmasked chunks, by a matrix product with ones
 };
 
 // Online-softmax step of one 16-row tile over a chunk whose 32 keys are all
 // visible (no mask): the tile's running max moves only when the chunk's max
-// exceeds it by more than kLazy (log2 units); returns the factor the tile's
-// accumulators must be scaled by (1 when the max did not move) and the chunk's
-// probabilities as the bf16 B operand of the PV product.
+// exceeds it by more than kLazy (log2 units).  Each lane first tests its own
+// eight scores; only when some lane's exceed the margin (rare) does the wave
+// take the row maxima across lanes.  Returns the factor the tile's
+// accumulators must be scaled by (1 when the max did not move) and the
+// chunk's probabilities as the bf16 B operand of the PV product.  Written
+// without short-circuit tests, so the common path is straight-line code.
 constexpr float kLazy = 8.f;
-__device__ __forceinline__ float softmax_plain(const tv_f32x4 (&sc)[2], float& m_run, float& l_run, float scale_log2,
+__device__ __forceinline__ float softmax_plain(const tv_f32x4 (&sc)[2], float& m_run, float scale_log2,
                                                tv_bf16x8& pop) {
-  float rmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-  rmax = tv_rows_max(rmax);
-  const float cmax = rmax * scale_log2;
-  // bitwise, not short-circuit: a branch here would split the scheduling region
-  const bool fresh = m_run == kNegInf;
-  const bool move = (cmax > m_run + kLazy) | (fresh & (cmax != kNegInf));
-  const float m_ref = move ? cmax : m_run;
-  const float alpha = (move & !fresh) ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.f;
-  m_run = m_ref;
-  const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+  const float lmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  float alpha = 1.f;
+  if (__any((lmax * scale_log2 > m_run + kLazy) | (m_run == kNegInf))) {
+    const float cmax = tv_rows_max(lmax) * scale_log2;
+    const bool fresh = m_run == kNegInf;
+    const bool move = (cmax > m_run + kLazy) | (fresh & (cmax != kNegInf));
+    const float m_ref = move ? cmax : m_run;
+    alpha = (move & !fresh) ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.f;
+    m_run = m_ref;
+  }
+  const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
   float e[8];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) e[4 * tt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[tt][i], scale_log2, neg_m));
-  l_run = l_run * alpha + (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
   const tv_u32x4 pw = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
                        pack_bf16x2(e[6], e[7])};
   pop = __builtin_bit_cast(tv_bf16x8, pw);
   return alpha;
 }
 
-// A chunk of visible prefix keys for a wave with two 16-row tiles, laid out
-// so that the matrix pipe and the VALU can overlap: tile 1's S^T = K Q^T can
-// run under tile 0's softmax, and tile 0's O^T += V^T P^T under tile 1's
-// softmax.  The softmax step is branch-free and accumulator rescaling (rare
-// with the lazy max) is a uniform branch between the two halves, so each half
-// is one straight-line region the compiler schedules as a whole (pinning the
-// order with scheduling-group barriers measured no better).
-template <int D>
-__device__ __forceinline__ void mfma_chunk_plain2(uint32_t slot, const tv_bf16x8 (&qop)[2][D / 32],
-                                                  WaveAcc<D, 2>& a, float scale_log2, int lane) {
+// A chunk of visible prefix keys (no mask).  With two 16-row tiles per wave
+// the products of one tile can run under the other's softmax: both tiles'
+// S^T = K Q^T first, then per tile its softmax, rescaling (a uniform branch,
+// rare with the lazy max) and O^T += V^T P^T.  The row sums come from one more
+// product per tile, with a V^T operand of ones: the sums of the same bf16
+// probabilities the PV product uses, with no VALU additions.
+template <int D, int NTW>
+__device__ __forceinline__ void mfma_chunk_plain(uint32_t slot, const tv_bf16x8 (&qop)[NTW][D / 32],
+                                                 WaveAcc<D, NTW>& a, float scale_log2, int lane) {
   constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT;
+  const tv_bf16x8 ones = __builtin_bit_cast(tv_bf16x8, (tv_u32x4){0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   tv_bf16x8 kop[2][KK], vop[DT];
-  tv_f32x4 sc[2][2];
-  tv_bf16x8 pop[2];
+  tv_f32x4 sc[NTW][2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = lds_read16(slot + (tt * KK + kk) * 1024 + lane * 16);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       tv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -954,22 +957,21 @@ __device__ __forceinline__ void mfma_chunk_plain2(uint32_t slot, const tv_bf16x8
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) vop[dt] = lds_vop<D>(slot + 2 * KK * 1024, dt, lane);
-  const float alpha0 = softmax_plain(sc[0], a.m_run[0], a.l_run[0], scale_log2, pop[0]);
-  if (__any(alpha0 != 1.f)) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) a.oacc[dt][0] *= alpha0;
+  for (int nt = 0; nt < NTW; ++nt) {
+    tv_bf16x8 pop;
+    const float alpha = softmax_plain(sc[nt], a.m_run[nt], scale_log2, pop);
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] *= alpha;
+      a.lacc[nt] *= alpha;
+      a.l_run[nt] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      a.oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop, a.oacc[dt][nt], 0, 0, 0);
+    a.lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, a.lacc[nt], 0, 0, 0);
   }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    a.oacc[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[0], a.oacc[dt][0], 0, 0, 0);
-  const float alpha1 = softmax_plain(sc[1], a.m_run[1], a.l_run[1], scale_log2, pop[1]);
-  if (__any(alpha1 != 1.f)) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) a.oacc[dt][1] *= alpha1;
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    a.oacc[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop[1], a.oacc[dt][1], 0, 0, 0);
 }
 
 // One 32-key chunk from an LDS slot: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
@@ -979,11 +981,9 @@ __device__ __forceinline__ void mfma_chunk(uint32_t slot, const tv_bf16x8 (&qop)
                                            const uint64_t (&ahi)[NTW], int key0, int P, int k_end,
                                            float scale_log2, int lane) {
   constexpr int KK = Chunk<D>::KK, DT = Chunk<D>::DT;
-  if constexpr (NTW == 2) {
-    if (key0 + 32 <= P && key0 + 32 <= k_end) {   // prefix keys only: no mask
-      mfma_chunk_plain2<D>(slot, qop, a, scale_log2, lane);
-      return;
-    }
+  if (key0 + 32 <= P && key0 + 32 <= k_end) {   // prefix keys only: no mask
+    mfma_chunk_plain<D, NTW>(slot, qop, a, scale_log2, lane);
+    return;
   }
   const int h4 = lane >> 4;
   tv_bf16x8 kop[2][KK], vop[DT];
@@ -1069,9 +1069,11 @@ __device__ __forceinline__ void mfma_chunk(uint32_t slot, const tv_bf16x8 (&qop)
   }
   if (__any(any_rescale)) {
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
+    for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] *= alpha[nt];
+      a.lacc[nt] *= alpha[nt];
+    }
   }
   // phase 3: O^T += V^T P^T for every row tile
 #pragma unroll
@@ -1414,6 +1416,7 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
   for (int nt = 0; nt < NTW; ++nt) {
     a.m_run[nt] = kNegInf;
     a.l_run[nt] = 0.f;
+    a.lacc[nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) a.oacc[dt][nt] = (tv_f32x4){0.f, 0.f, 0.f, 0.f};
   }
@@ -1448,7 +1451,7 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
   // row totals of l (a lane holds the sum over its own keys of each chunk)
   float L[NTW];
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) L[nt] = tv_rows_sum(a.l_run[nt]);
+  for (int nt = 0; nt < NTW; ++nt) L[nt] = tv_rows_sum(a.l_run[nt]) + a.lacc[nt][0];
   if constexpr (KG > 1) group_handoff<D, NTW, KG>(slot_lds, a, L, producer, kg, wr, lane);
   const bool writer = !producer && kg == 0;   // group 0 holds the workgroup's state now
 
