@@ -37,7 +37,9 @@
 // the LDS transpose load of gfx950, over rows whose 16-byte pieces the DMA
 // stores XOR-swizzled so that those reads are free of bank conflicts.  The
 // running max moves only when a row's max grows by more than 8 (log2 units),
-// which keeps most chunks free of rescaling.
+// which keeps most chunks free of rescaling.  Chunks of prefix keys only (no
+// mask) take a branch-free body whose row sums come from a matrix product
+// with ones; chunks holding tree keys or the request's end apply the mask.
 //
 // VALU path (fp32): the waves interleave 64-key chunks with lane = key for the
 // scores and lane = d for PV, merged in LDS.
