@@ -959,6 +959,9 @@ __device__ __forceinline__ void mfma_chunk_plain(uint32_t slot, const tv_bf16x8 
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) vop[dt] = lds_vop<D>(slot + 2 * KK * 1024, dt, lane);
+  // LLVM's interleave strategy 3 for matrix products beside exponentials
+  // (measured: 70B-shaped share 758 -> 733 us, ragged 70.1 -> 68.6 us)
+  __builtin_amdgcn_iglp_opt(3);
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     tv_bf16x8 pop;
@@ -973,6 +976,7 @@ __device__ __forceinline__ void mfma_chunk_plain(uint32_t slot, const tv_bf16x8 
     for (int dt = 0; dt < DT; ++dt)
       a.oacc[dt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pop, a.oacc[dt][nt], 0, 0, 0);
     a.lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, a.lacc[nt], 0, 0, 0);
+    __builtin_amdgcn_iglp_opt(3);
   }
 }
 
