@@ -61,6 +61,8 @@ SMALL = [
     ("llama8b", dict(prefix=95, n_nodes=37, tree="star")),          # star tree, ragged row tile
     ("llama8b", dict(prefix=40, n_nodes=128, tree="chain")),        # maximum depth
     ("chain", dict(batch=5, prefix=17, n_nodes=(1, 3))),            # R = 4..12: mostly padding rows
+    ("llama8b", dict(prefix=2000, n_nodes=3)),                      # 12 rows in a 64-row tile, many key splits
+    ("ragged", dict(batch=6, prefix=(50, 3000), n_nodes=2)),        # 8-row tiles, balanced plan
 ]
 
 
@@ -223,12 +225,13 @@ def test_attention_oversized_block_table(name, kw):
     check_all_rows(wl, out1, st1)
 
 
-@pytest.mark.parametrize("scale", [1e5, 1e-6])
-def test_attention_split_partials_extreme_values(scale):
+@pytest.mark.parametrize("scale,n_nodes", [(1e5, 40), (1e-6, 40), (1e5, 3), (1e-6, 3)])
+def test_attention_split_partials_extreme_values(scale, n_nodes):
     """Values of magnitude 1e5 and 1e-6 through the split-K partials (fp16 with
-    a per-row power-of-two scale): the same tolerance as unit-scale values."""
+    a per-row power-of-two scale), for a 40-node tree and a 3-node one (12 rows
+    of a 64-row tile): the same tolerance as unit-scale values."""
     from tree_verification_amd.workloads import round_to_bf16
-    wl = make_workload("llama8b", seed=23, with_logits=False, prefix=1500, n_nodes=40)
+    wl = make_workload("llama8b", seed=23, with_logits=False, prefix=1500, n_nodes=n_nodes)
     wl.v_cache = round_to_bf16(wl.v_cache * np.float32(scale))
     print(f"case partial scale {scale}", flush=True)
     out, st, _, _ = run_gpu(wl)
