@@ -48,10 +48,11 @@
  *               This synchronises, so it must not be set for calls made under
  *               stream capture.
  *   TV_CHASE_SPIN_LIMIT=<n>  a test hook: the verifiers' path-chasing
- *               workgroups give up waiting for their nodes after n polling
- *               rounds (default about 2 s worth) and report TV_REQ_TIMEOUT,
- *               invalidating the workspace; a negative n gives up without
- *               waiting.  Every workgroup still ends normally.
+ *               workgroups, and the attention's key splits waiting for each
+ *               other, give up after n polling rounds (default about 2 s and
+ *               0.5 s worth) and report TV_REQ_TIMEOUT, invalidating the
+ *               workspace; a negative n gives up without waiting.  Every
+ *               workgroup still ends normally.
  */
 #ifndef TREE_VERIFY_H
 #define TREE_VERIFY_H
@@ -135,7 +136,11 @@ size_t tree_attn_workspace_size(const tv_attn_desc* desc);
  *     the workspace was not prepared (its output rows are then not written)
  * The caches are only read.  TV_ERR_WORKSPACE: workspace missing or too small;
  * TV_ERR_INVALID_ARG: q, caches or out not 16-byte aligned, or a workspace
- * not 256-byte aligned. */
+ * not 256-byte aligned; TV_ERR_UNSUPPORTED: a call whose split partials would
+ * need 2 GiB of workspace or more.  When every workgroup of the call is
+ * resident at once, the key splits of a tile wait (bounded, see
+ * TV_CHASE_SPIN_LIMIT) for each other before merging; a wait that expires
+ * gives TV_REQ_TIMEOUT and invalidates the workspace header. */
 int tree_attn_forward(const tv_attn_desc* desc, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
                       const int32_t* n_nodes, const int32_t* parent, void* out, int32_t* status,

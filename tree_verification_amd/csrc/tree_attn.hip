@@ -1303,6 +1303,10 @@ __device__ void merge_together(const AttnParams& p, int* flag, int first, int n_
         }
       }
       if (!ok) {
+        // The request's first workgroup stores the request's status in its
+        // prologue and ORs this flag after that store when its own wait
+        // expires; the other workgroups OR it only after their whole split,
+        // with the grid resident at once well after that prologue.
         if (p.status) __hip_atomic_fetch_or(p.status + b, (int)TV_REQ_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store((unsigned long long*)p.header, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -1786,6 +1790,8 @@ int make_plan(const tv_attn_desc* d, int cu, int ntw, AttnPlan* pl) {
     pl->off_o = tv_align_up(pl->off_cnt + (size_t)slots * sizeof(int), 256);
     pl->off_ml = tv_align_up(pl->off_o + (size_t)slots * pl->rows_per_tile * (size_t)d->head_dim * esz, 256);
     bytes = pl->off_ml + (size_t)slots * pl->rows_per_tile * sizeof(float4);
+    // the partials are addressed through buffer resources with 32-bit sizes
+    if (bytes >= (1ull << 31)) return TV_ERR_UNSUPPORTED;
   }
   pl->bytes = tv_align_up(bytes, 256);
   return TV_OK;
