@@ -140,7 +140,9 @@ size_t tree_attn_workspace_size(const tv_attn_desc* desc);
  * need 2 GiB of workspace or more.  When every workgroup of the call is
  * resident at once, the key splits of a tile wait (bounded, see
  * TV_CHASE_SPIN_LIMIT) for each other before merging; a wait that expires
- * gives TV_REQ_TIMEOUT and invalidates the workspace header. */
+ * gives TV_REQ_TIMEOUT and invalidates the workspace header (a split of the
+ * same call that reads the header after that reports TV_REQ_BAD_WORKSPACE for
+ * its request instead, which needs the same remedy: prepare the workspace). */
 int tree_attn_forward(const tv_attn_desc* desc, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
                       const int32_t* n_nodes, const int32_t* parent, void* out, int32_t* status,

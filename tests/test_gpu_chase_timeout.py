@@ -102,10 +102,14 @@ def test_expired_chase_invalidates_the_workspace():
         assert st == [tv.REQ_BAD_WORKSPACE] * 3 and ln == [0] * 3, (name, st)
         st, ln = out[(name, "prepared")]   # prepared again: the wait expires again, nothing else
         assert st == [tv.REQ_TIMEOUT] * 3, (name, st)
-    # attention's split merge: the same contract for its workspace
-    assert out[("ATTN", "first")][0] == [tv.REQ_TIMEOUT]
+    # attention's split merge: the same contract for its workspace.  A split
+    # that gives up at once invalidates the header while other splits of the
+    # same call may still be in their prologue, so the forced call's request
+    # reports TIMEOUT, BAD_WORKSPACE or both; never success.
+    failed = (tv.REQ_TIMEOUT, tv.REQ_BAD_WORKSPACE, tv.REQ_TIMEOUT | tv.REQ_BAD_WORKSPACE)
+    assert out[("ATTN", "first")][0][0] in failed, out[("ATTN", "first")]
     assert out[("ATTN", "again")][0] == [tv.REQ_BAD_WORKSPACE]
-    assert out[("ATTN", "prepared")][0] == [tv.REQ_TIMEOUT]
+    assert out[("ATTN", "prepared")][0][0] in failed, out[("ATTN", "prepared")]
 
 
 def test_one_polling_round_completes_or_flags():
@@ -122,6 +126,6 @@ def test_one_polling_round_completes_or_flags():
             st2, _ = out[(name, "again")]
             assert st2 == [tv.REQ_BAD_WORKSPACE] * 3, (name, st2)
     st, _ = out[("ATTN", "first")]
-    assert st in ([0], [tv.REQ_TIMEOUT]), st
+    assert st in ([0], [tv.REQ_TIMEOUT], [tv.REQ_BAD_WORKSPACE], [tv.REQ_TIMEOUT | tv.REQ_BAD_WORKSPACE]), st
     st2, _ = out[("ATTN", "again")]
     assert st2 in (([0], [tv.REQ_TIMEOUT]) if st == [0] else ([tv.REQ_BAD_WORKSPACE],)), (st, st2)
