@@ -772,9 +772,6 @@ __device__ __forceinline__ tv_bf16x8 lds_read16(uint32_t addr) {
   return __builtin_bit_cast(tv_bf16x8, *(tv_lds_u32x4_ptr)(uintptr_t)addr);
 }
 
-__device__ __forceinline__ tv_bf16x8 lds_bf16x8(const unsigned char* ptr) {
-  return __builtin_bit_cast(tv_bf16x8, *(const tv_u32x4*)ptr);
-}
 
 // s_waitcnt that only waits for the vector-memory counter (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
@@ -1404,7 +1401,7 @@ __device__ __attribute__((always_inline)) void attn_mfma(const AttnParams& p, Co
   constexpr int DT = Chunk<D>::DT, NB = Chunk<D>::NBLK, NS = ring_steps<KG>();
   constexpr int NW = kMfmaWaves * KG;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int l16 = lane & 15, h4 = lane >> 4;
+  const int l16 = lane & 15;
   const int G = p.G;
   const bool producer = wave >= NW;
   // key group of an MFMA wave, or the group whose chunks a producer moves
