@@ -21,15 +21,14 @@
  *     bounds.
  *   - `workspace` is caller-owned device scratch (256-byte aligned) of at
  *     least the size the matching *_workspace_size() returns for the call's
- *     descriptor.  Both verifiers' workspaces and the attention's hold slots
- *     or counters that must start at zero: prepare each once with
- *     tree_verify_workspace_init (every call leaves them at zero again, so
- *     later calls need nothing).  A workspace that was not prepared, or was
- *     prepared with fewer bytes than the call needs, is detected on the
- *     device from its header and fails the requests that would use it with
- *     TV_REQ_BAD_WORKSPACE; nothing of it is read as exchange data.  The
- *     tree expansion's workspace holds only per-call results and needs no
- *     preparation.  Two calls that may run concurrently must use distinct
+ *     descriptor.  The verifiers', the attention's and the tree expansion's
+ *     workspaces hold slots or counters that must start at zero: prepare
+ *     each once with tree_verify_workspace_init (every call leaves them at
+ *     zero again, so later calls need nothing).  A workspace that was not
+ *     prepared, or was prepared with fewer bytes than the call needs, is
+ *     detected on the device from its header and fails the requests that
+ *     would use it with TV_REQ_BAD_WORKSPACE; nothing of it is read as
+ *     exchange data.  Two calls that may run concurrently must use distinct
  *     workspaces.
  *   - Node ids: a tree of n nodes is a parent array with parent[0] = -1 (node 0
  *     is the root: the last token already emitted) and 0 <= parent[i] < i.
@@ -48,9 +47,10 @@
  *               This synchronises, so it must not be set for calls made under
  *               stream capture.
  *   TV_CHASE_SPIN_LIMIT=<n>  a test hook: the verifiers' path-chasing
- *               workgroups, and the attention's key splits waiting for each
- *               other, give up after n polling rounds (default about 2 s and
- *               0.5 s worth) and report TV_REQ_TIMEOUT, invalidating the
+ *               workgroups, the attention's key splits waiting for each
+ *               other and the tree expansion's per-request workgroups give
+ *               up after n polling rounds (default about 2 s, 0.5 s and 2 s
+ *               worth) and report TV_REQ_TIMEOUT, invalidating the
  *               workspace; a negative n gives up without waiting.  Every
  *               workgroup still ends normally.
  */
@@ -350,7 +350,8 @@ typedef struct tv_expand_desc {
   int32_t k;            /* expansion factor of this level, 1..16 and <= V */
 } tv_expand_desc;
 
-/* Bytes of workspace tree_expand_topk needs for `desc` (0 for an invalid one). */
+/* Bytes of workspace tree_expand_topk needs for `desc` (0 for an invalid one);
+ * prepare it once with tree_verify_workspace_init. */
 size_t tree_expand_workspace_size(const tv_expand_desc* desc);
 
 /* One level of expansion-based construction ([guide] Method A, schedule
@@ -367,9 +368,13 @@ size_t tree_expand_workspace_size(const tv_expand_desc* desc);
  *   status [B]: TV_REQ_BAD_NNODES (n_nodes outside [1, n_max]),
  *   TV_REQ_BAD_LEN (n_frontier or a frontier id out of range),
  *   TV_REQ_TREE_OVERFLOW (more than n_max nodes), TV_REQ_NONFINITE (a read
- *   row holds NaN or +-inf); with any of them nothing is appended and n_new = 0.
- * Workspace: per-call partial results, no initialisation; concurrent calls
- * need distinct workspaces.  TV_ERR_UNSUPPORTED when V > 131072 at k = 16
+ *   row holds NaN or +-inf; reported only when the checks before it pass),
+ *   TV_REQ_BAD_WORKSPACE, TV_REQ_TIMEOUT (a request's wait for its rows'
+ *   partial results expired; the workspace is invalidated); with any of them
+ *   nothing is appended and n_new = 0.
+ * One launch: the per-chunk partial results pass through the prepared
+ * workspace (256-byte aligned, else TV_ERR_INVALID_ARG) to one workgroup per
+ * request in the same grid.  TV_ERR_UNSUPPORTED when V > 131072 at k = 16
  * (ceil(V / 8192) * k must stay <= 256). */
 int tree_expand_topk(const tv_expand_desc* desc, const float* draft_logits, const int32_t* frontier,
                      const int32_t* n_frontier, int32_t* tokens, int32_t* parent, int32_t* n_nodes,

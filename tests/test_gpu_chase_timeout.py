@@ -8,7 +8,9 @@ verify-and-compact then moves no K/V and keeps every request's length.
 Every workgroup still ends normally (the node and argmax workgroups finish
 their own work).  The limit 0 polls once and must leave results either
 complete or flagged.  Tree attention on a grid resident at once (its tiles'
-key splits wait for each other before merging) follows the same contract."""
+key splits wait for each other before merging) and the tree expansion (each
+request's workgroup waits for its rows' chunk results) follow the same
+contract."""
 import os
 import subprocess
 import sys
@@ -71,6 +73,27 @@ CHILD = textwrap.dedent("""
         o, s = tv.tree_attn_forward(da.q, da.k, da.v, da.table, da.prefix_len, da.n_nodes, da.parent, ws=aws)
         torch.cuda.synchronize()
         print("ATTN", step, s.tolist(), [1], flush=True)
+
+    # tree expansion: each request's workgroup waits for its rows' chunk results
+    import numpy as np
+    from tree_verification_amd.workloads import make_expand_rows
+    eB, eF, eV, ek, en = 3, 2, 30011, 2, 32
+    erows = torch.from_numpy(make_expand_rows(eB, eF, eV, 63)).cuda()
+    efr = torch.zeros((eB, eF), dtype=torch.int32, device="cuda:0")
+    enf = torch.full((eB,), eF, dtype=torch.int32, device="cuda:0")
+    edesc = tv.ExpandDesc()
+    edesc.batch, edesc.f_max, edesc.vocab, edesc.n_max, edesc.k = eB, eF, eV, en, ek
+    eneed = lib.tree_expand_workspace_size(ctypes.byref(edesc))
+    ews = tv.init_verify_workspace(torch.zeros(eneed, dtype=torch.uint8, device="cuda:0"))
+    for step in ("first", "again", "prepared"):
+        if step == "prepared":
+            tv.init_verify_workspace(ews)
+        etok = torch.zeros((eB, en), dtype=torch.int32, device="cuda:0")
+        epar = torch.full((eB, en), -1, dtype=torch.int32, device="cuda:0")
+        enn = torch.ones(eB, dtype=torch.int32, device="cuda:0")
+        nf, nn, s = tv.tree_expand_topk(erows, efr, enf, etok, epar, enn, ek, ws=ews)
+        torch.cuda.synchronize()
+        print("EXPAND", step, s.tolist(), nn.tolist(), flush=True)
 """)
 
 
@@ -110,6 +133,14 @@ def test_expired_chase_invalidates_the_workspace():
     assert out[("ATTN", "first")][0][0] in failed, out[("ATTN", "first")]
     assert out[("ATTN", "again")][0] == [tv.REQ_BAD_WORKSPACE]
     assert out[("ATTN", "prepared")][0][0] in failed, out[("ATTN", "prepared")]
+    # expansion: a request workgroup that gives up invalidates the header, which
+    # another request of the same call may read first (then it reports
+    # BAD_WORKSPACE and waits for nothing); at least one reports TIMEOUT
+    for step in ("first", "prepared"):
+        st, nn = out[("EXPAND", step)]
+        assert all(s in (tv.REQ_TIMEOUT, tv.REQ_BAD_WORKSPACE) for s in st), (step, st)
+        assert tv.REQ_TIMEOUT in st and nn == [0] * 3, (step, st, nn)
+    assert out[("EXPAND", "again")] == ([tv.REQ_BAD_WORKSPACE] * 3, [0] * 3)
 
 
 def test_one_polling_round_completes_or_flags():
@@ -129,3 +160,11 @@ def test_one_polling_round_completes_or_flags():
     assert st in ([0], [tv.REQ_TIMEOUT], [tv.REQ_BAD_WORKSPACE], [tv.REQ_TIMEOUT | tv.REQ_BAD_WORKSPACE]), st
     st2, _ = out[("ATTN", "again")]
     assert st2 in (([0], [tv.REQ_TIMEOUT]) if st == [0] else ([tv.REQ_BAD_WORKSPACE],)), (st, st2)
+    st, nn = out[("EXPAND", "first")]
+    for s, n in zip(st, nn):
+        assert (s == 0 and n == 4) or (s in (tv.REQ_TIMEOUT, tv.REQ_BAD_WORKSPACE) and n == 0), (st, nn)
+    st2, _ = out[("EXPAND", "again")]
+    if all(s == 0 for s in st):
+        assert all(s in (0, tv.REQ_TIMEOUT, tv.REQ_BAD_WORKSPACE) for s in st2), st2
+    else:
+        assert st2 == [tv.REQ_BAD_WORKSPACE] * 3, st2

@@ -166,6 +166,36 @@ def test_expand_errors():
     tokens2, parent2, n2 = fresh_trees(1, 20, 9, 3)
     st = check_expand(rows[:1], frontier[:1], nfr[:1], tokens2, parent2, n2, 4)
     assert st[0] == TREE_OVERFLOW
+    # The failed requests' chunk results were drained: the same workspace (one
+    # per descriptor) serves a clean call of the same shape with new rows.
+    rows3 = make_expand_rows(B, F, V, 10)
+    tokens3, parent3, n3 = fresh_trees(B, 20, 8, 10)
+    frontier3 = np.tile(np.arange(F, dtype=np.int32), (B, 1))
+    st = check_expand(rows3, frontier3, np.full(B, F, dtype=np.int32), tokens3, parent3, n3, k)
+    assert (st == 0).all()
+
+
+def test_expand_unprepared_workspace_is_reported():
+    from tree_verification_amd.binding import ExpandDesc, load_library
+    import ctypes
+    B, F, V, k = 2, 2, 9000, 3
+    rows = make_expand_rows(B, F, V, 11)
+    tokens, parent, n_nodes = fresh_trees(B, 32, 4, 11)
+    frontier = np.zeros((B, F), dtype=np.int32)
+    nfr = np.full(B, F, dtype=np.int32)
+    d = ExpandDesc()
+    d.batch, d.f_max, d.vocab, d.n_max, d.k = B, F, V, 32, k
+    need = load_library().tree_expand_workspace_size(ctypes.byref(d))
+    raw = torch.zeros(need, dtype=torch.uint8, device="cuda:0")   # zero, but no header
+    args = [dev(x) for x in (rows, frontier, nfr, tokens, parent, n_nodes)]
+    nf, nn, st = tv.tree_expand_topk(*args, k, ws=raw)
+    torch.cuda.synchronize()
+    assert st.tolist() == [tv.REQ_BAD_WORKSPACE] * B and nn.tolist() == [0] * B
+    assert args[5].tolist() == [4] * B   # nothing appended
+    tv.init_verify_workspace(raw)
+    nf, nn, st = tv.tree_expand_topk(*args, k, ws=raw)
+    torch.cuda.synchronize()
+    assert st.tolist() == [0] * B and nn.tolist() == [F * k] * B
 
 
 def test_expansion_schedule_on_gpu():

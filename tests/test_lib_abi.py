@@ -185,6 +185,8 @@ def test_construction_descriptors_rejected(lib):
     odd = ctypes.c_void_p(4100)
     assert lib.tree_expand_topk(ctypes.byref(e), odd, *([dummy] * 9), need, None) == -1
     assert lib.tree_expand_topk(ctypes.byref(e), *([dummy] * 10), need - 1, None) == -3
+    assert need >= 256 + 2 * 16 * 4 * 8                                        # header, then the key slots
+    assert lib.tree_expand_topk(ctypes.byref(e), *([dummy] * 9), ctypes.c_void_p(4096 + 64), need, None) == -1
 
 
 def test_binding_arity_matches_header():

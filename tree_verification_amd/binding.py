@@ -142,7 +142,7 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
 
 
 # Workspaces: each (device, stream, kind, descriptor) gets its own buffer.  The
-# verifiers' and the attention's are prepared once with
+# verifiers', the attention's and the expansion's are prepared once with
 # tree_verify_workspace_init (every call leaves their slots and counters at
 # zero again).
 _ws: dict = {}
@@ -160,7 +160,7 @@ def workspace(nbytes: int, device: torch.device, kind: str, desc=None) -> torch.
     buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        if kind in ("stochastic", "greedy", "attn"):
+        if kind in ("stochastic", "greedy", "attn", "expand"):
             init_verify_workspace(buf)
         _ws[key] = buf
     return buf

@@ -12,12 +12,19 @@
 // ordered by the creators of their depth-d prefixes (siblings in
 // first-candidate order).
 //
-// Expansion (Method A), one level: topk_chunk_kernel gives every (frontier
-// row, 8192-logit chunk) its k best 64-bit keys (value order, then lower
-// index) by k rounds of a workgroup maximum, each removing the winner from the
-// thread that holds it.  topk_append_kernel (one workgroup per request, one
-// wave per frontier row) merges the chunks' keys of each row the same way and
-// appends the children after the request's last node.
+// Expansion (Method A), one level, as one launch: topk_kernel's grid holds one
+// workgroup per (frontier row, 8192-logit chunk), which finds the chunk's k
+// best 64-bit keys (value order, then lower index) by k rounds of a workgroup
+// maximum, each removing the winner from the thread that holds it, and then
+// one workgroup per request.  Workgroups are dispatched in id order, so a
+// request's workgroup takes a slot only after every chunk workgroup has one;
+// one wave per frontier row polls (bounded) until the row's key slots are
+// written, merges them the same way, and clears them for the next call, and
+// the request's children are appended after its last node.  A key slot is a
+// 64-bit word written with one agent-scope store and never 0 once written
+// (reserved small values mark "no element left" and "non-finite logit"), so a
+// slot carries its own "written" mark and no ordering between addresses is
+// needed.
 
 #include "tv_common.h"
 
@@ -33,6 +40,7 @@ constexpr int kMaxTreeNodes = 1024;
 constexpr int kTopkThreads = 256;
 constexpr int kTopkChunk = kTopkThreads * 32;   // 8192 logits per workgroup
 constexpr int kMaxK = 16;
+constexpr long long kAppendSpinLimit = 1LL << 21;   // a request workgroup's bounded wait (~2 s)
 
 // ===========================================================================
 // merge
@@ -188,19 +196,27 @@ struct ExpandParams {
   int32_t* new_frontier;      // [B][F * k]
   int32_t* n_new;             // [B]
   int32_t* status;            // [B]
-  unsigned long long* keys;   // workspace [B][F][chunks][k]
-  int* flags;                 // workspace [B][F][chunks]: non-finite logit seen
+  unsigned long long* header; // workspace [2]: kWsMagic, bytes zero-filled by tree_verify_workspace_init
+  unsigned long long need;    // bytes this call's layout uses (header included)
+  unsigned long long* keys;   // workspace [B][F][chunks][k], zero between calls
   int B, F, V, n_max, k, chunks;
+  int G;                      // chunk workgroups; the B workgroups after them append the children
+  long long spin;             // polling rounds before a request workgroup gives up (negative: at once)
 };
 
-// Order-preserving key: larger value first, then lower index; never 0 for an
-// index below 2^32 - 1, so 0 marks "no element".  -0 and +0 tie.
+// Order-preserving key: larger value first, then lower index.  For a finite
+// or infinite value and an index below 2^31 it exceeds 2^32, so the values
+// below are free: 0 is an unwritten slot, kKeyNone a chunk with no element
+// left, kKeyBad a chunk holding a NaN or an infinity.  -0 and +0 tie.
 __device__ __forceinline__ unsigned long long topk_key(float v, int idx) {
   uint32_t b = __float_as_uint(v);
   if (b == 0x80000000u) b = 0u;
   const uint32_t hi = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
   return ((unsigned long long)hi << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
+
+constexpr unsigned long long kKeyNone = 1ull;
+constexpr unsigned long long kKeyBad = 2ull;
 
 __device__ __forceinline__ int key_index(unsigned long long key) {
   return (int)(0xFFFFFFFFu - (uint32_t)key);
@@ -241,15 +257,18 @@ __device__ __forceinline__ unsigned long long thread_best(const float (&x)[32], 
   return bj < 0 ? 0ull : topk_key(bv, bj < 16 ? e0 + bj : e1 + bj - 16);
 }
 
+// One (frontier row, chunk) unit: the chunk's k best keys into its k slots
+// (kKeyNone once the chunk has no element left; every slot kKeyBad when the
+// chunk holds a non-finite logit).  Rows at or past the request's frontier
+// size are skipped (the request workgroup reads only rows f < n_frontier).
 template <bool kVec>
-__global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(ExpandParams p) {
-  __shared__ unsigned long long red[2][kTopkThreads / 64];
+__device__ __forceinline__ void topk_chunk(const ExpandParams& p, unsigned long long (&red)[2][kTopkThreads / 64]) {
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int c = blockIdx.x % p.chunks;
   const int row = blockIdx.x / p.chunks;   // b * F + f
   const int b = row / p.F, f = row % p.F;
   const int nf = p.n_frontier[b];
-  if (nf < 0 || nf > p.F || f >= nf) return;   // the append kernel reads only rows f < nf
+  if (nf < 0 || nf > p.F || f >= nf) return;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.logits + (size_t)row * p.V), (short)0, p.V * 4, 0x00020000);
   const int lo = c * kTopkChunk, hi = min(p.V, lo + kTopkChunk);
@@ -263,8 +282,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(ExpandParams p
   if (hi - lo == kTopkChunk) {
     // A full chunk: no per-entry bounds tests.  The thread's best is its largest
     // value (three-input maxima) at the first entry holding it, the same key
-    // as thread_best gives when every entry is finite (a row with a non-finite
-    // entry is flagged, and its keys are not used).
+    // as thread_best gives when every entry is finite (a chunk with a
+    // non-finite entry publishes kKeyBad instead).
 #pragma unroll
     for (int j = 0; j < 32; ++j) bad |= !isfinite(x[j]);
     const float m = fmaxf(tv_max16(x), tv_max16(x + 16));
@@ -282,12 +301,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(ExpandParams p
     }
     key = thread_best(x, e0, e1, &jb);
   }
-  // written for every chunk of every row the append kernel reads, so the
-  // workspace needs no clearing (a non-finite row yields unspecified keys; the
-  // append kernel then writes nothing)
-  if (__syncthreads_or(bad) && t == 0) p.flags[(size_t)row * p.chunks + c] = 1;
-  else if (t == 0) p.flags[(size_t)row * p.chunks + c] = 0;
   unsigned long long* out = p.keys + ((size_t)row * p.chunks + c) * p.k;
+  if (__syncthreads_or(bad)) {
+    if (t < p.k) __hip_atomic_store(out + t, kKeyBad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   for (int r = 0; r < p.k; ++r) {
     const unsigned long long wmax = tv_wave_max_u64(key);
     if (l == 0) red[r & 1][w] = wmax;
@@ -295,7 +313,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(ExpandParams p
     unsigned long long m = red[r & 1][0];
 #pragma unroll
     for (int i = 1; i < kTopkThreads / 64; ++i) m = red[r & 1][i] > m ? red[r & 1][i] : m;
-    if (t == 0) out[r] = m;
+    if (t == 0) __hip_atomic_store(out + r, m ? m : kKeyNone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (m != 0ull && key == m) {   // keys are unique: exactly one thread holds the winner
 #pragma unroll
       for (int j = 0; j < 32; ++j)
@@ -305,44 +323,78 @@ __global__ __launch_bounds__(kTopkThreads) void topk_chunk_kernel(ExpandParams p
   }
 }
 
-// One workgroup per request: status, then one wave per frontier row merges the
-// chunks' keys (k rounds of a wave maximum) and appends the children.
-__global__ __launch_bounds__(kTopkThreads) void topk_append_kernel(ExpandParams p) {
-  __shared__ int s_bad;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, b = blockIdx.x;
+struct AppendSmem {
+  int flags;
+  int win[kMaxTreeNodes];     // the appended tokens, in id order (at most n_max - 1 of them)
+  int front[kMaxTreeNodes];   // the frontier ids (n_frontier * k < n_max once the checks pass)
+};
+
+// Request b's workgroup: status, then one wave per frontier row f <
+// n_frontier waits for the row's chunks * k slots (at most 256: four per
+// lane), merges them by k rounds of a wave maximum and clears them; the
+// children are appended once every row is in.  The slots of rows f <
+// n_frontier are drained whenever the chunk workgroups wrote them (the
+// workspace is prepared and n_frontier is in range), also when the request
+// fails its other checks, so that no slot stays set for the next call.  A row
+// not complete within p.spin rounds fails the request with TV_REQ_TIMEOUT and
+// invalidates the workspace header (its slots may still be written later):
+// later calls report TV_REQ_BAD_WORKSPACE until the workspace is prepared
+// again.
+__device__ void topk_append(const ExpandParams& p, AppendSmem& sm, int b) {
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int n0 = p.n_nodes[b], nf = p.n_frontier[b];
-  if (t == 0) s_bad = 0;
+  const unsigned long long magic = p.header[0], bytes = p.header[1];
+  const bool wsok = (magic == kWsMagic) & (bytes >= p.need);
+  if (t == 0) sm.flags = 0;
   __syncthreads();
   int fl = 0;
-  if (n0 < 1 || n0 > p.n_max) fl = TV_REQ_BAD_NNODES;
+  if (!wsok) fl = TV_REQ_BAD_WORKSPACE;
   else if (nf < 0 || nf > p.F) fl = TV_REQ_BAD_LEN;
+  else if (n0 < 1 || n0 > p.n_max) fl = TV_REQ_BAD_NNODES;
   else if (n0 + nf * p.k > p.n_max) fl = TV_REQ_TREE_OVERFLOW;
   if (fl == 0) {
     for (int f = t; f < nf; f += kTopkThreads) {
       const int u = p.frontier[(size_t)b * p.F + f];
-      if (u < 0 || u >= n0) atomicOr(&s_bad, TV_REQ_BAD_LEN);
+      sm.front[f] = u;
+      if (u < 0 || u >= n0) atomicOr(&sm.flags, TV_REQ_BAD_LEN);
     }
-    for (int q = t; q < nf * p.chunks; q += kTopkThreads)
-      if (p.flags[((size_t)b * p.F) * p.chunks + q]) atomicOr(&s_bad, TV_REQ_NONFINITE);
   }
-  __syncthreads();
-  fl |= s_bad;
-  if (fl) {
-    if (t == 0) {
-      p.status[b] = fl;
-      p.n_new[b] = 0;
-    }
-    return;
-  }
-  int32_t* tokens = p.tokens + (size_t)b * p.n_max;
-  int32_t* parent = p.parent + (size_t)b * p.n_max;
-  const int nk = p.chunks * p.k;   // candidate keys per row (<= 64 * 4 at V <= 2^21, k <= 16)
-  for (int f = w; f < nf; f += kTopkThreads / 64) {
-    const unsigned long long* keys = p.keys + ((size_t)b * p.F + f) * nk;
-    unsigned long long kk[4];
+  const bool drain = wsok && nf >= 0 && nf <= p.F;
+  const int nk = p.chunks * p.k;
+  for (int f = w; drain && f < nf; f += kTopkThreads / 64) {
+    unsigned long long* keys = p.keys + ((size_t)b * p.F + f) * nk;
+    unsigned long long kk[4] = {0ull, 0ull, 0ull, 0ull};
+    bool done = p.spin >= 0;
+    for (long long it = 0; done; ++it) {
+      bool mine = true;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kk[i] = l + 64 * i < nk ? keys[l + 64 * i] : 0ull;
-    const int u = p.frontier[(size_t)b * p.F + f];
+      for (int i = 0; i < 4; ++i) {
+        const int s = l + 64 * i;
+        if (s < nk && kk[i] == 0ull) kk[i] = __hip_atomic_load(keys + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mine = mine && (s >= nk || kk[i] != 0ull);
+      }
+      if (__all(mine)) break;
+      if (it >= p.spin) done = false;
+      else __builtin_amdgcn_s_sleep(2);
+    }
+    if (!done) {
+      if (l == 0) {
+        atomicOr(&sm.flags, TV_REQ_TIMEOUT);
+        p.header[0] = 0ull;
+      }
+      continue;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (l + 64 * i < nk) __hip_atomic_store(keys + l + 64 * i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bad = bad || kk[i] == kKeyBad;
+    if (__any(bad)) {
+      if (l == 0) atomicOr(&sm.flags, TV_REQ_NONFINITE);
+      continue;
+    }
+    if (fl) continue;   // drained only
     for (int r = 0; r < p.k; ++r) {
       unsigned long long mine = kk[0];
 #pragma unroll
@@ -350,20 +402,47 @@ __global__ __launch_bounds__(kTopkThreads) void topk_append_kernel(ExpandParams 
       const unsigned long long m = tv_wave_max_u64(mine);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (kk[i] == m) kk[i] = 0ull;   // unique keys: one lane, one slot
-      if (l == 0) {
-        const int id = n0 + f * p.k + r;
-        tokens[id] = key_index(m);
-        parent[id] = u;
-        p.new_frontier[(size_t)b * p.F * p.k + f * p.k + r] = id;
-      }
+        if (kk[i] == m) kk[i] = 0ull;   // the k best are unique keys: one lane, one slot
+      if (l == 0) sm.win[f * p.k + r] = key_index(m);
     }
   }
+  __syncthreads();
+  const int got = sm.flags;
+  // Precedence as in the checks above: a request that fails them reports only
+  // those flags (and a timeout); a non-finite row is reported otherwise.
+  if (fl == 0) fl = got;
+  else fl |= got & TV_REQ_TIMEOUT;
+  if (fl) {
+    if (t == 0) {
+      p.status[b] = fl;
+      p.n_new[b] = 0;
+    }
+    return;
+  }
+  const int nnew = nf * p.k;
+  int32_t* tokens = p.tokens + (size_t)b * p.n_max + n0;
+  int32_t* parent = p.parent + (size_t)b * p.n_max + n0;
+  int32_t* nfr = p.new_frontier + (size_t)b * p.F * p.k;
+  for (int i = t; i < nnew; i += kTopkThreads) {
+    tokens[i] = sm.win[i];
+    parent[i] = sm.front[i / p.k];
+    nfr[i] = n0 + i;
+  }
   if (t == 0) {
-    p.n_nodes[b] = n0 + nf * p.k;
-    p.n_new[b] = nf * p.k;
+    p.n_nodes[b] = n0 + nnew;
+    p.n_new[b] = nnew;
     p.status[b] = 0;
   }
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(ExpandParams p) {
+  __shared__ union {
+    unsigned long long red[2][kTopkThreads / 64];
+    AppendSmem a;
+  } sm;
+  if ((int)blockIdx.x >= p.G) topk_append(p, sm.a, (int)blockIdx.x - p.G);
+  else topk_chunk<kVec>(p, sm.red);
 }
 
 int check_expand(const tv_expand_desc* d) {
@@ -372,24 +451,22 @@ int check_expand(const tv_expand_desc* d) {
   if (d->k > d->vocab) return TV_ERR_INVALID_ARG;
   if (d->k > kMaxK || d->n_max > kMaxTreeNodes) return TV_ERR_UNSUPPORTED;
   const long long chunks = (d->vocab + kTopkChunk - 1) / kTopkChunk;
-  if (chunks * d->k > 256) return TV_ERR_UNSUPPORTED;   // the append kernel's wave holds 4 keys per lane
+  if (chunks * d->k > 256) return TV_ERR_UNSUPPORTED;   // a request workgroup's wave holds 4 slots per lane
   return TV_OK;
 }
 
 struct ExpandLayout {
-  size_t keys, flags, bytes;
+  size_t keys, bytes;
   int chunks;
 };
 
+// The workspace: the prepared-workspace header, then the key slots.
 ExpandLayout expand_layout(const tv_expand_desc* d) {
   ExpandLayout L;
   L.chunks = (d->vocab + kTopkChunk - 1) / kTopkChunk;
   const size_t rows = (size_t)d->batch * d->f_max;
-  L.keys = 0;
-  size_t o = tv_align_up(rows * L.chunks * d->k * sizeof(unsigned long long), 256);
-  L.flags = o;
-  o = tv_align_up(o + rows * L.chunks * sizeof(int), 256);
-  L.bytes = o;
+  L.keys = kWsHeader;
+  L.bytes = tv_align_up(L.keys + rows * L.chunks * d->k * sizeof(unsigned long long), 256);
   return L;
 }
 
@@ -448,6 +525,7 @@ static int tree_expand_topk_impl(const tv_expand_desc* desc, const float* draft_
   if (((uintptr_t)draft_logits & 15) != 0) return TV_ERR_INVALID_ARG;
   const ExpandLayout L = expand_layout(desc);
   if (!workspace || workspace_bytes < L.bytes) return TV_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255) != 0) return TV_ERR_INVALID_ARG;
   ExpandParams p;
   p.logits = draft_logits;
   p.frontier = frontier;
@@ -458,22 +536,24 @@ static int tree_expand_topk_impl(const tv_expand_desc* desc, const float* draft_
   p.new_frontier = new_frontier;
   p.n_new = n_new;
   p.status = status;
+  p.header = (unsigned long long*)workspace;
+  p.need = L.bytes;
   p.keys = (unsigned long long*)((char*)workspace + L.keys);
-  p.flags = (int*)((char*)workspace + L.flags);
   p.B = desc->batch;
   p.F = desc->f_max;
   p.V = desc->vocab;
   p.n_max = desc->n_max;
   p.k = desc->k;
   p.chunks = L.chunks;
-  const long long grid = (long long)desc->batch * desc->f_max * L.chunks;
+  const long long units = (long long)desc->batch * desc->f_max * L.chunks;
+  const long long grid = units + desc->batch;
   if (grid > 0x7fffffff || (long long)desc->vocab * 4 > 0x7fffffff) return TV_ERR_UNSUPPORTED;
+  p.G = (int)units;
+  p.spin = tv_chase_spin_limit(kAppendSpinLimit);
   if ((desc->vocab & 3) == 0)
-    hipLaunchKernelGGL(topk_chunk_kernel<true>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, p);
+    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(topk_chunk_kernel<false>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  hipLaunchKernelGGL(topk_append_kernel, dim3((unsigned)desc->batch), dim3(kTopkThreads), 0, stream, p);
+    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)grid), dim3(kTopkThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
